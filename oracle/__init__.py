@@ -1,0 +1,29 @@
+"""Plain, slow fp64 CPU oracle for attention-based prompt-token importance.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import this package.  The product library never calls it
+and shares no code with it.
+
+Parity pins for every function are listed in the ``kvs`` module docstring.
+"""
+from .kvs import (  # noqa: F401
+    bf16_to_f64,
+    score,
+    head_reduce,
+    pool,
+    pages,
+    pool_pages,
+    aggregate_layers,
+    cluster_priority,
+    topk,
+    block_select,
+    block_union_pagetable,
+    HEADS_NONE,
+    HEADS_GROUP_SUM,
+    HEADS_GROUP_MAX,
+    RED_NONE,
+    RED_SUM,
+    RED_MAX,
+    RED_MEAN,
+    RED_SUM_L1,
+)

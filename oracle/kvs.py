@@ -1,0 +1,361 @@
+"""fp64 reference of the scoring-and-selection path (TEST INFRASTRUCTURE ONLY).
+
+Every function is the plain definition written out with NumPy in float64; a
+matrix product, an argsort and a cumulative sum serve as library steps.  There
+is no blocking, fusion or reordering beyond what each definition states.  Only
+``tests/``, the smoke check and the bench's CPU-baseline leg use this module.
+
+Sources (web pages on the subject; cited by title and section):
+
+* [CLAA] "CLAA: cross-layer attention aggregation ..." (pinghaoyang.com.cn blog
+  post): section "Three representative token-ranking methods" (FastKV window
+  score: softmax over keys, summed over the window rows and all heads; logit
+  scale 1/sqrt(d_k)); section "Three design decisions" (per-layer window score,
+  Eq. 6 token-wise max over the buffered layers); section "The oracle
+  construction" (1-D pooling with kernel 7); section "Complete flow and cost"
+  (top-k by keep rate, kept tokens keep their original positions).
+* [ClusterAttn] "ClusterAttn: KV Cache Compression under Intrinsic Attention
+  Clustering" (papercache.org note): section "Background and key observations",
+  the feature-aggregation equations (window logits W_win, window mask M_win,
+  softmax A_win^m, column sum P); section "Method details" (density-based
+  clustering: block max, threshold theta, neighbourhood r, unique+topk fill;
+  Table 1 theta per compression size; window concatenated afterwards).
+* [CompactAttention] "CompactAttention: Accelerating Chunked Prefill with
+  Block-Union KV Selection": "Core method" / "Method step details" (Q-block
+  union, intra-group union, 4-head subgroups, per-group page table T_{b,g},
+  kv_indptr/kv_indices); "Technical novelty" (minimality of T_{b,g}).
+* [LookaheadKV] "LookaheadKV: Fast and Accurate KV Cache Eviction by Glimpsing
+  into the Future without Generation": "Background: KL divergence and ListNet"
+  (L1 normalisation s / ||s||_1).
+* [DELTA] "DELTA: Dynamic Layer-Aware Token Attention for Efficient
+  Long-Context Reasoning": "Key design 2" (token score = max over heads of the
+  post-softmax attention; page score = sum over the page's tokens; recency
+  pages forced); "Key design 3" (page size P = 16).
+
+Readings where the pages are silent or garbled (all restated in the design doc):
+contiguous GQA grouping h -> h // G; causal visibility t <= q_pos0 + j inside the
+window (the garbled ``max(W, M_win)`` read as an additive -inf mask); scores over
+all L keys; GROUP_MAX sums a head's W rows before the max over heads; pooling
+clipped to [0, n) (MEAN divides by the in-range count); argmax ties go to the
+lowest index; top-k key (priority desc, value desc, index asc), -0 == +0, NaN
+below every number; cluster centres are page argmaxes whose page max >= theta
+and a token is prioritised if within r of a centre; top-p keeps a block while
+the mass ranked strictly before it is < p.
+
+Parity pins (tests/test_oracle_*.py): row-stochastic mass, identical-key closed
+forms, SciPy softmax special case, GQA mapping by construction, linearity,
+permutation and shift invariance, planted spans rank first; SciPy filters for
+pooling; hand-built page/argmax, cluster, top-k, block-select and union cases
+with known answers; brute force on tiny arrays.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX = 0, 1, 2
+RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns, as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Scoring: masked softmax over keys, column sums over window rows and heads
+# ---------------------------------------------------------------------------
+
+def score(Q, K, *, L: int, W: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
+          heads: int = HEADS_GROUP_SUM, scale: Optional[float] = None,
+          per_row: bool = False) -> np.ndarray:
+    """Column sums of the masked, softmax-normalised window attention.
+
+    [ClusterAttn] feature aggregation: logits of the window queries against the
+    prompt keys, masked, softmax-normalised over keys, summed over window rows.
+    [CLAA] FastKV / per-layer window score: also summed over the heads of the
+    group (here the G query heads sharing KV head g).  [DELTA] key design 2:
+    maximum over heads instead of the sum.
+
+    Q: bf16 bits [H_q][W][d_k]; K: bf16 bits [H_kv][L][d_k].
+    Row j of every head sits at position q_pos0 + j and sees keys t <= q_pos0 + j.
+    Returns float64 [H_q][L] (NONE) or [H_kv][L] (GROUP_SUM / GROUP_MAX).
+    With ``per_row`` returns the attention rows [H_q][W][L] instead.
+    """
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    q = bf16_to_f64(Q).reshape(H_q, W, d_k)
+    k = bf16_to_f64(K).reshape(H_kv, L, d_k)
+    t = np.arange(L)
+    pos = q_pos0 + np.arange(W)
+    visible = t[None, :] <= pos[:, None]                 # [W][L]
+    per_head = np.zeros((H_q, L), dtype=np.float64)
+    rows = np.zeros((H_q, W, L), dtype=np.float64) if per_row else None
+    for h in range(H_q):
+        g = h // G                                        # contiguous GQA grouping
+        s = scale * (q[h] @ k[g].T)                       # [W][L] logits
+        s = np.where(visible, s, -np.inf)                 # additive -inf mask
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)                                 # masked entries -> 0
+        a = e / e.sum(axis=1, keepdims=True)              # softmax over keys
+        if per_row:
+            rows[h] = a
+        per_head[h] = a.sum(axis=0)                       # column sum over window rows
+    if per_row:
+        return rows
+    if heads == HEADS_NONE:
+        return per_head
+    grouped = per_head.reshape(H_kv, G, L)
+    if heads == HEADS_GROUP_SUM:
+        return grouped.sum(axis=1)
+    if heads == HEADS_GROUP_MAX:
+        return grouped.max(axis=1)
+    raise ValueError("unknown heads mode")
+
+
+# ---------------------------------------------------------------------------
+# Pooling and page aggregation
+# ---------------------------------------------------------------------------
+
+def head_reduce(x, mode: int) -> np.ndarray:
+    """Reduce the rows of x [H][n] to one row: SUM or MAX; NONE keeps x.
+
+    [DELTA] key design 2 takes the maximum over heads before paging.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if mode == RED_NONE:
+        return x
+    if mode == RED_SUM:
+        return x.sum(axis=0, keepdims=True)
+    if mode == RED_MAX:
+        return x.max(axis=0, keepdims=True)
+    raise ValueError("head reduce must be NONE, SUM or MAX")
+
+
+def pool(x, mode: int, k: int) -> np.ndarray:
+    """1-D pooling with odd kernel k over [t - r, t + r] clipped to [0, n).
+
+    [CLAA] the oracle construction and experimental setup: 1-D pooling with
+    kernel 7 smooths token scores before ranking (average there; max pooling is
+    the same window with max).  MEAN divides by the number of in-range terms.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if mode == RED_NONE:
+        return x.copy()
+    if k < 1 or k % 2 == 0:
+        raise ValueError("pool kernel must be odd")
+    r = (k - 1) // 2
+    H, n = x.shape
+    if mode == RED_MAX:
+        out = np.full((H, n), -np.inf)
+    elif mode == RED_MEAN:
+        out = np.zeros((H, n))
+    else:
+        raise ValueError("pool must be NONE, MAX or MEAN")
+    cnt = np.zeros(n)
+    for o in range(-r, r + 1):
+        lo = max(0, -o)
+        hi = min(n, n - o)
+        if hi <= lo:
+            continue
+        src = x[:, lo + o:hi + o]
+        if mode == RED_MAX:
+            out[:, lo:hi] = np.maximum(out[:, lo:hi], src)
+        else:
+            out[:, lo:hi] += src
+        cnt[lo:hi] += 1
+    if mode == RED_MEAN:
+        out = out / cnt[None, :]
+    return out
+
+
+def pages(x, P: int, mode: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Page aggregation over tokens [uP, min(uP + P, n)) and the page argmax.
+
+    [DELTA] key design 2 (page score = sum over the page's tokens) and key
+    design 3 (P = 16 tokens per page); [ClusterAttn] method details (block max
+    and the block-level max index).  The argmax is the lowest index attaining
+    the page maximum.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    H, n = x.shape
+    n_pages = (n + P - 1) // P
+    z = np.zeros((H, n_pages))
+    arg = np.zeros((H, n_pages), dtype=np.int64)
+    for u in range(n_pages):
+        seg = x[:, u * P:min(u * P + P, n)]
+        if mode == RED_SUM:
+            z[:, u] = seg.sum(axis=1)
+        elif mode == RED_MAX:
+            z[:, u] = seg.max(axis=1)
+        else:
+            raise ValueError("page reduce must be SUM or MAX")
+        arg[:, u] = u * P + np.argmax(seg, axis=1)       # first index of the maximum
+    return z, arg
+
+
+def pool_pages(S, *, head_mode: int = RED_NONE, pool_mode: int = RED_NONE, pool_k: int = 7,
+               P: int = 0, page_mode: int = RED_SUM):
+    """head reduce -> pool -> page, the order the library applies them in."""
+    y = pool(head_reduce(S, head_mode), pool_mode, pool_k)
+    if P:
+        z, arg = pages(y, P, page_mode)
+        return y, z, arg
+    return y, None, None
+
+
+# ---------------------------------------------------------------------------
+# Cross-layer aggregation
+# ---------------------------------------------------------------------------
+
+def aggregate_layers(layer_scores: Sequence[np.ndarray], mode: int) -> np.ndarray:
+    """Combine per-layer token scores into one vector.
+
+    Each layer's rows are summed over heads first (the FastKV / CLAA per-layer
+    score sums over all heads).  SUM_L1: each layer divided by its own L1 norm
+    ([LookaheadKV] s / ||s||_1), then summed over layers.  MAX: token-wise
+    maximum over layers ([CLAA] Eq. 6).
+    """
+    per_layer = [np.asarray(s, dtype=np.float64).sum(axis=0) for s in layer_scores]
+    if mode == RED_SUM_L1:
+        acc = np.zeros_like(per_layer[0])
+        for s in per_layer:
+            acc = acc + s / np.abs(s).sum()
+        return acc
+    if mode == RED_MAX:
+        acc = per_layer[0].copy()
+        for s in per_layer[1:]:
+            acc = np.maximum(acc, s)
+        return acc
+    raise ValueError("aggregate mode must be SUM_L1 or MAX")
+
+
+# ---------------------------------------------------------------------------
+# Density clustering priority ([ClusterAttn] method details)
+# ---------------------------------------------------------------------------
+
+def cluster_priority(page, page_arg, n: int, theta: float, r: int) -> np.ndarray:
+    """uint8 [H][n]: 1 where a token lies within r of a cluster centre.
+
+    Centres are the block-level max indices whose block maximum is not below
+    theta; each centre gathers its neighbourhood [c - r, c + r].
+    """
+    page = np.asarray(page, dtype=np.float64)
+    page_arg = np.asarray(page_arg)
+    H = page.shape[0]
+    prio = np.zeros((H, n), dtype=np.uint8)
+    for h in range(H):
+        for u in range(page.shape[1]):
+            if page[h, u] >= theta:
+                c = int(page_arg[h, u])
+                prio[h, max(0, c - r):min(n, c + r + 1)] = 1
+    return prio
+
+
+# ---------------------------------------------------------------------------
+# Top-k selection with stable ties and a forced suffix
+# ---------------------------------------------------------------------------
+
+def topk(S, budget: int, priority=None, n_forced: int = 0) -> np.ndarray:
+    """Indices of the ``budget`` best tokens per row, ascending, then the suffix.
+
+    Order: priority descending, value descending, index ascending (ties go to
+    the lower index).  -0.0 equals +0.0; NaN ranks below every number.  The
+    forced suffix [n, n + n_forced) is appended ([ClusterAttn] the observation
+    window is kept in full; [DELTA] recency pages).  Output is sorted ascending
+    so kept tokens keep their original order and positions ([CLAA] complete
+    flow: original position ids).
+    """
+    S = np.asarray(S)
+    H, n = S.shape
+    if not 0 <= budget <= n:
+        raise ValueError("budget must be in [0, n]")
+    out = np.zeros((H, budget + n_forced), dtype=np.int64)
+    for h in range(H):
+        v = S[h].astype(np.float64)
+        nan = np.isnan(v)
+        vv = np.where(nan, 0.0, v) + 0.0                   # -0.0 + 0.0 == +0.0
+        pr = np.zeros(n, dtype=np.int64) if priority is None else np.asarray(priority[h], dtype=np.int64)
+        idx = np.arange(n)
+        # lexsort: last key is primary.
+        order = np.lexsort((idx, -vv, (~nan).astype(np.int64) * -1, -pr))
+        chosen = np.sort(order[:budget])
+        out[h, :budget] = chosen
+        out[h, budget:] = np.arange(n, n + n_forced)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Chunked-prefill block selection and block union ([CompactAttention])
+# ---------------------------------------------------------------------------
+
+def block_select(Qc, K, *, Lq: int, L: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
+                 block: int = 64, p_mass: float = 0.9, scale: Optional[float] = None) -> np.ndarray:
+    """Binary block mask M [H_q][n_qb][n_kvb] from mean-pooled block logits.
+
+    Kb[g][j] = mean of the keys of block j; Qb[h][i] = mean of the chunk rows of
+    query block i.  Query block i ends at position q_pos0 + last row of the block;
+    KV block j is visible when its first token is not after that position.
+    Logits scale * Qb . Kb over visible blocks, softmax; blocks ordered by
+    (probability desc, j asc); block j is kept while the mass ranked strictly
+    before it is < p_mass (so the crossing block is kept).
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    G = H_q // H_kv
+    q = bf16_to_f64(Qc).reshape(H_q, Lq, d_k)
+    k = bf16_to_f64(K).reshape(H_kv, L, d_k)
+    n_qb = (Lq + block - 1) // block
+    n_kvb = (L + block - 1) // block
+    Kb = np.zeros((H_kv, n_kvb, d_k))
+    for j in range(n_kvb):
+        Kb[:, j] = k[:, j * block:min(L, j * block + block)].mean(axis=1)
+    M = np.zeros((H_q, n_qb, n_kvb), dtype=np.uint8)
+    for h in range(H_q):
+        g = h // G
+        for i in range(n_qb):
+            rows = q[h, i * block:min(Lq, i * block + block)]
+            qb = rows.mean(axis=0)
+            end_pos = q_pos0 + min(Lq, i * block + block) - 1
+            vis = np.arange(n_kvb) * block <= end_pos
+            b = scale * (Kb[g] @ qb)
+            b = np.where(vis, b, -np.inf)
+            e = np.exp(b - b.max())
+            p = e / e.sum()
+            order = np.lexsort((np.arange(n_kvb), -p))
+            before = np.cumsum(p[order]) - p[order]          # mass ranked strictly before
+            keep = (before < p_mass) & vis[order]
+            M[h, i, order[keep]] = 1
+    return M
+
+
+def block_union_pagetable(M, *, H_q: int, H_kv: int, sub_group: int = 0):
+    """Per-group KV page table (CSR) from a per-head 2-D block mask.
+
+    M_bar[h][j] = OR over query blocks i of M[h][i][j]; G[s][j] = OR over the
+    heads h of subgroup s (subgroups of ``sub_group`` consecutive heads inside a
+    KV group); T_s = {j : G[s][j] = 1} listed ascending.  Returns kv_indptr
+    [n_groups + 1] (exclusive prefix sum of |T_s|) and kv_indices.
+    """
+    M = np.asarray(M, dtype=np.uint8)
+    G = H_q // H_kv
+    sg = G if sub_group == 0 else sub_group
+    if G % sg:
+        raise ValueError("sub_group must divide H_q / H_kv")
+    n_groups = H_q // sg
+    mbar = M.max(axis=1)                                   # Q-block union
+    indptr = np.zeros(n_groups + 1, dtype=np.int64)
+    lists: List[np.ndarray] = []
+    for s in range(n_groups):
+        gm = mbar[s * sg:(s + 1) * sg].max(axis=0)        # intra-group union
+        js = np.nonzero(gm)[0]
+        lists.append(js)
+        indptr[s + 1] = indptr[s] + len(js)
+    indices = np.concatenate(lists) if lists else np.zeros(0, dtype=np.int64)
+    return indptr, indices.astype(np.int64)
