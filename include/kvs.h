@@ -1,0 +1,232 @@
+/*
+ * kvs.h - attention-based prompt-token importance scoring and selection on
+ * AMD Instinct MI355X (gfx950).  C ABI of libkvs.so.
+ *
+ * Every call enqueues HIP kernels on `stream` (a hipStream_t passed as void*;
+ * NULL selects the default stream) and returns without synchronizing.  All
+ * tensor pointers are DEVICE pointers that the caller allocates and owns; the
+ * library never allocates, frees or copies to the host, and never writes an
+ * input.  Scratch memory comes from the caller through the `ws` / `ws_bytes`
+ * workspace arguments, sized by the matching *_workspace() query.  Calls are
+ * stateless and reentrant; calls on different streams may run concurrently as
+ * long as their workspaces and outputs do not overlap.
+ *
+ * Errors: argument problems are detected on the host and reported BEFORE
+ * anything is enqueued.  KVS_EINVAL: a null pointer, a size out of range, a
+ * misaligned pointer or stride.  KVS_EUNSUPPORTED: a valid shape this build
+ * has no kernel for.  KVS_EWORKSPACE: ws_bytes below the query's answer.
+ * KVS_EHIP: a kernel launch failed.  Faults inside kernels surface at the
+ * caller's next synchronization.  No C++ exception crosses this boundary.
+ *
+ * Sources (web pages on the subject, cited by title and section):
+ *  [CLAA]   CLAA cross-layer attention aggregation blog post: "Three
+ *           representative token-ranking methods" (FastKV window score),
+ *           "Three design decisions" (per-layer window score; Eq. 6 max over
+ *           buffered layers), "The oracle construction" (1-D pooling, kernel
+ *           7), "Complete flow and cost" (topk by keep rate; original
+ *           position ids).
+ *  [ClusterAttn] "ClusterAttn: KV Cache Compression under Intrinsic Attention
+ *           Clustering": "Background and key observations" (window logits,
+ *           window mask, softmax, column sum P), "Method details" (density
+ *           clustering; Table 1 theta; window concatenated).
+ *  [CompactAttention] "CompactAttention: Accelerating Chunked Prefill with
+ *           Block-Union KV Selection": "Method step details" (Q-block union,
+ *           intra-group union, kv_indptr / kv_indices), "Technical novelty"
+ *           (minimal page table).
+ *  [LookaheadKV] "LookaheadKV: Fast and Accurate KV Cache Eviction by
+ *           Glimpsing into the Future without Generation": background on KL
+ *           divergence (L1 normalisation s / ||s||_1).
+ *  [DELTA]  "DELTA: Dynamic Layer-Aware Token Attention for Efficient
+ *           Long-Context Reasoning": key design 2 (max over heads; page sum;
+ *           recency pages), key design 3 (P = 16).
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvs_status;
+#define KVS_OK 0
+#define KVS_EINVAL (-1)
+#define KVS_EUNSUPPORTED (-2)
+#define KVS_EWORKSPACE (-3)
+#define KVS_EHIP (-4)
+
+/* Head reduction of the score: per query head, or over the G = H_q / H_kv
+ * query heads that share a KV head. */
+#define KVS_HEADS_NONE 0      /* output rows: H_q                         */
+#define KVS_HEADS_GROUP_SUM 1 /* output rows: H_kv, sum over the G heads  */
+#define KVS_HEADS_GROUP_MAX 2 /* output rows: H_kv, max over the G heads  */
+
+/* Reductions used by pooling, paging and layer aggregation. */
+#define KVS_RED_NONE 0
+#define KVS_RED_SUM 1
+#define KVS_RED_MAX 2
+#define KVS_RED_MEAN 3
+#define KVS_RED_SUM_L1 4
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kvs_status_string(kvs_status s);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t kvs_version(void);
+
+/* ------------------------------------------------------------------------
+ * kvs_score - window-attention column scores.
+ *
+ * [ClusterAttn] feature aggregation and [CLAA] FastKV / per-layer window
+ * score: for every query head h (KV head g = h / G, contiguous grouping) and
+ * window row j at absolute position q_pos0 + j,
+ *     s[h][j][t] = scale * sum_c Q[h][j][c] * K[g][t][c]     for t <= q_pos0 + j,
+ *     a[h][j][t] = softmax over the visible t of s[h][j][.] (masked t -> 0),
+ *     c_h[t]     = sum_j a[h][j][t],
+ * and the output row is c_h (NONE), sum over the G heads of group g
+ * (GROUP_SUM), or the max over those heads ([DELTA] key design 2, GROUP_MAX).
+ * Every one of the L columns is produced, so each GROUP_SUM row sums to W*G.
+ * With q_pos0 >= L - 1 every row sees all L keys (lookahead / decode queries).
+ *
+ * Q: bf16, element [h][j][c] at Q + h*q_head_stride + j*q_row_stride + c.
+ * K: bf16, element [g][t][c] at K + g*k_head_stride + t*k_tok_stride + c.
+ *    KV-head-major [H_kv][L][d_k] is the default; sequence-major [L][H_kv][d_k]
+ *    is k_head_stride = d_k, k_tok_stride = H_kv * d_k.
+ * S: float32, element [row][t] at S + row*s_ld + t; written (accumulate = 0)
+ *    or added to (accumulate = 1).
+ * Strides are in elements; 0 selects the contiguous default (W*d_k, d_k,
+ * L*d_k, d_k, L).  Q/K pointers and strides must be 16-byte aligned.
+ * Limits: d_k in {64, 128}; W*G <= 128 after padding each head's rows to
+ * 4, 8, 16 or a multiple of 32; otherwise KVS_EUNSUPPORTED.
+ * The workspace holds per-split softmax statistics; its size depends only on
+ * the shape.  The result is bit-identical from run to run.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t L, W, d_k, H_q, H_kv;
+  int32_t heads;      /* KVS_HEADS_*                                        */
+  int64_t q_pos0;     /* absolute position of window row 0, >= 0           */
+  int64_t q_head_stride, q_row_stride;
+  int64_t k_head_stride, k_tok_stride;
+  int64_t s_ld;       /* row stride of S in floats, >= L                    */
+  float scale;        /* logit scale, 0 => 1/sqrt(d_k); must be >= 0       */
+  int32_t accumulate; /* 0: S = score, 1: S += score                        */
+} kvs_score_args;
+
+size_t kvs_score_workspace(const kvs_score_args* a);
+kvs_status kvs_score(const kvs_score_args* a, const void* Q, const void* K, float* S,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_pool_pages - head reduction, 1-D pooling, page aggregation.
+ *
+ * Input S float32 [H][n] with row stride ld (>= n).  In this order:
+ *  1. head_reduce NONE keeps the H rows; SUM / MAX folds them into one row
+ *     ([DELTA] key design 2: max over heads).  H' = 1 or H rows remain.
+ *  2. pool NONE / MAX / MEAN over [t - r, t + r] clipped to [0, n),
+ *     r = (pool_k - 1) / 2, pool_k odd; MEAN divides by the in-range count
+ *     ([CLAA] 1-D pooling, kernel 7).
+ *  3. if P > 0: page u covers tokens [u*P, min(u*P + P, n)); page_reduce
+ *     SUM or MAX ([DELTA] page score; [ClusterAttn] block max) and page_arg =
+ *     lowest index attaining the page maximum.
+ * Outputs (contiguous, float32 / int32): pooled [H'][n] (may be NULL when
+ * P > 0), page [H'][ceil(n/P)] and page_arg [H'][ceil(n/P)] (each may be
+ * NULL).  Sums are taken left to right in float32.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
+                          int32_t head_reduce, int32_t pool, int32_t pool_k,
+                          int32_t P, int32_t page_reduce,
+                          float* pooled, float* page, int32_t* page_arg, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_topk - per-row top-`budget` selection with a forced suffix.
+ *
+ * [CLAA] topk(scores, keep_rate) over candidates [0, n) of each of the H rows
+ * of S (row stride ld >= n).  Order: priority descending (when `priority`,
+ * uint8 [H][n] contiguous, is given; nonzero = 1), value descending, index
+ * ascending: ties go to the lower index.  -0.0 ranks equal to +0.0; NaN ranks
+ * below every number.  The output row idx[h][0 .. budget + n_forced) lists the
+ * chosen indices in ascending order (original positions preserved), followed
+ * by n, n+1, ..., n + n_forced - 1 ([ClusterAttn] window appended; [DELTA]
+ * recency pages).  The result is unique for a given input.
+ * 0 <= budget <= n.  Workspace from kvs_topk_workspace().
+ * ---------------------------------------------------------------------- */
+size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget);
+kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
+                    const uint8_t* priority, int32_t n_forced, int32_t* idx,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_block_union_pagetable - per-group KV page table from a 2-D block mask.
+ *
+ * [CompactAttention] M uint8 [H_q][n_qb][n_kvb] (nonzero = selected).
+ * Q-block union  Mb[h][j] = OR_i M[h][i][j];  intra-group union over the
+ * sub_group consecutive query heads of subgroup s (inside one KV group;
+ * sub_group = 0 selects G = H_q / H_kv):  Gs[s][j] = OR_h Mb[h][j].
+ * T_s = { j : Gs[s][j] } ascending.  n_groups = H_q / sub_group.
+ * kv_indptr int32 [n_groups + 1] = exclusive prefix sum of |T_s|;
+ * kv_indices int32 [capacity >= n_groups * n_kvb] holds T_0, T_1, ... packed.
+ * The table is the smallest one covering every selected block.
+ * ---------------------------------------------------------------------- */
+size_t kvs_block_union_workspace(int32_t H_q, int32_t H_kv, int32_t sub_group, int32_t n_kvb);
+kvs_status kvs_block_union_pagetable(const uint8_t* M, int32_t H_q, int32_t H_kv, int32_t sub_group,
+                                     int32_t n_qb, int32_t n_kvb, int32_t* kv_indptr,
+                                     int32_t* kv_indices, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_aggregate_layers - fold one layer's scores into a cross-layer total.
+ *
+ * s[t] = sum over the H rows of S[h][t] (row stride ld >= n), then
+ *   SUM_L1: acc[t] (=|+=) s[t] / sum_t' |s[t']|  ([LookaheadKV] L1 norm),
+ *   MAX:    acc[t] = max(acc[t], s[t])           ([CLAA] Eq. 6).
+ * first_layer = 1 overwrites acc (float32 [n]) instead of combining.
+ * The L1 norm is accumulated in float64 in a fixed order.
+ * ---------------------------------------------------------------------- */
+size_t kvs_aggregate_workspace(int32_t n);
+kvs_status kvs_aggregate_layers(float* acc, const float* S, int32_t H, int32_t n, int64_t ld,
+                                int32_t mode, int32_t first_layer, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_cluster_priority - density-clustering priority mask.
+ *
+ * [ClusterAttn] method details: centres are the block-level max indices
+ * page_arg[h][u] whose block maximum page[h][u] >= theta; every token within
+ * r of a centre (|t - c| <= r, t in [0, n)) gets priority[h][t] = 1, else 0.
+ * page / page_arg [H][n_pages] come from kvs_pool_pages with page size P.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_cluster_priority(const float* page, const int32_t* page_arg, int32_t H,
+                                int32_t n_pages, int32_t P, int32_t n, float theta, int32_t r,
+                                uint8_t* priority, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_block_select - block mask of a prefill chunk from mean-pooled logits.
+ *
+ * Chunk queries Qc bf16 [H_q][Lq][d_k] at positions q_pos0 .. q_pos0 + Lq - 1
+ * against keys K bf16 [H_kv][L][d_k] (strides as in kvs_score).  Kb = mean of
+ * each `block` keys, Qb = mean of each `block` chunk rows (last blocks may be
+ * partial); query block i sees KV block j when j*block <= its last position.
+ * Logits scale * Qb . Kb, softmax over the visible blocks, blocks ordered by
+ * (probability desc, j asc); M[h][i][j] = 1 while the mass ranked strictly
+ * before block j is < p_mass.  Output M uint8 [H_q][n_qb][n_kvb].
+ * Stands in for the pages' learned / threshold selectors ([CompactAttention]
+ * step 1) with a training-free top-p rule.  n_kvb <= 4096.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t Lq, L, d_k, H_q, H_kv, block;
+  int64_t q_pos0;
+  int64_t q_head_stride, q_row_stride;
+  int64_t k_head_stride, k_tok_stride;
+  float scale;  /* 0 => 1/sqrt(d_k) */
+  float p_mass; /* in (0, 1]          */
+} kvs_block_select_args;
+
+size_t kvs_block_select_workspace(const kvs_block_select_args* a);
+kvs_status kvs_block_select(const kvs_block_select_args* a, const void* Qc, const void* K,
+                            uint8_t* M, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

@@ -1,0 +1,246 @@
+"""Python binding of libkvs (attention-based prompt-token importance on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libkvs.so``; this module passes device pointers, sizes and the current HIP
+stream through the C ABI declared in ``include/kvs.h`` and allocates output and
+workspace tensors with PyTorch when the caller does not pass them.  There is no
+CPU fallback: importing fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loaded first so libkvs binds to the same HIP runtime as torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvs.so")
+
+KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EWORKSPACE, KVS_EHIP = 0, -1, -2, -3, -4
+HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX = 0, 1, 2
+RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_lib.kvs_status_string(status).decode()} ({status})")
+        self.status = status
+
+
+class ScoreArgs(ctypes.Structure):
+    _fields_ = [
+        ("L", ctypes.c_int32), ("W", ctypes.c_int32), ("d_k", ctypes.c_int32),
+        ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
+        ("s_ld", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("accumulate", ctypes.c_int32),
+    ]
+
+
+class BlockSelectArgs(ctypes.Structure):
+    _fields_ = [
+        ("Lq", ctypes.c_int32), ("L", ctypes.c_int32), ("d_k", ctypes.c_int32),
+        ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("block", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("p_mass", ctypes.c_float),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m prompt_token_importance_amd.build`"
+            " (hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "kvs_status_string": (ctypes.c_char_p, [I32]),
+        "kvs_version": (I32, []),
+        "kvs_score_workspace": (SZ, [ctypes.POINTER(ScoreArgs)]),
+        "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
+        "kvs_topk_workspace": (SZ, [I32, I32, I32]),
+        "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, SZ, P]),
+        "kvs_block_union_workspace": (SZ, [I32, I32, I32, I32]),
+        "kvs_block_union_pagetable": (I32, [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "kvs_aggregate_workspace": (SZ, [I32]),
+        "kvs_aggregate_layers": (I32, [P, P, I32, I32, I64, I32, I32, P, SZ, P]),
+        "kvs_cluster_priority": (I32, [P, P, I32, I32, I32, I32, F32, I32, P, P]),
+        "kvs_block_select_workspace": (SZ, [ctypes.POINTER(BlockSelectArgs)]),
+        "kvs_block_select": (I32, [ctypes.POINTER(BlockSelectArgs), P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = (
+    "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_pool_pages",
+    "kvs_topk_workspace", "kvs_topk", "kvs_block_union_workspace", "kvs_block_union_pagetable",
+    "kvs_aggregate_workspace", "kvs_aggregate_layers", "kvs_cluster_priority",
+    "kvs_block_select_workspace", "kvs_block_select",
+)
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(st: int, what: str):
+    if st != KVS_OK:
+        raise KvsError(st, what)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def bf16_from_bits(bits, device="cuda") -> torch.Tensor:
+    """uint16 bfloat16 bit patterns (NumPy) -> torch.bfloat16 tensor on device."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+# --------------------------------------------------------------------------- score
+def score_args(*, L, W, d_k, H_q, H_kv, q_pos0, heads=HEADS_GROUP_SUM, scale=0.0, accumulate=False,
+               q_head_stride=0, q_row_stride=0, k_head_stride=0, k_tok_stride=0, s_ld=0) -> ScoreArgs:
+    return ScoreArgs(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, heads=heads, q_pos0=q_pos0,
+                     q_head_stride=q_head_stride, q_row_stride=q_row_stride,
+                     k_head_stride=k_head_stride, k_tok_stride=k_tok_stride, s_ld=s_ld,
+                     scale=scale, accumulate=int(bool(accumulate)))
+
+
+def kvs_score_workspace(args: ScoreArgs) -> int:
+    return int(_lib.kvs_score_workspace(ctypes.byref(args)))
+
+
+def kvs_score(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs, S: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Window column scores; S float32 [H_kv or H_q][s_ld] (allocated if None)."""
+    rows = args.H_q if args.heads == HEADS_NONE else args.H_kv
+    if S is None:
+        S = torch.empty(rows, args.s_ld or args.L, dtype=torch.float32, device=K.device)
+    ws, nb = _workspace(kvs_score_workspace(args), K.device, ws)
+    _check(_lib.kvs_score(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _ptr(ws), nb,
+                          _stream(stream)), "kvs_score")
+    return S
+
+
+# --------------------------------------------------------------------------- pool / pages
+def kvs_pool_pages(S: torch.Tensor, n: int, *, head_reduce=RED_NONE, pool=RED_NONE, pool_k=7, P=0,
+                   page_reduce=RED_SUM, ld: Optional[int] = None, want_pooled=True, stream=None):
+    """Returns (pooled or None, page or None, page_arg or None)."""
+    H = S.shape[0]
+    ld = S.stride(0) if ld is None else ld
+    rows = H if head_reduce == RED_NONE else 1
+    pooled = torch.empty(rows, n, dtype=torch.float32, device=S.device) if (want_pooled or P == 0) else None
+    page = arg = None
+    if P > 0:
+        n_pages = (n + P - 1) // P
+        page = torch.empty(rows, n_pages, dtype=torch.float32, device=S.device)
+        arg = torch.empty(rows, n_pages, dtype=torch.int32, device=S.device)
+    _check(_lib.kvs_pool_pages(_ptr(S), H, n, ld, head_reduce, pool, pool_k, P, page_reduce,
+                               _ptr(pooled), _ptr(page), _ptr(arg), _stream(stream)), "kvs_pool_pages")
+    return pooled, page, arg
+
+
+# --------------------------------------------------------------------------- top-k
+def kvs_topk(S: torch.Tensor, n: int, budget: int, *, priority: Optional[torch.Tensor] = None,
+             n_forced: int = 0, ld: Optional[int] = None, idx: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    H = S.shape[0]
+    ld = S.stride(0) if ld is None else ld
+    if idx is None:
+        idx = torch.empty(H, budget + n_forced, dtype=torch.int32, device=S.device)
+    ws, nb = _workspace(int(_lib.kvs_topk_workspace(H, n, budget)), S.device, ws)
+    _check(_lib.kvs_topk(_ptr(S), H, n, ld, budget, _ptr(priority), n_forced, _ptr(idx), _ptr(ws),
+                         nb, _stream(stream)), "kvs_topk")
+    return idx
+
+
+# --------------------------------------------------------------------------- union
+def kvs_block_union_pagetable(M: torch.Tensor, H_q: int, H_kv: int, sub_group: int = 0,
+                              ws: Optional[torch.Tensor] = None, stream=None):
+    """M uint8 [H_q][n_qb][n_kvb] -> (kv_indptr int32 [n_groups+1], kv_indices int32 [cap])."""
+    _, n_qb, n_kvb = M.shape
+    sg = (H_q // H_kv) if sub_group == 0 else sub_group
+    n_groups = H_q // sg
+    indptr = torch.empty(n_groups + 1, dtype=torch.int32, device=M.device)
+    indices = torch.empty(n_groups * n_kvb, dtype=torch.int32, device=M.device)
+    ws, nb = _workspace(int(_lib.kvs_block_union_workspace(H_q, H_kv, sub_group, n_kvb)), M.device, ws)
+    _check(_lib.kvs_block_union_pagetable(_ptr(M), H_q, H_kv, sub_group, n_qb, n_kvb, _ptr(indptr),
+                                          _ptr(indices), _ptr(ws), nb, _stream(stream)),
+           "kvs_block_union_pagetable")
+    return indptr, indices
+
+
+# --------------------------------------------------------------------------- layers
+def kvs_aggregate_layers(acc: torch.Tensor, S: torch.Tensor, n: int, mode: int, first_layer: bool,
+                         ld: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    H = S.shape[0]
+    ld = S.stride(0) if ld is None else ld
+    ws, nb = _workspace(int(_lib.kvs_aggregate_workspace(n)), S.device, ws)
+    _check(_lib.kvs_aggregate_layers(_ptr(acc), _ptr(S), H, n, ld, mode, int(bool(first_layer)),
+                                     _ptr(ws), nb, _stream(stream)), "kvs_aggregate_layers")
+    return acc
+
+
+# --------------------------------------------------------------------------- clusters
+def kvs_cluster_priority(page: torch.Tensor, page_arg: torch.Tensor, P: int, n: int, theta: float,
+                         r: int, priority: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    H, n_pages = page.shape
+    if priority is None:
+        priority = torch.empty(H, n, dtype=torch.uint8, device=page.device)
+    _check(_lib.kvs_cluster_priority(_ptr(page), _ptr(page_arg), H, n_pages, P, n, theta, r,
+                                     _ptr(priority), _stream(stream)), "kvs_cluster_priority")
+    return priority
+
+
+# --------------------------------------------------------------------------- block select
+def block_select_args(*, Lq, L, d_k, H_q, H_kv, q_pos0, block=64, p_mass=0.9, scale=0.0,
+                      q_head_stride=0, q_row_stride=0, k_head_stride=0, k_tok_stride=0) -> BlockSelectArgs:
+    return BlockSelectArgs(Lq=Lq, L=L, d_k=d_k, H_q=H_q, H_kv=H_kv, block=block, q_pos0=q_pos0,
+                           q_head_stride=q_head_stride, q_row_stride=q_row_stride,
+                           k_head_stride=k_head_stride, k_tok_stride=k_tok_stride,
+                           scale=scale, p_mass=p_mass)
+
+
+def kvs_block_select_workspace(args: BlockSelectArgs) -> int:
+    return int(_lib.kvs_block_select_workspace(ctypes.byref(args)))
+
+
+def kvs_block_select(Qc: torch.Tensor, K: torch.Tensor, args: BlockSelectArgs,
+                     M: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    n_qb = (args.Lq + args.block - 1) // args.block
+    n_kvb = (args.L + args.block - 1) // args.block
+    if M is None:
+        M = torch.empty(args.H_q, n_qb, n_kvb, dtype=torch.uint8, device=K.device)
+    ws, nb = _workspace(kvs_block_select_workspace(args), K.device, ws)
+    _check(_lib.kvs_block_select(ctypes.byref(args), _ptr(Qc), _ptr(K), _ptr(M), _ptr(ws), nb,
+                                 _stream(stream)), "kvs_block_select")
+    return M

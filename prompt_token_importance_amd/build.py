@@ -1,0 +1,47 @@
+"""Build libkvs.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree.
+
+Usage: python -m prompt_token_importance_amd.build   (or call build()).
+"""
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libkvs.so")
+ARCH = os.environ.get("KVS_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    # Never emit packed fp32 VALU ops (v_pk_*_f32).
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    lines = [l for l in (res.stdout + res.stderr).splitlines()
+             if "packed-fp32-ops" not in l]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(lines) + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    if verbose and lines:
+        print("\n".join(lines))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,230 @@
+// C ABI of libkvs: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before any kernel is enqueued; no call
+// allocates, frees or synchronizes.
+#include <math.h>
+
+#include "kvs_internal.h"
+
+using namespace kvs;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool mult8(int64_t x) { return (x & 7) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Fills defaults and validates everything but pointers.
+kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
+  if (!in) return KVS_EINVAL;
+  *a = *in;
+  if (a->L < 1 || a->W < 1 || a->H_q < 1 || a->H_kv < 1 || a->d_k < 1) return KVS_EINVAL;
+  if (a->H_q % a->H_kv) return KVS_EINVAL;
+  if (a->q_pos0 < 0) return KVS_EINVAL;
+  if (a->heads < KVS_HEADS_NONE || a->heads > KVS_HEADS_GROUP_MAX) return KVS_EINVAL;
+  if (a->accumulate != 0 && a->accumulate != 1) return KVS_EINVAL;
+  if (!(a->scale >= 0.f) || isinf(a->scale)) return KVS_EINVAL;
+  if (a->L > (1 << 30)) return KVS_EUNSUPPORTED;
+  if (a->d_k != 64 && a->d_k != 128) return KVS_EUNSUPPORTED;
+  if (a->q_head_stride == 0) a->q_head_stride = (int64_t)a->W * a->d_k;
+  if (a->q_row_stride == 0) a->q_row_stride = a->d_k;
+  if (a->k_head_stride == 0) a->k_head_stride = (int64_t)a->L * a->d_k;
+  if (a->k_tok_stride == 0) a->k_tok_stride = a->d_k;
+  if (a->s_ld == 0) a->s_ld = a->L;
+  if (a->q_head_stride < 0 || a->q_row_stride < 0 || a->k_head_stride < 0 || a->k_tok_stride < 0)
+    return KVS_EINVAL;
+  if (!mult8(a->q_head_stride) || !mult8(a->q_row_stride) || !mult8(a->k_head_stride) ||
+      !mult8(a->k_tok_stride))
+    return KVS_EINVAL;
+  if (a->s_ld < a->L) return KVS_EINVAL;
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvs_status_string(kvs_status s) {
+  switch (s) {
+    case KVS_OK: return "KVS_OK";
+    case KVS_EINVAL: return "KVS_EINVAL: invalid argument";
+    case KVS_EUNSUPPORTED: return "KVS_EUNSUPPORTED: shape not supported by this build";
+    case KVS_EWORKSPACE: return "KVS_EWORKSPACE: workspace too small";
+    case KVS_EHIP: return "KVS_EHIP: kernel launch failed";
+    default: return "KVS: unknown status";
+  }
+}
+
+int32_t kvs_version(void) { return 100; }
+
+size_t kvs_score_workspace(const kvs_score_args* in) {
+  kvs_score_args a;
+  if (check_score(in, &a) != KVS_OK) return 0;
+  ScorePlan pl;
+  if (score_plan(&a, &pl) != KVS_OK) return 0;
+  return pl.ws_total;
+}
+
+kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, float* S, void* ws,
+                     size_t ws_bytes, void* stream) {
+  kvs_score_args a;
+  kvs_status st = check_score(in, &a);
+  if (st != KVS_OK) return st;
+  if (!Q || !K || !S) return KVS_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || ((uintptr_t)S & 3u)) return KVS_EINVAL;
+  ScorePlan pl;
+  st = score_plan(&a, &pl);
+  if (st != KVS_OK) return st;
+  if (!ws || ws_bytes < pl.ws_total) return KVS_EWORKSPACE;
+  if (!aligned16(ws)) return KVS_EINVAL;
+  ScoreLaunch p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.S = S;
+  p.stats = static_cast<float2*>(ws);
+  p.rowc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_stats);
+  p.qhs = a.q_head_stride;
+  p.qrs = a.q_row_stride;
+  p.khs = a.k_head_stride;
+  p.kts = a.k_tok_stride;
+  p.s_ld = a.s_ld;
+  p.q_pos0 = a.q_pos0;
+  p.L = a.L;
+  p.W = a.W;
+  p.G = a.H_q / a.H_kv;
+  p.H_kv = a.H_kv;
+  p.d_k = a.d_k;
+  p.heads = a.heads;
+  p.accumulate = a.accumulate;
+  const double scale = a.scale > 0.f ? (double)a.scale : 1.0 / sqrt((double)a.d_k);
+  p.c = (float)(scale * 1.4426950408889634073599246810018921);  // scale * log2(e)
+  return score_run(pl, p, as_stream(stream));
+}
+
+kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld, int32_t head_reduce,
+                          int32_t pool, int32_t pool_k, int32_t P, int32_t page_reduce,
+                          float* pooled, float* page, int32_t* page_arg, void* stream) {
+  if (!S || H < 1 || n < 1 || ld < n) return KVS_EINVAL;
+  if (head_reduce != KVS_RED_NONE && head_reduce != KVS_RED_SUM && head_reduce != KVS_RED_MAX)
+    return KVS_EINVAL;
+  if (pool != KVS_RED_NONE && pool != KVS_RED_MAX && pool != KVS_RED_MEAN) return KVS_EINVAL;
+  if (pool != KVS_RED_NONE && (pool_k < 1 || (pool_k & 1) == 0)) return KVS_EINVAL;
+  if (pool != KVS_RED_NONE && pool_k > 129) return KVS_EUNSUPPORTED;
+  if (P < 0) return KVS_EINVAL;
+  if (P > 0 && page_reduce != KVS_RED_SUM && page_reduce != KVS_RED_MAX) return KVS_EINVAL;
+  if (P > 2048) return KVS_EUNSUPPORTED;
+  if (P == 0 && !pooled) return KVS_EINVAL;
+  if (P > 0 && !pooled && !page && !page_arg) return KVS_EINVAL;
+  if (((uintptr_t)S & 3u) || ((uintptr_t)pooled & 3u) || ((uintptr_t)page & 3u) ||
+      ((uintptr_t)page_arg & 3u))
+    return KVS_EINVAL;
+  return pool_pages_run(S, H, n, ld, head_reduce, pool, pool_k, P, page_reduce, pooled, page,
+                        page_arg, as_stream(stream));
+}
+
+size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget) {
+  if (H < 0 || n < 1 || budget < 0 || budget > n) return 0;
+  return topk_ws_bytes(H, n, budget);
+}
+
+kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
+                    const uint8_t* priority, int32_t n_forced, int32_t* idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!S || !idx || H < 0 || n < 1 || ld < n) return KVS_EINVAL;
+  if (budget < 0 || budget > n || n_forced < 0) return KVS_EINVAL;
+  if ((int64_t)n + n_forced > 0x7fffffff) return KVS_EINVAL;
+  if (((uintptr_t)S & 3u) || ((uintptr_t)idx & 3u)) return KVS_EINVAL;
+  const size_t need = topk_ws_bytes(H, n, budget);
+  if (need && (!ws || ws_bytes < need)) return KVS_EWORKSPACE;
+  return topk_run(S, H, n, ld, budget, priority, n_forced, idx, ws, as_stream(stream));
+}
+
+size_t kvs_block_union_workspace(int32_t H_q, int32_t H_kv, int32_t sub_group, int32_t n_kvb) {
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv || n_kvb < 1 || sub_group < 0) return 0;
+  const int G = H_q / H_kv;
+  if (sub_group && G % sub_group) return 0;
+  return union_ws_bytes(H_q, H_kv, sub_group, n_kvb);
+}
+
+kvs_status kvs_block_union_pagetable(const uint8_t* M, int32_t H_q, int32_t H_kv, int32_t sub_group,
+                                     int32_t n_qb, int32_t n_kvb, int32_t* kv_indptr,
+                                     int32_t* kv_indices, void* ws, size_t ws_bytes, void* stream) {
+  if (!M || !kv_indptr || !kv_indices) return KVS_EINVAL;
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv || n_qb < 1 || n_kvb < 1 || sub_group < 0) return KVS_EINVAL;
+  const int G = H_q / H_kv;
+  if (sub_group && G % sub_group) return KVS_EINVAL;
+  if (((uintptr_t)kv_indptr & 3u) || ((uintptr_t)kv_indices & 3u)) return KVS_EINVAL;
+  const size_t need = union_ws_bytes(H_q, H_kv, sub_group, n_kvb);
+  if (!ws || ws_bytes < need) return KVS_EWORKSPACE;
+  if (!aligned16(ws)) return KVS_EINVAL;
+  return union_run(M, H_q, H_kv, sub_group, n_qb, n_kvb, kv_indptr, kv_indices, ws,
+                   as_stream(stream));
+}
+
+size_t kvs_aggregate_workspace(int32_t n) {
+  if (n < 1) return 0;
+  return aggregate_ws_bytes(n);
+}
+
+kvs_status kvs_aggregate_layers(float* acc, const float* S, int32_t H, int32_t n, int64_t ld,
+                                int32_t mode, int32_t first_layer, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!acc || !S || H < 1 || n < 1 || ld < n) return KVS_EINVAL;
+  if (mode != KVS_RED_SUM_L1 && mode != KVS_RED_MAX) return KVS_EINVAL;
+  if (first_layer != 0 && first_layer != 1) return KVS_EINVAL;
+  if (((uintptr_t)acc & 3u) || ((uintptr_t)S & 3u)) return KVS_EINVAL;
+  if (mode == KVS_RED_SUM_L1) {
+    const size_t need = aggregate_ws_bytes(n);
+    if (!ws || ws_bytes < need) return KVS_EWORKSPACE;
+    if (((uintptr_t)ws & 7u)) return KVS_EINVAL;
+  }
+  return aggregate_run(acc, S, H, n, ld, mode, first_layer, ws, as_stream(stream));
+}
+
+kvs_status kvs_cluster_priority(const float* page, const int32_t* page_arg, int32_t H,
+                                int32_t n_pages, int32_t P, int32_t n, float theta, int32_t r,
+                                uint8_t* priority, void* stream) {
+  if (!page || !page_arg || !priority) return KVS_EINVAL;
+  if (H < 1 || n < 1 || P < 1 || r < 0 || n_pages != (n + P - 1) / P) return KVS_EINVAL;
+  if (isnan(theta)) return KVS_EINVAL;
+  return cluster_priority_run(page, page_arg, H, n_pages, P, n, theta, r, priority,
+                              as_stream(stream));
+}
+
+size_t kvs_block_select_workspace(const kvs_block_select_args* a) {
+  if (!a || a->Lq < 1 || a->L < 1 || a->block < 1 || a->H_q < 1 || a->H_kv < 1 ||
+      a->H_q % a->H_kv || (a->d_k != 64 && a->d_k != 128))
+    return 0;
+  BlockPlan pl;
+  if (block_plan(a, &pl) != KVS_OK) return 0;
+  return pl.ws_total;
+}
+
+kvs_status kvs_block_select(const kvs_block_select_args* in, const void* Qc, const void* K,
+                            uint8_t* M, void* ws, size_t ws_bytes, void* stream) {
+  if (!in || !Qc || !K || !M) return KVS_EINVAL;
+  kvs_block_select_args a = *in;
+  if (a.Lq < 1 || a.L < 1 || a.block < 1 || a.H_q < 1 || a.H_kv < 1 || a.d_k < 1) return KVS_EINVAL;
+  if (a.H_q % a.H_kv || a.q_pos0 < 0) return KVS_EINVAL;
+  if (a.q_pos0 + a.Lq > a.L) return KVS_EINVAL;  // the chunk's own keys are part of K
+  if (!(a.p_mass > 0.f) || a.p_mass > 1.f) return KVS_EINVAL;
+  if (!(a.scale >= 0.f) || isinf(a.scale)) return KVS_EINVAL;
+  if (a.d_k != 64 && a.d_k != 128) return KVS_EUNSUPPORTED;
+  if (a.q_head_stride == 0) a.q_head_stride = (int64_t)a.Lq * a.d_k;
+  if (a.q_row_stride == 0) a.q_row_stride = a.d_k;
+  if (a.k_head_stride == 0) a.k_head_stride = (int64_t)a.L * a.d_k;
+  if (a.k_tok_stride == 0) a.k_tok_stride = a.d_k;
+  if (!mult8(a.q_head_stride) || !mult8(a.q_row_stride) || !mult8(a.k_head_stride) ||
+      !mult8(a.k_tok_stride) || a.q_head_stride < 0 || a.q_row_stride < 0 || a.k_head_stride < 0 ||
+      a.k_tok_stride < 0)
+    return KVS_EINVAL;
+  if (!aligned16(Qc) || !aligned16(K)) return KVS_EINVAL;
+  BlockPlan pl;
+  kvs_status st = block_plan(&a, &pl);
+  if (st != KVS_OK) return st;
+  if (!ws || ws_bytes < pl.ws_total) return KVS_EWORKSPACE;
+  if (!aligned16(ws)) return KVS_EINVAL;
+  return block_select_run(&a, pl, static_cast<const uint16_t*>(Qc),
+                          static_cast<const uint16_t*>(K), M, ws, as_stream(stream));
+}
+
+}  // extern "C"

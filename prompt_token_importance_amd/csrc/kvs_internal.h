@@ -1,0 +1,77 @@
+// Internal declarations shared by the host-side API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+
+namespace kvs {
+
+constexpr size_t kWsAlign = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- score
+// Rows of one KV group: the W window rows of each of the G query heads are
+// padded to `head_rows` (4, 8, 16 or a multiple of 32) and the group to a
+// multiple of 32 rows (`rows_pad`); padding rows are masked out.
+struct ScorePlan {
+  int head_rows;
+  int rows_pad;     // multiple of 32, <= 128
+  int n_tiles;      // ceil(L / 32)
+  int n_split;      // splits of the key range per KV head
+  int tiles_per_split;
+  int head_batch;   // KV heads per (pass 1, merge, pass 2) round
+  size_t ws_stats;  // bytes of per-split (max, sum) pairs
+  size_t ws_rowc;   // bytes of per-row softmax constants
+  size_t ws_total;
+};
+
+struct ScoreLaunch {
+  const uint16_t* Q;
+  const uint16_t* K;
+  float* S;
+  float2* stats;  // [H_kv][n_split][rows_pad]
+  float* rowc;    // [H_kv][rows_pad]
+  int64_t qhs, qrs, khs, kts, s_ld;
+  int64_t q_pos0;
+  int L, W, G, H_kv, d_k, heads, accumulate;
+  float c;        // scale * log2(e)
+};
+
+kvs_status score_plan(const kvs_score_args* a, ScorePlan* plan);
+kvs_status score_run(const ScorePlan& plan, const ScoreLaunch& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- others
+kvs_status pool_pages_run(const float* S, int H, int n, int64_t ld, int head_reduce, int pool,
+                          int pool_k, int P, int page_reduce, float* pooled, float* page,
+                          int32_t* page_arg, hipStream_t stream);
+
+kvs_status cluster_priority_run(const float* page, const int32_t* page_arg, int H, int n_pages,
+                                int P, int n, float theta, int r, uint8_t* prio,
+                                hipStream_t stream);
+
+size_t aggregate_ws_bytes(int n);
+kvs_status aggregate_run(float* acc, const float* S, int H, int n, int64_t ld, int mode, int first,
+                         void* ws, hipStream_t stream);
+
+size_t topk_ws_bytes(int H, int n, int budget);
+kvs_status topk_run(const float* S, int H, int n, int64_t ld, int budget, const uint8_t* prio,
+                    int n_forced, int32_t* idx, void* ws, hipStream_t stream);
+
+size_t union_ws_bytes(int H_q, int H_kv, int sub_group, int n_kvb);
+kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_qb, int n_kvb,
+                     int32_t* indptr, int32_t* indices, void* ws, hipStream_t stream);
+
+struct BlockPlan {
+  int n_qb, n_kvb, sort_n;
+  size_t ws_kb, ws_qb, ws_total;
+};
+kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* plan);
+kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& plan,
+                            const uint16_t* Qc, const uint16_t* K, uint8_t* M, void* ws,
+                            hipStream_t stream);
+
+}  // namespace kvs

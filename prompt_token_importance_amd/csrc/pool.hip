@@ -1,0 +1,208 @@
+// Post-processing of token scores on gfx950: head reduction, 1-D pooling and
+// page aggregation (kvs_pool_pages), density-clustering priority
+// (kvs_cluster_priority) and cross-layer aggregation (kvs_aggregate_layers).
+//
+// These steps move a few bytes per token, so they are bound by HBM / L2
+// bandwidth: each workgroup stages a chunk of the head-reduced row plus the
+// pooling halo in LDS once, then pools and pages from LDS.  Every sum runs
+// left to right in float32 so the result does not depend on the launch shape.
+#include <math.h>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kChunk = 2048;   // tokens per workgroup (multiple of every page size used)
+constexpr int kThreads = 256;
+constexpr int kMaxHalo = 64;   // pool_k <= 129
+constexpr float kNegInf = -__builtin_inff();
+
+// Row h' of the head-reduced input at token t (caller guarantees 0 <= t < n).
+__device__ __forceinline__ float reduced(const float* S, int H, int64_t ld, int head_reduce,
+                                         int row, int t) {
+  if (head_reduce == KVS_RED_NONE) return S[(int64_t)row * ld + t];
+  float v = S[t];
+  for (int h = 1; h < H; ++h) {
+    const float x = S[(int64_t)h * ld + t];
+    v = head_reduce == KVS_RED_SUM ? v + x : fmaxf(v, x);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void pool_pages_kernel(
+    const float* __restrict__ S, int H, int n, int64_t ld, int head_reduce, int pool, int pool_k,
+    int P, int page_reduce, int chunk, float* __restrict__ pooled, float* __restrict__ page,
+    int32_t* __restrict__ page_arg) {
+  __shared__ float xs[kChunk + 2 * kMaxHalo];
+  __shared__ float ys[kChunk];
+  const int row = blockIdx.y;
+  const int c0 = blockIdx.x * chunk;
+  const int c1 = min(c0 + chunk, n);
+  const int r = pool == KVS_RED_NONE ? 0 : (pool_k - 1) / 2;
+  // 1. head-reduced values for [c0 - r, c1 + r) clipped to [0, n)
+  for (int i = threadIdx.x; i < (c1 - c0) + 2 * r; i += kThreads) {
+    const int t = c0 - r + i;
+    xs[i] = (t >= 0 && t < n) ? reduced(S, H, ld, head_reduce, row, t) : 0.f;
+  }
+  __syncthreads();
+  // 2. pooling over the clipped window, left to right
+  for (int i = threadIdx.x; i < c1 - c0; i += kThreads) {
+    const int t = c0 + i;
+    float y;
+    if (pool == KVS_RED_NONE) {
+      y = xs[i];
+    } else {
+      const int lo = max(t - r, 0), hi = min(t + r, n - 1);
+      if (pool == KVS_RED_MAX) {
+        y = kNegInf;
+        for (int u = lo; u <= hi; ++u) y = fmaxf(y, xs[u - c0 + r]);
+      } else {
+        float s = 0.f;
+        for (int u = lo; u <= hi; ++u) s += xs[u - c0 + r];
+        y = s / (float)(hi - lo + 1);
+      }
+    }
+    ys[i] = y;
+    if (pooled) pooled[(int64_t)row * n + t] = y;
+  }
+  if (P <= 0) return;
+  __syncthreads();
+  // 3. pages: chunk boundaries are multiples of P
+  const int n_pages = (n + P - 1) / P;
+  const int u0 = c0 / P;
+  const int u1 = (c1 + P - 1) / P;
+  for (int u = u0 + threadIdx.x; u < u1; u += kThreads) {
+    const int a = u * P, e = min(a + P, n);
+    float best = ys[a - c0];
+    int arg = a;
+    float acc = best;
+    for (int t = a + 1; t < e; ++t) {
+      const float y = ys[t - c0];
+      if (y > best) {
+        best = y;
+        arg = t;
+      }
+      acc = page_reduce == KVS_RED_SUM ? acc + y : acc;
+    }
+    const float z = page_reduce == KVS_RED_SUM ? acc : best;
+    if (page) page[(int64_t)row * n_pages + u] = z;
+    if (page_arg) page_arg[(int64_t)row * n_pages + u] = arg;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void cluster_kernel(const float* __restrict__ page,
+                                                           const int32_t* __restrict__ page_arg,
+                                                           int n_pages, int P, int n, float theta,
+                                                           int r, uint8_t* __restrict__ prio) {
+  const int row = blockIdx.y;
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= n) return;
+  int ua = (t - r) / P;
+  if (t - r < 0) ua = 0;
+  int ub = (t + r) / P;
+  if (ub > n_pages - 1) ub = n_pages - 1;
+  uint8_t hit = 0;
+  for (int u = ua; u <= ub; ++u) {
+    const float z = page[(int64_t)row * n_pages + u];
+    const int cc = page_arg[(int64_t)row * n_pages + u];
+    const int d = t - cc;
+    if (z >= theta && d <= r && d >= -r) hit = 1;
+  }
+  prio[(int64_t)row * n + t] = hit;
+}
+
+constexpr int kAggThreads = 256;
+constexpr int kAggItems = 8;
+constexpr int kAggTile = kAggThreads * kAggItems;
+
+__device__ __forceinline__ float head_sum(const float* S, int H, int64_t ld, int t) {
+  float v = S[t];
+  for (int h = 1; h < H; ++h) v += S[(int64_t)h * ld + t];
+  return v;
+}
+
+// Partial L1 norms, one float64 per workgroup, in a fixed order.
+__global__ __launch_bounds__(kAggThreads) void agg_norm_kernel(const float* __restrict__ S, int H,
+                                                               int n, int64_t ld,
+                                                               double* __restrict__ part) {
+  __shared__ double red[kAggThreads];
+  const int base = blockIdx.x * kAggTile;
+  double s = 0.0;
+  for (int k = 0; k < kAggItems; ++k) {
+    const int t = base + k * kAggThreads + threadIdx.x;
+    if (t < n) s += fabs((double)head_sum(S, H, ld, t));
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kAggThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kAggThreads) void agg_apply_kernel(
+    float* __restrict__ acc, const float* __restrict__ S, int H, int n, int64_t ld, int mode,
+    int first, const double* __restrict__ part, int n_part) {
+  float inv_norm = 0.f;
+  if (mode == KVS_RED_SUM_L1) {
+    double norm = 0.0;
+    for (int i = 0; i < n_part; ++i) norm += part[i];
+    inv_norm = (float)(1.0 / norm);
+  }
+  const int base = blockIdx.x * kAggTile;
+  for (int k = 0; k < kAggItems; ++k) {
+    const int t = base + k * kAggThreads + threadIdx.x;
+    if (t >= n) continue;
+    const float s = head_sum(S, H, ld, t);
+    if (mode == KVS_RED_SUM_L1) {
+      const float v = s * inv_norm;
+      acc[t] = first ? v : acc[t] + v;
+    } else {
+      acc[t] = first ? s : fmaxf(acc[t], s);
+    }
+  }
+}
+
+}  // namespace
+
+kvs_status pool_pages_run(const float* S, int H, int n, int64_t ld, int head_reduce, int pool,
+                          int pool_k, int P, int page_reduce, float* pooled, float* page,
+                          int32_t* page_arg, hipStream_t stream) {
+  const int rows = head_reduce == KVS_RED_NONE ? H : 1;
+  int chunk = kChunk;
+  if (P > 0) chunk = kChunk / P * P;  // page-aligned chunks
+  if (chunk <= 0) return KVS_EUNSUPPORTED;
+  dim3 grid((n + chunk - 1) / chunk, rows);
+  hipLaunchKernelGGL(pool_pages_kernel, grid, dim3(kThreads), 0, stream, S, H, n, ld, head_reduce,
+                     pool, pool_k, P, page_reduce, chunk, pooled, page, page_arg);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+kvs_status cluster_priority_run(const float* page, const int32_t* page_arg, int H, int n_pages,
+                                int P, int n, float theta, int r, uint8_t* prio,
+                                hipStream_t stream) {
+  dim3 grid((n + kThreads - 1) / kThreads, H);
+  hipLaunchKernelGGL(cluster_kernel, grid, dim3(kThreads), 0, stream, page, page_arg, n_pages, P, n,
+                     theta, r, prio);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+size_t aggregate_ws_bytes(int n) {
+  const size_t blocks = ((size_t)n + kAggTile - 1) / kAggTile;
+  return align_up(blocks * sizeof(double), kWsAlign);
+}
+
+kvs_status aggregate_run(float* acc, const float* S, int H, int n, int64_t ld, int mode, int first,
+                         void* ws, hipStream_t stream) {
+  const int blocks = (n + kAggTile - 1) / kAggTile;
+  double* part = static_cast<double*>(ws);
+  if (mode == KVS_RED_SUM_L1)
+    hipLaunchKernelGGL(agg_norm_kernel, dim3(blocks), dim3(kAggThreads), 0, stream, S, H, n, ld, part);
+  hipLaunchKernelGGL(agg_apply_kernel, dim3(blocks), dim3(kAggThreads), 0, stream, acc, S, H, n, ld,
+                     mode, first, part, blocks);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+}  // namespace kvs

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every symbol include/kvs.h declares, and
+rejects invalid arguments on the host before anything is enqueued (no GPU
+needed: every call here fails validation, so no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def kvs():
+    import prompt_token_importance_amd as k
+    return k
+
+
+def test_every_declared_symbol_is_exported(kvs):
+    names = _declared()
+    assert "kvs_score" in names and "kvs_topk" in names
+    lib = kvs.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kvs.EXPORTED)
+
+
+def test_status_strings(kvs):
+    lib = kvs.library()
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.kvs_status_string(st)
+    assert lib.kvs_version() >= 100
+
+
+def _score_args(kvs, **kw):
+    base = dict(L=512, W=16, d_k=64, H_q=4, H_kv=1, q_pos0=496)
+    base.update(kw)
+    return kvs.score_args(**base)
+
+
+def test_score_workspace_is_shape_only(kvs):
+    a = _score_args(kvs)
+    assert kvs.kvs_score_workspace(a) > 0
+    big = _score_args(kvs, L=131072, W=32, d_k=128, H_q=32, H_kv=8, q_pos0=131040)
+    assert kvs.kvs_score_workspace(big) > kvs.kvs_score_workspace(a)
+    assert kvs.kvs_score_workspace(_score_args(kvs, d_k=96)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), -1), (dict(W=0), -1), (dict(H_q=3, H_kv=2), -1), (dict(q_pos0=-1), -1),
+    (dict(heads=3), -1), (dict(scale=-1.0), -1), (dict(d_k=96), -2),
+    (dict(W=64, H_q=8, H_kv=1), -2), (dict(q_row_stride=65), -1), (dict(s_ld=100), -1),
+])
+def test_score_rejects(kvs, kw, status):
+    lib = kvs.library()
+    a = _score_args(kvs, **kw)
+    st = lib.kvs_score(ctypes.byref(a), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                       ctypes.c_void_p(256), 1 << 20, None)
+    assert st == status
+
+
+def test_score_rejects_null_misaligned_and_small_workspace(kvs):
+    lib = kvs.library()
+    a = _score_args(kvs)
+    P = ctypes.c_void_p
+    assert lib.kvs_score(ctypes.byref(a), None, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_score(ctypes.byref(a), P(18), P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_score(ctypes.byref(a), P(16), P(16), P(16), P(256), 8, None) == -3
+    assert lib.kvs_score(ctypes.byref(a), P(16), P(16), P(16), None, 1 << 20, None) == -3
+    assert lib.kvs_score(None, P(16), P(16), P(16), P(256), 1 << 20, None) == -1
+
+
+def test_other_entry_points_reject(kvs):
+    lib = kvs.library()
+    P = ctypes.c_void_p
+    # pool: even kernel, bad reductions, no outputs, ld < n
+    assert lib.kvs_pool_pages(P(16), 2, 10, 10, 0, 2, 6, 0, 1, P(16), None, None, None) == -1
+    assert lib.kvs_pool_pages(P(16), 2, 10, 10, 5, 2, 7, 0, 1, P(16), None, None, None) == -1
+    assert lib.kvs_pool_pages(P(16), 2, 10, 10, 0, 2, 7, 0, 1, None, None, None, None) == -1
+    assert lib.kvs_pool_pages(P(16), 2, 10, 9, 0, 2, 7, 0, 1, P(16), None, None, None) == -1
+    assert lib.kvs_pool_pages(P(16), 2, 10, 10, 0, 2, 7, 4, 3, None, P(16), None, None) == -1
+    # top-k: budget > n, negative forced, null output
+    assert lib.kvs_topk(P(16), 1, 10, 10, 11, None, 0, P(16), None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, -1, P(16), None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, 0, None, None, 0, None) == -1
+    # union: H_q not a multiple of H_kv, sub_group not dividing G, tiny workspace
+    assert lib.kvs_block_union_pagetable(P(16), 6, 4, 0, 2, 8, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_block_union_pagetable(P(16), 8, 2, 3, 2, 8, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_block_union_pagetable(P(16), 8, 2, 0, 2, 8, P(16), P(16), P(256), 4, None) == -3
+    # aggregate: bad mode, tiny workspace for SUM_L1
+    assert lib.kvs_aggregate_layers(P(16), P(16), 2, 10, 10, 3, 1, P(256), 1 << 20, None) == -1
+    assert lib.kvs_aggregate_layers(P(16), P(16), 2, 10, 10, 4, 1, P(256), 1, None) == -3
+    # cluster: page count inconsistent with n and P
+    assert lib.kvs_cluster_priority(P(16), P(16), 1, 3, 16, 100, 1e-3, 3, P(16), None) == -1
+    # block select: chunk beyond the keys, p_mass out of range, unsupported d_k
+    a = kvs.block_select_args(Lq=64, L=128, d_k=128, H_q=4, H_kv=1, q_pos0=100)
+    assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 24, None) == -1
+    a = kvs.block_select_args(Lq=64, L=128, d_k=128, H_q=4, H_kv=1, q_pos0=64, p_mass=1.5)
+    assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 24, None) == -1
+    a = kvs.block_select_args(Lq=64, L=128, d_k=80, H_q=4, H_kv=1, q_pos0=64)
+    assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 24, None) == -2
+    a = kvs.block_select_args(Lq=64, L=1 << 20, d_k=128, H_q=4, H_kv=1, q_pos0=64, block=64)
+    assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 30, None) == -2

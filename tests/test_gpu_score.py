@@ -1,0 +1,118 @@
+"""GPU parity of kvs_score against the fp64 oracle (element by element).
+
+Tolerance: |gpu - oracle| <= 2e-3 |oracle| + 2e-3 * 1e-3 * R / L (fp32
+accumulation of bf16 products and exp2 vs fp64); total mass within 1e-4 R.
+Sizes span several 32-key tiles, several key splits and a ragged tail; the
+full-size cases run the shapes of the Llama-3.1-8B (32K) and Mistral-7B (128K)
+layers in the launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_mass, assert_scores_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvs():
+    import prompt_token_importance_amd as k
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return k
+
+
+def _run(kvs, ly, heads, q_pos0=None, **kw):
+    q_pos0 = ly.q_pos0 if q_pos0 is None else q_pos0
+    Q = kvs.bf16_from_bits(ly.Q)
+    K = kvs.bf16_from_bits(ly.K)
+    a = kvs.score_args(L=ly.L, W=ly.W, d_k=ly.d_k, H_q=ly.H_q, H_kv=ly.H_kv, q_pos0=q_pos0,
+                       heads=heads, **kw)
+    S = kvs.kvs_score(Q, K, a)
+    torch.cuda.synchronize()
+    return S.cpu().numpy()
+
+
+CASES = [
+    # (name, L, W, d_k, H_q, H_kv, q_pos0 offset from L - W)
+    ("tiny", 512, 16, 64, 4, 1, 0),
+    ("ragged", 1000, 7, 128, 8, 2, 0),
+    ("ragged64", 777, 13, 64, 6, 3, 0),
+    ("gqa_w32", 4113, 32, 128, 32, 8, 0),
+    ("decode_w1", 2000, 1, 128, 32, 8, 0),
+    ("claa_w8", 3000, 8, 128, 32, 8, 0),
+    ("lookahead", 1500, 32, 128, 8, 2, 40),     # queries after the prompt: all keys visible
+    ("mha", 640, 32, 64, 4, 4, 0),
+    ("w64", 900, 64, 64, 4, 2, 0),
+    ("one_key", 1, 1, 64, 2, 1, 0),
+    ("short", 20, 20, 128, 4, 1, 0),            # window is the whole prompt
+]
+
+
+@pytest.mark.parametrize("name,L,W,d_k,H_q,H_kv,off", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("heads", [1, 0, 2], ids=["group_sum", "none", "group_max"])
+def test_score_parity(kvs, name, L, W, d_k, H_q, H_kv, off, heads):
+    print(f"case {name} heads={heads}", flush=True)
+    ly = synth.gaussian_layer(100 + L, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv)
+    q_pos0 = L - W + off
+    got = _run(kvs, ly, heads, q_pos0=q_pos0)
+    want = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0, heads=heads)
+    G = H_q // H_kv
+    R = W * G if heads == 1 else W
+    assert_scores_close(got, want, R, L, name)
+    if heads != 2:
+        assert_mass(got, R)
+
+
+def test_accumulate_and_strides(kvs):
+    """accumulate=1 adds into S; sequence-major K via strides; padded S rows."""
+    L, W, d_k, H_q, H_kv = 1100, 16, 128, 16, 4
+    ly = synth.gaussian_layer(7, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv)
+    want = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0)
+    Q = kvs.bf16_from_bits(ly.Q)
+    Kseq = kvs.bf16_from_bits(np.ascontiguousarray(ly.K.transpose(1, 0, 2)))  # [L][H_kv][d]
+    s_ld = 1152
+    S = torch.full((H_kv, s_ld), 0.5, dtype=torch.float32, device="cuda")
+    a = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, accumulate=True,
+                       k_head_stride=d_k, k_tok_stride=H_kv * d_k, s_ld=s_ld)
+    kvs.kvs_score(Q, Kseq, a, S=S)
+    torch.cuda.synchronize()
+    got = S.cpu().numpy()
+    assert_scores_close(got[:, :L] - 0.5, want, W * H_q // H_kv, L, "accumulate")
+    assert np.all(got[:, L:] == 0.5), "wrote past L"
+
+
+def test_deterministic(kvs):
+    ly = synth.gaussian_layer(3, L=5000, W=32, d_k=128, H_q=32, H_kv=8)
+    a = _run(kvs, ly, 1)
+    b = _run(kvs, ly, 1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_identical_keys_closed_form(kvs):
+    """All keys equal: prefix columns equal G * sum_j 1/(q_pos0 + j + 1)."""
+    L, W, G = 3000, 32, 4
+    ly = synth.gaussian_layer(9, L=L, W=W, d_k=128, H_q=G, H_kv=1)
+    ly.K = np.repeat(ly.K[:, :1, :], L, axis=1)
+    got = _run(kvs, ly, 1)[0]
+    q_pos0 = L - W
+    inv = np.array([1.0 / (q_pos0 + j + 1) for j in range(W)])
+    np.testing.assert_allclose(got[:q_pos0], G * inv.sum(), rtol=2e-3)
+    for i in range(W):
+        np.testing.assert_allclose(got[q_pos0 + i], G * inv[i:].sum(), rtol=2e-3)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["llama32k", "mistral128k"])
+def test_full_size_parity(kvs, which):
+    """BASELINE shapes, all heads, every column (the oracle takes a few seconds)."""
+    print(f"full-size {which}", flush=True)
+    ly = synth.llama_layer() if which == "llama32k" else synth.mistral_layer()
+    got = _run(kvs, ly, 1)
+    want = oracle.score(ly.Q, ly.K, L=ly.L, W=ly.W, d_k=ly.d_k, H_q=ly.H_q, H_kv=ly.H_kv,
+                        q_pos0=ly.q_pos0)
+    R = ly.W * ly.G
+    assert_scores_close(got, want, R, ly.L, which)
+    assert_mass(got, R)
