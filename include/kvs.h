@@ -99,8 +99,10 @@ int32_t kvs_version(void);
  * L*d_k, d_k, L).  Q/K pointers and strides must be 16-byte aligned.
  * Limits: d_k in {64, 128}; W*G <= 128 after padding each head's rows to
  * 4, 8, 16 or a multiple of 32; otherwise KVS_EUNSUPPORTED.
- * The workspace holds per-split softmax statistics; its size depends only on
- * the shape.  The result is bit-identical from run to run.
+ * The workspace holds per-split softmax statistics and the per-row constants
+ * m_r + log2 Z_r; its size depends only on the shape.  `phase` splits the
+ * call into its statistics pass and its column-sum pass (both read K once).
+ * The result is bit-identical from run to run.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t L, W, d_k, H_q, H_kv;
@@ -111,6 +113,9 @@ typedef struct {
   int64_t s_ld;       /* row stride of S in floats, >= L                    */
   float scale;        /* logit scale, 0 => 1/sqrt(d_k); must be >= 0       */
   int32_t accumulate; /* 0: S = score, 1: S += score                        */
+  int32_t phase;      /* 0: both passes; 1: row statistics only (fills ws);
+                         2: column sums only, from a ws that a phase-1 call
+                         with the same arguments filled                     */
 } kvs_score_args;
 
 size_t kvs_score_workspace(const kvs_score_args* a);
@@ -193,7 +198,9 @@ kvs_status kvs_aggregate_layers(float* acc, const float* S, int32_t H, int32_t n
  * [ClusterAttn] method details: centres are the block-level max indices
  * page_arg[h][u] whose block maximum page[h][u] >= theta; every token within
  * r of a centre (|t - c| <= r, t in [0, n)) gets priority[h][t] = 1, else 0.
- * page / page_arg [H][n_pages] come from kvs_pool_pages with page size P.
+ * page / page_arg [H][n_pages] come from kvs_pool_pages with page size P:
+ * page_arg[h][u] must lie in [u*P, min(u*P + P, n)) (a centre is only looked
+ * for in the pages that can hold a token within r of t).
  * ---------------------------------------------------------------------- */
 kvs_status kvs_cluster_priority(const float* page, const int32_t* page_arg, int32_t H,
                                 int32_t n_pages, int32_t P, int32_t n, float theta, int32_t r,

@@ -296,7 +296,8 @@ def topk(S, budget: int, priority=None, n_forced: int = 0) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def block_select(Qc, K, *, Lq: int, L: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
-                 block: int = 64, p_mass: float = 0.9, scale: Optional[float] = None) -> np.ndarray:
+                 block: int = 64, p_mass: float = 0.9, scale: Optional[float] = None,
+                 return_before: bool = False):
     """Binary block mask M [H_q][n_qb][n_kvb] from mean-pooled block logits.
 
     Kb[g][j] = mean of the keys of block j; Qb[h][i] = mean of the chunk rows of
@@ -304,7 +305,8 @@ def block_select(Qc, K, *, Lq: int, L: int, d_k: int, H_q: int, H_kv: int, q_pos
     KV block j is visible when its first token is not after that position.
     Logits scale * Qb . Kb over visible blocks, softmax; blocks ordered by
     (probability desc, j asc); block j is kept while the mass ranked strictly
-    before it is < p_mass (so the crossing block is kept).
+    before it is < p_mass (so the crossing block is kept).  With ``return_before``
+    also returns that preceding mass per block (+inf where not visible).
     """
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
@@ -317,6 +319,7 @@ def block_select(Qc, K, *, Lq: int, L: int, d_k: int, H_q: int, H_kv: int, q_pos
     for j in range(n_kvb):
         Kb[:, j] = k[:, j * block:min(L, j * block + block)].mean(axis=1)
     M = np.zeros((H_q, n_qb, n_kvb), dtype=np.uint8)
+    mass_before = np.full((H_q, n_qb, n_kvb), np.inf)
     for h in range(H_q):
         g = h // G
         for i in range(n_qb):
@@ -332,6 +335,9 @@ def block_select(Qc, K, *, Lq: int, L: int, d_k: int, H_q: int, H_kv: int, q_pos
             before = np.cumsum(p[order]) - p[order]          # mass ranked strictly before
             keep = (before < p_mass) & vis[order]
             M[h, i, order[keep]] = 1
+            mass_before[h, i, order] = np.where(vis[order], before, np.inf)
+    if return_before:
+        return M, mass_before
     return M
 
 

@@ -36,7 +36,7 @@ class ScoreArgs(ctypes.Structure):
         ("q_head_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
         ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
         ("s_ld", ctypes.c_int64),
-        ("scale", ctypes.c_float), ("accumulate", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("accumulate", ctypes.c_int32), ("phase", ctypes.c_int32),
     ]
 
 
@@ -127,11 +127,12 @@ def bf16_from_bits(bits, device="cuda") -> torch.Tensor:
 
 # --------------------------------------------------------------------------- score
 def score_args(*, L, W, d_k, H_q, H_kv, q_pos0, heads=HEADS_GROUP_SUM, scale=0.0, accumulate=False,
-               q_head_stride=0, q_row_stride=0, k_head_stride=0, k_tok_stride=0, s_ld=0) -> ScoreArgs:
+               q_head_stride=0, q_row_stride=0, k_head_stride=0, k_tok_stride=0, s_ld=0,
+               phase=0) -> ScoreArgs:
     return ScoreArgs(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, heads=heads, q_pos0=q_pos0,
                      q_head_stride=q_head_stride, q_row_stride=q_row_stride,
                      k_head_stride=k_head_stride, k_tok_stride=k_tok_stride, s_ld=s_ld,
-                     scale=scale, accumulate=int(bool(accumulate)))
+                     scale=scale, accumulate=int(bool(accumulate)), phase=phase)
 
 
 def kvs_score_workspace(args: ScoreArgs) -> int:

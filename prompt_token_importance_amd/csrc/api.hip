@@ -22,6 +22,7 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
   if (a->q_pos0 < 0) return KVS_EINVAL;
   if (a->heads < KVS_HEADS_NONE || a->heads > KVS_HEADS_GROUP_MAX) return KVS_EINVAL;
   if (a->accumulate != 0 && a->accumulate != 1) return KVS_EINVAL;
+  if (a->phase < 0 || a->phase > 2) return KVS_EINVAL;
   if (!(a->scale >= 0.f) || isinf(a->scale)) return KVS_EINVAL;
   if (a->L > (1 << 30)) return KVS_EUNSUPPORTED;
   if (a->d_k != 64 && a->d_k != 128) return KVS_EUNSUPPORTED;
@@ -95,6 +96,7 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   p.d_k = a.d_k;
   p.heads = a.heads;
   p.accumulate = a.accumulate;
+  p.phase = a.phase;
   const double scale = a.scale > 0.f ? (double)a.scale : 1.0 / sqrt((double)a.d_k);
   p.c = (float)(scale * 1.4426950408889634073599246810018921);  // scale * log2(e)
   return score_run(pl, p, as_stream(stream));
@@ -135,6 +137,7 @@ kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t bu
   if (((uintptr_t)S & 3u) || ((uintptr_t)idx & 3u)) return KVS_EINVAL;
   const size_t need = topk_ws_bytes(H, n, budget);
   if (need && (!ws || ws_bytes < need)) return KVS_EWORKSPACE;
+  if (need && !aligned16(ws)) return KVS_EINVAL;
   return topk_run(S, H, n, ld, budget, priority, n_forced, idx, ws, as_stream(stream));
 }
 

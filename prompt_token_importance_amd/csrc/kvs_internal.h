@@ -33,11 +33,11 @@ struct ScoreLaunch {
   const uint16_t* Q;
   const uint16_t* K;
   float* S;
-  float2* stats;  // [H_kv][n_split][rows_pad]
+  float2* stats;  // [H_kv][rows_pad][n_split]
   float* rowc;    // [H_kv][rows_pad]
   int64_t qhs, qrs, khs, kts, s_ld;
   int64_t q_pos0;
-  int L, W, G, H_kv, d_k, heads, accumulate;
+  int L, W, G, H_kv, d_k, heads, accumulate, phase;
   float c;        // scale * log2(e)
 };
 

@@ -41,6 +41,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStride = 36;  // floats per row of the LDS transpose buffers
+constexpr int kStages = 4;   // K tiles per wave in the LDS ring (kStages - 1 in flight)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
@@ -61,21 +62,94 @@ __device__ __forceinline__ void lds_order() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// K tiles travel HBM -> LDS with gfx950's direct-to-LDS 16-byte loads, so
+// several tiles per wave are in flight without holding VGPRs.  Each wave owns
+// a ring of kStages tile buffers.  Load instruction s writes 64 x 16 bytes in
+// lane order; lane l fetches key t0 + l%32, d range
+// [(l/32) * D/2 + 8s, +8), i.e. exactly the A-operand fragment lane l needs at
+// k-step s (MFMA k = 8 * (l/32) + e).  Reading it back is one conflict-free
+// ds_read_b128 per k-step at offset s*1024 + 16*l.
 template <int D>
-struct KTile {
-  bf16x8 v[D / 16];
-};
+constexpr int tile_bytes() { return 32 * D * 2; }
 
-// Lane l holds key t0 + l%32 and the d range [(l/32) * D/2, (l/32 + 1) * D/2):
-// k-step s covers d = (l/32) * D/2 + 8s + e, e < 8, i.e. MFMA k = 8 * (l/32) + e.
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D>
-__device__ __forceinline__ void load_k(KTile<D>& kt, const uint16_t* kbase, int64_t kts, int t0,
-                                       int L, int lane) {
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint16_t* kbase, int64_t kts,
+                                           int t0, int L, int lane) {
   int t = t0 + (lane & 31);
   t = t < L ? t : L - 1;  // clamp the ragged tail; masked later
-  const uint16_t* ptr = kbase + (int64_t)t * kts + (lane >> 5) * (D / 2);
+  const uint16_t* src = kbase + (int64_t)t * kts + (lane >> 5) * (D / 2);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) kt.v[s] = load16(ptr + 8 * s);
+  for (int s = 0; s < D / 16; ++s)
+    __builtin_amdgcn_global_load_lds(src + 8 * s, (lds_void*)(stage + s * 1024), 16, 0, 0);
+}
+
+// Waits until at most N vector-memory operations of this wave are outstanding
+// (vmcnt decrements in issue order), with a compiler memory barrier so no LDS
+// read is hoisted above it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS accesses inside the tile loops are issued through inline asm: the
+// compiler would otherwise guard every LDS read with a full vmcnt(0) wait
+// (it cannot tell the ring stage being read from the ones still being
+// filled), draining the load queue.  Each asm wait lists the registers it
+// guards as operands, so no consumer is scheduled above it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_read_b128(u32x4& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_read_b32(float& v, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_write_b128(uint32_t addr, const f32x4& v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm(u32x4 (&v)[N]) {
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
+__device__ __forceinline__ void wait_lgkm16(float (&v)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+template <int S, int KS>
+__device__ __forceinline__ void read_frags(u32x4 (&f)[KS], uint32_t addr) {
+  if constexpr (S < KS) {
+    ds_read_b128<S * 1024>(f[S], addr);
+    read_frags<S + 1, KS>(f, addr);
+  }
+}
+
+// Waits for the tile issued `ahead` tiles before the newest one.
+template <int D, int S>
+__device__ __forceinline__ void wait_tile(int ahead) {
+  constexpr int KS = D / 16;
+  if (S > 3 && ahead >= 3) wait_vm<3 * KS>();
+  else if (S > 2 && ahead == 2) wait_vm<2 * KS>();
+  else if (ahead == 1) wait_vm<KS>();
+  else wait_vm<0>();
 }
 
 // Query row fragments (B operand): N-tile T, lane l -> padded row 32T + l%32.
@@ -102,15 +176,21 @@ __device__ __forceinline__ void load_q(bf16x8 (&q)[NT][D / 16], int (&vis)[NT], 
 }
 
 template <int D, int NT>
-__device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const KTile<D>& kt,
-                                            const bf16x8 (&q)[NT][D / 16]) {
+__device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const uint8_t* stage,
+                                            const bf16x8 (&q)[NT][D / 16], int lane) {
+  constexpr int KS = D / 16;
+  u32x4 f[KS];
+  read_frags<0, KS>(f, lds_addr(stage) + 16 * lane);
+  wait_lgkm<KS>(f);
 #pragma unroll
   for (int T = 0; T < NT; ++T) acc[T] = f32x16{};
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
+  for (int s = 0; s < KS; ++s) {
+    const bf16x8 kf = __builtin_bit_cast(bf16x8, f[s]);
 #pragma unroll
     for (int T = 0; T < NT; ++T)
-      acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt.v[s], q[T][s], acc[T], 0, 0, 0);
+      acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[T][s], acc[T], 0, 0, 0);
+  }
 }
 
 // Key index of accumulator element i for lane half hl (32x32 MFMA output layout).
@@ -119,7 +199,8 @@ __device__ __forceinline__ int key_of(int i, int hl) { return 8 * (i >> 2) + 4 *
 // ------------------------------------------------------------------ pass 1
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 31, hl = lane >> 5;
   const int g = a.g0 + blockIdx.y;
   const int split = blockIdx.x;
@@ -137,16 +218,25 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     m[T] = kNegInf;
     z[T] = 0.f;
   }
+  // Q must be in VGPRs before the tile loop starts queueing K loads; a wait the
+  // compiler can see, so it does not drain the queue inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
 
+  constexpr int S = kStages;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
-  KTile<D> cur, nxt;
-  int tile = tb + wave;
-  if (tile < te) load_k<D>(cur, kbase, a.p.kts, tile * 32, a.p.L, lane);
-  for (; tile < te; tile += kWaves) {
-    const int tn = tile + kWaves;
-    if (tn < te) load_k<D>(nxt, kbase, a.p.kts, tn * 32, a.p.L, lane);
+  // this wave's tiles: tb + wave, tb + wave + kWaves, ...
+  const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  for (int i = 0; i < S - 1 && i < nt; ++i)
+    issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, a.p.L, lane);
+  for (int i = 0; i < nt; ++i) {
+    if (i + S - 1 < nt)
+      issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
+                    (tb + wave + (i + S - 1) * kWaves) * 32, a.p.L, lane);
+    wait_tile<D, S>(min(S - 1, nt - 1 - i));
+    const int tile = tb + wave + i * kWaves;
     f32x16 acc[NT];
-    tile_logits<D, NT>(acc, cur, q);
+    tile_logits<D, NT>(acc, ring[wave][i % S], q, lane);
     const int t0 = tile * 32;
     if (t0 + 31 <= a.min_vis) {
 #pragma unroll
@@ -181,7 +271,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
         }
       }
     }
-    cur = nxt;
   }
 
   __shared__ float2 sm[kWaves][32 * NT];
@@ -203,22 +292,36 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) zz += sm[w][r].y * ex2(sm[w][r].x - mm);
     }
-    a.p.stats[((int64_t)g * a.n_split + split) * a.rows_pad + r] = make_float2(mm, zz);
+    a.p.stats[((int64_t)g * a.rows_pad + r) * a.n_split + split] = make_float2(mm, zz);
   }
 }
 
 // ------------------------------------------------------------------ merge
-__global__ __launch_bounds__(128) void score_merge_kernel(KArgs a) {
-  const int g = a.g0 + blockIdx.x;
-  for (int r = threadIdx.x; r < a.rows_pad; r += blockDim.x) {
-    const float2* st = a.p.stats + (int64_t)g * a.n_split * a.rows_pad + r;
-    float mm = kNegInf;
-    for (int s = 0; s < a.n_split; ++s) mm = fmaxf(mm, st[(int64_t)s * a.rows_pad].x);
-    float zz = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float2 v = st[(int64_t)s * a.rows_pad];
+// Folds the per-split (max, sum) pairs of each row by log-sum-exp into the
+// row constant b = m + log2 Z.  Eight lanes share a row and stride over its
+// splits (stored contiguously), so all loads of a row are in flight at once;
+// the lanes combine with a fixed butterfly, so the result is reproducible.
+constexpr int kMergeLanes = 8;
+constexpr int kMergeRows = kThreads / kMergeLanes;   // 32 rows per workgroup
+
+__global__ __launch_bounds__(kThreads) void score_merge_kernel(KArgs a) {
+  const int g = a.g0 + blockIdx.y;
+  const int r = blockIdx.x * kMergeRows + threadIdx.x / kMergeLanes;
+  const int sub = threadIdx.x % kMergeLanes;
+  const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + r) * a.n_split;
+  float mm = kNegInf;
+  for (int s = sub; s < a.n_split; s += kMergeLanes) mm = fmaxf(mm, st[s].x);
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+  float zz = 0.f;
+  if (mm != kNegInf)
+    for (int s = sub; s < a.n_split; s += kMergeLanes) {
+      const float2 v = st[s];
       if (v.x != kNegInf) zz += v.y * exp2f(v.x - mm);
     }
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) zz += __shfl_xor(zz, off);
+  if (sub == 0) {
     const int hq = r / a.head_rows, j = r % a.head_rows;
     const bool valid = hq < a.p.G && j < a.p.W && mm != kNegInf;
     a.p.rowc[(int64_t)g * a.rows_pad + r] = valid ? mm + log2f(zz) : kPosInf;
@@ -234,7 +337,8 @@ __device__ __forceinline__ void store_out(float* o, float v, int accumulate) {
 // MODE 1: per query head sums (NONE) or their maximum (GROUP_MAX).
 template <int D, int NT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 31, hl = lane >> 5;
   const int g = a.g0 + blockIdx.y;
   const int split = blockIdx.x;
@@ -249,20 +353,26 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   float b[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) b[T] = a.p.rowc[(int64_t)g * a.rows_pad + 32 * T + nl];
+  __builtin_amdgcn_s_waitcnt(0);   // Q and row constants ready before the K queue starts
 
   __shared__ float tr[kWaves][32 * kStride];
   __shared__ float hacc[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * 32 : 1];
   float* wl = tr[wave];
 
+  constexpr int S = MODE == 0 ? kStages : kStages - 1;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
-  KTile<D> cur, nxt;
-  int tile = tb + wave;
-  if (tile < te) load_k<D>(cur, kbase, a.p.kts, tile * 32, L, lane);
-  for (; tile < te; tile += kWaves) {
-    const int tn = tile + kWaves;
-    if (tn < te) load_k<D>(nxt, kbase, a.p.kts, tn * 32, L, lane);
+  const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  for (int i = 0; i < S - 1 && i < nt; ++i)
+    issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
+  for (int i = 0; i < nt; ++i) {
+    if (i + S - 1 < nt)
+      issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
+                    (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
+    wait_tile<D, S>(min(S - 1, nt - 1 - i));
+    const int tile = tb + wave + i * kWaves;
     f32x16 acc[NT];
-    tile_logits<D, NT>(acc, cur, q);
+    tile_logits<D, NT>(acc, ring[wave][i % S], q, lane);
     const int t0 = tile * 32;
     const bool full = t0 + 31 <= a.min_vis;
     float p[NT][16];
@@ -284,17 +394,36 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         for (int T = 1; T < NT; ++T) s += p[T][i];
         part[i] = s;
       }
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa)
-        *reinterpret_cast<f32x4*>(&wl[nl * kStride + 8 * aa + 4 * hl]) =
-            f32x4{part[4 * aa], part[4 * aa + 1], part[4 * aa + 2], part[4 * aa + 3]};
-      lds_order();
+      // transpose through this wave's LDS buffer: row n = query row lane, 32 keys
+      const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
+      ds_write_b128<0>(waddr, f32x4{part[0], part[1], part[2], part[3]});
+      ds_write_b128<32>(waddr, f32x4{part[4], part[5], part[6], part[7]});
+      ds_write_b128<64>(waddr, f32x4{part[8], part[9], part[10], part[11]});
+      ds_write_b128<96>(waddr, f32x4{part[12], part[13], part[14], part[15]});
+      const uint32_t raddr = lds_addr(wl) + (16 * hl * kStride + k) * 4;
+      float r[16];
+      ds_read_b32<0 * kStride * 4>(r[0], raddr);
+      ds_read_b32<1 * kStride * 4>(r[1], raddr);
+      ds_read_b32<2 * kStride * 4>(r[2], raddr);
+      ds_read_b32<3 * kStride * 4>(r[3], raddr);
+      ds_read_b32<4 * kStride * 4>(r[4], raddr);
+      ds_read_b32<5 * kStride * 4>(r[5], raddr);
+      ds_read_b32<6 * kStride * 4>(r[6], raddr);
+      ds_read_b32<7 * kStride * 4>(r[7], raddr);
+      ds_read_b32<8 * kStride * 4>(r[8], raddr);
+      ds_read_b32<9 * kStride * 4>(r[9], raddr);
+      ds_read_b32<10 * kStride * 4>(r[10], raddr);
+      ds_read_b32<11 * kStride * 4>(r[11], raddr);
+      ds_read_b32<12 * kStride * 4>(r[12], raddr);
+      ds_read_b32<13 * kStride * 4>(r[13], raddr);
+      ds_read_b32<14 * kStride * 4>(r[14], raddr);
+      ds_read_b32<15 * kStride * 4>(r[15], raddr);
+      wait_lgkm16(r);
       float v = 0.f;
 #pragma unroll
-      for (int n = 0; n < 16; ++n) v += wl[(16 * hl + n) * kStride + k];
+      for (int n = 0; n < 16; ++n) v += r[n];
       v += __shfl_xor(v, 32);
       if (hl == 0 && t < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + t, v, a.p.accumulate);
-      lds_order();
     } else {
       float* ha = hacc[wave];
       for (int x = lane; x < a.p.G * 32; x += 64) ha[x] = 0.f;
@@ -333,7 +462,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       }
       lds_order();
     }
-    cur = nxt;
   }
 }
 
@@ -352,8 +480,12 @@ kvs_status launch_rounds(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t 
     const int64_t mv = p.q_pos0 < (int64_t)p.L - 1 ? p.q_pos0 : (int64_t)p.L - 1;
     a.min_vis = (int)mv;
     dim3 grid(pl.n_split, nb);
-    hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(score_merge_kernel, dim3(nb), dim3(128), 0, stream, a);
+    if (p.phase != 2) {
+      hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(score_merge_kernel, dim3(pl.rows_pad / kMergeRows, nb), dim3(kThreads), 0,
+                         stream, a);
+    }
+    if (p.phase == 1) continue;
     if (p.heads == KVS_HEADS_GROUP_SUM)
       hipLaunchKernelGGL((score_colsum_kernel<D, NT, 0>), grid, dim3(kThreads), 0, stream, a);
     else
@@ -397,9 +529,9 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   (void)head_bytes;
   batch = batch < a->H_kv ? batch : a->H_kv;
   pl->head_batch = batch;
-  // Splits of the key range: about two 4-wave workgroups per CU per launch,
-  // and at least 4 tiles (one per wave) per split.
-  const int target_wg = env_int("KVS_SCORE_TARGET_WG", 512);
+  // Splits of the key range: one 4-wave workgroup per CU (256 CUs), each
+  // streaming a contiguous run of tiles, and at least 4 tiles (one per wave).
+  const int target_wg = env_int("KVS_SCORE_TARGET_WG", 256);
   int per_head = (target_wg + batch - 1) / batch;
   int max_split = pl->n_tiles / 4 > 1 ? pl->n_tiles / 4 : 1;
   int ns = per_head < max_split ? per_head : max_split;
