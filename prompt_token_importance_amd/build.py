@@ -17,6 +17,9 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # Never emit packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax work reads them directly, no
+    # v_accvgpr_read copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -64,11 +64,13 @@ __device__ __forceinline__ void lds_order() {
 
 // K tiles travel HBM -> LDS with gfx950's direct-to-LDS 16-byte loads, so
 // several tiles per wave are in flight without holding VGPRs.  Each wave owns
-// a ring of kStages tile buffers.  Load instruction s writes 64 x 16 bytes in
-// lane order; lane l fetches key t0 + l%32, d range
-// [(l/32) * D/2 + 8s, +8), i.e. exactly the A-operand fragment lane l needs at
-// k-step s (MFMA k = 8 * (l/32) + e).  Reading it back is one conflict-free
-// ds_read_b128 per k-step at offset s*1024 + 16*l.
+// a ring of kStages tile buffers.  A tile is 32 keys x CR 16-byte chunks
+// (CR = D/8).  Load instruction j writes 64 x 16 bytes in lane order, i.e.
+// rows 64/CR * j ... of the tile, and its lanes read one contiguous 1 KiB run
+// of K, so each instruction touches only a few cache lines.  Inside a row the
+// chunks are XOR-swizzled: LDS position p of key row t holds chunk p ^ (t % CR),
+// which keeps the later fragment reads (32 rows, same chunk) spread over the
+// LDS banks.
 template <int D>
 constexpr int tile_bytes() { return 32 * D * 2; }
 
@@ -77,12 +79,30 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint16_t* kbase, int64_t kts,
                                            int t0, int L, int lane) {
-  int t = t0 + (lane & 31);
-  t = t < L ? t : L - 1;  // clamp the ragged tail; masked later
-  const uint16_t* src = kbase + (int64_t)t * kts + (lane >> 5) * (D / 2);
+  constexpr int CR = D / 8;          // 16-byte chunks per key row
+  constexpr int RPI = 64 / CR;       // key rows per load instruction
+  const int p = lane % CR;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    __builtin_amdgcn_global_load_lds(src + 8 * s, (lds_void*)(stage + s * 1024), 16, 0, 0);
+  for (int j = 0; j < D / 16; ++j) {
+    const int tr = j * RPI + lane / CR;          // row inside the tile
+    int t = t0 + tr;
+    t = t < L ? t : L - 1;                       // clamp the ragged tail; masked later
+    const int c = p ^ (tr % CR);                 // global chunk stored at position p
+    __builtin_amdgcn_global_load_lds(kbase + (int64_t)t * kts + 8 * c,
+                                     (lds_void*)(stage + j * 1024), 16, 0, 0);
+  }
+}
+
+// Byte offsets, inside a tile, of the A-operand fragment lane `lane` needs at
+// k-step s: key row t = lane % 32, chunk (lane / 32) * CR/2 + s, stored at
+// position chunk ^ (t % CR).
+template <int D>
+__device__ __forceinline__ void frag_offsets(uint32_t (&off)[D / 16], int lane) {
+  constexpr int CR = D / 8;
+  const int t = lane & 31;
+  const int base = ((lane >> 5) * (CR / 2)) ^ (t % CR);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) off[s] = (uint32_t)((t * CR + (base ^ s)) * 16);
 }
 
 // Waits until at most N vector-memory operations of this wave are outstanding
@@ -134,12 +154,10 @@ __device__ __forceinline__ void wait_lgkm16(float (&v)[16]) {
                  "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
 }
 
-template <int S, int KS>
-__device__ __forceinline__ void read_frags(u32x4 (&f)[KS], uint32_t addr) {
-  if constexpr (S < KS) {
-    ds_read_b128<S * 1024>(f[S], addr);
-    read_frags<S + 1, KS>(f, addr);
-  }
+template <int KS>
+__device__ __forceinline__ void read_frags(u32x4 (&f)[KS], uint32_t base, const uint32_t (&off)[KS]) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s) ds_read_b128<0>(f[s], base + off[s]);
 }
 
 // Waits for the tile issued `ahead` tiles before the newest one.
@@ -175,12 +193,37 @@ __device__ __forceinline__ void load_q(bf16x8 (&q)[NT][D / 16], int (&vis)[NT], 
   }
 }
 
+// Query fragments loaded straight into AGPRs (the only form the asm MFMAs
+// read them in).  Padding rows load row 0 of the group instead of zeros:
+// their statistics are discarded and their row constant is +inf, so their
+// logits never reach an output.
+template <int D, int NT>
+__device__ __forceinline__ void load_q_agpr(bf16x8 (&q)[NT][D / 16], int (&vis)[NT],
+                                            const KArgs& a, int g, int lane) {
+  const int nl = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    const int r = 32 * T + nl;
+    const int hq = r / a.head_rows, j = r % a.head_rows;
+    const bool valid = hq < a.p.G && j < a.p.W;
+    const int64_t pos = a.p.q_pos0 + j;
+    vis[T] = valid ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1) : -1;
+    const uint16_t* qp =
+        a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs + (int64_t)(valid ? j : 0) * a.p.qrs +
+        hl * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(q[T][s]) : "v"(qp + 8 * s) : "memory");
+  }
+}
+
 template <int D, int NT>
 __device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const uint8_t* stage,
-                                            const bf16x8 (&q)[NT][D / 16], int lane) {
+                                            const bf16x8 (&q)[NT][D / 16],
+                                            const uint32_t (&off)[D / 16]) {
   constexpr int KS = D / 16;
   u32x4 f[KS];
-  read_frags<0, KS>(f, lds_addr(stage) + 16 * lane);
+  read_frags<KS>(f, lds_addr(stage), off);
   wait_lgkm<KS>(f);
 #pragma unroll
   for (int T = 0; T < NT; ++T) acc[T] = f32x16{};
@@ -196,6 +239,243 @@ __device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const uint8_t* st
 // Key index of accumulator element i for lane half hl (32x32 MFMA output layout).
 __device__ __forceinline__ int key_of(int i, int hl) { return 8 * (i >> 2) + 4 * hl + (i & 3); }
 
+
+// MFMA through inline asm with the query fragment (B operand) read straight
+// from AGPRs: the 128 query-fragment registers of a wave live in the AGPR
+// file, leaving the VGPRs to the accumulators and the softmax work.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kf), "a"(qa));
+}
+__device__ __forceinline__ void mfma_zero(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(kf), "a"(qa));
+}
+// Wait states between an MFMA writing VGPRs and VALU instructions reading
+// them (the compiler does not track dependencies through inline asm).
+__device__ __forceinline__ void mfma_result_guard() {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+}
+
+// One pipeline phase: the NX*KS MFMAs of N-tiles XLO.. of the current tile
+// (fragments f) interleaved, 1 MFMA : EPM elements, with the softmax work on
+// the 16*NY logits of N-tiles YLO.. of the previous batch (accY).  Each slot is
+// fenced so the scheduler keeps the interleave.  WORK(T, i) is called for
+// every logit (T < NY, i < 16).
+template <int D, int NT, int XLO, int NX, int NY, typename Work>
+__device__ __forceinline__ void phase(f32x16 (&accX)[NX > 0 ? NX : 1], const u32x4 (&f)[D / 16],
+                                      const bf16x8 (&q)[NT][D / 16], Work&& work) {
+  constexpr int KS = D / 16;
+  constexpr int M = KS * NX;
+  constexpr int E = 16 * NY;
+  constexpr int EPM = M > 0 ? (E + M - 1) / M : E;
+  constexpr int SLOTS = M > 0 ? M : 1;
+  mfma_result_guard();
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    if constexpr (M > 0) {
+      const int ss = k / (NX > 0 ? NX : 1), T = k % (NX > 0 ? NX : 1);
+      if (ss == 0)
+        mfma_zero(accX[T], f[ss], q[XLO + T][ss]);
+      else
+        mfma_acc(accX[T], f[ss], q[XLO + T][ss]);
+    }
+#pragma unroll
+    for (int u = 0; u < EPM; ++u) {
+      const int e = k * EPM + u;
+      if (e < E) work(e / 16, e % 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ------------------------------------------------------------------ half-tile pipeline
+// A 32-key tile is processed as two halves of its N-tiles (query-row blocks):
+// group 0 = N-tiles [0, NA), group 1 = [NA, NT).  While the matrix cores run
+// the MFMAs of one half, the VALU works on the other half's logits from the
+// previous batch, so MFMA and exp/sum work overlap inside a single wave.
+template <int NT>
+struct Halves {
+  static constexpr int NA = (NT + 1) / 2;
+  static constexpr int NB = NT - NA;
+};
+
+template <int D, int NT, int LO, int N>
+__device__ __forceinline__ void mfma_part(f32x16 (&acc)[N > 0 ? N : 1], const u32x4 (&f)[D / 16],
+                                          const bf16x8 (&q)[NT][D / 16]) {
+  if constexpr (N > 0) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int T = 0; T < N; ++T) {
+        if (s == 0)
+          mfma_zero(acc[T], f[s], q[LO + T][s]);
+        else
+          mfma_acc(acc[T], f[s], q[LO + T][s]);
+      }
+  }
+}
+
+// Asks the scheduler to interleave the preceding block as (1 MFMA, V VALU) x M,
+// so the VALU work issues while the matrix core runs the MFMAs.
+template <int M, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  if constexpr (M > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    interleave_mfma_valu<M - 1, V>();
+  }
+}
+
+// Fast-path partial sums of exp2(x*c - m) for query rows LO .. LO+N-1 of a
+// full tile (no masking); returns whether some lane left [0, 2^64].
+template <int NT, int LO, int N>
+__device__ __forceinline__ bool stats_sums(const f32x16 (&acc)[N > 0 ? N : 1], const float (&m)[NT],
+                                           float c, float (&sum)[N > 0 ? N : 1]) {
+  bool bad = false;
+  if constexpr (N > 0) {
+#pragma unroll
+    for (int T = 0; T < N; ++T) {
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        sa += ex2(fmaf(acc[T][i], c, -m[LO + T]));
+        sb += ex2(fmaf(acc[T][i + 1], c, -m[LO + T]));
+      }
+      sum[T] = sa + sb;
+      bad |= !(sum[T] <= 0x1p64f);
+    }
+  }
+  return bad;
+}
+
+// Commits fast-path sums, or (wave-uniform, rare) recomputes the rows against
+// their exact tile max.
+template <int NT, int LO, int N>
+__device__ __forceinline__ void stats_commit(const f32x16 (&acc)[N > 0 ? N : 1], float (&m)[NT],
+                                             float (&z)[NT], float c, const float (&sum)[N > 0 ? N : 1],
+                                             bool bad) {
+  if constexpr (N > 0) {
+    if (!__any(bad)) {
+#pragma unroll
+      for (int T = 0; T < N; ++T) z[LO + T] += sum[T];
+      return;
+    }
+#pragma unroll
+    for (int T = 0; T < N; ++T) {
+      float mx = acc[T][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[T][i]);
+      const float mn = fmaxf(m[LO + T], mx * c);
+      float s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s2 += ex2(fmaf(acc[T][i], c, -mn));
+      z[LO + T] = z[LO + T] * ex2(m[LO + T] - mn) + s2;
+      m[LO + T] = mn;
+    }
+  }
+}
+
+// Probabilities of a full tile (no masking) summed over rows LO .. LO+N-1.
+template <int NT, int LO, int N, bool ADD>
+__device__ __forceinline__ void probs_full(const f32x16 (&acc)[N > 0 ? N : 1], float (&part)[16],
+                                           const float (&b)[NT], float c) {
+  if constexpr (!ADD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i] = 0.f;
+  }
+  if constexpr (N > 0) {
+#pragma unroll
+    for (int T = 0; T < N; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[i] += ex2(fmaf(acc[T][i], c, -b[LO + T]));
+  }
+}
+
+// Online (max, sum of exp2) update of query rows LO .. LO+N-1 for one tile.
+// The running max m only stabilises the exponentials, so it may lag the true
+// max: terms are summed against the current m, and m is refreshed (the whole
+// half recomputed against its exact max) only when some lane's sum leaves
+// [0, 2^64]; the first tile (m = -inf) always takes that path.  The branch is
+// wave-uniform.
+template <int NT, int LO, int N>
+__device__ __forceinline__ void stats_part(const f32x16 (&acc)[N > 0 ? N : 1], float (&m)[NT],
+                                           float (&z)[NT], float c, bool full, int t0, int hl,
+                                           const int (&vis)[NT]) {
+  if constexpr (N > 0) {
+    if (full) {
+      float sum[N];
+      bool bad = false;
+#pragma unroll
+      for (int T = 0; T < N; ++T) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          sa += ex2(fmaf(acc[T][i], c, -m[LO + T]));
+          sb += ex2(fmaf(acc[T][i + 1], c, -m[LO + T]));
+        }
+        sum[T] = sa + sb;
+        bad |= !(sum[T] <= 0x1p64f);
+      }
+      if (!__any(bad)) {
+#pragma unroll
+        for (int T = 0; T < N; ++T) z[LO + T] += sum[T];
+        return;
+      }
+#pragma unroll
+      for (int T = 0; T < N; ++T) {
+        float mx = acc[T][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[T][i]);
+        const float mn = fmaxf(m[LO + T], mx * c);
+        float s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s2 += ex2(fmaf(acc[T][i], c, -mn));
+        z[LO + T] = z[LO + T] * ex2(m[LO + T] - mn) + s2;
+        m[LO + T] = mn;
+      }
+    } else {
+#pragma unroll
+      for (int T = 0; T < N; ++T) {
+        float v[16];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[i] = (t0 + key_of(i, hl) <= vis[LO + T]) ? acc[T][i] : kNegInf;
+          mx = fmaxf(mx, v[i]);
+        }
+        const float mn = fmaxf(m[LO + T], mx * c);
+        if (mn != kNegInf) {
+          float s2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s2 += ex2(fmaf(v[i], c, -mn));
+          z[LO + T] = z[LO + T] * ex2(m[LO + T] - mn) + s2;
+          m[LO + T] = mn;
+        }
+      }
+    }
+  }
+}
+
+// Probabilities of query rows LO .. LO+N-1 for one tile, summed over those
+// rows into part[] (ADD: part += ..., else part = ...).
+template <int NT, int LO, int N, bool ADD>
+__device__ __forceinline__ void probs_part(const f32x16 (&acc)[N > 0 ? N : 1], float (&part)[16],
+                                           const float (&b)[NT], float c, bool full, int t0,
+                                           int hl, const int (&vis)[NT]) {
+  if constexpr (!ADD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i] = 0.f;
+  }
+  if constexpr (N > 0) {
+#pragma unroll
+    for (int T = 0; T < N; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = ex2(fmaf(acc[T][i], c, -b[LO + T]));
+        part[i] += (full || t0 + key_of(i, hl) <= vis[LO + T]) ? e : 0.f;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ pass 1
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
@@ -210,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 
   bf16x8 q[NT][D / 16];
   int vis[NT];
-  load_q<D, NT>(q, vis, a, g, lane);
+  load_q_agpr<D, NT>(q, vis, a, g, lane);
 
   float m[NT], z[NT];
 #pragma unroll
@@ -225,51 +505,65 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   constexpr int S = kStages;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
+  uint32_t foff[D / 16];
+  frag_offsets<D>(foff, lane);
   // this wave's tiles: tb + wave, tb + wave + kWaves, ...
   const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  constexpr int NA = Halves<NT>::NA, NB = Halves<NT>::NB;
+  f32x16 accA[NA], accB[NB > 0 ? NB : 1];
+  u32x4 f[D / 16];
   for (int i = 0; i < S - 1 && i < nt; ++i)
     issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, a.p.L, lane);
+  if (nt > 0) {
+    wait_tile<D, S>(min(S - 2, nt - 1));
+    read_frags<D / 16>(f, lds_addr(ring[wave][0]), foff);
+    wait_lgkm<D / 16>(f);
+    mfma_part<D, NT, 0, NA>(accA, f, q);
+  }
   for (int i = 0; i < nt; ++i) {
     if (i + S - 1 < nt)
       issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
                     (tb + wave + (i + S - 1) * kWaves) * 32, a.p.L, lane);
-    wait_tile<D, S>(min(S - 1, nt - 1 - i));
-    const int tile = tb + wave + i * kWaves;
-    f32x16 acc[NT];
-    tile_logits<D, NT>(acc, ring[wave][i % S], q, lane);
-    const int t0 = tile * 32;
+    const int t0 = (tb + wave + i * kWaves) * 32;
+    // The next tile's fragments come from stage (i + 1) % S; after the last
+    // tile that stage holds stale data whose MFMA results are never used.
+    const uint32_t next_stage = lds_addr(ring[wave][(i + 1) % S]);
+    const int ahead = i + 1 < nt ? min(S - 2, nt - 2 - i) : 0;
     if (t0 + 31 <= a.min_vis) {
+      // MFMA of tile i's second half || statistics of its first half
+      float sum[NA];
 #pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        float mx = acc[T][0];
+      for (int T = 0; T < NA; ++T) sum[T] = 0.f;
+      phase<D, NT, NA, NB, NA>(accB, f, q, [&](int T, int e) {
+        sum[T] += ex2(fmaf(accA[T][e], c, -m[T]));
+      });
+      bool bad0 = false;
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[T][i]);
-        const float mn = fmaxf(m[T], mx * c);
-        float sum = 0.f;
+      for (int T = 0; T < NA; ++T) bad0 |= !(sum[T] <= 0x1p64f);
+      stats_commit<NT, 0, NA>(accA, m, z, c, sum, bad0);
+      // next tile's fragments; its first-half MFMA || this tile's second half
+      wait_tile<D, S>(ahead);
+      read_frags<D / 16>(f, next_stage, foff);
+      wait_lgkm<D / 16>(f);
+      float sum1[NB > 0 ? NB : 1];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += ex2(fmaf(acc[T][i], c, -mn));
-        z[T] = z[T] * ex2(m[T] - mn) + sum;
-        m[T] = mn;
-      }
+      for (int T = 0; T < (NB > 0 ? NB : 1); ++T) sum1[T] = 0.f;
+      phase<D, NT, 0, NA, NB>(accA, f, q, [&](int T, int e) {
+        sum1[T] += ex2(fmaf(accB[T][e], c, -m[NA + T]));
+      });
+      bool bad1 = false;
+#pragma unroll
+      for (int T = 0; T < NB; ++T) bad1 |= !(sum1[T] <= 0x1p64f);
+      stats_commit<NT, NA, NB>(accB, m, z, c, sum1, bad1);
     } else {
-#pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        float v[16];
-        float mx = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          v[i] = (t0 + key_of(i, hl) <= vis[T]) ? acc[T][i] : kNegInf;
-          mx = fmaxf(mx, v[i]);
-        }
-        const float mn = fmaxf(m[T], mx * c);
-        if (mn != kNegInf) {
-          float sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum += ex2(fmaf(v[i], c, -mn));
-          z[T] = z[T] * ex2(m[T] - mn) + sum;
-          m[T] = mn;
-        }
-      }
+      mfma_result_guard();
+      mfma_part<D, NT, NA, NB>(accB, f, q);
+      stats_part<NT, 0, NA>(accA, m, z, c, false, t0, hl, vis);
+      wait_tile<D, S>(ahead);
+      read_frags<D / 16>(f, next_stage, foff);
+      wait_lgkm<D / 16>(f);
+      mfma_part<D, NT, 0, NA>(accA, f, q);
+      stats_part<NT, NA, NB>(accB, m, z, c, false, t0, hl, vis);
     }
   }
 
@@ -349,7 +643,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 
   bf16x8 q[NT][D / 16];
   int vis[NT];
-  load_q<D, NT>(q, vis, a, g, lane);
+  if constexpr (MODE == 0)
+    load_q_agpr<D, NT>(q, vis, a, g, lane);
+  else
+    load_q<D, NT>(q, vis, a, g, lane);
   float b[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) b[T] = a.p.rowc[(int64_t)g * a.rows_pad + 32 * T + nl];
@@ -362,37 +659,52 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   constexpr int S = MODE == 0 ? kStages : kStages - 1;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
+  uint32_t foff[D / 16];
+  frag_offsets<D>(foff, lane);
   const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
-  for (int i = 0; i < S - 1 && i < nt; ++i)
-    issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
-  for (int i = 0; i < nt; ++i) {
-    if (i + S - 1 < nt)
-      issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                    (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
-    wait_tile<D, S>(min(S - 1, nt - 1 - i));
-    const int tile = tb + wave + i * kWaves;
-    f32x16 acc[NT];
-    tile_logits<D, NT>(acc, ring[wave][i % S], q, lane);
-    const int t0 = tile * 32;
-    const bool full = t0 + 31 <= a.min_vis;
-    float p[NT][16];
+  const int k = lane & 31;
+  if constexpr (MODE == 0) {
+    constexpr int NA = Halves<NT>::NA, NB = Halves<NT>::NB;
+    f32x16 accA[NA], accB[NB > 0 ? NB : 1];
+    u32x4 f[D / 16];
+    float part[16];
+    for (int i = 0; i < S - 1 && i < nt; ++i)
+      issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
+    if (nt > 0) {
+      wait_tile<D, S>(min(S - 2, nt - 1));
+      read_frags<D / 16>(f, lds_addr(ring[wave][0]), foff);
+      wait_lgkm<D / 16>(f);
+      mfma_part<D, NT, 0, NA>(accA, f, q);
+    }
+    for (int i = 0; i < nt; ++i) {
+      if (i + S - 1 < nt)
+        issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
+                      (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
+      const int t0 = (tb + wave + i * kWaves) * 32;
+      const uint32_t next_stage = lds_addr(ring[wave][(i + 1) % S]);
+      const int ahead = i + 1 < nt ? min(S - 2, nt - 2 - i) : 0;
+      if (t0 + 31 <= a.min_vis) {
 #pragma unroll
-    for (int T = 0; T < NT; ++T)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = ex2(fmaf(acc[T][i], c, -b[T]));
-        p[T][i] = (full || t0 + key_of(i, hl) <= vis[T]) ? e : 0.f;
-      }
-    const int k = lane & 31;
-    const int t = t0 + k;
-    if constexpr (MODE == 0) {
-      float part[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = p[0][i];
-#pragma unroll
-        for (int T = 1; T < NT; ++T) s += p[T][i];
-        part[i] = s;
+        for (int e = 0; e < 16; ++e) part[e] = 0.f;
+        phase<D, NT, NA, NB, NA>(accB, f, q, [&](int T, int e) {
+          part[e] += ex2(fmaf(accA[T][e], c, -b[T]));
+        });
+        wait_tile<D, S>(ahead);
+        read_frags<D / 16>(f, next_stage, foff);
+        wait_lgkm<D / 16>(f);
+        phase<D, NT, 0, NA, NB>(accA, f, q, [&](int T, int e) {
+          part[e] += ex2(fmaf(accB[T][e], c, -b[NA + T]));
+        });
+        mfma_result_guard();
+      } else {
+        mfma_result_guard();
+        mfma_part<D, NT, NA, NB>(accB, f, q);
+        probs_part<NT, 0, NA, false>(accA, part, b, c, false, t0, hl, vis);
+        wait_tile<D, S>(ahead);
+        read_frags<D / 16>(f, next_stage, foff);
+        wait_lgkm<D / 16>(f);
+        mfma_part<D, NT, 0, NA>(accA, f, q);
+        probs_part<NT, NA, NB, true>(accB, part, b, c, false, t0, hl, vis);
       }
       // transpose through this wave's LDS buffer: row n = query row lane, 32 keys
       const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
@@ -423,8 +735,31 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) v += r[n];
       v += __shfl_xor(v, 32);
+      const int t = t0 + k;
       if (hl == 0 && t < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + t, v, a.p.accumulate);
-    } else {
+    }
+  } else {
+    for (int i = 0; i < S - 1 && i < nt; ++i)
+      issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
+    for (int i = 0; i < nt; ++i) {
+      if (i + S - 1 < nt)
+        issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
+                      (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
+      wait_tile<D, S>(min(S - 1, nt - 1 - i));
+      const int tile = tb + wave + i * kWaves;
+      f32x16 acc[NT];
+      tile_logits<D, NT>(acc, ring[wave][i % S], q, foff);
+      const int t0 = tile * 32;
+      const bool full = t0 + 31 <= a.min_vis;
+      float p[NT][16];
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) {
+          const float e = ex2(fmaf(acc[T][i2], c, -b[T]));
+          p[T][i2] = (full || t0 + key_of(i2, hl) <= vis[T]) ? e : 0.f;
+        }
+      const int t = t0 + k;
       float* ha = hacc[wave];
       for (int x = lane; x < a.p.G * 32; x += 64) ha[x] = 0.f;
 #pragma unroll

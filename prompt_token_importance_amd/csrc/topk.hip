@@ -12,9 +12,10 @@
 //     the float32 value) in three passes of 12, 11 and 10 bits.  A pass builds
 //     a per-workgroup LDS histogram of the digit among the elements matching
 //     the prefix found so far and adds it to the row's histogram in the
-//     workspace with integer atomics (exact, order-free).  The last workgroup
-//     of a row to finish (atomic ticket) scans the row histogram, fixes the next
-//     digit of the threshold key K* and how many K*-equal elements are needed.
+//     workspace with integer atomics (exact, order-free).  The next kernel's
+//     workgroups each scan the finished histograms to fix the digits of the
+//     threshold key K* and how many K*-equal elements are needed: kernel
+//     boundaries order the passes, so no device-wide fence is needed.
 //  2. A count pass records, per chunk, the elements above K* and equal to K*.
 //  3. The output pass gives each chunk its offset from the counts of the
 //     chunks before it; a thread owns kEpt consecutive elements, and two
@@ -38,7 +39,7 @@ constexpr int kShift[3] = {21, 10, 0};
 struct RowState {
   uint64_t prefix;   // fixed high bits of K*
   uint32_t need;     // elements still to take at or below the prefix
-  uint32_t ticket;   // arrival counter of the current pass
+  uint32_t unused;
 };
 
 struct Ws {
@@ -95,55 +96,17 @@ __global__ __launch_bounds__(kThreads) void topk_zero_kernel(Ws ws, int H, int n
   (void)n_chunks;
 }
 
-// One radix pass; the last workgroup of each row picks the digit.
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ S, int n,
-                                                             int64_t ld,
-                                                             const uint8_t* __restrict__ prio,
-                                                             int budget, int pass, Ws ws) {
-  __shared__ uint32_t h[kBins0];
-  __shared__ uint32_t scan[kThreads];
-  __shared__ bool s_last;
-  const int row = blockIdx.y;
-  const int c0 = blockIdx.x * kChunk;
-  const float* x = S + (int64_t)row * ld;
-  const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
-  const uint32_t nb = pass_bins(pass);
-  const int shift = kShift[pass];
-  RowState st = ws.state[row];
-  if (pass == 0) st = RowState{0ull, (uint32_t)budget, 0u};
-  const uint64_t pmask = pass_mask(pass);
-
-  for (uint32_t b = threadIdx.x; b < nb; b += kThreads) h[b] = 0u;
-  uint64_t k[kEpt];
-  uint32_t valid;
-  load_keys(x, pr, n, c0, k, valid);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e)
-    if (((valid >> e) & 1u) && (k[e] & pmask) == st.prefix)
-      atomicAdd(&h[(uint32_t)(k[e] >> shift) & (nb - 1)], 1u);
-  __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)row * (kBins0 + kBins1 + kBins2) + pass_offset(pass);
-  for (uint32_t b = threadIdx.x; b < nb; b += kThreads)
-    if (h[b]) atomicAdd(&gh[b], h[b]);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = atomicAdd(&ws.state[row].ticket, 1u);
-    s_last = (t == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // Last workgroup of the row: copy the row histogram to LDS (all loads in
-  // flight at once), then a suffix scan from the top bin.
+// Picks the digit of pass p from the row histogram of that pass (complete
+// because the pass ran in an earlier kernel): suffix scan from the top bin to
+// the bin holding the need-th candidate.  Every workgroup of a row computes
+// the same answer.  Returns the updated (prefix, need).
+__device__ void pick_digit(const uint32_t* __restrict__ gh, int p, uint64_t prefix, uint32_t need,
+                           uint32_t* h, uint32_t* scan, uint64_t* s_prefix, uint32_t* s_need) {
+  const uint32_t nb = pass_bins(p);
   const uint32_t per = nb / kThreads;   // 16, 8 or 4 bins per thread
   uint32_t vals[16];
 #pragma unroll
-  for (uint32_t b = 0; b < 16; ++b)
-    vals[b] = b < per ? __hip_atomic_load(&gh[threadIdx.x * per + b], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)
-                      : 0u;
+  for (uint32_t b = 0; b < 16; ++b) vals[b] = b < per ? gh[threadIdx.x * per + b] : 0u;
   uint32_t ls = 0;
 #pragma unroll
   for (uint32_t b = 0; b < 16; ++b) {
@@ -160,18 +123,73 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   }
   const int rt = kThreads - 1 - threadIdx.x;
   const uint32_t above = rt > 0 ? scan[rt - 1] : 0u;
-  if (above < st.need && st.need <= above + ls) {
+  if (above < need && need <= above + ls) {
     uint32_t cum = above;
     for (int b = (int)per - 1; b >= 0; --b) {
       const uint32_t bin = threadIdx.x * per + b;
       const uint32_t c = h[bin];
-      if (cum + c >= st.need) {
-        ws.state[row] = RowState{st.prefix | ((uint64_t)bin << shift), st.need - cum, 0u};
+      if (cum + c >= need) {
+        *s_prefix = prefix | ((uint64_t)bin << kShift[p]);
+        *s_need = need - cum;
         break;
       }
       cum += c;
     }
   }
+  __syncthreads();
+}
+
+// Threshold key K* and the number of K*-equal elements to take, from the
+// histograms of passes 0 .. upto-1.
+__device__ void replay_digits(const Ws& ws, int row, int budget, int upto, uint32_t* h,
+                              uint32_t* scan, uint64_t* s_prefix, uint32_t* s_need) {
+  if (threadIdx.x == 0) {
+    *s_prefix = 0ull;
+    *s_need = (uint32_t)budget;
+  }
+  __syncthreads();
+  const uint32_t* gh = ws.hist + (size_t)row * (kBins0 + kBins1 + kBins2);
+  for (int p = 0; p < upto; ++p) {
+    const uint64_t prefix = *s_prefix;
+    const uint32_t need = *s_need;
+    __syncthreads();
+    pick_digit(gh + pass_offset(p), p, prefix, need, h, scan, s_prefix, s_need);
+  }
+}
+
+// Radix pass p: per-workgroup LDS histogram of digit p among the elements
+// matching the prefix fixed by passes 0 .. p-1, added into the row histogram
+// with integer atomics (exact).
+__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ S, int n,
+                                                             int64_t ld,
+                                                             const uint8_t* __restrict__ prio,
+                                                             int budget, int pass, Ws ws) {
+  __shared__ uint32_t h[kBins0];
+  __shared__ uint32_t scan[kThreads];
+  __shared__ uint64_t s_prefix;
+  __shared__ uint32_t s_need;
+  const int row = blockIdx.y;
+  const int c0 = blockIdx.x * kChunk;
+  const float* x = S + (int64_t)row * ld;
+  const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
+  uint64_t k[kEpt];
+  uint32_t valid;
+  load_keys(x, pr, n, c0, k, valid);
+  replay_digits(ws, row, budget, pass, h, scan, &s_prefix, &s_need);
+  const uint64_t prefix = s_prefix;
+  const uint32_t nb = pass_bins(pass);
+  const int shift = kShift[pass];
+  const uint64_t pmask = pass_mask(pass);
+  for (uint32_t b = threadIdx.x; b < nb; b += kThreads) h[b] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kEpt; ++e)
+    if (((valid >> e) & 1u) && (k[e] & pmask) == prefix)
+      atomicAdd(&h[(uint32_t)(k[e] >> shift) & (nb - 1)], 1u);
+  __syncthreads();
+  uint32_t* gh = ws.hist + (size_t)row * (kBins0 + kBins1 + kBins2) + pass_offset(pass);
+  for (uint32_t b = threadIdx.x; b < nb; b += kThreads)
+    if (h[b]) atomicAdd(&gh[b], h[b]);
 }
 
 __device__ __forceinline__ void block_counts(uint32_t a, uint32_t b, uint32_t* red,
@@ -197,16 +215,22 @@ __device__ __forceinline__ void block_counts(uint32_t a, uint32_t b, uint32_t* r
 __global__ __launch_bounds__(kThreads) void topk_count_kernel(const float* __restrict__ S, int n,
                                                               int64_t ld,
                                                               const uint8_t* __restrict__ prio,
-                                                              Ws ws) {
+                                                              int budget, Ws ws) {
   __shared__ uint32_t red[2 * kWaves];
   const int row = blockIdx.y;
   const int c0 = blockIdx.x * kChunk;
   const float* x = S + (int64_t)row * ld;
   const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
-  const uint64_t kstar = ws.state[row].prefix;
+  __shared__ uint32_t h[kBins0];
+  __shared__ uint32_t scan[kThreads];
+  __shared__ uint64_t s_prefix;
+  __shared__ uint32_t s_need;
   uint64_t k[kEpt];
   uint32_t valid;
   load_keys(x, pr, n, c0, k, valid);
+  replay_digits(ws, row, budget, 3, h, scan, &s_prefix, &s_need);
+  const uint64_t kstar = s_prefix;
+  if (blockIdx.x == 0 && threadIdx.x == 0) ws.state[row] = RowState{s_prefix, s_need, 0u};
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < kEpt; ++e)
@@ -327,7 +351,8 @@ kvs_status topk_run(const float* S, int H, int n, int64_t ld, int budget, const 
     for (int p = 0; p < 3; ++p)
       hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
                          p, ws);
-    hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, ws);
+    hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
+                       ws);
   }
   hipLaunchKernelGGL(topk_out_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
                      n_forced, ws, idx);
