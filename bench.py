@@ -30,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+NL = chr(10)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 
@@ -45,7 +46,36 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=4, help="distinct K buffers cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_colsum_mistral128k_traffic.txt")
+SCORE_SOURCE = os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "score.hip")
+
+
+def source_hash():
+    import hashlib
+    return hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per column-sum launch from the committed counter summary, or
+    None when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=3):
@@ -71,7 +101,87 @@ def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=3
                       f"{sec:.2f} s each; score + page max + cluster priority + top-k in float64 NumPy"}
 
 
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace -o bench -- "
+             "python3 bench.py --no-cpu-baseline --copy-calibration",
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE -o bench -- "
+                  "python3 bench.py --no-cpu-baseline --copy-calibration --steps 10 --warmup 2",
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE -o bench -- "
+                  "python3 bench.py --no-cpu-baseline --copy-calibration --steps 10 --warmup 2",
+}
+
+
+def summarize_profiles(out_dir):
+    """Writes the committed profile summaries from rocprofv3 CSV output.
+
+    profiles/kvs_mistral128k_kernel_stats.md: per-kernel average durations;
+    profiles/score_colsum_mistral128k_traffic.txt: HBM bytes per column-sum
+    launch from FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+    reads for the plain 256 MiB copy in the same run.
+    """
+    import csv
+    import statistics as st
+
+    def short(name):
+        for pre in ("void ", "kvs::(anonymous namespace)::"):
+            name = name.replace(pre, "")
+        return name.split("(")[0]
+
+    stats = list(csv.DictReader(open(os.path.join(out_dir, "trace", "bench_kernel_stats.csv"))))
+    lines = ["# Kernel durations, Mistral-7B GQA layer at L = 131072 (bench.py workload)", "",
+             "Command (repo root on the GPU box, cd /tmp first):", "",
+             "    " + PROFILE_COMMANDS["trace"], "",
+             "Calls cover the timed steps, the warm-up steps and the per-kernel event loops.", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", f"Kernel source sha256[:16] of score.hip: {source_hash()}", ""]
+    open(os.path.join(ROOT, "profiles", "kvs_mistral128k_kernel_stats.md"), "w").write(NL.join(lines))
+
+    def counter(name):
+        rows = list(csv.DictReader(open(os.path.join(out_dir, f"pmc_{name}", "bench_counter_collection.csv"))))
+        per = {}
+        for r in rows:
+            n = r["Kernel_Name"]
+            key = ("colsum" if "score_colsum" in n else "stats" if "score_stats" in n else
+                   "copy" if "copyBuffer" in n else None)
+            if key:
+                per.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: st.median(v) for k, v in per.items()}
+
+    fetch, write = counter("FETCH_SIZE"), counter("WRITE_SIZE")
+    copy_kib = (256 << 20) / 1024
+    f_fetch, f_write = copy_kib / fetch["copy"], copy_kib / write["copy"]
+    traffic = (fetch["colsum"] * f_fetch + write["colsum"] * f_write) * 1024
+    txt = [
+        "# HBM traffic of score_colsum_kernel (kvs_score column-sum pass), Mistral-7B GQA layer, L = 131072",
+        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, medians), each scaled by the same counter's",
+        "# reading for a plain 256 MiB device copy (torch copy_) in the same run.",
+        "# Commands (repo root on the GPU box, cd /tmp first):",
+        "#   " + PROFILE_COMMANDS["FETCH_SIZE"],
+        "#   " + PROFILE_COMMANDS["WRITE_SIZE"],
+        f"source_sha256_16: {source_hash()}",
+        f"copy_fetch_kib: {fetch['copy']:.1f}",
+        f"copy_write_kib: {write['copy']:.1f}",
+        f"fetch_scale: {f_fetch:.4f}",
+        f"write_scale: {f_write:.4f}",
+        f"colsum_fetch_kib: {fetch['colsum']:.1f}",
+        f"colsum_write_kib: {write['colsum']:.1f}",
+        f"stats_fetch_kib: {fetch['stats']:.1f}",
+        f"stats_write_kib: {write['stats']:.1f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        "",
+    ]
+    open(TRAFFIC_SUMMARY, "w").write(NL.join(txt))
+    print(NL.join(lines[-6:]))
+    print(NL.join(txt))
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -152,17 +262,44 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
-    # Kernel timing: the same steps again with HIP events on the stream around
-    # the statistics pass, the column-sum pass and the selection kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
-    torch.cuda.synchronize()
-    pass1 = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps   # stats + merge kernels
-    pass2 = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps   # column-sum kernel
-    select = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps  # page + cluster + top-k
+    # Kernel timing: HIP events on the stream around K back-to-back launches of
+    # each part (the K copies hold identical keys, so the statistics from the
+    # last step stay valid for every copy).
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def call(st):
+        if st != 0:
+            raise RuntimeError("libkvs call failed")
+
+    pass1 = timed(lambda j: call(lib.kvs_score(ra1, pQ, pKs[j % len(pKs)], pS, pws, ws_bytes, sp)))
+    pass2 = timed(lambda j: call(lib.kvs_score(ra2, pQ, pKs[j % len(pKs)], pS, pws, ws_bytes, sp)))
+
+    def select_part(j):
+        call(lib.kvs_pool_pages(pS, H_kv, n, L, kvs.RED_NONE, kvs.RED_NONE, 7, P, kvs.RED_MAX,
+                                None, ppage, parg_p, sp))
+        call(lib.kvs_cluster_priority(ppage, parg_p, H_kv, n_pages, P, n, theta_f, r, pprio, sp))
+        call(lib.kvs_topk(pS, H_kv, n, L, budget, pprio, n_forced, pidx, ptk, tk_bytes, sp))
+
+    select = timed(select_part)
     log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1+merge {pass1 * 1e3:.1f} us, "
         f"pass2 {pass2 * 1e3:.1f} us, select {select * 1e3:.1f} us")
+    copy_gbs = None
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(2):
+            dst.copy_(src)
+        copy_ms = timed(lambda j: dst.copy_(src))
+        copy_gbs = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
+        log(f"plain 256 MiB copy: {copy_ms * 1e3:.1f} us, {copy_gbs:.0f} GB/s read+write")
 
     # Algorithmic bytes of one column-sum launch: K once, Q once, S written once,
     # per-row constants (negligible) -> 2048 + 32 + ~2 bytes per token.
@@ -199,12 +336,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": dom_ms * 1e3,
             "mfma_frac": flops / (dom_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "step_event_us": {"score_pass1_merge": pass1 * 1e3, "score_pass2": pass2 * 1e3,
-                              "page_cluster_topk": select * 1e3},
+            "kernel_source_sha256_16": source_hash(),
+            "event_us": {"score_pass1_stats_and_merge": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
+                         "page_cluster_topk": select * 1e3},
+            "copy_256MiB_GBs": copy_gbs,
         },
     }
     if not args.no_cpu_baseline:
