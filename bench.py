@@ -203,7 +203,6 @@ def main():
     L, W, d_k, H_q, H_kv = ly.L, ly.W, ly.d_k, ly.H_q, ly.H_kv
     n = L - W
     P, theta, r, budget, n_forced = 16, 2e-3, 3, 1024, W
-    n_pages = (n + P - 1) // P
     Q = kvs.bf16_from_bits(ly.Q)
     K0 = kvs.bf16_from_bits(ly.K)
     Ks = [K0] + [K0.clone() for _ in range(max(0, args.rotate - 1))]
@@ -214,11 +213,10 @@ def main():
     ws_bytes = kvs.kvs_score_workspace(a1)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     S = torch.empty(H_kv, L, dtype=torch.float32, device="cuda")
-    page = torch.empty(H_kv, n_pages, dtype=torch.float32, device="cuda")
-    parg = torch.empty(H_kv, n_pages, dtype=torch.int32, device="cuda")
-    prio = torch.empty(H_kv, n, dtype=torch.uint8, device="cuda")
     idx = torch.empty(H_kv, budget + n_forced, dtype=torch.int32, device="cuda")
-    tk_bytes = lib.kvs_topk_workspace(H_kv, n, budget)
+    sel_args = kvs.select_args(budget=budget, n_forced=n_forced, cluster_P=P, cluster_theta=theta,
+                               cluster_r=r)
+    tk_bytes = lib.kvs_select_workspace(H_kv, n, budget)
     tk_ws = torch.empty(max(tk_bytes, 1), dtype=torch.uint8, device="cuda")
 
     stream = torch.cuda.current_stream()
@@ -226,10 +224,9 @@ def main():
     V = ctypes.c_void_p
     pQ, pS, pws = V(Q.data_ptr()), V(S.data_ptr()), V(ws.data_ptr())
     pKs = [V(k.data_ptr()) for k in Ks]
-    ppage, parg_p, pprio, pidx = V(page.data_ptr()), V(parg.data_ptr()), V(prio.data_ptr()), V(idx.data_ptr())
+    pidx = V(idx.data_ptr())
     ptk = V(tk_ws.data_ptr())
-    ra1, ra2 = ctypes.byref(a1), ctypes.byref(a2)
-    theta_f = ctypes.c_float(theta)
+    ra1, ra2, rsel = ctypes.byref(a1), ctypes.byref(a2), ctypes.byref(sel_args)
 
     def step(i, ev=None):
         pK = pKs[i % len(pKs)]
@@ -241,10 +238,7 @@ def main():
         st |= lib.kvs_score(ra2, pQ, pK, pS, pws, ws_bytes, sp)
         if ev is not None:
             ev[2].record(stream)
-        st |= lib.kvs_pool_pages(pS, H_kv, n, L, kvs.RED_NONE, kvs.RED_NONE, 7, P, kvs.RED_MAX,
-                                 None, ppage, parg_p, sp)
-        st |= lib.kvs_cluster_priority(ppage, parg_p, H_kv, n_pages, P, n, theta_f, r, pprio, sp)
-        st |= lib.kvs_topk(pS, H_kv, n, L, budget, pprio, n_forced, pidx, ptk, tk_bytes, sp)
+        st |= lib.kvs_select(pS, H_kv, n, L, rsel, pidx, ptk, tk_bytes, sp)
         if ev is not None:
             ev[3].record(stream)
         if st != 0:
@@ -282,10 +276,7 @@ def main():
     pass2 = timed(lambda j: call(lib.kvs_score(ra2, pQ, pKs[j % len(pKs)], pS, pws, ws_bytes, sp)))
 
     def select_part(j):
-        call(lib.kvs_pool_pages(pS, H_kv, n, L, kvs.RED_NONE, kvs.RED_NONE, 7, P, kvs.RED_MAX,
-                                None, ppage, parg_p, sp))
-        call(lib.kvs_cluster_priority(ppage, parg_p, H_kv, n_pages, P, n, theta_f, r, pprio, sp))
-        call(lib.kvs_topk(pS, H_kv, n, L, budget, pprio, n_forced, pidx, ptk, tk_bytes, sp))
+        call(lib.kvs_select(pS, H_kv, n, L, rsel, pidx, ptk, tk_bytes, sp))
 
     select = timed(select_part)
     log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1+merge {pass1 * 1e3:.1f} us, "

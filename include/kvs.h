@@ -154,12 +154,51 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
  * chosen indices in ascending order (original positions preserved), followed
  * by n, n+1, ..., n + n_forced - 1 ([ClusterAttn] window appended; [DELTA]
  * recency pages).  The result is unique for a given input.
- * 0 <= budget <= n.  Workspace from kvs_topk_workspace().
+ * 0 <= budget <= n, H <= 65535.
+ *
+ * Workspace: kvs_topk_workspace bytes (0 when n <= 16384: rows that short
+ * finish in one kernel), 16-byte aligned, owned by the caller, contents
+ * undefined on entry and on return.  It holds the per-part candidates of the
+ * two-stage select; calls that share one must not overlap in time.
  * ---------------------------------------------------------------------- */
 size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget);
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
                     const uint8_t* priority, int32_t n_forced, int32_t* idx,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_select - pooled or cluster-prioritised top-k in one call.
+ *
+ * The same selection as kvs_topk (order, ties, forced suffix, ascending
+ * output, workspace contract), ranked on a transform of the scores that is
+ * computed on the fly and never stored:
+ *  pool = KVS_RED_MAX / KVS_RED_MEAN: value = max / mean of S over
+ *    [t - r, t + r] clipped to [0, n), r = (pool_k - 1) / 2 ([CLAA] oracle
+ *    construction: 1-D pooling of the token scores, kernel 7, before top-k).
+ *    MAX is NaN when a term is NaN; MEAN sums left to right in float32.
+ *  cluster_P > 0: priority = 1 for tokens within cluster_r of the argmax
+ *    (lowest index) of a page of cluster_P tokens whose maximum is
+ *    >= cluster_theta; a page holding a NaN has no centre ([ClusterAttn]
+ *    method details: block-max centres, threshold, gathered neighbourhood,
+ *    then the best remaining tokens).  Values are the scores themselves.
+ * Pooling and clustering are exclusive (KVS_EUNSUPPORTED otherwise).
+ * Limits: pool_k odd, (pool_k - 1) / 2 <= KVS_SELECT_HALO_MAX;
+ * cluster_P + cluster_r <= KVS_SELECT_HALO_MAX; cluster_theta not NaN.
+ * ---------------------------------------------------------------------- */
+#define KVS_SELECT_HALO_MAX 1024
+typedef struct kvs_select_args {
+  int32_t budget;        /* tokens kept per row, 0 <= budget <= n            */
+  int32_t n_forced;      /* suffix n .. n + n_forced - 1 appended per row    */
+  int32_t pool;          /* KVS_RED_NONE, KVS_RED_MAX or KVS_RED_MEAN        */
+  int32_t pool_k;        /* odd pooling window (ignored for KVS_RED_NONE)    */
+  int32_t cluster_P;     /* 0: no clustering; > 0: page size of the centres  */
+  float cluster_theta;   /* centre threshold on the page maximum             */
+  int32_t cluster_r;     /* gather radius around each centre, >= 0           */
+} kvs_select_args;
+
+size_t kvs_select_workspace(int32_t H, int32_t n, int32_t budget);
+kvs_status kvs_select(const float* S, int32_t H, int32_t n, int64_t ld, const kvs_select_args* a,
+                      int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_block_union_pagetable - per-group KV page table from a 2-D block mask.

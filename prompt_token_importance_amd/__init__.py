@@ -51,6 +51,14 @@ class BlockSelectArgs(ctypes.Structure):
     ]
 
 
+class SelectArgs(ctypes.Structure):
+    _fields_ = [
+        ("budget", ctypes.c_int32), ("n_forced", ctypes.c_int32), ("pool", ctypes.c_int32),
+        ("pool_k", ctypes.c_int32), ("cluster_P", ctypes.c_int32),
+        ("cluster_theta", ctypes.c_float), ("cluster_r", ctypes.c_int32),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -66,6 +74,8 @@ def _load():
         "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvs_topk_workspace": (SZ, [I32, I32, I32]),
         "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, SZ, P]),
+        "kvs_select_workspace": (SZ, [I32, I32, I32]),
+        "kvs_select": (I32, [P, I32, I32, I64, ctypes.POINTER(SelectArgs), P, P, SZ, P]),
         "kvs_block_union_workspace": (SZ, [I32, I32, I32, I32]),
         "kvs_block_union_pagetable": (I32, [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]),
         "kvs_aggregate_workspace": (SZ, [I32]),
@@ -85,7 +95,8 @@ _lib = _load()
 
 EXPORTED = (
     "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_pool_pages",
-    "kvs_topk_workspace", "kvs_topk", "kvs_block_union_workspace", "kvs_block_union_pagetable",
+    "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
+    "kvs_block_union_workspace", "kvs_block_union_pagetable",
     "kvs_aggregate_workspace", "kvs_aggregate_layers", "kvs_cluster_priority",
     "kvs_block_select_workspace", "kvs_block_select",
 )
@@ -173,6 +184,7 @@ def kvs_pool_pages(S: torch.Tensor, n: int, *, head_reduce=RED_NONE, pool=RED_NO
 def kvs_topk(S: torch.Tensor, n: int, budget: int, *, priority: Optional[torch.Tensor] = None,
              n_forced: int = 0, ld: Optional[int] = None, idx: Optional[torch.Tensor] = None,
              ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int32 [H][budget + n_forced]: chosen indices ascending, then n .. n + n_forced - 1."""
     H = S.shape[0]
     ld = S.stride(0) if ld is None else ld
     if idx is None:
@@ -180,6 +192,26 @@ def kvs_topk(S: torch.Tensor, n: int, budget: int, *, priority: Optional[torch.T
     ws, nb = _workspace(int(_lib.kvs_topk_workspace(H, n, budget)), S.device, ws)
     _check(_lib.kvs_topk(_ptr(S), H, n, ld, budget, _ptr(priority), n_forced, _ptr(idx), _ptr(ws),
                          nb, _stream(stream)), "kvs_topk")
+    return idx
+
+
+def select_args(*, budget, n_forced=0, pool=RED_NONE, pool_k=7, cluster_P=0, cluster_theta=0.0,
+                cluster_r=0) -> SelectArgs:
+    return SelectArgs(budget=budget, n_forced=n_forced, pool=pool, pool_k=pool_k,
+                      cluster_P=cluster_P, cluster_theta=cluster_theta, cluster_r=cluster_r)
+
+
+def kvs_select(S: torch.Tensor, n: int, args: SelectArgs, *, ld: Optional[int] = None,
+               idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Pooled or cluster-prioritised top-k (same output as kvs_topk)."""
+    H = S.shape[0]
+    ld = S.stride(0) if ld is None else ld
+    if idx is None:
+        idx = torch.empty(H, args.budget + args.n_forced, dtype=torch.int32, device=S.device)
+    ws, nb = _workspace(int(_lib.kvs_select_workspace(H, n, args.budget)), S.device, ws)
+    _check(_lib.kvs_select(_ptr(S), H, n, ld, ctypes.byref(args), _ptr(idx), _ptr(ws), nb,
+                           _stream(stream)), "kvs_select")
     return idx
 
 

@@ -124,21 +124,54 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld, int3
 }
 
 size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget) {
-  if (H < 0 || n < 1 || budget < 0 || budget > n) return 0;
+  if (H < 0 || H > 65535 || n < 1 || budget < 0 || budget > n) return 0;
   return topk_ws_bytes(H, n, budget);
 }
+
+namespace {
+kvs_status check_select(const SelectCall& c, size_t ws_bytes) {
+  if (!c.S || !c.idx || c.H < 0 || c.n < 1 || c.ld < c.n) return KVS_EINVAL;
+  if (c.H > 65535) return KVS_EUNSUPPORTED;
+  if (c.budget < 0 || c.budget > c.n || c.n_forced < 0) return KVS_EINVAL;
+  if ((int64_t)c.n + c.n_forced > 0x7fffffff) return KVS_EINVAL;
+  if (((uintptr_t)c.S & 3u) || ((uintptr_t)c.idx & 3u)) return KVS_EINVAL;
+  if (c.pool != KVS_RED_NONE && c.pool != KVS_RED_MAX && c.pool != KVS_RED_MEAN) return KVS_EINVAL;
+  if (c.pool != KVS_RED_NONE && (c.pool_k < 1 || (c.pool_k & 1) == 0)) return KVS_EINVAL;
+  if (c.pool != KVS_RED_NONE && (c.pool_k - 1) / 2 > kSelHaloMax) return KVS_EUNSUPPORTED;
+  if (c.cluster_P < 0 || c.cluster_r < 0) return KVS_EINVAL;
+  if (c.cluster_P > 0 && isnan(c.cluster_theta)) return KVS_EINVAL;
+  if (c.cluster_P > 0 && (int64_t)c.cluster_P + c.cluster_r > kSelHaloMax) return KVS_EUNSUPPORTED;
+  if (c.cluster_P > 0 && c.pool != KVS_RED_NONE) return KVS_EUNSUPPORTED;
+  const size_t need = c.H > 0 ? topk_ws_bytes(c.H, c.n, c.budget) : 0;
+  if (need && (!c.ws || ws_bytes < need)) return KVS_EWORKSPACE;
+  if (need && !aligned16(c.ws)) return KVS_EINVAL;
+  return KVS_OK;
+}
+}  // namespace
 
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
                     const uint8_t* priority, int32_t n_forced, int32_t* idx, void* ws,
                     size_t ws_bytes, void* stream) {
-  if (!S || !idx || H < 0 || n < 1 || ld < n) return KVS_EINVAL;
-  if (budget < 0 || budget > n || n_forced < 0) return KVS_EINVAL;
-  if ((int64_t)n + n_forced > 0x7fffffff) return KVS_EINVAL;
-  if (((uintptr_t)S & 3u) || ((uintptr_t)idx & 3u)) return KVS_EINVAL;
-  const size_t need = topk_ws_bytes(H, n, budget);
-  if (need && (!ws || ws_bytes < need)) return KVS_EWORKSPACE;
-  if (need && !aligned16(ws)) return KVS_EINVAL;
-  return topk_run(S, H, n, ld, budget, priority, n_forced, idx, ws, as_stream(stream));
+  SelectCall c{S, H, n, ld, budget, n_forced, priority, KVS_RED_NONE, 0, 0, 0.f, 0, idx, ws};
+  const kvs_status st = check_select(c, ws_bytes);
+  if (st != KVS_OK) return st;
+  return select_run(c, as_stream(stream));
+}
+
+size_t kvs_select_workspace(int32_t H, int32_t n, int32_t budget) {
+  if (H < 0 || H > 65535 || n < 1 || budget < 0 || budget > n) return 0;
+  return topk_ws_bytes(H, n, budget);
+}
+
+kvs_status kvs_select(const float* S, int32_t H, int32_t n, int64_t ld, const kvs_select_args* a,
+                      int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!a) return KVS_EINVAL;
+  SelectCall c{S,          H,        n,         ld,           a->budget,        a->n_forced,
+               nullptr,    a->pool,  a->pool_k, a->cluster_P, a->cluster_theta, a->cluster_r,
+               idx,        ws};
+  const kvs_status st = check_select(c, ws_bytes);
+  if (st != KVS_OK) return st;
+  return select_run(c, as_stream(stream));
 }
 
 size_t kvs_block_union_workspace(int32_t H_q, int32_t H_kv, int32_t sub_group, int32_t n_kvb) {

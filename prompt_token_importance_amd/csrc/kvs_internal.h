@@ -24,6 +24,7 @@ struct ScorePlan {
   int n_split;      // splits of the key range per KV head
   int tiles_per_split;
   int head_batch;   // KV heads per (pass 1, merge, pass 2) round
+  int reverse;      // pass 2 visits tiles in the reverse of pass 1's order
   size_t ws_stats;  // bytes of per-split (max, sum) pairs
   size_t ws_rowc;   // bytes of per-row softmax constants
   size_t ws_total;
@@ -57,9 +58,24 @@ size_t aggregate_ws_bytes(int n);
 kvs_status aggregate_run(float* acc, const float* S, int H, int n, int64_t ld, int mode, int first,
                          void* ws, hipStream_t stream);
 
+// Top-k selection; the key transform is one of: none (optionally with a
+// caller priority array), pooling, or the cluster priority (cluster_P > 0).
+constexpr int kSelHaloMax = KVS_SELECT_HALO_MAX;
+struct SelectCall {
+  const float* S;
+  int H, n;
+  int64_t ld;
+  int budget, n_forced;
+  const uint8_t* priority;
+  int pool, pool_k;
+  int cluster_P;
+  float cluster_theta;
+  int cluster_r;
+  int32_t* idx;
+  void* ws;
+};
 size_t topk_ws_bytes(int H, int n, int budget);
-kvs_status topk_run(const float* S, int H, int n, int64_t ld, int budget, const uint8_t* prio,
-                    int n_forced, int32_t* idx, void* ws, hipStream_t stream);
+kvs_status select_run(const SelectCall& c, hipStream_t stream);
 
 size_t union_ws_bytes(int H_q, int H_kv, int sub_group, int n_kvb);
 kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_qb, int n_kvb,

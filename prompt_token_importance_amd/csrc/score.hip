@@ -48,6 +48,7 @@ constexpr float kPosInf = __builtin_inff();
 struct KArgs {
   ScoreLaunch p;
   int head_rows, rows_pad, n_split, tps, n_tiles, g0, min_vis;
+  int rev;   // pass 2 walks each wave's tiles last to first
 };
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t* ptr) {
@@ -663,13 +664,17 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   frag_offsets<D>(foff, lane);
   const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
   const int k = lane & 31;
+  // Pass 2 may walk the tiles in the reverse of pass 1's order, so that the
+  // keys pass 1 streamed last, the likeliest to still sit in the memory-side
+  // cache, are read first.
+  const auto tile_at = [&](int x) { return tb + wave + (a.rev ? nt - 1 - x : x) * kWaves; };
   if constexpr (MODE == 0) {
     constexpr int NA = Halves<NT>::NA, NB = Halves<NT>::NB;
     f32x16 accA[NA], accB[NB > 0 ? NB : 1];
     u32x4 f[D / 16];
     float part[16];
     for (int i = 0; i < S - 1 && i < nt; ++i)
-      issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
+      issue_tile<D>(ring[wave][i], kbase, a.p.kts, tile_at(i) * 32, L, lane);
     if (nt > 0) {
       wait_tile<D, S>(min(S - 2, nt - 1));
       read_frags<D / 16>(f, lds_addr(ring[wave][0]), foff);
@@ -679,8 +684,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
     for (int i = 0; i < nt; ++i) {
       if (i + S - 1 < nt)
         issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                      (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
-      const int t0 = (tb + wave + i * kWaves) * 32;
+                      tile_at(i + S - 1) * 32, L, lane);
+      const int t0 = tile_at(i) * 32;
       const uint32_t next_stage = lds_addr(ring[wave][(i + 1) % S]);
       const int ahead = i + 1 < nt ? min(S - 2, nt - 2 - i) : 0;
       if (t0 + 31 <= a.min_vis) {
@@ -740,13 +745,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
     }
   } else {
     for (int i = 0; i < S - 1 && i < nt; ++i)
-      issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, L, lane);
+      issue_tile<D>(ring[wave][i], kbase, a.p.kts, tile_at(i) * 32, L, lane);
     for (int i = 0; i < nt; ++i) {
       if (i + S - 1 < nt)
         issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                      (tb + wave + (i + S - 1) * kWaves) * 32, L, lane);
+                      tile_at(i + S - 1) * 32, L, lane);
       wait_tile<D, S>(min(S - 1, nt - 1 - i));
-      const int tile = tb + wave + i * kWaves;
+      const int tile = tile_at(i);
       f32x16 acc[NT];
       tile_logits<D, NT>(acc, ring[wave][i % S], q, foff);
       const int t0 = tile * 32;
@@ -814,6 +819,7 @@ kvs_status launch_rounds(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t 
     a.g0 = g0;
     const int64_t mv = p.q_pos0 < (int64_t)p.L - 1 ? p.q_pos0 : (int64_t)p.L - 1;
     a.min_vis = (int)mv;
+    a.rev = pl.reverse;
     dim3 grid(pl.n_split, nb);
     if (p.phase != 2) {
       hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
@@ -864,6 +870,7 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   (void)head_bytes;
   batch = batch < a->H_kv ? batch : a->H_kv;
   pl->head_batch = batch;
+  pl->reverse = env_int("KVS_SCORE_REVERSE", 1) != 0;
   // Splits of the key range: one 4-wave workgroup per CU (256 CUs), each
   // streaming a contiguous run of tiles, and at least 4 tiles (one per wave).
   const int target_wg = env_int("KVS_SCORE_TARGET_WG", 256);

@@ -1,51 +1,75 @@
-// Top-k selection with stable ties and a forced suffix (kvs_topk).
+// Top-k selection with stable ties and a forced suffix (kvs_topk, kvs_select).
 //
 // The CLAA page selects topk(scores, keep_rate) and keeps the chosen tokens at
-// their original positions ("Complete flow and cost"); the ClusterAttn page
-// ranks clustered tokens first and fills with the best remaining ones, then
-// appends the observation window ("Method details").  Order: priority desc,
-// value desc, index asc; the output lists the chosen indices ascending.
+// their original positions ("Complete flow and cost"), after a 1-D pooling of
+// the scores ("Oracle construction"); the ClusterAttn page ranks the tokens
+// gathered around block-max centres first and fills with the best remaining
+// ones, then appends the observation window ("Method details").  Order:
+// priority desc, value desc, index asc; the chosen indices come out ascending.
 //
-// Every row is split into chunks of kChunk elements, one 256-thread workgroup
-// per (chunk, row), so a launch covers the whole GPU even for 8 rows:
-//  1. Radix select over the 33-bit key (priority bit, order-preserving map of
-//     the float32 value) in three passes of 12, 11 and 10 bits.  A pass builds
-//     a per-workgroup LDS histogram of the digit among the elements matching
-//     the prefix found so far and adds it to the row's histogram in the
-//     workspace with integer atomics (exact, order-free).  The next kernel's
-//     workgroups each scan the finished histograms to fix the digits of the
-//     threshold key K* and how many K*-equal elements are needed: kernel
-//     boundaries order the passes, so no device-wide fence is needed.
-//  2. A count pass records, per chunk, the elements above K* and equal to K*.
-//  3. The output pass gives each chunk its offset from the counts of the
-//     chunks before it; a thread owns kEpt consecutive elements, and two
-//     workgroup prefix sums (K*-equal elements, then chosen elements) give
-//     every element its rank and output slot in index order: ties go to the
-//     lower index and the output is ascending.
-// Everything is integer work on the keys: the result is exact and unique.
+// The ranking key is 33 bits: the priority bit above an order-preserving map
+// of the float32 value.  Selection runs inside single 1024-thread workgroups,
+// so no workgroup ever waits for another and no device-wide hand-off is paid:
+//  stage 1  a row is cut into parts of kCap = 16384 elements, one workgroup
+//           per (part, row).  The workgroup computes the keys of its part in
+//           registers (16 per thread, optional transform from LDS-staged
+//           scores), finds its local top-`budget` by a three-digit radix
+//           select (12, 11, 10 bits) with LDS histograms, and writes the
+//           chosen (key, index) pairs in index order.  Every element of the
+//           global top-`budget` is in its part's local top-`budget`, because
+//           fewer than `budget` elements of that part precede it.
+//  stage 2  one workgroup per row runs the same radix select over the
+//           candidates of all parts (in registers when they fit in kCap,
+//           else re-read tile by tile) and writes the chosen indices.
+// Rows of at most kCap elements finish in stage 1.  Ties at the threshold key
+// K* go to the lower index: after K* and the number `need` of K*-equal
+// elements to take are fixed, a workgroup prefix sum ranks the K*-equal
+// elements in index order, and a second one gives every chosen element its
+// output slot, so the output is ascending and unique.
+#include <math.h>
+
 #include "kvs_internal.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kEpt = 16;                       // elements per thread per chunk
-constexpr int kChunk = kThreads * kEpt;        // 4096
-constexpr int kBins0 = 4096, kBins1 = 2048, kBins2 = 1024;
-constexpr int kShift[3] = {21, 10, 0};
+constexpr int kT = 1024;                    // threads per workgroup
+constexpr int kW = kT / 64;                 // waves per workgroup
+constexpr int kKpt = 16;                    // keys per thread
+constexpr int kCap = kT * kKpt;             // keys per workgroup tile (16384)
+constexpr int kStage = kCap + 2 * kSelHaloMax;   // staged scores of a part and its halo
+constexpr uint64_t kIdxMask = 0x7FFFFFFFull;
 
-// Per-row state in the workspace.
-struct RowState {
-  uint64_t prefix;   // fixed high bits of K*
-  uint32_t need;     // elements still to take at or below the prefix
-  uint32_t unused;
+enum Transform { kPlain = 0, kPool = 1, kCluster = 2 };
+
+template <int T>
+struct LdsWords {
+  static constexpr int value = T == kPlain ? 4096 : T == kPool ? kStage : 2 * kStage + 8;
 };
 
-struct Ws {
-  RowState* state;   // [H]
-  uint32_t* hist;    // [H][kBins0 + kBins1 + kBins2]
-  uint32_t* counts;  // [H][n_chunks][2]  (above K*, equal to K*)
+struct Params {
+  const float* S;
+  int64_t ld;
+  int n;
+  const uint8_t* prio;   // kPlain: optional uint8 [H][n]
+  int pool_max;          // kPool: 1 = MAX, 0 = MEAN
+  int pool_r;            // kPool: half window
+  int P;                 // kCluster: page size
+  float theta;           // kCluster: centre threshold
+  int r;                 // kCluster: gather radius
+  int budget, n_forced;
+  int vec;               // S rows 16-byte aligned: vector loads
+  int parts;             // stage-1 parts per row
+  int stride;            // candidate slots per part: min(budget, kCap)
+  int64_t cand_ld;       // candidate slots per row (multiple of kCap)
+  uint64_t* cand;        // [H][cand_ld] (key << 31 | index)
+  int32_t* idx;
+};
+
+struct Shared {
+  uint32_t w[kW];
+  uint64_t prefix;
+  uint32_t need;
 };
 
 __device__ __forceinline__ uint32_t ord_key(float v) {
@@ -55,200 +79,12 @@ __device__ __forceinline__ uint32_t ord_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t make_key(float v, uint8_t pr) {
+__device__ __forceinline__ uint64_t make_key(float v, bool pr) {
   return ((uint64_t)(pr ? 1u : 0u) << 32) | ord_key(v);
 }
 
-__device__ __forceinline__ uint32_t pass_bins(int p) {
-  return p == 0 ? kBins0 : p == 1 ? kBins1 : kBins2;
-}
-__device__ __forceinline__ uint32_t pass_offset(int p) {
-  return p == 0 ? 0 : p == 1 ? kBins0 : kBins0 + kBins1;
-}
-__device__ __forceinline__ uint64_t pass_mask(int p) {  // bits fixed before pass p
-  return p == 0 ? 0ull : p == 1 ? (0xFFFull << 21) : (0x7FFFFFull << 10);  // bits 21..32, 10..32
-}
-
-// Loads this thread's kEpt keys of the chunk; invalid slots get valid = false.
-__device__ __forceinline__ void load_keys(const float* x, const uint8_t* pr, int n, int c0,
-                                          uint64_t (&k)[kEpt], uint32_t& valid) {
-  float v[kEpt];
-  uint8_t q[kEpt];
-  valid = 0;
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e) {
-    const int i = c0 + (int)threadIdx.x * kEpt + e;
-    const bool ok = i < n;
-    v[e] = ok ? x[i] : 0.f;
-    q[e] = (ok && pr) ? pr[i] : (uint8_t)0;
-    valid |= ok ? (1u << e) : 0u;
-  }
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e) k[e] = make_key(v[e], q[e]);
-}
-
-__global__ __launch_bounds__(kThreads) void topk_zero_kernel(Ws ws, int H, int n_chunks) {
-  const int total = H * (kBins0 + kBins1 + kBins2);
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads)
-    ws.hist[i] = 0u;
-  if (blockIdx.x == 0)
-    for (int h = threadIdx.x; h < H; h += kThreads) ws.state[h] = RowState{0ull, 0u, 0u};
-  (void)n_chunks;
-}
-
-// Picks the digit of pass p from the row histogram of that pass (complete
-// because the pass ran in an earlier kernel): suffix scan from the top bin to
-// the bin holding the need-th candidate.  Every workgroup of a row computes
-// the same answer.  Returns the updated (prefix, need).
-__device__ void pick_digit(const uint32_t* __restrict__ gh, int p, uint64_t prefix, uint32_t need,
-                           uint32_t* h, uint32_t* scan, uint64_t* s_prefix, uint32_t* s_need) {
-  const uint32_t nb = pass_bins(p);
-  const uint32_t per = nb / kThreads;   // 16, 8 or 4 bins per thread
-  uint32_t vals[16];
-#pragma unroll
-  for (uint32_t b = 0; b < 16; ++b) vals[b] = b < per ? gh[threadIdx.x * per + b] : 0u;
-  uint32_t ls = 0;
-#pragma unroll
-  for (uint32_t b = 0; b < 16; ++b) {
-    if (b < per) h[threadIdx.x * per + b] = vals[b];
-    ls += vals[b];
-  }
-  scan[kThreads - 1 - threadIdx.x] = ls;  // position 0 = highest bins
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const uint32_t v = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
-    __syncthreads();
-    scan[threadIdx.x] += v;
-    __syncthreads();
-  }
-  const int rt = kThreads - 1 - threadIdx.x;
-  const uint32_t above = rt > 0 ? scan[rt - 1] : 0u;
-  if (above < need && need <= above + ls) {
-    uint32_t cum = above;
-    for (int b = (int)per - 1; b >= 0; --b) {
-      const uint32_t bin = threadIdx.x * per + b;
-      const uint32_t c = h[bin];
-      if (cum + c >= need) {
-        *s_prefix = prefix | ((uint64_t)bin << kShift[p]);
-        *s_need = need - cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
-}
-
-// Threshold key K* and the number of K*-equal elements to take, from the
-// histograms of passes 0 .. upto-1.
-__device__ void replay_digits(const Ws& ws, int row, int budget, int upto, uint32_t* h,
-                              uint32_t* scan, uint64_t* s_prefix, uint32_t* s_need) {
-  if (threadIdx.x == 0) {
-    *s_prefix = 0ull;
-    *s_need = (uint32_t)budget;
-  }
-  __syncthreads();
-  const uint32_t* gh = ws.hist + (size_t)row * (kBins0 + kBins1 + kBins2);
-  for (int p = 0; p < upto; ++p) {
-    const uint64_t prefix = *s_prefix;
-    const uint32_t need = *s_need;
-    __syncthreads();
-    pick_digit(gh + pass_offset(p), p, prefix, need, h, scan, s_prefix, s_need);
-  }
-}
-
-// Radix pass p: per-workgroup LDS histogram of digit p among the elements
-// matching the prefix fixed by passes 0 .. p-1, added into the row histogram
-// with integer atomics (exact).
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ S, int n,
-                                                             int64_t ld,
-                                                             const uint8_t* __restrict__ prio,
-                                                             int budget, int pass, Ws ws) {
-  __shared__ uint32_t h[kBins0];
-  __shared__ uint32_t scan[kThreads];
-  __shared__ uint64_t s_prefix;
-  __shared__ uint32_t s_need;
-  const int row = blockIdx.y;
-  const int c0 = blockIdx.x * kChunk;
-  const float* x = S + (int64_t)row * ld;
-  const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
-  uint64_t k[kEpt];
-  uint32_t valid;
-  load_keys(x, pr, n, c0, k, valid);
-  replay_digits(ws, row, budget, pass, h, scan, &s_prefix, &s_need);
-  const uint64_t prefix = s_prefix;
-  const uint32_t nb = pass_bins(pass);
-  const int shift = kShift[pass];
-  const uint64_t pmask = pass_mask(pass);
-  for (uint32_t b = threadIdx.x; b < nb; b += kThreads) h[b] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e)
-    if (((valid >> e) & 1u) && (k[e] & pmask) == prefix)
-      atomicAdd(&h[(uint32_t)(k[e] >> shift) & (nb - 1)], 1u);
-  __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)row * (kBins0 + kBins1 + kBins2) + pass_offset(pass);
-  for (uint32_t b = threadIdx.x; b < nb; b += kThreads)
-    if (h[b]) atomicAdd(&gh[b], h[b]);
-}
-
-__device__ __forceinline__ void block_counts(uint32_t a, uint32_t b, uint32_t* red,
-                                             uint32_t& ta, uint32_t& tb) {
-  // sums of a and b over the workgroup (fixed order)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int off = 32; off > 0; off >>= 1) {
-    a += __shfl_down(a, off);
-    b += __shfl_down(b, off);
-  }
-  if (lane == 0) {
-    red[2 * wave] = a;
-    red[2 * wave + 1] = b;
-  }
-  __syncthreads();
-  ta = tb = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    ta += red[2 * w];
-    tb += red[2 * w + 1];
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void topk_count_kernel(const float* __restrict__ S, int n,
-                                                              int64_t ld,
-                                                              const uint8_t* __restrict__ prio,
-                                                              int budget, Ws ws) {
-  __shared__ uint32_t red[2 * kWaves];
-  const int row = blockIdx.y;
-  const int c0 = blockIdx.x * kChunk;
-  const float* x = S + (int64_t)row * ld;
-  const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
-  __shared__ uint32_t h[kBins0];
-  __shared__ uint32_t scan[kThreads];
-  __shared__ uint64_t s_prefix;
-  __shared__ uint32_t s_need;
-  uint64_t k[kEpt];
-  uint32_t valid;
-  load_keys(x, pr, n, c0, k, valid);
-  replay_digits(ws, row, budget, 3, h, scan, &s_prefix, &s_need);
-  const uint64_t kstar = s_prefix;
-  if (blockIdx.x == 0 && threadIdx.x == 0) ws.state[row] = RowState{s_prefix, s_need, 0u};
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e)
-    if ((valid >> e) & 1u) {
-      gt += k[e] > kstar;
-      eq += k[e] == kstar;
-    }
-  uint32_t tg, te;
-  block_counts(gt, eq, red, tg, te);
-  if (threadIdx.x == 0) {
-    uint32_t* c = ws.counts + ((size_t)row * gridDim.x + blockIdx.x) * 2;
-    c[0] = tg;
-    c[1] = te;
-  }
-}
-
-// Exclusive prefix sum of one value per thread over the workgroup.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot) {
+// Exclusive prefix sum of one value per thread over the workgroup, and the total.
+__device__ __forceinline__ uint32_t scan_excl(uint32_t v, Shared& sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = v;
 #pragma unroll
@@ -256,106 +92,424 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot) 
     const uint32_t u = __shfl_up(inc, off);
     if (lane >= off) inc += u;
   }
-  if (lane == 63) wtot[wave] = inc;
+  if (lane == 63) sh.w[wave] = inc;
   __syncthreads();
   uint32_t before = 0;
+  total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) before += w < wave ? wtot[w] : 0u;
+  for (int w = 0; w < kW; ++w) {
+    const uint32_t x = sh.w[w];
+    before += w < wave ? x : 0u;
+    total += x;
+  }
   __syncthreads();
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_out_kernel(const float* __restrict__ S, int n,
-                                                            int64_t ld,
-                                                            const uint8_t* __restrict__ prio,
-                                                            int budget, int n_forced, Ws ws,
-                                                            int32_t* __restrict__ idx) {
-  __shared__ uint32_t wtot[kWaves];
-  __shared__ uint32_t s_base[2];
-  const int row = blockIdx.y;
-  const int chunk = blockIdx.x;
-  const int c0 = chunk * kChunk;
-  int32_t* out = idx + (int64_t)row * (budget + n_forced);
-  if (chunk == 0)
-    for (int i = threadIdx.x; i < n_forced; i += kThreads) out[budget + i] = n + i;
-  if (budget == 0) return;
-  const float* x = S + (int64_t)row * ld;
-  const uint8_t* pr = prio ? prio + (int64_t)row * n : nullptr;
-  const RowState st = ws.state[row];
-  const uint64_t kstar = st.prefix;
-  const uint32_t need_eq = st.need;
-  if (threadIdx.x == 0) {
-    // offsets from the chunks before this one
-    const uint32_t* c = ws.counts + (size_t)row * gridDim.x * 2;
-    uint32_t eq_before = 0, sel_before = 0;
-    for (int j = 0; j < chunk; ++j) {
-      const uint32_t g = c[2 * j], e = c[2 * j + 1];
-      const uint32_t take = eq_before >= need_eq ? 0u : min(e, need_eq - eq_before);
-      sel_before += g + take;
-      eq_before += e;
-    }
-    s_base[0] = eq_before;
-    s_base[1] = sel_before;
+__device__ __forceinline__ int pass_bins(int p) { return p == 0 ? 4096 : p == 1 ? 2048 : 1024; }
+__device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
+__device__ __forceinline__ uint64_t pass_mask(int p) {  // key bits fixed before pass p
+  return p == 0 ? 0ull : p == 1 ? (0xFFFull << 21) : (0x7FFFFFull << 10);
+}
+
+// Adds this thread's matching keys to the LDS histogram of pass p.
+__device__ __forceinline__ void hist_add(uint32_t* hist, int p, uint64_t prefix,
+                                         const uint64_t (&k)[kKpt], uint32_t valid) {
+  const int shift = pass_shift(p);
+  const uint32_t bmask = (uint32_t)pass_bins(p) - 1u;
+  const uint64_t pmask = pass_mask(p);
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e)
+    if (((valid >> e) & 1u) && (k[e] & pmask) == prefix)
+      atomicAdd(&hist[(uint32_t)(k[e] >> shift) & bmask], 1u);
+}
+
+// Fixes the digit of pass p from the complete histogram: the bin holding the
+// need-th candidate counted from the top.  Thread t owns the bins of rank
+// [t * per, (t + 1) * per) from the top.  Leaves (prefix, need) in sh.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, int p, uint64_t prefix,
+                                           uint32_t need, Shared& sh) {
+  const int nb = pass_bins(p), per = nb / kT;   // 4, 2 or 1 bins per thread
+  const int top = nb - (int)threadIdx.x * per;  // one past this thread's highest bin
+  uint32_t c[4];
+  uint32_t ls = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    c[b] = b < per ? hist[top - 1 - b] : 0u;
+    ls += c[b];
   }
-  uint64_t k[kEpt];
-  uint32_t valid;
-  load_keys(x, pr, n, c0, k, valid);
+  uint32_t total;
+  const uint32_t above = scan_excl(ls, sh, total);
+  if (above < need && need <= above + ls) {
+    uint32_t cum = above;
+    bool done = false;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < per && !done) {
+        if (cum + c[b] >= need) {
+          sh.prefix = prefix | ((uint64_t)(top - 1 - b) << pass_shift(p));
+          sh.need = need - cum;
+          done = true;
+        } else {
+          cum += c[b];
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Radix select over keys held in registers: the threshold key K* and the
+// number of K*-equal elements to take so that exactly `budget` are chosen.
+__device__ __forceinline__ void radix_regs(const uint64_t (&k)[kKpt], uint32_t valid,
+                                           uint32_t budget, uint32_t* hist, Shared& sh,
+                                           uint64_t& kstar, uint32_t& need_eq) {
+  uint64_t prefix = 0;
+  uint32_t need = budget;
+  for (int p = 0; p < 3; ++p) {
+    for (int b = threadIdx.x; b < pass_bins(p); b += kT) hist[b] = 0u;
+    __syncthreads();
+    hist_add(hist, p, prefix, k, valid);
+    __syncthreads();
+    pick_digit(hist, p, prefix, need, sh);
+    prefix = sh.prefix;
+    need = sh.need;
+    __syncthreads();
+  }
+  kstar = prefix;
+  need_eq = need;
+}
+
+// Chosen elements of this thread (bit e), ranked in element order: all keys
+// above K*, then K*-equal keys while the running rank is below need_eq.
+// `eq_base` counts the K*-equal elements of earlier tiles.
+__device__ __forceinline__ uint32_t choose(const uint64_t (&k)[kKpt], uint32_t valid,
+                                           uint64_t kstar, uint32_t need_eq, uint32_t eq_base,
+                                           Shared& sh, uint32_t& eq_total) {
   uint32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int e = 0; e < kEpt; ++e) {
+  for (int e = 0; e < kKpt; ++e) {
     const bool ok = (valid >> e) & 1u;
     gt |= (ok && k[e] > kstar) ? (1u << e) : 0u;
     eq |= (ok && k[e] == kstar) ? (1u << e) : 0u;
   }
-  // rank of this thread's first K*-equal element among the row's K*-equal elements
-  uint32_t run_eq = block_excl_scan((uint32_t)__popc(eq), wtot) + s_base[0];
+  uint32_t rank = scan_excl((uint32_t)__popc(eq), sh, eq_total) + eq_base;
   uint32_t sel = gt;
 #pragma unroll
-  for (int e = 0; e < kEpt; ++e)
+  for (int e = 0; e < kKpt; ++e)
     if ((eq >> e) & 1u) {
-      if (run_eq < need_eq) sel |= 1u << e;
-      ++run_eq;
+      if (rank < need_eq) sel |= 1u << e;
+      ++rank;
     }
-  uint32_t pos = block_excl_scan((uint32_t)__popc(sel), wtot) + s_base[1];
-  const int i0 = c0 + (int)threadIdx.x * kEpt;
-#pragma unroll
-  for (int e = 0; e < kEpt; ++e)
-    if ((sel >> e) & 1u) out[pos++] = i0 + e;
+  return sel;
 }
 
-size_t ws_state_bytes(int H) { return align_up((size_t)H * sizeof(RowState), kWsAlign); }
-size_t ws_hist_bytes(int H) {
-  return align_up((size_t)H * (kBins0 + kBins1 + kBins2) * sizeof(uint32_t), kWsAlign);
+// Stages the scores [w0, w1) of a row in LDS (coalesced) and synchronizes.
+__device__ __forceinline__ void stage(const float* x, int w0, int w1, float* xs) {
+  for (int i = threadIdx.x; i < w1 - w0; i += kT) xs[i] = x[w0 + i];
+  __syncthreads();
 }
-int n_chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
+
+// Keys of this thread's elements i0 + e (i0 = p0 + 16 * tid) of the part
+// [p0, p1); bit e of `valid` tells whether i0 + e < p1.  Leaves `smem` free.
+template <int T>
+__device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int p1, uint32_t* smem,
+                                          uint64_t (&k)[kKpt], uint32_t& valid) {
+  const float* x = s.S + (int64_t)row * s.ld;
+  const int i0 = p0 + (int)threadIdx.x * kKpt;
+  valid = 0;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) valid |= (i0 + e < p1) ? (1u << e) : 0u;
+  if constexpr (T == kPlain) {
+    float v[kKpt];
+    if (s.vec && i0 + kKpt <= p1) {
+      const float4* p4 = reinterpret_cast<const float4*>(x + i0);
+#pragma unroll
+      for (int q = 0; q < kKpt / 4; ++q) {
+        const float4 f = p4[q];
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+    } else {
+      // clamped (always in-bounds) loads without branches; masked by `valid`
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e) v[e] = x[min(i0 + e, s.n - 1)];
+    }
+    if (s.prio) {
+      const uint8_t* pr = s.prio + (int64_t)row * s.n;
+      uint8_t q[kKpt];
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e) q[e] = pr[min(i0 + e, s.n - 1)];
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e) k[e] = make_key(v[e], q[e] != 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e) k[e] = make_key(v[e], false);
+    }
+  } else if constexpr (T == kPool) {
+    // pooled value over [t - r, t + r] clipped to [0, n): max (NaN if any term
+    // is NaN) or the left-to-right float32 mean of the in-range terms
+    float* xs = reinterpret_cast<float*>(smem);
+    const int rp = s.pool_r;
+    const int w0 = max(p0 - rp, 0), w1 = min(p1 + rp, s.n);
+    stage(x, w0, w1, xs);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      const int t = i0 + e;
+      float y = 0.f;
+      if (t < p1) {
+        const int lo = max(t - rp, 0), hi = min(t + rp, s.n - 1);
+        if (s.pool_max) {
+          float m = -__builtin_inff();
+          bool nan = false;
+          for (int u = lo; u <= hi; ++u) {
+            const float z = xs[u - w0];
+            nan |= z != z;
+            m = fmaxf(m, z);
+          }
+          y = nan ? __builtin_nanf("") : m;
+        } else {
+          float acc = 0.f;
+          for (int u = lo; u <= hi; ++u) acc += xs[u - w0];
+          y = acc / (float)(hi - lo + 1);
+        }
+      }
+      k[e] = make_key(y, false);
+    }
+    __syncthreads();
+  } else {
+    // cluster priority: a token is gathered when it lies within r of the
+    // argmax (lowest index) of a page of P tokens whose maximum is >= theta;
+    // a page holding a NaN has no centre.  Pages [qa, qb] hold every centre
+    // that can reach the part.
+    const int P = s.P, r = s.r;
+    const int qa = max(p0 - r, 0) / P;
+    const int qb = min(p1 - 1 + r, s.n - 1) / P;
+    const int w0 = qa * P, w1 = min((qb + 1) * P, s.n);
+    float* xs = reinterpret_cast<float*>(smem);
+    int* cen = reinterpret_cast<int*>(smem + kStage);
+    stage(x, w0, w1, xs);
+    for (int j = threadIdx.x; j <= qb - qa; j += kT) {
+      const int a0 = (qa + j) * P, a1 = min(a0 + P, s.n);
+      float best = xs[a0 - w0];
+      int arg = a0;
+      bool nan = best != best;
+      for (int t = a0 + 1; t < a1; ++t) {
+        const float z = xs[t - w0];
+        nan |= z != z;
+        if (z > best) {
+          best = z;
+          arg = t;
+        }
+      }
+      cen[j] = (!nan && best >= s.theta) ? arg : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      const int t = i0 + e;
+      bool pr = false;
+      float v = 0.f;
+      if (t < p1) {
+        v = xs[t - w0];
+        const int ua = max(t - r, 0) / P, ub = min(t + r, s.n - 1) / P;
+        for (int u = ua; u <= ub; ++u) {
+          const int cc = cen[u - qa];
+          pr |= cc >= 0 && t - cc <= r && cc - t <= r;
+        }
+      }
+      k[e] = make_key(v, pr);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void write_forced(const Params& s, int32_t* out) {
+  for (int i = threadIdx.x; i < s.n_forced; i += kT) out[s.budget + i] = s.n + i;
+}
+
+// Stage 1: local top-`budget` of one part.  With a single part per row this is
+// the final answer (indices), else the chosen (key, index) candidates.
+template <int T>
+__global__ __launch_bounds__(kT) void topk_part_kernel(Params s) {
+  __shared__ uint32_t smem[LdsWords<T>::value];
+  __shared__ Shared sh;
+  const int row = blockIdx.y, part = blockIdx.x;
+  const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
+  const int m = p1 - p0;
+  uint64_t k[kKpt];
+  uint32_t valid;
+  part_keys<T>(s, row, p0, p1, smem, k, valid);
+  const uint32_t keep = (uint32_t)min(s.budget, m);
+  uint32_t sel, tot;
+  if (keep == (uint32_t)m) {
+    sel = valid;
+  } else {
+    uint64_t kstar;
+    uint32_t need_eq;
+    radix_regs(k, valid, keep, smem, sh, kstar, need_eq);
+    sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
+  }
+  uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+  const int i0 = p0 + (int)threadIdx.x * kKpt;
+  if (s.parts == 1) {
+    int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if ((sel >> e) & 1u) out[pos++] = i0 + e;
+    write_forced(s, out);
+  } else {
+    uint64_t* c = s.cand + (int64_t)row * s.cand_ld + (int64_t)part * s.stride;
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if ((sel >> e) & 1u) c[pos++] = (k[e] << 31) | (uint64_t)(uint32_t)(i0 + e);
+  }
+}
+
+// Candidate keys of tile [t0, t0 + kCap) of a row: slot i belongs to part
+// i / stride and holds a candidate when i % stride < that part's count.
+__device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, int64_t t0,
+                                          uint64_t (&k)[kKpt], uint32_t (&ix)[kKpt],
+                                          uint32_t& valid) {
+  const int64_t i0 = t0 + (int64_t)threadIdx.x * kKpt;
+  const uint4* p4 = reinterpret_cast<const uint4*>(c + i0);
+  valid = 0;
+#pragma unroll
+  for (int q = 0; q < kKpt / 2; ++q) {
+    const uint4 v = p4[q];
+    const uint64_t a = ((uint64_t)v.y << 32) | v.x, b = ((uint64_t)v.w << 32) | v.z;
+    k[2 * q] = a >> 31;
+    k[2 * q + 1] = b >> 31;
+    ix[2 * q] = (uint32_t)(a & kIdxMask);
+    ix[2 * q + 1] = (uint32_t)(b & kIdxMask);
+  }
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const int64_t i = i0 + e;
+    const int part = (int)(i / s.stride);
+    const int slot = (int)(i - (int64_t)part * s.stride);
+    const int m = part < s.parts ? min(kCap, s.n - part * kCap) : 0;
+    valid |= slot < min(s.budget, m) ? (1u << e) : 0u;
+  }
+}
+
+// Stage 2: the final selection among the candidates of all parts of a row.
+__global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
+  __shared__ uint32_t hist[4096];
+  __shared__ Shared sh;
+  const int row = blockIdx.x;
+  const uint64_t* c = s.cand + (int64_t)row * s.cand_ld;
+  int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
+  const int64_t count = (int64_t)s.parts * s.stride;
+  uint64_t k[kKpt];
+  uint32_t ix[kKpt];
+  uint32_t valid;
+  uint32_t tot;
+  if (count <= kCap) {
+    cand_keys(s, c, 0, k, ix, valid);
+    uint64_t kstar;
+    uint32_t need_eq;
+    radix_regs(k, valid, (uint32_t)s.budget, hist, sh, kstar, need_eq);
+    const uint32_t sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
+    uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if ((sel >> e) & 1u) out[pos++] = (int32_t)ix[e];
+  } else {
+    // more candidates than registers hold: every pass re-reads them by tiles
+    uint64_t prefix = 0;
+    uint32_t need = (uint32_t)s.budget;
+    for (int p = 0; p < 3; ++p) {
+      for (int b = threadIdx.x; b < pass_bins(p); b += kT) hist[b] = 0u;
+      __syncthreads();
+      for (int64_t t0 = 0; t0 < count; t0 += kCap) {
+        cand_keys(s, c, t0, k, ix, valid);
+        hist_add(hist, p, prefix, k, valid);
+      }
+      __syncthreads();
+      pick_digit(hist, p, prefix, need, sh);
+      prefix = sh.prefix;
+      need = sh.need;
+      __syncthreads();
+    }
+    uint32_t eq_base = 0, sel_base = 0;
+    for (int64_t t0 = 0; t0 < count; t0 += kCap) {
+      cand_keys(s, c, t0, k, ix, valid);
+      uint32_t eq_tot;
+      const uint32_t sel = choose(k, valid, prefix, need, eq_base, sh, eq_tot);
+      uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot) + sel_base;
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e)
+        if ((sel >> e) & 1u) out[pos++] = (int32_t)ix[e];
+      eq_base += eq_tot;
+      sel_base += tot;
+    }
+  }
+  write_forced(s, out);
+}
+
+// budget == 0: only the forced suffix.
+__global__ __launch_bounds__(256) void topk_forced_kernel(int n, int n_forced,
+                                                          int32_t* __restrict__ idx) {
+  int32_t* out = idx + (int64_t)blockIdx.y * n_forced;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_forced; i += gridDim.x * 256)
+    out[i] = n + i;
+}
+
+int parts_of(int n) { return (n + kCap - 1) / kCap; }
+int stride_of(int budget) { return budget < kCap ? budget : kCap; }
+int64_t cand_ld_of(int n, int budget) {
+  const int64_t slots = (int64_t)parts_of(n) * stride_of(budget);
+  return (slots + kCap - 1) / kCap * kCap;
+}
+
+template <int T>
+void launch(const Params& s, int H, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_part_kernel<T>, dim3(s.parts, H), dim3(kT), 0, stream, s);
+  if (s.parts > 1) hipLaunchKernelGGL(topk_merge_kernel, dim3(H), dim3(kT), 0, stream, s);
+}
 
 }  // namespace
 
-size_t topk_ws_bytes(int H, int n, int) {
-  return ws_state_bytes(H) + ws_hist_bytes(H) +
-         align_up((size_t)H * n_chunks_of(n) * 2 * sizeof(uint32_t), kWsAlign);
+size_t topk_ws_bytes(int H, int n, int budget) {
+  if (budget <= 0 || parts_of(n) == 1) return 0;
+  return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
 }
 
-kvs_status topk_run(const float* S, int H, int n, int64_t ld, int budget, const uint8_t* prio,
-                    int n_forced, int32_t* idx, void* wsp, hipStream_t stream) {
-  if (H == 0) return KVS_OK;
-  char* base = static_cast<char*>(wsp);
-  Ws ws;
-  ws.state = reinterpret_cast<RowState*>(base);
-  ws.hist = reinterpret_cast<uint32_t*>(base + ws_state_bytes(H));
-  ws.counts = reinterpret_cast<uint32_t*>(base + ws_state_bytes(H) + ws_hist_bytes(H));
-  const int nc = n_chunks_of(n);
-  const dim3 grid(nc, H);
-  if (budget > 0) {
-    hipLaunchKernelGGL(topk_zero_kernel, dim3(min(64, H * 4)), dim3(kThreads), 0, stream, ws, H, nc);
-    for (int p = 0; p < 3; ++p)
-      hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
-                         p, ws);
-    hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
-                       ws);
+kvs_status select_run(const SelectCall& c, hipStream_t stream) {
+  if (c.H == 0) return KVS_OK;
+  if (c.budget == 0) {
+    if (c.n_forced > 0)
+      hipLaunchKernelGGL(topk_forced_kernel, dim3((c.n_forced + 255) / 256, c.H), dim3(256), 0,
+                         stream, c.n, c.n_forced, c.idx);
+    return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
   }
-  hipLaunchKernelGGL(topk_out_kernel, grid, dim3(kThreads), 0, stream, S, n, ld, prio, budget,
-                     n_forced, ws, idx);
+  Params s;
+  s.S = c.S;
+  s.ld = c.ld;
+  s.n = c.n;
+  s.prio = c.priority;
+  s.pool_max = c.pool == KVS_RED_MAX;
+  s.pool_r = c.pool == KVS_RED_NONE ? 0 : (c.pool_k - 1) / 2;
+  s.P = c.cluster_P;
+  s.theta = c.cluster_theta;
+  s.r = c.cluster_r;
+  s.budget = c.budget;
+  s.n_forced = c.n_forced;
+  s.vec = ((uintptr_t)c.S % 16 == 0) && (c.ld % 4 == 0);
+  s.parts = parts_of(c.n);
+  s.stride = stride_of(c.budget);
+  s.cand_ld = cand_ld_of(c.n, c.budget);
+  s.cand = static_cast<uint64_t*>(c.ws);
+  s.idx = c.idx;
+  if (c.cluster_P > 0)
+    launch<kCluster>(s, c.H, stream);
+  else if (c.pool != KVS_RED_NONE)
+    launch<kPool>(s, c.H, stream);
+  else
+    launch<kPlain>(s, c.H, stream);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 

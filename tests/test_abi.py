@@ -108,3 +108,30 @@ def test_other_entry_points_reject(kvs):
     assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 24, None) == -2
     a = kvs.block_select_args(Lq=64, L=1 << 20, d_k=128, H_q=4, H_kv=1, q_pos0=64, block=64)
     assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 30, None) == -2
+
+
+def test_select_rejects(kvs):
+    lib = kvs.library()
+    P = ctypes.c_void_p
+
+    def call(ws=P(256), nb=1 << 24, n=100000, ld=100000, **kw):
+        a = kvs.select_args(**{"budget": 10, **kw})
+        return lib.kvs_select(P(16), 2, n, ld, ctypes.byref(a), P(16), ws, nb, None)
+
+    assert call(pool=kvs.RED_MAX, pool_k=6) == -1            # even pooling window
+    assert call(pool=kvs.RED_SUM, pool_k=7) == -1            # SUM is not a pooling mode
+    assert call(pool=kvs.RED_MAX, pool_k=2051) == -2         # halo beyond the LDS stage
+    assert call(cluster_P=16, cluster_r=-1) == -1
+    assert call(cluster_P=16, cluster_theta=float("nan"), cluster_r=3) == -1
+    assert call(cluster_P=1000, cluster_r=100) == -2         # P + r beyond the halo
+    assert call(cluster_P=16, cluster_r=3, pool=kvs.RED_MAX, pool_k=7) == -2
+    assert call(budget=100001) == -1
+    assert call(ld=99999) == -1
+    assert call(nb=16) == -3                                  # workspace too small
+    assert call(ws=P(264)) == -1                              # workspace misaligned
+    assert lib.kvs_select(P(16), 2, 100, 100, None, P(16), P(256), 1 << 24, None) == -1
+    assert lib.kvs_topk(P(16), 1, 100000, 100000, 10, None, 0, P(16), P(256), 16, None) == -3
+    assert lib.kvs_select_workspace(8, 131040, 1024) == lib.kvs_topk_workspace(8, 131040, 1024)
+    assert lib.kvs_select_workspace(8, 131040, 1024) > 0
+    assert lib.kvs_select_workspace(8, 16384, 100) == 0      # one part: no candidates stored
+    assert lib.kvs_select_workspace(8, 100, 101) == 0        # budget > n

@@ -191,3 +191,112 @@ def test_deterministic_selection(kvs):
     a = kvs.kvs_topk(dev(x), 131040, 1024, n_forced=32).cpu().numpy()
     b = kvs.kvs_topk(dev(x), 131040, 1024, n_forced=32).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ fused select
+SELECT_POOL_CASES = [
+    # H, n, budget, n_forced, k, levels
+    (1, 496, 64, 16, 7, 0),            # Tiny: max-pool 7 + window
+    (8, 32736, 1024, 32, 7, 0),        # Llama 32K prefix
+    (8, 131040, 1024, 32, 7, 0),       # Mistral 128K prefix
+    (3, 4097, 700, 3, 9, 6),           # ragged tail, ties, NaN / inf
+    (2, 5, 2, 0, 7, 0),                # window wider than the row
+    (2, 9000, 4500, 0, 1, 4),          # k = 1: plain top-k
+    (1, 20000, 100, 0, 2049, 0),       # widest supported window
+]
+
+
+@pytest.mark.parametrize("H,n,budget,nf,k,levels", SELECT_POOL_CASES)
+def test_select_max_pool_bit_exact(kvs, H, n, budget, nf, k, levels):
+    """Max-pooled values are exact float32 copies: the selection is unique."""
+    x = synth.score_array(6000 + n + k, H, n, levels=levels, signed=levels > 0,
+                          with_zeros=levels > 0)
+    if levels > 0:
+        x[0, 17] = np.nan
+        x[-1, n // 2] = np.float32(np.inf)
+        x[-1, n // 3] = np.float32(-np.inf)
+    a = kvs.select_args(budget=budget, n_forced=nf, pool=kvs.RED_MAX, pool_k=k)
+    got = kvs.kvs_select(dev(x), n, a)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.pool(x, oracle.RED_MAX, k), budget, None, nf)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("H,n,budget,k", [(8, 32736, 1024, 7), (2, 3001, 1500, 5), (1, 70, 9, 31)])
+def test_select_mean_pool(kvs, H, n, budget, k):
+    """float32 left-to-right means against fp64 ones: decided elements agree."""
+    from helpers import assert_topk_parity
+    x = synth.score_array(6100 + n, H, n)
+    a = kvs.select_args(budget=budget, n_forced=4, pool=kvs.RED_MEAN, pool_k=k)
+    got = kvs.kvs_select(dev(x), n, a).cpu().numpy()
+    assert np.array_equal(got[:, budget:], np.tile(np.arange(n, n + 4), (H, 1)))
+    assert_topk_parity(got, oracle.pool(x, oracle.RED_MEAN, k), budget, rel=1e-5)
+
+
+SELECT_CLUSTER_CASES = [
+    # H, n, budget, n_forced, P, theta, r, scale
+    (8, 131040, 1024, 32, 16, 2e-3, 3, 1e-3),   # Mistral 128K shape; maxima straddle theta
+    (2, 1000, 100, 0, 16, 1.5, 3, 1.0),
+    (1, 100, 10, 3, 7, 0.0, 0, 1.0),
+    (3, 5000, 400, 0, 16, 3.0, 20, 1.0),
+    (2, 9000, 300, 0, 1, 2.0, 2, 1.0),          # every token a page
+    (2, 12000, 2000, 0, 24, 2.5, 1000, 1.0),    # P + r at the halo limit
+    (1, 4096, 4096, 0, 16, 1.0, 3, 1.0),        # budget = n
+]
+
+
+@pytest.mark.parametrize("H,n,budget,nf,P,theta,r,scale", SELECT_CLUSTER_CASES)
+def test_select_cluster_bit_exact(kvs, H, n, budget, nf, P, theta, r, scale):
+    x = synth.score_array(6200 + n + r, H, n) * np.float32(scale)
+    x[0, min(5, n - 1)] = np.nan                   # its page has no centre
+    a = kvs.select_args(budget=budget, n_forced=nf, cluster_P=P, cluster_theta=theta, cluster_r=r)
+    got = kvs.kvs_select(dev(x), n, a)
+    torch.cuda.synchronize()
+    z, arg = oracle.pages(x, P, oracle.RED_MAX)
+    prio = oracle.cluster_priority(z, arg, n, float(np.float32(theta)), r)
+    want = oracle.topk(x, budget, prio, nf)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def test_select_workspace_reuse(kvs):
+    """One workspace, sized for the largest call, serves calls of different
+    shapes, budgets and transforms back to back (stale candidates of an
+    earlier call never leak into a later one)."""
+    calls = [
+        (8, 131040, dict(budget=1024, n_forced=32, cluster_P=16, cluster_theta=2e-3, cluster_r=3)),
+        (3, 50000, dict(budget=77)),
+        (8, 32736, dict(budget=1024, pool=kvs.RED_MAX, pool_k=7)),
+        (1, 1, dict(budget=1)),
+        (5, 131040, dict(budget=0, n_forced=7)),
+        (8, 131040, dict(budget=131040)),                   # every part keeps everything
+        (2, 131040, dict(budget=3000)),                     # candidates exceed one tile
+        (8, 131040, dict(budget=1024, n_forced=32)),
+    ]
+    nbytes = max(kvs.library().kvs_select_workspace(H, n, kw["budget"]) for H, n, kw in calls)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    for i, (H, n, kw) in enumerate(calls):
+        x = synth.score_array(6300 + i, H, n, levels=0 if i % 2 else 40) * np.float32(1e-3)
+        got = kvs.kvs_select(dev(x), n, kvs.select_args(**kw), ws=ws)
+        torch.cuda.synchronize()
+        if kw.get("cluster_P"):
+            z, arg = oracle.pages(x, 16, oracle.RED_MAX)
+            prio = oracle.cluster_priority(z, arg, n, float(np.float32(2e-3)), 3)
+            want = oracle.topk(x, kw["budget"], prio, kw.get("n_forced", 0))
+        elif kw.get("pool"):
+            want = oracle.topk(oracle.pool(x, oracle.RED_MAX, 7), kw["budget"], None, 0)
+        else:
+            want = oracle.topk(x, kw["budget"], None, kw.get("n_forced", 0))
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"call {i}")
+
+
+def test_select_matches_three_call_path(kvs):
+    """The fused cluster select equals page max -> cluster priority -> top-k."""
+    H, n, P, theta, r = 8, 131040, 16, 2e-3, 3
+    x = dev(synth.score_array(6400, H, n) * np.float32(1e-3))
+    _, page, parg = kvs.kvs_pool_pages(x, n, P=P, page_reduce=kvs.RED_MAX, want_pooled=False)
+    prio = kvs.kvs_cluster_priority(page, parg, P, n, theta, r)
+    a = kvs.kvs_topk(x, n, 1024, priority=prio, n_forced=32)
+    b = kvs.kvs_select(x, n, kvs.select_args(budget=1024, n_forced=32, cluster_P=P,
+                                             cluster_theta=theta, cluster_r=r))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
