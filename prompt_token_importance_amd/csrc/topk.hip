@@ -12,8 +12,9 @@
 // so no workgroup ever waits for another and no device-wide hand-off is paid:
 //  stage 1  a row is cut into parts of kCap = 16384 elements, one workgroup
 //           per (part, row).  The workgroup computes the keys of its part in
-//           registers (16 per thread, optional transform from LDS-staged
-//           scores), finds its local top-`budget` by a three-digit radix
+//           registers (16 per thread; the optional pooling or cluster
+//           transform reads a 48-score register window per thread, or
+//           LDS-staged scores for wide windows), finds its local top-`budget` by a three-digit radix
 //           select (12, 11, 10 bits) with LDS histograms, and writes the
 //           chosen (key, index) pairs in index order.  Every element of the
 //           global top-`budget` is in its part's local top-`budget`, because
@@ -21,6 +22,7 @@
 //  stage 2  one workgroup per row runs the same radix select over the
 //           candidates of all parts (in registers when they fit in kCap,
 //           else re-read tile by tile) and writes the chosen indices.
+// Each radix pass has its own LDS histogram; one wave fixes the digit.
 // Rows of at most kCap elements finish in stage 1.  Ties at the threshold key
 // K* go to the lower index: after K* and the number `need` of K*-equal
 // elements to take are fixed, a workgroup prefix sum ranks the K*-equal
@@ -42,9 +44,11 @@ constexpr uint64_t kIdxMask = 0x7FFFFFFFull;
 
 enum Transform { kPlain = 0, kPool = 1, kCluster = 2 };
 
+constexpr int kHistWords = 4096 + 2048 + 1024;   // one histogram per radix pass
+
 template <int T>
 struct LdsWords {
-  static constexpr int value = T == kPlain ? 4096 : T == kPool ? kStage : 2 * kStage + 8;
+  static constexpr int value = T == kPlain ? kHistWords : T == kPool ? kStage : 2 * kStage + 8;
 };
 
 struct Params {
@@ -70,6 +74,7 @@ struct Shared {
   uint32_t w[kW];
   uint64_t prefix;
   uint32_t need;
+  uint32_t all_eq;   // the last digit's bin is taken whole: every K*-equal key is chosen
 };
 
 __device__ __forceinline__ uint32_t ord_key(float v) {
@@ -108,6 +113,7 @@ __device__ __forceinline__ uint32_t scan_excl(uint32_t v, Shared& sh, uint32_t& 
 
 __device__ __forceinline__ int pass_bins(int p) { return p == 0 ? 4096 : p == 1 ? 2048 : 1024; }
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
+__device__ __forceinline__ int pass_offset(int p) { return p == 0 ? 0 : p == 1 ? 4096 : 6144; }
 __device__ __forceinline__ uint64_t pass_mask(int p) {  // key bits fixed before pass p
   return p == 0 ? 0ull : p == 1 ? (0xFFFull << 21) : (0x7FFFFFull << 10);
 }
@@ -124,9 +130,10 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, int p, uint64_t prefix,
       atomicAdd(&hist[(uint32_t)(k[e] >> shift) & bmask], 1u);
 }
 
-// Fixes the digit of pass p from the complete histogram: the bin holding the
+// Fixes the digit of pass p from its complete histogram: the bin holding the
 // need-th candidate counted from the top.  Thread t owns the bins of rank
-// [t * per, (t + 1) * per) from the top.  Leaves (prefix, need) in sh.
+// [t * per, (t + 1) * per) from the top; a workgroup prefix sum of the
+// per-thread counts finds the owner.  Leaves (prefix, need, all_eq) in sh.
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, int p, uint64_t prefix,
                                            uint32_t need, Shared& sh) {
   const int nb = pass_bins(p), per = nb / kT;   // 4, 2 or 1 bins per thread
@@ -149,6 +156,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int p, uint64_t
         if (cum + c[b] >= need) {
           sh.prefix = prefix | ((uint64_t)(top - 1 - b) << pass_shift(p));
           sh.need = need - cum;
+          sh.all_eq = need - cum == c[b];
           done = true;
         } else {
           cum += c[b];
@@ -161,20 +169,21 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int p, uint64_t
 
 // Radix select over keys held in registers: the threshold key K* and the
 // number of K*-equal elements to take so that exactly `budget` are chosen.
+// `hist` holds kHistWords words: the three pass histograms, cleared together.
 __device__ __forceinline__ void radix_regs(const uint64_t (&k)[kKpt], uint32_t valid,
                                            uint32_t budget, uint32_t* hist, Shared& sh,
                                            uint64_t& kstar, uint32_t& need_eq) {
+  for (int b = threadIdx.x; b < kHistWords; b += kT) hist[b] = 0u;
+  __syncthreads();
   uint64_t prefix = 0;
   uint32_t need = budget;
   for (int p = 0; p < 3; ++p) {
-    for (int b = threadIdx.x; b < pass_bins(p); b += kT) hist[b] = 0u;
+    uint32_t* h = hist + pass_offset(p);
+    hist_add(h, p, prefix, k, valid);
     __syncthreads();
-    hist_add(hist, p, prefix, k, valid);
-    __syncthreads();
-    pick_digit(hist, p, prefix, need, sh);
+    pick_digit(h, p, prefix, need, sh);
     prefix = sh.prefix;
     need = sh.need;
-    __syncthreads();
   }
   kstar = prefix;
   need_eq = need;
@@ -193,6 +202,10 @@ __device__ __forceinline__ uint32_t choose(const uint64_t (&k)[kKpt], uint32_t v
     gt |= (ok && k[e] > kstar) ? (1u << e) : 0u;
     eq |= (ok && k[e] == kstar) ? (1u << e) : 0u;
   }
+  if (sh.all_eq) {
+    eq_total = 0;   // not needed: every K*-equal element is chosen
+    return gt | eq;
+  }
   uint32_t rank = scan_excl((uint32_t)__popc(eq), sh, eq_total) + eq_base;
   uint32_t sel = gt;
 #pragma unroll
@@ -206,8 +219,108 @@ __device__ __forceinline__ uint32_t choose(const uint64_t (&k)[kKpt], uint32_t v
 
 // Stages the scores [w0, w1) of a row in LDS (coalesced) and synchronizes.
 __device__ __forceinline__ void stage(const float* x, int w0, int w1, float* xs) {
+#pragma unroll 6
   for (int i = threadIdx.x; i < w1 - w0; i += kT) xs[i] = x[w0 + i];
   __syncthreads();
+}
+
+constexpr int kWin = 16;   // halo of the register window on each side
+
+// Scores x[i0 - 16 .. i0 + 32) of a row into registers (w[j] = x[i0 - 16 + j])
+// with 16-byte loads.  Requires n % 4 == 0 and 16-byte aligned rows; a float4
+// that lies outside [0, n) is read from a clamped in-range position instead,
+// and the caller masks every position outside [0, n).
+__device__ __forceinline__ void load_window(const Params& s, const float* x, int i0,
+                                            float (&w)[kKpt + 2 * kWin]) {
+  const float4* p4 = reinterpret_cast<const float4*>(x);
+  const int q0 = (i0 - kWin) / 4, qmax = s.n / 4 - 1;
+#pragma unroll
+  for (int q = 0; q < (kKpt + 2 * kWin) / 4; ++q) {
+    const float4 f = p4[min(max(q0 + q, 0), qmax)];
+    w[4 * q] = f.x;
+    w[4 * q + 1] = f.y;
+    w[4 * q + 2] = f.z;
+    w[4 * q + 3] = f.w;
+  }
+}
+
+// Pooling from the register window: element e's terms are w[e + 16 + o],
+// |o| <= r <= kWin, clipped to [0, n) and taken left to right.  Terms outside
+// [0, n) are replaced once by the identity of the reduction (-inf / +0, which
+// leaves a left-to-right float32 sum unchanged) and NaNs are tracked in a bit
+// mask, so the inner loop is a plain max or add.  R is r when known at
+// compile time, else kWin with a mask on |o|.
+template <int R, bool MAX>
+__device__ __forceinline__ void pool_regs(const Params& s, int i0, float (&w)[kKpt + 2 * kWin],
+                                          uint64_t (&k)[kKpt]) {
+  const int r = R < kWin ? R : s.pool_r;
+  uint64_t nanm = 0;
+#pragma unroll
+  for (int j = 0; j < kKpt + 2 * kWin; ++j) {
+    const int pos = i0 - kWin + j;
+    const bool in = pos >= 0 && pos < s.n;
+    nanm |= (uint64_t)(in && w[j] != w[j]) << j;
+    w[j] = in ? w[j] : (MAX ? -__builtin_inff() : 0.f);
+  }
+  const uint64_t span = (2ull << (2 * r)) - 1ull;   // 2r + 1 ones
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const int t = i0 + e;
+    float y = MAX ? -__builtin_inff() : 0.f;
+#pragma unroll
+    for (int o = -R; o <= R; ++o) {
+      const float z = w[e + kWin + o];
+      const bool use = R < kWin || (o >= -r && o <= r);
+      if (MAX)
+        y = use ? fmaxf(y, z) : y;
+      else
+        y = use ? y + z : y;
+    }
+    if (MAX) {
+      if ((nanm >> (e + kWin - r)) & span) y = __builtin_nanf("");
+    } else {
+      const int lo = max(t - r, 0), hi = min(t + r, s.n - 1);
+      y = y / (float)(hi - lo + 1);
+    }
+    k[e] = make_key(t < s.n ? y : 0.f, false);
+  }
+}
+
+// Cluster priority with pages of 16 tokens and radius r <= kWin from the
+// register window: i0 is page-aligned, so the centres that can reach this
+// thread's tokens lie in the previous, own and next pages.
+__device__ __forceinline__ void cluster_regs(const Params& s, int i0,
+                                             const float (&w)[kKpt + 2 * kWin],
+                                             uint64_t (&k)[kKpt]) {
+  int cen[3];
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    const int a0 = i0 + 16 * (g - 1);
+    float best = w[16 * g];
+    int arg = a0;
+    bool nan = best != best;
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+      const float z = w[16 * g + j];
+      const bool in = a0 + j < s.n;
+      nan |= in && z != z;
+      if (in && z > best) {
+        best = z;
+        arg = a0 + j;
+      }
+    }
+    const bool page = a0 >= 0 && a0 < s.n;
+    cen[g] = (page && !nan && best >= s.theta) ? arg : -1;
+  }
+  const int r = s.r;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const int t = i0 + e;
+    bool pr = false;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) pr |= cen[g] >= 0 && t - cen[g] <= r && cen[g] - t <= r;
+    k[e] = make_key(t < s.n ? w[e + kWin] : 0.f, pr);
+  }
 }
 
 // Keys of this thread's elements i0 + e (i0 = p0 + 16 * tid) of the part
@@ -251,6 +364,15 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
   } else if constexpr (T == kPool) {
     // pooled value over [t - r, t + r] clipped to [0, n): max (NaN if any term
     // is NaN) or the left-to-right float32 mean of the in-range terms
+    if (s.pool_r <= kWin && s.vec && s.n % 4 == 0) {
+      float w[kKpt + 2 * kWin];
+      load_window(s, x, i0, w);
+      if (s.pool_r == 3)
+        s.pool_max ? pool_regs<3, true>(s, i0, w, k) : pool_regs<3, false>(s, i0, w, k);
+      else
+        s.pool_max ? pool_regs<kWin, true>(s, i0, w, k) : pool_regs<kWin, false>(s, i0, w, k);
+      return;
+    }
     float* xs = reinterpret_cast<float*>(smem);
     const int rp = s.pool_r;
     const int w0 = max(p0 - rp, 0), w1 = min(p1 + rp, s.n);
@@ -284,6 +406,12 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
     // argmax (lowest index) of a page of P tokens whose maximum is >= theta;
     // a page holding a NaN has no centre.  Pages [qa, qb] hold every centre
     // that can reach the part.
+    if (s.P == 16 && s.r <= kWin && s.vec && s.n % 4 == 0) {
+      float w[kKpt + 2 * kWin];
+      load_window(s, x, i0, w);
+      cluster_regs(s, i0, w, k);
+      return;
+    }
     const int P = s.P, r = s.r;
     const int qa = max(p0 - r, 0) / P;
     const int qb = min(p1 - 1 + r, s.n - 1) / P;
@@ -397,7 +525,7 @@ __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, in
 
 // Stage 2: the final selection among the candidates of all parts of a row.
 __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
-  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t hist[kHistWords];
   __shared__ Shared sh;
   const int row = blockIdx.x;
   const uint64_t* c = s.cand + (int64_t)row * s.cand_ld;
@@ -419,20 +547,20 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
       if ((sel >> e) & 1u) out[pos++] = (int32_t)ix[e];
   } else {
     // more candidates than registers hold: every pass re-reads them by tiles
+    for (int b = threadIdx.x; b < kHistWords; b += kT) hist[b] = 0u;
+    __syncthreads();
     uint64_t prefix = 0;
     uint32_t need = (uint32_t)s.budget;
     for (int p = 0; p < 3; ++p) {
-      for (int b = threadIdx.x; b < pass_bins(p); b += kT) hist[b] = 0u;
-      __syncthreads();
+      uint32_t* h = hist + pass_offset(p);
       for (int64_t t0 = 0; t0 < count; t0 += kCap) {
         cand_keys(s, c, t0, k, ix, valid);
-        hist_add(hist, p, prefix, k, valid);
+        hist_add(h, p, prefix, k, valid);
       }
       __syncthreads();
-      pick_digit(hist, p, prefix, need, sh);
+      pick_digit(h, p, prefix, need, sh);
       prefix = sh.prefix;
       need = sh.need;
-      __syncthreads();
     }
     uint32_t eq_base = 0, sel_base = 0;
     for (int64_t t0 = 0; t0 < count; t0 += kCap) {

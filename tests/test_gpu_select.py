@@ -203,6 +203,10 @@ SELECT_POOL_CASES = [
     (2, 5, 2, 0, 7, 0),                # window wider than the row
     (2, 9000, 4500, 0, 1, 4),          # k = 1: plain top-k
     (1, 20000, 100, 0, 2049, 0),       # widest supported window
+    (2, 8, 3, 0, 7, 0),                # register window wider than the row
+    (3, 12, 5, 1, 31, 0),              # widest register-window pooling
+    (2, 48, 10, 0, 33, 3),             # beyond the register window: staged path
+    (2, 16388, 500, 0, 7, 5),          # second part of four elements
 ]
 
 
@@ -222,7 +226,8 @@ def test_select_max_pool_bit_exact(kvs, H, n, budget, nf, k, levels):
     np.testing.assert_array_equal(got.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("H,n,budget,k", [(8, 32736, 1024, 7), (2, 3001, 1500, 5), (1, 70, 9, 31)])
+@pytest.mark.parametrize("H,n,budget,k", [(8, 32736, 1024, 7), (2, 3001, 1500, 5), (1, 70, 9, 31),
+                                          (2, 16, 4, 31), (3, 32768, 100, 33), (2, 40000, 900, 9)])
 def test_select_mean_pool(kvs, H, n, budget, k):
     """float32 left-to-right means against fp64 ones: decided elements agree."""
     from helpers import assert_topk_parity
@@ -242,6 +247,10 @@ SELECT_CLUSTER_CASES = [
     (2, 9000, 300, 0, 1, 2.0, 2, 1.0),          # every token a page
     (2, 12000, 2000, 0, 24, 2.5, 1000, 1.0),    # P + r at the halo limit
     (1, 4096, 4096, 0, 16, 1.0, 3, 1.0),        # budget = n
+    (2, 20, 5, 0, 16, 0.5, 3, 1.0),             # partial last page, one thread
+    (1, 48, 7, 2, 16, 1.0, 16, 1.0),            # widest register-window radius
+    (3, 16388, 500, 0, 16, 2.0, 3, 1.0),        # second part of four elements
+    (2, 16390, 500, 0, 16, 2.0, 3, 1.0),        # n % 4 != 0: staged path
 ]
 
 
