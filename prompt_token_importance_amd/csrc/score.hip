@@ -11,15 +11,23 @@
 // Design (MI355X / CDNA4):
 //  * One 32 x 32 x 16 bf16 MFMA tile = 32 keys (M) x 32 query rows (N); the
 //    contraction runs over d_k.  All R = rows_pad (<= 128) query rows of the
-//    group stay in VGPRs as B operands for the whole kernel; each wave streams
-//    its own 32-key tiles of K straight from HBM into A operands with 16-byte
-//    loads, one tile ahead.  A lane owns the contiguous d_k/2 half-row of one
-//    key, so every byte of K fetched is used and no LDS staging is needed.
-//  * Pass 1 keeps, per lane and query row, an online (max, sum of exp2)
-//    over the keys it sees, in log2 units (x = s * scale * log2 e).  Lane
-//    halves and waves are merged in LDS and written per split of the key range;
-//    a small merge kernel folds the splits by log-sum-exp into one constant
-//    b_r = m_r + log2 Z_r per row (+inf for padding rows).
+//    group stay in AGPRs as B operands for the whole kernel.  One 4-wave
+//    workgroup per CU; each wave streams its own 32-key tiles of K through a
+//    4-stage LDS ring with direct-to-LDS 16-byte loads (every load instruction
+//    reads one contiguous 1 KiB run; rows are XOR-swizzled so the fragment
+//    reads are bank-conflict free).
+//  * Full tiles run a software pipeline: while the matrix cores compute tile
+//    j's logits (all N-tiles, k-major, fragments in AGPRs), the VALU works on
+//    tile j-1's logits, two of them per MFMA slot; tile j+3's loads are spread
+//    over the first slots and tile j+1's fragments are read in the later
+//    ones.  Causally masked and ragged tiles take a separate exact path.
+//  * Pass 1 keeps, per lane and query row, sums of exp2(x - m) over the keys
+//    it sees, in log2 units (x = s * scale * log2 e), against a max m fixed
+//    from the wave's first tile, so the pipeline carries no branch; a wave
+//    whose sums overflow [0, 2^64] redoes its tiles with the exact online
+//    update.  Lane halves and waves are merged in LDS and written per split
+//    of the key range; a small merge kernel folds the splits by log-sum-exp
+//    into one constant b_r = m_r + log2 Z_r per row (+inf for padding rows).
 //  * Pass 2 recomputes the tile, forms p = exp2(x - b_r) (no division), adds
 //    the rows a lane holds, transposes the 32 x 32 tile of partial sums
 //    through a per-wave LDS buffer and adds across lanes.  Every output element
@@ -41,7 +49,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStride = 36;  // floats per row of the LDS transpose buffers
-constexpr int kStages = 4;   // K tiles per wave in the LDS ring (kStages - 1 in flight)
+constexpr int kStages = 4;   // K tiles per wave in the LDS ring
+static_assert((kStages & (kStages - 1)) == 0, "ring stages are indexed with a mask");
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
@@ -161,6 +170,30 @@ __device__ __forceinline__ void read_frags(u32x4 (&f)[KS], uint32_t base, const 
   for (int s = 0; s < KS; ++s) ds_read_b128<0>(f[s], base + off[s]);
 }
 
+// The same reads with AGPR destinations: the pipelined loops keep the K
+// fragments, which only ever feed MFMAs, in the AGPR file next to Q.
+template <int OFF>
+__device__ __forceinline__ void ds_read_b128_a(u32x4& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(v) : "v"(addr), "n"(OFF));
+}
+
+template <int KS>
+__device__ __forceinline__ void read_frags_a(u32x4 (&f)[KS], uint32_t base,
+                                             const uint32_t (&off)[KS]) {
+#pragma unroll
+  for (int s = 0; s < KS; ++s) ds_read_b128_a<0>(f[s], base + off[s]);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm_a(u32x4 (&v)[N]) {
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]), "+a"(v[4]), "+a"(v[5]),
+                   "+a"(v[6]), "+a"(v[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]));
+}
+
 // Waits for the tile issued `ahead` tiles before the newest one.
 template <int D, int S>
 __device__ __forceinline__ void wait_tile(int ahead) {
@@ -243,61 +276,51 @@ __device__ __forceinline__ int key_of(int i, int hl) { return 8 * (i >> 2) + 4 *
 
 // MFMA through inline asm with the query fragment (B operand) read straight
 // from AGPRs: the 128 query-fragment registers of a wave live in the AGPR
-// file, leaving the VGPRs to the accumulators and the softmax work.
+// file, leaving the VGPRs to the accumulators and the softmax work.  The
+// compiler inserts no hazard wait states around inline asm, and its register
+// copies (v_accvgpr_write, v_mov) may write an operand right before the MFMA;
+// a VALU write followed by an MFMA read of the same register needs two wait
+// states, so every asm MFMA carries its own "s_nop 1".
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kf), "a"(qa));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kf), "a"(qa));
 }
 __device__ __forceinline__ void mfma_zero(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(kf), "a"(qa));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(kf), "a"(qa));
+}
+__device__ __forceinline__ void mfma_acc_a(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(kf), "a"(qa));
+}
+__device__ __forceinline__ void mfma_zero_a(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "a"(kf), "a"(qa));
 }
 // Wait states between an MFMA writing VGPRs and VALU instructions reading
 // them (the compiler does not track dependencies through inline asm).
 __device__ __forceinline__ void mfma_result_guard() {
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 }
-
-// One pipeline phase: the NX*KS MFMAs of N-tiles XLO.. of the current tile
-// (fragments f) interleaved, 1 MFMA : EPM elements, with the softmax work on
-// the 16*NY logits of N-tiles YLO.. of the previous batch (accY).  Each slot is
-// fenced so the scheduler keeps the interleave.  WORK(T, i) is called for
-// every logit (T < NY, i < 16).
-template <int D, int NT, int XLO, int NX, int NY, typename Work>
-__device__ __forceinline__ void phase(f32x16 (&accX)[NX > 0 ? NX : 1], const u32x4 (&f)[D / 16],
-                                      const bf16x8 (&q)[NT][D / 16], Work&& work) {
-  constexpr int KS = D / 16;
-  constexpr int M = KS * NX;
-  constexpr int E = 16 * NY;
-  constexpr int EPM = M > 0 ? (E + M - 1) / M : E;
-  constexpr int SLOTS = M > 0 ? M : 1;
-  mfma_result_guard();
-#pragma unroll
-  for (int k = 0; k < SLOTS; ++k) {
-    if constexpr (M > 0) {
-      const int ss = k / (NX > 0 ? NX : 1), T = k % (NX > 0 ? NX : 1);
-      if (ss == 0)
-        mfma_zero(accX[T], f[ss], q[XLO + T][ss]);
-      else
-        mfma_acc(accX[T], f[ss], q[XLO + T][ss]);
-    }
-#pragma unroll
-    for (int u = 0; u < EPM; ++u) {
-      const int e = k * EPM + u;
-      if (e < E) work(e / 16, e % 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+// The same wait states, naming the accumulators they protect, so no read of
+// them can be scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void mfma_guard(f32x16 (&acc)[N]) {
+  static_assert(N >= 1 && N <= 4, "one to four accumulators");
+  if constexpr (N == 1)
+    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0])::"memory");
+  else if constexpr (N == 2)
+    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0]), "+v"(acc[1])::"memory");
+  else if constexpr (N == 3)
+    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])::"memory");
+  else
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])::"memory");
 }
-
-// ------------------------------------------------------------------ half-tile pipeline
-// A 32-key tile is processed as two halves of its N-tiles (query-row blocks):
-// group 0 = N-tiles [0, NA), group 1 = [NA, NT).  While the matrix cores run
-// the MFMAs of one half, the VALU works on the other half's logits from the
-// previous batch, so MFMA and exp/sum work overlap inside a single wave.
-template <int NT>
-struct Halves {
-  static constexpr int NA = (NT + 1) / 2;
-  static constexpr int NB = NT - NA;
-};
+// x * c + nb as an inline-asm FMA: it reads the MFMA result register in
+// place, after the preceding wait states (volatile asm keeps program order),
+// and pins the logit's exp/sum work to its MFMA slot.
+__device__ __forceinline__ float fma_after_guard(float x, float c, float nb) {
+  float y;
+  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(y) : "v"(x), "s"(c), "v"(nb));
+  return y;
+}
 
 template <int D, int NT, int LO, int N>
 __device__ __forceinline__ void mfma_part(f32x16 (&acc)[N > 0 ? N : 1], const u32x4 (&f)[D / 16],
@@ -315,64 +338,18 @@ __device__ __forceinline__ void mfma_part(f32x16 (&acc)[N > 0 ? N : 1], const u3
   }
 }
 
-// Asks the scheduler to interleave the preceding block as (1 MFMA, V VALU) x M,
-// so the VALU work issues while the matrix core runs the MFMAs.
-template <int M, int V>
-__device__ __forceinline__ void interleave_mfma_valu() {
-  if constexpr (M > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-    interleave_mfma_valu<M - 1, V>();
-  }
-}
-
-// Fast-path partial sums of exp2(x*c - m) for query rows LO .. LO+N-1 of a
-// full tile (no masking); returns whether some lane left [0, 2^64].
-template <int NT, int LO, int N>
-__device__ __forceinline__ bool stats_sums(const f32x16 (&acc)[N > 0 ? N : 1], const float (&m)[NT],
-                                           float c, float (&sum)[N > 0 ? N : 1]) {
-  bool bad = false;
-  if constexpr (N > 0) {
+template <int D, int NT>
+__device__ __forceinline__ void mfma_all_a(f32x16 (&acc)[NT], const u32x4 (&f)[D / 16],
+                                           const bf16x8 (&q)[NT][D / 16]) {
 #pragma unroll
-    for (int T = 0; T < N; ++T) {
-      float sa = 0.f, sb = 0.f;
+  for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        sa += ex2(fmaf(acc[T][i], c, -m[LO + T]));
-        sb += ex2(fmaf(acc[T][i + 1], c, -m[LO + T]));
-      }
-      sum[T] = sa + sb;
-      bad |= !(sum[T] <= 0x1p64f);
+    for (int T = 0; T < NT; ++T) {
+      if (s == 0)
+        mfma_zero_a(acc[T], f[s], q[T][s]);
+      else
+        mfma_acc_a(acc[T], f[s], q[T][s]);
     }
-  }
-  return bad;
-}
-
-// Commits fast-path sums, or (wave-uniform, rare) recomputes the rows against
-// their exact tile max.
-template <int NT, int LO, int N>
-__device__ __forceinline__ void stats_commit(const f32x16 (&acc)[N > 0 ? N : 1], float (&m)[NT],
-                                             float (&z)[NT], float c, const float (&sum)[N > 0 ? N : 1],
-                                             bool bad) {
-  if constexpr (N > 0) {
-    if (!__any(bad)) {
-#pragma unroll
-      for (int T = 0; T < N; ++T) z[LO + T] += sum[T];
-      return;
-    }
-#pragma unroll
-    for (int T = 0; T < N; ++T) {
-      float mx = acc[T][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[T][i]);
-      const float mn = fmaxf(m[LO + T], mx * c);
-      float s2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s2 += ex2(fmaf(acc[T][i], c, -mn));
-      z[LO + T] = z[LO + T] * ex2(m[LO + T] - mn) + s2;
-      m[LO + T] = mn;
-    }
-  }
 }
 
 // Probabilities of a full tile (no masking) summed over rows LO .. LO+N-1.
@@ -478,8 +455,94 @@ __device__ __forceinline__ void probs_part(const f32x16 (&acc)[N > 0 ? N : 1], f
 }
 
 // ------------------------------------------------------------------ pass 1
+// One 16-byte-per-lane load instruction (1 KiB) of a tile: chunk jj of the KS
+// that issue_tile issues together.
+template <int D>
+__device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint16_t* kbase, int64_t kts,
+                                            int t0, int L, int lane, int jj) {
+  constexpr int CR = D / 8;
+  constexpr int RPI = 64 / CR;
+  const int p = lane % CR;
+  const int tr = jj * RPI + lane / CR;
+  int t = t0 + tr;
+  t = t < L ? t : L - 1;
+  const int c = p ^ (tr % CR);
+  __builtin_amdgcn_global_load_lds(kbase + (int64_t)t * kts + 8 * c,
+                                   (lds_void*)(stage + jj * 1024), 16, 0, 0);
+}
+
+// Slot schedule of a steady-state step with M MFMA slots and KS load/read
+// instructions per tile: the loads of a new tile go out over the first half
+// of the slots, then the wait for the next tile and its fragment reads.
+template <int M, int KS>
+struct StepSlots {
+  static constexpr int kWait = M / 2;
+  static constexpr int issue(int jj) { return (jj * (M / 2)) / KS; }
+  static constexpr int read(int jj) { return M / 2 + (jj * (M - M / 2)) / KS; }
+};
+
+// One step of the full-tile pipeline: the KS*NT MFMAs of the current tile
+// (fragments fc) into accC, k-major so consecutive MFMAs use different
+// accumulators, interleaved EPM logits per MFMA with WORK(T, i, x) on the
+// previous tile's logits accP (x = accP[T][i]; WORK reads it with
+// fma_after_guard, so the read stays behind the result guard).  ISSUE: the loads of tile `issue_t0` into `issue_stage`
+// are spread over the first slots.  NEXT: the next tile is waited for (WAITN
+// loads may stay outstanding) and its fragments are read into fn.
+template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work>
+__device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT],
+                                          const u32x4 (&fc)[D / 16], u32x4 (&fn)[D / 16],
+                                          const bf16x8 (&q)[NT][D / 16], uint8_t* issue_stage,
+                                          const uint16_t* kbase, int64_t kts, int issue_t0, int L,
+                                          int lane, uint32_t next_stage,
+                                          const uint32_t (&foff)[D / 16], Work&& work) {
+  constexpr int KS = D / 16;
+  constexpr int M = KS * NT;
+  constexpr int EPM = 16 / KS;
+  using SL = StepSlots<M, KS>;
+  // accP's last MFMAs may still be in flight: the wait states come first, and
+  // every read of accP below is pinned after this asm (volatile asm keeps
+  // program order)
+  mfma_result_guard();
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    const int s = k / NT, T = k % NT;
+    if (s == 0)
+      mfma_zero_a(accC[T], fc[s], q[T][s]);
+    else
+      mfma_acc_a(accC[T], fc[s], q[T][s]);
+#pragma unroll
+    for (int u = 0; u < EPM; ++u) {
+      const int e = k * EPM + u;
+      work(e / 16, e % 16, accP[e / 16][e % 16]);
+    }
+    if constexpr (ISSUE) {
+#pragma unroll
+      for (int jj = 0; jj < KS; ++jj)
+        if (SL::issue(jj) == k) issue_chunk<D>(issue_stage, kbase, kts, issue_t0, L, lane, jj);
+    }
+    if constexpr (NEXT) {
+      if (k == SL::kWait) wait_vm<WAITN>();
+#pragma unroll
+      for (int jj = 0; jj < KS; ++jj)
+        if (SL::read(jj) == k) ds_read_b128_a<0>(fn[jj], next_stage + foff[jj]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (NEXT) wait_lgkm_a<KS>(fn);
+}
+
+// Pass 1: per (row, split) online (max, sum of exp2) of the logits.
+// Full tiles (no causal masking) run a software pipeline: while the matrix
+// cores compute tile j's logits, the VALU sums tile j-1's exponentials
+// against a running max m that was set exactly from the wave's first tile
+// and never changes in the pipeline, so the sums need no branch.  A lane
+// whose tile sum leaves [0, 2^64] sets a flag; a wave with a flagged lane
+// recomputes its full tiles with the exact online update.  The few masked
+// tiles (causal window, ragged end) use the exact update directly.
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int S = kStages;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 31, hl = lane >> 5;
@@ -488,11 +551,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   const int tb = split * a.tps;
   const int te = min(tb + a.tps, a.n_tiles);
   const float c = a.p.c;
+  const int L = a.p.L;
 
-  bf16x8 q[NT][D / 16];
+  bf16x8 q[NT][KS];
   int vis[NT];
   load_q_agpr<D, NT>(q, vis, a, g, lane);
-
   float m[NT], z[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
@@ -503,69 +566,142 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   // compiler can see, so it does not drain the queue inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
 
-  constexpr int S = kStages;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
-  uint32_t foff[D / 16];
+  const int64_t kts = a.p.kts;
+  uint32_t foff[KS];
   frag_offsets<D>(foff, lane);
-  // this wave's tiles: tb + wave, tb + wave + kWaves, ...
+  const uint32_t ring0 = lds_addr(ring[wave][0]);
+  // this wave's tiles: tb + wave + j * kWaves; the first nf need no masking
   const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
-  constexpr int NA = Halves<NT>::NA, NB = Halves<NT>::NB;
-  f32x16 accA[NA], accB[NB > 0 ? NB : 1];
-  u32x4 f[D / 16];
-  for (int i = 0; i < S - 1 && i < nt; ++i)
-    issue_tile<D>(ring[wave][i], kbase, a.p.kts, (tb + wave + i * kWaves) * 32, a.p.L, lane);
-  if (nt > 0) {
-    wait_tile<D, S>(min(S - 2, nt - 1));
-    read_frags<D / 16>(f, lds_addr(ring[wave][0]), foff);
-    wait_lgkm<D / 16>(f);
-    mfma_part<D, NT, 0, NA>(accA, f, q);
-  }
-  for (int i = 0; i < nt; ++i) {
-    if (i + S - 1 < nt)
-      issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                    (tb + wave + (i + S - 1) * kWaves) * 32, a.p.L, lane);
-    const int t0 = (tb + wave + i * kWaves) * 32;
-    // The next tile's fragments come from stage (i + 1) % S; after the last
-    // tile that stage holds stale data whose MFMA results are never used.
-    const uint32_t next_stage = lds_addr(ring[wave][(i + 1) % S]);
-    const int ahead = i + 1 < nt ? min(S - 2, nt - 2 - i) : 0;
-    if (t0 + 31 <= a.min_vis) {
-      // MFMA of tile i's second half || statistics of its first half
-      float sum[NA];
-#pragma unroll
-      for (int T = 0; T < NA; ++T) sum[T] = 0.f;
-      phase<D, NT, NA, NB, NA>(accB, f, q, [&](int T, int e) {
-        sum[T] += ex2(fmaf(accA[T][e], c, -m[T]));
-      });
-      bool bad0 = false;
-#pragma unroll
-      for (int T = 0; T < NA; ++T) bad0 |= !(sum[T] <= 0x1p64f);
-      stats_commit<NT, 0, NA>(accA, m, z, c, sum, bad0);
-      // next tile's fragments; its first-half MFMA || this tile's second half
-      wait_tile<D, S>(ahead);
-      read_frags<D / 16>(f, next_stage, foff);
-      wait_lgkm<D / 16>(f);
-      float sum1[NB > 0 ? NB : 1];
-#pragma unroll
-      for (int T = 0; T < (NB > 0 ? NB : 1); ++T) sum1[T] = 0.f;
-      phase<D, NT, 0, NA, NB>(accA, f, q, [&](int T, int e) {
-        sum1[T] += ex2(fmaf(accB[T][e], c, -m[NA + T]));
-      });
-      bool bad1 = false;
-#pragma unroll
-      for (int T = 0; T < NB; ++T) bad1 |= !(sum1[T] <= 0x1p64f);
-      stats_commit<NT, NA, NB>(accB, m, z, c, sum1, bad1);
-    } else {
-      mfma_result_guard();
-      mfma_part<D, NT, NA, NB>(accB, f, q);
-      stats_part<NT, 0, NA>(accA, m, z, c, false, t0, hl, vis);
-      wait_tile<D, S>(ahead);
-      read_frags<D / 16>(f, next_stage, foff);
-      wait_lgkm<D / 16>(f);
-      mfma_part<D, NT, 0, NA>(accA, f, q);
-      stats_part<NT, NA, NB>(accB, m, z, c, false, t0, hl, vis);
+  const int full_end = (a.min_vis - 31) >= 0 ? (a.min_vis - 31) / 32 + 1 : 0;  // tiles < full_end are full
+  int nf = full_end > tb + wave ? (full_end - tb - wave + kWaves - 1) / kWaves : 0;
+  nf = nf < nt ? nf : nt;
+  const auto tile_t0 = [&](int j) { return (tb + wave + j * kWaves) * 32; };
+  const auto stage_of = [&](int j) { return ring[wave][j & (S - 1)]; };
+
+  if (nf > 0) {
+    f32x16 acc0[NT], acc1[NT];
+    u32x4 f0[KS], f1[KS];
+    // tiles 0 .. S-1 fill the ring; step j then refills tile j-1's stage
+    const int pre = nf < S ? nf : S;
+    for (int j = 0; j < pre; ++j) issue_tile<D>(stage_of(j), kbase, kts, tile_t0(j), L, lane);
+    if (pre == S)
+      wait_vm<(S - 1) * KS>();
+    else
+      wait_vm<0>();
+    read_frags_a<KS>(f0, ring0, foff);
+    wait_lgkm_a<KS>(f0);
+    mfma_all_a<D, NT>(acc0, f0, q);
+    if (nf > 1) {
+      if (pre == S)
+        wait_vm<(S - 2) * KS>();
+      else
+        wait_vm<0>();
+      read_frags_a<KS>(f1, ring0 + tile_bytes<D>(), foff);
+      wait_lgkm_a<KS>(f1);
     }
+    // the running max: exact max of the wave's first tile, per lane and row
+    mfma_guard<NT>(acc0);
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      float mx = acc0[T][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc0[T][i]);
+      m[T] = mx * c;
+    }
+    float sa[NT], sb[NT], nm[NT];
+#pragma unroll
+    for (int T = 0; T < NT; ++T) nm[T] = -m[T];
+    bool flag = false;
+#pragma unroll
+    for (int T = 0; T < NT; ++T) sa[T] = sb[T] = 0.f;
+    const auto commit = [&]() {
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        const float s2 = sa[T] + sb[T];
+        flag |= !(s2 <= 0x1p64f);
+        z[T] += s2;
+        sa[T] = sb[T] = 0.f;
+      }
+    };
+    // step j: MFMAs of tile j (fc) || sums of tile j-1 (accP); loads of tile
+    // j + S - 1 while it exists; then tile j + 1's fragments into fn.
+    const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
+                          u32x4(&fn)[KS], int j) {
+      const auto work = [&](int T, int i, float x) {
+        if (i & 1)
+          sb[T] += ex2(fma_after_guard(x, c, nm[T]));
+        else
+          sa[T] += ex2(fma_after_guard(x, c, nm[T]));
+      };
+      const uint32_t nxt = ring0 + ((j + 1) & (S - 1)) * tile_bytes<D>();
+      if (j + S - 1 < nf)
+        pipe_step<D, NT, true, true, (S - 2) * KS>(accC, accP, fc, fn, q, stage_of(j + S - 1),
+                                                    kbase, kts, tile_t0(j + S - 1), L, lane, nxt,
+                                                    foff, work);
+      else if (j + 1 < nf)
+        pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L, lane,
+                                         nxt, foff, work);
+      else
+        pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L, lane,
+                                          nxt, foff, work);
+      commit();
+    };
+    int j = 1;
+    for (; j + 1 < nf; j += 2) {
+      step(acc1, acc0, f1, f0, j);
+      step(acc0, acc1, f0, f1, j + 1);
+    }
+    if (j < nf) step(acc1, acc0, f1, f0, j);
+    // the last full tile's sums
+    const auto tail = [&](f32x16(&accP)[NT]) {
+      mfma_guard<NT>(accP);
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i & 1)
+            sb[T] += ex2(fmaf(accP[T][i], c, -m[T]));
+          else
+            sa[T] += ex2(fmaf(accP[T][i], c, -m[T]));
+        }
+      commit();
+    };
+    if ((nf - 1) & 1)
+      tail(acc1);
+    else
+      tail(acc0);
+    if (__any(flag)) {
+      // some logit rose more than 64 (log2 units) above the first tile's max:
+      // redo the full tiles with the exact online update
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        m[T] = kNegInf;
+        z[T] = 0.f;
+      }
+      for (int jj = 0; jj < nf; ++jj) {
+        issue_tile<D>(stage_of(0), kbase, kts, tile_t0(jj), L, lane);
+        wait_vm<0>();
+        read_frags_a<KS>(f0, ring0, foff);
+        wait_lgkm_a<KS>(f0);
+        mfma_all_a<D, NT>(acc0, f0, q);
+        mfma_guard<NT>(acc0);
+        stats_part<NT, 0, NT>(acc0, m, z, c, true, 0, hl, vis);
+      }
+    }
+  }
+  // masked tiles: exact online update with the causal / ragged-end mask
+  for (int j = nf; j < nt; ++j) {
+    f32x16 acc[NT];
+    u32x4 f[KS];
+    issue_tile<D>(stage_of(0), kbase, kts, tile_t0(j), L, lane);
+    wait_vm<0>();
+    read_frags<KS>(f, ring0, foff);
+    wait_lgkm<KS>(f);
+    mfma_part<D, NT, 0, NT>(acc, f, q);
+    mfma_guard<NT>(acc);
+    stats_part<NT, 0, NT>(acc, m, z, c, false, tile_t0(j), hl, vis);
   }
 
   __shared__ float2 sm[kWaves][32 * NT];
@@ -669,49 +805,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   // cache, are read first.
   const auto tile_at = [&](int x) { return tb + wave + (a.rev ? nt - 1 - x : x) * kWaves; };
   if constexpr (MODE == 0) {
-    constexpr int NA = Halves<NT>::NA, NB = Halves<NT>::NB;
-    f32x16 accA[NA], accB[NB > 0 ? NB : 1];
-    u32x4 f[D / 16];
-    float part[16];
-    for (int i = 0; i < S - 1 && i < nt; ++i)
-      issue_tile<D>(ring[wave][i], kbase, a.p.kts, tile_at(i) * 32, L, lane);
-    if (nt > 0) {
-      wait_tile<D, S>(min(S - 2, nt - 1));
-      read_frags<D / 16>(f, lds_addr(ring[wave][0]), foff);
-      wait_lgkm<D / 16>(f);
-      mfma_part<D, NT, 0, NA>(accA, f, q);
-    }
-    for (int i = 0; i < nt; ++i) {
-      if (i + S - 1 < nt)
-        issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                      tile_at(i + S - 1) * 32, L, lane);
-      const int t0 = tile_at(i) * 32;
-      const uint32_t next_stage = lds_addr(ring[wave][(i + 1) % S]);
-      const int ahead = i + 1 < nt ? min(S - 2, nt - 2 - i) : 0;
-      if (t0 + 31 <= a.min_vis) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) part[e] = 0.f;
-        phase<D, NT, NA, NB, NA>(accB, f, q, [&](int T, int e) {
-          part[e] += ex2(fmaf(accA[T][e], c, -b[T]));
-        });
-        wait_tile<D, S>(ahead);
-        read_frags<D / 16>(f, next_stage, foff);
-        wait_lgkm<D / 16>(f);
-        phase<D, NT, 0, NA, NB>(accA, f, q, [&](int T, int e) {
-          part[e] += ex2(fmaf(accB[T][e], c, -b[NA + T]));
-        });
-        mfma_result_guard();
-      } else {
-        mfma_result_guard();
-        mfma_part<D, NT, NA, NB>(accB, f, q);
-        probs_part<NT, 0, NA, false>(accA, part, b, c, false, t0, hl, vis);
-        wait_tile<D, S>(ahead);
-        read_frags<D / 16>(f, next_stage, foff);
-        wait_lgkm<D / 16>(f);
-        mfma_part<D, NT, 0, NA>(accA, f, q);
-        probs_part<NT, NA, NB, true>(accB, part, b, c, false, t0, hl, vis);
-      }
-      // transpose through this wave's LDS buffer: row n = query row lane, 32 keys
+    constexpr int KS = D / 16;
+    const int64_t kts = a.p.kts;
+    const uint32_t ring0 = lds_addr(ring[wave][0]);
+    // column sums of one tile's probabilities (part[i]: key 8(i/4) + 4hl + i%4,
+    // summed over this lane's rows) -> transpose through this wave's LDS buffer
+    // -> one store per key
+    const auto flush = [&](float (&part)[16], int t0) {
       const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
       ds_write_b128<0>(waddr, f32x4{part[0], part[1], part[2], part[3]});
       ds_write_b128<32>(waddr, f32x4{part[4], part[5], part[6], part[7]});
@@ -740,8 +840,93 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) v += r[n];
       v += __shfl_xor(v, 32);
-      const int t = t0 + k;
-      if (hl == 0 && t < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + t, v, a.p.accumulate);
+      const int tt = t0 + k;
+      if (hl == 0 && tt < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + tt, v, a.p.accumulate);
+    };
+    // tiles j = 0 .. nt-1 of this wave are tb + wave + j * kWaves; the first nf
+    // need no masking.  Masked tiles (causal window, ragged end) go first,
+    // one at a time, then the full tiles run the software pipeline (in
+    // reverse order when a.rev).
+    const int full_end = (a.min_vis - 31) >= 0 ? (a.min_vis - 31) / 32 + 1 : 0;
+    int nf = full_end > tb + wave ? (full_end - tb - wave + kWaves - 1) / kWaves : 0;
+    nf = nf < nt ? nf : nt;
+    for (int j = nf; j < nt; ++j) {
+      f32x16 acc[NT];
+      u32x4 f[KS];
+      float part[16];
+      const int t0 = (tb + wave + j * kWaves) * 32;
+      issue_tile<D>(ring[wave][0], kbase, kts, t0, L, lane);
+      wait_vm<0>();
+      read_frags<KS>(f, ring0, foff);
+      wait_lgkm<KS>(f);
+      mfma_part<D, NT, 0, NT>(acc, f, q);
+      mfma_guard<NT>(acc);
+      probs_part<NT, 0, NT, false>(acc, part, b, c, false, t0, hl, vis);
+      flush(part, t0);
+    }
+    if (nf > 0) {
+      // x-th processed full tile
+      const auto tj = [&](int x) { return a.rev ? nf - 1 - x : x; };
+      const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
+      const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
+      f32x16 acc0[NT], acc1[NT];
+      u32x4 f0[KS], f1[KS];
+      const int pre = nf < S ? nf : S;
+      for (int x = 0; x < pre; ++x) issue_tile<D>(stage_of(x), kbase, kts, t0_of(x), L, lane);
+      if (pre == S)
+        wait_vm<(S - 1) * KS>();
+      else
+        wait_vm<0>();
+      read_frags_a<KS>(f0, ring0, foff);
+      wait_lgkm_a<KS>(f0);
+      mfma_all_a<D, NT>(acc0, f0, q);
+      if (nf > 1) {
+        if (pre == S)
+          wait_vm<(S - 2) * KS>();
+        else
+          wait_vm<0>();
+        read_frags_a<KS>(f1, ring0 + tile_bytes<D>(), foff);
+        wait_lgkm_a<KS>(f1);
+      }
+      float part[16], nb[NT];
+#pragma unroll
+      for (int T = 0; T < NT; ++T) nb[T] = -b[T];
+      // step x: MFMAs of tile x || probabilities of tile x-1, then its flush
+      const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
+                            u32x4(&fn)[KS], int x) {
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) part[i2] = 0.f;
+        const auto work = [&](int T, int i2, float v) {
+          part[i2] += ex2(fma_after_guard(v, c, nb[T]));
+        };
+        const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
+        if (x + S - 1 < nf)
+          pipe_step<D, NT, true, true, (S - 2) * KS>(accC, accP, fc, fn, q, stage_of(x + S - 1),
+                                                      kbase, kts, t0_of(x + S - 1), L, lane, nxt,
+                                                      foff, work);
+        else if (x + 1 < nf)
+          pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L,
+                                           lane, nxt, foff, work);
+        else
+          pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L,
+                                            lane, nxt, foff, work);
+        flush(part, t0_of(x - 1));
+      };
+      int x = 1;
+      for (; x + 1 < nf; x += 2) {
+        step(acc1, acc0, f1, f0, x);
+        step(acc0, acc1, f0, f1, x + 1);
+      }
+      if (x < nf) step(acc1, acc0, f1, f0, x);
+      const auto tail = [&](f32x16(&accP)[NT]) {
+        mfma_guard<NT>(accP);
+        probs_full<NT, 0, NT, false>(accP, part, b, c);
+        flush(part, t0_of(nf - 1));
+      };
+      if ((nf - 1) & 1)
+        tail(acc1);
+      else
+        tail(acc0);
     }
   } else {
     for (int i = 0; i < S - 1 && i < nt; ++i)
