@@ -82,7 +82,6 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   p.K = static_cast<const uint16_t*>(K);
   p.S = S;
   p.stats = static_cast<float2*>(ws);
-  p.rowc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_stats);
   p.qhs = a.q_head_stride;
   p.qrs = a.q_row_stride;
   p.khs = a.k_head_stride;

@@ -23,10 +23,9 @@ struct ScorePlan {
   int n_tiles;      // ceil(L / 32)
   int n_split;      // splits of the key range per KV head
   int tiles_per_split;
-  int head_batch;   // KV heads per (pass 1, merge, pass 2) round
+  int head_batch;   // KV heads per (pass 1, pass 2) round
   int reverse;      // pass 2 visits tiles in the reverse of pass 1's order
   size_t ws_stats;  // bytes of per-split (max, sum) pairs
-  size_t ws_rowc;   // bytes of per-row softmax constants
   size_t ws_total;
 };
 
@@ -35,7 +34,6 @@ struct ScoreLaunch {
   const uint16_t* K;
   float* S;
   float2* stats;  // [H_kv][rows_pad][n_split]
-  float* rowc;    // [H_kv][rows_pad]
   int64_t qhs, qrs, khs, kts, s_ld;
   int64_t q_pos0;
   int L, W, G, H_kv, d_k, heads, accumulate, phase;

@@ -26,8 +26,9 @@
 //    from the wave's first tile, so the pipeline carries no branch; a wave
 //    whose sums overflow [0, 2^64] redoes its tiles with the exact online
 //    update.  Lane halves and waves are merged in LDS and written per split
-//    of the key range; a small merge kernel folds the splits by log-sum-exp
-//    into one constant b_r = m_r + log2 Z_r per row (+inf for padding rows).
+//    of the key range; each pass-2 workgroup folds the splits of its group's
+//    rows by log-sum-exp into one constant b_r = m_r + log2 Z_r per row (+inf
+//    for padding rows) before its tile loop.
 //  * Pass 2 recomputes the tile, forms p = exp2(x - b_r) (no division), adds
 //    the rows a lane holds, transposes the 32 x 32 tile of partial sums
 //    through a per-wave LDS buffer and adds across lanes.  Every output element
@@ -728,35 +729,37 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// Folds the per-split (max, sum) pairs of each row by log-sum-exp into the
-// row constant b = m + log2 Z.  Eight lanes share a row and stride over its
-// splits (stored contiguously), so all loads of a row are in flight at once;
-// the lanes combine with a fixed butterfly, so the result is reproducible.
-constexpr int kMergeLanes = 8;
-constexpr int kMergeRows = kThreads / kMergeLanes;   // 32 rows per workgroup
-
-__global__ __launch_bounds__(kThreads) void score_merge_kernel(KArgs a) {
-  const int g = a.g0 + blockIdx.y;
-  const int r = blockIdx.x * kMergeRows + threadIdx.x / kMergeLanes;
-  const int sub = threadIdx.x % kMergeLanes;
-  const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + r) * a.n_split;
-  float mm = kNegInf;
-  for (int s = sub; s < a.n_split; s += kMergeLanes) mm = fmaxf(mm, st[s].x);
-#pragma unroll
-  for (int off = 1; off < kMergeLanes; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
-  float zz = 0.f;
-  if (mm != kNegInf)
-    for (int s = sub; s < a.n_split; s += kMergeLanes) {
+// Folds the per-split (max, sum) pairs of each of the group's rows by
+// log-sum-exp into the row constant b = m + log2 Z (+inf for padding rows),
+// inside the pass-2 workgroup: two threads per row, each folding every other
+// split online in a fixed order, then combined.  The loads overlap the query
+// loads already in flight.  Leaves b for rows [0, rows_pad) in brow.
+__device__ __forceinline__ void merge_rows(const KArgs& a, int g, float* brow) {
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  if (r < a.rows_pad) {
+    const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + r) * a.n_split;
+    float mm = kNegInf, zz = 0.f;
+    for (int s = half; s < a.n_split; s += 2) {
       const float2 v = st[s];
-      if (v.x != kNegInf) zz += v.y * exp2f(v.x - mm);
+      if (v.x > mm) {
+        zz = (mm == kNegInf ? 0.f : zz * exp2f(mm - v.x)) + v.y;
+        mm = v.x;
+      } else if (v.x != kNegInf) {
+        zz += v.y * exp2f(v.x - mm);
+      }
     }
-#pragma unroll
-  for (int off = 1; off < kMergeLanes; off <<= 1) zz += __shfl_xor(zz, off);
-  if (sub == 0) {
-    const int hq = r / a.head_rows, j = r % a.head_rows;
-    const bool valid = hq < a.p.G && j < a.p.W && mm != kNegInf;
-    a.p.rowc[(int64_t)g * a.rows_pad + r] = valid ? mm + log2f(zz) : kPosInf;
+    const float m2 = __shfl_xor(mm, 1), z2 = __shfl_xor(zz, 1);
+    const float mx = fmaxf(mm, m2);
+    const float zt = mx == kNegInf ? 0.f
+                                   : (mm == kNegInf ? 0.f : zz * exp2f(mm - mx)) +
+                                         (m2 == kNegInf ? 0.f : z2 * exp2f(m2 - mx));
+    if (half == 0) {
+      const int hq = r / a.head_rows, jr = r % a.head_rows;
+      const bool valid = hq < a.p.G && jr < a.p.W && mx != kNegInf;
+      brow[r] = valid ? mx + log2f(zt) : kPosInf;
+    }
   }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -784,9 +787,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
     load_q_agpr<D, NT>(q, vis, a, g, lane);
   else
     load_q<D, NT>(q, vis, a, g, lane);
+  // row constants from pass 1's split statistics
+  __shared__ float brow[128];
+  merge_rows(a, g, brow);
   float b[NT];
 #pragma unroll
-  for (int T = 0; T < NT; ++T) b[T] = a.p.rowc[(int64_t)g * a.rows_pad + 32 * T + nl];
+  for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
   __builtin_amdgcn_s_waitcnt(0);   // Q and row constants ready before the K queue starts
 
   __shared__ float tr[kWaves][32 * kStride];
@@ -1008,8 +1014,6 @@ kvs_status launch_rounds(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t 
     dim3 grid(pl.n_split, nb);
     if (p.phase != 2) {
       hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
-      hipLaunchKernelGGL(score_merge_kernel, dim3(pl.rows_pad / kMergeRows, nb), dim3(kThreads), 0,
-                         stream, a);
     }
     if (p.phase == 1) continue;
     if (p.heads == KVS_HEADS_GROUP_SUM)
@@ -1067,8 +1071,7 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->tiles_per_split = tps;
   pl->n_split = (pl->n_tiles + tps - 1) / tps;
   pl->ws_stats = align_up((size_t)a->H_kv * pl->n_split * pl->rows_pad * sizeof(float2), kWsAlign);
-  pl->ws_rowc = align_up((size_t)a->H_kv * pl->rows_pad * sizeof(float), kWsAlign);
-  pl->ws_total = pl->ws_stats + pl->ws_rowc;
+  pl->ws_total = pl->ws_stats;
   return KVS_OK;
 }
 
