@@ -472,6 +472,38 @@ __device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint16_t* kbas
                                    (lds_void*)(stage + jj * 1024), 16, 0, 0);
 }
 
+// The same load for full tiles (no ragged end), addressed as a uniform tile
+// base plus a per-lane byte offset: key row tr = jj * RPI + lane / CR of the
+// tile, chunk p ^ (tr % CR).  (jj * RPI) % CR repeats every CR / RPI chunks,
+// so a lane needs NQ = CR / RPI distinct offsets (chunk_offsets), and the
+// load takes an SGPR base and a VGPR offset: no vector ALU work per load.
+template <int D>
+struct ChunkGeom {
+  static constexpr int CR = D / 8;
+  static constexpr int RPI = 64 / CR;
+  static constexpr int NQ = CR / RPI;
+};
+
+template <int D>
+__device__ __forceinline__ void chunk_offsets(uint32_t (&off)[ChunkGeom<D>::NQ], int lane,
+                                              int64_t kts) {
+  using G = ChunkGeom<D>;
+  const int p = lane % G::CR, lq = lane / G::CR;
+  const uint32_t row = (uint32_t)((int64_t)lq * kts * 2);
+#pragma unroll
+  for (int q2 = 0; q2 < G::NQ; ++q2)
+    off[q2] = row + 16u * (uint32_t)(p ^ ((q2 * G::RPI + lq) % G::CR));
+}
+
+template <int D>
+__device__ __forceinline__ void issue_chunk_full(uint8_t* stage, const uint8_t* tile_base,
+                                                 int64_t kts,
+                                                 const uint32_t (&off)[ChunkGeom<D>::NQ], int jj) {
+  using G = ChunkGeom<D>;
+  const uint8_t* src = tile_base + (int64_t)jj * G::RPI * kts * 2 + off[jj % G::NQ];
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + jj * 1024), 16, 0, 0);
+}
+
 // Slot schedule of a steady-state step with M MFMA slots and KS load/read
 // instructions per tile: the loads of a new tile go out over the first half
 // of the slots, then the wait for the next tile and its fragment reads.
@@ -493,9 +525,10 @@ template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work>
 __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT],
                                           const u32x4 (&fc)[D / 16], u32x4 (&fn)[D / 16],
                                           const bf16x8 (&q)[NT][D / 16], uint8_t* issue_stage,
-                                          const uint16_t* kbase, int64_t kts, int issue_t0, int L,
-                                          int lane, uint32_t next_stage,
-                                          const uint32_t (&foff)[D / 16], Work&& work) {
+                                          const uint8_t* issue_base, int64_t kts,
+                                          const uint32_t (&coff)[ChunkGeom<D>::NQ],
+                                          uint32_t next_stage, const uint32_t (&foff)[D / 16],
+                                          Work&& work) {
   constexpr int KS = D / 16;
   constexpr int M = KS * NT;
   constexpr int EPM = 16 / KS;
@@ -519,7 +552,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT]
     if constexpr (ISSUE) {
 #pragma unroll
       for (int jj = 0; jj < KS; ++jj)
-        if (SL::issue(jj) == k) issue_chunk<D>(issue_stage, kbase, kts, issue_t0, L, lane, jj);
+        if (SL::issue(jj) == k) issue_chunk_full<D>(issue_stage, issue_base, kts, coff, jj);
     }
     if constexpr (NEXT) {
       if (k == SL::kWait) wait_vm<WAITN>();
@@ -580,6 +613,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   nf = nf < nt ? nf : nt;
   const auto tile_t0 = [&](int j) { return (tb + wave + j * kWaves) * 32; };
   const auto stage_of = [&](int j) { return ring[wave][j & (S - 1)]; };
+  const auto tile_base = [&](int j) {
+    return reinterpret_cast<const uint8_t*>(kbase) + (int64_t)tile_t0(j) * kts * 2;
+  };
+  uint32_t coff[ChunkGeom<D>::NQ];
+  chunk_offsets<D>(coff, lane, kts);
 
   if (nf > 0) {
     f32x16 acc0[NT], acc1[NT];
@@ -639,13 +677,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
       const uint32_t nxt = ring0 + ((j + 1) & (S - 1)) * tile_bytes<D>();
       if (j + S - 1 < nf)
         pipe_step<D, NT, true, true, (S - 2) * KS>(accC, accP, fc, fn, q, stage_of(j + S - 1),
-                                                    kbase, kts, tile_t0(j + S - 1), L, lane, nxt,
-                                                    foff, work);
+                                                    tile_base(j + S - 1), kts, coff, nxt, foff,
+                                                    work);
       else if (j + 1 < nf)
-        pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L, lane,
-                                         nxt, foff, work);
+        pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff, nxt,
+                                         foff, work);
       else
-        pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L, lane,
+        pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
                                           nxt, foff, work);
       commit();
     };
@@ -875,6 +913,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       const auto tj = [&](int x) { return a.rev ? nf - 1 - x : x; };
       const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
       const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
+      uint32_t coff[ChunkGeom<D>::NQ];
+      chunk_offsets<D>(coff, lane, kts);
       f32x16 acc0[NT], acc1[NT];
       u32x4 f0[KS], f1[KS];
       const int pre = nf < S ? nf : S;
@@ -907,15 +947,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         };
         const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
         if (x + S - 1 < nf)
-          pipe_step<D, NT, true, true, (S - 2) * KS>(accC, accP, fc, fn, q, stage_of(x + S - 1),
-                                                      kbase, kts, t0_of(x + S - 1), L, lane, nxt,
-                                                      foff, work);
+          pipe_step<D, NT, true, true, (S - 2) * KS>(
+              accC, accP, fc, fn, q, stage_of(x + S - 1),
+              reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t0_of(x + S - 1) * kts * 2, kts,
+              coff, nxt, foff, work);
         else if (x + 1 < nf)
-          pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L,
-                                           lane, nxt, foff, work);
+          pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
+                                           nxt, foff, work);
         else
-          pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, kbase, kts, 0, L,
-                                            lane, nxt, foff, work);
+          pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
+                                            nxt, foff, work);
         flush(part, t0_of(x - 1));
       };
       int x = 1;
