@@ -37,6 +37,8 @@
 //  * No R x L logit matrix is ever stored: K is read once per pass.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -521,14 +523,14 @@ struct StepSlots {
 // fma_after_guard, so the read stays behind the result guard).  ISSUE: the loads of tile `issue_t0` into `issue_stage`
 // are spread over the first slots.  NEXT: the next tile is waited for (WAITN
 // loads may stay outstanding) and its fragments are read into fn.
-template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work>
+template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work, typename Side>
 __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT],
                                           const u32x4 (&fc)[D / 16], u32x4 (&fn)[D / 16],
                                           const bf16x8 (&q)[NT][D / 16], uint8_t* issue_stage,
                                           const uint8_t* issue_base, int64_t kts,
                                           const uint32_t (&coff)[ChunkGeom<D>::NQ],
                                           uint32_t next_stage, const uint32_t (&foff)[D / 16],
-                                          Work&& work) {
+                                          Work&& work, Side&& side) {
   constexpr int KS = D / 16;
   constexpr int M = KS * NT;
   constexpr int EPM = 16 / KS;
@@ -549,6 +551,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT]
       const int e = k * EPM + u;
       work(e / 16, e % 16, accP[e / 16][e % 16]);
     }
+    side(k, M);
     if constexpr (ISSUE) {
 #pragma unroll
       for (int jj = 0; jj < KS; ++jj)
@@ -664,6 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
         sa[T] = sb[T] = 0.f;
       }
     };
+    const auto no_side = [](int, int) {};
     // step j: MFMAs of tile j (fc) || sums of tile j-1 (accP); loads of tile
     // j + S - 1 while it exists; then tile j + 1's fragments into fn.
     const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
@@ -678,13 +682,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
       if (j + S - 1 < nf)
         pipe_step<D, NT, true, true, (S - 2) * KS>(accC, accP, fc, fn, q, stage_of(j + S - 1),
                                                     tile_base(j + S - 1), kts, coff, nxt, foff,
-                                                    work);
+                                                    work, no_side);
       else if (j + 1 < nf)
         pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff, nxt,
-                                         foff, work);
+                                         foff, work, no_side);
       else
         pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
-                                          nxt, foff, work);
+                                          nxt, foff, work, no_side);
       commit();
     };
     int j = 1;
@@ -854,31 +858,34 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
     const uint32_t ring0 = lds_addr(ring[wave][0]);
     // column sums of one tile's probabilities (part[i]: key 8(i/4) + 4hl + i%4,
     // summed over this lane's rows) -> transpose through this wave's LDS buffer
-    // -> one store per key
-    const auto flush = [&](float (&part)[16], int t0) {
-      const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
+    // -> one store per key.  In the pipeline the LDS writes and reads run
+    // inside the next step's MFMA slots (flush_side) and only the adds and the
+    // store follow it (flush_finish).
+    const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
+    const uint32_t raddr = lds_addr(wl) + (16 * hl * kStride + k) * 4;
+    float r[16];
+    const auto flush_write = [&](const float (&part)[16]) {
       ds_write_b128<0>(waddr, f32x4{part[0], part[1], part[2], part[3]});
       ds_write_b128<32>(waddr, f32x4{part[4], part[5], part[6], part[7]});
       ds_write_b128<64>(waddr, f32x4{part[8], part[9], part[10], part[11]});
       ds_write_b128<96>(waddr, f32x4{part[12], part[13], part[14], part[15]});
-      const uint32_t raddr = lds_addr(wl) + (16 * hl * kStride + k) * 4;
-      float r[16];
-      ds_read_b32<0 * kStride * 4>(r[0], raddr);
-      ds_read_b32<1 * kStride * 4>(r[1], raddr);
-      ds_read_b32<2 * kStride * 4>(r[2], raddr);
-      ds_read_b32<3 * kStride * 4>(r[3], raddr);
-      ds_read_b32<4 * kStride * 4>(r[4], raddr);
-      ds_read_b32<5 * kStride * 4>(r[5], raddr);
-      ds_read_b32<6 * kStride * 4>(r[6], raddr);
-      ds_read_b32<7 * kStride * 4>(r[7], raddr);
-      ds_read_b32<8 * kStride * 4>(r[8], raddr);
-      ds_read_b32<9 * kStride * 4>(r[9], raddr);
-      ds_read_b32<10 * kStride * 4>(r[10], raddr);
-      ds_read_b32<11 * kStride * 4>(r[11], raddr);
-      ds_read_b32<12 * kStride * 4>(r[12], raddr);
-      ds_read_b32<13 * kStride * 4>(r[13], raddr);
-      ds_read_b32<14 * kStride * 4>(r[14], raddr);
-      ds_read_b32<15 * kStride * 4>(r[15], raddr);
+    };
+    const auto read_pair = [&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      ds_read_b32<(2 * P) * kStride * 4>(r[2 * P], raddr);
+      ds_read_b32<(2 * P + 1) * kStride * 4>(r[2 * P + 1], raddr);
+    };
+    const auto read_all = [&]() {
+      read_pair(std::integral_constant<int, 0>{});
+      read_pair(std::integral_constant<int, 1>{});
+      read_pair(std::integral_constant<int, 2>{});
+      read_pair(std::integral_constant<int, 3>{});
+      read_pair(std::integral_constant<int, 4>{});
+      read_pair(std::integral_constant<int, 5>{});
+      read_pair(std::integral_constant<int, 6>{});
+      read_pair(std::integral_constant<int, 7>{});
+    };
+    const auto flush_finish = [&](int t0) {
       wait_lgkm16(r);
       float v = 0.f;
 #pragma unroll
@@ -886,6 +893,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       v += __shfl_xor(v, 32);
       const int tt = t0 + k;
       if (hl == 0 && tt < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + tt, v, a.p.accumulate);
+    };
+    const auto flush = [&](const float (&part)[16], int t0) {
+      flush_write(part);
+      read_all();
+      flush_finish(t0);
     };
     // tiles j = 0 .. nt-1 of this wave are tb + wave + j * kWaves; the first nf
     // need no masking.  Masked tiles (causal window, ragged end) go first,
@@ -934,41 +946,71 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         read_frags_a<KS>(f1, ring0 + tile_bytes<D>(), foff);
         wait_lgkm_a<KS>(f1);
       }
-      float part[16], nb[NT];
+      float partA[16], partB[16], nb[NT];
 #pragma unroll
       for (int T = 0; T < NT; ++T) nb[T] = -b[T];
-      // step x: MFMAs of tile x || probabilities of tile x-1, then its flush
-      const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
-                            u32x4(&fn)[KS], int x) {
+      // step x: MFMAs of tile x || probabilities of tile x-1 into pc; with
+      // FL, the LDS transpose of tile x-2's sums pp runs in the same slots and
+      // its store follows the step
+      const auto step = [&](auto fl, f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
+                            u32x4(&fn)[KS], float(&pc)[16], const float(&pp)[16], int x) {
+        constexpr bool FL = decltype(fl)::value;
 #pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) part[i2] = 0.f;
+        for (int i2 = 0; i2 < 16; ++i2) pc[i2] = 0.f;
         const auto work = [&](int T, int i2, float v) {
-          part[i2] += ex2(fma_after_guard(v, c, nb[T]));
+          pc[i2] += ex2(fma_after_guard(v, c, nb[T]));
+        };
+        const auto side = [&](int kk, int M) {
+          if constexpr (FL) {
+            if (kk == 0) flush_write(pp);
+            // the 8 read pairs in slots 1..8 (the last slot when M is small)
+            const auto at = [&](int pr) { return 1 + pr < M ? 1 + pr : M - 1; };
+            if (at(0) == kk) read_pair(std::integral_constant<int, 0>{});
+            if (at(1) == kk) read_pair(std::integral_constant<int, 1>{});
+            if (at(2) == kk) read_pair(std::integral_constant<int, 2>{});
+            if (at(3) == kk) read_pair(std::integral_constant<int, 3>{});
+            if (at(4) == kk) read_pair(std::integral_constant<int, 4>{});
+            if (at(5) == kk) read_pair(std::integral_constant<int, 5>{});
+            if (at(6) == kk) read_pair(std::integral_constant<int, 6>{});
+            if (at(7) == kk) read_pair(std::integral_constant<int, 7>{});
+          }
         };
         const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
         if (x + S - 1 < nf)
           pipe_step<D, NT, true, true, (S - 2) * KS>(
               accC, accP, fc, fn, q, stage_of(x + S - 1),
               reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t0_of(x + S - 1) * kts * 2, kts,
-              coff, nxt, foff, work);
+              coff, nxt, foff, work, side);
         else if (x + 1 < nf)
           pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
-                                           nxt, foff, work);
+                                           nxt, foff, work, side);
         else
           pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
-                                            nxt, foff, work);
-        flush(part, t0_of(x - 1));
+                                            nxt, foff, work, side);
+        if constexpr (FL) flush_finish(t0_of(x - 2));
       };
-      int x = 1;
+      using NoFl = std::integral_constant<bool, false>;
+      using Fl = std::integral_constant<bool, true>;
+      // partB holds the sums of odd steps, partA of even ones
+      if (nf > 1) step(NoFl{}, acc1, acc0, f1, f0, partB, partA, 1);
+      int x = 2;
       for (; x + 1 < nf; x += 2) {
-        step(acc1, acc0, f1, f0, x);
-        step(acc0, acc1, f0, f1, x + 1);
+        step(Fl{}, acc0, acc1, f0, f1, partA, partB, x);
+        step(Fl{}, acc1, acc0, f1, f0, partB, partA, x + 1);
       }
-      if (x < nf) step(acc1, acc0, f1, f0, x);
+      if (x < nf) step(Fl{}, acc0, acc1, f0, f1, partA, partB, x);
+      // sums of tile nf-2 (computed by step nf-1, not yet flushed), then the
+      // last tile's
+      if (nf > 1) {
+        if ((nf - 1) & 1)
+          flush(partB, t0_of(nf - 2));
+        else
+          flush(partA, t0_of(nf - 2));
+      }
       const auto tail = [&](f32x16(&accP)[NT]) {
         mfma_guard<NT>(accP);
-        probs_full<NT, 0, NT, false>(accP, part, b, c);
-        flush(part, t0_of(nf - 1));
+        probs_full<NT, 0, NT, false>(accP, partA, b, c);
+        flush(partA, t0_of(nf - 1));
       };
       if ((nf - 1) & 1)
         tail(acc1);
