@@ -6,16 +6,17 @@ at the Mistral-7B / Llama-3.1-8B GQA shape (H_q = 32, H_kv = 8, d_k = 128,
 W = 32 window queries) and L = 131072 prompt tokens:
 
   kvs_score (masked window softmax, column sums over rows and the 4 query
-  heads of each KV head) -> kvs_pool_pages (page max + argmax, P = 16) ->
-  kvs_cluster_priority (theta = 2e-3, r = 3) -> kvs_topk (1024 tokens per KV
-  head with cluster priority, window of 32 appended).
+  heads of each KV head) -> kvs_select (page max + argmax, P = 16; cluster
+  priority, theta = 2e-3, r = 3; top 1024 tokens per KV head with the
+  cluster priority, window of 32 appended).
 
 Inputs are resident in HBM before timing starts.  Four copies of K are rotated
 so that no step finds its keys in the 256 MB Infinity Cache left warm by the
 previous step.  The metric is prompt tokens scored per second (L per step).
 The roofline object covers the longest kernel of the step, timed with HIP
-events on the stream it runs on; its algorithmic bytes are the bytes the
-method must move: K once, Q once, the scores once.  The CPU baseline is the
+events on the stream it runs on, between the parts of K further steps; its
+algorithmic bytes are the bytes the method must move: K once, Q once, the
+scores once.  The CPU baseline is the
 fp64 oracle timed on the host on the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -131,7 +132,7 @@ def summarize_profiles(out_dir):
     lines = ["# Kernel durations, Mistral-7B GQA layer at L = 131072 (bench.py workload)", "",
              "Command (repo root on the GPU box, cd /tmp first):", "",
              "    " + PROFILE_COMMANDS["trace"], "",
-             "Calls cover the timed steps, the warm-up steps and the per-kernel event loops.", "",
+             "Calls cover the warm-up steps, the timed steps and the event-timed steps.", "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -256,9 +257,19 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
-    # Kernel timing: HIP events on the stream around K back-to-back launches of
-    # each part (the K copies hold identical keys, so the statistics from the
-    # last step stay valid for every copy).
+    # Kernel timing: K more steps with HIP events on the launch stream between
+    # the parts of each step, so every kernel is timed under the same
+    # conditions (clock, caches, neighbours) as in the timed region.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+
+    def part(a):
+        return sum(ev[a].elapsed_time(ev[a + 1]) for ev in evs) / args.steps
+
+    pass1, pass2, select = part(0), part(1), part(2)
+
     def timed(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -268,17 +279,6 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    def call(st):
-        if st != 0:
-            raise RuntimeError("libkvs call failed")
-
-    pass1 = timed(lambda j: call(lib.kvs_score(ra1, pQ, pKs[j % len(pKs)], pS, pws, ws_bytes, sp)))
-    pass2 = timed(lambda j: call(lib.kvs_score(ra2, pQ, pKs[j % len(pKs)], pS, pws, ws_bytes, sp)))
-
-    def select_part(j):
-        call(lib.kvs_select(pS, H_kv, n, L, rsel, pidx, ptk, tk_bytes, sp))
-
-    select = timed(select_part)
     log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1+merge {pass1 * 1e3:.1f} us, "
         f"pass2 {pass2 * 1e3:.1f} us, select {select * 1e3:.1f} us")
     copy_gbs = None

@@ -230,27 +230,70 @@ __device__ __forceinline__ void load_q(bf16x8 (&q)[NT][D / 16], int (&vis)[NT], 
   }
 }
 
-// Query fragments loaded straight into AGPRs (the only form the asm MFMAs
-// read them in).  Padding rows load row 0 of the group instead of zeros:
-// their statistics are discarded and their row constant is +inf, so their
-// logits never reach an output.
-template <int D, int NT>
-__device__ __forceinline__ void load_q_agpr(bf16x8 (&q)[NT][D / 16], int (&vis)[NT],
-                                            const KArgs& a, int g, int lane) {
-  const int nl = lane & 31, hl = lane >> 5;
+// Last visible key of the padded query rows a lane holds (N-tile T, lane l ->
+// padded row 32T + l%32), -1 for padding rows.
+template <int NT>
+__device__ __forceinline__ void q_vis(int (&vis)[NT], const KArgs& a, int lane) {
+  const int nl = lane & 31;
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
     const int r = 32 * T + nl;
     const int hq = r / a.head_rows, j = r % a.head_rows;
-    const bool valid = hq < a.p.G && j < a.p.W;
     const int64_t pos = a.p.q_pos0 + j;
-    vis[T] = valid ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1) : -1;
-    const uint16_t* qp =
-        a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs + (int64_t)(valid ? j : 0) * a.p.qrs +
-        hl * (D / 2);
+    vis[T] = hq < a.p.G && j < a.p.W ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1)
+                                     : -1;
+  }
+}
+
+// Padded query row r of group g.  Padding rows read row 0 of the group
+// instead: their statistics are discarded and their row constant is +inf, so
+// their logits never reach an output.
+__device__ __forceinline__ const uint16_t* q_row(const KArgs& a, int g, int r) {
+  const int hq = r / a.head_rows, j = r % a.head_rows;
+  const bool valid = hq < a.p.G && j < a.p.W;
+  return a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs +
+         (int64_t)(valid ? j : 0) * a.p.qrs;
+}
+
+// Padded query rows 32w .. 32w+31 into an LDS stage with the K-tile layout
+// (same chunk swizzle), so the fragment offsets of a K tile address them too.
+// Loading a lane's fragments straight from global memory would touch a
+// different cache line in every lane of every load; staged, each load
+// instruction reads whole rows.
+template <int D>
+__device__ __forceinline__ void issue_q_rows(uint8_t* stage, const KArgs& a, int g, int w,
+                                             int lane) {
+  constexpr int CR = D / 8;
+  constexpr int RPI = 64 / CR;
+  const int p = lane % CR;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const int tr = j * RPI + lane / CR;
+    const int c = p ^ (tr % CR);
+    __builtin_amdgcn_global_load_lds(q_row(a, g, 32 * w + tr) + 8 * c,
+                                     (lds_void*)(stage + j * 1024), 16, 0, 0);
+  }
+}
+
+// Every wave's AGPR copy of all query fragments (the only form the asm MFMAs
+// read them in), from the rows staged by issue_q_rows: N-tile T sits at
+// base + T * stride.  Returns once the reads have landed.
+template <int D, int NT>
+__device__ __forceinline__ void read_q_agpr(bf16x8 (&q)[NT][D / 16], uint32_t base,
+                                            uint32_t stride, const uint32_t (&off)[D / 16]) {
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(q[T][s]) : "v"(qp + 8 * s) : "memory");
+      asm volatile("ds_read_b128 %0, %1" : "=a"(q[T][s]) : "v"(base + T * stride + off[s]));
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    if constexpr (D / 16 == 8)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+a"(q[T][0]), "+a"(q[T][1]), "+a"(q[T][2]), "+a"(q[T][3]), "+a"(q[T][4]),
+                     "+a"(q[T][5]), "+a"(q[T][6]), "+a"(q[T][7]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+a"(q[T][0]), "+a"(q[T][1]), "+a"(q[T][2]), "+a"(q[T][3]));
   }
 }
 
@@ -592,17 +635,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 
   bf16x8 q[NT][KS];
   int vis[NT];
-  load_q_agpr<D, NT>(q, vis, a, g, lane);
+  q_vis<NT>(vis, a, lane);
   float m[NT], z[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
     m[T] = kNegInf;
     z[T] = 0.f;
   }
-  // Q must be in VGPRs before the tile loop starts queueing K loads; a wait the
-  // compiler can see, so it does not drain the queue inside the loop.
-  __builtin_amdgcn_s_waitcnt(0);
-
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
   const int64_t kts = a.p.kts;
@@ -622,12 +661,27 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   uint32_t coff[ChunkGeom<D>::NQ];
   chunk_offsets<D>(coff, lane, kts);
 
+  // Tiles 0 .. S-1 fill the ring; step j then refills tile j-1's stage.  The
+  // query rows travel first, through every wave's last stage, while tiles
+  // 0 .. S-2 are queued behind them (vector memory operations complete in
+  // issue order); tile S-1 follows once every wave has its copy of Q.  The
+  // barriers are bare: a fenced one would wait for the queued tiles too.
+  const int pre = nf < S ? nf : S;
+  if (wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
+  for (int j = 0; j < pre && j < S - 1; ++j)
+    issue_tile<D>(stage_of(j), kbase, kts, tile_t0(j), L, lane);
+  if (pre >= S - 1)
+    wait_vm<(S - 1) * KS>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
+  __builtin_amdgcn_s_barrier();
+  if (pre == S) issue_tile<D>(stage_of(S - 1), kbase, kts, tile_t0(S - 1), L, lane);
+
   if (nf > 0) {
     f32x16 acc0[NT], acc1[NT];
     u32x4 f0[KS], f1[KS];
-    // tiles 0 .. S-1 fill the ring; step j then refills tile j-1's stage
-    const int pre = nf < S ? nf : S;
-    for (int j = 0; j < pre; ++j) issue_tile<D>(stage_of(j), kbase, kts, tile_t0(j), L, lane);
     if (pre == S)
       wait_vm<(S - 1) * KS>();
     else
@@ -774,21 +828,35 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 // Folds the per-split (max, sum) pairs of each of the group's rows by
 // log-sum-exp into the row constant b = m + log2 Z (+inf for padding rows),
 // inside the pass-2 workgroup: two threads per row, each folding every other
-// split online in a fixed order, then combined.  The loads overlap the query
-// loads already in flight.  Leaves b for rows [0, rows_pad) in brow.
+// split online in a fixed order, then combined.  The pairs are loaded in
+// batches of kMergeBatch independent loads, so a row costs one memory round
+// trip per batch rather than one per split.  Leaves b for rows [0, rows_pad)
+// in brow.
+constexpr int kMergeBatch = 16;
+
+__device__ __forceinline__ void fold_pair(float& mm, float& zz, float2 v) {
+  if (v.x > mm) {
+    zz = (mm == kNegInf ? 0.f : zz * exp2f(mm - v.x)) + v.y;
+    mm = v.x;
+  } else if (v.x != kNegInf) {
+    zz += v.y * exp2f(v.x - mm);
+  }
+}
+
 __device__ __forceinline__ void merge_rows(const KArgs& a, int g, float* brow) {
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
   if (r < a.rows_pad) {
     const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + r) * a.n_split;
     float mm = kNegInf, zz = 0.f;
-    for (int s = half; s < a.n_split; s += 2) {
-      const float2 v = st[s];
-      if (v.x > mm) {
-        zz = (mm == kNegInf ? 0.f : zz * exp2f(mm - v.x)) + v.y;
-        mm = v.x;
-      } else if (v.x != kNegInf) {
-        zz += v.y * exp2f(v.x - mm);
+    for (int s0 = half; s0 < a.n_split; s0 += 2 * kMergeBatch) {
+      float2 v[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int s = s0 + 2 * i;
+        v[i] = s < a.n_split ? st[s] : make_float2(kNegInf, 0.f);
       }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) fold_pair(mm, zz, v[i]);
     }
     const float m2 = __shfl_xor(mm, 1), z2 = __shfl_xor(zz, 1);
     const float mx = fmaxf(mm, m2);
@@ -801,6 +869,7 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, int g, float* brow) {
       brow[r] = valid ? mx + log2f(zt) : kPosInf;
     }
   }
+  wait_vm<0>();   // also every load the caller queued before the merge
   __syncthreads();
 }
 
@@ -823,38 +892,56 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const float c = a.p.c;
   const int L = a.p.L;
 
+  constexpr int S = MODE == 0 ? kStages : kStages - 1;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
+  const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
+  const int64_t kts = a.p.kts;
+  const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  // tiles j = 0 .. nt-1 of this wave are tb + wave + j * kWaves; the first nf
+  // need no masking
+  const int full_end = (a.min_vis - 31) >= 0 ? (a.min_vis - 31) / 32 + 1 : 0;
+  int nf = full_end > tb + wave ? (full_end - tb - wave + kWaves - 1) / kWaves : 0;
+  nf = nf < nt ? nf : nt;
+  // Pass 2 may walk the full tiles in the reverse of pass 1's order, so that
+  // the keys pass 1 streamed last, the likeliest to still sit in the
+  // memory-side cache, are read first.  x-th processed full tile:
+  const auto tj = [&](int x) { return a.rev ? nf - 1 - x : x; };
+  const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
+
   bf16x8 q[NT][D / 16];
   int vis[NT];
-  if constexpr (MODE == 0)
-    load_q_agpr<D, NT>(q, vis, a, g, lane);
-  else
+  if constexpr (MODE == 0) {
+    // The query rows (through every wave's last ring stage, see the pass-1
+    // kernel) and the first full tile load while the row constants are
+    // merged; the merge's barrier waits for all three.
+    q_vis<NT>(vis, a, lane);
+    if (wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
+    if (nf > 0) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
+  } else {
     load_q<D, NT>(q, vis, a, g, lane);
+  }
   // row constants from pass 1's split statistics
   __shared__ float brow[128];
   merge_rows(a, g, brow);
   float b[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
-  __builtin_amdgcn_s_waitcnt(0);   // Q and row constants ready before the K queue starts
+  __builtin_amdgcn_s_waitcnt(0);   // Q, the first tile and the row constants are in
 
   __shared__ float tr[kWaves][32 * kStride];
   __shared__ float hacc[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * 32 : 1];
   float* wl = tr[wave];
 
-  constexpr int S = MODE == 0 ? kStages : kStages - 1;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
-  const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
   uint32_t foff[D / 16];
   frag_offsets<D>(foff, lane);
-  const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  if constexpr (MODE == 0) {
+    read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
+    __builtin_amdgcn_s_barrier();   // every wave has its copy before the stage is refilled
+  }
   const int k = lane & 31;
-  // Pass 2 may walk the tiles in the reverse of pass 1's order, so that the
-  // keys pass 1 streamed last, the likeliest to still sit in the memory-side
-  // cache, are read first.
   const auto tile_at = [&](int x) { return tb + wave + (a.rev ? nt - 1 - x : x) * kWaves; };
   if constexpr (MODE == 0) {
     constexpr int KS = D / 16;
-    const int64_t kts = a.p.kts;
     const uint32_t ring0 = lds_addr(ring[wave][0]);
     // column sums of one tile's probabilities (part[i]: key 8(i/4) + 4hl + i%4,
     // summed over this lane's rows) -> transpose through this wave's LDS buffer
@@ -899,38 +986,17 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       read_all();
       flush_finish(t0);
     };
-    // tiles j = 0 .. nt-1 of this wave are tb + wave + j * kWaves; the first nf
-    // need no masking.  Masked tiles (causal window, ragged end) go first,
-    // one at a time, then the full tiles run the software pipeline (in
-    // reverse order when a.rev).
-    const int full_end = (a.min_vis - 31) >= 0 ? (a.min_vis - 31) / 32 + 1 : 0;
-    int nf = full_end > tb + wave ? (full_end - tb - wave + kWaves - 1) / kWaves : 0;
-    nf = nf < nt ? nf : nt;
-    for (int j = nf; j < nt; ++j) {
-      f32x16 acc[NT];
-      u32x4 f[KS];
-      float part[16];
-      const int t0 = (tb + wave + j * kWaves) * 32;
-      issue_tile<D>(ring[wave][0], kbase, kts, t0, L, lane);
-      wait_vm<0>();
-      read_frags<KS>(f, ring0, foff);
-      wait_lgkm<KS>(f);
-      mfma_part<D, NT, 0, NT>(acc, f, q);
-      mfma_guard<NT>(acc);
-      probs_part<NT, 0, NT, false>(acc, part, b, c, false, t0, hl, vis);
-      flush(part, t0);
-    }
+    // The full tiles run the software pipeline (in reverse order when a.rev);
+    // the masked ones (causal window, ragged end) follow one at a time.
     if (nf > 0) {
-      // x-th processed full tile
-      const auto tj = [&](int x) { return a.rev ? nf - 1 - x : x; };
-      const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
       const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
       uint32_t coff[ChunkGeom<D>::NQ];
       chunk_offsets<D>(coff, lane, kts);
       f32x16 acc0[NT], acc1[NT];
       u32x4 f0[KS], f1[KS];
       const int pre = nf < S ? nf : S;
-      for (int x = 0; x < pre; ++x) issue_tile<D>(stage_of(x), kbase, kts, t0_of(x), L, lane);
+      // tile 0 was issued before the merge and has arrived
+      for (int x = 1; x < pre; ++x) issue_tile<D>(stage_of(x), kbase, kts, t0_of(x), L, lane);
       if (pre == S)
         wait_vm<(S - 1) * KS>();
       else
@@ -1016,6 +1082,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         tail(acc1);
       else
         tail(acc0);
+    }
+    for (int j = nf; j < nt; ++j) {
+      f32x16 acc[NT];
+      u32x4 f[KS];
+      float part[16];
+      const int t0 = (tb + wave + j * kWaves) * 32;
+      issue_tile<D>(ring[wave][0], kbase, kts, t0, L, lane);
+      wait_vm<0>();
+      read_frags<KS>(f, ring0, foff);
+      wait_lgkm<KS>(f);
+      mfma_part<D, NT, 0, NT>(acc, f, q);
+      mfma_guard<NT>(acc);
+      probs_part<NT, 0, NT, false>(acc, part, b, c, false, t0, hl, vis);
+      flush(part, t0);
     }
   } else {
     for (int i = 0; i < S - 1 && i < nt; ++i)
