@@ -79,7 +79,7 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=3):
+def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=8):
     """The fp64 oracle, as it stands, on the full workload, one BLAS thread."""
     import numpy as np
     import oracle
