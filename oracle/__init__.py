@@ -9,6 +9,8 @@ Parity pins for every function are listed in the ``kvs`` module docstring.
 from .kvs import (  # noqa: F401
     bf16_to_f64,
     score,
+    score_raw,
+    aggregate_raw,
     head_reduce,
     pool,
     pages,

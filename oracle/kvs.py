@@ -42,6 +42,10 @@ below every number; cluster centres are page argmaxes whose page max >= theta
 and a token is prioritised if within r of a centre; top-p keeps a block while
 the mass ranked strictly before it is < p.
 
+Raw scores (GemFilter, Speculative Prefill, answer oracle): the queries sit at
+or after the last prompt token, so nothing is masked; the scale defaults to
+1/sqrt(d_k) as for the softmax scores.
+
 Parity pins (tests/test_oracle_*.py): row-stochastic mass, identical-key closed
 forms, SciPy softmax special case, GQA mapping by construction, linearity,
 permutation and shift invariance, planted spans rank first; SciPy filters for
@@ -120,13 +124,73 @@ def score(Q, K, *, L: int, W: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
 
 
 # ---------------------------------------------------------------------------
+# Raw (pre-softmax) scoring
+# ---------------------------------------------------------------------------
+
+def score_raw(Q, K, *, L: int, W: int, d_k: int, H_q: int, H_kv: int, reduce: int = RED_SUM,
+              scale: Optional[float] = None) -> np.ndarray:
+    """Raw attention logits of W query rows, reduced over all H_q query heads.
+
+    [CLAA] "Three representative token-ranking methods": GemFilter scores a
+    prompt token by the pre-softmax attention logit of the last prompt token's
+    query, scaled by 1/sqrt(d_k) and summed over all heads (SUM with W = 1).
+    Speculative Prefill takes, for each lookahead query, the maximum raw logit
+    over all layers and heads (MAX here, the layers in ``aggregate_raw``); the
+    answer-informed oracle ("The oracle construction") does the same with the
+    queries of the generated answer (``use_softmax=False``).
+
+    Q: bf16 bits [H_q][W][d_k]; K: bf16 bits [H_kv][L][d_k]; head h reads KV
+    head h // G.  These queries come at or after the last prompt token, so every
+    row sees every key and nothing is masked.
+    Returns float64 [W][L]: R[j][t] = SUM or MAX over h of scale * q[h][j] . k[h//G][t].
+    """
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    if reduce not in (RED_SUM, RED_MAX):
+        raise ValueError("raw scores reduce over heads by SUM or MAX")
+    G = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    q = bf16_to_f64(Q).reshape(H_q, W, d_k)
+    k = bf16_to_f64(K).reshape(H_kv, L, d_k)
+    out = None
+    for h in range(H_q):
+        s = scale * (q[h] @ k[h // G].T)                  # [W][L] raw logits of head h
+        if out is None:
+            out = s
+        elif reduce == RED_SUM:
+            out = out + s
+        else:
+            out = np.maximum(out, s)
+    return out
+
+
+def aggregate_raw(layer_scores: Sequence[np.ndarray], pool_k: int = 7) -> np.ndarray:
+    """Speculative Prefill / answer-oracle token scores from per-layer raw scores.
+
+    [CLAA] "The oracle construction" and the Speculative Prefill paragraph:
+    maximum over layers (each layer's [W][L] already holds the maximum over its
+    heads), then the mean over the W queries, then 1-D average pooling with
+    kernel ``pool_k`` (0 or 1: no pooling).  Returns float64 [L].
+    """
+    acc = np.asarray(layer_scores[0], dtype=np.float64).copy()
+    for s in layer_scores[1:]:
+        acc = np.maximum(acc, np.asarray(s, dtype=np.float64))
+    y = acc.mean(axis=0, keepdims=True)
+    if pool_k > 1:
+        y = pool(y, RED_MEAN, pool_k)
+    return y[0]
+
+
+# ---------------------------------------------------------------------------
 # Pooling and page aggregation
 # ---------------------------------------------------------------------------
 
 def head_reduce(x, mode: int) -> np.ndarray:
-    """Reduce the rows of x [H][n] to one row: SUM or MAX; NONE keeps x.
+    """Reduce the rows of x [H][n] to one row: SUM, MAX or MEAN; NONE keeps x.
 
-    [DELTA] key design 2 takes the maximum over heads before paging.
+    [DELTA] key design 2 takes the maximum over heads before paging; the
+    Speculative Prefill / answer-oracle aggregation averages over queries.
     """
     x = np.asarray(x, dtype=np.float64)
     if mode == RED_NONE:
@@ -135,7 +199,9 @@ def head_reduce(x, mode: int) -> np.ndarray:
         return x.sum(axis=0, keepdims=True)
     if mode == RED_MAX:
         return x.max(axis=0, keepdims=True)
-    raise ValueError("head reduce must be NONE, SUM or MAX")
+    if mode == RED_MEAN:
+        return x.mean(axis=0, keepdims=True)
+    raise ValueError("head reduce must be NONE, SUM, MAX or MEAN")
 
 
 def pool(x, mode: int, k: int) -> np.ndarray:
