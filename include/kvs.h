@@ -123,11 +123,58 @@ kvs_status kvs_score(const kvs_score_args* a, const void* Q, const void* K, floa
                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_score_raw - raw (pre-softmax) attention logits reduced over all heads.
+ *
+ * [CLAA] "Three representative token-ranking methods": GemFilter ranks the
+ * prompt tokens by the logit of the last prompt token's query, scaled by
+ * 1/sqrt(d_k) and summed over all heads (reduce = KVS_RED_SUM, W = 1).
+ * Speculative Prefill, and the answer-informed oracle of "The oracle
+ * construction" (use_softmax=False), take for each lookahead or answer query
+ * the maximum raw logit over all layers and heads, then the mean over the
+ * queries, then a 1-D average pooling with kernel 7: reduce = KVS_RED_MAX
+ * once per layer into the same S with accumulate = KVS_ACC_MAX (the first
+ * layer KVS_ACC_WRITE), then kvs_pool_pages over the W rows with head_reduce
+ * KVS_RED_MEAN and pool KVS_RED_MEAN.
+ * For every query row j < W and key t < L:
+ *     R[j][t] = SUM or MAX over the H_q query heads h of
+ *               scale * sum_c Q[h][j][c] * K[h / G][t][c]      (G = H_q / H_kv)
+ * and S[j][t] (row stride s_ld) receives R (KVS_ACC_WRITE), S + R
+ * (KVS_ACC_ADD) or max(S, R) (KVS_ACC_MAX).  These queries sit at or after the
+ * last prompt token (q_pos0 >= L - 1), so every row sees every key; Q and K
+ * hold finite values.
+ * Q, K: layouts, strides, defaults and alignment as for kvs_score; scale 0
+ * selects 1/sqrt(d_k).  S: float32, 4-byte aligned.
+ * Limits (else KVS_EUNSUPPORTED): d_k in {64, 128}; W <= 32; the W rows of a
+ * head padded to 8, 16 or 32 rows, G times that at most 128 rows per KV
+ * head, and all KV heads' padded rows (each KV head's rounded up to a
+ * multiple of 32) at most 256 (d_k = 128) or 896 (d_k = 64) rows.  K is read once, no workspace is used, and the result is
+ * bit-identical from run to run.
+ * ---------------------------------------------------------------------- */
+#define KVS_ACC_WRITE 0
+#define KVS_ACC_ADD 1
+#define KVS_ACC_MAX 2
+typedef struct {
+  int32_t L, W, d_k, H_q, H_kv;
+  int32_t reduce;     /* KVS_RED_SUM or KVS_RED_MAX over all query heads    */
+  int64_t q_pos0;     /* absolute position of query row 0, >= L - 1         */
+  int64_t q_head_stride, q_row_stride;
+  int64_t k_head_stride, k_tok_stride;
+  int64_t s_ld;       /* row stride of S in floats, >= L                    */
+  float scale;        /* logit scale, 0 => 1/sqrt(d_k); must be >= 0       */
+  int32_t accumulate; /* KVS_ACC_WRITE, KVS_ACC_ADD or KVS_ACC_MAX          */
+} kvs_raw_args;
+
+kvs_status kvs_score_raw(const kvs_raw_args* a, const void* Q, const void* K, float* S,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_pool_pages - head reduction, 1-D pooling, page aggregation.
  *
  * Input S float32 [H][n] with row stride ld (>= n).  In this order:
- *  1. head_reduce NONE keeps the H rows; SUM / MAX folds them into one row
- *     ([DELTA] key design 2: max over heads).  H' = 1 or H rows remain.
+ *  1. head_reduce NONE keeps the H rows; SUM / MAX / MEAN folds them into
+ *     one row ([DELTA] key design 2: max over heads; [CLAA] Speculative
+ *     Prefill: mean over the lookahead queries).  H' = 1 or H rows remain;
+ *     MEAN divides the float32 sum by H.
  *  2. pool NONE / MAX / MEAN over [t - r, t + r] clipped to [0, n),
  *     r = (pool_k - 1) / 2, pool_k odd; MEAN divides by the in-range count
  *     ([CLAA] 1-D pooling, kernel 7).

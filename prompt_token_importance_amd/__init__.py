@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkvs.so")
 
 KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EWORKSPACE, KVS_EHIP = 0, -1, -2, -3, -4
 HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX = 0, 1, 2
+ACC_WRITE, ACC_ADD, ACC_MAX = 0, 1, 2
 RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
 
 
@@ -37,6 +38,18 @@ class ScoreArgs(ctypes.Structure):
         ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
         ("s_ld", ctypes.c_int64),
         ("scale", ctypes.c_float), ("accumulate", ctypes.c_int32), ("phase", ctypes.c_int32),
+    ]
+
+
+class RawArgs(ctypes.Structure):
+    _fields_ = [
+        ("L", ctypes.c_int32), ("W", ctypes.c_int32), ("d_k", ctypes.c_int32),
+        ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("reduce", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
+        ("s_ld", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("accumulate", ctypes.c_int32),
     ]
 
 
@@ -71,6 +84,7 @@ def _load():
         "kvs_version": (I32, []),
         "kvs_score_workspace": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvs_score_raw": (I32, [ctypes.POINTER(RawArgs), P, P, P, P]),
         "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvs_topk_workspace": (SZ, [I32, I32, I32]),
         "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, SZ, P]),
@@ -94,7 +108,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = (
-    "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_pool_pages",
+    "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_raw",
+    "kvs_pool_pages",
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
     "kvs_block_union_workspace", "kvs_block_union_pagetable",
     "kvs_aggregate_workspace", "kvs_aggregate_layers", "kvs_cluster_priority",
@@ -159,6 +174,25 @@ def kvs_score(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs, S: Optional[tor
     ws, nb = _workspace(kvs_score_workspace(args), K.device, ws)
     _check(_lib.kvs_score(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _ptr(ws), nb,
                           _stream(stream)), "kvs_score")
+    return S
+
+
+# --------------------------------------------------------------------------- raw logits
+def raw_args(*, L, W, d_k, H_q, H_kv, q_pos0, reduce=RED_SUM, scale=0.0, accumulate=ACC_WRITE,
+             q_head_stride=0, q_row_stride=0, k_head_stride=0, k_tok_stride=0, s_ld=0) -> RawArgs:
+    return RawArgs(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, reduce=reduce, q_pos0=q_pos0,
+                   q_head_stride=q_head_stride, q_row_stride=q_row_stride,
+                   k_head_stride=k_head_stride, k_tok_stride=k_tok_stride, s_ld=s_ld,
+                   scale=scale, accumulate=accumulate)
+
+
+def kvs_score_raw(Q: torch.Tensor, K: torch.Tensor, args: RawArgs, S: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Raw logits reduced over all heads; S float32 [W][s_ld] (allocated if None)."""
+    if S is None:
+        S = torch.empty(args.W, args.s_ld or args.L, dtype=torch.float32, device=K.device)
+    _check(_lib.kvs_score_raw(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _stream(stream)),
+           "kvs_score_raw")
     return S
 
 

@@ -101,11 +101,62 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   return score_run(pl, p, as_stream(stream));
 }
 
+kvs_status kvs_score_raw(const kvs_raw_args* in, const void* Q, const void* K, float* S,
+                         void* stream) {
+  if (!in) return KVS_EINVAL;
+  kvs_raw_args a = *in;
+  if (a.L < 1 || a.W < 1 || a.H_q < 1 || a.H_kv < 1 || a.d_k < 1) return KVS_EINVAL;
+  if (a.H_q % a.H_kv) return KVS_EINVAL;
+  if (a.reduce != KVS_RED_SUM && a.reduce != KVS_RED_MAX) return KVS_EINVAL;
+  if (a.accumulate < KVS_ACC_WRITE || a.accumulate > KVS_ACC_MAX) return KVS_EINVAL;
+  if (!(a.scale >= 0.f) || isinf(a.scale)) return KVS_EINVAL;
+  if (a.q_pos0 < (int64_t)a.L - 1) return KVS_EUNSUPPORTED;   // rows that see only part of the keys
+  if (a.L > (1 << 30)) return KVS_EUNSUPPORTED;
+  if (a.d_k != 64 && a.d_k != 128) return KVS_EUNSUPPORTED;
+  if (a.W > 32) return KVS_EUNSUPPORTED;
+  if (a.q_head_stride == 0) a.q_head_stride = (int64_t)a.W * a.d_k;
+  if (a.q_row_stride == 0) a.q_row_stride = a.d_k;
+  if (a.k_head_stride == 0) a.k_head_stride = (int64_t)a.L * a.d_k;
+  if (a.k_tok_stride == 0) a.k_tok_stride = a.d_k;
+  if (a.s_ld == 0) a.s_ld = a.L;
+  if (a.q_head_stride < 0 || a.q_row_stride < 0 || a.k_head_stride < 0 || a.k_tok_stride < 0)
+    return KVS_EINVAL;
+  if (!mult8(a.q_head_stride) || !mult8(a.q_row_stride) || !mult8(a.k_head_stride) ||
+      !mult8(a.k_tok_stride))
+    return KVS_EINVAL;
+  if (a.s_ld < a.L) return KVS_EINVAL;
+  const int G = a.H_q / a.H_kv;
+  const int hr = a.W <= 8 ? 8 : a.W <= 16 ? 16 : 32;   // a head's rows, padded
+  if ((int64_t)G * hr > 128) return KVS_EUNSUPPORTED;
+  if (!Q || !K || !S) return KVS_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || ((uintptr_t)S & 3u)) return KVS_EINVAL;
+  RawLaunch p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.S = S;
+  p.qhs = a.q_head_stride;
+  p.qrs = a.q_row_stride;
+  p.khs = a.k_head_stride;
+  p.kts = a.k_tok_stride;
+  p.s_ld = a.s_ld;
+  p.L = a.L;
+  p.W = a.W;
+  p.G = G;
+  p.H_kv = a.H_kv;
+  p.d_k = a.d_k;
+  p.head_rows = hr;
+  p.reduce_max = a.reduce == KVS_RED_MAX;
+  p.accumulate = a.accumulate;
+  p.scale = a.scale > 0.f ? a.scale : (float)(1.0 / sqrt((double)a.d_k));
+  return score_raw_run(p, as_stream(stream));
+}
+
 kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld, int32_t head_reduce,
                           int32_t pool, int32_t pool_k, int32_t P, int32_t page_reduce,
                           float* pooled, float* page, int32_t* page_arg, void* stream) {
   if (!S || H < 1 || n < 1 || ld < n) return KVS_EINVAL;
-  if (head_reduce != KVS_RED_NONE && head_reduce != KVS_RED_SUM && head_reduce != KVS_RED_MAX)
+  if (head_reduce != KVS_RED_NONE && head_reduce != KVS_RED_SUM && head_reduce != KVS_RED_MAX &&
+      head_reduce != KVS_RED_MEAN)
     return KVS_EINVAL;
   if (pool != KVS_RED_NONE && pool != KVS_RED_MAX && pool != KVS_RED_MEAN) return KVS_EINVAL;
   if (pool != KVS_RED_NONE && (pool_k < 1 || (pool_k & 1) == 0)) return KVS_EINVAL;

@@ -43,6 +43,18 @@ struct ScoreLaunch {
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* plan);
 kvs_status score_run(const ScorePlan& plan, const ScoreLaunch& p, hipStream_t stream);
 
+// Raw logits reduced over all heads (kvs_score_raw); head_rows pads each
+// head's W rows as for the softmax scores.
+struct RawLaunch {
+  const uint16_t* Q;
+  const uint16_t* K;
+  float* S;
+  int64_t qhs, qrs, khs, kts, s_ld;
+  int L, W, G, H_kv, d_k, head_rows, reduce_max, accumulate;
+  float scale;
+};
+kvs_status score_raw_run(const RawLaunch& p, hipStream_t stream);
+
 // ---------------------------------------------------------------- others
 kvs_status pool_pages_run(const float* S, int H, int n, int64_t ld, int head_reduce, int pool,
                           int pool_k, int P, int page_reduce, float* pooled, float* page,

@@ -25,9 +25,9 @@ __device__ __forceinline__ float reduced(const float* S, int H, int64_t ld, int 
   float v = S[t];
   for (int h = 1; h < H; ++h) {
     const float x = S[(int64_t)h * ld + t];
-    v = head_reduce == KVS_RED_SUM ? v + x : fmaxf(v, x);
+    v = head_reduce == KVS_RED_MAX ? fmaxf(v, x) : v + x;
   }
-  return v;
+  return head_reduce == KVS_RED_MEAN ? v / (float)H : v;
 }
 
 __global__ __launch_bounds__(kThreads) void pool_pages_kernel(

@@ -1159,6 +1159,188 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ raw logits
+// kvs_score_raw: R[j][t] = SUM or MAX over all query heads of scale * q.k, in
+// one pass over K.  Each workgroup owns a run of key tiles for every KV head,
+// so the reduction over heads, and over KV heads, happens in registers in a
+// fixed order: no atomics, no second kernel, bit-reproducible.  The padded
+// query rows of all KV heads sit in LDS for the whole kernel (staged once
+// with coalesced loads, in the K-tile layout); each (key tile, KV head) step
+// reads its K tile from the wave's 3-stage ring and the head's query
+// fragments from LDS, the next step's fragments being read while this step's
+// MFMAs run.
+// The MFMA tile is 32 padded query rows (M) x 32 keys (N), so a lane holds one
+// key and 16 rows: rows 8(i/4) + 4(l/32) + i%4 of each row tile.  Each head's
+// W rows are padded to HR = 8, 16 or 32 rows, which puts the rows of every
+// head that share a query index j in the same lane: the reduction over heads
+// is in-lane, and each output row j is stored as 32 consecutive keys.
+constexpr int kRawStages = 3;
+template <int D>
+constexpr int raw_q_tiles() { return D == 128 ? 8 : 28; }   // LDS left beside the ring
+
+struct RawArgs {
+  RawLaunch p;
+  int n_tiles, tps;
+};
+
+// Padded query rows 32T .. 32T+31 of KV head g into an LDS tile (layout of
+// issue_tile).  Padding rows read the group's first row; they are dropped
+// before the reduction.
+template <int D>
+__device__ __forceinline__ void issue_raw_q(uint8_t* dst, const RawArgs& a, int g, int T, int lane) {
+  constexpr int CR = D / 8;
+  constexpr int RPI = 64 / CR;
+  const int p = lane % CR;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const int tr = j * RPI + lane / CR;
+    const int r = 32 * T + tr;
+    const int hq = r / a.p.head_rows, jr = r % a.p.head_rows;
+    const bool valid = hq < a.p.G && jr < a.p.W;
+    const uint16_t* row = a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs +
+                          (int64_t)(valid ? jr : 0) * a.p.qrs;
+    const int c = p ^ (tr % CR);
+    __builtin_amdgcn_global_load_lds(row + 8 * c, (lds_void*)(dst + j * 1024), 16, 0, 0);
+  }
+}
+
+template <bool MAX>
+__device__ __forceinline__ float raw_combine(float x, float y) {
+  return MAX ? fmaxf(x, y) : x + y;
+}
+
+template <int D, int HR, int NT, bool MAX>
+__global__ __launch_bounds__(kThreads, 1) void score_raw_kernel(RawArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int S = kRawStages;
+  constexpr int TB = tile_bytes<D>();
+  constexpr int NS = HR / 2;   // output rows j a lane holds
+  __shared__ __attribute__((aligned(16))) uint8_t qs[raw_q_tiles<D>()][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][TB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 31, hl = lane >> 5;
+  const int H = a.p.H_kv;
+  const int tb = blockIdx.x * a.tps;
+  const int te = min(tb + a.tps, a.n_tiles);
+  const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
+  const int steps = nt * H;   // (key tile, KV head) pairs, KV head fastest
+  const auto kbase = [&](int s) { return a.p.K + (int64_t)(s % H) * a.p.khs; };
+  const auto t0_of = [&](int s) { return (tb + wave + (s / H) * kWaves) * 32; };
+  const auto issue_k = [&](int s) {
+    issue_tile<D>(ring[wave][s % S], kbase(s), a.p.kts, t0_of(s), a.p.L, lane);
+  };
+
+  // query rows of every KV head, then the first K tiles behind them
+  for (int u = wave; u < H * NT; u += kWaves) issue_raw_q<D>(qs[u], a, u / NT, u % NT, lane);
+  const int pre = steps < S - 1 ? steps : S - 1;
+  for (int s = 0; s < pre; ++s) issue_k(s);
+  if (pre == 2)
+    wait_vm<2 * KS>();
+  else if (pre == 1)
+    wait_vm<KS>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();   // bare: a fenced barrier would wait for the K tiles too
+
+  uint32_t foff[KS];
+  frag_offsets<D>(foff, lane);
+  const uint32_t q0 = lds_addr(qs[0]);
+  const auto read_k = [&](int s, u32x4(&f)[KS]) {
+    read_frags<KS>(f, lds_addr(ring[wave][s % S]), foff);
+  };
+  const auto read_q = [&](int s, u32x4(&f)[NT][KS]) {
+#pragma unroll
+    for (int T = 0; T < NT; ++T) read_frags<KS>(f[T], q0 + ((s % H) * NT + T) * TB, foff);
+  };
+  const auto wait_frags = [&](u32x4(&k)[KS], u32x4(&q)[NT][KS]) {
+    wait_lgkm<KS>(k);
+#pragma unroll
+    for (int T = 0; T < NT; ++T) wait_lgkm<KS>(q[T]);
+  };
+  float run[NS];
+  // step s: MFMAs on the fragments in kc/qc while tile s+1's are read into kn/qn
+  const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&qc)[NT][KS], u32x4(&kn)[KS],
+                        u32x4(&qn)[NT][KS]) {
+    const int g = s % H;
+    const bool last = g == H - 1;
+    const int t = t0_of(s) + nl;
+    // the values an accumulating call combines with, queued before the next tile
+    float prev[NS];
+    if (last && a.p.accumulate != KVS_ACC_WRITE) {
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int j = 8 * (q / 4) + 4 * hl + (q % 4);
+        prev[q] = (j < a.p.W && t < a.p.L) ? a.p.S[(int64_t)j * a.p.s_ld + t] : 0.f;
+      }
+    }
+    if (s + S - 1 < steps) issue_k(s + S - 1);
+    f32x16 acc[NT];
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      acc[T] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qc[T][k]),
+                                                         __builtin_bit_cast(bf16x8, kc[k]), acc[T],
+                                                         0, 0, 0);
+    }
+    if (s + 1 < steps) {
+      if (s + S - 1 < steps)
+        wait_vm<KS>();   // tile s+1 in, tile s+2 may still be on its way
+      else
+        wait_vm<0>();
+      read_k(s + 1, kn);
+      read_q(s + 1, qn);
+    }
+    // reduce over the heads: row tile T, element i is head (32T + 8(i/4) + 4hl + i%4) / HR
+    float v[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) v[q] = MAX ? kNegInf : 0.f;
+#pragma unroll
+    for (int T = 0; T < NT; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hq = (32 * T + 8 * (i / 4) + (i % 4)) / HR;   // same for both lane halves
+        if (hq < a.p.G) v[i % NS] = raw_combine<MAX>(v[i % NS], acc[T][i] * a.p.scale);
+      }
+#pragma unroll
+    for (int q = 0; q < NS; ++q) run[q] = g == 0 ? v[q] : raw_combine<MAX>(run[q], v[q]);
+    if (last && t < a.p.L) {
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int j = 8 * (q / 4) + 4 * hl + (q % 4);
+        if (j < a.p.W) {
+          float y = run[q];
+          if (a.p.accumulate == KVS_ACC_ADD)
+            y += prev[q];
+          else if (a.p.accumulate == KVS_ACC_MAX)
+            y = fmaxf(prev[q], y);
+          a.p.S[(int64_t)j * a.p.s_ld + t] = y;
+        }
+      }
+    }
+    if (s + 1 < steps) wait_frags(kn, qn);
+  };
+
+  u32x4 k0[KS], k1[KS], q0f[NT][KS], q1f[NT][KS];
+  if (steps > 0) {
+    if (pre == 2)
+      wait_vm<KS>();
+    else
+      wait_vm<0>();
+    read_k(0, k0);
+    read_q(0, q0f);
+    wait_frags(k0, q0f);
+  }
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(s, k0, q0f, k1, q1f);
+    step(s + 1, k1, q1f, k0, q0f);
+  }
+  if (s < steps) step(s, k0, q0f, k1, q1f);
+}
+
 template <int D, int NT>
 kvs_status launch_rounds(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t stream) {
   for (int g0 = 0; g0 < p.H_kv; g0 += pl.head_batch) {
@@ -1236,6 +1418,58 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->ws_stats = align_up((size_t)a->H_kv * pl->n_split * pl->rows_pad * sizeof(float2), kWsAlign);
   pl->ws_total = pl->ws_stats;
   return KVS_OK;
+}
+
+namespace {
+
+template <int D, int HR, int NT>
+kvs_status raw_launch(const RawLaunch& p, hipStream_t stream) {
+  if (p.H_kv * NT > raw_q_tiles<D>()) return KVS_EUNSUPPORTED;
+  RawArgs a;
+  a.p = p;
+  a.n_tiles = (p.L + 31) / 32;
+  // One 4-wave workgroup per CU, each over a contiguous run of key tiles (of
+  // every KV head), at least one tile per wave.
+  const int max_split = a.n_tiles / kWaves > 1 ? a.n_tiles / kWaves : 1;
+  const int ns = 256 < max_split ? 256 : max_split;
+  a.tps = (a.n_tiles + ns - 1) / ns;
+  const int n_split = (a.n_tiles + a.tps - 1) / a.tps;
+  if (p.reduce_max)
+    hipLaunchKernelGGL((score_raw_kernel<D, HR, NT, true>), dim3(n_split), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((score_raw_kernel<D, HR, NT, false>), dim3(n_split), dim3(kThreads), 0,
+                       stream, a);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+template <int D, int HR>
+kvs_status raw_launch_hr(const RawLaunch& p, hipStream_t stream) {
+  switch ((p.G * HR + 31) / 32) {
+    case 1: return raw_launch<D, HR, 1>(p, stream);
+    case 2: return raw_launch<D, HR, 2>(p, stream);
+    case 3: return raw_launch<D, HR, 3>(p, stream);
+    case 4: return raw_launch<D, HR, 4>(p, stream);
+    default: return KVS_EUNSUPPORTED;
+  }
+}
+
+template <int D>
+kvs_status raw_launch_d(const RawLaunch& p, hipStream_t stream) {
+  switch (p.head_rows) {
+    case 8: return raw_launch_hr<D, 8>(p, stream);
+    case 16: return raw_launch_hr<D, 16>(p, stream);
+    case 32: return raw_launch_hr<D, 32>(p, stream);
+    default: return KVS_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+kvs_status score_raw_run(const RawLaunch& p, hipStream_t stream) {
+  if (p.d_k == 128) return raw_launch_d<128>(p, stream);
+  if (p.d_k == 64) return raw_launch_d<64>(p, stream);
+  return KVS_EUNSUPPORTED;
 }
 
 kvs_status score_run(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t stream) {

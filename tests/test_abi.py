@@ -77,6 +77,38 @@ def test_score_rejects_null_misaligned_and_small_workspace(kvs):
     assert lib.kvs_score(None, P(16), P(16), P(16), P(256), 1 << 20, None) == -1
 
 
+def _raw_args(kvs, **kw):
+    base = dict(L=4096, W=8, d_k=128, H_q=32, H_kv=8, q_pos0=4096, reduce=kvs.RED_MAX)
+    base.update(kw)
+    return kvs.raw_args(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), -1), (dict(W=0), -1), (dict(H_q=3, H_kv=2), -1), (dict(reduce=0), -1),
+    (dict(reduce=3), -1), (dict(accumulate=3), -1), (dict(scale=-1.0), -1),
+    (dict(q_pos0=4094), -2), (dict(d_k=96), -2), (dict(W=33), -2),
+    (dict(H_q=16, H_kv=1, W=16), -2),             # 16 heads x 16 padded rows > 128
+    (dict(H_q=64, H_kv=16), -2),                  # 16 KV heads of query rows exceed the LDS share
+    (dict(d_k=64, H_q=120, H_kv=30, W=8), -2),    # 30 row tiles > 28 at d_k 64
+    (dict(q_row_stride=65), -1), (dict(s_ld=100), -1),
+])
+def test_score_raw_rejects(kvs, kw, status):
+    lib = kvs.library()
+    a = _raw_args(kvs, **kw)
+    P = ctypes.c_void_p
+    assert lib.kvs_score_raw(ctypes.byref(a), P(16), P(16), P(16), None) == status
+
+
+def test_score_raw_rejects_null_and_misaligned(kvs):
+    lib = kvs.library()
+    a = _raw_args(kvs)
+    P = ctypes.c_void_p
+    assert lib.kvs_score_raw(ctypes.byref(a), None, P(16), P(16), None) == -1
+    assert lib.kvs_score_raw(ctypes.byref(a), P(16), P(24), P(16), None) == -1
+    assert lib.kvs_score_raw(ctypes.byref(a), P(16), P(16), P(18), None) == -1
+    assert lib.kvs_score_raw(None, P(16), P(16), P(16), None) == -1
+
+
 def test_other_entry_points_reject(kvs):
     lib = kvs.library()
     P = ctypes.c_void_p
