@@ -49,10 +49,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--workload", default="mistral128k", choices=sorted(WORKLOADS),
+                    help="mistral128k: the softmax window-score path (default); gemfilter128k and "
+                         "specprefill128k: the raw-logit paths")
     return ap.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_colsum_mistral128k_traffic.txt")
+WORKLOADS = {
+    # workload: (kernel-stats summary, traffic summary, kernel name fragment, kernel label)
+    "mistral128k": ("kvs_mistral128k_kernel_stats.md", "score_colsum_mistral128k_traffic.txt",
+                    "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
+    "gemfilter128k": ("kvs_gemfilter128k_kernel_stats.md", "score_raw_gemfilter128k_traffic.txt",
+                      "score_raw", "score_raw_kernel (kvs_score_raw, SUM over heads, W = 1)"),
+    "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
+                        "score_raw", "score_raw_kernel (kvs_score_raw, MAX over heads, W = 8)"),
+}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 SCORE_SOURCE = os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "score.hip")
 
 
@@ -61,13 +73,14 @@ def source_hash():
     return hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per column-sum launch from the committed counter summary, or
-    None when the summary is missing or was taken on another kernel source."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def measured_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per launch of the roofline kernel from a committed counter
+    summary, or None when the summary is missing or was taken on another
+    kernel source."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -102,50 +115,65 @@ def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=8
                       f"{sec:.2f} s each; score + page max + cluster priority + top-k in float64 NumPy"}
 
 
-PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace -o bench -- "
-             "python3 bench.py --no-cpu-baseline --copy-calibration",
-    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE -o bench -- "
-                  "python3 bench.py --no-cpu-baseline --copy-calibration --steps 10 --warmup 2",
-    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE -o bench -- "
-                  "python3 bench.py --no-cpu-baseline --copy-calibration --steps 10 --warmup 2",
+def profile_commands(workload="mistral128k"):
+    wl = "" if workload == "mistral128k" else f" --workload {workload}"
+    d = "" if workload == "mistral128k" else f"_{workload}"
+    base = "python3 bench.py --no-cpu-baseline --copy-calibration" + wl
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace{d} -o bench -- {base}",
+        "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE{d} -o bench -- "
+                      f"{base} --steps 10 --warmup 2",
+        "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE{d} -o bench -- "
+                      f"{base} --steps 10 --warmup 2",
+    }
+
+
+WORKLOAD_TITLES = {
+    "mistral128k": "Mistral-7B GQA layer at L = 131072, softmax window scores + cluster top-k",
+    "gemfilter128k": "Mistral-7B GQA layer at L = 131072, GemFilter raw last-token scores + pooled top-k",
+    "specprefill128k": "Mistral-7B GQA layer at L = 131072, Speculative-Prefill raw scores (8 lookahead "
+                       "queries) + mean, pool and top-k",
 }
 
 
-def summarize_profiles(out_dir):
-    """Writes the committed profile summaries from rocprofv3 CSV output.
+def summarize_profiles(out_dir, workload="mistral128k"):
+    """Writes the committed profile summaries of one bench workload from rocprofv3 CSV output.
 
-    profiles/kvs_mistral128k_kernel_stats.md: per-kernel average durations;
-    profiles/score_colsum_mistral128k_traffic.txt: HBM bytes per column-sum
-    launch from FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
-    reads for the plain 256 MiB copy in the same run.
+    profiles/kvs_<workload>_kernel_stats.md: per-kernel average durations;
+    profiles/<kernel>_<workload>_traffic.txt: HBM bytes per launch of the
+    roofline kernel from FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for the plain 256 MiB copy in the same run.
     """
     import csv
     import statistics as st
+
+    stats_name, traffic_name, frag, label = WORKLOADS[workload]
+    cmds = profile_commands(workload)
+    d = "" if workload == "mistral128k" else f"_{workload}"
 
     def short(name):
         for pre in ("void ", "kvs::(anonymous namespace)::"):
             name = name.replace(pre, "")
         return name.split("(")[0]
 
-    stats = list(csv.DictReader(open(os.path.join(out_dir, "trace", "bench_kernel_stats.csv"))))
-    lines = ["# Kernel durations, Mistral-7B GQA layer at L = 131072 (bench.py workload)", "",
+    stats = list(csv.DictReader(open(os.path.join(out_dir, f"trace{d}", "bench_kernel_stats.csv"))))
+    lines = [f"# Kernel durations, {WORKLOAD_TITLES[workload]} (bench.py workload)", "",
              "Command (repo root on the GPU box, cd /tmp first):", "",
-             "    " + PROFILE_COMMANDS["trace"], "",
+             "    " + cmds["trace"], "",
              "Calls cover the warm-up steps, the timed steps and the event-timed steps.", "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     lines += ["", f"Kernel source sha256[:16] of score.hip: {source_hash()}", ""]
-    open(os.path.join(ROOT, "profiles", "kvs_mistral128k_kernel_stats.md"), "w").write(NL.join(lines))
+    open(os.path.join(ROOT, "profiles", stats_name), "w").write(NL.join(lines))
 
     def counter(name):
-        rows = list(csv.DictReader(open(os.path.join(out_dir, f"pmc_{name}", "bench_counter_collection.csv"))))
+        rows = list(csv.DictReader(open(os.path.join(out_dir, f"pmc_{name}{d}", "bench_counter_collection.csv"))))
         per = {}
         for r in rows:
             n = r["Kernel_Name"]
-            key = ("colsum" if "score_colsum" in n else "stats" if "score_stats" in n else
+            key = ("kernel" if frag in n else "stats" if "score_stats" in n else
                    "copy" if "copyBuffer" in n else None)
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -154,40 +182,216 @@ def summarize_profiles(out_dir):
     fetch, write = counter("FETCH_SIZE"), counter("WRITE_SIZE")
     copy_kib = (256 << 20) / 1024
     f_fetch, f_write = copy_kib / fetch["copy"], copy_kib / write["copy"]
-    traffic = (fetch["colsum"] * f_fetch + write["colsum"] * f_write) * 1024
+    traffic = (fetch["kernel"] * f_fetch + write["kernel"] * f_write) * 1024
     txt = [
-        "# HBM traffic of score_colsum_kernel (kvs_score column-sum pass), Mistral-7B GQA layer, L = 131072",
+        f"# HBM traffic of {label}, {WORKLOAD_TITLES[workload]}",
         "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, medians), each scaled by the same counter's",
         "# reading for a plain 256 MiB device copy (torch copy_) in the same run.",
         "# Commands (repo root on the GPU box, cd /tmp first):",
-        "#   " + PROFILE_COMMANDS["FETCH_SIZE"],
-        "#   " + PROFILE_COMMANDS["WRITE_SIZE"],
+        "#   " + cmds["FETCH_SIZE"],
+        "#   " + cmds["WRITE_SIZE"],
         f"source_sha256_16: {source_hash()}",
         f"copy_fetch_kib: {fetch['copy']:.1f}",
         f"copy_write_kib: {write['copy']:.1f}",
         f"fetch_scale: {f_fetch:.4f}",
         f"write_scale: {f_write:.4f}",
-        f"colsum_fetch_kib: {fetch['colsum']:.1f}",
-        f"colsum_write_kib: {write['colsum']:.1f}",
-        f"stats_fetch_kib: {fetch['stats']:.1f}",
-        f"stats_write_kib: {write['stats']:.1f}",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
-        "",
+        f"kernel_fetch_kib: {fetch['kernel']:.1f}",
+        f"kernel_write_kib: {write['kernel']:.1f}",
     ]
-    open(TRAFFIC_SUMMARY, "w").write(NL.join(txt))
+    if "stats" in fetch:
+        txt += [f"stats_fetch_kib: {fetch['stats']:.1f}", f"stats_write_kib: {write['stats']:.1f}"]
+    txt += [f"traffic_bytes_per_launch: {traffic:.0f}", ""]
+    open(os.path.join(ROOT, "profiles", traffic_name), "w").write(NL.join(txt))
     print(NL.join(lines[-6:]))
     print(NL.join(txt))
 
 
+def copy_calibration(timed):
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    copy_ms = timed(lambda j: dst.copy_(src))
+    gbs = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
+    log(f"plain 256 MiB copy: {copy_ms * 1e3:.1f} us, {gbs:.0f} GB/s read+write")
+    return gbs
+
+
+def bench_raw(args):
+    """Raw-logit workloads: one layer scored with kvs_score_raw, then the selection.
+
+    gemfilter128k: the last prompt token's raw logits summed over all 32 heads
+    -> kvs_select with average pooling k = 7 -> top 20% of the prompt.
+    specprefill128k: 8 lookahead queries, max over all heads, combined into the
+    running max over layers -> kvs_pool_pages (mean over the queries, average
+    pooling k = 7) -> kvs_topk of 20%.  The step scores one layer and finalises,
+    which a multi-layer caller would do once per prompt (a conservative step).
+    """
+    import ctypes
+    import torch
+    import synth
+    import prompt_token_importance_amd as kvs
+
+    lib = kvs.library()
+    gem = args.workload == "gemfilter128k"
+    t0 = time.perf_counter()
+    ly = synth.last_token_layer() if gem else synth.lookahead_layer(0)
+    L, W, d_k, H_q, H_kv = ly.L, ly.W, ly.d_k, ly.H_q, ly.H_kv
+    budget = L // 5
+    Q = kvs.bf16_from_bits(ly.Q)
+    K0 = kvs.bf16_from_bits(ly.K)
+    Ks = [K0] + [K0.clone() for _ in range(max(0, args.rotate - 1))]
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+    reduce = kvs.RED_SUM if gem else kvs.RED_MAX
+    acc = kvs.ACC_WRITE if gem else kvs.ACC_MAX
+    ra = kvs.raw_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, reduce=reduce,
+                      accumulate=acc)
+    S = torch.zeros(W, L, dtype=torch.float32, device="cuda")
+    pooled = torch.empty(1, L, dtype=torch.float32, device="cuda")
+    idx = torch.empty(1, budget, dtype=torch.int32, device="cuda")
+    sel = kvs.select_args(budget=budget, pool=kvs.RED_MEAN, pool_k=7)
+    ws_bytes = lib.kvs_select_workspace(1, L, budget) if gem else lib.kvs_topk_workspace(1, L, budget)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+    pQ, pS, pP, pI, pW = V(Q.data_ptr()), V(S.data_ptr()), V(pooled.data_ptr()), V(idx.data_ptr()), V(ws.data_ptr())
+    pKs = [V(k.data_ptr()) for k in Ks]
+    rra, rsel = ctypes.byref(ra), ctypes.byref(sel)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.kvs_score_raw(rra, pQ, pKs[i % len(pKs)], pS, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        if gem:
+            st |= lib.kvs_select(pS, 1, L, L, rsel, pI, pW, ws_bytes, sp)
+        else:
+            st |= lib.kvs_pool_pages(pS, W, L, L, kvs.RED_MEAN, kvs.RED_MEAN, 7, 0, kvs.RED_SUM, pP,
+                                     None, None, sp)
+            st |= lib.kvs_topk(pP, 1, L, L, budget, None, 0, pI, pW, ws_bytes, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libkvs call failed in step {i}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    raw_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: raw scores {raw_ms * 1e3:.1f} us, "
+        f"selection {sel_ms * 1e3:.1f} us")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    copy_gbs = copy_calibration(timed) if args.copy_calibration else None
+    # Algorithmic bytes of one raw launch: K once, Q once, S written once (and
+    # read once when combined with the running max over layers).
+    alg_bytes = H_kv * L * d_k * 2 + H_q * W * d_k * 2 + W * L * 4 * (1 if acc == kvs.ACC_WRITE else 2)
+    achieved = alg_bytes / (raw_ms * 1e-3) / 1e9
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    desc = ("gemfilter_last_token_128k: H_q=32 H_kv=8 d_k=128 L=131072 W=1; raw logits summed over "
+            "heads -> average pool 7 -> top 20%" if gem else
+            "specprefill_lookahead_128k: H_q=32 H_kv=8 d_k=128 L=131072 W=8 lookahead queries; raw "
+            "logits max over heads into the running layer max -> mean over queries -> average pool 7 "
+            "-> top 20%")
+    out = {
+        "metric": "prompt tokens scored/sec at L=128K, 8B GQA shape; % of HBM roofline",
+        "value": L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "L": L, "W": W, "d_k": d_k, "H_q": H_q, "H_kv": H_kv,
+                   "budget": budget, "k_buffers_rotated": len(Ks)},
+        "roofline": {
+            "kernel": label,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_us": raw_ms * 1e3,
+            "kernel_source_sha256_16": source_hash(),
+            "event_us": {"raw_scores": raw_ms * 1e3, "selection": sel_ms * 1e3},
+            "copy_256MiB_GBs": copy_gbs,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline_raw(ly, gem, budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_raw(ly, gem, budget, min_seconds=10.0, max_reps=8):
+    """The fp64 oracle, as it stands, on the full raw-logit workload, one BLAS thread."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    L = ly.L
+    reps, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while reps < max_reps and (reps == 0 or t_total < min_seconds):
+            t0 = time.perf_counter()
+            R = oracle.score_raw(ly.Q, ly.K, L=L, W=ly.W, d_k=ly.d_k, H_q=ly.H_q, H_kv=ly.H_kv,
+                                 reduce=oracle.RED_SUM if gem else oracle.RED_MAX)
+            y = oracle.pool(R, oracle.RED_MEAN, 7) if gem else oracle.aggregate_raw([R], pool_k=7)[None, :]
+            oracle.topk(y, budget)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    sec = t_total / reps
+    return {"value": L / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload (one layer, all 32 heads, L={L}), {reps} repetition(s), "
+                      f"{sec:.2f} s each; raw scores + pooling + top-k in float64 NumPy"}
+
+
 def main():
-    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
-        summarize_profiles(sys.argv[2])
+    if len(sys.argv) in (3, 4) and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2], *sys.argv[3:])
         return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no collectives; see DESIGN.md for how it would shard).")
+              "(the path has no collectives; it would shard by KV head, every GPU running the same "
+              "kernels on its share of the heads).")
         sys.exit(2)
+    if args.workload != "mistral128k":
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU (torch.cuda.is_available() is False)")
+            sys.exit(1)
+        bench_raw(args)
+        return
 
     import torch
     import synth
@@ -281,16 +485,7 @@ def main():
 
     log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1+merge {pass1 * 1e3:.1f} us, "
         f"pass2 {pass2 * 1e3:.1f} us, select {select * 1e3:.1f} us")
-    copy_gbs = None
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(2):
-            dst.copy_(src)
-        copy_ms = timed(lambda j: dst.copy_(src))
-        copy_gbs = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
-        log(f"plain 256 MiB copy: {copy_ms * 1e3:.1f} us, {copy_gbs:.0f} GB/s read+write")
+    copy_gbs = copy_calibration(timed) if args.copy_calibration else None
 
     # Algorithmic bytes of one column-sum launch: K once, Q once, S written once,
     # per-row constants (negligible) -> 2048 + 32 + ~2 bytes per token.

@@ -67,6 +67,7 @@ struct Params {
   int stride;            // candidate slots per part: min(budget, kCap)
   int64_t cand_ld;       // candidate slots per row (multiple of kCap)
   uint64_t* cand;        // [H][cand_ld] (key << 31 | index)
+  uint32_t* wide;        // wide path: per-(row, part) histograms and counts
   int32_t* idx;
 };
 
@@ -578,6 +579,130 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
   write_forced(s, out);
 }
 
+// ------------------------------------------------------------------ wide rows
+// Rows whose candidates would not fit one workgroup (parts * min(budget,
+// kCap) > kCap, e.g. a 20% keep rate of a 128K-token row) run the radix
+// select across all parts of the row instead: five launches, each one
+// workgroup per (part, row), with no workgroup ever waiting for another.
+// Every launch recomputes its part's keys.  Launch P (0 < P <= 3) first fixes
+// digit P-1 from the sum over parts of that pass's per-part histograms and
+// the state (prefix, need) the previous launch left; every workgroup of the
+// row reaches the same digit, and part 0 records the new state for the next
+// launch.  Launches 0-2 then write their part's histogram of pass P; launch 3,
+// which has fixed K* and the number of K*-equal elements to take, writes the
+// part's counts of keys above and equal to K*.  Launch 4 gives each part its
+// output offset and its share of the K*-equal elements (in part order, so
+// ties still go to the lower index) and writes the chosen indices.
+constexpr int kWideMaxParts = 16;
+constexpr int kCnt = 4096 + 2048 + 1024;       // per part: the three histograms, then (gt, eq)
+constexpr int kState = kCnt + 2;               // part 0 only: state after pass p at kState + 4p
+constexpr int kWideWords = kState + 12;        // per (row, part)
+
+__device__ __forceinline__ uint32_t* wide_of(const Params& s, int row, int part) {
+  return s.wide + ((int64_t)row * s.parts + part) * kWideWords;
+}
+
+// The digit of pass p from the per-part histograms of the row, given the
+// prefix and need before it.  Leaves (prefix, need, all_eq) in sh.
+__device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint64_t prefix,
+                                          uint32_t need, uint32_t* hist, Shared& sh) {
+  const int nb = pass_bins(p);
+  for (int b = threadIdx.x; b < nb; b += kT) {
+    uint32_t c[kWideMaxParts];
+#pragma unroll
+    for (int q = 0; q < kWideMaxParts; ++q)
+      c[q] = q < s.parts ? wide_of(s, row, q)[pass_offset(p) + b] : 0u;
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < kWideMaxParts; ++q) v += c[q];
+    hist[b] = v;
+  }
+  __syncthreads();
+  pick_digit(hist, p, prefix, need, sh);
+}
+
+template <int T, int STAGE>
+__global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
+  __shared__ uint32_t smem[LdsWords<T>::value];
+  __shared__ Shared sh;
+  const int row = blockIdx.y, part = blockIdx.x;
+  const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
+  uint64_t k[kKpt];
+  uint32_t valid;
+  part_keys<T>(s, row, p0, p1, smem, k, valid);
+  uint32_t* mine = wide_of(s, row, part);
+  uint32_t* state = wide_of(s, row, 0) + kState;
+  // the state before this launch's digit, then the digit itself
+  uint64_t prefix = 0;
+  uint32_t need = (uint32_t)s.budget;
+  if constexpr (STAGE >= 2) {
+    const uint32_t* st = state + 4 * (STAGE - 2);
+    prefix = ((uint64_t)st[1] << 32) | st[0];
+    need = st[2];
+    if constexpr (STAGE == 4) {
+      if (threadIdx.x == 0) sh.all_eq = st[3];
+      __syncthreads();
+    }
+  }
+  if constexpr (STAGE >= 1 && STAGE <= 3) {
+    wide_pick(s, row, STAGE - 1, prefix, need, smem, sh);
+    prefix = sh.prefix;
+    need = sh.need;
+    if (part == 0 && threadIdx.x == 0) {
+      uint32_t* st = state + 4 * (STAGE - 1);
+      st[0] = (uint32_t)prefix;
+      st[1] = (uint32_t)(prefix >> 32);
+      st[2] = need;
+      st[3] = sh.all_eq;
+    }
+  }
+  if constexpr (STAGE < 3) {
+    uint32_t* h = smem;
+    for (int b = threadIdx.x; b < pass_bins(STAGE); b += kT) h[b] = 0u;
+    __syncthreads();
+    hist_add(h, STAGE, prefix, k, valid);
+    __syncthreads();
+    for (int b = threadIdx.x; b < pass_bins(STAGE); b += kT) mine[pass_offset(STAGE) + b] = h[b];
+  } else if constexpr (STAGE == 3) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      const bool ok = (valid >> e) & 1u;
+      gt += (ok && k[e] > prefix) ? 1u : 0u;
+      eq += (ok && k[e] == prefix) ? 1u : 0u;
+    }
+    uint32_t tot_gt, tot_eq;
+    scan_excl(gt, sh, tot_gt);
+    scan_excl(eq, sh, tot_eq);
+    if (threadIdx.x == 0) {
+      mine[kCnt] = tot_gt;
+      mine[kCnt + 1] = tot_eq;
+    }
+  } else {
+    // offset of this part's output and its share of the K*-equal elements
+    uint32_t gt_before = 0, eq_before = 0;
+    for (int q = 0; q < part; ++q) {
+      gt_before += wide_of(s, row, q)[kCnt];
+      eq_before += wide_of(s, row, q)[kCnt + 1];
+    }
+    const uint32_t my_eq = mine[kCnt + 1];
+    const uint32_t take_eq = need > eq_before ? min(need - eq_before, my_eq) : 0u;
+    const uint32_t base = gt_before + min(eq_before, need);
+    uint32_t sel_eq, tot;
+    const uint32_t sel = choose(k, valid, prefix, take_eq, 0u, sh, sel_eq);
+    uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot) + base;
+    int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
+    const int i0 = p0 + (int)threadIdx.x * kKpt;
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if ((sel >> e) & 1u) {
+        if (pos < (uint32_t)s.budget) out[pos] = i0 + e;   // the counts make pos < budget
+        ++pos;
+      }
+    if (part == 0) write_forced(s, out);
+  }
+}
+
 // budget == 0: only the forced suffix.
 __global__ __launch_bounds__(256) void topk_forced_kernel(int n, int n_forced,
                                                           int32_t* __restrict__ idx) {
@@ -599,10 +724,27 @@ void launch(const Params& s, int H, hipStream_t stream) {
   if (s.parts > 1) hipLaunchKernelGGL(topk_merge_kernel, dim3(H), dim3(kT), 0, stream, s);
 }
 
+bool wide_path(int n, int budget) {
+  const int parts = parts_of(n);
+  return parts > 1 && parts <= kWideMaxParts && (int64_t)parts * stride_of(budget) > kCap;
+}
+
+template <int T>
+void launch_wide(const Params& s, int H, hipStream_t stream) {
+  const dim3 grid(s.parts, H);
+  hipLaunchKernelGGL((topk_wide_kernel<T, 0>), grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL((topk_wide_kernel<T, 1>), grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL((topk_wide_kernel<T, 2>), grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL((topk_wide_kernel<T, 3>), grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL((topk_wide_kernel<T, 4>), grid, dim3(kT), 0, stream, s);
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(int H, int n, int budget) {
   if (budget <= 0 || parts_of(n) == 1) return 0;
+  if (wide_path(n, budget))
+    return align_up((size_t)H * parts_of(n) * kWideWords * sizeof(uint32_t), kWsAlign);
   return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
 }
 
@@ -631,13 +773,15 @@ kvs_status select_run(const SelectCall& c, hipStream_t stream) {
   s.stride = stride_of(c.budget);
   s.cand_ld = cand_ld_of(c.n, c.budget);
   s.cand = static_cast<uint64_t*>(c.ws);
+  s.wide = static_cast<uint32_t*>(c.ws);
   s.idx = c.idx;
+  const bool wide = wide_path(c.n, c.budget);
   if (c.cluster_P > 0)
-    launch<kCluster>(s, c.H, stream);
+    wide ? launch_wide<kCluster>(s, c.H, stream) : launch<kCluster>(s, c.H, stream);
   else if (c.pool != KVS_RED_NONE)
-    launch<kPool>(s, c.H, stream);
+    wide ? launch_wide<kPool>(s, c.H, stream) : launch<kPool>(s, c.H, stream);
   else
-    launch<kPlain>(s, c.H, stream);
+    wide ? launch_wide<kPlain>(s, c.H, stream) : launch<kPlain>(s, c.H, stream);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 

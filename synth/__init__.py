@@ -209,6 +209,21 @@ def cross_layer(layer: int, L: int = 16384, base_seed: int = 3, H_q: int = 32, H
                           fixed_span_seed=base_seed, n_fixed=4)
 
 
+def last_token_layer(L: int = 131072, seed: int = 5, n_spans: int = 16, span_len: int = 512) -> Layer:
+    """Mistral-7B-shaped layer with one query row, the last prompt token (GemFilter)."""
+    return gaussian_layer(seed, L=L, W=1, d_k=128, H_q=32, H_kv=8, q_pos0=L - 1,
+                          n_spans=n_spans, span_len=span_len, lift=2.0, span_region=L - 1)
+
+
+def lookahead_layer(layer: int = 0, L: int = 131072, k: int = 8, base_seed: int = 6,
+                    n_spans: int = 16, span_len: int = 512) -> Layer:
+    """Layer ``layer`` of a Mistral-7B-shaped model with k lookahead queries after the
+    prompt (Speculative Prefill); span slots 0-7 fixed across layers."""
+    return gaussian_layer(base_seed + layer, L=L, W=k, d_k=128, H_q=32, H_kv=8, q_pos0=L,
+                          n_spans=n_spans, span_len=span_len, lift=2.0, span_region=L,
+                          fixed_span_seed=base_seed, n_fixed=n_spans // 2)
+
+
 @dataclasses.dataclass
 class Chunk:
     """Chunked-prefill block-selection inputs."""

@@ -85,6 +85,13 @@ TOPK_CASES = [
     (3, 4097, 4097, 0, 4, True),
     (2, 2048, 1000, 0, 2, False),        # two values only: ties decide almost everything
     (4, 3001, 1500, 0, 0, True),
+    # rows selected across all their parts (more candidates than one workgroup holds)
+    (1, 131072, 26214, 0, 0, False),     # 20% of a 128K row
+    (2, 40000, 6000, 3, 7, True),        # ties, NaN, +-inf, priority; three parts
+    (3, 50000, 20000, 2, 2, False),      # two values only: ties spread over the parts
+    (2, 32769, 16385, 0, 5, True),       # last part of one element
+    (1, 262144, 100000, 0, 0, False),    # the most parts this path takes
+    (1, 262145, 100000, 0, 3, False),    # one part more: the single-workgroup merge
 ]
 
 
@@ -207,6 +214,8 @@ SELECT_POOL_CASES = [
     (3, 12, 5, 1, 31, 0),              # widest register-window pooling
     (2, 48, 10, 0, 33, 3),             # beyond the register window: staged path
     (2, 16388, 500, 0, 7, 5),          # second part of four elements
+    (1, 131072, 26214, 0, 7, 0),       # GemFilter keep rate 20%, across all parts
+    (2, 40000, 9000, 5, 7, 6),         # across all parts, with ties
 ]
 
 
@@ -251,6 +260,7 @@ SELECT_CLUSTER_CASES = [
     (1, 48, 7, 2, 16, 1.0, 16, 1.0),            # widest register-window radius
     (3, 16388, 500, 0, 16, 2.0, 3, 1.0),        # second part of four elements
     (2, 16390, 500, 0, 16, 2.0, 3, 1.0),        # n % 4 != 0: staged path
+    (2, 60000, 20000, 4, 16, 2.0, 3, 1.0),      # across all parts
 ]
 
 
