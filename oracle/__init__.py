@@ -16,6 +16,7 @@ from .kvs import (  # noqa: F401
     pages,
     pool_pages,
     aggregate_layers,
+    delta_pages,
     cluster_priority,
     topk,
     block_select,

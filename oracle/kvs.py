@@ -277,6 +277,42 @@ def pool_pages(S, *, head_mode: int = RED_NONE, pool_mode: int = RED_NONE, pool_
 
 
 # ---------------------------------------------------------------------------
+# DELTA decode-time page sets
+# ---------------------------------------------------------------------------
+
+def delta_pages(Q, K, *, L: int, d_k: int, H_q: int, H_kv: int, P: int = 16, K_pages: int = 64,
+                L_recent: int = 8, scale: Optional[float] = None):
+    """DELTA's page set rho for one decode query of one sequence at a Delta-layer.
+
+    [DELTA] "Key design 2": the token score is the maximum over the heads of the
+    decode query's softmax attention, s_t = max_j alpha_j(t); a page's score is
+    the sum of its tokens' scores; rho is the last L pages together with the
+    top K - L of the remaining pages by page score.  "Key design 3": pages of
+    P = 16 tokens, K = 64 pages, L = 8 recent pages.
+
+    Q: bf16 bits [H_q][d_k], the decode token's query at position L - 1 (it sees
+    every cached key).  K: bf16 bits [H_kv][L][d_k].
+    Returns (rho, page_scores): rho int64 [K_pages] lists the chosen older pages
+    in ascending order, then the recent pages in ascending order, then -1 for
+    unused slots; page_scores float64 [ceil(L / P)].
+    """
+    if K_pages < L_recent or L_recent < 0:
+        raise ValueError("need 0 <= L_recent <= K_pages")
+    a = score(np.asarray(Q).reshape(H_q, 1, d_k), K, L=L, W=1, d_k=d_k, H_q=H_q, H_kv=H_kv,
+              q_pos0=L - 1, heads=HEADS_NONE, scale=scale)     # [H_q][L] softmax rows
+    s = a.max(axis=0, keepdims=True)                          # max over heads
+    z, _ = pages(s, P, RED_SUM)                               # page sums
+    n_pages = z.shape[1]
+    n_recent = min(L_recent, n_pages)
+    n_cand = n_pages - n_recent
+    keep = min(K_pages - L_recent, n_cand)
+    chosen = topk(z[:, :n_cand], keep, None, n_recent)[0]     # ascending, then the recent pages
+    rho = np.full(K_pages, -1, dtype=np.int64)
+    rho[:len(chosen)] = chosen
+    return rho, z[0]
+
+
+# ---------------------------------------------------------------------------
 # Cross-layer aggregation
 # ---------------------------------------------------------------------------
 
