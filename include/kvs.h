@@ -168,6 +168,50 @@ kvs_status kvs_score_raw(const kvs_raw_args* a, const void* Q, const void* K, fl
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_delta_pages - DELTA decode-time page sets for a batch of sequences.
+ *
+ * [DELTA] "Key design 2": at a Delta-layer, for the decode query of each
+ * sequence b (context length L_b, the query at position L_b - 1 sees every
+ * cached key), the token score is the maximum over the H_q heads of the
+ * softmax attention, s_t = max_h softmax_t(scale * Q[b][h] . K_b[h / G][t]);
+ * the page score is S_u = sum of s_t over the P tokens of page u (the last page
+ * may be partial); rho_b = the top K_pages - L_recent of the pages before the
+ * last L_recent by S_u, in ascending order, then the last min(L_recent,
+ * pages) pages in ascending order, then -1 up to K_pages entries.  Page-score
+ * ties go to the lower page.  "Key design 3": P = 16, K_pages = 64,
+ * L_recent = 8.
+ * Q: bf16 [B][H_q][d_k], contiguous.  K: device array of B device pointers,
+ * each 16-byte aligned; sequence b's keys are bf16, element [g][t][c] at
+ * K[b] + g * k_head_stride +
+ * t * k_tok_stride + c (k_head_stride 0 selects L_b * d_k, k_tok_stride 0
+ * selects d_k).  L: device int32 [B]; each length is clamped to [0, L_max]
+ * (a sequence of length 0 gets an all -1 row).  rho: int32 [B][K_pages].
+ * page_scores: float32 [B][ceil(L_max / P)] receiving S_u for the pages of
+ * each sequence (other entries untouched), or NULL.
+ * Workspace: kvs_delta_workspace bytes, 16-byte aligned, contents undefined
+ * on entry and return (the logits of every head, 4 * H_q bytes per cached
+ * token, and per-chunk softmax statistics).
+ * Limits (else KVS_EUNSUPPORTED): d_k in {64, 128}; H_q <= 128; P divides
+ * 2048; ceil(L_max / P) <= 16384.  K is read once; the result is
+ * bit-identical from run to run.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t B;          /* sequences                                            */
+  int32_t d_k, H_q, H_kv;
+  int32_t P;          /* tokens per page                                      */
+  int32_t K_pages;    /* pages in each rho row, >= L_recent                   */
+  int32_t L_recent;   /* most recent pages always kept, >= 0                  */
+  int32_t L_max;      /* bound on every context length, >= 1                  */
+  int64_t k_head_stride, k_tok_stride;
+  float scale;        /* logit scale, 0 => 1/sqrt(d_k); must be >= 0          */
+} kvs_delta_args;
+
+size_t kvs_delta_workspace(const kvs_delta_args* a);
+kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* const* K,
+                           const int32_t* L, int32_t* rho, float* page_scores, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_pool_pages - head reduction, 1-D pooling, page aggregation.
  *
  * Input S float32 [H][n] with row stride ld (>= n).  In this order:

@@ -53,6 +53,16 @@ class RawArgs(ctypes.Structure):
     ]
 
 
+class DeltaArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("d_k", ctypes.c_int32), ("H_q", ctypes.c_int32),
+        ("H_kv", ctypes.c_int32), ("P", ctypes.c_int32), ("K_pages", ctypes.c_int32),
+        ("L_recent", ctypes.c_int32), ("L_max", ctypes.c_int32),
+        ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
 class BlockSelectArgs(ctypes.Structure):
     _fields_ = [
         ("Lq", ctypes.c_int32), ("L", ctypes.c_int32), ("d_k", ctypes.c_int32),
@@ -85,6 +95,8 @@ def _load():
         "kvs_score_workspace": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvs_score_raw": (I32, [ctypes.POINTER(RawArgs), P, P, P, P]),
+        "kvs_delta_workspace": (SZ, [ctypes.POINTER(DeltaArgs)]),
+        "kvs_delta_pages": (I32, [ctypes.POINTER(DeltaArgs), P, P, P, P, P, P, SZ, P]),
         "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvs_topk_workspace": (SZ, [I32, I32, I32]),
         "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, SZ, P]),
@@ -109,6 +121,7 @@ _lib = _load()
 
 EXPORTED = (
     "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_raw",
+    "kvs_delta_workspace", "kvs_delta_pages",
     "kvs_pool_pages",
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
     "kvs_block_union_workspace", "kvs_block_union_pagetable",
@@ -194,6 +207,31 @@ def kvs_score_raw(Q: torch.Tensor, K: torch.Tensor, args: RawArgs, S: Optional[t
     _check(_lib.kvs_score_raw(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _stream(stream)),
            "kvs_score_raw")
     return S
+
+
+# --------------------------------------------------------------------------- DELTA page sets
+def delta_args(*, B, d_k, H_q, H_kv, L_max, P=16, K_pages=64, L_recent=8, k_head_stride=0,
+               k_tok_stride=0, scale=0.0) -> DeltaArgs:
+    return DeltaArgs(B=B, d_k=d_k, H_q=H_q, H_kv=H_kv, P=P, K_pages=K_pages, L_recent=L_recent,
+                     L_max=L_max, k_head_stride=k_head_stride, k_tok_stride=k_tok_stride,
+                     scale=scale)
+
+
+def kvs_delta_workspace(args: DeltaArgs) -> int:
+    return int(_lib.kvs_delta_workspace(ctypes.byref(args)))
+
+
+def kvs_delta_pages(Q: torch.Tensor, K_ptrs: torch.Tensor, L: torch.Tensor, args: DeltaArgs,
+                    rho: Optional[torch.Tensor] = None, page_scores: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rho int32 [B][K_pages].  K_ptrs: int64 device tensor [B] of bf16 K base
+    addresses; L: int32 device tensor [B] of context lengths."""
+    if rho is None:
+        rho = torch.empty(args.B, args.K_pages, dtype=torch.int32, device=Q.device)
+    ws, nb = _workspace(kvs_delta_workspace(args), Q.device, ws)
+    _check(_lib.kvs_delta_pages(ctypes.byref(args), _ptr(Q), _ptr(K_ptrs), _ptr(L), _ptr(rho),
+                                _ptr(page_scores), _ptr(ws), nb, _stream(stream)), "kvs_delta_pages")
+    return rho
 
 
 # --------------------------------------------------------------------------- pool / pages

@@ -40,6 +40,38 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
   return KVS_OK;
 }
 
+struct DeltaPlan {
+  size_t x2, cstats, S, total;   // byte offsets of the workspace parts
+  int n_chunk, n_pages_max;
+};
+
+kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
+  if (!a) return KVS_EINVAL;
+  if (a->B < 0 || a->H_q < 1 || a->H_kv < 1 || a->d_k < 1 || a->P < 1 || a->L_max < 1)
+    return KVS_EINVAL;
+  if (a->H_q % a->H_kv) return KVS_EINVAL;
+  if (a->L_recent < 0 || a->K_pages < 1 || a->K_pages < a->L_recent) return KVS_EINVAL;
+  if (!(a->scale >= 0.f) || isinf(a->scale)) return KVS_EINVAL;
+  if (a->k_head_stride < 0 || a->k_tok_stride < 0 || !mult8(a->k_head_stride) ||
+      !mult8(a->k_tok_stride))
+    return KVS_EINVAL;
+  if (a->d_k != 64 && a->d_k != 128) return KVS_EUNSUPPORTED;
+  if (a->H_q > 128 || 2048 % a->P) return KVS_EUNSUPPORTED;
+  const int64_t n_pages = ((int64_t)a->L_max + a->P - 1) / a->P;
+  if (n_pages > 16384) return KVS_EUNSUPPORTED;
+  pl->n_chunk = delta_chunks(a->L_max);
+  pl->n_pages_max = (int)n_pages;
+  size_t off = 0;
+  pl->x2 = off;
+  off = align_up(off + (size_t)a->B * a->H_q * a->L_max * sizeof(float), kWsAlign);
+  pl->cstats = off;
+  off = align_up(off + (size_t)a->B * pl->n_chunk * a->H_q * sizeof(float2), kWsAlign);
+  pl->S = off;
+  off = align_up(off + (size_t)a->B * n_pages * sizeof(float), kWsAlign);
+  pl->total = off;
+  return KVS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,6 +181,54 @@ kvs_status kvs_score_raw(const kvs_raw_args* in, const void* Q, const void* K, f
   p.accumulate = a.accumulate;
   p.scale = a.scale > 0.f ? a.scale : (float)(1.0 / sqrt((double)a.d_k));
   return score_raw_run(p, as_stream(stream));
+}
+
+size_t kvs_delta_workspace(const kvs_delta_args* a) {
+  DeltaPlan pl;
+  return delta_plan(a, &pl) == KVS_OK ? pl.total : 0;
+}
+
+kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* const* K,
+                           const int32_t* L, int32_t* rho, float* page_scores, void* ws,
+                           size_t ws_bytes, void* stream) {
+  DeltaPlan pl;
+  kvs_status st = delta_plan(a, &pl);
+  if (st != KVS_OK) return st;
+  if (a->B == 0) return KVS_OK;
+  if (!Q || !K || !L || !rho) return KVS_EINVAL;
+  if (!aligned16(Q) || ((uintptr_t)K & 7u) || ((uintptr_t)L & 3u) || ((uintptr_t)rho & 3u) ||
+      ((uintptr_t)page_scores & 3u))
+    return KVS_EINVAL;
+  if (!ws || ws_bytes < pl.total) return KVS_EWORKSPACE;
+  if (!aligned16(ws)) return KVS_EINVAL;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  DeltaLaunch p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = reinterpret_cast<const uint16_t* const*>(K);
+  p.L = L;
+  p.x2 = reinterpret_cast<float*>(w + pl.x2);
+  p.cstats = reinterpret_cast<float2*>(w + pl.cstats);
+  p.S = page_scores ? page_scores : reinterpret_cast<float*>(w + pl.S);
+  p.rho = rho;
+  p.khs = a->k_head_stride;
+  p.kts = a->k_tok_stride ? a->k_tok_stride : a->d_k;
+  p.B = a->B;
+  p.H_q = a->H_q;
+  p.H_kv = a->H_kv;
+  p.G = a->H_q / a->H_kv;
+  p.d_k = a->d_k;
+  p.P = a->P;
+  p.K_pages = a->K_pages;
+  p.L_recent = a->L_recent;
+  p.L_max = a->L_max;
+  p.n_chunk = pl.n_chunk;
+  p.n_pages_max = pl.n_pages_max;
+  const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->d_k);
+  p.c = (float)(scale * 1.4426950408889634073599246810018921);  // scale * log2(e)
+  hipStream_t s = as_stream(stream);
+  st = delta_scores_run(p, s);
+  if (st != KVS_OK) return st;
+  return delta_topk_run(p, s);
 }
 
 kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld, int32_t head_reduce,

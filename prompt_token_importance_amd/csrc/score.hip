@@ -1466,6 +1466,278 @@ kvs_status raw_launch_d(const RawLaunch& p, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+
+// ------------------------------------------------------------------ DELTA decode pages
+// kvs_delta_pages, scores half: for every sequence of the batch, the decode
+// query's logits against its cached keys and the softmax statistics per head
+// (delta_logits_kernel), then the page scores: per token the maximum over heads
+// of the softmax probability, summed over each page (delta_page_kernel).
+// A decode query is one row per head, so the logits of all heads (128 B per
+// token at 32 heads) are cheaper to keep than a second pass over K
+// (2 KiB per token at 8 KV heads x 128 dims): the first kernel writes them,
+// head-major and in log2 units, and the second reads them back.
+// delta_logits_kernel: one workgroup per (256-key chunk, sequence); each wave
+// streams (key tile, KV head) pairs like the raw-logit kernel, with all the
+// sequence's query rows (one per head) in LDS and the MFMA tile oriented
+// rows x keys.  A lane keeps, per key tile, the 16 logits of the rows it holds,
+// each taken from the step whose KV head owns the row, then writes them and
+// folds them into per-lane online statistics.
+struct DeltaArgs {
+  DeltaLaunch p;
+};
+
+template <int D>
+__device__ __forceinline__ void issue_delta_q(uint8_t* dst, const DeltaLaunch& p, int b, int T,
+                                              int lane) {
+  constexpr int CR = D / 8;
+  constexpr int RPI = 64 / CR;
+  const int pc = lane % CR;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const int tr = j * RPI + lane / CR;
+    const int h = 32 * T + tr;
+    const uint16_t* row = p.Q + ((int64_t)b * p.H_q + (h < p.H_q ? h : 0)) * D;
+    const int c = pc ^ (tr % CR);
+    __builtin_amdgcn_global_load_lds(row + 8 * c, (lds_void*)(dst + j * 1024), 16, 0, 0);
+  }
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int S = kRawStages;
+  constexpr int TB = tile_bytes<D>();
+  constexpr int TPW = kDeltaChunk / 32 / kWaves;   // key tiles per wave
+  __shared__ __attribute__((aligned(16))) uint8_t qs[NT][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][TB];
+  __shared__ float2 red[kWaves][32 * NT];
+  const DeltaLaunch& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 31, hl = lane >> 5;
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int tb = chunk * kDeltaChunk;
+  if (tb >= Lb) return;   // the whole workgroup: nothing of this sequence here
+  const uint16_t* Kb = p.K[b];
+  const int64_t khs = p.khs ? p.khs : (int64_t)Lb * D;
+  const int H = p.H_kv;
+  int nt = 0;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) nt += (tb + (wave + kWaves * j) * 32 < Lb) ? 1 : 0;
+  const int steps = nt * H;   // (key tile, KV head) pairs, KV head fastest
+  const auto t0_of = [&](int s) { return tb + (wave + kWaves * (s / H)) * 32; };
+  const auto issue_k = [&](int s) {
+    issue_tile<D>(ring[wave][s % S], Kb + (int64_t)(s % H) * khs, p.kts, t0_of(s), Lb, lane);
+  };
+
+  for (int u = wave; u < NT; u += kWaves) issue_delta_q<D>(qs[u], p, b, u, lane);
+  const int pre = steps < S - 1 ? steps : S - 1;
+  for (int s = 0; s < pre; ++s) issue_k(s);
+  if (pre == 2)
+    wait_vm<2 * KS>();
+  else if (pre == 1)
+    wait_vm<KS>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();   // bare: a fenced barrier would wait for the K tiles too
+
+  uint32_t foff[KS];
+  frag_offsets<D>(foff, lane);
+  const uint32_t q0 = lds_addr(qs[0]);
+  float out[NT][16];
+  float m[NT][16], z[NT][16];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      out[T][i] = 0.f;
+      m[T][i] = kNegInf;
+      z[T][i] = 0.f;
+    }
+  float* x2b = p.x2 + (int64_t)b * p.H_q * p.L_max;
+  for (int s = 0; s < steps; ++s) {
+    const int g = s % H;
+    if (s + S - 1 < steps) issue_k(s + S - 1);
+    const int ahead = min(steps - 1 - s, S - 1);
+    if (ahead >= 2)
+      wait_vm<2 * KS>();
+    else if (ahead == 1)
+      wait_vm<KS>();
+    else
+      wait_vm<0>();
+    u32x4 kf[KS];
+    read_frags<KS>(kf, lds_addr(ring[wave][s % S]), foff);
+    wait_lgkm<KS>(kf);
+    // the row tiles holding this KV head's query heads
+    const int t_lo = (g * p.G) / 32, t_hi = (g * p.G + p.G - 1) / 32;
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      if (T < t_lo || T > t_hi) continue;
+      u32x4 qf[KS];
+      read_frags<KS>(qf, q0 + T * TB, foff);
+      wait_lgkm<KS>(qf);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf[k]),
+                                                      __builtin_bit_cast(bf16x8, kf[k]), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = 32 * T + 8 * (i / 4) + 4 * hl + (i % 4);
+        if (h / p.G == g) out[T][i] = acc[i] * p.c;
+      }
+    }
+    if (g == H - 1) {
+      // every head's logit of key t is in: store it and fold it into the statistics
+      const int t = t0_of(s) + nl;
+      const bool valid = t < Lb;
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int h = 32 * T + 8 * (i / 4) + 4 * hl + (i % 4);
+          if (valid && h < p.H_q) {
+            const float x = out[T][i];
+            x2b[(int64_t)h * p.L_max + t] = x;
+            const float mn = fmaxf(m[T][i], x);
+            z[T][i] = z[T][i] * ex2(m[T][i] - mn) + ex2(x - mn);
+            m[T][i] = mn;
+          }
+        }
+    }
+  }
+  // statistics of each row over the workgroup's keys: lanes of a half, then waves
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float mm = m[T][i], zz = z[T][i];
+#pragma unroll
+      for (int d = 1; d < 32; d *= 2) {
+        const float m2 = __shfl_xor(mm, d), z2 = __shfl_xor(zz, d);
+        const float mx = fmaxf(mm, m2);
+        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + z2 * ex2(m2 - mx);
+        mm = mx;
+      }
+      if (nl == 0) red[wave][32 * T + 8 * (i / 4) + 4 * hl + (i % 4)] = make_float2(mm, zz);
+    }
+  __syncthreads();
+  for (int h = threadIdx.x; h < p.H_q; h += kThreads) {
+    float mm = kNegInf, zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float2 v = red[w][h];
+      const float mx = fmaxf(mm, v.x);
+      zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + v.y * ex2(v.x - mx);
+      mm = mx;
+    }
+    p.cstats[((int64_t)b * p.n_chunk + chunk) * p.H_q + h] = make_float2(mm, zz);
+  }
+}
+
+// delta_page_kernel: one workgroup per (chunk of kDeltaPageTokens tokens,
+// sequence).  It folds the sequence's per-chunk statistics into b_h = m_h +
+// log2 Z_h per head, forms s_t = max over heads of exp2(x_t,h - b_h) for its
+// tokens (a thread per token, coalesced over the head-major logits), and sums
+// each page's tokens left to right.
+constexpr int kDeltaPageTokens = 2048;
+
+__global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
+  __shared__ float bh[128];
+  __shared__ float ys[kDeltaPageTokens];
+  __shared__ float2 part[256];
+  const DeltaLaunch& p = a.p;
+  const int b = blockIdx.y;
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int t_begin = blockIdx.x * kDeltaPageTokens;
+  if (t_begin >= Lb) return;
+  const int t_end = min(t_begin + kDeltaPageTokens, Lb);
+  // 1. row constants: threads per head fold a strided share of the chunks
+  const int tph = 256 / p.H_q;                  // threads per head (H_q <= 128)
+  const int h = threadIdx.x / tph, j = threadIdx.x % tph;
+  const int nch = (Lb + kDeltaChunk - 1) / kDeltaChunk;
+  float mm = kNegInf, zz = 0.f;
+  if (h < p.H_q) {
+    const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q + h;
+    for (int c0 = j; c0 < nch; c0 += 8 * tph) {
+      float2 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = c0 + q * tph;
+        v[q] = c < nch ? cs[(int64_t)c * p.H_q] : make_float2(kNegInf, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float mx = fmaxf(mm, v[q].x);
+        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + v[q].y * ex2(v[q].x - mx);
+        mm = mx;
+      }
+    }
+  }
+  part[threadIdx.x] = make_float2(mm, zz);
+  __syncthreads();
+  if (threadIdx.x < p.H_q) {
+    float m2 = kNegInf, z2 = 0.f;
+    for (int q = 0; q < tph; ++q) {
+      const float2 v = part[threadIdx.x * tph + q];
+      const float mx = fmaxf(m2, v.x);
+      z2 = mx == kNegInf ? 0.f : z2 * ex2(m2 - mx) + v.y * ex2(v.x - mx);
+      m2 = mx;
+    }
+    bh[threadIdx.x] = m2 + log2f(z2);
+  }
+  __syncthreads();
+  // 2. token scores: max over heads of the softmax probability
+  const float* x2b = p.x2 + (int64_t)b * p.H_q * p.L_max;
+  for (int t = t_begin + (int)threadIdx.x; t < t_end; t += 256) {
+    float sv = 0.f;
+    for (int hh = 0; hh < p.H_q; ++hh) sv = fmaxf(sv, ex2(x2b[(int64_t)hh * p.L_max + t] - bh[hh]));
+    ys[t - t_begin] = sv;
+  }
+  __syncthreads();
+  // 3. page sums, left to right (chunk boundaries are multiples of P)
+  const int u0 = t_begin / p.P, u1 = (t_end + p.P - 1) / p.P;
+  float* Sb = p.S + (int64_t)b * p.n_pages_max;
+  for (int u = u0 + (int)threadIdx.x; u < u1; u += 256) {
+    const int a0 = u * p.P, a1 = min(a0 + p.P, t_end);
+    float acc = 0.f;
+    for (int t = a0; t < a1; ++t) acc += ys[t - t_begin];
+    Sb[u] = acc;
+  }
+}
+
+template <int D, int NT>
+kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream) {
+  DeltaArgs a{p};
+  hipLaunchKernelGGL((delta_logits_kernel<D, NT>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
+  const int n_page_wg = (p.L_max + kDeltaPageTokens - 1) / kDeltaPageTokens;
+  hipLaunchKernelGGL(delta_page_kernel, dim3(n_page_wg, p.B), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+template <int D>
+kvs_status delta_launch_d(const DeltaLaunch& p, hipStream_t stream) {
+  switch ((p.H_q + 31) / 32) {
+    case 1: return delta_launch<D, 1>(p, stream);
+    case 2: return delta_launch<D, 2>(p, stream);
+    case 3: return delta_launch<D, 3>(p, stream);
+    case 4: return delta_launch<D, 4>(p, stream);
+    default: return KVS_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int delta_chunks(int L_max) { return (L_max + kDeltaChunk - 1) / kDeltaChunk; }
+
+kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream) {
+  if (p.d_k == 128) return delta_launch_d<128>(p, stream);
+  if (p.d_k == 64) return delta_launch_d<64>(p, stream);
+  return KVS_EUNSUPPORTED;
+}
+
 kvs_status score_raw_run(const RawLaunch& p, hipStream_t stream) {
   if (p.d_k == 128) return raw_launch_d<128>(p, stream);
   if (p.d_k == 64) return raw_launch_d<64>(p, stream);

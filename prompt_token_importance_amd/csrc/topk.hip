@@ -703,6 +703,49 @@ __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
   }
 }
 
+// ------------------------------------------------------------------ DELTA page sets
+// One workgroup per sequence: rho = the top K - L older pages by page score
+// (ascending), then the last min(L, pages) pages, then -1.  [DELTA] key design
+// 2; pages per sequence <= kCap.
+__global__ __launch_bounds__(kT) void topk_delta_kernel(DeltaLaunch p) {
+  __shared__ uint32_t hist[kHistWords];
+  __shared__ Shared sh;
+  const int b = blockIdx.x;
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int n_pages = (Lb + p.P - 1) / p.P;
+  const int n_recent = min(p.L_recent, n_pages);
+  const int n_cand = n_pages - n_recent;
+  const int keep = min(p.K_pages - p.L_recent, n_cand);
+  const float* Sb = p.S + (int64_t)b * p.n_pages_max;
+  int32_t* out = p.rho + (int64_t)b * p.K_pages;
+  const int i0 = (int)threadIdx.x * kKpt;
+  uint64_t k[kKpt];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool in = i0 + e < n_cand;
+    valid |= in ? (1u << e) : 0u;
+    k[e] = make_key(in ? Sb[i0 + e] : 0.f, false);
+  }
+  uint32_t sel, tot;
+  if (keep >= n_cand) {
+    sel = valid;
+  } else if (keep == 0) {
+    sel = 0;
+  } else {
+    uint64_t kstar;
+    uint32_t need_eq;
+    radix_regs(k, valid, (uint32_t)keep, hist, sh, kstar, need_eq);
+    sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
+  }
+  uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e)
+    if ((sel >> e) & 1u) out[pos++] = i0 + e;
+  for (int i = threadIdx.x; i < p.K_pages - keep; i += kT)
+    out[keep + i] = i < n_recent ? n_cand + i : -1;
+}
+
 // budget == 0: only the forced suffix.
 __global__ __launch_bounds__(256) void topk_forced_kernel(int n, int n_forced,
                                                           int32_t* __restrict__ idx) {
@@ -746,6 +789,12 @@ size_t topk_ws_bytes(int H, int n, int budget) {
   if (wide_path(n, budget))
     return align_up((size_t)H * parts_of(n) * kWideWords * sizeof(uint32_t), kWsAlign);
   return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
+}
+
+kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream) {
+  if (p.n_pages_max > kCap) return KVS_EUNSUPPORTED;
+  hipLaunchKernelGGL(topk_delta_kernel, dim3(p.B), dim3(kT), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
 kvs_status select_run(const SelectCall& c, hipStream_t stream) {

@@ -109,6 +109,42 @@ def test_score_raw_rejects_null_and_misaligned(kvs):
     assert lib.kvs_score_raw(None, P(16), P(16), P(16), None) == -1
 
 
+def _delta_args(kvs, **kw):
+    base = dict(B=4, d_k=128, H_q=32, H_kv=8, L_max=8192)
+    base.update(kw)
+    return kvs.delta_args(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1), (dict(H_q=30), -1), (dict(P=0), -1), (dict(L_max=0), -1),
+    (dict(L_recent=65), -1), (dict(K_pages=0, L_recent=0), -1), (dict(scale=-1.0), -1),
+    (dict(k_tok_stride=12), -1), (dict(d_k=96), -2), (dict(H_q=256, H_kv=8), -2),
+    (dict(P=24), -2), (dict(L_max=300000), -2),
+])
+def test_delta_rejects(kvs, kw, status):
+    lib = kvs.library()
+    a = _delta_args(kvs, **kw)
+    P = ctypes.c_void_p
+    assert lib.kvs_delta_pages(ctypes.byref(a), P(16), P(16), P(16), P(16), None, P(256), 1 << 40,
+                               None) == status
+    assert (kvs.kvs_delta_workspace(a) == 0) == (status != 0)
+
+
+def test_delta_rejects_pointers_and_workspace(kvs):
+    lib = kvs.library()
+    a = _delta_args(kvs)
+    need = kvs.kvs_delta_workspace(a)
+    assert need >= 4 * 32 * 8192 * 4           # every head's logits of every cached token
+    P = ctypes.c_void_p
+    assert lib.kvs_delta_pages(ctypes.byref(a), None, P(16), P(16), P(16), None, P(256), need, None) == -1
+    assert lib.kvs_delta_pages(ctypes.byref(a), P(8), P(16), P(16), P(16), None, P(256), need, None) == -1
+    assert lib.kvs_delta_pages(ctypes.byref(a), P(16), P(16), P(16), P(16), None, P(256), need - 1,
+                               None) == -3
+    assert lib.kvs_delta_pages(ctypes.byref(a), P(16), P(16), P(16), P(16), None, None, need, None) == -3
+    b0 = _delta_args(kvs, B=0)
+    assert lib.kvs_delta_pages(ctypes.byref(b0), None, None, None, None, None, None, 0, None) == 0
+
+
 def test_other_entry_points_reject(kvs):
     lib = kvs.library()
     P = ctypes.c_void_p
