@@ -51,7 +51,7 @@ def parse():
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--workload", default="mistral128k", choices=sorted(WORKLOADS),
                     help="mistral128k: the softmax window-score path (default); gemfilter128k and "
-                         "specprefill128k: the raw-logit paths")
+                         "specprefill128k: the raw-logit paths; delta32x8k: DELTA decode page sets")
     return ap.parse_args()
 
 
@@ -63,6 +63,8 @@ WORKLOADS = {
                       "score_raw", "score_raw_kernel (kvs_score_raw, SUM over heads, W = 1)"),
     "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
                         "score_raw", "score_raw_kernel (kvs_score_raw, MAX over heads, W = 8)"),
+    "delta32x8k": ("kvs_delta32x8k_kernel_stats.md", "delta_pages_delta32x8k_traffic.txt",
+                   "delta", "kvs_delta_pages (delta_logits_kernel + delta_page_kernel + topk_delta_kernel)"),
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 SCORE_SOURCE = os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "score.hip")
@@ -133,6 +135,8 @@ WORKLOAD_TITLES = {
     "gemfilter128k": "Mistral-7B GQA layer at L = 131072, GemFilter raw last-token scores + pooled top-k",
     "specprefill128k": "Mistral-7B GQA layer at L = 131072, Speculative-Prefill raw scores (8 lookahead "
                        "queries) + mean, pool and top-k",
+    "delta32x8k": "Llama-3.1-8B GQA Delta-layer decode step, 32 sequences x 8192 cached tokens, DELTA "
+                  "page sets (P = 16, K = 64, L = 8)",
 }
 
 
@@ -177,7 +181,17 @@ def summarize_profiles(out_dir, workload="mistral128k"):
                    "copy" if "copyBuffer" in n else None)
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
-        return {k: st.median(v) for k, v in per.items()}
+        out = {k: st.median(v) for k, v in per.items()}
+        if workload == "delta32x8k":
+            # the roofline covers the whole call: the sum of its three kernels' medians
+            parts = {}
+            for r in rows:
+                n = r["Kernel_Name"]
+                for kn in ("delta_logits_kernel", "delta_page_kernel", "topk_delta_kernel"):
+                    if kn in n:
+                        parts.setdefault(kn, []).append(float(r["Counter_Value"]))
+            out["kernel"] = sum(st.median(v) for v in parts.values())
+        return out
 
     fetch, write = counter("FETCH_SIZE"), counter("WRITE_SIZE")
     copy_kib = (256 << 20) / 1024
@@ -353,6 +367,142 @@ def bench_raw(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_delta(args):
+    """DELTA decode step at a Delta-layer for a batch: 32 sequences of 8192 cached
+    tokens (Llama-3.1-8B heads), one decode query each -> kvs_delta_pages
+    (per-head softmax, max over heads, page sums over P = 16, 8 recent pages +
+    the top 56 older pages)."""
+    import ctypes
+    import torch
+    import synth
+    import prompt_token_importance_amd as kvs
+
+    lib = kvs.library()
+    B, L, H_q, H_kv, d_k, P, K_pages, L_recent = 32, 8192, 32, 8, 128, 16, 64, 8
+    t0 = time.perf_counter()
+    layers = [synth.gaussian_layer(700 + b, L=L, W=1, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=L - 1,
+                                   n_spans=8, span_len=64, lift=2.0, span_region=L - 1)
+              for b in range(B)]
+    import numpy as np
+    Q = kvs.bf16_from_bits(np.stack([ly.Q[:, 0, :] for ly in layers]))
+    Ks = [kvs.bf16_from_bits(ly.K) for ly in layers]
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s (K of the batch: "
+        f"{sum(k.numel() for k in Ks) * 2 / 2**20:.0f} MiB, above the 256 MB cache)")
+    ptrs = torch.tensor([k.data_ptr() for k in Ks], dtype=torch.int64, device="cuda")
+    Lt = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    a = kvs.delta_args(B=B, d_k=d_k, H_q=H_q, H_kv=H_kv, L_max=L, P=P, K_pages=K_pages,
+                       L_recent=L_recent)
+    ws_bytes = kvs.kvs_delta_workspace(a)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    rho = torch.empty(B, K_pages, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+    args_ = (ctypes.byref(a), V(Q.data_ptr()), V(ptrs.data_ptr()), V(Lt.data_ptr()), V(rho.data_ptr()),
+             None, V(ws.data_ptr()), ws_bytes, sp)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if lib.kvs_delta_pages(*args_) != 0:
+            raise RuntimeError(f"kvs_delta_pages failed in step {i}")
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: kvs_delta_pages {call_ms * 1e3:.1f} us")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    copy_gbs = copy_calibration(timed) if args.copy_calibration else None
+    n_pages = (L + P - 1) // P
+    # Algorithmic bytes of one call: every cached key once, the queries once,
+    # the page sets written once.  The logits the implementation spills and
+    # reads back (2 x 128 B per token) are not counted.
+    alg_bytes = B * (H_kv * L * d_k * 2 + H_q * d_k * 2 + K_pages * 4)
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    out = {
+        "metric": "cached tokens scored/sec (DELTA decode page selection, batch 32 x 8K, 8B GQA shape); "
+                  "% of HBM roofline",
+        "value": B * L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "delta_decode_b32x8k: 32 sequences x 8192 cached tokens, H_q=32 H_kv=8 "
+                               "d_k=128, one decode query each; per-head softmax -> max over heads -> "
+                               "page sums P=16 -> 8 recent + top 56 pages",
+                   "B": B, "L": L, "H_q": H_q, "H_kv": H_kv, "d_k": d_k, "P": P, "K_pages": K_pages,
+                   "L_recent": L_recent, "n_pages": n_pages},
+        "roofline": {
+            "kernel": label,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_us": call_ms * 1e3,
+            "kernel_source_sha256_16": source_hash(),
+            "copy_256MiB_GBs": copy_gbs,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline_delta(layers, L, d_k, H_q, H_kv, P, K_pages, L_recent)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_delta(layers, L, d_k, H_q, H_kv, P, K_pages, L_recent, min_seconds=10.0,
+                       max_passes=8):
+    """The fp64 oracle, as it stands, over the batch's sequences (repeated until
+    min_seconds or max_passes passes), one BLAS thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    done, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while done < max_passes * len(layers) and (done < len(layers) or t_total < min_seconds):
+            ly = layers[done % len(layers)]
+            t0 = time.perf_counter()
+            oracle.delta_pages(ly.Q[:, 0, :], ly.K, L=L, d_k=d_k, H_q=H_q, H_kv=H_kv, P=P,
+                               K_pages=K_pages, L_recent=L_recent)
+            t_total += time.perf_counter() - t0
+            done += 1
+    return {"value": done * L / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequence evaluations over the batch's {len(layers)} sequences "
+                      f"({L} cached tokens each), {t_total / done * 1e3:.1f} ms each; softmax per "
+                      "head, max, page sums, page top-k in float64 NumPy"}
+
+
 def cpu_baseline_raw(ly, gem, budget, min_seconds=10.0, max_reps=8):
     """The fp64 oracle, as it stands, on the full raw-logit workload, one BLAS thread."""
     import numpy as np
@@ -390,7 +540,7 @@ def main():
         if not torch.cuda.is_available():
             print("bench.py needs a GPU (torch.cuda.is_available() is False)")
             sys.exit(1)
-        bench_raw(args)
+        bench_delta(args) if args.workload == "delta32x8k" else bench_raw(args)
         return
 
     import torch

@@ -192,7 +192,7 @@ kvs_status kvs_score_raw(const kvs_raw_args* a, const void* Q, const void* K, fl
  * on entry and return (the logits of every head, 4 * H_q bytes per cached
  * token, and per-chunk softmax statistics).
  * Limits (else KVS_EUNSUPPORTED): d_k in {64, 128}; H_q <= 128; P divides
- * 2048; ceil(L_max / P) <= 16384.  K is read once; the result is
+ * 512; ceil(L_max / P) <= 16384.  K is read once; the result is
  * bit-identical from run to run.
  * ---------------------------------------------------------------------- */
 typedef struct {

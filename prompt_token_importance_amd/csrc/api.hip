@@ -42,7 +42,8 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
 
 struct DeltaPlan {
   size_t x2, cstats, S, total;   // byte offsets of the workspace parts
-  int n_chunk, n_pages_max;
+  int chunk, n_chunk, n_pages_max;
+  int64_t x2_ld;
 };
 
 kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
@@ -56,14 +57,17 @@ kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
       !mult8(a->k_tok_stride))
     return KVS_EINVAL;
   if (a->d_k != 64 && a->d_k != 128) return KVS_EUNSUPPORTED;
-  if (a->H_q > 128 || 2048 % a->P) return KVS_EUNSUPPORTED;
+  if (a->H_q > 128 || 512 % a->P) return KVS_EUNSUPPORTED;
   const int64_t n_pages = ((int64_t)a->L_max + a->P - 1) / a->P;
   if (n_pages > 16384) return KVS_EUNSUPPORTED;
-  pl->n_chunk = delta_chunks(a->L_max);
+  pl->chunk = delta_chunk(a->B, a->L_max);
+  pl->n_chunk = (a->L_max + pl->chunk - 1) / pl->chunk;
   pl->n_pages_max = (int)n_pages;
   size_t off = 0;
+  // rows hold L_max rounded up to 32, then 32 spare columns
+  pl->x2_ld = ((int64_t)a->L_max + 31) / 32 * 32 + 32;
   pl->x2 = off;
-  off = align_up(off + (size_t)a->B * a->H_q * a->L_max * sizeof(float), kWsAlign);
+  off = align_up(off + (size_t)a->B * a->H_q * pl->x2_ld * sizeof(float), kWsAlign);
   pl->cstats = off;
   off = align_up(off + (size_t)a->B * pl->n_chunk * a->H_q * sizeof(float2), kWsAlign);
   pl->S = off;
@@ -221,6 +225,8 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
   p.K_pages = a->K_pages;
   p.L_recent = a->L_recent;
   p.L_max = a->L_max;
+  p.chunk = pl.chunk;
+  p.x2_ld = pl.x2_ld;
   p.n_chunk = pl.n_chunk;
   p.n_pages_max = pl.n_pages_max;
   const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->d_k);

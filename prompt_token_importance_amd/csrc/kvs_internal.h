@@ -60,16 +60,19 @@ struct DeltaLaunch {
   const uint16_t* Q;               // [B][H_q][d_k]
   const uint16_t* const* K;        // [B] device pointers
   const int32_t* L;                // [B] context lengths (clamped to [0, L_max])
-  float* x2;                       // [B][H_q][L_max] logits in log2 units
+  float* x2;                       // [B][H_q][x2_ld] logits in log2 units
   float2* cstats;                  // [B][n_chunk][H_q] per-chunk (max, sum of exp2)
   float* S;                        // [B][n_pages_max] page scores
   int32_t* rho;                    // [B][K_pages]
   int64_t khs, kts;                // khs 0: L_b * d_k
   int B, H_q, H_kv, G, d_k, P, K_pages, L_recent, L_max, n_chunk, n_pages_max;
+  int chunk;                       // keys per logits workgroup, a multiple of 128
+  int64_t x2_ld;                   // row stride of x2 (L_max rounded up to 32, plus 32)
   float c;                         // scale * log2(e)
 };
-constexpr int kDeltaChunk = 256;   // keys per logits workgroup
-int delta_chunks(int L_max);
+// Keys per logits workgroup for a batch: enough workgroups for every CU,
+// each streaming as long a run of keys as that allows.
+int delta_chunk(int B, int L_max);
 kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream);
 kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream);
 

@@ -1477,7 +1477,7 @@ namespace {
 // token at 32 heads) are cheaper to keep than a second pass over K
 // (2 KiB per token at 8 KV heads x 128 dims): the first kernel writes them,
 // head-major and in log2 units, and the second reads them back.
-// delta_logits_kernel: one workgroup per (256-key chunk, sequence); each wave
+// delta_logits_kernel: one workgroup per (chunk of keys, sequence); each wave
 // streams (key tile, KV head) pairs like the raw-logit kernel, with all the
 // sequence's query rows (one per head) in LDS and the MFMA tile oriented
 // rows x keys.  A lane keeps, per key tile, the 16 logits of the rows it holds,
@@ -1508,7 +1508,6 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
   constexpr int KS = D / 16;
   constexpr int S = kRawStages;
   constexpr int TB = tile_bytes<D>();
-  constexpr int TPW = kDeltaChunk / 32 / kWaves;   // key tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t qs[NT][TB];
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][TB];
   __shared__ float2 red[kWaves][32 * NT];
@@ -1518,14 +1517,14 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
   const int nl = lane & 31, hl = lane >> 5;
   const int b = blockIdx.y, chunk = blockIdx.x;
   const int Lb = min(max(p.L[b], 0), p.L_max);
-  const int tb = chunk * kDeltaChunk;
+  const int tb = chunk * p.chunk;
   if (tb >= Lb) return;   // the whole workgroup: nothing of this sequence here
+  const int te = min(tb + p.chunk, Lb);
   const uint16_t* Kb = p.K[b];
   const int64_t khs = p.khs ? p.khs : (int64_t)Lb * D;
   const int H = p.H_kv;
-  int nt = 0;
-#pragma unroll
-  for (int j = 0; j < TPW; ++j) nt += (tb + (wave + kWaves * j) * 32 < Lb) ? 1 : 0;
+  const int n_tiles = (te - tb + 31) / 32;
+  const int nt = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
   const int steps = nt * H;   // (key tile, KV head) pairs, KV head fastest
   const auto t0_of = [&](int s) { return tb + (wave + kWaves * (s / H)) * 32; };
   const auto issue_k = [&](int s) {
@@ -1556,38 +1555,47 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
       m[T][i] = kNegInf;
       z[T][i] = 0.f;
     }
-  float* x2b = p.x2 + (int64_t)b * p.H_q * p.L_max;
-  for (int s = 0; s < steps; ++s) {
+  float* x2b = p.x2 + (int64_t)b * p.H_q * p.x2_ld;
+  // the KV head owning each of this lane's rows (H_kv for padding rows)
+  int own[NT][16];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 32 * T + 8 * (i / 4) + 4 * hl + (i % 4);
+      own[T][i] = h < p.H_q ? h / p.G : H;
+    }
+  // the row tiles holding KV head g's query heads
+  const auto t_lo = [&](int g) { return (g * p.G) / 32; };
+  const auto t_hi = [&](int g) { return (g * p.G + p.G - 1) / 32; };
+  // With one row tile (H_q <= 32) the next step's K and Q fragments are read
+  // while this step's MFMAs run; with more, only the K fragments are.
+  constexpr bool PQ = NT == 1;
+  const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&qc)[KS], u32x4(&kn)[KS], u32x4(&qn)[KS]) {
     const int g = s % H;
     if (s + S - 1 < steps) issue_k(s + S - 1);
-    const int ahead = min(steps - 1 - s, S - 1);
-    if (ahead >= 2)
-      wait_vm<2 * KS>();
-    else if (ahead == 1)
-      wait_vm<KS>();
-    else
-      wait_vm<0>();
-    u32x4 kf[KS];
-    read_frags<KS>(kf, lds_addr(ring[wave][s % S]), foff);
-    wait_lgkm<KS>(kf);
-    // the row tiles holding this KV head's query heads
-    const int t_lo = (g * p.G) / 32, t_hi = (g * p.G + p.G - 1) / 32;
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
-      if (T < t_lo || T > t_hi) continue;
-      u32x4 qf[KS];
-      read_frags<KS>(qf, q0 + T * TB, foff);
-      wait_lgkm<KS>(qf);
+      if (T < t_lo(g) || T > t_hi(g)) continue;
+      if constexpr (!PQ) {
+        read_frags<KS>(qc, q0 + T * TB, foff);
+        wait_lgkm<KS>(qc);
+      }
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int k = 0; k < KS; ++k)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf[k]),
-                                                      __builtin_bit_cast(bf16x8, kf[k]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qc[k]),
+                                                      __builtin_bit_cast(bf16x8, kc[k]), acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = 32 * T + 8 * (i / 4) + 4 * hl + (i % 4);
-        if (h / p.G == g) out[T][i] = acc[i] * p.c;
-      }
+      for (int i = 0; i < 16; ++i) out[T][i] = own[T][i] == g ? acc[i] * p.c : out[T][i];
+    }
+    if (s + 1 < steps) {
+      if (s + S - 1 < steps)
+        wait_vm<KS>();   // tile s+1 in, tile s+2 may still be on its way
+      else
+        wait_vm<0>();
+      read_frags<KS>(kn, lds_addr(ring[wave][(s + 1) % S]), foff);
+      if constexpr (PQ) read_frags<KS>(qn, q0, foff);
     }
     if (g == H - 1) {
       // every head's logit of key t is in: store it and fold it into the statistics
@@ -1598,16 +1606,39 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int h = 32 * T + 8 * (i / 4) + 4 * hl + (i % 4);
-          if (valid && h < p.H_q) {
+          if (valid && own[T][i] < H) {
             const float x = out[T][i];
-            x2b[(int64_t)h * p.L_max + t] = x;
+            x2b[(int64_t)h * p.x2_ld + t] = x;
             const float mn = fmaxf(m[T][i], x);
             z[T][i] = z[T][i] * ex2(m[T][i] - mn) + ex2(x - mn);
             m[T][i] = mn;
           }
         }
     }
+    if (s + 1 < steps) {
+      wait_lgkm<KS>(kn);
+      if constexpr (PQ) wait_lgkm<KS>(qn);
+    }
+  };
+  u32x4 k0[KS], k1[KS], qa[KS], qb[KS];
+  if (steps > 0) {
+    if (pre == 2)
+      wait_vm<KS>();
+    else
+      wait_vm<0>();
+    read_frags<KS>(k0, lds_addr(ring[wave][0]), foff);
+    wait_lgkm<KS>(k0);
+    if constexpr (PQ) {
+      read_frags<KS>(qa, q0, foff);
+      wait_lgkm<KS>(qa);
+    }
   }
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(s, k0, qa, k1, qb);
+    step(s + 1, k1, qb, k0, qa);
+  }
+  if (s < steps) step(s, k0, qa, k1, qb);
   // statistics of each row over the workgroup's keys: lanes of a half, then waves
 #pragma unroll
   for (int T = 0; T < NT; ++T)
@@ -1640,9 +1671,10 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
 // delta_page_kernel: one workgroup per (chunk of kDeltaPageTokens tokens,
 // sequence).  It folds the sequence's per-chunk statistics into b_h = m_h +
 // log2 Z_h per head, forms s_t = max over heads of exp2(x_t,h - b_h) for its
-// tokens (a thread per token, coalesced over the head-major logits), and sums
-// each page's tokens left to right.
-constexpr int kDeltaPageTokens = 2048;
+// tokens (a thread per token, coalesced over the head-major logits, the heads'
+// loads issued in batches), and sums each page's tokens left to right.
+constexpr int kDeltaPageTokens = 512;
+constexpr int kDeltaBatch = 16;
 
 __global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
   __shared__ float bh[128];
@@ -1657,19 +1689,19 @@ __global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
   // 1. row constants: threads per head fold a strided share of the chunks
   const int tph = 256 / p.H_q;                  // threads per head (H_q <= 128)
   const int h = threadIdx.x / tph, j = threadIdx.x % tph;
-  const int nch = (Lb + kDeltaChunk - 1) / kDeltaChunk;
+  const int nch = (Lb + p.chunk - 1) / p.chunk;
   float mm = kNegInf, zz = 0.f;
   if (h < p.H_q) {
     const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q + h;
-    for (int c0 = j; c0 < nch; c0 += 8 * tph) {
-      float2 v[8];
+    for (int c0 = j; c0 < nch; c0 += kDeltaBatch * tph) {
+      float2 v[kDeltaBatch];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kDeltaBatch; ++q) {
         const int c = c0 + q * tph;
         v[q] = c < nch ? cs[(int64_t)c * p.H_q] : make_float2(kNegInf, 0.f);
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kDeltaBatch; ++q) {
         const float mx = fmaxf(mm, v[q].x);
         zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + v[q].y * ex2(v[q].x - mx);
         mm = mx;
@@ -1690,10 +1722,18 @@ __global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
   }
   __syncthreads();
   // 2. token scores: max over heads of the softmax probability
-  const float* x2b = p.x2 + (int64_t)b * p.H_q * p.L_max;
+  const float* x2b = p.x2 + (int64_t)b * p.H_q * p.x2_ld;
   for (int t = t_begin + (int)threadIdx.x; t < t_end; t += 256) {
     float sv = 0.f;
-    for (int hh = 0; hh < p.H_q; ++hh) sv = fmaxf(sv, ex2(x2b[(int64_t)hh * p.L_max + t] - bh[hh]));
+    for (int h0 = 0; h0 < p.H_q; h0 += kDeltaBatch) {
+      float v[kDeltaBatch];
+#pragma unroll
+      for (int q = 0; q < kDeltaBatch; ++q)
+        v[q] = h0 + q < p.H_q ? x2b[(int64_t)(h0 + q) * p.x2_ld + t] : kNegInf;
+#pragma unroll
+      for (int q = 0; q < kDeltaBatch; ++q)
+        if (h0 + q < p.H_q) sv = fmaxf(sv, ex2(v[q] - bh[h0 + q]));
+    }
     ys[t - t_begin] = sv;
   }
   __syncthreads();
@@ -1730,7 +1770,12 @@ kvs_status delta_launch_d(const DeltaLaunch& p, hipStream_t stream) {
 
 }  // namespace
 
-int delta_chunks(int L_max) { return (L_max + kDeltaChunk - 1) / kDeltaChunk; }
+int delta_chunk(int B, int L_max) {
+  const int64_t tiles = (int64_t)B * ((L_max + 31) / 32);
+  int64_t tpw = tiles / (256 * kWaves);   // key tiles per wave for one workgroup per CU
+  tpw = tpw < 1 ? 1 : tpw > 16 ? 16 : tpw;
+  return (int)(32 * kWaves * tpw);
+}
 
 kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream) {
   if (p.d_k == 128) return delta_launch_d<128>(p, stream);

@@ -119,7 +119,7 @@ def _delta_args(kvs, **kw):
     (dict(B=-1), -1), (dict(H_q=30), -1), (dict(P=0), -1), (dict(L_max=0), -1),
     (dict(L_recent=65), -1), (dict(K_pages=0, L_recent=0), -1), (dict(scale=-1.0), -1),
     (dict(k_tok_stride=12), -1), (dict(d_k=96), -2), (dict(H_q=256, H_kv=8), -2),
-    (dict(P=24), -2), (dict(L_max=300000), -2),
+    (dict(P=24), -2), (dict(P=1024), -2), (dict(L_max=300000), -2),
 ])
 def test_delta_rejects(kvs, kw, status):
     lib = kvs.library()
