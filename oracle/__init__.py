@@ -17,6 +17,7 @@ from .kvs import (  # noqa: F401
     pool_pages,
     aggregate_layers,
     delta_pages,
+    gather_kv,
     cluster_priority,
     topk,
     block_select,

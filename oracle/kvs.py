@@ -313,6 +313,41 @@ def delta_pages(Q, K, *, L: int, d_k: int, H_q: int, H_kv: int, P: int = 16, K_p
 
 
 # ---------------------------------------------------------------------------
+# KV gather (compaction of the selected tokens, pages or blocks)
+# ---------------------------------------------------------------------------
+
+def gather_kv(X, *, L: int, indices, n: int, unit: int = 1, idx_ld: int = 0, indptr=None):
+    """Compact copy of the selected tokens of X (bf16 bits, [H][L][d]).
+
+    [CLAA] "Complete flow and cost": each layer keeps its KV cache for the
+    indices chosen by top-k of that layer's scores, gathered from K and V.
+    [CompactAttention] "Core method" contrasts this explicit copy with its
+    page-table path; [DELTA] "Key design 3" reads whole pages.
+    Head g's list is indices[indptr[g] : indptr[g+1]] (at most n entries) when
+    indptr is given, else indices[g * idx_ld : g * idx_ld + n] (idx_ld = 0: one
+    list shared by every head).  Entry e with value i selects the `unit` tokens
+    [i * unit, i * unit + unit); tokens at or past L, and negative entries,
+    give zero rows.  Returns uint16 [H][n * unit][d]; rows past a head's list
+    are zero.
+    """
+    X = np.asarray(X, dtype=np.uint16)
+    H, _, d = X.shape
+    idx = np.asarray(indices, dtype=np.int64).reshape(-1)
+    out = np.zeros((H, n * unit, d), dtype=np.uint16)
+    for g in range(H):
+        if indptr is not None:
+            lst = idx[int(indptr[g]):int(indptr[g + 1])][:n]
+        else:
+            lst = idx[g * idx_ld:g * idx_ld + n]
+        for e, i in enumerate(lst):
+            for o in range(unit):
+                t = int(i) * unit + o
+                if i >= 0 and t < L:
+                    out[g, e * unit + o] = X[g, t]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Cross-layer aggregation
 # ---------------------------------------------------------------------------
 
