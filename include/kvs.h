@@ -212,6 +212,31 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
                            size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_gather_kv - compact copy of the selected tokens, pages or blocks.
+ *
+ * [CLAA] "Complete flow and cost": each layer keeps its KV cache for the
+ * indices top-k chose from that layer's scores, gathered from K and V.
+ * [CompactAttention] "Core method" and its execution ablation: the explicit
+ * copy of the selected blocks, next to the page-table path of
+ * kvs_block_union_pagetable.  [DELTA] "Key design 3": whole pages.
+ * For KV head g < H, its list is indices[indptr[g] .. indptr[g+1]) (at most n
+ * entries) when indptr is given, else indices[g * idx_ld .. g * idx_ld + n)
+ * (idx_ld = 0: one list shared by every head, as a CLAA layer keeps).  Entry e
+ * with value i selects the unit tokens [i * unit, i * unit + unit); output row
+ * e * unit + o of head g holds token i * unit + o.  Negative entries, tokens
+ * at or past L, and rows past the head's list are written as zeros.
+ * K, V: bf16 (any 2-byte type: bits are copied), element [g][t][c] at
+ * X + g * head_stride + t * tok_stride + c (0, 0 select [H][L][d_k]).
+ * K_out, V_out: [H][n * unit][d_k] contiguous.  V and V_out may be NULL.
+ * Limits: d_k a multiple of 8 and at most 2048; pointers and strides 16-byte
+ * aligned (else KVS_EINVAL).  The indices and indptr are device int32 arrays.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_gather_kv(const void* K, const void* V, int32_t H, int32_t L, int32_t d_k,
+                         int64_t head_stride, int64_t tok_stride, const int32_t* indices,
+                         int64_t idx_ld, const int32_t* indptr, int32_t n, int32_t unit,
+                         void* K_out, void* V_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_pool_pages - head reduction, 1-D pooling, page aggregation.
  *
  * Input S float32 [H][n] with row stride ld (>= n).  In this order:

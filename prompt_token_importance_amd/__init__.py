@@ -85,7 +85,7 @@ class SelectArgs(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m prompt_token_importance_amd.build`"
+            f"{LIB_PATH} is missing: build it with `python prompt_token_importance_amd/build.py`"
             " (hipcc, gfx950). There is no CPU fallback.")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -96,6 +96,7 @@ def _load():
         "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvs_score_raw": (I32, [ctypes.POINTER(RawArgs), P, P, P, P]),
         "kvs_delta_workspace": (SZ, [ctypes.POINTER(DeltaArgs)]),
+        "kvs_gather_kv": (I32, [P, P, I32, I32, I32, I64, I64, P, I64, P, I32, I32, P, P, P]),
         "kvs_delta_pages": (I32, [ctypes.POINTER(DeltaArgs), P, P, P, P, P, P, SZ, P]),
         "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvs_topk_workspace": (SZ, [I32, I32, I32]),
@@ -121,7 +122,7 @@ _lib = _load()
 
 EXPORTED = (
     "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_raw",
-    "kvs_delta_workspace", "kvs_delta_pages",
+    "kvs_delta_workspace", "kvs_delta_pages", "kvs_gather_kv",
     "kvs_pool_pages",
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
     "kvs_block_union_workspace", "kvs_block_union_pagetable",
@@ -232,6 +233,27 @@ def kvs_delta_pages(Q: torch.Tensor, K_ptrs: torch.Tensor, L: torch.Tensor, args
     _check(_lib.kvs_delta_pages(ctypes.byref(args), _ptr(Q), _ptr(K_ptrs), _ptr(L), _ptr(rho),
                                 _ptr(page_scores), _ptr(ws), nb, _stream(stream)), "kvs_delta_pages")
     return rho
+
+
+# --------------------------------------------------------------------------- KV gather
+def kvs_gather_kv(K: torch.Tensor, indices: torch.Tensor, n: int, *, V: Optional[torch.Tensor] = None,
+                  unit: int = 1, idx_ld: int = 0, indptr: Optional[torch.Tensor] = None,
+                  L: Optional[int] = None, H: Optional[int] = None, head_stride: int = 0,
+                  tok_stride: int = 0, K_out: Optional[torch.Tensor] = None,
+                  V_out: Optional[torch.Tensor] = None, stream=None):
+    """Returns (K_out, V_out or None), each [H][n * unit][d_k].  K: [H][L][d_k]
+    unless strides are given (then pass H and L)."""
+    d_k = K.shape[-1]
+    H = K.shape[0] if H is None else H
+    L = K.shape[1] if L is None else L
+    if K_out is None:
+        K_out = torch.empty(H, n * unit, d_k, dtype=K.dtype, device=K.device)
+    if V is not None and V_out is None:
+        V_out = torch.empty(H, n * unit, d_k, dtype=V.dtype, device=V.device)
+    _check(_lib.kvs_gather_kv(_ptr(K), _ptr(V), H, L, d_k, head_stride, tok_stride, _ptr(indices),
+                              idx_ld, _ptr(indptr), n, unit, _ptr(K_out), _ptr(V_out),
+                              _stream(stream)), "kvs_gather_kv")
+    return K_out, V_out
 
 
 # --------------------------------------------------------------------------- pool / pages

@@ -1,6 +1,8 @@
 """Build libkvs.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree.
 
-Usage: python -m prompt_token_importance_amd.build   (or call build()).
+Usage: python prompt_token_importance_amd/build.py   (or call build()).  Run
+it as a file: importing the package loads libkvs.so, which may be missing or
+older than the sources.
 """
 import glob
 import os

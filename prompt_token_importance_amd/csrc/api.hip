@@ -237,6 +237,39 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
   return delta_topk_run(p, s);
 }
 
+kvs_status kvs_gather_kv(const void* K, const void* V, int32_t H, int32_t L, int32_t d_k,
+                         int64_t head_stride, int64_t tok_stride, const int32_t* indices,
+                         int64_t idx_ld, const int32_t* indptr, int32_t n, int32_t unit,
+                         void* K_out, void* V_out, void* stream) {
+  if (H < 0 || L < 0 || n < 0 || unit < 1 || idx_ld < 0 || d_k < 8 || d_k % 8 || d_k > 2048)
+    return KVS_EINVAL;
+  if (head_stride == 0) head_stride = (int64_t)L * d_k;
+  if (tok_stride == 0) tok_stride = d_k;
+  if (head_stride < 0 || tok_stride < 0 || !mult8(head_stride) || !mult8(tok_stride))
+    return KVS_EINVAL;
+  if (H == 0 || n == 0) return KVS_OK;
+  if (!K || !K_out || !indices || (V && !V_out) || (!V && V_out)) return KVS_EINVAL;
+  if (!aligned16(K) || !aligned16(K_out) || (V && (!aligned16(V) || !aligned16(V_out))) ||
+      ((uintptr_t)indices & 3u) || ((uintptr_t)indptr & 3u))
+    return KVS_EINVAL;
+  GatherLaunch p;
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.K_out = static_cast<uint16_t*>(K_out);
+  p.V_out = static_cast<uint16_t*>(V_out);
+  p.indices = indices;
+  p.indptr = indptr;
+  p.idx_ld = idx_ld;
+  p.khs = head_stride;
+  p.kts = tok_stride;
+  p.H = H;
+  p.L = L;
+  p.d_k = d_k;
+  p.n = n;
+  p.unit = unit;
+  return gather_run(p, as_stream(stream));
+}
+
 kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld, int32_t head_reduce,
                           int32_t pool, int32_t pool_k, int32_t P, int32_t page_reduce,
                           float* pooled, float* page, int32_t* page_arg, void* stream) {

@@ -108,6 +108,19 @@ struct SelectCall {
 size_t topk_ws_bytes(int H, int n, int budget);
 kvs_status select_run(const SelectCall& c, hipStream_t stream);
 
+// KV gather (kvs_gather_kv).
+struct GatherLaunch {
+  const uint16_t* K;
+  const uint16_t* V;        // may be null
+  uint16_t* K_out;
+  uint16_t* V_out;
+  const int32_t* indices;
+  const int32_t* indptr;    // may be null
+  int64_t idx_ld, khs, kts;
+  int H, L, d_k, n, unit;
+};
+kvs_status gather_run(const GatherLaunch& p, hipStream_t stream);
+
 size_t union_ws_bytes(int H_q, int H_kv, int sub_group, int n_kvb);
 kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_qb, int n_kvb,
                      int32_t* indptr, int32_t* indices, void* ws, hipStream_t stream);

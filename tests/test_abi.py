@@ -145,6 +145,39 @@ def test_delta_rejects_pointers_and_workspace(kvs):
     assert lib.kvs_delta_pages(ctypes.byref(b0), None, None, None, None, None, None, 0, None) == 0
 
 
+@pytest.mark.parametrize("args,status", [
+    # H, L, d_k, head_stride, tok_stride, idx_ld, n, unit
+    ((-1, 10, 128, 0, 0, 0, 4, 1), -1), ((2, 10, 128, 0, 0, 0, 4, 0), -1),
+    ((2, 10, 12, 0, 0, 0, 4, 1), -1), ((2, 10, 2056, 0, 0, 0, 4, 1), -1),
+    ((2, 10, 128, 12, 0, 0, 4, 1), -1), ((2, 10, 128, 0, 0, -1, 4, 1), -1),
+    ((2, -1, 128, 0, 0, 0, 4, 1), -1),
+])
+def test_gather_rejects(kvs, args, status):
+    lib = kvs.library()
+    H, L, d, hs, ts, ld, n, unit = args
+    P = ctypes.c_void_p
+    assert lib.kvs_gather_kv(P(16), None, H, L, d, hs, ts, P(16), ld, None, n, unit, P(16), None,
+                             None) == status
+
+
+def test_gather_rejects_pointers(kvs):
+    lib = kvs.library()
+    P = ctypes.c_void_p
+
+    def call(K, V, idx, K_out, V_out, H=2, n=4):
+        return lib.kvs_gather_kv(K, V, H, 10, 128, 0, 0, idx, 0, None, n, 1, K_out, V_out, None)
+
+    assert call(None, None, P(16), P(16), None) == -1          # no K
+    assert call(P(16), P(16), P(16), P(16), None) == -1        # V without V_out
+    assert call(P(16), None, P(16), P(16), P(16)) == -1        # V_out without V
+    assert call(P(18), None, P(16), P(16), None) == -1         # misaligned K
+    assert call(P(16), None, P(18), P(16), None) == -1         # misaligned indices
+    assert call(P(16), None, None, P(16), None) == -1          # no indices
+    # nothing to copy: accepted without touching memory
+    assert call(None, None, None, None, None, H=0) == 0
+    assert call(None, None, None, None, None, n=0) == 0
+
+
 def test_other_entry_points_reject(kvs):
     lib = kvs.library()
     P = ctypes.c_void_p
