@@ -51,7 +51,8 @@ def parse():
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--workload", default="mistral128k", choices=sorted(WORKLOADS),
                     help="mistral128k: the softmax window-score path (default); gemfilter128k and "
-                         "specprefill128k: the raw-logit paths; delta32x8k: DELTA decode page sets")
+                         "specprefill128k: the raw-logit paths; delta32x8k: DELTA decode page sets; "
+                         "gather128k: compaction of the kept K and V")
     return ap.parse_args()
 
 
@@ -65,14 +66,21 @@ WORKLOADS = {
                         "score_raw", "score_raw_kernel (kvs_score_raw, MAX over heads, W = 8)"),
     "delta32x8k": ("kvs_delta32x8k_kernel_stats.md", "delta_pages_delta32x8k_traffic.txt",
                    "delta", "kvs_delta_pages (delta_logits_kernel + delta_page_kernel + topk_delta_kernel)"),
+    "gather128k": ("kvs_gather128k_kernel_stats.md", "gather_gather128k_traffic.txt",
+                   "gather_kernel", "gather_kernel (kvs_gather_kv, K and V)"),
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
-SCORE_SOURCE = os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "score.hip")
 
 
 def source_hash():
+    """sha256[:16] over every HIP source of the library, in name order: a summary
+    taken on other kernel sources does not describe these."""
+    import glob
     import hashlib
-    return hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "*.hip"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(path=TRAFFIC_SUMMARY):
@@ -137,6 +145,8 @@ WORKLOAD_TITLES = {
                        "queries) + mean, pool and top-k",
     "delta32x8k": "Llama-3.1-8B GQA Delta-layer decode step, 32 sequences x 8192 cached tokens, DELTA "
                   "page sets (P = 16, K = 64, L = 8)",
+    "gather128k": "Mistral-7B GQA layer at L = 131072, K and V of the kept 20% of every KV head "
+                  "gathered into compact arrays",
 }
 
 
@@ -169,7 +179,7 @@ def summarize_profiles(out_dir, workload="mistral128k"):
     for r in stats:
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", f"Kernel source sha256[:16] of score.hip: {source_hash()}", ""]
+    lines += ["", f"Kernel sources (csrc/*.hip) sha256[:16]: {source_hash()}", ""]
     open(os.path.join(ROOT, "profiles", stats_name), "w").write(NL.join(lines))
 
     def counter(name):
@@ -503,6 +513,129 @@ def cpu_baseline_delta(layers, L, d_k, H_q, H_kv, P, K_pages, L_recent, min_seco
                       "head, max, page sums, page top-k in float64 NumPy"}
 
 
+def bench_gather(args):
+    """KV compaction for a 128K-token Mistral-7B layer: every KV head keeps 20%
+    of its tokens (ascending per-head lists, as kvs_select produces them), and
+    K and V of the kept tokens are copied into [8][26214][128] arrays."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    import prompt_token_importance_amd as kvs
+
+    lib = kvs.library()
+    H, L, d = 8, 131072, 128
+    n = L // 5
+    t0 = time.perf_counter()
+    ly = synth.mistral_layer()
+    K = kvs.bf16_from_bits(ly.K)
+    V = kvs.bf16_from_bits(np.ascontiguousarray(ly.K[:, ::-1, :]))   # another tensor of the same shape
+    # per-head kept lists: the top 20% of seeded scores, ascending
+    x = synth.score_array(77, H, L)
+    idx = np.sort(np.argsort(-x, axis=1, kind="stable")[:, :n], axis=1).astype(np.int32)
+    I = torch.from_numpy(idx).cuda()
+    Ko = torch.empty(H, n, d, dtype=torch.bfloat16, device="cuda")
+    Vo = torch.empty_like(Ko)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V_ = ctypes.c_void_p
+    call = (V_(K.data_ptr()), V_(V.data_ptr()), H, L, d, 0, 0, V_(I.data_ptr()), n, None, n, 1,
+            V_(Ko.data_ptr()), V_(Vo.data_ptr()), sp)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if lib.kvs_gather_kv(*call) != 0:
+            raise RuntimeError(f"kvs_gather_kv failed in step {i}")
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: kvs_gather_kv {call_ms * 1e3:.1f} us")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    copy_gbs = copy_calibration(timed) if args.copy_calibration else None
+    # every kept row of K and V read once and written once, plus the lists
+    alg_bytes = 2 * 2 * H * n * d * 2 + H * n * 4
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    out = {
+        "metric": "kept tokens gathered/sec (K and V, 20% of every KV head of a 128K layer); "
+                  "% of HBM roofline",
+        "value": H * n / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gather_keep20_128k: H_kv=8 L=131072 d_k=128, 26214 kept tokens per KV "
+                               "head, K and V copied to [8][26214][128]", "H_kv": H, "L": L, "d_k": d,
+                   "kept_per_head": n},
+        "roofline": {
+            "kernel": label,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_us": call_ms * 1e3,
+            "kernel_source_sha256_16": source_hash(),
+            "copy_256MiB_GBs": copy_gbs,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline_gather(ly.K, idx, L, n)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_gather(Kbits, idx, L, n, min_seconds=10.0, max_reps=8):
+    """The oracle's gather, as it stands, on the workload (K and V: twice per
+    repetition), one thread."""
+    import oracle
+    reps, t_total = 0, 0.0
+    while reps < max_reps and (reps == 0 or t_total < min_seconds):
+        t0 = time.perf_counter()
+        oracle.gather_kv(Kbits, L=L, indices=idx, n=n, idx_ld=n)
+        oracle.gather_kv(Kbits, L=L, indices=idx, n=n, idx_ld=n)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    sec = t_total / reps
+    return {"value": idx.shape[0] * n / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload (8 KV heads x {n} kept tokens, K and V), {reps} repetition(s), "
+                      f"{sec:.2f} s each; NumPy row copies in Python loops"}
+
+
 def cpu_baseline_raw(ly, gem, budget, min_seconds=10.0, max_reps=8):
     """The fp64 oracle, as it stands, on the full raw-logit workload, one BLAS thread."""
     import numpy as np
@@ -540,7 +673,12 @@ def main():
         if not torch.cuda.is_available():
             print("bench.py needs a GPU (torch.cuda.is_available() is False)")
             sys.exit(1)
-        bench_delta(args) if args.workload == "delta32x8k" else bench_raw(args)
+        if args.workload == "delta32x8k":
+            bench_delta(args)
+        elif args.workload == "gather128k":
+            bench_gather(args)
+        else:
+            bench_raw(args)
         return
 
     import torch

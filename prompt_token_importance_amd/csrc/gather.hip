@@ -17,7 +17,9 @@ namespace kvs {
 namespace {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherRows = 64;   // output rows per workgroup per tensor
+constexpr int kIter = 8;   // rows per thread: a workgroup copies (256 / pieces per row) * 8 rows
+
+__host__ __device__ inline int gather_rows(int d_k) { return kGatherThreads / (d_k / 8) * kIter; }
 
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherLaunch p) {
   const int g = blockIdx.y;
@@ -32,25 +34,36 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherLaunch p) 
     list = p.indices + lo;
   }
   const int64_t out_rows = (int64_t)p.n * p.unit;
-  for (int k = threadIdx.x / cpr; k < kGatherRows; k += rows_per_iter) {
-    const int64_t r = (int64_t)blockIdx.x * kGatherRows + k;
-    if (r >= out_rows) break;
+  // all of this thread's rows are loaded before any is stored, so the loads
+  // of a workgroup are in flight together
+  uint4 kv[kIter], vv[kIter];
+  int64_t dst[kIter];
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int k = threadIdx.x / cpr + it * rows_per_iter;
+    const int64_t r = (int64_t)blockIdx.x * rows_per_iter * kIter + k;
+    dst[it] = -1;
+    kv[it] = vv[it] = zero;
+    if (threadIdx.x >= rows_per_iter * cpr || r >= out_rows) continue;
     const int e = (int)(r / p.unit), o = (int)(r % p.unit);
     int64_t t = -1;
     if (e < count) {
       const int i = list[e];
       if (i >= 0) t = (int64_t)i * p.unit + o;
     }
-    const bool valid = t >= 0 && t < p.L;
-    const int64_t src = (int64_t)g * p.khs + (valid ? t : 0) * p.kts + 8 * piece;
-    const int64_t dst = ((int64_t)g * out_rows + r) * p.d_k + 8 * piece;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 kv = valid ? *reinterpret_cast<const uint4*>(p.K + src) : zero;
-    *reinterpret_cast<uint4*>(p.K_out + dst) = kv;
-    if (p.V) {
-      const uint4 vv = valid ? *reinterpret_cast<const uint4*>(p.V + src) : zero;
-      *reinterpret_cast<uint4*>(p.V_out + dst) = vv;
+    dst[it] = ((int64_t)g * out_rows + r) * p.d_k + 8 * piece;
+    if (t >= 0 && t < p.L) {
+      const int64_t src = (int64_t)g * p.khs + t * p.kts + 8 * piece;
+      kv[it] = *reinterpret_cast<const uint4*>(p.K + src);
+      if (p.V) vv[it] = *reinterpret_cast<const uint4*>(p.V + src);
     }
+  }
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    if (dst[it] < 0) continue;
+    *reinterpret_cast<uint4*>(p.K_out + dst[it]) = kv[it];
+    if (p.V) *reinterpret_cast<uint4*>(p.V_out + dst[it]) = vv[it];
   }
 }
 
@@ -59,7 +72,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherLaunch p) 
 kvs_status gather_run(const GatherLaunch& p, hipStream_t stream) {
   const int64_t out_rows = (int64_t)p.n * p.unit;
   if (out_rows == 0 || p.H == 0) return KVS_OK;
-  const int64_t blocks = (out_rows + kGatherRows - 1) / kGatherRows;
+  const int64_t blocks = (out_rows + gather_rows(p.d_k) - 1) / gather_rows(p.d_k);
   if (blocks > 0x7fffffff) return KVS_EUNSUPPORTED;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks, p.H), dim3(kGatherThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;

@@ -40,7 +40,8 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("H,L,d,n,unit", [(8, 4096, 128, 300, 1), (3, 1000, 64, 77, 1),
-                                          (2, 999, 128, 20, 16), (4, 130, 64, 9, 16)])
+                                          (2, 999, 128, 20, 16), (4, 130, 64, 9, 16),
+                                          (2, 300, 256, 40, 1), (1, 50, 2048, 5, 2), (2, 77, 96, 13, 3)])
 def test_gather_per_head_lists(kvs, H, L, d, n, unit):
     K, V = _coded(H, L, d, 1), _coded(H, L, d, 5)
     rng = np.random.default_rng(H * L + n)
