@@ -387,6 +387,26 @@ size_t kvs_block_select_workspace(const kvs_block_select_args* a);
 kvs_status kvs_block_select(const kvs_block_select_args* a, const void* Qc, const void* K,
                             uint8_t* M, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * kvs_block_select_cached - kvs_block_select with key-block means carried
+ * from one prefill chunk to the next.
+ *
+ * [CompactAttention] "Core method": each chunk scores its query blocks against
+ * the whole accumulated KV cache; the key blocks that earlier chunks completed
+ * do not change, so their means need not be recomputed.  Kb is a caller-owned
+ * float32 cache [H_kv][kb_cap][d_k] (16-byte aligned, kb_cap >= ceil(L /
+ * block)); its first n_cached blocks of every KV head must hold the means of
+ * those complete blocks of the same K (as an earlier call left them), and
+ * n_cached <= floor(L / block).  The call writes the means of blocks
+ * n_cached .. ceil(L / block) - 1 into Kb and otherwise computes exactly what
+ * kvs_block_select computes (bit-identical M): a chunk reads only the keys of
+ * its new blocks.  After the call, floor(L / block) blocks of Kb are complete
+ * for the next chunk.  Workspace as for kvs_block_select.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_block_select_cached(const kvs_block_select_args* a, const void* Qc, const void* K,
+                                   float* Kb, int32_t kb_cap, int32_t n_cached, uint8_t* M,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,6 +110,8 @@ def _load():
         "kvs_cluster_priority": (I32, [P, P, I32, I32, I32, I32, F32, I32, P, P]),
         "kvs_block_select_workspace": (SZ, [ctypes.POINTER(BlockSelectArgs)]),
         "kvs_block_select": (I32, [ctypes.POINTER(BlockSelectArgs), P, P, P, P, SZ, P]),
+        "kvs_block_select_cached": (I32, [ctypes.POINTER(BlockSelectArgs), P, P, P, I32, I32, P, P,
+                                          SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -127,7 +129,7 @@ EXPORTED = (
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
     "kvs_block_union_workspace", "kvs_block_union_pagetable",
     "kvs_aggregate_workspace", "kvs_aggregate_layers", "kvs_cluster_priority",
-    "kvs_block_select_workspace", "kvs_block_select",
+    "kvs_block_select_workspace", "kvs_block_select", "kvs_block_select_cached",
 )
 
 
@@ -258,12 +260,16 @@ def kvs_gather_kv(K: torch.Tensor, indices: torch.Tensor, n: int, *, V: Optional
 
 # --------------------------------------------------------------------------- pool / pages
 def kvs_pool_pages(S: torch.Tensor, n: int, *, head_reduce=RED_NONE, pool=RED_NONE, pool_k=7, P=0,
-                   page_reduce=RED_SUM, ld: Optional[int] = None, want_pooled=True, stream=None):
-    """Returns (pooled or None, page or None, page_arg or None)."""
+                   page_reduce=RED_SUM, ld: Optional[int] = None, want_pooled=True,
+                   out: Optional[torch.Tensor] = None, stream=None):
+    """Returns (pooled or None, page or None, page_arg or None); `out` (contiguous
+    float32, rows x n) receives the pooled rows when given."""
     H = S.shape[0]
     ld = S.stride(0) if ld is None else ld
     rows = H if head_reduce == RED_NONE else 1
-    pooled = torch.empty(rows, n, dtype=torch.float32, device=S.device) if (want_pooled or P == 0) else None
+    pooled = out
+    if pooled is None and (want_pooled or P == 0):
+        pooled = torch.empty(rows, n, dtype=torch.float32, device=S.device)
     page = arg = None
     if P > 0:
         n_pages = (n + P - 1) // P
@@ -370,4 +376,20 @@ def kvs_block_select(Qc: torch.Tensor, K: torch.Tensor, args: BlockSelectArgs,
     ws, nb = _workspace(kvs_block_select_workspace(args), K.device, ws)
     _check(_lib.kvs_block_select(ctypes.byref(args), _ptr(Qc), _ptr(K), _ptr(M), _ptr(ws), nb,
                                  _stream(stream)), "kvs_block_select")
+    return M
+
+
+def kvs_block_select_cached(Qc: torch.Tensor, K: torch.Tensor, args: BlockSelectArgs,
+                            Kb: torch.Tensor, n_cached: int, M: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvs_block_select with the key-block means cached in Kb float32
+    [H_kv][kb_cap][d_k]; the first n_cached blocks must already be valid."""
+    n_qb = (args.Lq + args.block - 1) // args.block
+    n_kvb = (args.L + args.block - 1) // args.block
+    if M is None:
+        M = torch.empty(args.H_q, n_qb, n_kvb, dtype=torch.uint8, device=K.device)
+    ws, nb = _workspace(kvs_block_select_workspace(args), K.device, ws)
+    _check(_lib.kvs_block_select_cached(ctypes.byref(args), _ptr(Qc), _ptr(K), _ptr(Kb), Kb.shape[1],
+                                        n_cached, _ptr(M), _ptr(ws), nb, _stream(stream)),
+           "kvs_block_select_cached")
     return M

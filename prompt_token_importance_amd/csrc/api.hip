@@ -406,6 +406,12 @@ size_t kvs_block_select_workspace(const kvs_block_select_args* a) {
 
 kvs_status kvs_block_select(const kvs_block_select_args* in, const void* Qc, const void* K,
                             uint8_t* M, void* ws, size_t ws_bytes, void* stream) {
+  return kvs_block_select_cached(in, Qc, K, nullptr, 0, 0, M, ws, ws_bytes, stream);
+}
+
+kvs_status kvs_block_select_cached(const kvs_block_select_args* in, const void* Qc, const void* K,
+                                   float* Kb, int32_t kb_cap, int32_t n_cached, uint8_t* M,
+                                   void* ws, size_t ws_bytes, void* stream) {
   if (!in || !Qc || !K || !M) return KVS_EINVAL;
   kvs_block_select_args a = *in;
   if (a.Lq < 1 || a.L < 1 || a.block < 1 || a.H_q < 1 || a.H_kv < 1 || a.d_k < 1) return KVS_EINVAL;
@@ -426,10 +432,15 @@ kvs_status kvs_block_select(const kvs_block_select_args* in, const void* Qc, con
   BlockPlan pl;
   kvs_status st = block_plan(&a, &pl);
   if (st != KVS_OK) return st;
+  if (Kb) {
+    if (((uintptr_t)Kb & 15u) || kb_cap < pl.n_kvb || n_cached < 0 || n_cached > a.L / a.block)
+      return KVS_EINVAL;
+  }
   if (!ws || ws_bytes < pl.ws_total) return KVS_EWORKSPACE;
   if (!aligned16(ws)) return KVS_EINVAL;
   return block_select_run(&a, pl, static_cast<const uint16_t*>(Qc),
-                          static_cast<const uint16_t*>(K), M, ws, as_stream(stream));
+                          static_cast<const uint16_t*>(K), M, ws, Kb, kb_cap, n_cached,
+                          as_stream(stream));
 }
 
 }  // extern "C"

@@ -25,15 +25,17 @@ constexpr int kMaxKvb = 4096;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ block means
-// out[head][blk][d] = mean of rows [blk*block, min(L, blk*block + block)) of
-// in[head][row][d]; rows are summed in a fixed order.  One workgroup per
-// (block, head); a thread loads 8 bf16 of one row at a time.
+// out[head][blk][d] (n_blk blocks per head) = mean of rows [blk*block,
+// min(L, blk*block + block)) of in[head][row][d] for blocks blk0, blk0 + 1,
+// ...; rows are summed in a fixed order, so a block's mean does not depend on
+// the call that computed it.  One workgroup per (block, head); a thread loads
+// 8 bf16 of one row at a time.
 __global__ __launch_bounds__(kThreads) void block_mean_kernel(const uint16_t* __restrict__ in,
                                                               int64_t hs, int64_t rs, int L, int d_k,
-                                                              int block, int n_blk,
+                                                              int block, int n_blk, int blk0,
                                                               float* __restrict__ out) {
   __shared__ float part[kThreads / 8][128 + 4];
-  const int blk = blockIdx.x, head = blockIdx.y;
+  const int blk = blk0 + blockIdx.x, head = blockIdx.y;
   const int tpr = d_k / 8;                 // threads per row
   const int rows_per = kThreads / tpr;     // rows covered per step
   const int rsub = threadIdx.x / tpr, dc = (threadIdx.x % tpr) * 8;
@@ -62,8 +64,8 @@ __device__ __forceinline__ uint32_t ord_pos(float p) { return __float_as_uint(p)
 
 // ------------------------------------------------------------------ top-p per (head, query block)
 __global__ __launch_bounds__(kThreads) void block_topp_kernel(
-    const float* __restrict__ Qb, const float* __restrict__ Kb, int G, int n_qb, int n_kvb,
-    int sort_n, int d_k, int block, int Lq, int64_t q_pos0, float scale, float p_mass,
+    const float* __restrict__ Qb, const float* __restrict__ Kb, int kb_ld, int G, int n_qb,
+    int n_kvb, int sort_n, int d_k, int block, int Lq, int64_t q_pos0, float scale, float p_mass,
     uint8_t* __restrict__ M) {
   __shared__ uint64_t keys[kMaxKvb];
   __shared__ float val[kMaxKvb];
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
   __syncthreads();
   const int64_t last_row = min((int64_t)(i + 1) * block, (int64_t)Lq) - 1;
   const int64_t end_pos = q_pos0 + last_row;
-  const float* kg = Kb + (int64_t)g * n_kvb * d_k;
+  const float* kg = Kb + (int64_t)g * kb_ld * d_k;
   // 1. logits of visible blocks
   float mloc = -__builtin_inff();
   for (int j = tid; j < n_kvb; j += kThreads) {
@@ -231,16 +233,22 @@ kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* pl) {
 
 kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& pl,
                             const uint16_t* Qc, const uint16_t* K, uint8_t* M, void* ws,
-                            hipStream_t stream) {
-  float* Kb = static_cast<float*>(ws);
+                            float* Kb, int kb_ld, int n_cached, hipStream_t stream) {
+  if (!Kb) {   // no cache: every key block's mean goes to the workspace
+    Kb = static_cast<float*>(ws);
+    kb_ld = pl.n_kvb;
+    n_cached = 0;
+  }
   float* Qb = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_kb);
   const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->d_k);
-  hipLaunchKernelGGL(block_mean_kernel, dim3(pl.n_kvb, a->H_kv), dim3(kThreads), 0, stream, K,
-                     a->k_head_stride, a->k_tok_stride, a->L, a->d_k, a->block, pl.n_kvb, Kb);
+  if (pl.n_kvb > n_cached)
+    hipLaunchKernelGGL(block_mean_kernel, dim3(pl.n_kvb - n_cached, a->H_kv), dim3(kThreads), 0,
+                       stream, K, a->k_head_stride, a->k_tok_stride, a->L, a->d_k, a->block, kb_ld,
+                       n_cached, Kb);
   hipLaunchKernelGGL(block_mean_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, Qc,
-                     a->q_head_stride, a->q_row_stride, a->Lq, a->d_k, a->block, pl.n_qb, Qb);
+                     a->q_head_stride, a->q_row_stride, a->Lq, a->d_k, a->block, pl.n_qb, 0, Qb);
   hipLaunchKernelGGL(block_topp_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, Qb, Kb,
-                     a->H_q / a->H_kv, pl.n_qb, pl.n_kvb, pl.sort_n, a->d_k, a->block, a->Lq,
+                     kb_ld, a->H_q / a->H_kv, pl.n_qb, pl.n_kvb, pl.sort_n, a->d_k, a->block, a->Lq,
                      a->q_pos0, scale, a->p_mass, M);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }

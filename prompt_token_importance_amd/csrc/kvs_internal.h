@@ -130,8 +130,10 @@ struct BlockPlan {
   size_t ws_kb, ws_qb, ws_total;
 };
 kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* plan);
+// Kb null: key-block means go to the workspace.  Else Kb is a caller cache of
+// kb_ld blocks per KV head whose first n_cached blocks are already valid.
 kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& plan,
                             const uint16_t* Qc, const uint16_t* K, uint8_t* M, void* ws,
-                            hipStream_t stream);
+                            float* Kb, int kb_ld, int n_cached, hipStream_t stream);
 
 }  // namespace kvs

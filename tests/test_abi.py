@@ -209,6 +209,12 @@ def test_other_entry_points_reject(kvs):
     assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 24, None) == -2
     a = kvs.block_select_args(Lq=64, L=1 << 20, d_k=128, H_q=4, H_kv=1, q_pos0=64, block=64)
     assert lib.kvs_block_select(ctypes.byref(a), P(16), P(16), P(16), P(256), 1 << 30, None) == -2
+    # cached block means: cache too small, more cached blocks than complete ones, misaligned
+    a = kvs.block_select_args(Lq=64, L=200, d_k=128, H_q=4, H_kv=1, q_pos0=136, block=64)
+    cached = lib.kvs_block_select_cached
+    assert cached(ctypes.byref(a), P(16), P(16), P(256), 3, 0, P(16), P(256), 1 << 24, None) == -1
+    assert cached(ctypes.byref(a), P(16), P(16), P(256), 4, 4, P(16), P(256), 1 << 24, None) == -1
+    assert cached(ctypes.byref(a), P(16), P(16), P(264), 4, 3, P(16), P(256), 1 << 24, None) == -1
 
 
 def test_select_rejects(kvs):
