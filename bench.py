@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--workload", default="mistral128k", choices=sorted(WORKLOADS),
                     help="mistral128k: the softmax window-score path (default); gemfilter128k and "
                          "specprefill128k: the raw-logit paths; delta32x8k: DELTA decode page sets; "
-                         "gather128k: compaction of the kept K and V")
+                         "gather128k: compaction of the kept K and V; chunksel128k: chunked-prefill "
+                         "block selection with cached key-block means")
     return ap.parse_args()
 
 
@@ -68,6 +69,8 @@ WORKLOADS = {
                    "delta", "kvs_delta_pages (delta_logits_kernel + delta_page_kernel + topk_delta_kernel)"),
     "gather128k": ("kvs_gather128k_kernel_stats.md", "gather_gather128k_traffic.txt",
                    "gather_kernel", "gather_kernel (kvs_gather_kv, K and V)"),
+    "chunksel128k": ("kvs_chunksel128k_kernel_stats.md", "block_topp_chunksel128k_traffic.txt",
+                     "block_topp_kernel", "block_topp_kernel (kvs_block_select_cached)"),
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 
@@ -147,6 +150,8 @@ WORKLOAD_TITLES = {
                   "page sets (P = 16, K = 64, L = 8)",
     "gather128k": "Mistral-7B GQA layer at L = 131072, K and V of the kept 20% of every KV head "
                   "gathered into compact arrays",
+    "chunksel128k": "chunked prefill at L = 131072, last 1024-token chunk: cached key-block means, "
+                    "block top-p 0.9 and the per-group page table",
 }
 
 
@@ -636,6 +641,163 @@ def cpu_baseline_gather(Kbits, idx, L, n, min_seconds=10.0, max_reps=8):
                       f"{sec:.2f} s each; NumPy row copies in Python loops"}
 
 
+def bench_chunksel(args):
+    """The last 1024-query chunk of a 131072-token chunked prefill (Llama-3.1-8B
+    heads, blocks of 64): kvs_block_select_cached with the means of the 2032
+    earlier key blocks cached, then kvs_block_union_pagetable.  The same chunk
+    without the cache (kvs_block_select, every key block's mean recomputed from
+    the 256 MiB of K) is timed beside it."""
+    import ctypes
+    import torch
+    import synth
+    import prompt_token_importance_amd as kvs
+
+    lib = kvs.library()
+    t0 = time.perf_counter()
+    ch = synth.chunk_select()
+    Qc = kvs.bf16_from_bits(ch.Qc)
+    K = kvs.bf16_from_bits(ch.K)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+    blk = ch.block
+    a = kvs.block_select_args(Lq=ch.Lq, L=ch.L, d_k=ch.d_k, H_q=ch.H_q, H_kv=ch.H_kv, q_pos0=ch.q_pos0,
+                              block=blk)
+    n_qb, n_kvb = ch.Lq // blk, ch.L // blk
+    n_cached = ch.q_pos0 // blk
+    Kb = torch.empty(ch.H_kv, n_kvb, ch.d_k, dtype=torch.float32, device="cuda")
+    # the cache as the earlier chunks left it
+    a_prev = kvs.block_select_args(Lq=blk, L=ch.q_pos0, d_k=ch.d_k, H_q=ch.H_q, H_kv=ch.H_kv,
+                                   q_pos0=ch.q_pos0 - blk, block=blk, k_head_stride=ch.L * ch.d_k)
+    kvs.kvs_block_select_cached(Qc[:, :blk].contiguous(), K, a_prev, Kb, 0)
+    M = torch.empty(ch.H_q, n_qb, n_kvb, dtype=torch.uint8, device="cuda")
+    ws_b = kvs.kvs_block_select_workspace(a)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+    G = ch.H_q // ch.H_kv
+    indptr = torch.empty(ch.H_kv + 1, dtype=torch.int32, device="cuda")
+    indices = torch.empty(ch.H_kv * n_kvb, dtype=torch.int32, device="cuda")
+    uws_b = int(lib.kvs_block_union_workspace(ch.H_q, ch.H_kv, 0, n_kvb))
+    uws = torch.empty(max(uws_b, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V_ = ctypes.c_void_p
+    ra = ctypes.byref(a)
+    pQ, pK, pKb, pM, pws = V_(Qc.data_ptr()), V_(K.data_ptr()), V_(Kb.data_ptr()), V_(M.data_ptr()), V_(ws.data_ptr())
+
+    def select_cached():
+        return lib.kvs_block_select_cached(ra, pQ, pK, pKb, n_kvb, n_cached, pM, pws, ws_b, sp)
+
+    def select_full():
+        return lib.kvs_block_select(ra, pQ, pK, pM, pws, ws_b, sp)
+
+    def union():
+        return lib.kvs_block_union_pagetable(pM, ch.H_q, ch.H_kv, 0, n_qb, n_kvb, V_(indptr.data_ptr()),
+                                             V_(indices.data_ptr()), V_(uws.data_ptr()), uws_b, sp)
+
+    def step(i, ev=None, full=False):
+        if ev is not None:
+            ev[0].record(stream)
+        st = select_full() if full else select_cached()
+        if ev is not None:
+            ev[1].record(stream)
+        st |= union()
+        if ev is not None:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"chunk selection failed in step {i}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    uni_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    for i in range(args.steps):
+        step(i, evs[i], full=True)
+    torch.cuda.synchronize()
+    full_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: cached select {sel_ms * 1e3:.1f} us, "
+        f"union {uni_ms * 1e3:.1f} us; uncached select {full_ms * 1e3:.1f} us")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    if args.copy_calibration:
+        copy_calibration(timed)
+    # block_topp_kernel bound: per (head, query block) the n_kvb fp32 key-block
+    # means (d_k floats each) are read and dotted with the query block mean
+    flops = 2.0 * ch.H_q * n_qb * n_kvb * ch.d_k
+    achieved = flops / (sel_ms * 1e-3) / 1e12
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    out = {
+        "metric": "KV tokens covered/sec (chunked-prefill block selection, last chunk at L=128K); "
+                  "% of fp32 vector roofline",
+        "value": ch.L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "chunk_select_128k_last_chunk: K [8][131072][128], chunk Q [32][1024][128], "
+                               "block 64, top-p 0.9, cached means of 2032 earlier blocks -> union page "
+                               "table", "L": ch.L, "Lq": ch.Lq, "block": blk, "n_cached_blocks": n_cached},
+        "roofline": {
+            "kernel": "kvs_block_select_cached (block_mean_kernel x2 + block_topp_kernel)",
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": 157.3,
+            "unit": "TFLOP/s",
+            "frac": achieved / 157.3,
+            "traffic": None,
+            "kernel_us": sel_ms * 1e3,
+            "kernel_source_sha256_16": source_hash(),
+            "event_us": {"select_cached": sel_ms * 1e3, "union": uni_ms * 1e3,
+                         "select_uncached": full_ms * 1e3},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline_chunksel(ch)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_chunksel(ch, min_seconds=10.0, max_reps=8):
+    """The oracle's block selection and union on the same chunk, one BLAS thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    reps, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while reps < max_reps and (reps == 0 or t_total < min_seconds):
+            t0 = time.perf_counter()
+            M = oracle.block_select(ch.Qc, ch.K, Lq=ch.Lq, L=ch.L, d_k=ch.d_k, H_q=ch.H_q,
+                                       H_kv=ch.H_kv, q_pos0=ch.q_pos0, block=ch.block)
+            oracle.block_union_pagetable(M, H_q=ch.H_q, H_kv=ch.H_kv)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    sec = t_total / reps
+    return {"value": ch.L / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload (the chunk, all heads), {reps} repetition(s), {sec:.2f} s each; "
+                      "block means, top-p and union in float64 NumPy"}
+
+
 def cpu_baseline_raw(ly, gem, budget, min_seconds=10.0, max_reps=8):
     """The fp64 oracle, as it stands, on the full raw-logit workload, one BLAS thread."""
     import numpy as np
@@ -677,6 +839,8 @@ def main():
             bench_delta(args)
         elif args.workload == "gather128k":
             bench_gather(args)
+        elif args.workload == "chunksel128k":
+            bench_chunksel(args)
         else:
             bench_raw(args)
         return

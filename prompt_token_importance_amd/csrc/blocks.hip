@@ -60,37 +60,78 @@ __global__ __launch_bounds__(kThreads) void block_mean_kernel(const uint16_t* __
   }
 }
 
+// ------------------------------------------------------------------ block logits
+// logit[h][i][j] = scale * Qb[h][i] . Kb[g][j] for every query block i of the
+// G heads of KV group g and every key block j: a small fp32 GEMM per group,
+// tiled 64 rows (head, query block) x 64 key blocks in LDS; each thread sums
+// its 4 x 4 outputs over d in a fixed order.
+constexpr int kLt = 64;   // tile edge
+
+__global__ __launch_bounds__(kThreads) void block_logits_kernel(
+    const float* __restrict__ Qb, const float* __restrict__ Kb, int kb_ld, int G, int n_qb,
+    int n_kvb, int d_k, float scale, float* __restrict__ logit) {
+  __shared__ float qs[kLt][128 + 1];
+  __shared__ float ks[kLt][128 + 1];
+  const int g = blockIdx.y;
+  const int j0 = blockIdx.x * kLt, r0 = blockIdx.z * kLt;
+  const int rows = G * n_qb;   // row r = (head g*G + r / n_qb, query block r % n_qb)
+  const float* qg = Qb + (int64_t)g * G * n_qb * d_k;   // the group's heads are consecutive
+  const float* kg = Kb + (int64_t)g * kb_ld * d_k;
+#pragma unroll 8
+  for (int x = threadIdx.x; x < kLt * d_k; x += kThreads) {
+    const int r = x / d_k, d = x % d_k;
+    qs[r][d] = r0 + r < rows ? qg[(int64_t)(r0 + r) * d_k + d] : 0.f;
+    ks[r][d] = j0 + r < n_kvb ? kg[(int64_t)(j0 + r) * d_k + d] : 0.f;
+  }
+  __syncthreads();
+  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;
+  float acc[4][4] = {};
+  for (int d = 0; d < d_k; ++d) {
+    float a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = qs[tr + 16 * u][d];
+      b[u] = ks[tc + 16 * u][d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r0 + tr + 16 * u;
+    if (r >= rows) continue;
+    const int h = g * G + r / n_qb, i = r % n_qb;
+    float* out = logit + ((int64_t)h * n_qb + i) * n_kvb;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + tc + 16 * v;
+      if (j < n_kvb) out[j] = scale * acc[u][v];
+    }
+  }
+}
+
 __device__ __forceinline__ uint32_t ord_pos(float p) { return __float_as_uint(p) | 0x80000000u; }
 
 // ------------------------------------------------------------------ top-p per (head, query block)
 __global__ __launch_bounds__(kThreads) void block_topp_kernel(
-    const float* __restrict__ Qb, const float* __restrict__ Kb, int kb_ld, int G, int n_qb,
-    int n_kvb, int sort_n, int d_k, int block, int Lq, int64_t q_pos0, float scale, float p_mass,
-    uint8_t* __restrict__ M) {
-  __shared__ uint64_t keys[kMaxKvb];
+    const float* __restrict__ logit, int n_qb, int n_kvb, int block, int Lq,
+    int64_t q_pos0, float p_mass, uint8_t* __restrict__ M) {
+  __shared__ uint64_t keys[2048];
   __shared__ float val[kMaxKvb];
-  __shared__ float qv[128];
   __shared__ float red[kThreads];
-  const int i = blockIdx.x, h = blockIdx.y, g = h / G;
+  const int i = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
-  for (int d = tid; d < d_k; d += kThreads) qv[d] = Qb[((int64_t)h * n_qb + i) * d_k + d];
-  __syncthreads();
   const int64_t last_row = min((int64_t)(i + 1) * block, (int64_t)Lq) - 1;
   const int64_t end_pos = q_pos0 + last_row;
-  const float* kg = Kb + (int64_t)g * kb_ld * d_k;
-  // 1. logits of visible blocks
+  // 1. logits of the visible blocks
+  const float* lr = logit + ((int64_t)h * n_qb + i) * n_kvb;
+  for (int j = tid; j < n_kvb; j += kThreads)
+    val[j] = (int64_t)j * block <= end_pos ? lr[j] : -__builtin_inff();
+  __syncthreads();
   float mloc = -__builtin_inff();
-  for (int j = tid; j < n_kvb; j += kThreads) {
-    float v = -__builtin_inff();
-    if ((int64_t)j * block <= end_pos) {
-      const float* kr = kg + (int64_t)j * d_k;
-      float s = 0.f;
-      for (int d = 0; d < d_k; ++d) s = fmaf(qv[d], kr[d], s);
-      v = scale * s;
-    }
-    val[j] = v;
-    mloc = fmaxf(mloc, v);
-  }
+  for (int j = tid; j < n_kvb; j += kThreads) mloc = fmaxf(mloc, val[j]);
   red[tid] = mloc;
   __syncthreads();
   for (int w = kThreads / 2; w > 0; w >>= 1) {
@@ -114,58 +155,90 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
   }
   const float inv_z = 1.0f / red[0];
   __syncthreads();
-  // 3. sort keys: probability desc, then j asc (bit-inverted j in the low word)
-  for (int j = tid; j < sort_n; j += kThreads) {
-    uint64_t k = 0ull;  // padding sorts last
-    if (j < n_kvb) {
+  // 3. the kept blocks are a prefix of the order (probability desc, j asc): a
+  // block is kept while the mass ranked strictly before it is < p_mass.  The
+  // prefix ends at the block K* where the running mass first reaches p_mass;
+  // K* is found by a radix select over the 44-bit key (probability bits, then
+  // 4095 - j) with per-digit histograms of mass instead of counts.  Masses are
+  // fixed point (2^-40 units) summed with integer atomics: exact and
+  // independent of the order of the additions.
+  uint64_t* hm = keys;   // 2048-bin mass histogram (the key array's first 16 KiB)
+  const uint64_t need0 = (uint64_t)((double)p_mass * 1099511627776.0);   // 2^40
+  uint64_t prefix = 0, need = need0;
+  bool all = false;      // the whole order stays below p_mass: keep every visible block
+  for (int pass = 0; pass < 4 && !all; ++pass) {
+    const int shift = 33 - 11 * pass;
+    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 11)) & ((1ull << 44) - 1);
+    for (int b = tid; b < 2048; b += kThreads) hm[b] = 0ull;
+    __syncthreads();
+    for (int j = tid; j < n_kvb; j += kThreads) {
       const float p = val[j] * inv_z;
-      k = ((uint64_t)ord_pos(p) << 32) | (uint64_t)(~(uint32_t)j);
+      const uint64_t key = ((uint64_t)ord_pos(p) << 12) | (uint64_t)(4095 - j);
+      if ((key & pmask) == prefix)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hm[(key >> shift) & 2047u]),
+                  (unsigned long long)(p * 1099511627776.0f));
     }
-    keys[j] = k;
-  }
-  __syncthreads();
-  for (int size = 2; size <= sort_n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < sort_n; x += kThreads) {
-        const int y = x ^ stride;
-        if (y > x) {
-          const bool desc = (x & size) == 0;
-          const uint64_t a = keys[x], b = keys[y];
-          if (desc ? (a < b) : (a > b)) {
-            keys[x] = b;
-            keys[y] = a;
-          }
+    __syncthreads();
+    // thread t owns bins [2047 - 8t - 7, 2047 - 8t]: mass above it, then its crossing bin
+    uint64_t c[8], ls = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c[u] = hm[2047 - 8 * tid - u];
+      ls += c[u];
+    }
+    // exclusive prefix of the per-thread masses over the workgroup (waves, then LDS)
+    const int lane = tid & 63, wave = tid >> 6;
+    uint64_t inc = ls;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t v = __shfl_up(inc, off);
+      if (lane >= off) inc += v;
+    }
+    __shared__ uint64_t wsum[kThreads / 64];
+    __shared__ uint64_t sel_prefix, sel_need;
+    __shared__ int found;
+    if (lane == 63) wsum[wave] = inc;
+    if (tid == 0) found = 0;
+    __syncthreads();
+    uint64_t above = inc - ls;
+    for (int w = 0; w < wave; ++w) above += wsum[w];
+    if (above < need && need <= above + ls) {
+      uint64_t cum = above;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (cum < need && need <= cum + c[u]) {
+          sel_prefix = prefix | ((uint64_t)(2047 - 8 * tid - u) << shift);
+          sel_need = need - cum;
+          found = 1;
         }
+        cum += c[u];
       }
-      __syncthreads();
     }
+    __syncthreads();
+    if (!found) {
+      all = true;   // the prefix's whole mass is below need
+    } else {
+      prefix = sel_prefix;
+      need = sel_need;
+    }
+    __syncthreads();
   }
-  // 4. exclusive prefix of the sorted probabilities: contiguous chunk per thread
-  const int per = sort_n / kThreads > 0 ? sort_n / kThreads : 1;
-  const int lo = tid * per;
-  float csum = 0.f;
-  for (int s = lo; s < lo + per && s < sort_n; ++s)
-    csum += __uint_as_float((uint32_t)(keys[s] >> 32) & 0x7fffffffu);
-  red[tid] = csum;
-  __syncthreads();
-  float before = 0.f;
-  for (int t = 0; t < tid; ++t) before += red[t];
+  // 4. keep the visible blocks at or above K* (every visible block when `all`)
   uint8_t* mrow = M + ((int64_t)h * n_qb + i) * n_kvb;
-  for (int s = lo; s < lo + per && s < sort_n; ++s) {
-    const uint64_t k = keys[s];
-    const uint32_t j = ~(uint32_t)k;
-    const float p = __uint_as_float((uint32_t)(k >> 32) & 0x7fffffffu);
-    if (k != 0ull && j < (uint32_t)n_kvb) {
-      const bool visible = (int64_t)j * block <= end_pos;
-      mrow[j] = (visible && before < p_mass) ? 1 : 0;
-    }
-    before += p;
+  for (int j = tid; j < n_kvb; j += kThreads) {
+    const float p = val[j] * inv_z;
+    const uint64_t key = ((uint64_t)ord_pos(p) << 12) | (uint64_t)(4095 - j);
+    const bool visible = (int64_t)j * block <= end_pos;
+    mrow[j] = (visible && (all || key >= prefix)) ? 1 : 0;
   }
 }
 
 // ------------------------------------------------------------------ union
 // One workgroup per subgroup: OR over its heads and query blocks, then an
-// ascending compaction of the set KV blocks into staging.
+// ascending compaction of the set KV blocks into staging.  Thread t owns the
+// 16 KV blocks [16t, 16t + 16) (n_kvb <= 4096): it reads them from every mask
+// row it ORs (one 16-byte load per row when the rows are 16-byte aligned), all
+// rows' loads independent of each other.
 __global__ __launch_bounds__(kThreads) void union_group_kernel(const uint8_t* __restrict__ M,
                                                                int sg, int n_qb, int n_kvb,
                                                                int32_t* __restrict__ staging,
@@ -173,32 +246,47 @@ __global__ __launch_bounds__(kThreads) void union_group_kernel(const uint8_t* __
   __shared__ uint32_t wc[kThreads / 64];
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  uint32_t run = 0;
-  for (int base = 0; base < n_kvb; base += kThreads) {
-    const int j = base + tid;
-    bool on = false;
-    if (j < n_kvb) {
-      for (int h = s * sg; h < (s + 1) * sg && !on; ++h)
-        for (int i = 0; i < n_qb; ++i)
-          if (M[((int64_t)h * n_qb + i) * n_kvb + j]) {
-            on = true;
-            break;
-          }
+  const int j0 = 16 * tid;
+  const int nrows = sg * n_qb;
+  const uint8_t* base = M + (int64_t)s * sg * n_qb * n_kvb;
+  uint32_t bits = 0;
+  if (j0 < n_kvb) {
+    if (n_kvb % 16 == 0 && ((uintptr_t)M & 15u) == 0) {
+      u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll 8
+      for (int r = 0; r < nrows; ++r)
+        acc |= *reinterpret_cast<const u32x4*>(base + (int64_t)r * n_kvb + j0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bits |= ((acc[e / 4] >> (8 * (e % 4))) & 0xffu) ? (1u << e) : 0u;
+    } else {
+      for (int r = 0; r < nrows; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (j0 + e < n_kvb && base[(int64_t)r * n_kvb + j0 + e]) bits |= 1u << e;
     }
-    const uint64_t m = __ballot(on);
-    if (lane == 0) wc[wave] = (uint32_t)__popcll(m);
-    __syncthreads();
-    uint32_t before = 0, tile = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
-      before += w < wave ? wc[w] : 0u;
-      tile += wc[w];
-    }
-    if (on) staging[(int64_t)s * n_kvb + run + before + __popcll(m & lt_mask)] = j;
-    run += tile;
-    __syncthreads();
   }
-  if (tid == 0) counts[s] = (int32_t)run;
+  // exclusive prefix of the per-thread counts: this thread's first output slot
+  uint32_t c = __popc(bits);
+  uint32_t inc = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(inc, off);
+    if (lane >= off) inc += u;
+  }
+  if (lane == 63) wc[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    before += w < wave ? wc[w] : 0u;
+    total += wc[w];
+  }
+  uint32_t pos = before + inc - c;
+  int32_t* st = staging + (int64_t)s * n_kvb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((bits >> e) & 1u) st[pos++] = j0 + e;
+  if (tid == 0) counts[s] = (int32_t)total;
 }
 
 __global__ __launch_bounds__(kThreads) void union_pack_kernel(const int32_t* __restrict__ staging,
@@ -222,12 +310,10 @@ kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* pl) {
   pl->n_qb = (a->Lq + a->block - 1) / a->block;
   pl->n_kvb = (a->L + a->block - 1) / a->block;
   if (pl->n_kvb > kMaxKvb) return KVS_EUNSUPPORTED;
-  int s = 1;
-  while (s < pl->n_kvb) s <<= 1;
-  pl->sort_n = s;
   pl->ws_kb = align_up((size_t)a->H_kv * pl->n_kvb * a->d_k * sizeof(float), kWsAlign);
   pl->ws_qb = align_up((size_t)a->H_q * pl->n_qb * a->d_k * sizeof(float), kWsAlign);
-  pl->ws_total = pl->ws_kb + pl->ws_qb;
+  pl->ws_logit = align_up((size_t)a->H_q * pl->n_qb * pl->n_kvb * sizeof(float), kWsAlign);
+  pl->ws_total = pl->ws_kb + pl->ws_qb + pl->ws_logit;
   return KVS_OK;
 }
 
@@ -240,6 +326,7 @@ kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& pl,
     n_cached = 0;
   }
   float* Qb = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_kb);
+  float* logit = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_kb + pl.ws_qb);
   const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->d_k);
   if (pl.n_kvb > n_cached)
     hipLaunchKernelGGL(block_mean_kernel, dim3(pl.n_kvb - n_cached, a->H_kv), dim3(kThreads), 0,
@@ -247,9 +334,13 @@ kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& pl,
                        n_cached, Kb);
   hipLaunchKernelGGL(block_mean_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, Qc,
                      a->q_head_stride, a->q_row_stride, a->Lq, a->d_k, a->block, pl.n_qb, 0, Qb);
-  hipLaunchKernelGGL(block_topp_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, Qb, Kb,
-                     kb_ld, a->H_q / a->H_kv, pl.n_qb, pl.n_kvb, pl.sort_n, a->d_k, a->block, a->Lq,
-                     a->q_pos0, scale, a->p_mass, M);
+  const int G = a->H_q / a->H_kv;
+  hipLaunchKernelGGL(block_logits_kernel,
+                     dim3((pl.n_kvb + kLt - 1) / kLt, a->H_kv, (G * pl.n_qb + kLt - 1) / kLt),
+                     dim3(kThreads), 0, stream, Qb, Kb, kb_ld, G, pl.n_qb, pl.n_kvb, a->d_k, scale,
+                     logit);
+  hipLaunchKernelGGL(block_topp_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, logit,
+                     pl.n_qb, pl.n_kvb, a->block, a->Lq, a->q_pos0, a->p_mass, M);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 

@@ -126,8 +126,8 @@ kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_q
                      int32_t* indptr, int32_t* indices, void* ws, hipStream_t stream);
 
 struct BlockPlan {
-  int n_qb, n_kvb, sort_n;
-  size_t ws_kb, ws_qb, ws_total;
+  int n_qb, n_kvb;
+  size_t ws_kb, ws_qb, ws_logit, ws_total;
 };
 kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* plan);
 // Kb null: key-block means go to the workspace.  Else Kb is a caller cache of
