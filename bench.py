@@ -75,21 +75,39 @@ WORKLOADS = {
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 
 
-def source_hash():
-    """sha256[:16] over every HIP source of the library, in name order: a summary
-    taken on other kernel sources does not describe these."""
+# Sources of each workload's roofline kernel(s), besides the shared header.
+KERNEL_SOURCES = {
+    "mistral128k": ("score.hip",),
+    "gemfilter128k": ("score.hip",),
+    "specprefill128k": ("score.hip",),
+    "delta32x8k": ("score.hip", "topk.hip"),
+    "gather128k": ("gather.hip",),
+    "chunksel128k": ("blocks.hip",),
+}
+
+
+def source_hash(workload=None):
+    """sha256[:16] over HIP sources of the library, in name order: with a
+    workload, the files of its roofline kernel plus the internal header (a
+    counter summary taken on other sources of that kernel does not describe
+    it); without one, every HIP source."""
     import glob
     import hashlib
+    csrc = os.path.join(ROOT, "prompt_token_importance_amd", "csrc")
+    if workload is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*.hip")))
+    else:
+        files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[workload] + ("kvs_internal.h",))]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "prompt_token_importance_amd", "csrc", "*.hip"))):
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path=TRAFFIC_SUMMARY):
+def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
     """HBM bytes per launch of the roofline kernel from a committed counter
     summary, or None when the summary is missing or was taken on another
-    kernel source."""
+    source of that kernel."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -97,7 +115,7 @@ def measured_traffic(path=TRAFFIC_SUMMARY):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != source_hash():
+    if kv.get("source_sha256_16") != source_hash(workload):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -184,7 +202,8 @@ def summarize_profiles(out_dir, workload="mistral128k"):
     for r in stats:
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", f"Kernel sources (csrc/*.hip) sha256[:16]: {source_hash()}", ""]
+    srcs = ", ".join(sorted(KERNEL_SOURCES[workload] + ("kvs_internal.h",)))
+    lines += ["", f"Sources of the roofline kernel ({srcs}) sha256[:16]: {source_hash(workload)}", ""]
     open(os.path.join(ROOT, "profiles", stats_name), "w").write(NL.join(lines))
 
     def counter(name):
@@ -219,7 +238,8 @@ def summarize_profiles(out_dir, workload="mistral128k"):
         "# Commands (repo root on the GPU box, cd /tmp first):",
         "#   " + cmds["FETCH_SIZE"],
         "#   " + cmds["WRITE_SIZE"],
-        f"source_sha256_16: {source_hash()}",
+        f"# source_sha256_16 covers {', '.join(sorted(KERNEL_SOURCES[workload] + ('kvs_internal.h',)))}",
+        f"source_sha256_16: {source_hash(workload)}",
         f"copy_fetch_kib: {fetch['copy']:.1f}",
         f"copy_write_kib: {write['copy']:.1f}",
         f"fetch_scale: {f_fetch:.4f}",
@@ -366,10 +386,10 @@ def bench_raw(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name), args.workload),
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": raw_ms * 1e3,
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source_sha256_16": source_hash(args.workload),
             "event_us": {"raw_scores": raw_ms * 1e3, "selection": sel_ms * 1e3},
             "copy_256MiB_GBs": copy_gbs,
         },
@@ -482,10 +502,10 @@ def bench_delta(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name), args.workload),
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": call_ms * 1e3,
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source_sha256_16": source_hash(args.workload),
             "copy_256MiB_GBs": copy_gbs,
         },
     }
@@ -609,10 +629,10 @@ def bench_gather(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name)),
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name), args.workload),
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": call_ms * 1e3,
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source_sha256_16": source_hash(args.workload),
             "copy_256MiB_GBs": copy_gbs,
         },
     }
@@ -767,7 +787,7 @@ def bench_chunksel(args):
             "frac": achieved / 157.3,
             "traffic": None,
             "kernel_us": sel_ms * 1e3,
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source_sha256_16": source_hash(args.workload),
             "event_us": {"select_cached": sel_ms * 1e3, "union": uni_ms * 1e3,
                          "select_uncached": full_ms * 1e3},
         },
@@ -978,7 +998,7 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": dom_ms * 1e3,
             "mfma_frac": flops / (dom_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source_sha256_16": source_hash("mistral128k"),
             "event_us": {"score_pass1_stats_and_merge": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
                          "page_cluster_topk": select * 1e3},
             "copy_256MiB_GBs": copy_gbs,

@@ -63,50 +63,60 @@ __global__ __launch_bounds__(kThreads) void block_mean_kernel(const uint16_t* __
 // ------------------------------------------------------------------ block logits
 // logit[h][i][j] = scale * Qb[h][i] . Kb[g][j] for every query block i of the
 // G heads of KV group g and every key block j: a small fp32 GEMM per group,
-// tiled 64 rows (head, query block) x 64 key blocks in LDS; each thread sums
-// its 4 x 4 outputs over d in a fixed order.
+// tiled 64 rows (head, query block) x 64 key blocks.  Both tiles are staged
+// in LDS transposed ([d][64], 16-byte aligned rows) from coalesced 16-byte
+// global loads, so each thread reads its 4 rows and 4 columns at a given d with
+// two 16-byte LDS reads and sums its 4 x 4 outputs over d in a fixed order.
 constexpr int kLt = 64;   // tile edge
+constexpr int kLs = 68;   // LDS row stride of the transposed tiles (floats)
 
 __global__ __launch_bounds__(kThreads) void block_logits_kernel(
     const float* __restrict__ Qb, const float* __restrict__ Kb, int kb_ld, int G, int n_qb,
     int n_kvb, int d_k, float scale, float* __restrict__ logit) {
-  __shared__ float qs[kLt][128 + 1];
-  __shared__ float ks[kLt][128 + 1];
+  __shared__ __attribute__((aligned(16))) float qs[128][kLs];
+  __shared__ __attribute__((aligned(16))) float ks[128][kLs];
   const int g = blockIdx.y;
   const int j0 = blockIdx.x * kLt, r0 = blockIdx.z * kLt;
   const int rows = G * n_qb;   // row r = (head g*G + r / n_qb, query block r % n_qb)
   const float* qg = Qb + (int64_t)g * G * n_qb * d_k;   // the group's heads are consecutive
   const float* kg = Kb + (int64_t)g * kb_ld * d_k;
-#pragma unroll 8
-  for (int x = threadIdx.x; x < kLt * d_k; x += kThreads) {
-    const int r = x / d_k, d = x % d_k;
-    qs[r][d] = r0 + r < rows ? qg[(int64_t)(r0 + r) * d_k + d] : 0.f;
-    ks[r][d] = j0 + r < n_kvb ? kg[(int64_t)(j0 + r) * d_k + d] : 0.f;
+  const int qpr = d_k / 4;     // float4 per row
+#pragma unroll 4
+  for (int x = threadIdx.x; x < kLt * qpr; x += kThreads) {
+    const int r = x / qpr, dq = x % qpr;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 q = r0 + r < rows ? *reinterpret_cast<const float4*>(qg + (int64_t)(r0 + r) * d_k + 4 * dq) : zero;
+    const float4 k = j0 + r < n_kvb ? *reinterpret_cast<const float4*>(kg + (int64_t)(j0 + r) * d_k + 4 * dq) : zero;
+    qs[4 * dq][r] = q.x;
+    qs[4 * dq + 1][r] = q.y;
+    qs[4 * dq + 2][r] = q.z;
+    qs[4 * dq + 3][r] = q.w;
+    ks[4 * dq][r] = k.x;
+    ks[4 * dq + 1][r] = k.y;
+    ks[4 * dq + 2][r] = k.z;
+    ks[4 * dq + 3][r] = k.w;
   }
   __syncthreads();
-  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;
+  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;   // rows 4tr.., columns 4tc..
   float acc[4][4] = {};
   for (int d = 0; d < d_k; ++d) {
-    float a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = qs[tr + 16 * u][d];
-      b[u] = ks[tc + 16 * u][d];
-    }
+    const float4 a = *reinterpret_cast<const float4*>(&qs[d][4 * tr]);
+    const float4 b = *reinterpret_cast<const float4*>(&ks[d][4 * tc]);
+    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int r = r0 + tr + 16 * u;
+    const int r = r0 + 4 * tr + u;
     if (r >= rows) continue;
     const int h = g * G + r / n_qb, i = r % n_qb;
     float* out = logit + ((int64_t)h * n_qb + i) * n_kvb;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int j = j0 + tc + 16 * v;
+      const int j = j0 + 4 * tc + v;
       if (j < n_kvb) out[j] = scale * acc[u][v];
     }
   }
