@@ -7,27 +7,29 @@
 // ones, then appends the observation window ("Method details").  Order:
 // priority desc, value desc, index asc; the chosen indices come out ascending.
 //
-// The ranking key is 33 bits: the priority bit above an order-preserving map
-// of the float32 value.  Selection runs inside single 1024-thread workgroups,
-// so no workgroup ever waits for another and no device-wide hand-off is paid:
-//  stage 1  a row is cut into parts of kCap = 16384 elements, one workgroup
-//           per (part, row).  The workgroup computes the keys of its part in
-//           registers (16 per thread; the optional pooling or cluster
-//           transform reads a 48-score register window per thread, or
-//           LDS-staged scores for wide windows), finds its local top-`budget` by a three-digit radix
-//           select (12, 11, 10 bits) with LDS histograms, and writes the
-//           chosen (key, index) pairs in index order.  Every element of the
-//           global top-`budget` is in its part's local top-`budget`, because
-//           fewer than `budget` elements of that part precede it.
-//  stage 2  one workgroup per row runs the same radix select over the
-//           candidates of all parts (in registers when they fit in kCap,
-//           else re-read tile by tile) and writes the chosen indices.
-// Each radix pass has its own LDS histogram; one wave fixes the digit.
-// Rows of at most kCap elements finish in stage 1.  Ties at the threshold key
-// K* go to the lower index: after K* and the number `need` of K*-equal
-// elements to take are fixed, a workgroup prefix sum ranks the K*-equal
-// elements in index order, and a second one gives every chosen element its
-// output slot, so the output is ascending and unique.
+// An element's rank is decided by its class (1 = priority) and then by an
+// order-preserving 32-bit map of its float32 value.  Selection runs inside
+// single workgroups, so no workgroup ever waits for another:
+//  stage 1  a row is cut into parts (8192 elements for 512-thread workgroups
+//           when the candidates of all parts fit one merge, else 16384 for
+//           1024 threads), one workgroup per (part, row).  The workgroup
+//           computes its keys in registers (16 per thread; the pooling or
+//           cluster transform is applied here and never stored), finds its
+//           local top-`budget` and writes the chosen (key, index) pairs in
+//           index order.  Every element of the global top-`budget` is in its
+//           part's local top-`budget`, because fewer than `budget` elements of
+//           that part precede it.
+//  stage 2  one 1024-thread workgroup per row runs the same selection over the
+//           candidates of all parts and writes the chosen indices.
+// The selection first counts the priority elements, which fixes the class of
+// the threshold key K*, then reduces the minimum and maximum value of that
+// class: their common leading bits are shared by the whole class, so the
+// radix digits (12, 11 and 10 bits, one LDS histogram each) cover only the
+// bits below them.  Clustered values then spread over the histogram instead
+// of piling into a few bins, and a narrow class needs fewer passes.  Ties at
+// K* go to the lower index: one workgroup prefix sum of the per-thread counts
+// of keys above and equal to K* gives every chosen element its output slot,
+// so the output is ascending and unique.
 #include <math.h>
 
 #include "kvs_internal.h"
@@ -35,20 +37,31 @@
 namespace kvs {
 namespace {
 
-constexpr int kT = 1024;                    // threads per workgroup
-constexpr int kW = kT / 64;                 // waves per workgroup
+constexpr int kT = 1024;                    // threads of a merge or single-part workgroup
+constexpr int kWMax = kT / 64;              // waves per workgroup, at most
 constexpr int kKpt = 16;                    // keys per thread
-constexpr int kCap = kT * kKpt;             // keys per workgroup tile (16384)
-constexpr int kStage = kCap + 2 * kSelHaloMax;   // staged scores of a part and its halo
-constexpr uint64_t kIdxMask = 0x7FFFFFFFull;
+constexpr int kCap = kT * kKpt;             // keys of a 1024-thread workgroup (16384)
+constexpr int kSmallT = 512;                // threads of a stage-1 workgroup on small parts
+constexpr int kSmallCap = kSmallT * kKpt;   // 8192
+constexpr uint32_t kIdxMask = 0x7FFFFFFFu;
 
 enum Transform { kPlain = 0, kPool = 1, kCluster = 2 };
 
 constexpr int kHistWords = 4096 + 2048 + 1024;   // one histogram per radix pass
+constexpr int kList = 4096;                       // keys left after the first pass, at most
+constexpr int kSelWords = kHistWords + kList;     // LDS words of a selection
+__device__ __forceinline__ constexpr int pass_width(int p) { return p == 0 ? 12 : p == 1 ? 11 : 10; }
+__device__ __forceinline__ constexpr int pass_offset(int p) { return p == 0 ? 0 : p == 1 ? 4096 : 6144; }
 
-template <int T>
+template <int NT>
+constexpr int stage_words() { return NT * kKpt + 2 * kSelHaloMax; }   // a part and its halo
+
+template <int T, int NT>
 struct LdsWords {
-  static constexpr int value = T == kPlain ? kHistWords : T == kPool ? kStage : 2 * kStage + 8;
+  static constexpr int staged = T == kPlain ? 0
+                                : T == kPool ? stage_words<NT>()
+                                             : 2 * stage_words<NT>() + 8;
+  static constexpr int value = staged > kSelWords ? staged : kSelWords;
 };
 
 struct Params {
@@ -63,19 +76,28 @@ struct Params {
   int r;                 // kCluster: gather radius
   int budget, n_forced;
   int vec;               // S rows 16-byte aligned: vector loads
+  int part;              // elements per stage-1 part (threads of its workgroup * kKpt)
   int parts;             // stage-1 parts per row
-  int stride;            // candidate slots per part: min(budget, kCap)
+  int stride;            // candidate slots per part: min(budget, part)
   int64_t cand_ld;       // candidate slots per row (multiple of kCap)
-  uint64_t* cand;        // [H][cand_ld] (key << 31 | index)
+  uint64_t* cand;        // [H][cand_ld] (priority << 63 | value << 31 | index)
   uint32_t* wide;        // wide path: per-(row, part) histograms and counts
   int32_t* idx;
 };
 
 struct Shared {
-  uint32_t w[kW];
-  uint64_t prefix;
-  uint32_t need;
-  uint32_t all_eq;   // the last digit's bin is taken whole: every K*-equal key is chosen
+  uint32_t w[2][kWMax];   // block scans: per-wave totals, the two buffers used in turn
+  uint32_t r[5][kWMax];   // class statistics: per-wave partial results
+  uint32_t digit, need;   // result of a digit pick: the bin and the need within it,
+  uint32_t cnt;           // and the bin's count
+  uint32_t list_n;        // keys compacted into the list
+};
+
+// The threshold of a selection: K* = (cls, value).  Every element of a higher
+// class, or of class cls with a larger value, is chosen, and so are the first
+// need_eq elements (in index order) of class cls with value K*.value.
+struct Kstar {
+  uint32_t cls, value, need_eq;
 };
 
 __device__ __forceinline__ uint32_t ord_key(float v) {
@@ -85,143 +107,282 @@ __device__ __forceinline__ uint32_t ord_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t make_key(float v, bool pr) {
-  return ((uint64_t)(pr ? 1u : 0u) << 32) | ord_key(v);
+// ------------------------------------------------------------------ wave and block scans
+// Inclusive scan over the 64 lanes of a wave through DPP row shifts (within
+// rows of 16 lanes) and the two row broadcasts; lanes that a shift or a row
+// mask leaves out read the identity `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-// Exclusive prefix sum of one value per thread over the workgroup, and the total.
-__device__ __forceinline__ uint32_t scan_excl(uint32_t v, Shared& sh, uint32_t& total) {
+struct OpAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct OpMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id) {
+  Op op;
+  v = op(v, dpp_mov<0x111, 0xF>(id, v));   // row_shr:1
+  v = op(v, dpp_mov<0x112, 0xF>(id, v));   // row_shr:2
+  v = op(v, dpp_mov<0x114, 0xF>(id, v));   // row_shr:4
+  v = op(v, dpp_mov<0x118, 0xF>(id, v));   // row_shr:8
+  v = op(v, dpp_mov<0x142, 0xA>(id, v));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_mov<0x143, 0xC>(id, v));   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over the workgroup, and the
+// total.  The per-wave totals alternate between two LDS buffers (`ph`), so one
+// barrier suffices: a buffer is written again only two scans later, after
+// every thread has passed the barrier of the scan in between.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared& sh, int& ph, uint32_t& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t u = __shfl_up(inc, off);
-    if (lane >= off) inc += u;
-  }
-  if (lane == 63) sh.w[wave] = inc;
+  const uint32_t inc = wave_scan<OpAdd>(v, 0u);
+  uint32_t* w = sh.w[ph];
+  ph ^= 1;
+  if (lane == 63) w[wave] = inc;
   __syncthreads();
-  uint32_t before = 0;
-  total = 0;
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kW; ++w) {
-    const uint32_t x = sh.w[w];
-    before += w < wave ? x : 0u;
-    total += x;
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t x = w[i];
+    before += i < wave ? x : 0u;
+    tot += x;
   }
-  __syncthreads();
+  total = tot;
   return before + inc - v;
 }
 
-__device__ __forceinline__ int pass_bins(int p) { return p == 0 ? 4096 : p == 1 ? 2048 : 1024; }
-__device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
-__device__ __forceinline__ int pass_offset(int p) { return p == 0 ? 0 : p == 1 ? 4096 : 6144; }
-__device__ __forceinline__ uint64_t pass_mask(int p) {  // key bits fixed before pass p
-  return p == 0 ? 0ull : p == 1 ? (0xFFFull << 21) : (0x7FFFFFull << 10);
-}
-
-// Adds this thread's matching keys to the LDS histogram of pass p.
-__device__ __forceinline__ void hist_add(uint32_t* hist, int p, uint64_t prefix,
-                                         const uint64_t (&k)[kKpt], uint32_t valid) {
-  const int shift = pass_shift(p);
-  const uint32_t bmask = (uint32_t)pass_bins(p) - 1u;
-  const uint64_t pmask = pass_mask(p);
-#pragma unroll
-  for (int e = 0; e < kKpt; ++e)
-    if (((valid >> e) & 1u) && (k[e] & pmask) == prefix)
-      atomicAdd(&hist[(uint32_t)(k[e] >> shift) & bmask], 1u);
-}
-
-// Fixes the digit of pass p from its complete histogram: the bin holding the
-// need-th candidate counted from the top.  Thread t owns the bins of rank
-// [t * per, (t + 1) * per) from the top; a workgroup prefix sum of the
-// per-thread counts finds the owner.  Leaves (prefix, need, all_eq) in sh.
-__device__ __forceinline__ void pick_digit(const uint32_t* hist, int p, uint64_t prefix,
-                                           uint32_t need, Shared& sh) {
-  const int nb = pass_bins(p), per = nb / kT;   // 4, 2 or 1 bins per thread
+// ------------------------------------------------------------------ radix select
+// Fixes the digit of a pass from its complete histogram h of nb bins: the bin
+// holding the need-th matching key counted from the top.  Thread t owns the
+// bins of rank [t * per, (t + 1) * per) from the top; a workgroup prefix sum
+// of the per-thread counts finds the owner, which leaves (digit, need within
+// the bin) in sh.
+template <int NT>
+__device__ __forceinline__ void pick_digit(const uint32_t* h, int nb, uint32_t need, Shared& sh,
+                                           int& ph) {
+  constexpr int kPer = 4096 / NT;               // bins per thread at the widest digit
+  const int per = (nb + NT - 1) / NT;
   const int top = nb - (int)threadIdx.x * per;  // one past this thread's highest bin
-  uint32_t c[4];
+  uint32_t c[kPer];
   uint32_t ls = 0;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    c[b] = b < per ? hist[top - 1 - b] : 0u;
+  for (int b = 0; b < kPer; ++b) {
+    c[b] = (b < per && top - 1 - b >= 0) ? h[top - 1 - b] : 0u;
     ls += c[b];
   }
   uint32_t total;
-  const uint32_t above = scan_excl(ls, sh, total);
+  const uint32_t above = block_scan<NT>(ls, sh, ph, total);
   if (above < need && need <= above + ls) {
     uint32_t cum = above;
     bool done = false;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < per && !done) {
-        if (cum + c[b] >= need) {
-          sh.prefix = prefix | ((uint64_t)(top - 1 - b) << pass_shift(p));
-          sh.need = need - cum;
-          sh.all_eq = need - cum == c[b];
-          done = true;
-        } else {
-          cum += c[b];
-        }
+    for (int b = 0; b < kPer; ++b) {
+      if (!done && cum + c[b] >= need) {
+        sh.digit = (uint32_t)(top - 1 - b);
+        sh.need = need - cum;
+        sh.cnt = c[b];
+        done = true;
       }
+      cum += c[b];
     }
   }
   __syncthreads();
 }
 
-// Radix select over keys held in registers: the threshold key K* and the
-// number of K*-equal elements to take so that exactly `budget` are chosen.
-// `hist` holds kHistWords words: the three pass histograms, cleared together.
-__device__ __forceinline__ void radix_regs(const uint64_t (&k)[kKpt], uint32_t valid,
-                                           uint32_t budget, uint32_t* hist, Shared& sh,
-                                           uint64_t& kstar, uint32_t& need_eq) {
-  for (int b = threadIdx.x; b < kHistWords; b += kT) hist[b] = 0u;
-  __syncthreads();
-  uint64_t prefix = 0;
-  uint32_t need = budget;
-  for (int p = 0; p < 3; ++p) {
-    uint32_t* h = hist + pass_offset(p);
-    hist_add(h, p, prefix, k, valid);
-    __syncthreads();
-    pick_digit(h, p, prefix, need, sh);
-    prefix = sh.prefix;
-    need = sh.need;
-  }
-  kstar = prefix;
-  need_eq = need;
-}
-
-// Chosen elements of this thread (bit e), ranked in element order: all keys
-// above K*, then K*-equal keys while the running rank is below need_eq.
-// `eq_base` counts the K*-equal elements of earlier tiles.
-__device__ __forceinline__ uint32_t choose(const uint64_t (&k)[kKpt], uint32_t valid,
-                                           uint64_t kstar, uint32_t need_eq, uint32_t eq_base,
-                                           Shared& sh, uint32_t& eq_total) {
-  uint32_t gt = 0, eq = 0;
+// Class statistics of this thread's keys (the number of priority keys and the
+// (min, max) value of each class), block-reduced into out.
+template <int NT>
+__device__ __forceinline__ void class_stats(const uint32_t (&o)[kKpt], uint32_t pb, uint32_t valid,
+                                            Shared& sh, uint32_t (&out)[5]) {
+  constexpr int NW = NT / 64;
+  uint32_t v[5] = {(uint32_t)__popc(pb & valid), ~0u, 0u, ~0u, 0u};
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
-    const bool ok = (valid >> e) & 1u;
-    gt |= (ok && k[e] > kstar) ? (1u << e) : 0u;
-    eq |= (ok && k[e] == kstar) ? (1u << e) : 0u;
+    const bool ok = (valid >> e) & 1u, p = (pb >> e) & 1u;
+    const uint32_t x = o[e];
+    v[1] = (ok && !p && x < v[1]) ? x : v[1];
+    v[2] = (ok && !p && x > v[2]) ? x : v[2];
+    v[3] = (ok && p && x < v[3]) ? x : v[3];
+    v[4] = (ok && p && x > v[4]) ? x : v[4];
   }
-  if (sh.all_eq) {
-    eq_total = 0;   // not needed: every K*-equal element is chosen
-    return gt | eq;
-  }
-  uint32_t rank = scan_excl((uint32_t)__popc(eq), sh, eq_total) + eq_base;
-  uint32_t sel = gt;
+  v[0] = wave_scan<OpAdd>(v[0], 0u);
+  v[1] = wave_scan<OpMin>(v[1], ~0u);
+  v[2] = wave_scan<OpMax>(v[2], 0u);
+  v[3] = wave_scan<OpMin>(v[3], ~0u);
+  v[4] = wave_scan<OpMax>(v[4], 0u);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 63) {
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e)
-    if ((eq >> e) & 1u) {
-      if (rank < need_eq) sel |= 1u << e;
-      ++rank;
-    }
-  return sel;
+    for (int j = 0; j < 5; ++j) sh.r[j][wave] = v[j];
+  }
+  __syncthreads();
+  out[0] = 0u;
+  out[1] = ~0u;
+  out[2] = 0u;
+  out[3] = ~0u;
+  out[4] = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    out[0] += sh.r[0][i];
+    out[1] = min(out[1], sh.r[1][i]);
+    out[2] = max(out[2], sh.r[2][i]);
+    out[3] = min(out[3], sh.r[3][i]);
+    out[4] = max(out[4], sh.r[4][i]);
+  }
 }
 
-// Stages the scores [w0, w1) of a row in LDS (coalesced) and synchronizes.
+// Class of K*, the budget left within it, and the value bits still to be
+// decided: the class's values all share the leading bits of its (min, max).
+struct SelectStart {
+  uint32_t cls, need, prefix;
+  int hi;   // number of low value bits not yet fixed
+};
+
+__device__ __forceinline__ SelectStart select_start(const uint32_t (&st)[5], uint32_t budget) {
+  SelectStart a;
+  a.cls = st[0] >= budget ? 1u : 0u;
+  a.need = a.cls ? budget : budget - st[0];
+  const uint32_t mn = a.cls ? st[3] : st[1], mx = a.cls ? st[4] : st[2];
+  a.hi = mn == mx ? 0 : 32 - __clz(mn ^ mx);
+  a.prefix = a.hi == 32 ? 0u : (mn >> a.hi) << a.hi;
+  return a;
+}
+
+// Adds the keys of mask cm whose bits above `hi` equal the prefix (all of
+// them on the first pass) to the histogram of the digit of bits [hi - w, hi).
+__device__ __forceinline__ void hist_add(uint32_t* h, const uint32_t (&o)[kKpt], uint32_t cm,
+                                         uint32_t prefix, int hi, int w, bool first) {
+  const int shift = hi - w;
+  const uint32_t dm = (1u << w) - 1u;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e)
+    if (((cm >> e) & 1u) && (first || ((o[e] ^ prefix) >> hi) == 0u))
+      atomicAdd(&h[(o[e] >> shift) & dm], 1u);
+}
+
+// Radix select over keys held in registers.  `hist` holds kSelWords words:
+// the three pass histograms, then the list.  After the first pass only the
+// class keys of the chosen bin can hold K*; when they fit the list they are
+// compacted into it, and the later passes read the list instead of every key.
+template <int NT>
+__device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t pb,
+                                             uint32_t valid, uint32_t budget, uint32_t* hist,
+                                             Shared& sh, int& ph) {
+  uint4* h4 = reinterpret_cast<uint4*>(hist);
+  for (int b = threadIdx.x; b < kHistWords / 4; b += NT) h4[b] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) sh.list_n = 0u;
+  uint32_t st[5];
+  class_stats<NT>(o, pb, valid, sh, st);   // its barrier also orders the clear
+  SelectStart a = select_start(st, budget);
+  if (a.hi == 0) return {a.cls, a.prefix, a.need};
+  const uint32_t cm = valid & (a.cls ? pb : ~pb);
+  int w = min(a.hi, pass_width(0));
+  hist_add(hist, o, cm, a.prefix, a.hi, w, true);
+  __syncthreads();
+  pick_digit<NT>(hist, 1 << w, a.need, sh, ph);
+  a.hi -= w;
+  a.prefix |= sh.digit << a.hi;
+  a.need = sh.need;
+  const uint32_t c0 = sh.cnt;
+  if (a.hi == 0) return {a.cls, a.prefix, a.need};
+  if (c0 <= (uint32_t)kList) {
+    uint32_t* list = hist + kHistWords;
+    uint32_t mm = 0;
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      mm |= (((cm >> e) & 1u) && (o[e] >> a.hi) == (a.prefix >> a.hi)) ? (1u << e) : 0u;
+    const uint32_t cnt = (uint32_t)__popc(mm);
+    const uint32_t inc = wave_scan<OpAdd>(cnt, 0u);
+    const uint32_t wtot = __builtin_amdgcn_readlane(inc, 63);
+    uint32_t base = 0;
+    if ((threadIdx.x & 63) == 0 && wtot) base = atomicAdd(&sh.list_n, wtot);
+    uint32_t at = __builtin_amdgcn_readlane(base, 0) + inc - cnt;
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if ((mm >> e) & 1u) list[at++] = o[e];
+    __syncthreads();
+#pragma unroll 1
+    for (int p = 1; p < 3 && a.hi > 0; ++p) {
+      w = min(a.hi, pass_width(p));
+      uint32_t* h = hist + pass_offset(p);
+      const int shift = a.hi - w;
+      const uint32_t dm = (1u << w) - 1u;
+      for (uint32_t i = threadIdx.x; i < c0; i += NT) {
+        const uint32_t x = list[i];
+        if (((x ^ a.prefix) >> a.hi) == 0u) atomicAdd(&h[(x >> shift) & dm], 1u);
+      }
+      __syncthreads();
+      pick_digit<NT>(h, 1 << w, a.need, sh, ph);
+      a.hi -= w;
+      a.prefix |= sh.digit << a.hi;
+      a.need = sh.need;
+    }
+  } else {
+#pragma unroll 1
+    for (int p = 1; p < 3 && a.hi > 0; ++p) {
+      w = min(a.hi, pass_width(p));
+      uint32_t* h = hist + pass_offset(p);
+      hist_add(h, o, cm, a.prefix, a.hi, w, false);
+      __syncthreads();
+      pick_digit<NT>(h, 1 << w, a.need, sh, ph);
+      a.hi -= w;
+      a.prefix |= sh.digit << a.hi;
+      a.need = sh.need;
+    }
+  }
+  return {a.cls, a.prefix, a.need};
+}
+
+// Chosen-key masks of this thread: gt = above K*, eq = equal to K*.
+__device__ __forceinline__ void classify(const uint32_t (&o)[kKpt], uint32_t pb, uint32_t valid,
+                                         const Kstar& ks, uint32_t& gt, uint32_t& eq) {
+  const uint32_t cm = valid & (ks.cls ? pb : ~pb);
+  gt = ks.cls ? 0u : (valid & pb);
+  eq = 0u;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool in = (cm >> e) & 1u;
+    gt |= (in && o[e] > ks.value) ? (1u << e) : 0u;
+    eq |= (in && o[e] == ks.value) ? (1u << e) : 0u;
+  }
+}
+
+// Output slot of this thread's first chosen element and the rank of its first
+// K*-equal element, from one prefix sum of the packed counts (gt << 16 | eq;
+// each total is at most 16384): an element's slot is the number of keys above
+// K* before it plus min(K*-equal keys before it, need_eq).  gt_base / eq_base
+// count the elements of earlier tiles or parts; tot_gt / tot_eq return this
+// workgroup's totals.
+template <int NT>
+__device__ __forceinline__ void place(uint32_t gt, uint32_t eq, uint32_t need_eq, uint32_t gt_base,
+                                      uint32_t eq_base, Shared& sh, int& ph, uint32_t& pos,
+                                      uint32_t& rank, uint32_t& tot_gt, uint32_t& tot_eq) {
+  uint32_t total;
+  const uint32_t before =
+      block_scan<NT>(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq), sh, ph, total);
+  const uint32_t gb = gt_base + (before >> 16), eb = eq_base + (before & 0xFFFFu);
+  pos = gb + min(eb, need_eq);
+  rank = eb;
+  tot_gt = total >> 16;
+  tot_eq = total & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------ keys
+template <int NT>
 __device__ __forceinline__ void stage(const float* x, int w0, int w1, float* xs) {
 #pragma unroll 6
-  for (int i = threadIdx.x; i < w1 - w0; i += kT) xs[i] = x[w0 + i];
+  for (int i = threadIdx.x; i < w1 - w0; i += NT) xs[i] = x[w0 + i];
   __syncthreads();
 }
 
@@ -245,15 +406,30 @@ __device__ __forceinline__ void load_window(const Params& s, const float* x, int
   }
 }
 
-// Pooling from the register window: element e's terms are w[e + 16 + o],
-// |o| <= r <= kWin, clipped to [0, n) and taken left to right.  Terms outside
+// The 16 scores x[a0 .. a0 + 16) (a0 >= 0, a multiple of 4) with clamped
+// 16-byte loads, under the same conditions as load_window.
+__device__ __forceinline__ void load_page(const Params& s, const float* x, int a0, float (&v)[16]) {
+  const float4* p4 = reinterpret_cast<const float4*>(x);
+  const int q0 = a0 / 4, qmax = s.n / 4 - 1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 f = p4[min(q0 + q, qmax)];
+    v[4 * q] = f.x;
+    v[4 * q + 1] = f.y;
+    v[4 * q + 2] = f.z;
+    v[4 * q + 3] = f.w;
+  }
+}
+
+// Pooling from the register window: element e's terms are w[e + 16 + d],
+// |d| <= r <= kWin, clipped to [0, n) and taken left to right.  Terms outside
 // [0, n) are replaced once by the identity of the reduction (-inf / +0, which
 // leaves a left-to-right float32 sum unchanged) and NaNs are tracked in a bit
 // mask, so the inner loop is a plain max or add.  R is r when known at
-// compile time, else kWin with a mask on |o|.
+// compile time, else kWin with a mask on |d|.
 template <int R, bool MAX>
 __device__ __forceinline__ void pool_regs(const Params& s, int i0, float (&w)[kKpt + 2 * kWin],
-                                          uint64_t (&k)[kKpt]) {
+                                          uint32_t (&o)[kKpt]) {
   const int r = R < kWin ? R : s.pool_r;
   uint64_t nanm = 0;
 #pragma unroll
@@ -269,9 +445,9 @@ __device__ __forceinline__ void pool_regs(const Params& s, int i0, float (&w)[kK
     const int t = i0 + e;
     float y = MAX ? -__builtin_inff() : 0.f;
 #pragma unroll
-    for (int o = -R; o <= R; ++o) {
-      const float z = w[e + kWin + o];
-      const bool use = R < kWin || (o >= -r && o <= r);
+    for (int d = -R; d <= R; ++d) {
+      const float z = w[e + kWin + d];
+      const bool use = R < kWin || (d >= -r && d <= r);
       if (MAX)
         y = use ? fmaxf(y, z) : y;
       else
@@ -283,55 +459,73 @@ __device__ __forceinline__ void pool_regs(const Params& s, int i0, float (&w)[kK
       const int lo = max(t - r, 0), hi = min(t + r, s.n - 1);
       y = y / (float)(hi - lo + 1);
     }
-    k[e] = make_key(t < s.n ? y : 0.f, false);
+    o[e] = ord_key(t < s.n ? y : 0.f);
   }
 }
 
-// Cluster priority with pages of 16 tokens and radius r <= kWin from the
-// register window: i0 is page-aligned, so the centres that can reach this
-// thread's tokens lie in the previous, own and next pages.
-__device__ __forceinline__ void cluster_regs(const Params& s, int i0,
-                                             const float (&w)[kKpt + 2 * kWin],
-                                             uint64_t (&k)[kKpt]) {
-  int cen[3];
+// Centre of the page of 16 tokens starting at a0: the argmax (lowest index)
+// over its in-range tokens when the page exists, holds no NaN and its maximum
+// is >= theta; else -1.
+__device__ __forceinline__ int page_centre(const Params& s, const float (&v)[16], int a0) {
+  float best = v[0];
+  int arg = a0;
+  bool nan = best != best;
 #pragma unroll
-  for (int g = 0; g < 3; ++g) {
-    const int a0 = i0 + 16 * (g - 1);
-    float best = w[16 * g];
-    int arg = a0;
-    bool nan = best != best;
-#pragma unroll
-    for (int j = 1; j < 16; ++j) {
-      const float z = w[16 * g + j];
-      const bool in = a0 + j < s.n;
-      nan |= in && z != z;
-      if (in && z > best) {
-        best = z;
-        arg = a0 + j;
-      }
+  for (int j = 1; j < 16; ++j) {
+    const float z = v[j];
+    const bool in = a0 + j < s.n;
+    nan |= in && z != z;
+    if (in && z > best) {
+      best = z;
+      arg = a0 + j;
     }
-    const bool page = a0 >= 0 && a0 < s.n;
-    cen[g] = (page && !nan && best >= s.theta) ? arg : -1;
   }
+  const bool page = a0 >= 0 && a0 < s.n;
+  return (page && !nan && best >= s.theta) ? arg : -1;
+}
+
+// Cluster priority with pages of 16 tokens and radius r <= 16: a thread's 16
+// keys are exactly one page (i0 is page-aligned), and the centres that can
+// reach them are those of its own page and of the pages on either side.
+// Every thread finds its own page's centre; the neighbours' come from LDS,
+// with the pages just outside the part found by the first and last threads.
+template <int NT>
+__device__ __forceinline__ void cluster_page_keys(const Params& s, const float* x, int i0, int p0,
+                                                  int* cen, uint32_t (&o)[kKpt], uint32_t& pb) {
+  const bool first = threadIdx.x == 0, last = threadIdx.x == NT - 1;
+  const int ea = first ? p0 - 16 : p0 + NT * kKpt;   // the page outside the part
+  const bool extra = (first && p0 > 0) || (last && ea < s.n);
+  float v[16], u[16];
+  load_page(s, x, i0, v);
+  if (extra) load_page(s, x, ea, u);
+  cen[threadIdx.x + 1] = page_centre(s, v, i0);
+  if (first || last) cen[first ? 0 : NT + 1] = extra ? page_centre(s, u, ea) : -1;
+  __syncthreads();
+  const int cc[3] = {cen[threadIdx.x], cen[threadIdx.x + 1], cen[threadIdx.x + 2]};
   const int r = s.r;
+  pb = 0;
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
     const int t = i0 + e;
     bool pr = false;
 #pragma unroll
-    for (int g = 0; g < 3; ++g) pr |= cen[g] >= 0 && t - cen[g] <= r && cen[g] - t <= r;
-    k[e] = make_key(t < s.n ? w[e + kWin] : 0.f, pr);
+    for (int g = 0; g < 3; ++g) pr |= cc[g] >= 0 && t - cc[g] <= r && cc[g] - t <= r;
+    pb |= pr ? (1u << e) : 0u;
+    o[e] = ord_key(t < s.n ? v[e] : 0.f);
   }
 }
 
 // Keys of this thread's elements i0 + e (i0 = p0 + 16 * tid) of the part
-// [p0, p1); bit e of `valid` tells whether i0 + e < p1.  Leaves `smem` free.
-template <int T>
+// [p0, p1): value bits o[e], priority bit e of pb, and bit e of `valid` when
+// i0 + e < p1.  Leaves `smem` free.
+template <int T, int NT>
 __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int p1, uint32_t* smem,
-                                          uint64_t (&k)[kKpt], uint32_t& valid) {
+                                          int* cen, uint32_t (&o)[kKpt], uint32_t& pb,
+                                          uint32_t& valid) {
   const float* x = s.S + (int64_t)row * s.ld;
   const int i0 = p0 + (int)threadIdx.x * kKpt;
   valid = 0;
+  pb = 0;
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) valid |= (i0 + e < p1) ? (1u << e) : 0u;
   if constexpr (T == kPlain) {
@@ -353,15 +547,11 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
     }
     if (s.prio) {
       const uint8_t* pr = s.prio + (int64_t)row * s.n;
-      uint8_t q[kKpt];
 #pragma unroll
-      for (int e = 0; e < kKpt; ++e) q[e] = pr[min(i0 + e, s.n - 1)];
-#pragma unroll
-      for (int e = 0; e < kKpt; ++e) k[e] = make_key(v[e], q[e] != 0);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kKpt; ++e) k[e] = make_key(v[e], false);
+      for (int e = 0; e < kKpt; ++e) pb |= pr[min(i0 + e, s.n - 1)] != 0 ? (1u << e) : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) o[e] = ord_key(v[e]);
   } else if constexpr (T == kPool) {
     // pooled value over [t - r, t + r] clipped to [0, n): max (NaN if any term
     // is NaN) or the left-to-right float32 mean of the in-range terms
@@ -369,15 +559,15 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
       float w[kKpt + 2 * kWin];
       load_window(s, x, i0, w);
       if (s.pool_r == 3)
-        s.pool_max ? pool_regs<3, true>(s, i0, w, k) : pool_regs<3, false>(s, i0, w, k);
+        s.pool_max ? pool_regs<3, true>(s, i0, w, o) : pool_regs<3, false>(s, i0, w, o);
       else
-        s.pool_max ? pool_regs<kWin, true>(s, i0, w, k) : pool_regs<kWin, false>(s, i0, w, k);
+        s.pool_max ? pool_regs<kWin, true>(s, i0, w, o) : pool_regs<kWin, false>(s, i0, w, o);
       return;
     }
     float* xs = reinterpret_cast<float*>(smem);
     const int rp = s.pool_r;
     const int w0 = max(p0 - rp, 0), w1 = min(p1 + rp, s.n);
-    stage(x, w0, w1, xs);
+    stage<NT>(x, w0, w1, xs);
 #pragma unroll
     for (int e = 0; e < kKpt; ++e) {
       const int t = i0 + e;
@@ -399,7 +589,7 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
           y = acc / (float)(hi - lo + 1);
         }
       }
-      k[e] = make_key(y, false);
+      o[e] = ord_key(y);
     }
     __syncthreads();
   } else {
@@ -408,9 +598,7 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
     // a page holding a NaN has no centre.  Pages [qa, qb] hold every centre
     // that can reach the part.
     if (s.P == 16 && s.r <= kWin && s.vec && s.n % 4 == 0) {
-      float w[kKpt + 2 * kWin];
-      load_window(s, x, i0, w);
-      cluster_regs(s, i0, w, k);
+      cluster_page_keys<NT>(s, x, i0, p0, cen, o, pb);
       return;
     }
     const int P = s.P, r = s.r;
@@ -418,9 +606,9 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
     const int qb = min(p1 - 1 + r, s.n - 1) / P;
     const int w0 = qa * P, w1 = min((qb + 1) * P, s.n);
     float* xs = reinterpret_cast<float*>(smem);
-    int* cen = reinterpret_cast<int*>(smem + kStage);
-    stage(x, w0, w1, xs);
-    for (int j = threadIdx.x; j <= qb - qa; j += kT) {
+    int* pc = reinterpret_cast<int*>(smem + stage_words<NT>());
+    stage<NT>(x, w0, w1, xs);
+    for (int j = threadIdx.x; j <= qb - qa; j += NT) {
       const int a0 = (qa + j) * P, a1 = min(a0 + P, s.n);
       float best = xs[a0 - w0];
       int arg = a0;
@@ -433,7 +621,7 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
           arg = t;
         }
       }
-      cen[j] = (!nan && best >= s.theta) ? arg : -1;
+      pc[j] = (!nan && best >= s.theta) ? arg : -1;
     }
     __syncthreads();
 #pragma unroll
@@ -445,168 +633,223 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
         v = xs[t - w0];
         const int ua = max(t - r, 0) / P, ub = min(t + r, s.n - 1) / P;
         for (int u = ua; u <= ub; ++u) {
-          const int cc = cen[u - qa];
-          pr |= cc >= 0 && t - cc <= r && cc - t <= r;
+          const int c = pc[u - qa];
+          pr |= c >= 0 && t - c <= r && c - t <= r;
         }
       }
-      k[e] = make_key(v, pr);
+      pb |= pr ? (1u << e) : 0u;
+      o[e] = ord_key(v);
     }
     __syncthreads();
   }
 }
 
+template <int NT>
 __device__ __forceinline__ void write_forced(const Params& s, int32_t* out) {
-  for (int i = threadIdx.x; i < s.n_forced; i += kT) out[s.budget + i] = s.n + i;
+  for (int i = threadIdx.x; i < s.n_forced; i += NT) out[s.budget + i] = s.n + i;
 }
 
-// Stage 1: local top-`budget` of one part.  With a single part per row this is
-// the final answer (indices), else the chosen (key, index) candidates.
-template <int T>
-__global__ __launch_bounds__(kT) void topk_part_kernel(Params s) {
-  __shared__ uint32_t smem[LdsWords<T>::value];
+// Candidate slot i of a row is stored at cand_at(i): within each tile of kCap
+// slots, slot 16t + e (key e of merge thread t) sits at (e / 2) * 2 * kT +
+// 2t + e % 2, so every 16-byte load of the merge is coalesced across a wave.
+__device__ __forceinline__ int64_t cand_at(int64_t i) {
+  const int64_t tile = i & ~(int64_t)(kCap - 1);
+  const int u = (int)(i & (kCap - 1)), t = u >> 4, e = u & 15;
+  return tile + (e >> 1) * (2 * kT) + 2 * t + (e & 1);
+}
+
+// ------------------------------------------------------------------ stage 1
+// Local top-`budget` of one part.  With a single part per row this is the
+// final answer (indices), else the chosen (key, index) candidates.  Workgroup
+// i takes part i / H of row i % H: workgroups are dealt to the XCDs in turn,
+// so with H a multiple of 8 every part of a row runs on the XCD that then
+// runs the row's merge workgroup, and the candidates stay in its L2.
+template <int T, int NT>
+__global__ __launch_bounds__(NT) void topk_part_kernel(Params s, int H) {
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LdsWords<T, NT>::value];
+  __shared__ int cen[T == kCluster ? NT + 2 : 1];
   __shared__ Shared sh;
-  const int row = blockIdx.y, part = blockIdx.x;
-  const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
+  const int row = (int)(blockIdx.x % (unsigned)H), part = (int)(blockIdx.x / (unsigned)H);
+  const int p0 = part * s.part, p1 = min(p0 + s.part, s.n);
   const int m = p1 - p0;
-  uint64_t k[kKpt];
-  uint32_t valid;
-  part_keys<T>(s, row, p0, p1, smem, k, valid);
+  uint32_t o[kKpt], pb, valid;
+  part_keys<T, NT>(s, row, p0, p1, smem, cen, o, pb, valid);
   const uint32_t keep = (uint32_t)min(s.budget, m);
-  uint32_t sel, tot;
-  if (keep == (uint32_t)m) {
-    sel = valid;
-  } else {
-    uint64_t kstar;
-    uint32_t need_eq;
-    radix_regs(k, valid, keep, smem, sh, kstar, need_eq);
-    sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
+  int ph = 0;
+  Kstar ks{0u, 0u, 0u};
+  uint32_t gt = valid, eq = 0u;
+  if (keep != (uint32_t)m) {
+    ks = select_regs<NT>(o, pb, valid, keep, smem, sh, ph);
+    classify(o, pb, valid, ks, gt, eq);
   }
-  uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+  uint32_t pos, rank, tg, te;
+  place<NT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
   const int i0 = p0 + (int)threadIdx.x * kKpt;
   if (s.parts == 1) {
     int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
 #pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if ((sel >> e) & 1u) out[pos++] = i0 + e;
-    write_forced(s, out);
+    for (int e = 0; e < kKpt; ++e) {
+      const bool q = (eq >> e) & 1u;
+      if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = i0 + e;
+      rank += q;
+    }
+    write_forced<NT>(s, out);
   } else {
-    uint64_t* c = s.cand + (int64_t)row * s.cand_ld + (int64_t)part * s.stride;
+    uint64_t* c = s.cand + (int64_t)row * s.cand_ld;
+    const int64_t slot0 = (int64_t)part * s.stride;
 #pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if ((sel >> e) & 1u) c[pos++] = (k[e] << 31) | (uint64_t)(uint32_t)(i0 + e);
+    for (int e = 0; e < kKpt; ++e) {
+      const bool q = (eq >> e) & 1u;
+      if (((gt >> e) & 1u) || (q && rank < ks.need_eq))
+        c[cand_at(slot0 + pos++)] = ((uint64_t)((pb >> e) & 1u) << 63) | ((uint64_t)o[e] << 31) |
+                                    (uint64_t)(uint32_t)(i0 + e);
+      rank += q;
+    }
   }
 }
 
-// Candidate keys of tile [t0, t0 + kCap) of a row: slot i belongs to part
-// i / stride and holds a candidate when i % stride < that part's count.
+// ------------------------------------------------------------------ stage 2
+// Candidate keys of tile [t0, t0 + kCap) of a row (count slots in all), this
+// thread's slots t0 + 16 * tid + e: slot i belongs to part i / stride and
+// holds a candidate when i % stride < that part's count.
 __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, int64_t t0,
-                                          uint64_t (&k)[kKpt], uint32_t (&ix)[kKpt],
-                                          uint32_t& valid) {
+                                          int64_t count, uint32_t (&o)[kKpt], uint32_t& pb,
+                                          uint32_t (&ix)[kKpt], uint32_t& valid) {
   const int64_t i0 = t0 + (int64_t)threadIdx.x * kKpt;
-  const uint4* p4 = reinterpret_cast<const uint4*>(c + i0);
   valid = 0;
+  pb = 0;
+  if (i0 >= count) {
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) o[e] = ix[e] = 0u;
+    return;
+  }
+  const uint4* p4 = reinterpret_cast<const uint4*>(c + t0 + 2 * threadIdx.x);
 #pragma unroll
   for (int q = 0; q < kKpt / 2; ++q) {
-    const uint4 v = p4[q];
-    const uint64_t a = ((uint64_t)v.y << 32) | v.x, b = ((uint64_t)v.w << 32) | v.z;
-    k[2 * q] = a >> 31;
-    k[2 * q + 1] = b >> 31;
-    ix[2 * q] = (uint32_t)(a & kIdxMask);
-    ix[2 * q + 1] = (uint32_t)(b & kIdxMask);
+    const uint4 v = p4[q * kT];
+    o[2 * q] = (v.y << 1) | (v.x >> 31);
+    o[2 * q + 1] = (v.w << 1) | (v.z >> 31);
+    pb |= (v.y >> 31) << (2 * q);
+    pb |= (v.w >> 31) << (2 * q + 1);
+    ix[2 * q] = v.x & kIdxMask;
+    ix[2 * q + 1] = v.z & kIdxMask;
   }
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
     const int64_t i = i0 + e;
     const int part = (int)(i / s.stride);
     const int slot = (int)(i - (int64_t)part * s.stride);
-    const int m = part < s.parts ? min(kCap, s.n - part * kCap) : 0;
+    const int m = part < s.parts ? min(s.part, s.n - part * s.part) : 0;
     valid |= slot < min(s.budget, m) ? (1u << e) : 0u;
   }
 }
 
-// Stage 2: the final selection among the candidates of all parts of a row.
+// The final selection among the candidates of all parts of a row.
 __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
-  __shared__ uint32_t hist[kHistWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWords];
   __shared__ Shared sh;
   const int row = blockIdx.x;
   const uint64_t* c = s.cand + (int64_t)row * s.cand_ld;
   int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
   const int64_t count = (int64_t)s.parts * s.stride;
-  uint64_t k[kKpt];
-  uint32_t ix[kKpt];
-  uint32_t valid;
-  uint32_t tot;
+  uint32_t o[kKpt], ix[kKpt], pb, valid;
+  int ph = 0;
+  uint32_t gt, eq, pos, rank, tg, te;
   if (count <= kCap) {
-    cand_keys(s, c, 0, k, ix, valid);
-    uint64_t kstar;
-    uint32_t need_eq;
-    radix_regs(k, valid, (uint32_t)s.budget, hist, sh, kstar, need_eq);
-    const uint32_t sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
-    uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+    cand_keys(s, c, 0, count, o, pb, ix, valid);
+    const Kstar ks = select_regs<kT>(o, pb, valid, (uint32_t)s.budget, hist, sh, ph);
+    classify(o, pb, valid, ks, gt, eq);
+    place<kT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
 #pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if ((sel >> e) & 1u) out[pos++] = (int32_t)ix[e];
+    for (int e = 0; e < kKpt; ++e) {
+      const bool q = (eq >> e) & 1u;
+      if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = (int32_t)ix[e];
+      rank += q;
+    }
   } else {
     // more candidates than registers hold: every pass re-reads them by tiles
     for (int b = threadIdx.x; b < kHistWords; b += kT) hist[b] = 0u;
-    __syncthreads();
-    uint64_t prefix = 0;
-    uint32_t need = (uint32_t)s.budget;
-    for (int p = 0; p < 3; ++p) {
+    uint32_t acc[5] = {0u, ~0u, 0u, ~0u, 0u};
+    for (int64_t t0 = 0; t0 < count; t0 += kCap) {
+      cand_keys(s, c, t0, count, o, pb, ix, valid);
+      uint32_t st[5];
+      class_stats<kT>(o, pb, valid, sh, st);
+      acc[0] += st[0];
+      acc[1] = min(acc[1], st[1]);
+      acc[2] = max(acc[2], st[2]);
+      acc[3] = min(acc[3], st[3]);
+      acc[4] = max(acc[4], st[4]);
+      __syncthreads();   // sh.r is written again by the next tile
+    }
+    SelectStart a = select_start(acc, (uint32_t)s.budget);
+#pragma unroll 1
+    for (int p = 0; p < 3 && a.hi > 0; ++p) {
+      const int w = min(a.hi, pass_width(p));
       uint32_t* h = hist + pass_offset(p);
       for (int64_t t0 = 0; t0 < count; t0 += kCap) {
-        cand_keys(s, c, t0, k, ix, valid);
-        hist_add(h, p, prefix, k, valid);
+        cand_keys(s, c, t0, count, o, pb, ix, valid);
+        hist_add(h, o, valid & (a.cls ? pb : ~pb), a.prefix, a.hi, w, p == 0);
       }
       __syncthreads();
-      pick_digit(h, p, prefix, need, sh);
-      prefix = sh.prefix;
-      need = sh.need;
+      pick_digit<kT>(h, 1 << w, a.need, sh, ph);
+      a.hi -= w;
+      a.prefix |= sh.digit << a.hi;
+      a.need = sh.need;
     }
-    uint32_t eq_base = 0, sel_base = 0;
+    const Kstar ks{a.cls, a.prefix, a.need};
+    uint32_t gt_base = 0, eq_base = 0;
     for (int64_t t0 = 0; t0 < count; t0 += kCap) {
-      cand_keys(s, c, t0, k, ix, valid);
-      uint32_t eq_tot;
-      const uint32_t sel = choose(k, valid, prefix, need, eq_base, sh, eq_tot);
-      uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot) + sel_base;
+      cand_keys(s, c, t0, count, o, pb, ix, valid);
+      classify(o, pb, valid, ks, gt, eq);
+      place<kT>(gt, eq, ks.need_eq, gt_base, eq_base, sh, ph, pos, rank, tg, te);
 #pragma unroll
-      for (int e = 0; e < kKpt; ++e)
-        if ((sel >> e) & 1u) out[pos++] = (int32_t)ix[e];
-      eq_base += eq_tot;
-      sel_base += tot;
+      for (int e = 0; e < kKpt; ++e) {
+        const bool q = (eq >> e) & 1u;
+        if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = (int32_t)ix[e];
+        rank += q;
+      }
+      gt_base += tg;
+      eq_base += te;
     }
   }
-  write_forced(s, out);
+  write_forced<kT>(s, out);
 }
 
 // ------------------------------------------------------------------ wide rows
 // Rows whose candidates would not fit one workgroup (parts * min(budget,
 // kCap) > kCap, e.g. a 20% keep rate of a 128K-token row) run the radix
 // select across all parts of the row instead: five launches, each one
-// workgroup per (part, row), with no workgroup ever waiting for another.
-// Every launch recomputes its part's keys.  Launch P (0 < P <= 3) first fixes
-// digit P-1 from the sum over parts of that pass's per-part histograms and
-// the state (prefix, need) the previous launch left; every workgroup of the
-// row reaches the same digit, and part 0 records the new state for the next
-// launch.  Launches 0-2 then write their part's histogram of pass P; launch 3,
-// which has fixed K* and the number of K*-equal elements to take, writes the
-// part's counts of keys above and equal to K*.  Launch 4 gives each part its
-// output offset and its share of the K*-equal elements (in part order, so
-// ties still go to the lower index) and writes the chosen indices.
+// workgroup per (part, row) of kCap elements, with no workgroup ever waiting
+// for another.  The key is the 33-bit (class, value) and the digits are fixed:
+// bits 32-21, 20-10 and 9-0.  Every launch recomputes its part's keys.
+// Launch P (0 < P <= 3) first fixes digit P-1 from the sum over parts of that
+// pass's per-part histograms and the state (prefix, need) the previous launch
+// left; every workgroup of the row reaches the same digit, and part 0 records
+// the new state for the next launch.  Launches 0-2 then write their part's
+// histogram of pass P; launch 3, which has fixed K* and the number of
+// K*-equal elements to take, writes the part's counts of keys above and equal
+// to K*.  Launch 4 gives each part its output offset and its share of the
+// K*-equal elements (in part order, so ties still go to the lower index) and
+// writes the chosen indices.
 constexpr int kWideMaxParts = 16;
 constexpr int kCnt = 4096 + 2048 + 1024;       // per part: the three histograms, then (gt, eq)
 constexpr int kState = kCnt + 2;               // part 0 only: state after pass p at kState + 4p
 constexpr int kWideWords = kState + 12;        // per (row, part)
+__device__ __forceinline__ constexpr int wide_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
+
+__device__ __forceinline__ uint64_t key33(const uint32_t (&o)[kKpt], uint32_t pb, int e) {
+  return ((uint64_t)((pb >> e) & 1u) << 32) | o[e];
+}
 
 __device__ __forceinline__ uint32_t* wide_of(const Params& s, int row, int part) {
   return s.wide + ((int64_t)row * s.parts + part) * kWideWords;
 }
 
-// The digit of pass p from the per-part histograms of the row, given the
-// prefix and need before it.  Leaves (prefix, need, all_eq) in sh.
-__device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint64_t prefix,
-                                          uint32_t need, uint32_t* hist, Shared& sh) {
-  const int nb = pass_bins(p);
+// The digit of pass p from the per-part histograms of the row, given the need
+// before it.  Leaves (digit, need) in sh.
+__device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint32_t need,
+                                          uint32_t* hist, Shared& sh, int& ph) {
+  const int nb = 1 << pass_width(p);
   for (int b = threadIdx.x; b < nb; b += kT) {
     uint32_t c[kWideMaxParts];
 #pragma unroll
@@ -618,20 +861,21 @@ __device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint6
     hist[b] = v;
   }
   __syncthreads();
-  pick_digit(hist, p, prefix, need, sh);
+  pick_digit<kT>(hist, nb, need, sh, ph);
 }
 
 template <int T, int STAGE>
 __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
-  __shared__ uint32_t smem[LdsWords<T>::value];
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LdsWords<T, kT>::value];
+  __shared__ int cen[T == kCluster ? kT + 2 : 1];
   __shared__ Shared sh;
   const int row = blockIdx.y, part = blockIdx.x;
   const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
-  uint64_t k[kKpt];
-  uint32_t valid;
-  part_keys<T>(s, row, p0, p1, smem, k, valid);
+  uint32_t o[kKpt], pb, valid;
+  part_keys<T, kT>(s, row, p0, p1, smem, cen, o, pb, valid);
   uint32_t* mine = wide_of(s, row, part);
   uint32_t* state = wide_of(s, row, 0) + kState;
+  int ph = 0;
   // the state before this launch's digit, then the digit itself
   uint64_t prefix = 0;
   uint32_t need = (uint32_t)s.budget;
@@ -639,67 +883,66 @@ __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
     const uint32_t* st = state + 4 * (STAGE - 2);
     prefix = ((uint64_t)st[1] << 32) | st[0];
     need = st[2];
-    if constexpr (STAGE == 4) {
-      if (threadIdx.x == 0) sh.all_eq = st[3];
-      __syncthreads();
-    }
   }
   if constexpr (STAGE >= 1 && STAGE <= 3) {
-    wide_pick(s, row, STAGE - 1, prefix, need, smem, sh);
-    prefix = sh.prefix;
+    wide_pick(s, row, STAGE - 1, need, smem, sh, ph);
+    prefix |= (uint64_t)sh.digit << wide_shift(STAGE - 1);
     need = sh.need;
     if (part == 0 && threadIdx.x == 0) {
       uint32_t* st = state + 4 * (STAGE - 1);
       st[0] = (uint32_t)prefix;
       st[1] = (uint32_t)(prefix >> 32);
       st[2] = need;
-      st[3] = sh.all_eq;
     }
   }
   if constexpr (STAGE < 3) {
     uint32_t* h = smem;
-    for (int b = threadIdx.x; b < pass_bins(STAGE); b += kT) h[b] = 0u;
+    constexpr int nb = 1 << pass_width(STAGE);
+    constexpr int shift = wide_shift(STAGE);
+    constexpr int above = shift + pass_width(STAGE);   // bits above the digit are fixed
+    for (int b = threadIdx.x; b < nb; b += kT) h[b] = 0u;
     __syncthreads();
-    hist_add(h, STAGE, prefix, k, valid);
-    __syncthreads();
-    for (int b = threadIdx.x; b < pass_bins(STAGE); b += kT) mine[pass_offset(STAGE) + b] = h[b];
-  } else if constexpr (STAGE == 3) {
-    uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < kKpt; ++e) {
-      const bool ok = (valid >> e) & 1u;
-      gt += (ok && k[e] > prefix) ? 1u : 0u;
-      eq += (ok && k[e] == prefix) ? 1u : 0u;
+      const uint64_t k = key33(o, pb, e);
+      if (((valid >> e) & 1u) && (STAGE == 0 || (k >> above) == (prefix >> above)))
+        atomicAdd(&h[(uint32_t)(k >> shift) & (uint32_t)(nb - 1)], 1u);
     }
-    uint32_t tot_gt, tot_eq;
-    scan_excl(gt, sh, tot_gt);
-    scan_excl(eq, sh, tot_eq);
-    if (threadIdx.x == 0) {
-      mine[kCnt] = tot_gt;
-      mine[kCnt + 1] = tot_eq;
-    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < nb; b += kT) mine[pass_offset(STAGE) + b] = h[b];
   } else {
-    // offset of this part's output and its share of the K*-equal elements
-    uint32_t gt_before = 0, eq_before = 0;
-    for (int q = 0; q < part; ++q) {
-      gt_before += wide_of(s, row, q)[kCnt];
-      eq_before += wide_of(s, row, q)[kCnt + 1];
-    }
-    const uint32_t my_eq = mine[kCnt + 1];
-    const uint32_t take_eq = need > eq_before ? min(need - eq_before, my_eq) : 0u;
-    const uint32_t base = gt_before + min(eq_before, need);
-    uint32_t sel_eq, tot;
-    const uint32_t sel = choose(k, valid, prefix, take_eq, 0u, sh, sel_eq);
-    uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot) + base;
-    int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
-    const int i0 = p0 + (int)threadIdx.x * kKpt;
-#pragma unroll
-    for (int e = 0; e < kKpt; ++e)
-      if ((sel >> e) & 1u) {
-        if (pos < (uint32_t)s.budget) out[pos] = i0 + e;   // the counts make pos < budget
-        ++pos;
+    const Kstar ks{(uint32_t)(prefix >> 32), (uint32_t)prefix, need};
+    uint32_t gt, eq;
+    classify(o, pb, valid, ks, gt, eq);
+    if constexpr (STAGE == 3) {
+      uint32_t total;
+      block_scan<kT>(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq), sh, ph, total);
+      if (threadIdx.x == 0) {
+        mine[kCnt] = total >> 16;
+        mine[kCnt + 1] = total & 0xFFFFu;
       }
-    if (part == 0) write_forced(s, out);
+    } else {
+      // offset of this part's output and its share of the K*-equal elements
+      uint32_t gt_before = 0, eq_before = 0;
+      for (int q = 0; q < part; ++q) {
+        gt_before += wide_of(s, row, q)[kCnt];
+        eq_before += wide_of(s, row, q)[kCnt + 1];
+      }
+      uint32_t pos, rank, tg, te;
+      place<kT>(gt, eq, need, gt_before, eq_before, sh, ph, pos, rank, tg, te);
+      int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
+      const int i0 = p0 + (int)threadIdx.x * kKpt;
+#pragma unroll
+      for (int e = 0; e < kKpt; ++e) {
+        const bool q = (eq >> e) & 1u;
+        if (((gt >> e) & 1u) || (q && rank < need)) {
+          if (pos < (uint32_t)s.budget) out[pos] = i0 + e;   // the counts make pos < budget
+          ++pos;
+        }
+        rank += q;
+      }
+      if (part == 0) write_forced<kT>(s, out);
+    }
   }
 }
 
@@ -708,7 +951,7 @@ __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
 // (ascending), then the last min(L, pages) pages, then -1.  [DELTA] key design
 // 2; pages per sequence <= kCap.
 __global__ __launch_bounds__(kT) void topk_delta_kernel(DeltaLaunch p) {
-  __shared__ uint32_t hist[kHistWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWords];
   __shared__ Shared sh;
   const int b = blockIdx.x;
   const int Lb = min(max(p.L[b], 0), p.L_max);
@@ -719,29 +962,30 @@ __global__ __launch_bounds__(kT) void topk_delta_kernel(DeltaLaunch p) {
   const float* Sb = p.S + (int64_t)b * p.n_pages_max;
   int32_t* out = p.rho + (int64_t)b * p.K_pages;
   const int i0 = (int)threadIdx.x * kKpt;
-  uint64_t k[kKpt];
-  uint32_t valid = 0;
+  uint32_t o[kKpt], valid = 0;
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
     const bool in = i0 + e < n_cand;
     valid |= in ? (1u << e) : 0u;
-    k[e] = make_key(in ? Sb[i0 + e] : 0.f, false);
+    o[e] = ord_key(in ? Sb[i0 + e] : 0.f);
   }
-  uint32_t sel, tot;
-  if (keep >= n_cand) {
-    sel = valid;
-  } else if (keep == 0) {
-    sel = 0;
-  } else {
-    uint64_t kstar;
-    uint32_t need_eq;
-    radix_regs(k, valid, (uint32_t)keep, hist, sh, kstar, need_eq);
-    sel = choose(k, valid, kstar, need_eq, 0u, sh, tot);
+  int ph = 0;
+  Kstar ks{0u, 0u, 0u};
+  uint32_t gt = valid, eq = 0u;
+  if (keep == 0) {
+    gt = 0u;
+  } else if (keep < n_cand) {
+    ks = select_regs<kT>(o, 0u, valid, (uint32_t)keep, hist, sh, ph);
+    classify(o, 0u, valid, ks, gt, eq);
   }
-  uint32_t pos = scan_excl((uint32_t)__popc(sel), sh, tot);
+  uint32_t pos, rank, tg, te;
+  place<kT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e)
-    if ((sel >> e) & 1u) out[pos++] = i0 + e;
+  for (int e = 0; e < kKpt; ++e) {
+    const bool q = (eq >> e) & 1u;
+    if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = i0 + e;
+    rank += q;
+  }
   for (int i = threadIdx.x; i < p.K_pages - keep; i += kT)
     out[keep + i] = i < n_recent ? n_cand + i : -1;
 }
@@ -754,22 +998,38 @@ __global__ __launch_bounds__(256) void topk_forced_kernel(int n, int n_forced,
     out[i] = n + i;
 }
 
-int parts_of(int n) { return (n + kCap - 1) / kCap; }
-int stride_of(int budget) { return budget < kCap ? budget : kCap; }
+// ------------------------------------------------------------------ host
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bool wide_path(int n, int budget) {
+  const int parts = ceil_div(n, kCap);
+  const int stride = budget < kCap ? budget : kCap;
+  return parts > 1 && parts <= kWideMaxParts && (int64_t)parts * stride > kCap;
+}
+
+// Elements per stage-1 part: small parts (twice the workgroups, each with half
+// the keys) when the candidates of all of them still fit one merge workgroup.
+int part_of(int n, int budget) {
+  if (n <= kCap || wide_path(n, budget)) return kCap;
+  const int stride = budget < kSmallCap ? budget : kSmallCap;
+  return (int64_t)ceil_div(n, kSmallCap) * stride <= kCap ? kSmallCap : kCap;
+}
+
 int64_t cand_ld_of(int n, int budget) {
-  const int64_t slots = (int64_t)parts_of(n) * stride_of(budget);
+  const int part = part_of(n, budget);
+  const int stride = budget < part ? budget : part;
+  const int64_t slots = (int64_t)ceil_div(n, part) * stride;
   return (slots + kCap - 1) / kCap * kCap;
 }
 
 template <int T>
 void launch(const Params& s, int H, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_part_kernel<T>, dim3(s.parts, H), dim3(kT), 0, stream, s);
+  const unsigned grid = (unsigned)s.parts * (unsigned)H;
+  if (s.part == kSmallCap)
+    hipLaunchKernelGGL((topk_part_kernel<T, kSmallT>), dim3(grid), dim3(kSmallT), 0, stream, s, H);
+  else
+    hipLaunchKernelGGL((topk_part_kernel<T, kT>), dim3(grid), dim3(kT), 0, stream, s, H);
   if (s.parts > 1) hipLaunchKernelGGL(topk_merge_kernel, dim3(H), dim3(kT), 0, stream, s);
-}
-
-bool wide_path(int n, int budget) {
-  const int parts = parts_of(n);
-  return parts > 1 && parts <= kWideMaxParts && (int64_t)parts * stride_of(budget) > kCap;
 }
 
 template <int T>
@@ -785,9 +1045,9 @@ void launch_wide(const Params& s, int H, hipStream_t stream) {
 }  // namespace
 
 size_t topk_ws_bytes(int H, int n, int budget) {
-  if (budget <= 0 || parts_of(n) == 1) return 0;
+  if (budget <= 0 || n <= kCap) return 0;
   if (wide_path(n, budget))
-    return align_up((size_t)H * parts_of(n) * kWideWords * sizeof(uint32_t), kWsAlign);
+    return align_up((size_t)H * ceil_div(n, kCap) * kWideWords * sizeof(uint32_t), kWsAlign);
   return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
 }
 
@@ -818,13 +1078,15 @@ kvs_status select_run(const SelectCall& c, hipStream_t stream) {
   s.budget = c.budget;
   s.n_forced = c.n_forced;
   s.vec = ((uintptr_t)c.S % 16 == 0) && (c.ld % 4 == 0);
-  s.parts = parts_of(c.n);
-  s.stride = stride_of(c.budget);
+  s.part = part_of(c.n, c.budget);
+  s.parts = ceil_div(c.n, s.part);
+  s.stride = c.budget < s.part ? c.budget : s.part;
   s.cand_ld = cand_ld_of(c.n, c.budget);
   s.cand = static_cast<uint64_t*>(c.ws);
   s.wide = static_cast<uint32_t*>(c.ws);
   s.idx = c.idx;
   const bool wide = wide_path(c.n, c.budget);
+  if (!wide && (int64_t)s.parts * c.H > 0x7FFFFFFF) return KVS_EUNSUPPORTED;
   if (c.cluster_P > 0)
     wide ? launch_wide<kCluster>(s, c.H, stream) : launch<kCluster>(s, c.H, stream);
   else if (c.pool != KVS_RED_NONE)

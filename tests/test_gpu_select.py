@@ -92,6 +92,10 @@ TOPK_CASES = [
     (2, 32769, 16385, 0, 5, True),       # last part of one element
     (1, 262144, 100000, 0, 0, False),    # the most parts this path takes
     (1, 262145, 100000, 0, 3, False),    # one part more: the single-workgroup merge
+    # stage-1 parts of 8192 elements (the candidates of all parts fit one merge)
+    (1, 16385, 1000, 0, 3, True),        # last part of one element
+    (2, 40000, 3000, 2, 5, True),        # five parts, ties across part edges
+    (2, 131040, 1025, 0, 0, False),      # one slot too many for small parts: parts of 16384
 ]
 
 
@@ -191,6 +195,32 @@ def test_union_golden(kvs):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(indptr.cpu().numpy(), c["kv_indptr"])
     np.testing.assert_array_equal(indices.cpu().numpy()[:c["kv_indptr"][-1]], c["kv_indices"])
+
+
+@pytest.mark.parametrize("n,budget", [(5000, 700), (131040, 1024), (20000, 19999)])
+def test_topk_equal_values(kvs, n, budget):
+    """Every value of a class equal: no radix pass, ties decided by index."""
+    x = np.full((2, n), np.float32(0.25), dtype=np.float32)
+    x[1, ::7] = np.float32(0.5)
+    prio = synth.priority_array(77, 2, n)
+    for pr in (None, prio):
+        got = kvs.kvs_topk(dev(x), n, budget, priority=dev(pr) if pr is not None else None,
+                           n_forced=3)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x, budget, pr, 3))
+
+
+@pytest.mark.parametrize("n,budget", [(16000, 1600), (131040, 1024), (60000, 20000)])
+def test_topk_narrow_values(kvs, n, budget):
+    """Values within a few ulps of each other share all their leading bits."""
+    steps = (synth.u64(91, 1, np.arange(2 * n)) % np.uint64(37)).astype(np.float32)
+    x = (np.float32(1.0) + steps * np.float32(2.0 ** -20)).reshape(2, n).astype(np.float32)
+    x[1] = np.float32(-3.0) - steps.reshape(2, n)[1] * np.float32(2.0 ** -18)
+    prio = synth.priority_array(92, 2, n, 1, 50)
+    for pr in (None, prio):
+        got = kvs.kvs_topk(dev(x), n, budget, priority=dev(pr) if pr is not None else None)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x, budget, pr, 0))
 
 
 def test_deterministic_selection(kvs):
