@@ -50,6 +50,7 @@ enum Transform { kPlain = 0, kPool = 1, kCluster = 2 };
 constexpr int kHistWords = 4096 + 2048 + 1024;   // one histogram per radix pass
 constexpr int kList = 4096;                       // keys left after the first pass, at most
 constexpr int kSelWords = kHistWords + kList;     // LDS words of a selection
+constexpr uint32_t kFinish = 32;                  // lists this short are finished by one wave
 __device__ __forceinline__ constexpr int pass_width(int p) { return p == 0 ? 12 : p == 1 ? 11 : 10; }
 __device__ __forceinline__ constexpr int pass_offset(int p) { return p == 0 ? 0 : p == 1 ? 4096 : 6144; }
 
@@ -91,6 +92,7 @@ struct Shared {
   uint32_t digit, need;   // result of a digit pick: the bin and the need within it,
   uint32_t cnt;           // and the bin's count
   uint32_t list_n;        // keys compacted into the list
+  uint32_t kval, need_eq; // K* found from the list
 };
 
 // The threshold of a selection: K* = (cls, value).  Every element of a higher
@@ -163,38 +165,64 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared& sh, int& ph, 
 }
 
 // ------------------------------------------------------------------ radix select
-// Fixes the digit of a pass from its complete histogram h of nb bins: the bin
-// holding the need-th matching key counted from the top.  Thread t owns the
-// bins of rank [t * per, (t + 1) * per) from the top; a workgroup prefix sum
-// of the per-thread counts finds the owner, which leaves (digit, need within
-// the bin) in sh.
-template <int NT>
-__device__ __forceinline__ void pick_digit(const uint32_t* h, int nb, uint32_t need, Shared& sh,
-                                           int& ph) {
-  constexpr int kPer = 4096 / NT;               // bins per thread at the widest digit
-  const int per = (nb + NT - 1) / NT;
-  const int top = nb - (int)threadIdx.x * per;  // one past this thread's highest bin
-  uint32_t c[kPer];
-  uint32_t ls = 0;
-#pragma unroll
-  for (int b = 0; b < kPer; ++b) {
-    c[b] = (b < per && top - 1 - b >= 0) ? h[top - 1 - b] : 0u;
-    ls += c[b];
-  }
-  uint32_t total;
-  const uint32_t above = block_scan<NT>(ls, sh, ph, total);
-  if (above < need && need <= above + ls) {
-    uint32_t cum = above;
-    bool done = false;
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) {
-      if (!done && cum + c[b] >= need) {
-        sh.digit = (uint32_t)(top - 1 - b);
-        sh.need = need - cum;
-        sh.cnt = c[b];
-        done = true;
+// Fixes the digit of a pass from its complete histogram h of nb bins (a power
+// of two, at most 4096): the bin holding the need-th matching key counted
+// from the top.  Wave 0 alone: lane l owns the bins of rank [l * per,
+// (l + 1) * per) from the top; a wave prefix sum finds the owner lane, whose
+// bins are then spread over the lanes for a second one.  Leaves (digit, need
+// within the bin, the bin's count) in sh and synchronises the workgroup.
+__device__ __forceinline__ void pick_digit(const uint32_t* h, int nb, uint32_t need, Shared& sh) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = nb >= 64 ? nb >> 6 : 1;
+    const int top = nb - lane * per;   // one past the lane's highest bin
+    uint32_t ls = 0;
+    if (per >= 4) {
+      const uint4* h4 = reinterpret_cast<const uint4*>(h + (top - per));
+      for (int k = 0; k < (per >> 2); ++k) {
+        const uint4 v = h4[k];
+        ls += v.x + v.y + v.z + v.w;
       }
-      cum += c[b];
+    } else {
+      for (int b = 0; b < per; ++b)
+        if (top - 1 - b >= 0) ls += h[top - 1 - b];
+    }
+    const uint32_t inc = wave_scan<OpAdd>(ls, 0u);
+    const uint64_t own = __ballot(inc - ls < need && need <= inc);
+    const int L = (int)__builtin_ctzll(own);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(inc - ls), L);
+    const int topL = nb - L * per;
+    const uint32_t c = (lane < per && topL - 1 - lane >= 0) ? h[topL - 1 - lane] : 0u;
+    const uint32_t inc2 = above + wave_scan<OpAdd>(c, 0u);
+    const uint64_t hit = __ballot(lane < per && inc2 - c < need && need <= inc2);
+    if (lane == (int)__builtin_ctzll(hit)) {
+      sh.digit = (uint32_t)(topL - 1 - lane);
+      sh.need = need - (inc2 - c);
+      sh.cnt = c;
+    }
+  }
+  __syncthreads();
+}
+
+// K* among the c <= 64 keys of list: the need-th largest, and how many of the
+// keys equal to it are taken.  Wave 0 alone: lane l counts the keys above and
+// at least its own.  Leaves (kval, need_eq) in sh and synchronises.
+__device__ __forceinline__ void finish_list(const uint32_t* list, uint32_t c, uint32_t need,
+                                            Shared& sh) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const bool ok = (uint32_t)lane < c;
+    const uint32_t x = ok ? list[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < c; ++j) {
+      const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
+      gt += y > x ? 1u : 0u;
+      ge += y >= x ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(ok && gt < need && need <= ge);
+    if (lane == (int)__builtin_ctzll(hit)) {
+      sh.kval = x;
+      sh.need_eq = need - gt;
     }
   }
   __syncthreads();
@@ -290,7 +318,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
   int w = min(a.hi, pass_width(0));
   hist_add(hist, o, cm, a.prefix, a.hi, w, true);
   __syncthreads();
-  pick_digit<NT>(hist, 1 << w, a.need, sh, ph);
+  pick_digit(hist, 1 << w, a.need, sh);
   a.hi -= w;
   a.prefix |= sh.digit << a.hi;
   a.need = sh.need;
@@ -312,6 +340,10 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
     for (int e = 0; e < kKpt; ++e)
       if ((mm >> e) & 1u) list[at++] = o[e];
     __syncthreads();
+    if (c0 <= kFinish) {
+      finish_list(list, c0, a.need, sh);
+      return {a.cls, sh.kval, sh.need_eq};
+    }
 #pragma unroll 1
     for (int p = 1; p < 3 && a.hi > 0; ++p) {
       w = min(a.hi, pass_width(p));
@@ -323,7 +355,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
         if (((x ^ a.prefix) >> a.hi) == 0u) atomicAdd(&h[(x >> shift) & dm], 1u);
       }
       __syncthreads();
-      pick_digit<NT>(h, 1 << w, a.need, sh, ph);
+      pick_digit(h, 1 << w, a.need, sh);
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
@@ -335,7 +367,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
       uint32_t* h = hist + pass_offset(p);
       hist_add(h, o, cm, a.prefix, a.hi, w, false);
       __syncthreads();
-      pick_digit<NT>(h, 1 << w, a.need, sh, ph);
+      pick_digit(h, 1 << w, a.need, sh);
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
@@ -709,9 +741,16 @@ __global__ __launch_bounds__(NT) void topk_part_kernel(Params s, int H) {
 }
 
 // ------------------------------------------------------------------ stage 2
+// Candidates of part q of a row: min(budget, elements of the part).
+__device__ __forceinline__ uint32_t part_count(const Params& s, uint32_t q) {
+  if (q >= (uint32_t)s.parts) return 0u;
+  const int64_t m = min((int64_t)s.part, (int64_t)s.n - (int64_t)q * s.part);
+  return (uint32_t)min((int64_t)s.budget, m);
+}
+
 // Candidate keys of tile [t0, t0 + kCap) of a row (count slots in all), this
-// thread's slots t0 + 16 * tid + e: slot i belongs to part i / stride and
-// holds a candidate when i % stride < that part's count.
+// thread's slots t0 + 16 * tid + e: slot j belongs to part j / stride and
+// holds a candidate when j % stride < that part's count.
 __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, int64_t t0,
                                           int64_t count, uint32_t (&o)[kKpt], uint32_t& pb,
                                           uint32_t (&ix)[kKpt], uint32_t& valid) {
@@ -734,13 +773,27 @@ __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, in
     ix[2 * q] = v.x & kIdxMask;
     ix[2 * q + 1] = v.z & kIdxMask;
   }
+  // one division per thread; the slots then step through at most two parts
+  // (stride >= 16) or one part at a time
+  const uint32_t stride = (uint32_t)s.stride, j0 = (uint32_t)i0;
+  uint32_t q = j0 / stride, slot = j0 - q * stride;
+  if (stride >= (uint32_t)kKpt) {
+    const uint32_t c0 = part_count(s, q), c1 = part_count(s, q + 1u), b = stride - slot;
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e) {
-    const int64_t i = i0 + e;
-    const int part = (int)(i / s.stride);
-    const int slot = (int)(i - (int64_t)part * s.stride);
-    const int m = part < s.parts ? min(s.part, s.n - part * s.part) : 0;
-    valid |= slot < min(s.budget, m) ? (1u << e) : 0u;
+    for (int e = 0; e < kKpt; ++e) {
+      const uint32_t u = (uint32_t)e;
+      valid |= (u < b ? slot + u < c0 : u - b < c1) ? (1u << e) : 0u;
+    }
+  } else {
+    uint32_t cq = part_count(s, q);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      valid |= slot < cq ? (1u << e) : 0u;
+      if (++slot == stride) {
+        slot = 0;
+        cq = part_count(s, ++q);
+      }
+    }
   }
 }
 
@@ -791,7 +844,7 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
         hist_add(h, o, valid & (a.cls ? pb : ~pb), a.prefix, a.hi, w, p == 0);
       }
       __syncthreads();
-      pick_digit<kT>(h, 1 << w, a.need, sh, ph);
+      pick_digit(h, 1 << w, a.need, sh);
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
@@ -861,7 +914,7 @@ __device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint3
     hist[b] = v;
   }
   __syncthreads();
-  pick_digit<kT>(hist, nb, need, sh, ph);
+  pick_digit(hist, nb, need, sh);
 }
 
 template <int T, int STAGE>
