@@ -533,18 +533,21 @@ __device__ __forceinline__ void cluster_page_keys(const Params& s, const float* 
   cen[threadIdx.x + 1] = page_centre(s, v, i0);
   if (first || last) cen[first ? 0 : NT + 1] = extra ? page_centre(s, u, ea) : -1;
   __syncthreads();
+  // centre c gathers the tokens [c - r, c + r]: over this thread's 16 tokens,
+  // the bits [lo, hi1) with lo = c - r - i0 and hi1 = c + r + 1 - i0 clamped
+  // to [0, 16]
   const int cc[3] = {cen[threadIdx.x], cen[threadIdx.x + 1], cen[threadIdx.x + 2]};
   const int r = s.r;
   pb = 0;
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e) {
-    const int t = i0 + e;
-    bool pr = false;
-#pragma unroll
-    for (int g = 0; g < 3; ++g) pr |= cc[g] >= 0 && t - cc[g] <= r && cc[g] - t <= r;
-    pb |= pr ? (1u << e) : 0u;
-    o[e] = ord_key(t < s.n ? v[e] : 0.f);
+  for (int g = 0; g < 3; ++g) {
+    const int lo = min(max(cc[g] - r - i0, 0), kKpt);
+    const int hi1 = min(max(cc[g] + r + 1 - i0, 0), kKpt);
+    const uint32_t span = hi1 > lo ? (1u << hi1) - (1u << lo) : 0u;
+    pb |= cc[g] >= 0 ? span : 0u;
   }
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) o[e] = ord_key(i0 + e < s.n ? v[e] : 0.f);
 }
 
 // Keys of this thread's elements i0 + e (i0 = p0 + 16 * tid) of the part
