@@ -62,62 +62,51 @@ __global__ __launch_bounds__(kThreads) void block_mean_kernel(const uint16_t* __
 
 // ------------------------------------------------------------------ block logits
 // logit[h][i][j] = scale * Qb[h][i] . Kb[g][j] for every query block i of the
-// G heads of KV group g and every key block j: a small fp32 GEMM per group,
-// tiled 64 rows (head, query block) x 64 key blocks.  Both tiles are staged
-// in LDS transposed ([d][64], 16-byte aligned rows) from coalesced 16-byte
-// global loads, so each thread reads its 4 rows and 4 columns at a given d with
-// two 16-byte LDS reads and sums its 4 x 4 outputs over d in a fixed order.
+// G heads of KV group g and every key block j: a small fp32 GEMM per group on
+// the matrix cores (v_mfma_f32_32x32x2_f32: fp32 products, fp32 sums).  A
+// workgroup covers 64 rows (head, query block) x 64 key blocks, one 32 x 32
+// block per wave.  Step m of the contraction takes dimension m from the lanes
+// of the first half-wave and m + d/2 from the second, so a lane's operands
+// for consecutive steps are consecutive floats of its row: 16-byte loads
+// straight from global memory (L2-resident block means), no LDS.
 constexpr int kLt = 64;   // tile edge
-constexpr int kLs = 68;   // LDS row stride of the transposed tiles (floats)
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __global__ __launch_bounds__(kThreads) void block_logits_kernel(
     const float* __restrict__ Qb, const float* __restrict__ Kb, int kb_ld, int G, int n_qb,
     int n_kvb, int d_k, float scale, float* __restrict__ logit) {
-  __shared__ __attribute__((aligned(16))) float qs[128][kLs];
-  __shared__ __attribute__((aligned(16))) float ks[128][kLs];
   const int g = blockIdx.y;
-  const int j0 = blockIdx.x * kLt, r0 = blockIdx.z * kLt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rows = G * n_qb;   // row r = (head g*G + r / n_qb, query block r % n_qb)
-  const float* qg = Qb + (int64_t)g * G * n_qb * d_k;   // the group's heads are consecutive
-  const float* kg = Kb + (int64_t)g * kb_ld * d_k;
-  const int qpr = d_k / 4;     // float4 per row
-#pragma unroll 4
-  for (int x = threadIdx.x; x < kLt * qpr; x += kThreads) {
-    const int r = x / qpr, dq = x % qpr;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 q = r0 + r < rows ? *reinterpret_cast<const float4*>(qg + (int64_t)(r0 + r) * d_k + 4 * dq) : zero;
-    const float4 k = j0 + r < n_kvb ? *reinterpret_cast<const float4*>(kg + (int64_t)(j0 + r) * d_k + 4 * dq) : zero;
-    qs[4 * dq][r] = q.x;
-    qs[4 * dq + 1][r] = q.y;
-    qs[4 * dq + 2][r] = q.z;
-    qs[4 * dq + 3][r] = q.w;
-    ks[4 * dq][r] = k.x;
-    ks[4 * dq + 1][r] = k.y;
-    ks[4 * dq + 2][r] = k.z;
-    ks[4 * dq + 3][r] = k.w;
+  const int r0 = blockIdx.z * kLt + 32 * (wave >> 1), j0 = blockIdx.x * kLt + 32 * (wave & 1);
+  const int half = d_k / 2;
+  const int ra = min(r0 + (lane & 31), rows - 1), jb = min(j0 + (lane & 31), n_kvb - 1);
+  const float* qa = Qb + ((int64_t)g * rows + ra) * d_k + half * (lane >> 5);
+  const float* kb = Kb + ((int64_t)g * kb_ld + jb) * d_k + half * (lane >> 5);
+  f32x16_t acc = {};
+  for (int m0 = 0; m0 < half; m0 += 16) {
+    float4 av[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      av[q] = *reinterpret_cast<const float4*>(qa + m0 + 4 * q);
+      bv[q] = *reinterpret_cast<const float4*>(kb + m0 + 4 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q].x, bv[q].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q].y, bv[q].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q].z, bv[q].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q].w, bv[q].w, acc, 0, 0, 0);
+    }
   }
-  __syncthreads();
-  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;   // rows 4tr.., columns 4tc..
-  float acc[4][4] = {};
-  for (int d = 0; d < d_k; ++d) {
-    const float4 a = *reinterpret_cast<const float4*>(&qs[d][4 * tr]);
-    const float4 b = *reinterpret_cast<const float4*>(&ks[d][4 * tc]);
-    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  // accumulator i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+  const int j = j0 + (lane & 31);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = r0 + 4 * tr + u;
-    if (r >= rows) continue;
-    const int h = g * G + r / n_qb, i = r % n_qb;
-    float* out = logit + ((int64_t)h * n_qb + i) * n_kvb;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = j0 + 4 * tc + v;
-      if (j < n_kvb) out[j] = scale * acc[u][v];
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+    if (r < rows && j < n_kvb) {
+      const int h = g * G + r / n_qb, qi = r % n_qb;
+      logit[((int64_t)h * n_qb + qi) * n_kvb + j] = scale * acc[i];
     }
   }
 }

@@ -96,6 +96,9 @@ TOPK_CASES = [
     (1, 16385, 1000, 0, 3, True),        # last part of one element
     (2, 40000, 3000, 2, 5, True),        # five parts, ties across part edges
     (2, 131040, 1025, 0, 0, False),      # one slot too many for small parts: parts of 16384
+    # two values only: the first pass leaves thousands of keys in the threshold bin
+    (1, 16384, 3000, 0, 2, False),       # one part: later passes over the registers
+    (2, 40000, 3000, 2, 2, True),        # small parts and a merge of tied candidates
 ]
 
 
