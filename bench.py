@@ -80,9 +80,9 @@ KERNEL_SOURCES = {
     "mistral128k": ("score.hip",),
     "gemfilter128k": ("score.hip",),
     "specprefill128k": ("score.hip",),
-    "delta32x8k": ("score.hip", "topk.hip"),
+    "delta32x8k": ("score.hip", "topk.hip", "wave_ops.h"),
     "gather128k": ("gather.hip",),
-    "chunksel128k": ("blocks.hip",),
+    "chunksel128k": ("blocks.hip", "wave_ops.h"),
 }
 
 

@@ -15,6 +15,7 @@
 #include <math.h>
 
 #include "kvs_internal.h"
+#include "wave_ops.h"
 
 namespace kvs {
 namespace {
@@ -113,122 +114,193 @@ __global__ __launch_bounds__(kThreads) void block_logits_kernel(
 
 __device__ __forceinline__ uint32_t ord_pos(float p) { return __float_as_uint(p) | 0x80000000u; }
 
+// Probability mass in fixed point, 2^-30 units, summed exactly with 32-bit
+// integer adds: each term is truncated by less than 2^-30, the total stays
+// below 2^31.
+constexpr float kMassOne = 1073741824.0f;
+__device__ __forceinline__ uint32_t mass_of(float p) { return (uint32_t)(p * kMassOne); }
+// The 44-bit order key of block j: probability bits, then 4095 - j (ties go
+// to the lower block index).
+__device__ __forceinline__ uint64_t key44(uint32_t o, int j) {
+  return ((uint64_t)o << 12) | (uint64_t)(4095 - j);
+}
+
+constexpr int kPerThread = kMaxKvb / kThreads;   // key blocks per thread
+constexpr uint32_t kTopFinish = 32;              // crossing bins this small: one wave finishes
+
+struct ToppShared {
+  uint32_t hm[2048];          // mass histogram of one 11-bit digit
+  uint32_t lo[kMaxKvb];       // keys of the crossing bin: probability bits
+  uint16_t lj[kMaxKvb];       //   and block index
+  float red[2][kThreads / 64];
+  uint32_t digit, need, found, n;
+  uint64_t kstar;
+};
+
+// Wave 0 fixes the digit whose bin holds the need-th unit of mass counted
+// from the top of histogram hm (2048 bins): lane l owns 32 bins; a wave
+// prefix sum of their masses finds the owner lane, whose bins are then spread
+// over the lanes for a second one.  found = 0 when the histogram's whole mass
+// is below need.  The caller synchronises.
+__device__ __forceinline__ void topp_pick(ToppShared& sh, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  const int top = 2048 - 32 * lane;   // one past the lane's highest bin
+  const uint4* h4 = reinterpret_cast<const uint4*>(sh.hm + top - 32);
+  uint32_t ls = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 v = h4[k];
+    ls += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t inc = wave_scan<OpAdd>(ls, 0u);
+  const uint64_t own = __ballot(inc - ls < need && need <= inc);
+  if (own == 0) {
+    if (lane == 0) sh.found = 0u;
+    return;
+  }
+  const int L = (int)__builtin_ctzll(own);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(inc - ls), L);
+  const int topL = 2048 - 32 * L;
+  const uint32_t c = lane < 32 ? sh.hm[topL - 1 - lane] : 0u;
+  const uint32_t inc2 = above + wave_scan<OpAdd>(c, 0u);
+  const uint64_t hit = __ballot(lane < 32 && inc2 - c < need && need <= inc2);
+  if (lane == (int)__builtin_ctzll(hit)) {
+    sh.digit = (uint32_t)(topL - 1 - lane);
+    sh.need = need - (inc2 - c);
+    sh.found = 1u;
+  }
+}
+
 // ------------------------------------------------------------------ top-p per (head, query block)
+// One workgroup per (head, query block); thread t holds key blocks t + 256 u.
+// Softmax over the visible blocks with wave and workgroup reductions in a
+// fixed order.  The kept blocks are a prefix of the order (probability desc,
+// j asc): a block is kept while the mass ranked strictly before it is <
+// p_mass, so the prefix ends at the block K* where the running mass first
+// reaches p_mass.  K* is found by a radix select over the 44-bit key with
+// per-digit histograms of mass instead of counts: the first 11-bit digit over
+// all keys, then the keys of the crossing bin are compacted into a list; a
+// short list is finished by one wave (each lane sums the mass of the keys
+// above its own), a long one by three more digits over the list.
 __global__ __launch_bounds__(kThreads) void block_topp_kernel(
     const float* __restrict__ logit, int n_qb, int n_kvb, int block, int Lq,
     int64_t q_pos0, float p_mass, uint8_t* __restrict__ M) {
-  __shared__ uint64_t keys[2048];
-  __shared__ float val[kMaxKvb];
-  __shared__ float red[kThreads];
+  __shared__ __attribute__((aligned(16))) ToppShared sh;
   const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t last_row = min((int64_t)(i + 1) * block, (int64_t)Lq) - 1;
   const int64_t end_pos = q_pos0 + last_row;
-  // 1. logits of the visible blocks
   const float* lr = logit + ((int64_t)h * n_qb + i) * n_kvb;
-  for (int j = tid; j < n_kvb; j += kThreads)
-    val[j] = (int64_t)j * block <= end_pos ? lr[j] : -__builtin_inff();
-  __syncthreads();
+  // 1. logits of the visible blocks and their maximum
+  float v[kPerThread];
+  uint32_t vis = 0;
   float mloc = -__builtin_inff();
-  for (int j = tid; j < n_kvb; j += kThreads) mloc = fmaxf(mloc, val[j]);
-  red[tid] = mloc;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int j = tid + kThreads * u;
+    const bool in = j < n_kvb && (int64_t)j * block <= end_pos;
+    v[u] = in ? lr[j] : -__builtin_inff();
+    vis |= in ? (1u << u) : 0u;
+    mloc = fmaxf(mloc, v[u]);
   }
-  const float mx = red[0];
+  uint4* h4 = reinterpret_cast<uint4*>(sh.hm);
+  for (int b = tid; b < 2048 / 4; b += kThreads) h4[b] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) sh.n = 0u;
+  mloc = __uint_as_float(wave_scan<OpMaxF>(__float_as_uint(mloc), __float_as_uint(-__builtin_inff())));
+  if (lane == 63) sh.red[0][wave] = mloc;
   __syncthreads();
-  // 2. softmax numerators and their sum (fixed tree order)
+  float mx = sh.red[0][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) mx = fmaxf(mx, sh.red[0][w]);
+  // 2. softmax numerators and their sum
   float sloc = 0.f;
-  for (int j = tid; j < n_kvb; j += kThreads) {
-    const float e = val[j] == -__builtin_inff() ? 0.f : expf(val[j] - mx);
-    val[j] = e;
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const float e = ((vis >> u) & 1u) ? expf(v[u] - mx) : 0.f;
+    v[u] = e;
     sloc += e;
   }
-  red[tid] = sloc;
+  sloc = __uint_as_float(wave_scan<OpAddF>(__float_as_uint(sloc), 0u));
+  if (lane == 63) sh.red[1][wave] = sloc;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+  float z = sh.red[1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) z += sh.red[1][w];
+  const float inv_z = 1.0f / z;
+  uint32_t o[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    v[u] *= inv_z;   // probability
+    o[u] = ord_pos(v[u]);
   }
-  const float inv_z = 1.0f / red[0];
+  // 3. first digit: the 11 leading bits of the key (o >> 21), over every key
+  const uint32_t need0 = (uint32_t)((double)p_mass * 1073741824.0);
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u)
+    if ((vis >> u) & 1u) atomicAdd(&sh.hm[o[u] >> 21], mass_of(v[u]));
   __syncthreads();
-  // 3. the kept blocks are a prefix of the order (probability desc, j asc): a
-  // block is kept while the mass ranked strictly before it is < p_mass.  The
-  // prefix ends at the block K* where the running mass first reaches p_mass;
-  // K* is found by a radix select over the 44-bit key (probability bits, then
-  // 4095 - j) with per-digit histograms of mass instead of counts.  Masses are
-  // fixed point (2^-40 units) summed with integer atomics: exact and
-  // independent of the order of the additions.
-  uint64_t* hm = keys;   // 2048-bin mass histogram (the key array's first 16 KiB)
-  const uint64_t need0 = (uint64_t)((double)p_mass * 1099511627776.0);   // 2^40
-  uint64_t prefix = 0, need = need0;
-  bool all = false;      // the whole order stays below p_mass: keep every visible block
-  for (int pass = 0; pass < 4 && !all; ++pass) {
-    const int shift = 33 - 11 * pass;
-    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 11)) & ((1ull << 44) - 1);
-    for (int b = tid; b < 2048; b += kThreads) hm[b] = 0ull;
-    __syncthreads();
-    for (int j = tid; j < n_kvb; j += kThreads) {
-      const float p = val[j] * inv_z;
-      const uint64_t key = ((uint64_t)ord_pos(p) << 12) | (uint64_t)(4095 - j);
-      if ((key & pmask) == prefix)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hm[(key >> shift) & 2047u]),
-                  (unsigned long long)(p * 1099511627776.0f));
-    }
-    __syncthreads();
-    // thread t owns bins [2047 - 8t - 7, 2047 - 8t]: mass above it, then its crossing bin
-    uint64_t c[8], ls = 0;
+  if (wave == 0) topp_pick(sh, need0);
+  __syncthreads();
+  const bool all = sh.found == 0u;   // the whole mass stays below p_mass: keep every visible block
+  uint64_t kstar = 0;
+  if (!all) {
+    const uint32_t d0 = sh.digit;
+    uint32_t need = sh.need;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      c[u] = hm[2047 - 8 * tid - u];
-      ls += c[u];
-    }
-    // exclusive prefix of the per-thread masses over the workgroup (waves, then LDS)
-    const int lane = tid & 63, wave = tid >> 6;
-    uint64_t inc = ls;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t v = __shfl_up(inc, off);
-      if (lane >= off) inc += v;
-    }
-    __shared__ uint64_t wsum[kThreads / 64];
-    __shared__ uint64_t sel_prefix, sel_need;
-    __shared__ int found;
-    if (lane == 63) wsum[wave] = inc;
-    if (tid == 0) found = 0;
-    __syncthreads();
-    uint64_t above = inc - ls;
-    for (int w = 0; w < wave; ++w) above += wsum[w];
-    if (above < need && need <= above + ls) {
-      uint64_t cum = above;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (cum < need && need <= cum + c[u]) {
-          sel_prefix = prefix | ((uint64_t)(2047 - 8 * tid - u) << shift);
-          sel_need = need - cum;
-          found = 1;
-        }
-        cum += c[u];
+    for (int u = 0; u < kPerThread; ++u)
+      if (((vis >> u) & 1u) && (o[u] >> 21) == d0) {
+        const uint32_t at = atomicAdd(&sh.n, 1u);
+        sh.lo[at] = o[u];
+        sh.lj[at] = (uint16_t)(tid + kThreads * u);
       }
-    }
     __syncthreads();
-    if (!found) {
-      all = true;   // the prefix's whole mass is below need
+    const uint32_t n = sh.n;
+    if (n <= kTopFinish) {
+      if (wave == 0) {
+        const bool ok = (uint32_t)lane < n;
+        const uint32_t x = ok ? sh.lo[lane] : 0u;
+        const int jx = ok ? (int)sh.lj[lane] : 0;
+        const uint32_t mxs = mass_of(__uint_as_float(x & 0x7FFFFFFFu));
+        uint32_t above = 0;   // mass of the list keys above this lane's key
+        for (uint32_t y = 0; y < n; ++y) {
+          const uint32_t xy = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)y);
+          const int jy = __builtin_amdgcn_readlane(jx, (int)y);
+          const uint32_t my = (uint32_t)__builtin_amdgcn_readlane((int)mxs, (int)y);
+          above += (xy > x || (xy == x && jy < jx)) ? my : 0u;
+        }
+        const uint64_t hit = __ballot(ok && above < need && need <= above + mxs);
+        if (lane == (int)__builtin_ctzll(hit)) sh.kstar = key44(x, jx);
+      }
+      __syncthreads();
+      kstar = sh.kstar;
     } else {
-      prefix = sel_prefix;
-      need = sel_need;
+      uint64_t prefix = (uint64_t)d0 << 33;
+#pragma unroll 1
+      for (int pass = 1; pass < 4; ++pass) {
+        const int shift = 33 - 11 * pass;
+        for (int b = tid; b < 2048 / 4; b += kThreads) h4[b] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        for (uint32_t idx = tid; idx < n; idx += kThreads) {
+          const uint32_t x = sh.lo[idx];
+          const uint64_t key = key44(x, sh.lj[idx]);
+          if ((key >> (shift + 11)) == (prefix >> (shift + 11)))
+            atomicAdd(&sh.hm[(key >> shift) & 2047u], mass_of(__uint_as_float(x & 0x7FFFFFFFu)));
+        }
+        __syncthreads();
+        if (wave == 0) topp_pick(sh, need);
+        __syncthreads();
+        prefix |= (uint64_t)sh.digit << shift;
+        need = sh.need;
+      }
+      kstar = prefix;
     }
-    __syncthreads();
   }
   // 4. keep the visible blocks at or above K* (every visible block when `all`)
   uint8_t* mrow = M + ((int64_t)h * n_qb + i) * n_kvb;
-  for (int j = tid; j < n_kvb; j += kThreads) {
-    const float p = val[j] * inv_z;
-    const uint64_t key = ((uint64_t)ord_pos(p) << 12) | (uint64_t)(4095 - j);
-    const bool visible = (int64_t)j * block <= end_pos;
-    mrow[j] = (visible && (all || key >= prefix)) ? 1 : 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int j = tid + kThreads * u;
+    if (j < n_kvb) mrow[j] = (((vis >> u) & 1u) && (all || key44(o[u], j) >= kstar)) ? 1 : 0;
   }
 }
 
