@@ -305,59 +305,68 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
 }
 
 // ------------------------------------------------------------------ union
-// One workgroup per subgroup: OR over its heads and query blocks, then an
-// ascending compaction of the set KV blocks into staging.  Thread t owns the
-// 16 KV blocks [16t, 16t + 16) (n_kvb <= 4096): it reads them from every mask
-// row it ORs (one 16-byte load per row when the rows are 16-byte aligned), all
-// rows' loads independent of each other.
+// OR over the heads and query blocks of a (sub)group, then an ascending CSR.
+// union_group_kernel: one workgroup per (segment of kSeg KV blocks, group).
+// Thread t reads 16 blocks (one 16-byte chunk, t % 8) of the rows t / 8,
+// t / 8 + 32, ...; the partial ORs are combined across the lanes of a wave
+// that share a chunk (shuffles), then across the waves in LDS, and wave 0
+// writes the segment's set blocks in ascending order with their count.
+// union_pack_kernel: one workgroup per (segment, group) piece adds up the
+// counts of the pieces before it (groups in order, segments in order) and
+// copies the piece's blocks to its place in the CSR.
+constexpr int kSeg = 128;             // KV blocks per union segment
+constexpr int kSegChunks = kSeg / 16; // 16-byte chunks per segment row
+
 __global__ __launch_bounds__(kThreads) void union_group_kernel(const uint8_t* __restrict__ M,
                                                                int sg, int n_qb, int n_kvb,
                                                                int32_t* __restrict__ staging,
                                                                int32_t* __restrict__ counts) {
-  __shared__ uint32_t wc[kThreads / 64];
-  const int s = blockIdx.x;
+  __shared__ u32x4 part[kThreads / 64][kSegChunks];
+  const int seg = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j0 = 16 * tid;
+  const int c = tid % kSegChunks, rl = tid / kSegChunks;
+  const int j0 = seg * kSeg + 16 * c;   // first KV block of this thread's chunk
   const int nrows = sg * n_qb;
-  const uint8_t* base = M + (int64_t)s * sg * n_qb * n_kvb;
-  uint32_t bits = 0;
+  const uint8_t* base = M + (int64_t)g * nrows * n_kvb;
+  u32x4 acc = {0u, 0u, 0u, 0u};
   if (j0 < n_kvb) {
     if (n_kvb % 16 == 0 && ((uintptr_t)M & 15u) == 0) {
-      u32x4 acc = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-      for (int r = 0; r < nrows; ++r)
+#pragma unroll 4
+      for (int r = rl; r < nrows; r += kThreads / kSegChunks)
         acc |= *reinterpret_cast<const u32x4*>(base + (int64_t)r * n_kvb + j0);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) bits |= ((acc[e / 4] >> (8 * (e % 4))) & 0xffu) ? (1u << e) : 0u;
     } else {
-      for (int r = 0; r < nrows; ++r)
+      for (int r = rl; r < nrows; r += kThreads / kSegChunks)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (j0 + e < n_kvb && base[(int64_t)r * n_kvb + j0 + e]) bits |= 1u << e;
+          if (j0 + e < n_kvb && base[(int64_t)r * n_kvb + j0 + e])
+            acc[e / 4] |= 0xffu << (8 * (e % 4));
     }
   }
-  // exclusive prefix of the per-thread counts: this thread's first output slot
-  uint32_t c = __popc(bits);
-  uint32_t inc = c;
+  // lanes l, l ^ 8, l ^ 16, ... of a wave hold the same chunk
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t u = __shfl_up(inc, off);
-    if (lane >= off) inc += u;
-  }
-  if (lane == 63) wc[wave] = inc;
+  for (int d = kSegChunks; d < 64; d *= 2)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] |= (uint32_t)__shfl_xor((int)acc[q], d);
+  if (lane < kSegChunks) part[wave][lane] = acc;
   __syncthreads();
-  uint32_t before = 0, total = 0;
+  if (wave == 0) {
+    uint32_t bits = 0;
+    if (lane < kSegChunks) {
+      u32x4 o = part[0][lane];
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    before += w < wave ? wc[w] : 0u;
-    total += wc[w];
+      for (int w = 1; w < kThreads / 64; ++w) o |= part[w][lane];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bits |= ((o[e / 4] >> (8 * (e % 4))) & 0xffu) ? (1u << e) : 0u;
+    }
+    const uint32_t cnt = (uint32_t)__popc(bits);
+    const uint32_t inc = wave_scan<OpAdd>(cnt, 0u);
+    uint32_t pos = inc - cnt;
+    int32_t* st = staging + (int64_t)g * n_kvb + seg * kSeg;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((bits >> e) & 1u) st[pos++] = j0 + e;
+    if (lane == 63) counts[(int64_t)g * gridDim.x + seg] = (int32_t)inc;
   }
-  uint32_t pos = before + inc - c;
-  int32_t* st = staging + (int64_t)s * n_kvb;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((bits >> e) & 1u) st[pos++] = j0 + e;
-  if (tid == 0) counts[s] = (int32_t)total;
 }
 
 __global__ __launch_bounds__(kThreads) void union_pack_kernel(const int32_t* __restrict__ staging,
@@ -365,14 +374,25 @@ __global__ __launch_bounds__(kThreads) void union_pack_kernel(const int32_t* __r
                                                               int n_groups, int n_kvb,
                                                               int32_t* __restrict__ indptr,
                                                               int32_t* __restrict__ indices) {
-  int off = 0;
-  for (int s = 0; s < n_groups; ++s) {
-    const int c = counts[s];
-    if (threadIdx.x == 0) indptr[s] = off;
-    for (int x = threadIdx.x; x < c; x += kThreads) indices[off + x] = staging[(int64_t)s * n_kvb + x];
-    off += c;
+  __shared__ uint32_t wsum[kThreads / 64];
+  const int seg = blockIdx.x, g = blockIdx.y, n_seg = gridDim.x;
+  const int64_t piece = (int64_t)g * n_seg + seg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t before = 0;
+  for (int64_t x = tid; x < piece; x += kThreads) before += (uint32_t)counts[x];
+  before = wave_scan<OpAdd>(before, 0u);
+  if (lane == 63) wsum[wave] = before;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) off += wsum[w];
+  const int c = counts[piece];
+  const int32_t* st = staging + (int64_t)g * n_kvb + seg * kSeg;
+  for (int x = tid; x < c; x += kThreads) indices[off + x] = st[x];
+  if (tid == 0) {
+    if (seg == 0) indptr[g] = (int32_t)off;
+    if (g == n_groups - 1 && seg == n_seg - 1) indptr[n_groups] = (int32_t)(off + c);
   }
-  if (threadIdx.x == 0) indptr[n_groups] = off;
 }
 
 }  // namespace
@@ -419,8 +439,9 @@ size_t union_ws_bytes(int H_q, int H_kv, int sub_group, int n_kvb) {
   const int G = H_q / H_kv;
   const int sg = sub_group == 0 ? G : sub_group;
   const int n_groups = H_q / sg;
+  const int n_seg = (n_kvb + kSeg - 1) / kSeg;
   return align_up((size_t)n_groups * n_kvb * sizeof(int32_t), kWsAlign) +
-         align_up((size_t)n_groups * sizeof(int32_t), kWsAlign);
+         align_up((size_t)n_groups * n_seg * sizeof(int32_t), kWsAlign);
 }
 
 kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_qb, int n_kvb,
@@ -431,10 +452,11 @@ kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_q
   int32_t* staging = static_cast<int32_t*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(
       static_cast<char*>(ws) + align_up((size_t)n_groups * n_kvb * sizeof(int32_t), kWsAlign));
-  hipLaunchKernelGGL(union_group_kernel, dim3(n_groups), dim3(kThreads), 0, stream, M, sg, n_qb,
-                     n_kvb, staging, counts);
-  hipLaunchKernelGGL(union_pack_kernel, dim3(1), dim3(kThreads), 0, stream, staging, counts,
-                     n_groups, n_kvb, indptr, indices);
+  const int n_seg = (n_kvb + kSeg - 1) / kSeg;
+  hipLaunchKernelGGL(union_group_kernel, dim3(n_seg, n_groups), dim3(kThreads), 0, stream, M, sg,
+                     n_qb, n_kvb, staging, counts);
+  hipLaunchKernelGGL(union_pack_kernel, dim3(n_seg, n_groups), dim3(kThreads), 0, stream, staging,
+                     counts, n_groups, n_kvb, indptr, indices);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
