@@ -13,19 +13,30 @@
 namespace kvs {
 namespace {
 
-constexpr int kChunk = 2048;   // tokens per workgroup (multiple of every page size used)
+constexpr int kChunk = 2048;   // most tokens per workgroup (the LDS stage)
+constexpr int kChunkTarget = 512;   // tokens per workgroup when pages allow: many workgroups
 constexpr int kThreads = 256;
 constexpr int kMaxHalo = 64;   // pool_k <= 129
 constexpr float kNegInf = -__builtin_inff();
 
 // Row h' of the head-reduced input at token t (caller guarantees 0 <= t < n).
+// The heads are loaded kHeadBatch at a time, all loads of a batch in flight
+// together, and combined in head order.
+constexpr int kHeadBatch = 16;
 __device__ __forceinline__ float reduced(const float* S, int H, int64_t ld, int head_reduce,
                                          int row, int t) {
   if (head_reduce == KVS_RED_NONE) return S[(int64_t)row * ld + t];
-  float v = S[t];
-  for (int h = 1; h < H; ++h) {
-    const float x = S[(int64_t)h * ld + t];
-    v = head_reduce == KVS_RED_MAX ? fmaxf(v, x) : v + x;
+  float v = 0.f;
+  for (int h0 = 0; h0 < H; h0 += kHeadBatch) {
+    float x[kHeadBatch];
+#pragma unroll
+    for (int k = 0; k < kHeadBatch; ++k)
+      x[k] = h0 + k < H ? S[(int64_t)(h0 + k) * ld + t] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kHeadBatch; ++k) {
+      if (h0 + k >= H) break;
+      v = h0 + k == 0 ? x[k] : head_reduce == KVS_RED_MAX ? fmaxf(v, x[k]) : v + x[k];
+    }
   }
   return head_reduce == KVS_RED_MEAN ? v / (float)H : v;
 }
@@ -171,9 +182,10 @@ kvs_status pool_pages_run(const float* S, int H, int n, int64_t ld, int head_red
                           int pool_k, int P, int page_reduce, float* pooled, float* page,
                           int32_t* page_arg, hipStream_t stream) {
   const int rows = head_reduce == KVS_RED_NONE ? H : 1;
-  int chunk = kChunk;
-  if (P > 0) chunk = kChunk / P * P;  // page-aligned chunks
-  if (chunk <= 0) return KVS_EUNSUPPORTED;
+  // page-aligned chunks of about kChunkTarget tokens (a whole page when pages are longer)
+  int chunk = kChunkTarget;
+  if (P > 0) chunk = P <= kChunkTarget ? kChunkTarget / P * P : P;
+  if (chunk <= 0 || chunk > kChunk) return KVS_EUNSUPPORTED;
   dim3 grid((n + chunk - 1) / chunk, rows);
   hipLaunchKernelGGL(pool_pages_kernel, grid, dim3(kThreads), 0, stream, S, H, n, ld, head_reduce,
                      pool, pool_k, P, page_reduce, chunk, pooled, page, page_arg);
