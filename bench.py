@@ -763,7 +763,7 @@ def bench_chunksel(args):
     stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
     out = {
         "metric": "KV tokens covered/sec (chunked-prefill block selection, last chunk at L=128K); "
-                  "% of fp32 vector roofline",
+                  "% of fp32 matrix roofline",
         "value": ch.L / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -779,8 +779,8 @@ def bench_chunksel(args):
                                "block 64, top-p 0.9, cached means of 2032 earlier blocks -> union page "
                                "table", "L": ch.L, "Lq": ch.Lq, "block": blk, "n_cached_blocks": n_cached},
         "roofline": {
-            "kernel": "kvs_block_select_cached (block_mean_kernel x2 + block_topp_kernel)",
-            "bound": "alu",
+            "kernel": "kvs_block_select_cached (block means of the chunk and its new key blocks, block_logits_kernel on fp32 MFMA, block_topp_kernel)",
+            "bound": "mfma",
             "achieved": achieved,
             "peak": 157.3,
             "unit": "TFLOP/s",
