@@ -99,6 +99,7 @@ TOPK_CASES = [
     # two values only: the first pass leaves thousands of keys in the threshold bin
     (1, 16384, 3000, 0, 2, False),       # one part: later passes over the registers
     (2, 40000, 3000, 2, 2, True),        # small parts and a merge of tied candidates
+    (100, 20000, 500, 0, 3, True),       # many rows: workgroup i takes row i % 100
 ]
 
 
@@ -294,6 +295,7 @@ SELECT_CLUSTER_CASES = [
     (3, 16388, 500, 0, 16, 2.0, 3, 1.0),        # second part of four elements
     (2, 16390, 500, 0, 16, 2.0, 3, 1.0),        # n % 4 != 0: staged path
     (2, 60000, 20000, 4, 16, 2.0, 3, 1.0),      # across all parts
+    (3, 70000, 1024, 4, 16, 1.0, 16, 1.0),      # parts of 8192: centres reach across part edges
 ]
 
 
