@@ -844,44 +844,79 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
 
 // ------------------------------------------------------------------ wide rows
 // Rows whose candidates would not fit one workgroup (parts * min(budget,
-// kCap) > kCap, e.g. a 20% keep rate of a 128K-token row) run the radix
-// select across all parts of the row instead: five launches, each one
-// workgroup per (part, row) of kCap elements, with no workgroup ever waiting
-// for another.  The key is the 33-bit (class, value) and the digits are fixed:
-// bits 32-21, 20-10 and 9-0.  Every launch recomputes its part's keys.
-// Launch P (0 < P <= 3) first fixes digit P-1 from the sum over parts of that
-// pass's per-part histograms and the state (prefix, need) the previous launch
-// left; every workgroup of the row reaches the same digit, and part 0 records
-// the new state for the next launch.  Launches 0-2 then write their part's
-// histogram of pass P; launch 3, which has fixed K* and the number of
-// K*-equal elements to take, writes the part's counts of keys above and equal
-// to K*.  Launch 4 gives each part its output offset and its share of the
-// K*-equal elements (in part order, so ties still go to the lower index) and
-// writes the chosen indices.
+// kCap) > kCap, e.g. a 20% keep rate of a 128K-token row) run the selection
+// across all parts of the row instead: six launches, each one workgroup per
+// (part, row) of kCap elements, with no workgroup ever waiting for another.
+//  launch 0  computes the part's keys (the transform runs once), stores them
+//            and the part's class statistics;
+//  launch 1  combines every part's statistics into the row's (the class of
+//            K*, the budget left in it, the value bits still open: the same
+//            start as the in-register selection), and part 0 records that
+//            state; every part then writes its histogram of the first digit;
+//  launch 2, 3  fix the previous digit from the sum over parts of that
+//            digit's per-part histograms, record the new state (part 0) and
+//            write the next digit's histogram;
+//  launch 4  fixes the last digit, which settles K* and the number of
+//            K*-equal elements to take, and writes the part's counts of keys
+//            above and equal to K*;
+//  launch 5  gives each part its output offset and its share of the K*-equal
+//            elements (in part order, so ties still go to the lower index)
+//            and writes the chosen indices.
+// Every workgroup of a row reaches the same digits.  Workspace: per (row,
+// part) statistics, counts and three histograms; per row four states and the
+// stored keys (value bits and priority bits).
 constexpr int kWideMaxParts = 16;
-constexpr int kCnt = 4096 + 2048 + 1024;       // per part: the three histograms, then (gt, eq)
-constexpr int kState = kCnt + 2;               // part 0 only: state after pass p at kState + 4p
-constexpr int kWideWords = kState + 12;        // per (row, part)
-__device__ __forceinline__ constexpr int wide_shift(int p) { return p == 0 ? 21 : p == 1 ? 10 : 0; }
+constexpr int kWStat = 8;                         // per part: class stats (5), counts (2), pad
+constexpr int kPartWords = kWStat + kHistWords;   // then the three digit histograms
+constexpr int kRowState = 16;                     // per row: four states of (cls, prefix, need, hi)
 
-__device__ __forceinline__ uint64_t key33(const uint32_t (&o)[kKpt], uint32_t pb, int e) {
-  return ((uint64_t)((pb >> e) & 1u) << 32) | o[e];
+__device__ __forceinline__ uint32_t* wide_part(const Params& s, int row, int part) {
+  return s.wide + ((int64_t)row * s.parts + part) * kPartWords;
+}
+__device__ __forceinline__ uint32_t* wide_state(const Params& s, int row) {
+  return s.wide + (int64_t)gridDim.y * s.parts * kPartWords + (int64_t)row * kRowState;
+}
+__device__ __forceinline__ uint32_t* wide_keys(const Params& s, int row) {
+  return s.wide + (int64_t)gridDim.y * (s.parts * kPartWords + kRowState) +
+         (int64_t)row * s.parts * kCap;
+}
+__device__ __forceinline__ uint16_t* wide_prio(const Params& s, int row) {
+  uint32_t* end = s.wide + (int64_t)gridDim.y * (s.parts * kPartWords + kRowState + s.parts * kCap);
+  return reinterpret_cast<uint16_t*>(end) + (int64_t)row * s.parts * kT;
 }
 
-__device__ __forceinline__ uint32_t* wide_of(const Params& s, int row, int part) {
-  return s.wide + ((int64_t)row * s.parts + part) * kWideWords;
+template <int T>
+__global__ __launch_bounds__(kT) void topk_wide_keys_kernel(Params s) {
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LdsWords<T, kT>::value];
+  __shared__ int cen[T == kCluster ? kT + 2 : 1];
+  __shared__ Shared sh;
+  const int row = blockIdx.y, part = blockIdx.x;
+  const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
+  uint32_t o[kKpt], pb, valid;
+  part_keys<T, kT>(s, row, p0, p1, smem, cen, o, pb, valid);
+  const int i0 = p0 + (int)threadIdx.x * kKpt;
+  uint4* k4 = reinterpret_cast<uint4*>(wide_keys(s, row) + i0);
+#pragma unroll
+  for (int q = 0; q < kKpt / 4; ++q) k4[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  wide_prio(s, row)[i0 / kKpt] = (uint16_t)(pb & valid);
+  uint32_t st[5];
+  class_stats<kT>(o, pb, valid, sh, st);
+  if (threadIdx.x == 0) {
+    uint32_t* w = wide_part(s, row, part);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) w[j] = st[j];
+  }
 }
 
-// The digit of pass p from the per-part histograms of the row, given the need
-// before it.  Leaves (digit, need) in sh.
-__device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint32_t need,
-                                          uint32_t* hist, Shared& sh, int& ph) {
-  const int nb = 1 << pass_width(p);
+// The sum over parts of the per-part histograms of pass p (nb bins) into
+// LDS, then the digit holding the need-th key.  Leaves (digit, need) in sh.
+__device__ __forceinline__ void wide_pick(const Params& s, int row, int p, int nb, uint32_t need,
+                                          uint32_t* hist, Shared& sh) {
   for (int b = threadIdx.x; b < nb; b += kT) {
     uint32_t c[kWideMaxParts];
 #pragma unroll
     for (int q = 0; q < kWideMaxParts; ++q)
-      c[q] = q < s.parts ? wide_of(s, row, q)[pass_offset(p) + b] : 0u;
+      c[q] = q < s.parts ? wide_part(s, row, q)[kWStat + pass_offset(p) + b] : 0u;
     uint32_t v = 0;
 #pragma unroll
     for (int q = 0; q < kWideMaxParts; ++q) v += c[q];
@@ -891,78 +926,102 @@ __device__ __forceinline__ void wide_pick(const Params& s, int row, int p, uint3
   pick_digit(hist, nb, need, sh);
 }
 
-template <int T, int STAGE>
+template <int STAGE>
 __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
-  __shared__ __attribute__((aligned(16))) uint32_t smem[LdsWords<T, kT>::value];
-  __shared__ int cen[T == kCluster ? kT + 2 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kHistWords];
   __shared__ Shared sh;
   const int row = blockIdx.y, part = blockIdx.x;
   const int p0 = part * kCap, p1 = min(p0 + kCap, s.n);
-  uint32_t o[kKpt], pb, valid;
-  part_keys<T, kT>(s, row, p0, p1, smem, cen, o, pb, valid);
-  uint32_t* mine = wide_of(s, row, part);
-  uint32_t* state = wide_of(s, row, 0) + kState;
-  int ph = 0;
-  // the state before this launch's digit, then the digit itself
-  uint64_t prefix = 0;
-  uint32_t need = (uint32_t)s.budget;
-  if constexpr (STAGE >= 2) {
-    const uint32_t* st = state + 4 * (STAGE - 2);
-    prefix = ((uint64_t)st[1] << 32) | st[0];
-    need = st[2];
-  }
-  if constexpr (STAGE >= 1 && STAGE <= 3) {
-    wide_pick(s, row, STAGE - 1, need, smem, sh, ph);
-    prefix |= (uint64_t)sh.digit << wide_shift(STAGE - 1);
-    need = sh.need;
-    if (part == 0 && threadIdx.x == 0) {
-      uint32_t* st = state + 4 * (STAGE - 1);
-      st[0] = (uint32_t)prefix;
-      st[1] = (uint32_t)(prefix >> 32);
-      st[2] = need;
-    }
-  }
-  if constexpr (STAGE < 3) {
-    uint32_t* h = smem;
-    constexpr int nb = 1 << pass_width(STAGE);
-    constexpr int shift = wide_shift(STAGE);
-    constexpr int above = shift + pass_width(STAGE);   // bits above the digit are fixed
-    for (int b = threadIdx.x; b < nb; b += kT) h[b] = 0u;
-    __syncthreads();
+  const int i0 = p0 + (int)threadIdx.x * kKpt;
+  // the stored keys
+  uint32_t o[kKpt], valid = 0;
+  const uint4* k4 = reinterpret_cast<const uint4*>(wide_keys(s, row) + i0);
 #pragma unroll
-    for (int e = 0; e < kKpt; ++e) {
-      const uint64_t k = key33(o, pb, e);
-      if (((valid >> e) & 1u) && (STAGE == 0 || (k >> above) == (prefix >> above)))
-        atomicAdd(&h[(uint32_t)(k >> shift) & (uint32_t)(nb - 1)], 1u);
+  for (int q = 0; q < kKpt / 4; ++q) {
+    const uint4 v = k4[q];
+    o[4 * q] = v.x;
+    o[4 * q + 1] = v.y;
+    o[4 * q + 2] = v.z;
+    o[4 * q + 3] = v.w;
+  }
+  const uint32_t pb = wide_prio(s, row)[i0 / kKpt];
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) valid |= (i0 + e < p1) ? (1u << e) : 0u;
+  uint32_t* state = wide_state(s, row);
+  SelectStart a;
+  if constexpr (STAGE == 1) {
+    uint32_t st[5] = {0u, ~0u, 0u, ~0u, 0u};
+    for (int q = 0; q < s.parts; ++q) {
+      const uint32_t* w = wide_part(s, row, q);
+      st[0] += w[0];
+      st[1] = min(st[1], w[1]);
+      st[2] = max(st[2], w[2]);
+      st[3] = min(st[3], w[3]);
+      st[4] = max(st[4], w[4]);
     }
-    __syncthreads();
-    for (int b = threadIdx.x; b < nb; b += kT) mine[pass_offset(STAGE) + b] = h[b];
+    a = select_start(st, (uint32_t)s.budget);
   } else {
-    const Kstar ks{(uint32_t)(prefix >> 32), (uint32_t)prefix, need};
+    const uint32_t* st = state + 4 * (STAGE - 2);
+    a.cls = st[0];
+    a.prefix = st[1];
+    a.need = st[2];
+    a.hi = (int)st[3];
+    if (STAGE <= 4 && a.hi > 0) {
+      const int w = min(a.hi, pass_width(STAGE - 2));
+      wide_pick(s, row, STAGE - 2, 1 << w, a.need, smem, sh);
+      a.hi -= w;
+      a.prefix |= sh.digit << a.hi;
+      a.need = sh.need;
+    }
+  }
+  if (STAGE <= 4 && part == 0 && threadIdx.x == 0) {
+    uint32_t* st = state + 4 * (STAGE - 1);
+    st[0] = a.cls;
+    st[1] = a.prefix;
+    st[2] = a.need;
+    st[3] = (uint32_t)a.hi;
+  }
+  if constexpr (STAGE <= 3) {
+    if (a.hi > 0) {
+      const int p = STAGE - 1;
+      const int w = min(a.hi, pass_width(p));
+      const int nb = 1 << w;
+      uint32_t* h = smem;
+      __syncthreads();   // the pick's LDS sums are read
+      for (int b = threadIdx.x; b < nb; b += kT) h[b] = 0u;
+      __syncthreads();
+      hist_add(h, o, valid & (a.cls ? pb : ~pb), a.prefix, a.hi, w, STAGE == 1);
+      __syncthreads();
+      uint32_t* mine = wide_part(s, row, part) + kWStat + pass_offset(p);
+      for (int b = threadIdx.x; b < nb; b += kT) mine[b] = h[b];
+    }
+  } else {
+    const Kstar ks{a.cls, a.prefix, a.need};
     uint32_t gt, eq;
     classify(o, pb, valid, ks, gt, eq);
-    if constexpr (STAGE == 3) {
+    int ph = 0;
+    uint32_t* mine = wide_part(s, row, part);
+    if constexpr (STAGE == 4) {
       uint32_t total;
       block_scan<kT>(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq), sh, ph, total);
       if (threadIdx.x == 0) {
-        mine[kCnt] = total >> 16;
-        mine[kCnt + 1] = total & 0xFFFFu;
+        mine[5] = total >> 16;
+        mine[6] = total & 0xFFFFu;
       }
     } else {
       // offset of this part's output and its share of the K*-equal elements
       uint32_t gt_before = 0, eq_before = 0;
       for (int q = 0; q < part; ++q) {
-        gt_before += wide_of(s, row, q)[kCnt];
-        eq_before += wide_of(s, row, q)[kCnt + 1];
+        gt_before += wide_part(s, row, q)[5];
+        eq_before += wide_part(s, row, q)[6];
       }
       uint32_t pos, rank, tg, te;
-      place<kT>(gt, eq, need, gt_before, eq_before, sh, ph, pos, rank, tg, te);
+      place<kT>(gt, eq, ks.need_eq, gt_before, eq_before, sh, ph, pos, rank, tg, te);
       int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
-      const int i0 = p0 + (int)threadIdx.x * kKpt;
 #pragma unroll
       for (int e = 0; e < kKpt; ++e) {
         const bool q = (eq >> e) & 1u;
-        if (((gt >> e) & 1u) || (q && rank < need)) {
+        if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) {
           if (pos < (uint32_t)s.budget) out[pos] = i0 + e;   // the counts make pos < budget
           ++pos;
         }
@@ -1062,19 +1121,23 @@ void launch(const Params& s, int H, hipStream_t stream) {
 template <int T>
 void launch_wide(const Params& s, int H, hipStream_t stream) {
   const dim3 grid(s.parts, H);
-  hipLaunchKernelGGL((topk_wide_kernel<T, 0>), grid, dim3(kT), 0, stream, s);
-  hipLaunchKernelGGL((topk_wide_kernel<T, 1>), grid, dim3(kT), 0, stream, s);
-  hipLaunchKernelGGL((topk_wide_kernel<T, 2>), grid, dim3(kT), 0, stream, s);
-  hipLaunchKernelGGL((topk_wide_kernel<T, 3>), grid, dim3(kT), 0, stream, s);
-  hipLaunchKernelGGL((topk_wide_kernel<T, 4>), grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_keys_kernel<T>, grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_kernel<1>, grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_kernel<2>, grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_kernel<3>, grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_kernel<4>, grid, dim3(kT), 0, stream, s);
+  hipLaunchKernelGGL(topk_wide_kernel<5>, grid, dim3(kT), 0, stream, s);
 }
 
 }  // namespace
 
 size_t topk_ws_bytes(int H, int n, int budget) {
   if (budget <= 0 || n <= kCap) return 0;
-  if (wide_path(n, budget))
-    return align_up((size_t)H * ceil_div(n, kCap) * kWideWords * sizeof(uint32_t), kWsAlign);
+  if (wide_path(n, budget)) {
+    const size_t parts = (size_t)ceil_div(n, kCap);
+    const size_t words = parts * kPartWords + kRowState + parts * kCap + parts * kT / 2;
+    return align_up((size_t)H * words * sizeof(uint32_t), kWsAlign);
+  }
   return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
 }
 
