@@ -146,15 +146,16 @@ def cpu_baseline(ly, theta, r, budget, n_forced, P, min_seconds=10.0, max_reps=8
                       f"{sec:.2f} s each; score + page max + cluster priority + top-k in float64 NumPy"}
 
 
-def profile_commands(workload="mistral128k"):
+def profile_commands(workload="mistral128k", out="profile_out"):
+    """The rocprofv3 runs a workload's summaries come from, writing under `out`."""
     wl = "" if workload == "mistral128k" else f" --workload {workload}"
     d = "" if workload == "mistral128k" else f"_{workload}"
     base = "python3 bench.py --no-cpu-baseline --copy-calibration" + wl
     return {
-        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace{d} -o bench -- {base}",
-        "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE{d} -o bench -- "
+        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d {out}/trace{d} -o bench -- {base}",
+        "FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_FETCH_SIZE{d} -o bench -- "
                       f"{base} --steps 10 --warmup 2",
-        "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE{d} -o bench -- "
+        "WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_WRITE_SIZE{d} -o bench -- "
                       f"{base} --steps 10 --warmup 2",
     }
 
@@ -185,7 +186,7 @@ def summarize_profiles(out_dir, workload="mistral128k"):
     import statistics as st
 
     stats_name, traffic_name, frag, label = WORKLOADS[workload]
-    cmds = profile_commands(workload)
+    cmds = profile_commands(workload, os.path.normpath(out_dir))
     d = "" if workload == "mistral128k" else f"_{workload}"
 
     def short(name):
@@ -195,7 +196,7 @@ def summarize_profiles(out_dir, workload="mistral128k"):
 
     stats = list(csv.DictReader(open(os.path.join(out_dir, f"trace{d}", "bench_kernel_stats.csv"))))
     lines = [f"# Kernel durations, {WORKLOAD_TITLES[workload]} (bench.py workload)", "",
-             "Command (repo root on the GPU box, cd /tmp first):", "",
+             "Command (from the repository root, with rocprofv3 started in /tmp):", "",
              "    " + cmds["trace"], "",
              "Calls cover the warm-up steps, the timed steps and the event-timed steps.", "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -235,7 +236,7 @@ def summarize_profiles(out_dir, workload="mistral128k"):
         f"# HBM traffic of {label}, {WORKLOAD_TITLES[workload]}",
         "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, medians), each scaled by the same counter's",
         "# reading for a plain 256 MiB device copy (torch copy_) in the same run.",
-        "# Commands (repo root on the GPU box, cd /tmp first):",
+        "# Commands (from the repository root, with rocprofv3 started in /tmp):",
         "#   " + cmds["FETCH_SIZE"],
         "#   " + cmds["WRITE_SIZE"],
         f"# source_sha256_16 covers {', '.join(sorted(KERNEL_SOURCES[workload] + ('kvs_internal.h',)))}",

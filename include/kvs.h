@@ -13,8 +13,8 @@
  *
  * Errors: argument problems are detected on the host and reported BEFORE
  * anything is enqueued.  KVS_EINVAL: a null pointer, a size out of range, a
- * misaligned pointer or stride.  KVS_EUNSUPPORTED: a valid shape this build
- * has no kernel for.  KVS_EWORKSPACE: ws_bytes below the query's answer.
+ * misaligned pointer or stride.  KVS_EUNSUPPORTED: a valid shape the
+ * kernels do not cover.  KVS_EWORKSPACE: ws_bytes below the query's answer.
  * KVS_EHIP: a kernel launch failed.  Faults inside kernels surface at the
  * caller's next synchronization.  No C++ exception crosses this boundary.
  *

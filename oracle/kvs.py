@@ -32,7 +32,7 @@ Sources (web pages on the subject; cited by title and section):
   post-softmax attention; page score = sum over the page's tokens; recency
   pages forced); "Key design 3" (page size P = 16).
 
-Readings where the pages are silent or garbled (all restated in the design doc):
+Readings where the pages are silent or garbled:
 contiguous GQA grouping h -> h // G; causal visibility t <= q_pos0 + j inside the
 window (the garbled ``max(W, M_win)`` read as an additive -inf mask); scores over
 all L keys; GROUP_MAX sums a head's W rows before the max over heads; pooling

@@ -84,7 +84,7 @@ const char* kvs_status_string(kvs_status s) {
   switch (s) {
     case KVS_OK: return "KVS_OK";
     case KVS_EINVAL: return "KVS_EINVAL: invalid argument";
-    case KVS_EUNSUPPORTED: return "KVS_EUNSUPPORTED: shape not supported by this build";
+    case KVS_EUNSUPPORTED: return "KVS_EUNSUPPORTED: a valid shape outside what the kernels cover";
     case KVS_EWORKSPACE: return "KVS_EWORKSPACE: workspace too small";
     case KVS_EHIP: return "KVS_EHIP: kernel launch failed";
     default: return "KVS: unknown status";

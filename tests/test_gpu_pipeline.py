@@ -37,7 +37,7 @@ def _oscore(ly):
 
 @pytest.mark.parametrize("which,budget", [("tiny", 64), ("llama32k", 1024)])
 def test_window_maxpool_topk(kvs, which, budget):
-    """Configs 1-2: score -> max-pool 7 over the prefix -> top-budget + window."""
+    """Tiny layer and Llama 32K layer: score -> max-pool 7 over the prefix -> top-budget + window."""
     print(f"pipeline {which}", flush=True)
     ly = synth.tiny() if which == "tiny" else synth.llama_layer()
     n = ly.L - ly.W
@@ -76,7 +76,7 @@ def _robust_priority(So_pref, P, theta, r):
 
 
 def test_cluster_topk_128k(kvs):
-    """Config 3: score -> page max P=16 -> clusters (theta 2e-3, r 3) -> top-1024 + window."""
+    """Mistral 128K layer: score -> page max P=16 -> clusters (theta 2e-3, r 3) -> top-1024 + window."""
     ly = synth.mistral_layer()
     n, P, theta, r, budget = ly.L - ly.W, 16, 2e-3, 3, 1024
     S = _score(kvs, ly)
@@ -117,7 +117,7 @@ def test_cluster_topk_128k(kvs):
 
 
 def test_cross_layer_l1_sum(kvs):
-    """Config 4: 32 layers x 16K, per-layer L1-normalised sums, top 20% of all tokens."""
+    """32 layers x 16K: per-layer L1-normalised sums, top 20% of all tokens."""
     layers, L = 32, 16384
     budget = int(0.2 * L)
     acc = torch.empty(L, dtype=torch.float32, device="cuda")
@@ -138,7 +138,7 @@ def test_cross_layer_l1_sum(kvs):
 
 
 def test_chunk_block_union(kvs):
-    """Config 5: block select (64, top-p 0.9) -> Q-block union -> group union -> CSR."""
+    """Chunked prefill at 128K: block select (64, top-p 0.9) -> Q-block union -> group union -> CSR."""
     ch = synth.chunk_select()
     a = kvs.block_select_args(Lq=ch.Lq, L=ch.L, d_k=ch.d_k, H_q=ch.H_q, H_kv=ch.H_kv,
                               q_pos0=ch.q_pos0, block=ch.block, p_mass=0.9)
