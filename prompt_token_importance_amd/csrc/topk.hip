@@ -1033,10 +1033,11 @@ __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
 }
 
 // ------------------------------------------------------------------ DELTA page sets
-// One workgroup per sequence: rho = the top K - L older pages by page score
-// (ascending), then the last min(L, pages) pages, then -1.  [DELTA] key design
-// 2; pages per sequence <= kCap.
-__global__ __launch_bounds__(kT) void topk_delta_kernel(DeltaLaunch p) {
+// One workgroup per sequence (one wave when the pages fit 16 per lane): rho =
+// the top K - L older pages by page score (ascending), then the last min(L,
+// pages) pages, then -1.  [DELTA] key design 2; pages per sequence <= kCap.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_delta_kernel(DeltaLaunch p) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWords];
   __shared__ Shared sh;
   const int b = blockIdx.x;
@@ -1061,18 +1062,18 @@ __global__ __launch_bounds__(kT) void topk_delta_kernel(DeltaLaunch p) {
   if (keep == 0) {
     gt = 0u;
   } else if (keep < n_cand) {
-    ks = select_regs<kT>(o, 0u, valid, (uint32_t)keep, hist, sh, ph);
+    ks = select_regs<NT>(o, 0u, valid, (uint32_t)keep, hist, sh, ph);
     classify(o, 0u, valid, ks, gt, eq);
   }
   uint32_t pos, rank, tg, te;
-  place<kT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
+  place<NT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
     const bool q = (eq >> e) & 1u;
     if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = i0 + e;
     rank += q;
   }
-  for (int i = threadIdx.x; i < p.K_pages - keep; i += kT)
+  for (int i = threadIdx.x; i < p.K_pages - keep; i += NT)
     out[keep + i] = i < n_recent ? n_cand + i : -1;
 }
 
@@ -1143,7 +1144,11 @@ size_t topk_ws_bytes(int H, int n, int budget) {
 
 kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream) {
   if (p.n_pages_max > kCap) return KVS_EUNSUPPORTED;
-  hipLaunchKernelGGL(topk_delta_kernel, dim3(p.B), dim3(kT), 0, stream, p);
+  // one wave per sequence while its pages fit 16 per lane: no barrier waits on other waves
+  if (p.n_pages_max <= 64 * kKpt)
+    hipLaunchKernelGGL(topk_delta_kernel<64>, dim3(p.B), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(topk_delta_kernel<kT>, dim3(p.B), dim3(kT), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
