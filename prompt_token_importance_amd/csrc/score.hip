@@ -1669,41 +1669,52 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
 }
 
 // delta_page_kernel: one workgroup per (chunk of kDeltaPageTokens tokens,
-// sequence).  It folds the sequence's per-chunk statistics into b_h = m_h +
-// log2 Z_h per head, forms s_t = max over heads of exp2(x_t,h - b_h) for its
-// tokens (a thread per token, coalesced over the head-major logits, the heads'
-// loads issued in batches), and sums each page's tokens left to right.
+// sequence), a thread per token.  The thread first issues the loads of its
+// token's logits for the first kDeltaBatch heads (coalesced over the
+// head-major logits), then folds the sequence's per-chunk statistics into b_h
+// = m_h + log2 Z_h per head while they are in flight, forms s_t = max over
+// heads of exp2(x_t,h - b_h), and sums each page's tokens left to right.
 constexpr int kDeltaPageTokens = 512;
-constexpr int kDeltaBatch = 16;
+constexpr int kDeltaBatch = 32;
 
-__global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs a) {
+  constexpr int NTH = kDeltaPageTokens;   // threads
   __shared__ float bh[128];
   __shared__ float ys[kDeltaPageTokens];
-  __shared__ float2 part[256];
+  __shared__ float2 part[NTH];
   const DeltaLaunch& p = a.p;
   const int b = blockIdx.y;
   const int Lb = min(max(p.L[b], 0), p.L_max);
   const int t_begin = blockIdx.x * kDeltaPageTokens;
   if (t_begin >= Lb) return;
   const int t_end = min(t_begin + kDeltaPageTokens, Lb);
+  const int t = t_begin + (int)threadIdx.x;
+  const bool has_t = t < t_end;
+  const float* x2b = p.x2 + (int64_t)b * p.H_q * p.x2_ld;
+  // 0. this token's logits of the first heads, in flight during step 1
+  float v[kDeltaBatch];
+#pragma unroll
+  for (int q = 0; q < kDeltaBatch; ++q)
+    v[q] = has_t && q < p.H_q ? x2b[(int64_t)q * p.x2_ld + t] : kNegInf;
   // 1. row constants: threads per head fold a strided share of the chunks
-  const int tph = 256 / p.H_q;                  // threads per head (H_q <= 128)
+  const int tph = NTH / p.H_q;                  // threads per head (H_q <= 128)
   const int h = threadIdx.x / tph, j = threadIdx.x % tph;
   const int nch = (Lb + p.chunk - 1) / p.chunk;
   float mm = kNegInf, zz = 0.f;
   if (h < p.H_q) {
     const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q + h;
-    for (int c0 = j; c0 < nch; c0 += kDeltaBatch * tph) {
-      float2 v[kDeltaBatch];
+    constexpr int kCsBatch = 16;
+    for (int c0 = j; c0 < nch; c0 += kCsBatch * tph) {
+      float2 w[kCsBatch];
 #pragma unroll
-      for (int q = 0; q < kDeltaBatch; ++q) {
+      for (int q = 0; q < kCsBatch; ++q) {
         const int c = c0 + q * tph;
-        v[q] = c < nch ? cs[(int64_t)c * p.H_q] : make_float2(kNegInf, 0.f);
+        w[q] = c < nch ? cs[(int64_t)c * p.H_q] : make_float2(kNegInf, 0.f);
       }
 #pragma unroll
-      for (int q = 0; q < kDeltaBatch; ++q) {
-        const float mx = fmaxf(mm, v[q].x);
-        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + v[q].y * ex2(v[q].x - mx);
+      for (int q = 0; q < kCsBatch; ++q) {
+        const float mx = fmaxf(mm, w[q].x);
+        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + w[q].y * ex2(w[q].x - mx);
         mm = mx;
       }
     }
@@ -1713,37 +1724,36 @@ __global__ __launch_bounds__(256) void delta_page_kernel(DeltaArgs a) {
   if (threadIdx.x < p.H_q) {
     float m2 = kNegInf, z2 = 0.f;
     for (int q = 0; q < tph; ++q) {
-      const float2 v = part[threadIdx.x * tph + q];
-      const float mx = fmaxf(m2, v.x);
-      z2 = mx == kNegInf ? 0.f : z2 * ex2(m2 - mx) + v.y * ex2(v.x - mx);
+      const float2 w = part[threadIdx.x * tph + q];
+      const float mx = fmaxf(m2, w.x);
+      z2 = mx == kNegInf ? 0.f : z2 * ex2(m2 - mx) + w.y * ex2(w.x - mx);
       m2 = mx;
     }
     bh[threadIdx.x] = m2 + log2f(z2);
   }
   __syncthreads();
-  // 2. token scores: max over heads of the softmax probability
-  const float* x2b = p.x2 + (int64_t)b * p.H_q * p.x2_ld;
-  for (int t = t_begin + (int)threadIdx.x; t < t_end; t += 256) {
-    float sv = 0.f;
-    for (int h0 = 0; h0 < p.H_q; h0 += kDeltaBatch) {
-      float v[kDeltaBatch];
+  // 2. token score: max over heads of the softmax probability
+  float sv = 0.f;
 #pragma unroll
-      for (int q = 0; q < kDeltaBatch; ++q)
-        v[q] = h0 + q < p.H_q ? x2b[(int64_t)(h0 + q) * p.x2_ld + t] : kNegInf;
+  for (int q = 0; q < kDeltaBatch; ++q)
+    if (q < p.H_q) sv = fmaxf(sv, ex2(v[q] - bh[q]));
+  for (int h0 = kDeltaBatch; h0 < p.H_q; h0 += kDeltaBatch) {
 #pragma unroll
-      for (int q = 0; q < kDeltaBatch; ++q)
-        if (h0 + q < p.H_q) sv = fmaxf(sv, ex2(v[q] - bh[h0 + q]));
-    }
-    ys[t - t_begin] = sv;
+    for (int q = 0; q < kDeltaBatch; ++q)
+      v[q] = has_t && h0 + q < p.H_q ? x2b[(int64_t)(h0 + q) * p.x2_ld + t] : kNegInf;
+#pragma unroll
+    for (int q = 0; q < kDeltaBatch; ++q)
+      if (h0 + q < p.H_q) sv = fmaxf(sv, ex2(v[q] - bh[h0 + q]));
   }
+  if (has_t) ys[t - t_begin] = sv;
   __syncthreads();
   // 3. page sums, left to right (chunk boundaries are multiples of P)
   const int u0 = t_begin / p.P, u1 = (t_end + p.P - 1) / p.P;
   float* Sb = p.S + (int64_t)b * p.n_pages_max;
-  for (int u = u0 + (int)threadIdx.x; u < u1; u += 256) {
+  for (int u = u0 + (int)threadIdx.x; u < u1; u += NTH) {
     const int a0 = u * p.P, a1 = min(a0 + p.P, t_end);
     float acc = 0.f;
-    for (int t = a0; t < a1; ++t) acc += ys[t - t_begin];
+    for (int tt = a0; tt < a1; ++tt) acc += ys[tt - t_begin];
     Sb[u] = acc;
   }
 }
@@ -1753,7 +1763,7 @@ kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream) {
   DeltaArgs a{p};
   hipLaunchKernelGGL((delta_logits_kernel<D, NT>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
   const int n_page_wg = (p.L_max + kDeltaPageTokens - 1) / kDeltaPageTokens;
-  hipLaunchKernelGGL(delta_page_kernel, dim3(n_page_wg, p.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(delta_page_kernel, dim3(n_page_wg, p.B), dim3(kDeltaPageTokens), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
