@@ -275,7 +275,10 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
  * Workspace: kvs_topk_workspace bytes (0 when n <= 16384: rows that short
  * finish in one kernel), 16-byte aligned, owned by the caller, contents
  * undefined on entry and on return.  It holds the per-part candidates of the
- * two-stage select; calls that share one must not overlap in time.
+ * two-stage select or, for rows whose candidates would not fit one merge
+ * (more than 16384 of them: a large budget over several parts of 16384), the
+ * rows' ranking keys with per-part histograms and counts; calls that share one
+ * must not overlap in time.
  * ---------------------------------------------------------------------- */
 size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget);
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
@@ -287,7 +290,8 @@ kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t bu
  *
  * The same selection as kvs_topk (order, ties, forced suffix, ascending
  * output, workspace contract), ranked on a transform of the scores that is
- * computed on the fly and never stored:
+ * computed on the fly (kept only in the workspace, for rows that take the
+ * multi-part path):
  *  pool = KVS_RED_MAX / KVS_RED_MEAN: value = max / mean of S over
  *    [t - r, t + r] clipped to [0, n), r = (pool_k - 1) / 2 ([CLAA] oracle
  *    construction: 1-D pooling of the token scores, kernel 7, before top-k).
