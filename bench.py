@@ -104,10 +104,9 @@ def source_hash(workload=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
-    """HBM bytes per launch of the roofline kernel from a committed counter
-    summary, or None when the summary is missing or was taken on another
-    source of that kernel."""
+def traffic_summary(path=TRAFFIC_SUMMARY, workload="mistral128k"):
+    """The key: value lines of a committed counter summary, or None when the
+    summary is missing or was taken on another source of its kernel."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -117,8 +116,25 @@ def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
             kv[k.strip()] = v.strip()
     if kv.get("source_sha256_16") != source_hash(workload):
         return None
+    return kv
+
+
+def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
+    """HBM bytes per launch of the roofline kernel, or None (see traffic_summary)."""
+    kv = traffic_summary(path, workload)
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv["traffic_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_stats_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per launch of the score statistics pass from the same counter
+    runs (scaled like the roofline kernel's), or None."""
+    kv = traffic_summary(path, "mistral128k")
+    try:
+        return (float(kv["stats_fetch_kib"]) * float(kv["fetch_scale"]) +
+                float(kv["stats_write_kib"]) * float(kv["write_scale"])) * 1024 if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -946,6 +962,7 @@ def main():
         return sum(ev[a].elapsed_time(ev[a + 1]) for ev in evs) / args.steps
 
     pass1, pass2, select = part(0), part(1), part(2)
+    step_us = sorted(ev[0].elapsed_time(ev[3]) * 1e3 for ev in evs)
 
     def timed(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -968,6 +985,8 @@ def main():
     alg_bytes = k_bytes + q_bytes + s_bytes
     dom_ms = pass2
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    t2, t1 = measured_traffic(), measured_stats_traffic()
+    passes_gbs = (t1 + t2) / ((pass1 + pass2) * 1e-3) / 1e9 if (t1 and t2) else None
     flops = 2.0 * H_q * W * L * d_k
     out = {
         "metric": "prompt tokens scored/sec at L=128K, 8B GQA shape; % of HBM roofline",
@@ -977,6 +996,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "event_step_us_p50_p90": [step_us[len(step_us) // 2], step_us[min(len(step_us) - 1, (9 * len(step_us)) // 10)]],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1003,6 +1023,9 @@ def main():
             "event_us": {"score_pass1_stats_and_merge": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
                          "page_cluster_topk": select * 1e3},
             "copy_256MiB_GBs": copy_gbs,
+            # both score passes from the counter runs: their bytes over their time
+            "score_passes_counter_GBs": passes_gbs,
+            "score_passes_counter_frac": passes_gbs / HBM_PEAK_GBS if passes_gbs else None,
         },
     }
     if not args.no_cpu_baseline:
