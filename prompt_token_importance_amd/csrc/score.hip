@@ -1568,19 +1568,22 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
   // the row tiles holding KV head g's query heads
   const auto t_lo = [&](int g) { return (g * p.G) / 32; };
   const auto t_hi = [&](int g) { return (g * p.G + p.G - 1) / 32; };
-  // With one row tile (H_q <= 32) the next step's K and Q fragments are read
-  // while this step's MFMAs run; with more, only the K fragments are.
+  // With one row tile (H_q <= 32) the query fragments stay in registers for
+  // the whole loop; with more, each step reads those of the row tiles it
+  // needs.  The next step's K fragments are read while this step's MFMAs run.
   constexpr bool PQ = NT == 1;
-  const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&qc)[KS], u32x4(&kn)[KS], u32x4(&qn)[KS]) {
+  u32x4 qf[KS];
+  const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&kn)[KS]) {
     const int g = s % H;
     if (s + S - 1 < steps) issue_k(s + S - 1);
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
       if (T < t_lo(g) || T > t_hi(g)) continue;
       if constexpr (!PQ) {
-        read_frags<KS>(qc, q0 + T * TB, foff);
-        wait_lgkm<KS>(qc);
+        read_frags<KS>(qf, q0 + T * TB, foff);
+        wait_lgkm<KS>(qf);
       }
+      const u32x4(&qc)[KS] = qf;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int k = 0; k < KS; ++k)
@@ -1595,7 +1598,6 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
       else
         wait_vm<0>();
       read_frags<KS>(kn, lds_addr(ring[wave][(s + 1) % S]), foff);
-      if constexpr (PQ) read_frags<KS>(qn, q0, foff);
     }
     if (g == H - 1) {
       // every head's logit of key t is in: store it and fold it into the statistics
@@ -1615,12 +1617,9 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
           }
         }
     }
-    if (s + 1 < steps) {
-      wait_lgkm<KS>(kn);
-      if constexpr (PQ) wait_lgkm<KS>(qn);
-    }
+    if (s + 1 < steps) wait_lgkm<KS>(kn);
   };
-  u32x4 k0[KS], k1[KS], qa[KS], qb[KS];
+  u32x4 k0[KS], k1[KS];
   if (steps > 0) {
     if (pre == 2)
       wait_vm<KS>();
@@ -1629,16 +1628,16 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
     read_frags<KS>(k0, lds_addr(ring[wave][0]), foff);
     wait_lgkm<KS>(k0);
     if constexpr (PQ) {
-      read_frags<KS>(qa, q0, foff);
-      wait_lgkm<KS>(qa);
+      read_frags<KS>(qf, q0, foff);
+      wait_lgkm<KS>(qf);
     }
   }
   int s = 0;
   for (; s + 1 < steps; s += 2) {
-    step(s, k0, qa, k1, qb);
-    step(s + 1, k1, qb, k0, qa);
+    step(s, k0, k1);
+    step(s + 1, k1, k0);
   }
-  if (s < steps) step(s, k0, qa, k1, qb);
+  if (s < steps) step(s, k0, k1);
   // statistics of each row over the workgroup's keys: lanes of a half, then waves
 #pragma unroll
   for (int T = 0; T < NT; ++T)
