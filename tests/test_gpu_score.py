@@ -107,7 +107,8 @@ def test_identical_keys_closed_form(kvs):
 @pytest.mark.slow
 @pytest.mark.parametrize("which", ["llama32k", "mistral128k"])
 def test_full_size_parity(kvs, which):
-    """BASELINE shapes, all heads, every column (the oracle takes a few seconds)."""
+    """Full layer shapes (Llama-3.1-8B at 32K, Mistral-7B at 128K), all heads, every column
+    (the oracle takes a few seconds)."""
     print(f"full-size {which}", flush=True)
     ly = synth.llama_layer() if which == "llama32k" else synth.mistral_layer()
     got = _run(kvs, ly, 1)

@@ -3,7 +3,7 @@
 Integer outputs (top-k indices, page argmax, cluster priority, block-union page
 tables) must equal the oracle's exactly; float outputs (pooled values, page
 sums, layer aggregates) agree within float32 rounding of the same sums.  Inputs
-include forced ties, +-0, NaN, ragged sizes and the full BASELINE sizes.
+include forced ties, +-0, NaN, ragged sizes and the full 32K and 128K layer sizes.
 """
 import json
 import os
