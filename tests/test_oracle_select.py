@@ -162,6 +162,26 @@ def test_block_select_uniform_blocks(V):
     np.testing.assert_array_equal(np.nonzero(M[0, 0])[0], np.arange(want))
 
 
+@pytest.mark.parametrize("q_lo,q_hi,want", [(1.5, 2.5, [1, 1]), (2.0, 3.0, [1, 0])])
+def test_block_select_mass_closed_form(q_lo, q_hi, want):
+    """Two visible key blocks with block-mean logits x and 0: the first holds e^x / (e^x + 1)
+    of the softmax mass, and the second is kept iff that is below 0.9.  Query rows alternate
+    q_lo, q_hi (mean x/8 on axis 0), key block 0 alternates 7, 9 (mean 8), block 1 is zero, and
+    scale = 1/sqrt(64), so x = 2.0 (mass 0.881: keep both) or x = 2.5 (mass 0.924: keep one).
+    Block sums instead of means, a missing scale, or the last query row instead of the mean
+    block query all flip the first case; a base-2 softmax flips the second."""
+    d_k, blk, L, Lq = 64, 4, 8, 4
+    Kf = np.zeros((1, L, d_k), dtype=np.float32)
+    Kf[0, 0:4, 0] = [7.0, 9.0, 7.0, 9.0]
+    Qf = np.zeros((1, Lq, d_k), dtype=np.float32)
+    Qf[0, :, 0] = [q_lo, q_hi, q_lo, q_hi]
+    Q, K = _chunk(Qf, Kf)
+    x = 0.125 * 8.0 * (q_lo + q_hi) / 2
+    assert (math.exp(x) / (math.exp(x) + 1) < 0.9) == (want == [1, 1])
+    M = oracle.block_select(Q, K, Lq=Lq, L=L, d_k=d_k, H_q=1, H_kv=1, q_pos0=L - Lq, block=blk)
+    np.testing.assert_array_equal(M[0, 0], want)
+
+
 def test_block_select_causal_visibility():
     """Query block i sees KV blocks j with first token <= its last position."""
     d_k, blk, L, Lq = 64, 4, 24, 8
