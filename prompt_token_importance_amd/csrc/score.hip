@@ -275,9 +275,9 @@ __device__ __forceinline__ void issue_q_rows(uint8_t* stage, const KArgs& a, int
   }
 }
 
-// Every wave's AGPR copy of all query fragments (the only form the asm MFMAs
-// read them in), from the rows staged by issue_q_rows: N-tile T sits at
-// base + T * stride.  Returns once the reads have landed.
+// Every wave's AGPR copy of all query fragments, from the rows staged by
+// issue_q_rows: N-tile T sits at base + T * stride.  Returns once the reads
+// have landed.
 template <int D, int NT>
 __device__ __forceinline__ void read_q_agpr(bf16x8 (&q)[NT][D / 16], uint32_t base,
                                             uint32_t stride, const uint32_t (&off)[D / 16]) {
@@ -320,24 +320,20 @@ __device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const uint8_t* st
 __device__ __forceinline__ int key_of(int i, int hl) { return 8 * (i >> 2) + 4 * hl + (i & 3); }
 
 
-// MFMA through inline asm with the query fragment (B operand) read straight
-// from AGPRs: the 128 query-fragment registers of a wave live in the AGPR
-// file, leaving the VGPRs to the accumulators and the softmax work.  The
-// compiler inserts no hazard wait states around inline asm, and its register
-// copies (v_accvgpr_write, v_mov) may write an operand right before the MFMA;
-// a VALU write followed by an MFMA read of the same register needs two wait
-// states, so every asm MFMA carries its own "s_nop 1".
+// The tile MFMAs are compiler builtins.  The query fragments (B operand) are
+// read into AGPRs and stay there, leaving the VGPRs to the accumulators and
+// the softmax work; the K fragments land in AGPRs too, and the compiler takes
+// either operand from whichever file holds it.  Where its register copies
+// (v_accvgpr_read/write) write an operand just before an MFMA, the compiler
+// places the wait states itself, so only those MFMAs wait (an inline-asm MFMA
+// would need an unconditional wait before it: the compiler checks no hazards
+// into inline asm).
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kf), "a"(qa));
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qa, acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mfma_zero(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(kf), "a"(qa));
-}
-__device__ __forceinline__ void mfma_acc_a(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(kf), "a"(qa));
-}
-__device__ __forceinline__ void mfma_zero_a(f32x16& acc, const u32x4& kf, const bf16x8& qa) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "a"(kf), "a"(qa));
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qa, f32x16{}, 0, 0,
+                                               0);
 }
 // Wait states between an MFMA writing VGPRs and VALU instructions reading
 // them (the compiler does not track dependencies through inline asm).
@@ -392,9 +388,9 @@ __device__ __forceinline__ void mfma_all_a(f32x16 (&acc)[NT], const u32x4 (&f)[D
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
       if (s == 0)
-        mfma_zero_a(acc[T], f[s], q[T][s]);
+        mfma_zero(acc[T], f[s], q[T][s]);
       else
-        mfma_acc_a(acc[T], f[s], q[T][s]);
+        mfma_acc(acc[T], f[s], q[T][s]);
     }
 }
 
@@ -586,9 +582,9 @@ __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT]
   for (int k = 0; k < M; ++k) {
     const int s = k / NT, T = k % NT;
     if (s == 0)
-      mfma_zero_a(accC[T], fc[s], q[T][s]);
+      mfma_zero(accC[T], fc[s], q[T][s]);
     else
-      mfma_acc_a(accC[T], fc[s], q[T][s]);
+      mfma_acc(accC[T], fc[s], q[T][s]);
 #pragma unroll
     for (int u = 0; u < EPM; ++u) {
       const int e = k * EPM + u;
