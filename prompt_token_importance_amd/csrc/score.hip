@@ -335,34 +335,6 @@ __device__ __forceinline__ void mfma_zero(f32x16& acc, const u32x4& kf, const bf
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qa, f32x16{}, 0, 0,
                                                0);
 }
-// Wait states between an MFMA writing VGPRs and VALU instructions reading
-// them (the compiler does not track dependencies through inline asm).
-__device__ __forceinline__ void mfma_result_guard() {
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-}
-// The same wait states, naming the accumulators they protect, so no read of
-// them can be scheduled above the wait.
-template <int N>
-__device__ __forceinline__ void mfma_guard(f32x16 (&acc)[N]) {
-  static_assert(N >= 1 && N <= 4, "one to four accumulators");
-  if constexpr (N == 1)
-    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0])::"memory");
-  else if constexpr (N == 2)
-    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0]), "+v"(acc[1])::"memory");
-  else if constexpr (N == 3)
-    asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])::"memory");
-  else
-    asm volatile("s_nop 15\n\ts_nop 15"
-                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])::"memory");
-}
-// x * c + nb as an inline-asm FMA: it reads the MFMA result register in
-// place, after the preceding wait states (volatile asm keeps program order),
-// and pins the logit's exp/sum work to its MFMA slot.
-__device__ __forceinline__ float fma_after_guard(float x, float c, float nb) {
-  float y;
-  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(y) : "v"(x), "s"(c), "v"(nb));
-  return y;
-}
 
 template <int D, int NT, int LO, int N>
 __device__ __forceinline__ void mfma_part(f32x16 (&acc)[N > 0 ? N : 1], const u32x4 (&f)[D / 16],
@@ -558,9 +530,9 @@ struct StepSlots {
 // One step of the full-tile pipeline: the KS*NT MFMAs of the current tile
 // (fragments fc) into accC, k-major so consecutive MFMAs use different
 // accumulators, interleaved EPM logits per MFMA with WORK(T, i, x) on the
-// previous tile's logits accP (x = accP[T][i]; WORK reads it with
-// fma_after_guard, so the read stays behind the result guard).  ISSUE: the loads of tile `issue_t0` into `issue_stage`
-// are spread over the first slots.  NEXT: the next tile is waited for (WAITN
+// previous tile's logits accP (x = accP[T][i]; the compiler places the wait
+// states between the MFMA that wrote it and this read).  ISSUE: the loads of
+// the tile at `issue_base` into `issue_stage` are spread over the first slots.  NEXT: the next tile is waited for (WAITN
 // loads may stay outstanding) and its fragments are read into fn.
 template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work, typename Side>
 __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT],
@@ -574,10 +546,6 @@ __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT]
   constexpr int M = KS * NT;
   constexpr int EPM = 16 / KS;
   using SL = StepSlots<M, KS>;
-  // accP's last MFMAs may still be in flight: the wait states come first, and
-  // every read of accP below is pinned after this asm (volatile asm keeps
-  // program order)
-  mfma_result_guard();
 #pragma unroll
   for (int k = 0; k < M; ++k) {
     const int s = k / NT, T = k % NT;
@@ -694,7 +662,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
       wait_lgkm_a<KS>(f1);
     }
     // the running max: exact max of the wave's first tile, per lane and row
-    mfma_guard<NT>(acc0);
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
       float mx = acc0[T][0];
@@ -724,9 +691,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
                           u32x4(&fn)[KS], int j) {
       const auto work = [&](int T, int i, float x) {
         if (i & 1)
-          sb[T] += ex2(fma_after_guard(x, c, nm[T]));
+          sb[T] += ex2(fmaf(x, c, nm[T]));
         else
-          sa[T] += ex2(fma_after_guard(x, c, nm[T]));
+          sa[T] += ex2(fmaf(x, c, nm[T]));
       };
       const uint32_t nxt = ring0 + ((j + 1) & (S - 1)) * tile_bytes<D>();
       if (j + S - 1 < nf)
@@ -749,7 +716,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     if (j < nf) step(acc1, acc0, f1, f0, j);
     // the last full tile's sums
     const auto tail = [&](f32x16(&accP)[NT]) {
-      mfma_guard<NT>(accP);
 #pragma unroll
       for (int T = 0; T < NT; ++T)
 #pragma unroll
@@ -779,7 +745,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
         read_frags_a<KS>(f0, ring0, foff);
         wait_lgkm_a<KS>(f0);
         mfma_all_a<D, NT>(acc0, f0, q);
-        mfma_guard<NT>(acc0);
         stats_part<NT, 0, NT>(acc0, m, z, c, true, 0, hl, vis);
       }
     }
@@ -793,7 +758,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     read_frags<KS>(f, ring0, foff);
     wait_lgkm<KS>(f);
     mfma_part<D, NT, 0, NT>(acc, f, q);
-    mfma_guard<NT>(acc);
     stats_part<NT, 0, NT>(acc, m, z, c, false, tile_t0(j), hl, vis);
   }
 
@@ -1020,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 #pragma unroll
         for (int i2 = 0; i2 < 16; ++i2) pc[i2] = 0.f;
         const auto work = [&](int T, int i2, float v) {
-          pc[i2] += ex2(fma_after_guard(v, c, nb[T]));
+          pc[i2] += ex2(fmaf(v, c, nb[T]));
         };
         const auto side = [&](int kk, int M) {
           if constexpr (FL) {
@@ -1070,7 +1034,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           flush(partA, t0_of(nf - 2));
       }
       const auto tail = [&](f32x16(&accP)[NT]) {
-        mfma_guard<NT>(accP);
         probs_full<NT, 0, NT, false>(accP, partA, b, c);
         flush(partA, t0_of(nf - 1));
       };
@@ -1089,7 +1052,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       read_frags<KS>(f, ring0, foff);
       wait_lgkm<KS>(f);
       mfma_part<D, NT, 0, NT>(acc, f, q);
-      mfma_guard<NT>(acc);
       probs_part<NT, 0, NT, false>(acc, part, b, c, false, t0, hl, vis);
       flush(part, t0);
     }
