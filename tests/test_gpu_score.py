@@ -48,6 +48,8 @@ CASES = [
     ("w64", 900, 64, 64, 4, 2, 0),
     ("one_key", 1, 1, 64, 2, 1, 0),
     ("short", 20, 20, 128, 4, 1, 0),            # window is the whole prompt
+    ("g3_w32", 2500, 32, 128, 6, 2, 0),         # 96 padded rows: three row tiles
+    ("g6_w16_64", 1200, 16, 64, 12, 2, 0),      # 96 padded rows at d_k = 64
 ]
 
 
