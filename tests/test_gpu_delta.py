@@ -82,6 +82,8 @@ CASES = [
     ([2048, 4096], 64, 8, 128, 16, 64, 8),                          # two row tiles
     ([1500], 32, 1, 64, 8, 20, 3),                                  # one KV head, P = 8
     ([777, 1234], 16, 16, 128, 32, 10, 0),                          # MHA, no recent pages
+    ([900, 2049], 96, 8, 64, 16, 8, 2),                             # three row tiles, G = 12
+    ([1500, 700], 128, 8, 128, 16, 16, 4),                          # four row tiles, G = 16
 ]
 
 
