@@ -119,3 +119,25 @@ def test_full_size_parity(kvs, which):
     R = ly.W * ly.G
     assert_scores_close(got, want, R, ly.L, which)
     assert_mass(got, R)
+
+
+@pytest.mark.parametrize("which", ["ragged", pytest.param("mistral128k", marks=pytest.mark.slow)])
+def test_phase_split_matches_one_call(kvs, which):
+    """phase 1 (row statistics into ws) then phase 2 (column sums from that ws), as the bench
+    times the 128K layer, equals a single phase-0 call bit for bit."""
+    print(f"phase split {which}", flush=True)
+    if which == "ragged":
+        ly = synth.gaussian_layer(4113, L=4113, W=32, d_k=128, H_q=32, H_kv=8)
+    else:
+        ly = synth.mistral_layer()
+    Q = kvs.bf16_from_bits(ly.Q)
+    K = kvs.bf16_from_bits(ly.K)
+    shape = dict(L=ly.L, W=ly.W, d_k=ly.d_k, H_q=ly.H_q, H_kv=ly.H_kv, q_pos0=ly.q_pos0)
+    one = kvs.kvs_score(Q, K, kvs.score_args(**shape))
+    ws = torch.empty(kvs.kvs_score_workspace(kvs.score_args(**shape)), dtype=torch.uint8,
+                     device="cuda")
+    S = torch.full_like(one, float("nan"))
+    kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=1), S=S, ws=ws)
+    kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=2), S=S, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32), S.view(torch.int32))
