@@ -184,6 +184,31 @@ def gaussian_layer(seed: int, L: int, W: int, d_k: int, H_q: int, H_kv: int,
     return Layer(Q=Q, K=K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0, spans=spans)
 
 
+def plant_outliers(ly: Layer, seed: int, outliers, a: float = 16.0) -> Layer:
+    """Plant outlier keys: a few logits far above every other logit of some rows.
+
+    ``outliers`` lists ``(g, head_slot, t, lift)``: query head ``g * G +
+    head_slot``'s window rows get ``+a * u`` and key ``t`` of KV head ``g`` gets
+    ``+(lift * sqrt(d_k) / a) * u``, with ``u`` a unit direction drawn for that
+    (g, head_slot) pair, so the planted logit ``q . k / sqrt(d_k)`` sits about
+    ``lift`` above the row's ordinary logits (attention sinks and outlier keys of
+    real models).  The rows of one head share one direction, whatever lifts its
+    outliers carry; each row is lifted once.  Returns a new Layer; ``ly`` is
+    unchanged.
+    """
+    G = ly.H_q // ly.H_kv
+    q = bf16_to_f32(ly.Q).astype(np.float64)
+    k = bf16_to_f32(ly.K).astype(np.float64)
+    lifted = set()
+    for (g, hs, t, lift) in outliers:
+        u = unit_direction(seed, 1000 + g * G + hs, ly.d_k)
+        if (g, hs) not in lifted:
+            q[g * G + hs] += a * u
+            lifted.add((g, hs))
+        k[g, t] += (lift * math.sqrt(ly.d_k) / a) * u
+    return dataclasses.replace(ly, Q=to_bf16(q.astype(np.float32)), K=to_bf16(k.astype(np.float32)))
+
+
 def tiny(seed: int = 0) -> Layer:
     """1 layer, H_q=4, H_kv=1, d_k=64, L=512, W=16, N(0,1) bf16."""
     return gaussian_layer(seed, L=512, W=16, d_k=64, H_q=4, H_kv=1)
