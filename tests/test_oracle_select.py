@@ -65,6 +65,27 @@ def test_head_reduce_then_pool_then_page_order():
     np.testing.assert_array_equal(arg, [[1, 6]])
 
 
+def test_head_reduce_hand_worked():
+    """Head reduction over the rows, worked by hand: SUM (the per-layer score summed
+    over all heads, CLAA "Three design decisions"), MEAN (the mean over lookahead
+    queries, CLAA Speculative Prefill) and MAX ([DELTA] key design 2).  Summing
+    along the token axis, or keeping one row, fails every line."""
+    x = np.array([[1.0, 2.0, -3.0, 0.5],
+                  [4.0, -1.0, 3.0, 0.25],
+                  [0.0, 0.0, 1.0, 0.25]])
+    np.testing.assert_array_equal(oracle.head_reduce(x, oracle.RED_SUM), [[5.0, 1.0, 1.0, 1.0]])
+    np.testing.assert_array_equal(oracle.head_reduce(x, oracle.RED_MAX), [[4.0, 2.0, 3.0, 0.5]])
+    np.testing.assert_allclose(oracle.head_reduce(x, oracle.RED_MEAN),
+                               [[5.0 / 3, 1.0 / 3, 1.0 / 3, 1.0 / 3]], rtol=1e-15)
+    np.testing.assert_array_equal(oracle.head_reduce(x, oracle.RED_NONE), x)
+    # SUM over heads, then max-pool 3 ([5, 5, 1, 1]), then page sums with P = 2
+    y, z, arg = oracle.pool_pages(x, head_mode=oracle.RED_SUM, pool_mode=oracle.RED_MAX, pool_k=3,
+                                  P=2, page_mode=oracle.RED_SUM)
+    np.testing.assert_array_equal(y, [[5.0, 5.0, 1.0, 1.0]])
+    np.testing.assert_array_equal(z, [[10.0, 2.0]])
+    np.testing.assert_array_equal(arg, [[0, 2]])
+
+
 # ---------------------------------------------------------------- layers
 def test_aggregate_identical_layers():
     s = synth.score_array(3, 4, 64)
