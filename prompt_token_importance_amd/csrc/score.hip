@@ -1338,11 +1338,6 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 }  // namespace
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
@@ -1353,21 +1348,15 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->head_rows = hr;
   pl->rows_pad = (G * hr + 31) / 32 * 32;
   pl->n_tiles = (a->L + 31) / 32;
-  // KV heads per round: a round's K is re-read by pass 2 soon after pass 1
-  // streamed it, so a round sized below the 256 MB Infinity Cache can serve
-  // the second read from the cache.  Tunable for measurement.
-  const int64_t head_bytes = (int64_t)a->L * a->d_k * 2;
-  int batch = env_int("KVS_SCORE_HEAD_BATCH", 0);
-  if (batch <= 0) batch = a->H_kv;
-  (void)head_bytes;
-  batch = batch < a->H_kv ? batch : a->H_kv;
-  pl->head_batch = batch;
-  pl->reverse = env_int("KVS_SCORE_REVERSE", 1) != 0;
-  // Splits of the key range: one 4-wave workgroup per CU (256 CUs), each
-  // streaming a contiguous run of tiles, and at least 4 tiles (one per wave).
-  const int target_wg = env_int("KVS_SCORE_TARGET_WG", 256);
-  int per_head = (target_wg + batch - 1) / batch;
-  int max_split = pl->n_tiles / 4 > 1 ? pl->n_tiles / 4 : 1;
+  // Every KV head in one round (one pass-1 launch, one pass-2 launch).  The
+  // key range of each head is cut into splits so that the grid holds one
+  // 4-wave workgroup per CU (256 CUs), each streaming a contiguous run of
+  // tiles, and at least 4 tiles (one per wave).  The plan depends only on the
+  // shape, so the workspace, phase 1 and phase 2 always agree on it.
+  pl->head_batch = a->H_kv;
+  pl->reverse = 1;
+  const int per_head = (256 + a->H_kv - 1) / a->H_kv;
+  const int max_split = pl->n_tiles / 4 > 1 ? pl->n_tiles / 4 : 1;
   int ns = per_head < max_split ? per_head : max_split;
   if (ns < 1) ns = 1;
   const int tps = (pl->n_tiles + ns - 1) / ns;
