@@ -338,7 +338,7 @@ def bench_raw(args):
         else:
             st |= lib.kvs_pool_pages(pS, W, L, L, kvs.RED_MEAN, kvs.RED_MEAN, 7, 0, kvs.RED_SUM, pP,
                                      None, None, sp)
-            st |= lib.kvs_topk(pP, 1, L, L, budget, None, 0, pI, pW, ws_bytes, sp)
+            st |= lib.kvs_topk(pP, 1, L, L, budget, None, 0, pI, None, pW, ws_bytes, sp)
         if ev is not None:
             ev[2].record(stream)
         if st != 0:

@@ -270,6 +270,10 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
  * chosen indices in ascending order (original positions preserved), followed
  * by n, n+1, ..., n + n_forced - 1 ([ClusterAttn] window appended; [DELTA]
  * recency pages).  The result is unique for a given input.
+ * val, when not NULL, float32 [H][budget + n_forced] (contiguous) receives the
+ * kept scores in the order of idx: val[h][e] = S[h][idx[h][e]] for e < budget
+ * (a bit copy, [CLAA] topk returns the values with the indices) and NaN for
+ * the forced suffix, whose positions lie outside the candidate range.
  * 0 <= budget <= n, H <= 65535.
  *
  * Workspace: kvs_topk_workspace bytes (0 when n <= 16384: rows that short
@@ -282,7 +286,7 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
  * ---------------------------------------------------------------------- */
 size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget);
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
-                    const uint8_t* priority, int32_t n_forced, int32_t* idx,
+                    const uint8_t* priority, int32_t n_forced, int32_t* idx, float* val,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

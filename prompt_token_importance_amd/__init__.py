@@ -100,7 +100,7 @@ def _load():
         "kvs_delta_pages": (I32, [ctypes.POINTER(DeltaArgs), P, P, P, P, P, P, SZ, P]),
         "kvs_pool_pages": (I32, [P, I32, I32, I64, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvs_topk_workspace": (SZ, [I32, I32, I32]),
-        "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, SZ, P]),
+        "kvs_topk": (I32, [P, I32, I32, I64, I32, P, I32, P, P, P, SZ, P]),
         "kvs_select_workspace": (SZ, [I32, I32, I32]),
         "kvs_select": (I32, [P, I32, I32, I64, ctypes.POINTER(SelectArgs), P, P, SZ, P]),
         "kvs_block_union_workspace": (SZ, [I32, I32, I32, I32]),
@@ -283,16 +283,23 @@ def kvs_pool_pages(S: torch.Tensor, n: int, *, head_reduce=RED_NONE, pool=RED_NO
 # --------------------------------------------------------------------------- top-k
 def kvs_topk(S: torch.Tensor, n: int, budget: int, *, priority: Optional[torch.Tensor] = None,
              n_forced: int = 0, ld: Optional[int] = None, idx: Optional[torch.Tensor] = None,
-             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """int32 [H][budget + n_forced]: chosen indices ascending, then n .. n + n_forced - 1."""
+             val: Optional[torch.Tensor] = None, want_val: bool = False,
+             ws: Optional[torch.Tensor] = None, stream=None):
+    """int32 [H][budget + n_forced]: chosen indices ascending, then n .. n + n_forced - 1.
+
+    With ``want_val`` (or a ``val`` tensor) also returns the kept scores, float32
+    [H][budget + n_forced] in the order of the indices (NaN for the forced suffix):
+    ``(idx, val)``."""
     H = S.shape[0]
     ld = S.stride(0) if ld is None else ld
     if idx is None:
         idx = torch.empty(H, budget + n_forced, dtype=torch.int32, device=S.device)
+    if want_val and val is None:
+        val = torch.empty(H, budget + n_forced, dtype=torch.float32, device=S.device)
     ws, nb = _workspace(int(_lib.kvs_topk_workspace(H, n, budget)), S.device, ws)
-    _check(_lib.kvs_topk(_ptr(S), H, n, ld, budget, _ptr(priority), n_forced, _ptr(idx), _ptr(ws),
-                         nb, _stream(stream)), "kvs_topk")
-    return idx
+    _check(_lib.kvs_topk(_ptr(S), H, n, ld, budget, _ptr(priority), n_forced, _ptr(idx), _ptr(val),
+                         _ptr(ws), nb, _stream(stream)), "kvs_topk")
+    return (idx, val) if val is not None else idx
 
 
 def select_args(*, budget, n_forced=0, pool=RED_NONE, pool_k=7, cluster_P=0, cluster_theta=0.0,

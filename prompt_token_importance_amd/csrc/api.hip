@@ -319,9 +319,10 @@ kvs_status check_select(const SelectCall& c, size_t ws_bytes) {
 }  // namespace
 
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
-                    const uint8_t* priority, int32_t n_forced, int32_t* idx, void* ws,
+                    const uint8_t* priority, int32_t n_forced, int32_t* idx, float* val, void* ws,
                     size_t ws_bytes, void* stream) {
-  SelectCall c{S, H, n, ld, budget, n_forced, priority, KVS_RED_NONE, 0, 0, 0.f, 0, idx, ws};
+  SelectCall c{S, H, n, ld, budget, n_forced, priority, KVS_RED_NONE, 0, 0, 0.f, 0, idx, ws, val};
+  if ((uintptr_t)val & 3u) return KVS_EINVAL;
   const kvs_status st = check_select(c, ws_bytes);
   if (st != KVS_OK) return st;
   return select_run(c, as_stream(stream));
@@ -337,7 +338,7 @@ kvs_status kvs_select(const float* S, int32_t H, int32_t n, int64_t ld, const kv
   if (!a) return KVS_EINVAL;
   SelectCall c{S,          H,        n,         ld,           a->budget,        a->n_forced,
                nullptr,    a->pool,  a->pool_k, a->cluster_P, a->cluster_theta, a->cluster_r,
-               idx,        ws};
+               idx,        ws,       nullptr};
   const kvs_status st = check_select(c, ws_bytes);
   if (st != KVS_OK) return st;
   return select_run(c, as_stream(stream));

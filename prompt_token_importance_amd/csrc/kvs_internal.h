@@ -104,6 +104,7 @@ struct SelectCall {
   int cluster_r;
   int32_t* idx;
   void* ws;
+  float* val;   // kvs_topk's kept scores, or null
 };
 size_t topk_ws_bytes(int H, int n, int budget);
 kvs_status select_run(const SelectCall& c, hipStream_t stream);

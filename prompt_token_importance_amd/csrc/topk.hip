@@ -1085,6 +1085,19 @@ __global__ __launch_bounds__(256) void topk_forced_kernel(int n, int n_forced,
     out[i] = n + i;
 }
 
+// kvs_topk's kept scores: val[h][e] = S[h][idx[h][e]] for the budget chosen
+// entries (a bit copy), NaN for the forced suffix.
+__global__ __launch_bounds__(256) void topk_values_kernel(const float* __restrict__ S, int64_t ld,
+                                                          const int32_t* __restrict__ idx,
+                                                          int budget, int n_forced,
+                                                          float* __restrict__ val) {
+  const int w = budget + n_forced;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= w) return;
+  const int64_t o = (int64_t)blockIdx.y * w + e;
+  val[o] = e < budget ? S[(int64_t)blockIdx.y * ld + idx[o]] : __builtin_nanf("");
+}
+
 // ------------------------------------------------------------------ host
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -1152,8 +1165,21 @@ kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
+namespace {
+kvs_status select_indices(const SelectCall& c, hipStream_t stream);
+}
+
 kvs_status select_run(const SelectCall& c, hipStream_t stream) {
   if (c.H == 0) return KVS_OK;
+  const kvs_status st = select_indices(c, stream);
+  if (st != KVS_OK || !c.val || c.budget + c.n_forced == 0) return st;
+  hipLaunchKernelGGL(topk_values_kernel, dim3(ceil_div(c.budget + c.n_forced, 256), c.H), dim3(256),
+                     0, stream, c.S, c.ld, c.idx, c.budget, c.n_forced, c.val);
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+}
+
+namespace {
+kvs_status select_indices(const SelectCall& c, hipStream_t stream) {
   if (c.budget == 0) {
     if (c.n_forced > 0)
       hipLaunchKernelGGL(topk_forced_kernel, dim3((c.n_forced + 255) / 256, c.H), dim3(256), 0,
@@ -1190,5 +1216,6 @@ kvs_status select_run(const SelectCall& c, hipStream_t stream) {
     wide ? launch_wide<kPlain>(s, c.H, stream) : launch<kPlain>(s, c.H, stream);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
+}  // namespace
 
 }  // namespace kvs

@@ -188,9 +188,10 @@ def test_other_entry_points_reject(kvs):
     assert lib.kvs_pool_pages(P(16), 2, 10, 9, 0, 2, 7, 0, 1, P(16), None, None, None) == -1
     assert lib.kvs_pool_pages(P(16), 2, 10, 10, 0, 2, 7, 4, 3, None, P(16), None, None) == -1
     # top-k: budget > n, negative forced, null output
-    assert lib.kvs_topk(P(16), 1, 10, 10, 11, None, 0, P(16), None, 0, None) == -1
-    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, -1, P(16), None, 0, None) == -1
-    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, 0, None, None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 11, None, 0, P(16), None, None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, -1, P(16), None, None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, 0, None, None, None, 0, None) == -1
+    assert lib.kvs_topk(P(16), 1, 10, 10, 5, None, 0, P(16), P(18), None, 0, None) == -1
     # union: H_q not a multiple of H_kv, sub_group not dividing G, tiny workspace
     assert lib.kvs_block_union_pagetable(P(16), 6, 4, 0, 2, 8, P(16), P(16), P(256), 1 << 20, None) == -1
     assert lib.kvs_block_union_pagetable(P(16), 8, 2, 3, 2, 8, P(16), P(16), P(256), 1 << 20, None) == -1
@@ -237,7 +238,7 @@ def test_select_rejects(kvs):
     assert call(nb=16) == -3                                  # workspace too small
     assert call(ws=P(264)) == -1                              # workspace misaligned
     assert lib.kvs_select(P(16), 2, 100, 100, None, P(16), P(256), 1 << 24, None) == -1
-    assert lib.kvs_topk(P(16), 1, 100000, 100000, 10, None, 0, P(16), P(256), 16, None) == -3
+    assert lib.kvs_topk(P(16), 1, 100000, 100000, 10, None, 0, P(16), None, P(256), 16, None) == -3
     assert lib.kvs_select_workspace(8, 131040, 1024) == lib.kvs_topk_workspace(8, 131040, 1024)
     assert lib.kvs_select_workspace(8, 131040, 1024) > 0
     assert lib.kvs_select_workspace(8, 16384, 100) == 0      # one part: no candidates stored

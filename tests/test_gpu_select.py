@@ -141,6 +141,22 @@ def test_topk_row_stride(kvs):
     np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x[:, :n], 300, None, 32))
 
 
+@pytest.mark.parametrize("H,n,budget,nf,ld", [(3, 5000, 700, 16, 5000), (2, 40000, 3000, 2, 40008),
+                                              (1, 131040, 26208, 0, 131072), (4, 300, 0, 5, 300)])
+def test_topk_values(kvs, H, n, budget, nf, ld):
+    """kvs_topk's val output: the input scores at the oracle's indices, bit for bit,
+    in index order; NaN for the forced suffix (one-part, merged and wide rows)."""
+    x = synth.score_array(5100 + n, H, ld, levels=5, signed=True, with_zeros=True)
+    idx, val = kvs.kvs_topk(dev(x), n, budget, n_forced=nf, ld=ld, want_val=True)
+    torch.cuda.synchronize()
+    want = oracle.topk(x[:, :n], budget, None, nf)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+    v = val.cpu().numpy()
+    gathered = np.take_along_axis(x, want[:, :budget], axis=1)
+    assert np.array_equal(v[:, :budget].view(np.uint32), gathered.view(np.uint32))
+    assert np.isnan(v[:, budget:]).all()
+
+
 # ------------------------------------------------------------------ clusters
 @pytest.mark.parametrize("H,n,P,theta,r", [(8, 131040, 16, 2e-3, 3), (2, 1000, 16, 1.5, 3),
                                            (1, 100, 7, 0.0, 0), (3, 5000, 16, 3.0, 20)])
