@@ -97,11 +97,16 @@ int32_t kvs_version(void);
  *    or added to (accumulate = 1).
  * Strides are in elements; 0 selects the contiguous default (W*d_k, d_k,
  * L*d_k, d_k, L).  Q/K pointers and strides must be 16-byte aligned.
- * Limits: d_k in {64, 128}; W*G <= 128 after padding each head's rows to
- * 4, 8, 16 or a multiple of 32; otherwise KVS_EUNSUPPORTED.
- * The workspace holds per-split softmax statistics and the per-row constants
- * m_r + log2 Z_r; its size depends only on the shape.  `phase` splits the
- * call into its statistics pass and its column-sum pass (both read K once).
+ * Limits: d_k in {64, 128}; W*G <= 256 after padding each head's rows to
+ * 4, 8, 16 or a multiple of 32 (every W*G <= 256 with W a power of two from
+ * 4 up, e.g. G = 8 with W = 32 or G = 4 with W = 64; W = 12 with G = 20 pads
+ * to 320 rows and is refused); otherwise KVS_EUNSUPPORTED.
+ * More than 128 padded rows are scored in two row groups (each pass reads K
+ * once per group).
+ * The workspace holds per-split softmax statistics (and, for GROUP_MAX over
+ * two row groups, every query head's column sums, 4 * H_q * L bytes); its
+ * size depends only on the arguments.  `phase` splits the call into its
+ * statistics pass and its column-sum pass (each reads K once per row group).
  * The result is bit-identical from run to run.
  * ---------------------------------------------------------------------- */
 typedef struct {

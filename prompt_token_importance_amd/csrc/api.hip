@@ -118,6 +118,8 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   p.K = static_cast<const uint16_t*>(K);
   p.S = S;
   p.stats = static_cast<float2*>(ws);
+  p.head_rows_ws = pl.ws_heads ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.ws_stats)
+                               : nullptr;
   p.qhs = a.q_head_stride;
   p.qrs = a.q_row_stride;
   p.khs = a.k_head_stride;

@@ -16,16 +16,22 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------- score
 // Rows of one KV group: the W window rows of each of the G query heads are
 // padded to `head_rows` (4, 8, 16 or a multiple of 32) and the group to a
-// multiple of 32 rows (`rows_pad`); padding rows are masked out.
+// multiple of 32 rows (`rows_pad`, at most 256); padding rows are masked out.
+// The rows are processed in one or two row groups of at most 128 rows.
 struct ScorePlan {
   int head_rows;
-  int rows_pad;     // multiple of 32, <= 128
+  int rows_pad;     // multiple of 32, <= 256
   int n_tiles;      // ceil(L / 32)
   int n_split;      // splits of the key range per KV head
   int tiles_per_split;
   int head_batch;   // KV heads per (pass 1, pass 2) round
   int reverse;      // pass 2 visits tiles in the reverse of pass 1's order
+  int n_groups;     // row groups (1 or 2)
+  int grp_row0[2];  // first padded row of each group
+  int grp_rows[2];  // padded rows of each group (multiple of 32, <= 128)
+  int grp_h0[2], grp_h1[2];   // query heads of each group
   size_t ws_stats;  // bytes of per-split (max, sum) pairs
+  size_t ws_heads;  // bytes of per-head column sums (GROUP_MAX over two groups)
   size_t ws_total;
 };
 
@@ -34,6 +40,7 @@ struct ScoreLaunch {
   const uint16_t* K;
   float* S;
   float2* stats;  // [H_kv][rows_pad][n_split]
+  float* head_rows_ws;   // [H_q][L] per-head column sums (GROUP_MAX over two row groups)
   int64_t qhs, qrs, khs, kts, s_ld;
   int64_t q_pos0;
   int L, W, G, H_kv, d_k, heads, accumulate, phase;

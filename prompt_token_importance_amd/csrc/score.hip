@@ -57,10 +57,19 @@ static_assert((kStages & (kStages - 1)) == 0, "ring stages are indexed with a ma
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
+// One launch covers the padded query rows [row0, row0 + 32 * NT) of every KV
+// group (a row group: all of them when the padded rows fit 128, else one of
+// two), the query heads [h0, h1) of each group.
 struct KArgs {
   ScoreLaunch p;
   int head_rows, rows_pad, n_split, tps, n_tiles, g0, min_vis;
-  int rev;   // pass 2 walks each wave's tiles last to first
+  int rev;        // pass 2 walks each wave's tiles last to first
+  int row0;       // first padded row of this row group
+  int h0, h1;     // query heads (inside the KV group) whose rows this launch holds
+  int acc;        // column sums: 0 store, 1 add
+  int per_head;   // MODE 1: 1 writes each head's row, 0 the maximum over the heads
+  float* out;     // MODE 1 output rows (S, or the per-head workspace rows)
+  int64_t out_ld;
 };
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t* ptr) {
@@ -214,7 +223,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&q)[NT][D / 16], int (&vis)[NT], 
   const int nl = lane & 31, hl = lane >> 5;
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
-    const int r = 32 * T + nl;
+    const int r = a.row0 + 32 * T + nl;
     const int hq = r / a.head_rows, j = r % a.head_rows;
     const bool valid = hq < a.p.G && j < a.p.W;
     const int64_t pos = a.p.q_pos0 + j;
@@ -237,7 +246,7 @@ __device__ __forceinline__ void q_vis(int (&vis)[NT], const KArgs& a, int lane) 
   const int nl = lane & 31;
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
-    const int r = 32 * T + nl;
+    const int r = a.row0 + 32 * T + nl;
     const int hq = r / a.head_rows, j = r % a.head_rows;
     const int64_t pos = a.p.q_pos0 + j;
     vis[T] = hq < a.p.G && j < a.p.W ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1)
@@ -245,10 +254,11 @@ __device__ __forceinline__ void q_vis(int (&vis)[NT], const KArgs& a, int lane) 
   }
 }
 
-// Padded query row r of group g.  Padding rows read row 0 of the group
+// Padded query row row0 + r of group g.  Padding rows read row 0 of the group
 // instead: their statistics are discarded and their row constant is +inf, so
 // their logits never reach an output.
 __device__ __forceinline__ const uint16_t* q_row(const KArgs& a, int g, int r) {
+  r += a.row0;
   const int hq = r / a.head_rows, j = r % a.head_rows;
   const bool valid = hq < a.p.G && j < a.p.W;
   return a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs +
@@ -780,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) zz += sm[w][r].y * ex2(sm[w][r].x - mm);
     }
-    a.p.stats[((int64_t)g * a.rows_pad + r) * a.n_split + split] = make_float2(mm, zz);
+    a.p.stats[((int64_t)g * a.rows_pad + a.row0 + r) * a.n_split + split] = make_float2(mm, zz);
   }
 }
 
@@ -803,10 +813,10 @@ __device__ __forceinline__ void fold_pair(float& mm, float& zz, float2 v) {
   }
 }
 
-__device__ __forceinline__ void merge_rows(const KArgs& a, int g, float* brow) {
+__device__ __forceinline__ void merge_rows(const KArgs& a, int g, int rows, float* brow) {
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-  if (r < a.rows_pad) {
-    const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + r) * a.n_split;
+  if (r < rows) {
+    const float2* st = a.p.stats + ((int64_t)g * a.rows_pad + a.row0 + r) * a.n_split;
     float mm = kNegInf, zz = 0.f;
     for (int s0 = half; s0 < a.n_split; s0 += 2 * kMergeBatch) {
       float2 v[kMergeBatch];
@@ -824,7 +834,7 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, int g, float* brow) {
                                    : (mm == kNegInf ? 0.f : zz * exp2f(mm - mx)) +
                                          (m2 == kNegInf ? 0.f : z2 * exp2f(m2 - mx));
     if (half == 0) {
-      const int hq = r / a.head_rows, jr = r % a.head_rows;
+      const int hq = (a.row0 + r) / a.head_rows, jr = (a.row0 + r) % a.head_rows;
       const bool valid = hq < a.p.G && jr < a.p.W && mx != kNegInf;
       brow[r] = valid ? mx + log2f(zt) : kPosInf;
     }
@@ -882,7 +892,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   }
   // row constants from pass 1's split statistics
   __shared__ float brow[128];
-  merge_rows(a, g, brow);
+  merge_rows(a, g, 32 * NT, brow);
   float b[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
@@ -939,7 +949,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       for (int n = 0; n < 16; ++n) v += r[n];
       v += __shfl_xor(v, 32);
       const int tt = t0 + k;
-      if (hl == 0 && tt < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + tt, v, a.p.accumulate);
+      if (hl == 0 && tt < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + tt, v, a.acc);
     };
     const auto flush = [&](const float (&part)[16], int t0) {
       flush_write(part);
@@ -1077,8 +1087,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           p[T][i2] = (full || t0 + key_of(i2, hl) <= vis[T]) ? e : 0.f;
         }
       const int t = t0 + k;
-      float* ha = hacc[wave];
-      for (int x = lane; x < a.p.G * 32; x += 64) ha[x] = 0.f;
+      float* ha = hacc[wave];   // column sums of heads h0 .. h1-1, 32 keys each
+      for (int x = lane; x < (a.h1 - a.h0) * 32; x += 64) ha[x] = 0.f;
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
 #pragma unroll
@@ -1086,10 +1096,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           *reinterpret_cast<f32x4*>(&wl[nl * kStride + 8 * aa + 4 * hl]) =
               f32x4{p[T][4 * aa], p[T][4 * aa + 1], p[T][4 * aa + 2], p[T][4 * aa + 3]};
         lds_order();
-        const int r0 = 32 * T;
-        const int h_first = r0 / a.head_rows;
+        const int r0 = a.row0 + 32 * T;   // padded row of the tile's first row
+        int h_first = r0 / a.head_rows;
+        h_first = h_first > a.h0 ? h_first : a.h0;
         int h_last = (r0 + 31) / a.head_rows;
-        h_last = h_last < a.p.G - 1 ? h_last : a.p.G - 1;
+        h_last = h_last < a.h1 - 1 ? h_last : a.h1 - 1;
         for (int hq = h_first; hq <= h_last; ++hq) {
           if ((hq & 1) != hl) continue;
           int lo = hq * a.head_rows, hi = lo + a.p.W;
@@ -1097,20 +1108,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           hi = hi < r0 + 32 ? hi : r0 + 32;
           float v = 0.f;
           for (int r = lo; r < hi; ++r) v += wl[(r - r0) * kStride + k];
-          ha[hq * 32 + k] += v;
+          ha[(hq - a.h0) * 32 + k] += v;
         }
         lds_order();
       }
-      if (a.p.heads == KVS_HEADS_NONE) {
-        for (int hq = hl; hq < a.p.G; hq += 2)
+      if (a.per_head) {
+        for (int hq = a.h0 + hl; hq < a.h1; hq += 2)
           if (t < L)
-            store_out(a.p.S + (int64_t)(g * a.p.G + hq) * a.p.s_ld + t, ha[hq * 32 + k],
-                      a.p.accumulate);
+            store_out(a.out + (int64_t)(g * a.p.G + hq) * a.out_ld + t, ha[(hq - a.h0) * 32 + k],
+                      a.acc);
       } else {
         float mx = kNegInf;
-        for (int hq = hl; hq < a.p.G; hq += 2) mx = fmaxf(mx, ha[hq * 32 + k]);
+        for (int hq = a.h0 + hl; hq < a.h1; hq += 2) mx = fmaxf(mx, ha[(hq - a.h0) * 32 + k]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (hl == 0 && t < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + t, mx, a.p.accumulate);
+        if (hl == 0 && t < L) store_out(a.out + (int64_t)g * a.out_ld + t, mx, a.acc);
       }
       lds_order();
     }
@@ -1299,43 +1310,81 @@ __global__ __launch_bounds__(kThreads, 1) void score_raw_kernel(RawArgs a) {
   if (s < steps) step(s, k0, q0f, k1, q1f);
 }
 
+// GROUP_MAX over two row groups: the per-head rows both groups wrote into the
+// workspace are folded here, S[g][t] (=|+=) max over the G heads.
+__global__ __launch_bounds__(256) void score_head_max_kernel(const float* __restrict__ rows,
+                                                             int64_t rows_ld, int G, int L,
+                                                             float* __restrict__ S, int64_t s_ld,
+                                                             int accumulate) {
+  const int g = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= L) return;
+  const float* r = rows + (int64_t)g * G * rows_ld + t;
+  float mx = r[0];
+  for (int h = 1; h < G; ++h) mx = fmaxf(mx, r[(int64_t)h * rows_ld]);
+  store_out(S + (int64_t)g * s_ld + t, mx, accumulate);
+}
+
 template <int D, int NT>
-kvs_status launch_rounds(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t stream) {
-  for (int g0 = 0; g0 < p.H_kv; g0 += pl.head_batch) {
-    const int nb = min(pl.head_batch, p.H_kv - g0);
-    KArgs a;
-    a.p = p;
-    a.head_rows = pl.head_rows;
-    a.rows_pad = pl.rows_pad;
-    a.n_split = pl.n_split;
-    a.tps = pl.tiles_per_split;
-    a.n_tiles = pl.n_tiles;
-    a.g0 = g0;
-    const int64_t mv = p.q_pos0 < (int64_t)p.L - 1 ? p.q_pos0 : (int64_t)p.L - 1;
-    a.min_vis = (int)mv;
-    a.rev = pl.reverse;
-    dim3 grid(pl.n_split, nb);
-    if (p.phase != 2) {
-      hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
-    }
-    if (p.phase == 1) continue;
-    if (p.heads == KVS_HEADS_GROUP_SUM)
-      hipLaunchKernelGGL((score_colsum_kernel<D, NT, 0>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((score_colsum_kernel<D, NT, 1>), grid, dim3(kThreads), 0, stream, a);
-  }
-  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+void launch_group(const KArgs& a, int pass, int mode, dim3 grid, hipStream_t stream) {
+  if (pass == 1)
+    hipLaunchKernelGGL((score_stats_kernel<D, NT>), grid, dim3(kThreads), 0, stream, a);
+  else if (mode == 0)
+    hipLaunchKernelGGL((score_colsum_kernel<D, NT, 0>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_colsum_kernel<D, NT, 1>), grid, dim3(kThreads), 0, stream, a);
 }
 
 template <int D>
-kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t stream) {
-  switch (pl.rows_pad / 32) {
-    case 1: return launch_rounds<D, 1>(pl, p, stream);
-    case 2: return launch_rounds<D, 2>(pl, p, stream);
-    case 3: return launch_rounds<D, 3>(pl, p, stream);
-    case 4: return launch_rounds<D, 4>(pl, p, stream);
-    default: return KVS_EUNSUPPORTED;
+void launch_group_nt(int nt, const KArgs& a, int pass, int mode, dim3 grid, hipStream_t stream) {
+  switch (nt) {
+    case 1: launch_group<D, 1>(a, pass, mode, grid, stream); break;
+    case 2: launch_group<D, 2>(a, pass, mode, grid, stream); break;
+    case 3: launch_group<D, 3>(a, pass, mode, grid, stream); break;
+    default: launch_group<D, 4>(a, pass, mode, grid, stream); break;
   }
+}
+
+// Pass 1 of every row group, then pass 2 of every row group.  With two row
+// groups, GROUP_SUM (and any head mode of a single query head, whose rows are
+// split) adds the second group's column sums to the first's; NONE writes each
+// group's own heads; GROUP_MAX writes the per-head rows of both groups into
+// the workspace and folds them with score_head_max_kernel.
+template <int D>
+kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t stream) {
+  KArgs a;
+  a.p = p;
+  a.head_rows = pl.head_rows;
+  a.rows_pad = pl.rows_pad;
+  a.n_split = pl.n_split;
+  a.tps = pl.tiles_per_split;
+  a.n_tiles = pl.n_tiles;
+  a.g0 = 0;
+  const int64_t mv = p.q_pos0 < (int64_t)p.L - 1 ? p.q_pos0 : (int64_t)p.L - 1;
+  a.min_vis = (int)mv;
+  a.rev = pl.reverse;
+  const dim3 grid(pl.n_split, p.H_kv);
+  const bool split_max = pl.n_groups > 1 && p.heads == KVS_HEADS_GROUP_MAX && p.G > 1;
+  const int mode = (p.heads == KVS_HEADS_GROUP_SUM || pl.head_rows > 128) ? 0 : 1;
+  for (int pass = 1; pass <= 2; ++pass) {
+    if ((pass == 1 && p.phase == 2) || (pass == 2 && p.phase == 1)) continue;
+    for (int gr = 0; gr < pl.n_groups; ++gr) {
+      a.row0 = pl.grp_row0[gr];
+      a.h0 = pl.grp_h0[gr];
+      a.h1 = pl.grp_h1[gr];
+      a.acc = (mode == 0 && gr > 0) ? 1 : p.accumulate;
+      a.per_head = p.heads == KVS_HEADS_NONE || split_max;
+      a.out = split_max ? p.head_rows_ws : p.S;
+      a.out_ld = split_max ? (int64_t)p.L : p.s_ld;
+      if (split_max) a.acc = 0;
+      launch_group_nt<D>(pl.grp_rows[gr] / 32, a, pass, mode, grid, stream);
+    }
+    if (pass == 2 && split_max)
+      hipLaunchKernelGGL(score_head_max_kernel, dim3((p.L + 255) / 256, p.H_kv), dim3(256), 0,
+                         stream, p.head_rows_ws, (int64_t)p.L, p.G, p.L, p.S, p.s_ld,
+                         p.accumulate);
+  }
+  return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
 }  // namespace
@@ -1344,15 +1393,37 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   const int G = a->H_q / a->H_kv;
   const int W = a->W;
   const int hr = W <= 4 ? 4 : W <= 8 ? 8 : W <= 16 ? 16 : (W + 31) / 32 * 32;
-  if ((int64_t)G * hr > 128) return KVS_EUNSUPPORTED;
+  if ((int64_t)G * hr > 256) return KVS_EUNSUPPORTED;
   pl->head_rows = hr;
   pl->rows_pad = (G * hr + 31) / 32 * 32;
   pl->n_tiles = (a->L + 31) / 32;
-  // Every KV head in one round (one pass-1 launch, one pass-2 launch).  The
-  // key range of each head is cut into splits so that the grid holds one
-  // 4-wave workgroup per CU (256 CUs), each streaming a contiguous run of
-  // tiles, and at least 4 tiles (one per wave).  The plan depends only on the
-  // shape, so the workspace, phase 1 and phase 2 always agree on it.
+  // Row groups of at most 128 padded rows, the query rows a wave keeps as
+  // MFMA operands.  Two groups split at a head boundary, or, for a single
+  // query head with more than 128 rows, at row 128.
+  if (pl->rows_pad <= 128) {
+    pl->n_groups = 1;
+    pl->grp_row0[0] = 0;
+    pl->grp_rows[0] = pl->rows_pad;
+    pl->grp_h0[0] = 0;
+    pl->grp_h1[0] = G;
+  } else {
+    pl->n_groups = 2;
+    const int hpg = hr <= 128 ? 128 / hr : 0;   // heads in the first group (0: one head split)
+    const int r1 = hr <= 128 ? hpg * hr : 128;
+    pl->grp_row0[0] = 0;
+    pl->grp_rows[0] = hr <= 128 ? (r1 + 31) / 32 * 32 : 128;
+    pl->grp_row0[1] = r1;
+    pl->grp_rows[1] = pl->rows_pad - r1;
+    pl->grp_h0[0] = 0;
+    pl->grp_h1[0] = hr <= 128 ? hpg : G;
+    pl->grp_h0[1] = hr <= 128 ? hpg : 0;
+    pl->grp_h1[1] = G;
+  }
+  // Every KV head in one round (one pass-1 launch, one pass-2 launch per row
+  // group).  The key range of each head is cut into splits so that the grid
+  // holds one 4-wave workgroup per CU (256 CUs), each streaming a contiguous
+  // run of tiles, and at least 4 tiles (one per wave).  The plan depends only
+  // on the arguments, so the workspace, phase 1 and phase 2 always agree.
   pl->head_batch = a->H_kv;
   pl->reverse = 1;
   const int per_head = (256 + a->H_kv - 1) / a->H_kv;
@@ -1363,7 +1434,10 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->tiles_per_split = tps;
   pl->n_split = (pl->n_tiles + tps - 1) / tps;
   pl->ws_stats = align_up((size_t)a->H_kv * pl->n_split * pl->rows_pad * sizeof(float2), kWsAlign);
-  pl->ws_total = pl->ws_stats;
+  // GROUP_MAX over two row groups keeps every query head's column sums
+  const bool split_max = pl->n_groups > 1 && a->heads == KVS_HEADS_GROUP_MAX && G > 1;
+  pl->ws_heads = split_max ? align_up((size_t)a->H_q * a->L * sizeof(float), kWsAlign) : 0;
+  pl->ws_total = pl->ws_stats + pl->ws_heads;
   return KVS_OK;
 }
 

@@ -53,10 +53,23 @@ def test_score_workspace_is_shape_only(kvs):
     assert kvs.kvs_score_workspace(_score_args(kvs, d_k=96)) == 0
 
 
+def test_score_row_limit(kvs):
+    """Up to 256 padded rows per KV head (two row groups); GROUP_MAX over two
+    groups also keeps every query head's column sums in the workspace."""
+    ok = dict(L=4096, W=32, d_k=128, H_q=64, H_kv=8, q_pos0=4064)
+    ws_sum = kvs.kvs_score_workspace(_score_args(kvs, **ok))
+    ws_max = kvs.kvs_score_workspace(_score_args(kvs, **ok, heads=kvs.HEADS_GROUP_MAX))
+    assert ws_sum > 0 and ws_max >= ws_sum + 64 * 4096 * 4
+    assert kvs.kvs_score_workspace(_score_args(kvs, L=4096, W=200, d_k=128, H_q=2, H_kv=2,
+                                               q_pos0=3896)) > 0
+    for bad in (dict(W=33, H_q=8, H_kv=1), dict(W=16, H_q=17, H_kv=1), dict(W=257, H_q=1, H_kv=1)):
+        assert kvs.kvs_score_workspace(_score_args(kvs, **bad)) == 0, bad
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(L=0), -1), (dict(W=0), -1), (dict(H_q=3, H_kv=2), -1), (dict(q_pos0=-1), -1),
     (dict(heads=3), -1), (dict(scale=-1.0), -1), (dict(d_k=96), -2),
-    (dict(W=64, H_q=8, H_kv=1), -2), (dict(q_row_stride=65), -1), (dict(s_ld=100), -1),
+    (dict(W=64, H_q=8, H_kv=1), -2), (dict(W=33, H_q=8, H_kv=1), -2), (dict(q_row_stride=65), -1), (dict(s_ld=100), -1),
 ])
 def test_score_rejects(kvs, kw, status):
     lib = kvs.library()

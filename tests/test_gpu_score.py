@@ -50,6 +50,15 @@ CASES = [
     ("short", 20, 20, 128, 4, 1, 0),            # window is the whole prompt
     ("g3_w32", 2500, 32, 128, 6, 2, 0),         # 96 padded rows: three row tiles
     ("g6_w16_64", 1200, 16, 64, 12, 2, 0),      # 96 padded rows at d_k = 64
+    # more than 128 padded rows per KV head: two row groups
+    ("r160_g8_w20", 3001, 20, 128, 64, 8, 0),   # R = 160 (heads padded to 32 rows)
+    ("r160_g4_w40", 2100, 40, 128, 16, 4, 0),   # R = 160 (heads padded to 64 rows)
+    ("r192_g8_w24", 1500, 24, 64, 16, 2, 0),    # R = 192
+    ("r192_g6_w32", 2500, 32, 128, 12, 2, 0),   # R = 192: groups of 4 heads and 2 heads
+    ("r192_g2_w96", 1000, 96, 128, 4, 2, 0),    # one head per group (96 rows each)
+    ("r256_g8_w32", 4113, 32, 128, 64, 8, 0),   # R = 256: Llama shape with G = 8
+    ("r256_g4_w64", 2000, 64, 64, 8, 2, 0),     # R = 256
+    ("r200_g1_w200", 1200, 200, 128, 2, 2, 0),  # one head of 200 rows, split at row 128
 ]
 
 
@@ -119,6 +128,32 @@ def test_full_size_parity(kvs, which):
     R = ly.W * ly.G
     assert_scores_close(got, want, R, ly.L, which)
     assert_mass(got, R)
+
+
+@pytest.mark.parametrize("heads", [1, 0, 2], ids=["group_sum", "none", "group_max"])
+def test_two_row_groups_accumulate_and_phases(kvs, heads):
+    """R = 256 (G = 8, W = 32): accumulate = 1 adds the score once, and the phase-1 /
+    phase-2 calls equal one call bit for bit."""
+    L, W, d_k, H_q, H_kv = 3000, 32, 128, 32, 4
+    ly = synth.gaussian_layer(41, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv)
+    Q = kvs.bf16_from_bits(ly.Q)
+    K = kvs.bf16_from_bits(ly.K)
+    shape = dict(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, heads=heads)
+    rows = H_q if heads == 0 else H_kv
+    one = kvs.kvs_score(Q, K, kvs.score_args(**shape))
+    ws = torch.empty(kvs.kvs_score_workspace(kvs.score_args(**shape)), dtype=torch.uint8,
+                     device="cuda")
+    S = torch.full((rows, L), float("nan"), dtype=torch.float32, device="cuda")
+    kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=1), S=S, ws=ws)
+    kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=2), S=S, ws=ws)
+    acc = torch.full((rows, L), 0.25, dtype=torch.float32, device="cuda")
+    kvs.kvs_score(Q, K, kvs.score_args(**shape, accumulate=True), S=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32), S.view(torch.int32))
+    want = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0,
+                        heads=heads)
+    R = W * (H_q // H_kv) if heads == 1 else W
+    assert_scores_close(acc.cpu().numpy() - 0.25, want, R, L, "accumulate")
 
 
 @pytest.mark.parametrize("which", ["ragged", pytest.param("mistral128k", marks=pytest.mark.slow)])
