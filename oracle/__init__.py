@@ -22,9 +22,11 @@ from .kvs import (  # noqa: F401
     topk,
     block_select,
     block_union_pagetable,
+    token_pagetable,
     HEADS_NONE,
     HEADS_GROUP_SUM,
     HEADS_GROUP_MAX,
+    HEADS_ALL_SUM,
     RED_NONE,
     RED_SUM,
     RED_MAX,

@@ -59,7 +59,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX = 0, 1, 2
+HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX, HEADS_ALL_SUM = 0, 1, 2, 3
 RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
 
 
@@ -81,12 +81,14 @@ def score(Q, K, *, L: int, W: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
     [ClusterAttn] feature aggregation: logits of the window queries against the
     prompt keys, masked, softmax-normalised over keys, summed over window rows.
     [CLAA] FastKV / per-layer window score: also summed over the heads of the
-    group (here the G query heads sharing KV head g).  [DELTA] key design 2:
-    maximum over heads instead of the sum.
+    group (here the G query heads sharing KV head g), or over every head of the
+    layer (ALL_SUM: the per-layer score CLAA buffers, "Three design
+    decisions").  [DELTA] key design 2: maximum over heads instead of the sum.
 
     Q: bf16 bits [H_q][W][d_k]; K: bf16 bits [H_kv][L][d_k].
     Row j of every head sits at position q_pos0 + j and sees keys t <= q_pos0 + j.
-    Returns float64 [H_q][L] (NONE) or [H_kv][L] (GROUP_SUM / GROUP_MAX).
+    Returns float64 [H_q][L] (NONE), [H_kv][L] (GROUP_SUM / GROUP_MAX) or
+    [1][L] (ALL_SUM).
     With ``per_row`` returns the attention rows [H_q][W][L] instead.
     """
     if H_q % H_kv:
@@ -115,6 +117,8 @@ def score(Q, K, *, L: int, W: int, d_k: int, H_q: int, H_kv: int, q_pos0: int,
         return rows
     if heads == HEADS_NONE:
         return per_head
+    if heads == HEADS_ALL_SUM:
+        return per_head.sum(axis=0, keepdims=True)
     grouped = per_head.reshape(H_kv, G, L)
     if heads == HEADS_GROUP_SUM:
         return grouped.sum(axis=1)
@@ -502,3 +506,35 @@ def block_union_pagetable(M, *, H_q: int, H_kv: int, sub_group: int = 0):
         indptr[s + 1] = indptr[s] + len(js)
     indices = np.concatenate(lists) if lists else np.zeros(0, dtype=np.int64)
     return indptr, indices.astype(np.int64)
+
+
+def token_pagetable(idx, *, P: int, n_pages: int, rows_per_group: int = 1):
+    """Per-group KV page table (CSR) from token index lists.
+
+    [CompactAttention] "Method step details": a group's page table lists, in
+    ascending order, every KV page that one of its heads needs (kv_indices),
+    kv_indptr being the exclusive prefix sum of the counts; "Technical
+    novelty": the table is the smallest one that covers the selection.  [DELTA]
+    "Key design 3": the cache is read in whole pages of P tokens.
+    idx: int [H][n], the kept token positions of each row (for instance a top-k
+    list with its window); group s holds rows s * rows_per_group ...
+    (s + 1) * rows_per_group - 1.  Token i lies in page i // P; entries outside
+    [0, n_pages * P) (such as -1 padding) name no page; repeated pages are
+    listed once.  Returns (indptr int64 [n_groups + 1], indices int64).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    H = idx.shape[0]
+    if rows_per_group < 1 or H % rows_per_group:
+        raise ValueError("rows_per_group must divide the number of rows")
+    n_groups = H // rows_per_group
+    indptr = np.zeros(n_groups + 1, dtype=np.int64)
+    out: List[int] = []
+    for s in range(n_groups):
+        pages = set()
+        for h in range(s * rows_per_group, (s + 1) * rows_per_group):
+            for i in idx[h]:
+                if 0 <= i < n_pages * P:
+                    pages.add(int(i) // P)
+        out.extend(sorted(pages))
+        indptr[s + 1] = len(out)
+    return indptr, np.array(out, dtype=np.int64)

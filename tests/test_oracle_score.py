@@ -42,6 +42,10 @@ def test_mass_equals_rows(L, W, d_k, H_q, H_kv, q_pos0):
     N = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0,
                      heads=oracle.HEADS_NONE)
     np.testing.assert_allclose(N.sum(axis=1), W, rtol=1e-12)
+    A = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0,
+                     heads=oracle.HEADS_ALL_SUM)
+    assert A.shape == (1, L)
+    np.testing.assert_allclose(A.sum(), W * H_q, rtol=1e-12)   # every row of every head
     assert (S >= 0).all()
 
 
@@ -66,6 +70,15 @@ def test_identical_keys_closed_form(L, W, G):
     M = oracle.score(ly.Q, K, L=L, W=W, d_k=d_k, H_q=G, H_kv=1, q_pos0=q_pos0,
                      heads=oracle.HEADS_GROUP_MAX)[0]
     np.testing.assert_allclose(M, S / G, rtol=1e-12)
+    # two KV heads with identical keys: the sum over every head of the layer
+    # doubles the one-group closed form
+    K2 = np.concatenate([K, K], axis=0)
+    Q2 = np.concatenate([ly.Q, ly.Q[::-1]], axis=0)
+    A = oracle.score(Q2, K2, L=L, W=W, d_k=d_k, H_q=2 * G, H_kv=2, q_pos0=q_pos0,
+                     heads=oracle.HEADS_ALL_SUM)[0]
+    np.testing.assert_allclose(A[:q_pos0], 2 * prefix, rtol=1e-12)
+    for i in range(W):
+        np.testing.assert_allclose(A[q_pos0 + i], 2 * G * inv[i:].sum(), rtol=1e-12)
 
 
 @pytest.mark.parametrize("d_k", [64, 128])
@@ -186,3 +199,7 @@ def test_brute_force_tiny():
                 out[h // G][t] += math.exp(logits[t] - m) / z
     S = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0)
     np.testing.assert_allclose(S, np.array(out), rtol=1e-12)
+    A = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=q_pos0,
+                     heads=oracle.HEADS_ALL_SUM)
+    every = [sum(out[g][t] for g in range(H_kv)) for t in range(L)]
+    np.testing.assert_allclose(A[0], np.array(every), rtol=1e-12)

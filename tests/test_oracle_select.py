@@ -241,3 +241,44 @@ def test_union_minimal_and_covering(sub):
                 assert set(np.nonzero(M[h, i])[0]) <= set(T)
         for j in T:
             assert any(M[h, i, j] for h in heads for i in range(n_qb))
+
+
+# ---------------------------------------------------------------- token page tables
+def test_token_pagetable_hand_worked():
+    """[CompactAttention] per-group page table from kept token positions, worked by
+    hand with P = 4 and 5 pages (20 tokens): -1 padding and a token past the
+    cache name no page, repeats collapse, lists are ascending."""
+    idx = np.array([[0, 3, 9, 17, -1],
+                    [2, 8, 19, 25, 11],
+                    [4, 5, 6, 7, -1],
+                    [-1, -1, -1, -1, -1]])
+    ptr, ind = oracle.token_pagetable(idx, P=4, n_pages=5, rows_per_group=2)
+    np.testing.assert_array_equal(ptr, [0, 3, 4])
+    np.testing.assert_array_equal(ind, [0, 2, 4, 1])
+    ptr, ind = oracle.token_pagetable(idx, P=4, n_pages=5, rows_per_group=1)
+    np.testing.assert_array_equal(ptr, [0, 3, 6, 7, 7])
+    np.testing.assert_array_equal(ind, [0, 2, 4, 0, 2, 4, 1])
+    # P = 1: the table is the sorted set of valid tokens itself
+    ptr, ind = oracle.token_pagetable(idx[:1], P=1, n_pages=20)
+    np.testing.assert_array_equal(ind, [0, 3, 9, 17])
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 6), st.integers(1, 40), st.integers(1, 9), st.integers(1, 3), st.data())
+def test_token_pagetable_covers_minimally(H0, n, P, rpg, data):
+    """Coverage and minimality: every valid token's page is listed for its group,
+    every listed page holds a kept token of the group, lists strictly ascending."""
+    H = H0 * rpg
+    n_pages = data.draw(st.integers(1, 12))
+    idx = np.array(data.draw(st.lists(st.lists(st.integers(-2, n_pages * P + 3), min_size=n,
+                                               max_size=n), min_size=H, max_size=H)))
+    ptr, ind = oracle.token_pagetable(idx, P=P, n_pages=n_pages, rows_per_group=rpg)
+    for s in range(H0):
+        lst = ind[ptr[s]:ptr[s + 1]]
+        assert np.all(np.diff(lst) > 0)
+        toks = idx[s * rpg:(s + 1) * rpg].reshape(-1)
+        toks = toks[(toks >= 0) & (toks < n_pages * P)]
+        for t in toks:
+            assert t // P in lst
+        for pg in lst:
+            assert np.any((toks >= pg * P) & (toks < pg * P + P))
