@@ -53,6 +53,37 @@ def test_block_select_cached_matches_uncached(kvs, L_total, Lq, block, H_q, H_kv
         n_cached = L // block
 
 
+@pytest.mark.parametrize("L_total,Lq,block,H_q,H_kv,d_k", [(6000, 1024, 64, 8, 2, 128),
+                                                        (4100, 512, 64, 16, 4, 64)])
+def test_block_select_cached_matches_oracle(kvs, L_total, Lq, block, H_q, H_kv, d_k):
+    """A chunked prefill (5-8 chunks, growing L) through the cached select, every
+    chunk's mask checked against the oracle's block select on the same keys
+    (decidable blocks: preceding mass more than 2e-3 relative away from 0.9)."""
+    print(f"chunked prefill vs oracle L={L_total} Lq={Lq}", flush=True)
+    ly = synth.gaussian_layer(23, L=L_total, W=Lq, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=0)
+    K = kvs.bf16_from_bits(ly.K)
+    rng = np.random.default_rng(5)
+    Kb = torch.empty(H_kv, (L_total + block - 1) // block, d_k, dtype=torch.float32, device="cuda")
+    n_cached, chunks = 0, 0
+    for c0 in range(0, L_total, Lq):
+        L = min(c0 + Lq, L_total)
+        rows = L - c0
+        qbits = synth.to_bf16(rng.standard_normal((H_q, rows, d_k)).astype(np.float32))
+        a = kvs.block_select_args(Lq=rows, L=L, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=c0, block=block,
+                                  k_head_stride=L_total * d_k)
+        got = kvs.kvs_block_select_cached(kvs.bf16_from_bits(qbits), K, a, Kb, n_cached)
+        torch.cuda.synchronize()
+        want, before = oracle.block_select(qbits, np.ascontiguousarray(ly.K[:, :L]), Lq=rows, L=L,
+                                           d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=c0, block=block,
+                                           return_before=True)
+        dec = np.abs(before - 0.9) > 2e-3 * 0.9
+        g = got.cpu().numpy()
+        assert np.array_equal(g[dec], want[dec]), f"chunk at {c0}"
+        n_cached = L // block
+        chunks += 1
+    assert chunks >= 5
+
+
 def test_claa_rolling_buffer(kvs):
     """CLAA: per-layer window scores summed over heads, a buffer of the last n = 4
     layers, the token-wise max at the pruning layer (Eq. 6), then top 20%."""
