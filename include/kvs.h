@@ -62,6 +62,7 @@ typedef int32_t kvs_status;
 #define KVS_HEADS_NONE 0      /* output rows: H_q                         */
 #define KVS_HEADS_GROUP_SUM 1 /* output rows: H_kv, sum over the G heads  */
 #define KVS_HEADS_GROUP_MAX 2 /* output rows: H_kv, max over the G heads  */
+#define KVS_HEADS_ALL_SUM 3   /* output rows: 1, sum over all H_q heads    */
 
 /* Reductions used by pooling, paging and layer aggregation. */
 #define KVS_RED_NONE 0
@@ -85,8 +86,13 @@ int32_t kvs_version(void);
  *     a[h][j][t] = softmax over the visible t of s[h][j][.] (masked t -> 0),
  *     c_h[t]     = sum_j a[h][j][t],
  * and the output row is c_h (NONE), sum over the G heads of group g
- * (GROUP_SUM), or the max over those heads ([DELTA] key design 2, GROUP_MAX).
- * Every one of the L columns is produced, so each GROUP_SUM row sums to W*G.
+ * (GROUP_SUM), the max over those heads ([DELTA] key design 2, GROUP_MAX), or
+ * one row summed over every query head of the layer (ALL_SUM: the per-layer
+ * score [CLAA] buffers, "Three design decisions"; the KV groups are added in
+ * order g = 0, 1, ..., so a caller keeping the last n layers writes each layer
+ * straight into slot l mod n of an [n][s_ld] buffer).
+ * Every one of the L columns is produced, so each GROUP_SUM row sums to W*G
+ * (an ALL_SUM row to W*H_q).
  * With q_pos0 >= L - 1 every row sees all L keys (lookahead / decode queries).
  *
  * Q: bf16, element [h][j][c] at Q + h*q_head_stride + j*q_row_stride + c.
@@ -104,8 +110,9 @@ int32_t kvs_version(void);
  * More than 128 padded rows are scored in two row groups (each pass reads K
  * once per group).
  * The workspace holds per-split softmax statistics (and, for GROUP_MAX over
- * two row groups, every query head's column sums, 4 * H_q * L bytes); its
- * size depends only on the arguments.  `phase` splits the call into its
+ * two row groups, every query head's column sums, 4 * H_q * L bytes; for
+ * ALL_SUM each KV group's, 4 * H_kv * L bytes); its size depends only on the
+ * arguments.  `phase` splits the call into its
  * statistics pass and its column-sum pass (each reads K once per row group).
  * The result is bit-identical from run to run.
  * ---------------------------------------------------------------------- */
@@ -345,6 +352,32 @@ size_t kvs_block_union_workspace(int32_t H_q, int32_t H_kv, int32_t sub_group, i
 kvs_status kvs_block_union_pagetable(const uint8_t* M, int32_t H_q, int32_t H_kv, int32_t sub_group,
                                      int32_t n_qb, int32_t n_kvb, int32_t* kv_indptr,
                                      int32_t* kv_indices, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_token_pagetable - per-group KV page table from kept token positions.
+ *
+ * [CompactAttention] "Method step details": a paged attention kernel reads a
+ * group's KV through a page table kv_indptr / kv_indices, built on the GPU;
+ * "Technical novelty": the smallest table covering the selection.  [DELTA]
+ * "Key design 3": whole pages of P tokens.  This turns token lists (kvs_topk
+ * or kvs_select rows, window included) into such tables.
+ * idx int32 [H][n] with row stride idx_ld (0 selects n): row h's kept token
+ * positions, any order, duplicates allowed; entries < 0 or >= n_pages * P
+ * name no page.  Group s covers rows s * rows_per_group ... (s + 1) *
+ * rows_per_group - 1 (rows_per_group divides H; 1: one table per row, e.g.
+ * per KV head).  T_s = { i / P : i an entry of the group } ascending;
+ * kv_indptr int32 [H / rows_per_group + 1] = exclusive prefix sum of |T_s|;
+ * kv_indices int32 [capacity >= (H / rows_per_group) * n_pages] holds T_0,
+ * T_1, ... packed.  Workspace: kvs_token_pagetable_workspace bytes, 16-byte
+ * aligned (a page mask per group and the union staging), contents undefined
+ * on entry; nothing needs clearing.  Limits: n_pages <= 2^26 (else
+ * KVS_EUNSUPPORTED), n_pages * P < 2^31.
+ * ---------------------------------------------------------------------- */
+size_t kvs_token_pagetable_workspace(int32_t H, int32_t rows_per_group, int32_t n_pages);
+kvs_status kvs_token_pagetable(const int32_t* idx, int32_t H, int32_t n, int64_t idx_ld,
+                               int32_t rows_per_group, int32_t P, int32_t n_pages,
+                               int32_t* kv_indptr, int32_t* kv_indices, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_aggregate_layers - fold one layer's scores into a cross-layer total.

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvs.so")
 
 KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EWORKSPACE, KVS_EHIP = 0, -1, -2, -3, -4
-HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX = 0, 1, 2
+HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX, HEADS_ALL_SUM = 0, 1, 2, 3
 ACC_WRITE, ACC_ADD, ACC_MAX = 0, 1, 2
 RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
 
@@ -105,6 +105,8 @@ def _load():
         "kvs_select": (I32, [P, I32, I32, I64, ctypes.POINTER(SelectArgs), P, P, SZ, P]),
         "kvs_block_union_workspace": (SZ, [I32, I32, I32, I32]),
         "kvs_block_union_pagetable": (I32, [P, I32, I32, I32, I32, I32, P, P, P, SZ, P]),
+        "kvs_token_pagetable_workspace": (SZ, [I32, I32, I32]),
+        "kvs_token_pagetable": (I32, [P, I32, I32, I64, I32, I32, I32, P, P, P, SZ, P]),
         "kvs_aggregate_workspace": (SZ, [I32]),
         "kvs_aggregate_layers": (I32, [P, P, I32, I32, I64, I32, I32, P, SZ, P]),
         "kvs_cluster_priority": (I32, [P, P, I32, I32, I32, I32, F32, I32, P, P]),
@@ -128,6 +130,7 @@ EXPORTED = (
     "kvs_pool_pages",
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
     "kvs_block_union_workspace", "kvs_block_union_pagetable",
+    "kvs_token_pagetable_workspace", "kvs_token_pagetable",
     "kvs_aggregate_workspace", "kvs_aggregate_layers", "kvs_cluster_priority",
     "kvs_block_select_workspace", "kvs_block_select", "kvs_block_select_cached",
 )
@@ -183,8 +186,8 @@ def kvs_score_workspace(args: ScoreArgs) -> int:
 
 def kvs_score(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs, S: Optional[torch.Tensor] = None,
               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Window column scores; S float32 [H_kv or H_q][s_ld] (allocated if None)."""
-    rows = args.H_q if args.heads == HEADS_NONE else args.H_kv
+    """Window column scores; S float32 [H_kv, H_q or 1][s_ld] (allocated if None)."""
+    rows = {HEADS_NONE: args.H_q, HEADS_ALL_SUM: 1}.get(args.heads, args.H_kv)
     if S is None:
         S = torch.empty(rows, args.s_ld or args.L, dtype=torch.float32, device=K.device)
     ws, nb = _workspace(kvs_score_workspace(args), K.device, ws)
@@ -335,6 +338,24 @@ def kvs_block_union_pagetable(M: torch.Tensor, H_q: int, H_kv: int, sub_group: i
     _check(_lib.kvs_block_union_pagetable(_ptr(M), H_q, H_kv, sub_group, n_qb, n_kvb, _ptr(indptr),
                                           _ptr(indices), _ptr(ws), nb, _stream(stream)),
            "kvs_block_union_pagetable")
+    return indptr, indices
+
+
+# --------------------------------------------------------------------------- token page tables
+def kvs_token_pagetable(idx: torch.Tensor, P: int, n_pages: int, rows_per_group: int = 1,
+                        n: Optional[int] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """idx int32 [H][>= n] kept token positions -> (kv_indptr int32 [n_groups+1],
+    kv_indices int32 [n_groups * n_pages]) of the pages they fall in, per group of rows."""
+    H = idx.shape[0]
+    n = idx.shape[1] if n is None else n
+    n_groups = H // rows_per_group
+    indptr = torch.empty(n_groups + 1, dtype=torch.int32, device=idx.device)
+    indices = torch.empty(n_groups * n_pages, dtype=torch.int32, device=idx.device)
+    ws, nb = _workspace(int(_lib.kvs_token_pagetable_workspace(H, rows_per_group, n_pages)),
+                        idx.device, ws)
+    _check(_lib.kvs_token_pagetable(_ptr(idx), H, n, idx.stride(0), rows_per_group, P, n_pages,
+                                    _ptr(indptr), _ptr(indices), _ptr(ws), nb, _stream(stream)),
+           "kvs_token_pagetable")
     return indptr, indices
 
 

@@ -20,7 +20,7 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
   if (a->L < 1 || a->W < 1 || a->H_q < 1 || a->H_kv < 1 || a->d_k < 1) return KVS_EINVAL;
   if (a->H_q % a->H_kv) return KVS_EINVAL;
   if (a->q_pos0 < 0) return KVS_EINVAL;
-  if (a->heads < KVS_HEADS_NONE || a->heads > KVS_HEADS_GROUP_MAX) return KVS_EINVAL;
+  if (a->heads < KVS_HEADS_NONE || a->heads > KVS_HEADS_ALL_SUM) return KVS_EINVAL;
   if (a->accumulate != 0 && a->accumulate != 1) return KVS_EINVAL;
   if (a->phase < 0 || a->phase > 2) return KVS_EINVAL;
   if (!(a->scale >= 0.f) || isinf(a->scale)) return KVS_EINVAL;
@@ -366,6 +366,32 @@ kvs_status kvs_block_union_pagetable(const uint8_t* M, int32_t H_q, int32_t H_kv
   if (!aligned16(ws)) return KVS_EINVAL;
   return union_run(M, H_q, H_kv, sub_group, n_qb, n_kvb, kv_indptr, kv_indices, ws,
                    as_stream(stream));
+}
+
+size_t kvs_token_pagetable_workspace(int32_t H, int32_t rows_per_group, int32_t n_pages) {
+  if (H < 1 || rows_per_group < 1 || H % rows_per_group || n_pages < 1 || n_pages > (1 << 26))
+    return 0;
+  return token_pagetable_ws_bytes(H, rows_per_group, n_pages);
+}
+
+kvs_status kvs_token_pagetable(const int32_t* idx, int32_t H, int32_t n, int64_t idx_ld,
+                               int32_t rows_per_group, int32_t P, int32_t n_pages,
+                               int32_t* kv_indptr, int32_t* kv_indices, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!kv_indptr || !kv_indices || (n > 0 && !idx)) return KVS_EINVAL;
+  if (H < 1 || n < 0 || rows_per_group < 1 || H % rows_per_group || P < 1 || n_pages < 1)
+    return KVS_EINVAL;
+  if (idx_ld == 0) idx_ld = n;
+  if (idx_ld < n) return KVS_EINVAL;
+  if ((int64_t)n_pages * P > 0x7fffffff) return KVS_EINVAL;
+  if (n_pages > (1 << 26)) return KVS_EUNSUPPORTED;
+  if (((uintptr_t)idx & 3u) || ((uintptr_t)kv_indptr & 3u) || ((uintptr_t)kv_indices & 3u))
+    return KVS_EINVAL;
+  const size_t need = token_pagetable_ws_bytes(H, rows_per_group, n_pages);
+  if (!ws || ws_bytes < need) return KVS_EWORKSPACE;
+  if (!aligned16(ws)) return KVS_EINVAL;
+  return token_pagetable_run(idx, H, n, idx_ld, rows_per_group, P, n_pages, kv_indptr, kv_indices,
+                             ws, as_stream(stream));
 }
 
 size_t kvs_aggregate_workspace(int32_t n) {

@@ -395,7 +395,53 @@ __global__ __launch_bounds__(kThreads) void union_pack_kernel(const int32_t* __r
   }
 }
 
+// ------------------------------------------------------------------ token page tables
+// kvs_token_pagetable: the pages of kept token positions, per group of rows.
+// A zeroed byte mask [group][page] (rows padded to 16 pages) is set by one
+// thread per list entry (threads that hit the same page store the same byte),
+// then lowered to CSR by the union kernels with one query block per group.
+__global__ __launch_bounds__(kThreads) void zero16_kernel(u32x4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+__global__ __launch_bounds__(kThreads) void token_pages_kernel(const int32_t* __restrict__ idx,
+                                                               int n, int64_t idx_ld, int rpg,
+                                                               int P, int n_pages, int64_t row_ld,
+                                                               uint8_t* __restrict__ mask) {
+  const int h = blockIdx.y;
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= n) return;
+  const int i = idx[(int64_t)h * idx_ld + e];
+  if (i >= 0 && i / P < n_pages) mask[(int64_t)(h / rpg) * row_ld + i / P] = 1;
+}
+
 }  // namespace
+
+size_t token_pagetable_ws_bytes(int H, int rpg, int n_pages) {
+  const int n_groups = H / rpg;
+  const int ld = (n_pages + 15) / 16 * 16;
+  return align_up((size_t)n_groups * ld, kWsAlign) + union_ws_bytes(n_groups, n_groups, 1, ld);
+}
+
+kvs_status token_pagetable_run(const int32_t* idx, int H, int n, int64_t idx_ld, int rpg, int P,
+                               int n_pages, int32_t* indptr, int32_t* indices, void* ws,
+                               hipStream_t stream) {
+  const int n_groups = H / rpg;
+  const int ld = (n_pages + 15) / 16 * 16;
+  uint8_t* mask = static_cast<uint8_t*>(ws);
+  void* uws = static_cast<char*>(ws) + align_up((size_t)n_groups * ld, kWsAlign);
+  const int64_t n16 = (int64_t)n_groups * ld / 16;
+  const int zb = (int)((n16 + kThreads - 1) / kThreads < 1024 ? (n16 + kThreads - 1) / kThreads : 1024);
+  hipLaunchKernelGGL(zero16_kernel, dim3(zb), dim3(kThreads), 0, stream,
+                     reinterpret_cast<u32x4*>(mask), n16);
+  if (n > 0)
+    hipLaunchKernelGGL(token_pages_kernel, dim3((n + kThreads - 1) / kThreads, H), dim3(kThreads), 0,
+                       stream, idx, n, idx_ld, rpg, P, n_pages, (int64_t)ld, mask);
+  if (hipGetLastError() != hipSuccess) return KVS_EHIP;
+  return union_run(mask, n_groups, n_groups, 1, 1, ld, indptr, indices, uws, stream);
+}
 
 kvs_status block_plan(const kvs_block_select_args* a, BlockPlan* pl) {
   pl->n_qb = (a->Lq + a->block - 1) / a->block;

@@ -133,6 +133,12 @@ size_t union_ws_bytes(int H_q, int H_kv, int sub_group, int n_kvb);
 kvs_status union_run(const uint8_t* M, int H_q, int H_kv, int sub_group, int n_qb, int n_kvb,
                      int32_t* indptr, int32_t* indices, void* ws, hipStream_t stream);
 
+// Per-group page tables from token lists (kvs_token_pagetable).
+size_t token_pagetable_ws_bytes(int H, int rows_per_group, int n_pages);
+kvs_status token_pagetable_run(const int32_t* idx, int H, int n, int64_t idx_ld,
+                               int rows_per_group, int P, int n_pages, int32_t* indptr,
+                               int32_t* indices, void* ws, hipStream_t stream);
+
 struct BlockPlan {
   int n_qb, n_kvb;
   size_t ws_kb, ws_qb, ws_logit, ws_total;

@@ -949,7 +949,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       for (int n = 0; n < 16; ++n) v += r[n];
       v += __shfl_xor(v, 32);
       const int tt = t0 + k;
-      if (hl == 0 && tt < L) store_out(a.p.S + (int64_t)g * a.p.s_ld + tt, v, a.acc);
+      if (hl == 0 && tt < L) store_out(a.out + (int64_t)g * a.out_ld + tt, v, a.acc);
     };
     const auto flush = [&](const float (&part)[16], int t0) {
       flush_write(part);
@@ -1310,6 +1310,19 @@ __global__ __launch_bounds__(kThreads, 1) void score_raw_kernel(RawArgs a) {
   if (s < steps) step(s, k0, q0f, k1, q1f);
 }
 
+// ALL_SUM: the per-KV-head column sums the column-sum pass wrote into the
+// workspace are added here in head order, S[0][t] (=|+=) sum over g.
+__global__ __launch_bounds__(256) void score_head_sum_kernel(const float* __restrict__ rows,
+                                                             int64_t rows_ld, int H, int L,
+                                                             float* __restrict__ S,
+                                                             int accumulate) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= L) return;
+  float v = rows[t];
+  for (int g = 1; g < H; ++g) v += rows[(int64_t)g * rows_ld + t];
+  store_out(S + t, v, accumulate);
+}
+
 // GROUP_MAX over two row groups: the per-head rows both groups wrote into the
 // workspace are folded here, S[g][t] (=|+=) max over the G heads.
 __global__ __launch_bounds__(256) void score_head_max_kernel(const float* __restrict__ rows,
@@ -1365,7 +1378,9 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
   a.rev = pl.reverse;
   const dim3 grid(pl.n_split, p.H_kv);
   const bool split_max = pl.n_groups > 1 && p.heads == KVS_HEADS_GROUP_MAX && p.G > 1;
-  const int mode = (p.heads == KVS_HEADS_GROUP_SUM || pl.head_rows > 128) ? 0 : 1;
+  const bool all_sum = p.heads == KVS_HEADS_ALL_SUM;
+  const int mode =
+      (p.heads == KVS_HEADS_GROUP_SUM || all_sum || pl.head_rows > 128) ? 0 : 1;
   for (int pass = 1; pass <= 2; ++pass) {
     if ((pass == 1 && p.phase == 2) || (pass == 2 && p.phase == 1)) continue;
     for (int gr = 0; gr < pl.n_groups; ++gr) {
@@ -1374,11 +1389,14 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
       a.h1 = pl.grp_h1[gr];
       a.acc = (mode == 0 && gr > 0) ? 1 : p.accumulate;
       a.per_head = p.heads == KVS_HEADS_NONE || split_max;
-      a.out = split_max ? p.head_rows_ws : p.S;
-      a.out_ld = split_max ? (int64_t)p.L : p.s_ld;
-      if (split_max) a.acc = 0;
+      a.out = (split_max || all_sum) ? p.head_rows_ws : p.S;
+      a.out_ld = (split_max || all_sum) ? (int64_t)p.L : p.s_ld;
+      if (split_max || all_sum) a.acc = gr > 0 && mode == 0 ? 1 : 0;
       launch_group_nt<D>(pl.grp_rows[gr] / 32, a, pass, mode, grid, stream);
     }
+    if (pass == 2 && all_sum)
+      hipLaunchKernelGGL(score_head_sum_kernel, dim3((p.L + 255) / 256), dim3(256), 0, stream,
+                         p.head_rows_ws, (int64_t)p.L, p.H_kv, p.L, p.S, p.accumulate);
     if (pass == 2 && split_max)
       hipLaunchKernelGGL(score_head_max_kernel, dim3((p.L + 255) / 256, p.H_kv), dim3(256), 0,
                          stream, p.head_rows_ws, (int64_t)p.L, p.G, p.L, p.S, p.s_ld,
@@ -1435,8 +1453,13 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->n_split = (pl->n_tiles + tps - 1) / tps;
   pl->ws_stats = align_up((size_t)a->H_kv * pl->n_split * pl->rows_pad * sizeof(float2), kWsAlign);
   // GROUP_MAX over two row groups keeps every query head's column sums
+  // GROUP_MAX over two row groups keeps every query head's column sums; the
+  // sum over every head keeps each KV head's
   const bool split_max = pl->n_groups > 1 && a->heads == KVS_HEADS_GROUP_MAX && G > 1;
-  pl->ws_heads = split_max ? align_up((size_t)a->H_q * a->L * sizeof(float), kWsAlign) : 0;
+  pl->ws_heads = split_max ? align_up((size_t)a->H_q * a->L * sizeof(float), kWsAlign)
+                 : a->heads == KVS_HEADS_ALL_SUM
+                     ? align_up((size_t)a->H_kv * a->L * sizeof(float), kWsAlign)
+                     : 0;
   pl->ws_total = pl->ws_stats + pl->ws_heads;
   return KVS_OK;
 }

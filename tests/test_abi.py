@@ -68,7 +68,7 @@ def test_score_row_limit(kvs):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(L=0), -1), (dict(W=0), -1), (dict(H_q=3, H_kv=2), -1), (dict(q_pos0=-1), -1),
-    (dict(heads=3), -1), (dict(scale=-1.0), -1), (dict(d_k=96), -2),
+    (dict(heads=4), -1), (dict(scale=-1.0), -1), (dict(d_k=96), -2),
     (dict(W=64, H_q=8, H_kv=1), -2), (dict(W=33, H_q=8, H_kv=1), -2), (dict(q_row_stride=65), -1), (dict(s_ld=100), -1),
 ])
 def test_score_rejects(kvs, kw, status):
@@ -189,6 +189,22 @@ def test_gather_rejects_pointers(kvs):
     # nothing to copy: accepted without touching memory
     assert call(None, None, None, None, None, H=0) == 0
     assert call(None, None, None, None, None, n=0) == 0
+
+
+def test_token_pagetable_rejects(kvs):
+    lib = kvs.library()
+    P = ctypes.c_void_p
+    ws = lib.kvs_token_pagetable_workspace(8, 1, 8192)
+    assert ws > 0
+    assert lib.kvs_token_pagetable_workspace(8, 3, 100) == 0          # 3 does not divide 8
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 10, 3, 16, 100, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 9, 1, 16, 100, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 10, 1, 0, 100, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 10, 1, 16, 100, None, P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_token_pagetable(P(18), 8, 10, 10, 1, 16, 100, P(16), P(16), P(256), 1 << 20, None) == -1
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 10, 1, 1 << 20, 1 << 12, P(16), P(16), P(256), 1 << 20,
+                                   None) == -1                          # n_pages * P >= 2^31
+    assert lib.kvs_token_pagetable(P(16), 8, 10, 10, 1, 16, 100, P(16), P(16), P(256), 8, None) == -3
 
 
 def test_other_entry_points_reject(kvs):

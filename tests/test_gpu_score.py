@@ -176,3 +176,39 @@ def test_phase_split_matches_one_call(kvs, which):
     kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=2), S=S, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int32), S.view(torch.int32))
+
+
+ALL_SUM_CASES = [
+    # (name, L, W, d_k, H_q, H_kv): the CLAA layer score, summed over every head
+    ("claa_w8", 3000, 8, 128, 32, 8),
+    ("tiny", 512, 16, 64, 4, 1),
+    ("ragged64", 777, 13, 64, 6, 3),
+    ("two_groups", 2100, 32, 128, 64, 8),
+]
+
+
+@pytest.mark.parametrize("name,L,W,d_k,H_q,H_kv", ALL_SUM_CASES, ids=[c[0] for c in ALL_SUM_CASES])
+def test_all_heads_sum(kvs, name, L, W, d_k, H_q, H_kv):
+    """ALL_SUM: one row per layer summed over every query head, written into a row of a
+    longer buffer (s_ld > L) and accumulated on a second call."""
+    print(f"all-heads sum {name}", flush=True)
+    ly = synth.gaussian_layer(300 + L, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv)
+    Q = kvs.bf16_from_bits(ly.Q)
+    K = kvs.bf16_from_bits(ly.K)
+    s_ld = L + 64
+    ring = torch.full((3, s_ld), -5.0, dtype=torch.float32, device="cuda")
+    a = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0,
+                       heads=kvs.HEADS_ALL_SUM, s_ld=s_ld)
+    kvs.kvs_score(Q, K, a, S=ring[1:2])
+    b = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0,
+                       heads=kvs.HEADS_ALL_SUM, s_ld=s_ld, accumulate=True)
+    kvs.kvs_score(Q, K, b, S=ring[2:3])
+    torch.cuda.synchronize()
+    got = ring.cpu().numpy()
+    want = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0,
+                        heads=oracle.HEADS_ALL_SUM)
+    R = W * H_q
+    assert_scores_close(got[1:2, :L], want, R, L, name)
+    assert_mass(got[1:2, :L], R)
+    assert_scores_close(got[2:3, :L] + 5.0, want, R, L, name + " accumulate")
+    assert (got[0] == -5.0).all() and (got[1:, L:] == -5.0).all(), "wrote outside the slot"

@@ -104,3 +104,32 @@ def test_claa_rolling_buffer(kvs):
     want = oracle.aggregate_layers(kept[-n_buf:], oracle.RED_MAX)
     np.testing.assert_allclose(agg.cpu().numpy()[0], want, rtol=2e-3, atol=1e-6)
     assert_topk_parity(idx.cpu().numpy(), want[None, :], budget)
+
+
+@pytest.mark.slow
+def test_claa_ring_all_heads_32k(kvs):
+    """CLAA at 32K: each of 9 layers' window scores summed over every head straight into
+    slot l mod 4 of the ring (kvs_score ALL_SUM), Eq. 6's token-wise max over the ring at
+    the pruning layer, then the top 20%, against the oracle (selection parity)."""
+    L, W, n_buf, layers = 32768, 8, 4, 9
+    ring = torch.empty(n_buf, L, dtype=torch.float32, device="cuda")
+    kept = []
+    for l in range(layers):
+        ly = synth.gaussian_layer(600 + l, L=L, W=W, d_k=128, H_q=32, H_kv=8, n_spans=8,
+                                  span_len=256, lift=2.0, fixed_span_seed=600, n_fixed=4)
+        a = kvs.score_args(L=L, W=W, d_k=128, H_q=32, H_kv=8, q_pos0=ly.q_pos0,
+                           heads=kvs.HEADS_ALL_SUM)
+        kvs.kvs_score(kvs.bf16_from_bits(ly.Q), kvs.bf16_from_bits(ly.K), a,
+                      S=ring[l % n_buf:l % n_buf + 1])
+        if l >= layers - n_buf:
+            kept.append(oracle.score(ly.Q, ly.K, L=L, W=W, d_k=128, H_q=32, H_kv=8,
+                                     q_pos0=ly.q_pos0, heads=oracle.HEADS_ALL_SUM))
+    acc = torch.empty(L, dtype=torch.float32, device="cuda")
+    for i in range(n_buf):
+        kvs.kvs_aggregate_layers(acc, ring[i:i + 1], L, kvs.RED_MAX, first_layer=(i == 0))
+    budget = L // 5
+    idx = kvs.kvs_topk(acc.view(1, L), L, budget)
+    torch.cuda.synchronize()
+    want = oracle.aggregate_layers(kept, oracle.RED_MAX)
+    np.testing.assert_allclose(acc.cpu().numpy(), want, rtol=2e-3, atol=2e-3 * 1e-3 * W * 32 / L)
+    assert_topk_parity(idx.cpu().numpy(), want[None, :], budget)
