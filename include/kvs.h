@@ -56,6 +56,7 @@ typedef int32_t kvs_status;
 #define KVS_EUNSUPPORTED (-2)
 #define KVS_EWORKSPACE (-3)
 #define KVS_EHIP (-4)
+#define KVS_ESCRATCH (-5) /* kvs_score_noalloc: the call needs more than its static scratch */
 
 /* Head reduction of the score: per query head, or over the G = H_q / H_kv
  * query heads that share a KV head. */
@@ -133,6 +134,22 @@ typedef struct {
 size_t kvs_score_workspace(const kvs_score_args* a);
 kvs_status kvs_score(const kvs_score_args* a, const void* Q, const void* K, float* S,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* kvs_score_noalloc - kvs_score without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results (bit for
+ * bit) and errors as kvs_score; the workspace is a static 8 MiB array that
+ * the library holds on every GPU it runs on until the process ends (its
+ * device address is looked up on the first call on each device).  A call
+ * whose kvs_score_workspace() exceeds 8 MiB returns KVS_ESCRATCH before
+ * anything is enqueued (e.g. ALL_SUM needs 4 * H_kv * L bytes beside the
+ * statistics).  Allocates nothing and frees nothing.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind: a phase-2 call reads
+ * what the last phase-1 call on that GPU wrote, so calls that overlap in time
+ * on one GPU (other streams, other threads) race and must be serialized by
+ * the caller. */
+kvs_status kvs_score_noalloc(const kvs_score_args* a, const void* Q, const void* K, float* S,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_score_raw - raw (pre-softmax) attention logits reduced over all heads.

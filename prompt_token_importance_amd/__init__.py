@@ -17,7 +17,7 @@ import torch  # loaded first so libkvs binds to the same HIP runtime as torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvs.so")
 
-KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EWORKSPACE, KVS_EHIP = 0, -1, -2, -3, -4
+KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EWORKSPACE, KVS_EHIP, KVS_ESCRATCH = 0, -1, -2, -3, -4, -5
 HEADS_NONE, HEADS_GROUP_SUM, HEADS_GROUP_MAX, HEADS_ALL_SUM = 0, 1, 2, 3
 ACC_WRITE, ACC_ADD, ACC_MAX = 0, 1, 2
 RED_NONE, RED_SUM, RED_MAX, RED_MEAN, RED_SUM_L1 = 0, 1, 2, 3, 4
@@ -94,6 +94,7 @@ def _load():
         "kvs_version": (I32, []),
         "kvs_score_workspace": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvs_score_noalloc": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P]),
         "kvs_score_raw": (I32, [ctypes.POINTER(RawArgs), P, P, P, P]),
         "kvs_delta_workspace": (SZ, [ctypes.POINTER(DeltaArgs)]),
         "kvs_gather_kv": (I32, [P, P, I32, I32, I32, I64, I64, P, I64, P, I32, I32, P, P, P]),
@@ -125,7 +126,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = (
-    "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_raw",
+    "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_noalloc",
+    "kvs_score_raw",
     "kvs_delta_workspace", "kvs_delta_pages", "kvs_gather_kv",
     "kvs_pool_pages",
     "kvs_topk_workspace", "kvs_topk", "kvs_select_workspace", "kvs_select",
@@ -193,6 +195,17 @@ def kvs_score(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs, S: Optional[tor
     ws, nb = _workspace(kvs_score_workspace(args), K.device, ws)
     _check(_lib.kvs_score(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _ptr(ws), nb,
                           _stream(stream)), "kvs_score")
+    return S
+
+
+def kvs_score_noalloc(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs,
+                      S: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvs_score with the library's static scratch instead of a workspace."""
+    rows = {HEADS_NONE: args.H_q, HEADS_ALL_SUM: 1}.get(args.heads, args.H_kv)
+    if S is None:
+        S = torch.empty(rows, args.s_ld or args.L, dtype=torch.float32, device=K.device)
+    _check(_lib.kvs_score_noalloc(ctypes.byref(args), _ptr(Q), _ptr(K), _ptr(S), _stream(stream)),
+           "kvs_score_noalloc")
     return S
 
 

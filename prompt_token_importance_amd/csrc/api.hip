@@ -3,6 +3,8 @@
 // allocates, frees or synchronizes.
 #include <math.h>
 
+#include <mutex>
+
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -76,6 +78,40 @@ kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
   return KVS_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// kvs_score_noalloc's workspace: one array of kScratchBytes on every GPU the
+// library runs on, held until the process ends.  In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, or null
+
+// Device address of the scratch array on the device that runs `stream`.
+kvs_status scratch_on(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return KVS_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVS_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KVS_EHIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return KVS_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return KVS_EHIP;
+    if (e != hipSuccess || !p) return KVS_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +123,8 @@ const char* kvs_status_string(kvs_status s) {
     case KVS_EUNSUPPORTED: return "KVS_EUNSUPPORTED: a valid shape outside what the kernels cover";
     case KVS_EWORKSPACE: return "KVS_EWORKSPACE: workspace too small";
     case KVS_EHIP: return "KVS_EHIP: kernel launch failed";
+    case KVS_ESCRATCH:
+      return "KVS_ESCRATCH: the call needs more scratch than the library's static buffer holds";
     default: return "KVS: unknown status";
   }
 }
@@ -137,6 +175,21 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   const double scale = a.scale > 0.f ? (double)a.scale : 1.0 / sqrt((double)a.d_k);
   p.c = (float)(scale * 1.4426950408889634073599246810018921);  // scale * log2(e)
   return score_run(pl, p, as_stream(stream));
+}
+
+kvs_status kvs_score_noalloc(const kvs_score_args* in, const void* Q, const void* K, float* S,
+                             void* stream) {
+  kvs_score_args a;
+  kvs_status st = check_score(in, &a);
+  if (st != KVS_OK) return st;
+  ScorePlan pl;
+  st = score_plan(&a, &pl);
+  if (st != KVS_OK) return st;
+  if (pl.ws_total > kScratchBytes) return KVS_ESCRATCH;
+  void* ws = nullptr;
+  st = scratch_on(as_stream(stream), &ws);
+  if (st != KVS_OK) return st;
+  return kvs_score(in, Q, K, S, ws, kScratchBytes, stream);
 }
 
 kvs_status kvs_score_raw(const kvs_raw_args* in, const void* Q, const void* K, float* S,
