@@ -50,10 +50,12 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--workload", default="mistral128k", choices=sorted(WORKLOADS),
-                    help="mistral128k: the softmax window-score path (default); gemfilter128k and "
-                         "specprefill128k: the raw-logit paths; delta32x8k: DELTA decode page sets; "
-                         "gather128k: compaction of the kept K and V; chunksel128k: chunked-prefill "
-                         "block selection with cached key-block means")
+                    help="mistral128k: the softmax window-score path at 128K (default); llama32k: the "
+                         "same path at 32K with max-pool 7; cross32x16k: 32-layer cross-layer "
+                         "aggregation at 16K; gemfilter128k and specprefill128k: the raw-logit paths; "
+                         "delta32x8k: DELTA decode page sets; gather128k: compaction of the kept K and "
+                         "V; chunksel128k: chunked-prefill block selection with cached key-block "
+                         "means; chunksel128k_uncached: the same chunk recomputing every key-block mean")
     return ap.parse_args()
 
 
@@ -61,6 +63,10 @@ WORKLOADS = {
     # workload: (kernel-stats summary, traffic summary, kernel name fragment, kernel label)
     "mistral128k": ("kvs_mistral128k_kernel_stats.md", "score_colsum_mistral128k_traffic.txt",
                     "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
+    "llama32k": ("kvs_llama32k_kernel_stats.md", "score_colsum_llama32k_traffic.txt",
+                 "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
+    "cross32x16k": ("kvs_cross32x16k_kernel_stats.md", "score_colsum_cross32x16k_traffic.txt",
+                    "score_colsum", "32 x kvs_score (ALL_SUM) + kvs_aggregate_layers (SUM_L1)"),
     "gemfilter128k": ("kvs_gemfilter128k_kernel_stats.md", "score_raw_gemfilter128k_traffic.txt",
                       "score_raw", "score_raw_kernel (kvs_score_raw, SUM over heads, W = 1)"),
     "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
@@ -71,6 +77,10 @@ WORKLOADS = {
                    "gather_kernel", "gather_kernel (kvs_gather_kv, K and V)"),
     "chunksel128k": ("kvs_chunksel128k_kernel_stats.md", "block_topp_chunksel128k_traffic.txt",
                      "block_topp_kernel", "block_topp_kernel (kvs_block_select_cached)"),
+    "chunksel128k_uncached": ("kvs_chunksel128k_uncached_kernel_stats.md",
+                              "block_mean_chunksel128k_uncached_traffic.txt", "block_mean_kernel",
+                              "kvs_block_select (every key-block mean from K: block_mean_kernel, "
+                              "block_logits_kernel, block_topp_kernel)"),
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 
@@ -78,11 +88,14 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 # Sources of each workload's roofline kernel(s), besides the shared header.
 KERNEL_SOURCES = {
     "mistral128k": ("score.hip",),
+    "llama32k": ("score.hip",),
+    "cross32x16k": ("score.hip",),
     "gemfilter128k": ("score.hip",),
     "specprefill128k": ("score.hip",),
     "delta32x8k": ("score.hip", "topk.hip", "wave_ops.h"),
     "gather128k": ("gather.hip",),
     "chunksel128k": ("blocks.hip", "wave_ops.h"),
+    "chunksel128k_uncached": ("blocks.hip", "wave_ops.h"),
 }
 
 
@@ -128,10 +141,10 @@ def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
         return None
 
 
-def measured_stats_traffic(path=TRAFFIC_SUMMARY):
+def measured_stats_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
     """HBM bytes per launch of the score statistics pass from the same counter
     runs (scaled like the roofline kernel's), or None."""
-    kv = traffic_summary(path, "mistral128k")
+    kv = traffic_summary(path, workload)
     try:
         return (float(kv["stats_fetch_kib"]) * float(kv["fetch_scale"]) +
                 float(kv["stats_write_kib"]) * float(kv["write_scale"])) * 1024 if kv else None
@@ -178,6 +191,9 @@ def profile_commands(workload="mistral128k", out="profile_out"):
 
 WORKLOAD_TITLES = {
     "mistral128k": "Mistral-7B GQA layer at L = 131072, softmax window scores + cluster top-k",
+    "llama32k": "Llama-3.1-8B GQA layer at L = 32768, softmax window scores + max-pool 7 top-k",
+    "cross32x16k": "32 layers of the Llama-3.1-8B GQA shape at L = 16384, per-layer scores summed over "
+                   "every head, L1-normalised sum over layers, top 20%",
     "gemfilter128k": "Mistral-7B GQA layer at L = 131072, GemFilter raw last-token scores + pooled top-k",
     "specprefill128k": "Mistral-7B GQA layer at L = 131072, Speculative-Prefill raw scores (8 lookahead "
                        "queries) + mean, pool and top-k",
@@ -187,6 +203,8 @@ WORKLOAD_TITLES = {
                   "gathered into compact arrays",
     "chunksel128k": "chunked prefill at L = 131072, last 1024-token chunk: cached key-block means, "
                     "block top-p 0.9 and the per-group page table",
+    "chunksel128k_uncached": "chunked prefill at L = 131072, last 1024-token chunk: every key-block "
+                             "mean from K, block top-p 0.9 and the per-group page table",
 }
 
 
@@ -741,12 +759,13 @@ def bench_chunksel(args):
         if st != 0:
             raise RuntimeError(f"chunk selection failed in step {i}")
 
+    uncached = args.workload == "chunksel128k_uncached"
     for i in range(args.warmup):
-        step(i)
+        step(i, full=uncached)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(i, full=uncached)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -778,9 +797,30 @@ def bench_chunksel(args):
     flops = 2.0 * ch.H_q * n_qb * n_kvb * ch.d_k
     achieved = flops / (sel_ms * 1e-3) / 1e12
     stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    event_us = {"select_cached": sel_ms * 1e3, "union": uni_ms * 1e3,
+                "select_uncached": full_ms * 1e3}
+    if not uncached:
+        roof = {
+            "kernel": "kvs_block_select_cached (block means of the chunk and its new key blocks, "
+                      "block_logits_kernel on fp32 MFMA, block_topp_kernel)",
+            "bound": "mfma", "achieved": achieved, "peak": 157.3, "unit": "TFLOP/s",
+            "frac": achieved / 157.3, "traffic": None, "kernel_us": sel_ms * 1e3,
+        }
+    else:
+        # the uncached select is bound by reading K once for the key-block means:
+        # K once, the chunk's queries once, the mask written once
+        alg = ch.H_kv * ch.L * ch.d_k * 2 + ch.H_q * ch.Lq * ch.d_k * 2 + ch.H_q * n_qb * n_kvb
+        gbs = alg / (full_ms * 1e-3) / 1e9
+        roof = {
+            "kernel": label, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": measured_traffic(os.path.join(ROOT, "profiles", traffic_name), args.workload),
+            "alg_bytes_per_launch": alg, "kernel_us": full_ms * 1e3,
+        }
+    roof.update({"kernel_source_sha256_16": source_hash(args.workload), "event_us": event_us})
     out = {
         "metric": "KV tokens covered/sec (chunked-prefill block selection, last chunk at L=128K); "
-                  "% of fp32 matrix roofline",
+                  + ("% of fp32 matrix roofline" if not uncached else "% of HBM roofline"),
         "value": ch.L / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -790,24 +830,15 @@ def bench_chunksel(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if not uncached else "bf16",
         "data": "synthetic",
         "config": {"workload": "chunk_select_128k_last_chunk: K [8][131072][128], chunk Q [32][1024][128], "
-                               "block 64, top-p 0.9, cached means of 2032 earlier blocks -> union page "
-                               "table", "L": ch.L, "Lq": ch.Lq, "block": blk, "n_cached_blocks": n_cached},
-        "roofline": {
-            "kernel": "kvs_block_select_cached (block means of the chunk and its new key blocks, block_logits_kernel on fp32 MFMA, block_topp_kernel)",
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": 157.3,
-            "unit": "TFLOP/s",
-            "frac": achieved / 157.3,
-            "traffic": None,
-            "kernel_us": sel_ms * 1e3,
-            "kernel_source_sha256_16": source_hash(args.workload),
-            "event_us": {"select_cached": sel_ms * 1e3, "union": uni_ms * 1e3,
-                         "select_uncached": full_ms * 1e3},
-        },
+                               "block 64, top-p 0.9, " + ("cached means of 2032 earlier blocks"
+                                                          if not uncached else
+                                                          "every key-block mean recomputed from K")
+                               + " -> union page table", "L": ch.L, "Lq": ch.Lq, "block": blk,
+                   "n_cached_blocks": 0 if uncached else n_cached},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -857,49 +888,99 @@ def cpu_baseline_raw(ly, gem, budget, min_seconds=10.0, max_reps=8):
                       f"{sec:.2f} s each; raw scores + pooling + top-k in float64 NumPy"}
 
 
-def main():
-    if len(sys.argv) in (3, 4) and sys.argv[1] == "--summarize-profiles":
-        summarize_profiles(sys.argv[2], *sys.argv[3:])
-        return
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no collectives; it would shard by KV head, every GPU running the same "
-              "kernels on its share of the heads).")
-        sys.exit(2)
-    if args.workload != "mistral128k":
-        import torch
-        if not torch.cuda.is_available():
-            print("bench.py needs a GPU (torch.cuda.is_available() is False)")
-            sys.exit(1)
-        if args.workload == "delta32x8k":
-            bench_delta(args)
-        elif args.workload == "gather128k":
-            bench_gather(args)
-        elif args.workload == "chunksel128k":
-            bench_chunksel(args)
-        else:
-            bench_raw(args)
-        return
+def cpu_info():
+    """CPU model and the cores this process may use (capped at the 16 a one-GPU machine shares)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, max(1, min(16, len(os.sched_getaffinity(0))))
 
+
+def oracle_layer_scores(ly, heads, threads):
+    """oracle.score on one layer, its KV groups spread over `threads` Python threads
+    (NumPy releases the GIL in its kernels; each call uses one BLAS thread)."""
+    import numpy as np
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    G = ly.H_q // ly.H_kv
+
+    def one(g):
+        return oracle.score(ly.Q[g * G:(g + 1) * G], ly.K[g:g + 1], L=ly.L, W=ly.W, d_k=ly.d_k,
+                            H_q=G, H_kv=1, q_pos0=ly.q_pos0, heads=heads)
+
+    if threads <= 1:
+        parts = [one(g) for g in range(ly.H_kv)]
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(one, range(ly.H_kv)))
+    return np.concatenate(parts, axis=0)
+
+
+def cpu_baseline_softmax(ly, sel, min_seconds=5.0, max_reps=8):
+    """The fp64 oracle as it stands on the full layer: scores (KV groups in parallel
+    threads), then the selection rows; timed with all cores and with one."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    n = ly.L - ly.W
+
+    def run(threads):
+        S = oracle_layer_scores(ly, oracle.HEADS_GROUP_SUM, threads)[:, :n]
+        if sel["kind"] == "cluster":
+            z, arg = oracle.pages(S, sel["P"], oracle.RED_MAX)
+            prio = oracle.cluster_priority(z, arg, n, float(np.float32(sel["theta"])), sel["r"])
+            oracle.topk(S, sel["budget"], prio, ly.W)
+        else:
+            y = oracle.pool(S, oracle.RED_MAX, sel["pool_k"])
+            oracle.topk(y, sel["budget"], None, ly.W)
+
+    def timed(threads):
+        reps, t_total = 0, 0.0
+        while reps < max_reps and (reps == 0 or t_total < min_seconds):
+            t0 = time.perf_counter()
+            run(threads)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return t_total / reps, reps
+
+    model, cores = cpu_info()
+    used = min(cores, ly.H_kv)
+    with threadpool_limits(limits=1):
+        sec_all, reps_all = timed(used)
+        sec_one, reps_one = timed(1)
+    return {"value": ly.L / sec_all, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"full workload (all {ly.H_kv} KV heads, L={ly.L}); {reps_all} repetition(s) of "
+                      f"{sec_all:.2f} s on {used} threads (one per KV group), {reps_one} of "
+                      f"{sec_one:.2f} s on one; score + selection in float64 NumPy",
+            "one_core_value": ly.L / sec_one, "cpu_model": model, "cores_available": cores}
+
+
+def bench_softmax(args):
+    """The softmax window-score path on one layer: kvs_score phase 1 and phase 2,
+    then kvs_select.  mistral128k: page max P = 16 + cluster priority (theta =
+    2e-3, r = 3) + top 1024 per KV head with the window; llama32k: max-pool 7 +
+    top 1024 per KV head with the window."""
     import torch
     import synth
     import prompt_token_importance_amd as kvs
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU (torch.cuda.is_available() is False)")
-        sys.exit(1)
     lib = kvs.library()
-
-    # ------------------------------------------------------------ workload
+    mistral = args.workload == "mistral128k"
     t0 = time.perf_counter()
-    ly = synth.mistral_layer()
+    ly = synth.mistral_layer() if mistral else synth.llama_layer()
     L, W, d_k, H_q, H_kv = ly.L, ly.W, ly.d_k, ly.H_q, ly.H_kv
     n = L - W
-    P, theta, r, budget, n_forced = 16, 2e-3, 3, 1024, W
+    budget, n_forced = 1024, W
+    # K buffers cycled so no step finds its keys warm in the 256 MB Infinity Cache
+    rotate = args.rotate if mistral else max(args.rotate, 8)
     Q = kvs.bf16_from_bits(ly.Q)
     K0 = kvs.bf16_from_bits(ly.K)
-    Ks = [K0] + [K0.clone() for _ in range(max(0, args.rotate - 1))]
+    Ks = [K0] + [K0.clone() for _ in range(max(0, rotate - 1))]
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
 
     a1 = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, phase=1)
@@ -908,8 +989,13 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     S = torch.empty(H_kv, L, dtype=torch.float32, device="cuda")
     idx = torch.empty(H_kv, budget + n_forced, dtype=torch.int32, device="cuda")
-    sel_args = kvs.select_args(budget=budget, n_forced=n_forced, cluster_P=P, cluster_theta=theta,
-                               cluster_r=r)
+    if mistral:
+        sel = {"kind": "cluster", "P": 16, "theta": 2e-3, "r": 3, "budget": budget}
+        sel_args = kvs.select_args(budget=budget, n_forced=n_forced, cluster_P=16,
+                                   cluster_theta=2e-3, cluster_r=3)
+    else:
+        sel = {"kind": "pool", "pool_k": 7, "budget": budget}
+        sel_args = kvs.select_args(budget=budget, n_forced=n_forced, pool=kvs.RED_MAX, pool_k=7)
     tk_bytes = lib.kvs_select_workspace(H_kv, n, budget)
     tk_ws = torch.empty(max(tk_bytes, 1), dtype=torch.uint8, device="cuda")
 
@@ -938,7 +1024,6 @@ def main():
         if st != 0:
             raise RuntimeError(f"libkvs call failed in step {i}")
 
-    # ------------------------------------------------------------ timing
     # Timed region: K whole steps, bracketed by synchronizations, no events
     # inside (an event record idles the GPU for a few microseconds).
     for i in range(args.warmup):
@@ -973,67 +1058,261 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1+merge {pass1 * 1e3:.1f} us, "
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1 {pass1 * 1e3:.1f} us, "
         f"pass2 {pass2 * 1e3:.1f} us, select {select * 1e3:.1f} us")
     copy_gbs = copy_calibration(timed) if args.copy_calibration else None
 
-    # Algorithmic bytes of one column-sum launch: K once, Q once, S written once,
-    # per-row constants (negligible) -> 2048 + 32 + ~2 bytes per token.
+    # Algorithmic bytes of the layer (and of one column-sum launch): K once, Q
+    # once, S written once -> 2048 + 32 + ~2 bytes per token.
     k_bytes = H_kv * L * d_k * 2
     q_bytes = H_q * W * d_k * 2
     s_bytes = H_kv * L * 4
     alg_bytes = k_bytes + q_bytes + s_bytes
     dom_ms = pass2
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
-    t2, t1 = measured_traffic(), measured_stats_traffic()
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    tpath = os.path.join(ROOT, "profiles", traffic_name)
+    t2, t1 = measured_traffic(tpath, args.workload), measured_stats_traffic(tpath, args.workload)
     passes_gbs = (t1 + t2) / ((pass1 + pass2) * 1e-3) / 1e9 if (t1 and t2) else None
     flops = 2.0 * H_q * W * L * d_k
+    tag = "128K" if mistral else "32K"
     out = {
-        "metric": "prompt tokens scored/sec at L=128K, 8B GQA shape; % of HBM roofline",
+        "metric": f"prompt tokens scored/sec at L={tag}, 8B GQA shape; % of HBM roofline",
         "value": L / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "event_step_us_p50_p90": [step_us[len(step_us) // 2], step_us[min(len(step_us) - 1, (9 * len(step_us)) // 10)]],
+        "event_step_us_p50_p90": [step_us[len(step_us) // 2],
+                                  step_us[min(len(step_us) - 1, (9 * len(step_us)) // 10)]],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "mistral7b_gqa_layer_128k: H_q=32 H_kv=8 d_k=128 L=131072 W=32; "
-                        "score -> page max P=16 -> cluster theta=2e-3 r=3 -> top-1024 + 32 window per KV head",
+            "workload": ("mistral7b_gqa_layer_128k: H_q=32 H_kv=8 d_k=128 L=131072 W=32; score -> page "
+                         "max P=16 -> cluster theta=2e-3 r=3 -> top-1024 + 32 window per KV head"
+                         if mistral else
+                         "llama31_8b_gqa_layer_32k: H_q=32 H_kv=8 d_k=128 L=32768 W=32; score -> max-pool 7 "
+                         "-> top-1024 + 32 window per KV head"),
             "L": L, "W": W, "d_k": d_k, "H_q": H_q, "H_kv": H_kv, "budget": budget,
             "k_buffers_rotated": len(Ks),
         },
         "roofline": {
-            "kernel": "score_colsum_kernel (kvs_score column-sum pass)",
+            "kernel": label,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
+            "traffic": t2,
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": dom_ms * 1e3,
             "mfma_frac": flops / (dom_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "kernel_source_sha256_16": source_hash("mistral128k"),
-            "event_us": {"score_pass1_stats_and_merge": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
-                         "page_cluster_topk": select * 1e3},
+            "kernel_source_sha256_16": source_hash(args.workload),
+            "event_us": {"score_pass1_stats": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
+                         "selection": select * 1e3},
             "copy_256MiB_GBs": copy_gbs,
-            # both score passes from the counter runs: their bytes over their time
+            # the layer's algorithmic bytes (K once) over the time of both score passes,
+            # and over the whole step
+            "alg_frac_score_pair": alg_bytes / ((pass1 + pass2) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_frac_step": alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # both score passes from the counter runs (K read twice): their bytes over their time
             "score_passes_counter_GBs": passes_gbs,
             "score_passes_counter_frac": passes_gbs / HBM_PEAK_GBS if passes_gbs else None,
         },
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline ...")
-        out["cpu_baseline"] = cpu_baseline(ly, theta, r, budget, n_forced, P)
+        out["cpu_baseline"] = cpu_baseline_softmax(ly, sel)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def bench_cross(args):
+    """Cross-layer aggregation over 32 layers of the Llama-3.1-8B GQA shape at
+    L = 16384: each layer's window score summed over every head (kvs_score
+    ALL_SUM, phase 0), L1-normalised and summed over the layers
+    (kvs_aggregate_layers SUM_L1), then the top 20% of the tokens (kvs_topk).
+    A step is the whole 32-layer pass; tokens/s = 32 * L / t."""
+    import torch
+    import synth
+    import prompt_token_importance_amd as kvs
+
+    lib = kvs.library()
+    n_layers, L = 32, 16384
+    t0 = time.perf_counter()
+    layers = [synth.cross_layer(l, L=L) for l in range(n_layers)]
+    W, d_k, H_q, H_kv = layers[0].W, layers[0].d_k, layers[0].H_q, layers[0].H_kv
+    Qs = [kvs.bf16_from_bits(ly.Q) for ly in layers]
+    Ks = [kvs.bf16_from_bits(ly.K) for ly in layers]
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s (K of the 32 layers: "
+        f"{sum(k.numel() for k in Ks) * 2 / 2**20:.0f} MiB)")
+    budget = (2 * L) // 10
+    a = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=layers[0].q_pos0,
+                       heads=kvs.HEADS_ALL_SUM)
+    ws_bytes = kvs.kvs_score_workspace(a)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    row = torch.empty(1, L, dtype=torch.float32, device="cuda")
+    acc = torch.empty(1, L, dtype=torch.float32, device="cuda")
+    idx = torch.empty(1, budget, dtype=torch.int32, device="cuda")
+    ag_bytes = lib.kvs_aggregate_workspace(L)
+    ag_ws = torch.empty(max(ag_bytes, 1), dtype=torch.uint8, device="cuda")
+    tk_bytes = lib.kvs_topk_workspace(1, L, budget)
+    tk_ws = torch.empty(max(tk_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+    ra = ctypes.byref(a)
+    pQs = [V(q.data_ptr()) for q in Qs]
+    pKs = [V(k.data_ptr()) for k in Ks]
+    prow, pacc, pws, pag, ptk, pidx = (V(row.data_ptr()), V(acc.data_ptr()), V(ws.data_ptr()),
+                                       V(ag_ws.data_ptr()), V(tk_ws.data_ptr()), V(idx.data_ptr()))
+
+    def step(i, ev=None):
+        st = 0
+        if ev is not None:
+            ev[0].record(stream)
+        for l in range(n_layers):
+            st |= lib.kvs_score(ra, pQs[l], pKs[l], prow, pws, ws_bytes, sp)
+            st |= lib.kvs_aggregate_layers(pacc, prow, 1, L, L, kvs.RED_SUM_L1, int(l == 0), pag,
+                                           ag_bytes, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.kvs_topk(pacc, 1, L, L, budget, None, 0, pidx, None, ptk, tk_bytes, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libkvs call failed in step {i}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    layers_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    topk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: 32 layers (score + aggregate) "
+        f"{layers_ms * 1e3:.1f} us, top-k {topk_ms * 1e3:.1f} us")
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(args.steps):
+            fn(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    copy_gbs = copy_calibration(timed) if args.copy_calibration else None
+    # algorithmic bytes of the 32-layer pass: every layer's K and Q once, one score row per layer
+    alg_bytes = n_layers * (H_kv * L * d_k * 2 + H_q * W * d_k * 2 + L * 4)
+    achieved = alg_bytes / (layers_ms * 1e-3) / 1e9
+    stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
+    out = {
+        "metric": "prompt tokens scored/sec, 32-layer cross-layer aggregation at L=16K, 8B GQA shape; "
+                  "% of HBM roofline",
+        "value": n_layers * L / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "cross_layer_32x16k: 32 layers, H_q=32 H_kv=8 d_k=128 L=16384 W=32; "
+                               "per-layer score summed over every head -> L1-normalised sum over "
+                               "layers -> top 20% (3276)", "layers": n_layers, "L": L, "W": W,
+                   "budget": budget},
+        "roofline": {
+            "kernel": label,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_us": layers_ms * 1e3,
+            "kernel_source_sha256_16": source_hash(args.workload),
+            "event_us": {"layers_score_and_aggregate": layers_ms * 1e3, "topk": topk_ms * 1e3},
+            "copy_256MiB_GBs": copy_gbs,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline_cross(layers, budget)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_cross(layers, budget, min_seconds=0.0):
+    """The oracle on the 32-layer pass: per-layer scores (KV groups in threads),
+    L1-normalised sum, top-k; all cores and one."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    L = layers[0].L
+
+    def run(threads):
+        per = [oracle_layer_scores(ly, oracle.HEADS_ALL_SUM, threads) for ly in layers]
+        agg = oracle.aggregate_layers(per, oracle.RED_SUM_L1)
+        oracle.topk(agg[None, :], budget)
+
+    model, cores = cpu_info()
+    used = min(cores, layers[0].H_kv)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run(used)
+        sec_all = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        run(1)
+        sec_one = time.perf_counter() - t0
+    n = len(layers) * L
+    return {"value": n / sec_all, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"full workload ({len(layers)} layers x {L} tokens), one pass of {sec_all:.2f} s "
+                      f"on {used} threads and one of {sec_one:.2f} s on one; float64 NumPy",
+            "one_core_value": n / sec_one, "cpu_model": model, "cores_available": cores}
+
+
+def main():
+    if len(sys.argv) in (3, 4) and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2], *sys.argv[3:])
+        return
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no collectives; it would shard by KV head, every GPU running the same "
+              "kernels on its share of the heads).")
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)")
+        sys.exit(1)
+    if args.workload in ("mistral128k", "llama32k"):
+        bench_softmax(args)
+    elif args.workload == "cross32x16k":
+        bench_cross(args)
+    elif args.workload == "delta32x8k":
+        bench_delta(args)
+    elif args.workload == "gather128k":
+        bench_gather(args)
+    elif args.workload in ("chunksel128k", "chunksel128k_uncached"):
+        bench_chunksel(args)
+    else:
+        bench_raw(args)
 
 
 if __name__ == "__main__":
