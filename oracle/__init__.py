@@ -5,6 +5,9 @@ CPU-baseline leg may import this package.  The product library never calls it
 and shares no code with it.
 
 Parity pins for every function are listed in the ``kvs`` module docstring.
+``score_ref.c`` (built by ``build_ref``) is a second, independent fp64
+implementation of the window score, in plain C, that the NumPy oracle is
+checked against.
 """
 from .kvs import (  # noqa: F401
     bf16_to_f64,
