@@ -130,26 +130,18 @@ def test_raw_deterministic(kvs):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def _sample_columns(L, count, seed):
-    rng = np.random.default_rng(seed)
-    cols = np.unique(np.concatenate([rng.integers(0, L, count), [0, 1, 31, 32, L - 33, L - 1]]))
-    return cols
-
-
 @pytest.mark.slow
 @pytest.mark.parametrize("W,reduce", [(1, 1), (8, 2)], ids=["gemfilter", "specprefill"])
-def test_raw_full_size_sampled(kvs, W, reduce):
+def test_raw_full_size(kvs, W, reduce):
     """Mistral-7B GQA layer at L = 131072 in the launch configuration the bench
-    uses; the oracle computes 512 sampled key columns (raw scores are per key)."""
+    uses, every key column against the oracle."""
     L = 131072
     print(f"raw full size W={W}", flush=True)
     ly = synth.gaussian_layer(5 + W, L=L, W=W, d_k=128, H_q=32, H_kv=8, q_pos0=L - 1,
                               n_spans=16, span_len=512, lift=2.0, span_region=L - 1)
     got = _run(kvs, ly, reduce, q_pos0=L - 1).cpu().numpy()
-    cols = _sample_columns(L, 512, W)
-    Ks = np.ascontiguousarray(ly.K[:, cols, :])
-    want, bound = _oracle(ly, reduce, K=Ks, L=len(cols))
-    _assert_raw_close(got[:, cols], want, bound, "sampled columns")
+    want, bound = _oracle(ly, reduce)
+    _assert_raw_close(got[:, :L], want, bound, "every column")
     assert np.isfinite(got).all()
 
 
