@@ -251,6 +251,22 @@ def summarize_profiles(out_dir, workload="mistral128k"):
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
         out = {k: st.median(v) for k, v in per.items()}
+        if workload == "chunksel128k_uncached":
+            # the roofline covers the whole uncached select: the medians of the key-block
+            # mean launch (over K), the query-block mean launch, the logits and the top-p
+            means, parts = [], {}
+            for r in rows:
+                n = r["Kernel_Name"]
+                if "block_mean_kernel" in n:
+                    means.append(float(r["Counter_Value"]))
+                for kn in ("block_logits_kernel", "block_topp_kernel"):
+                    if kn in n:
+                        parts.setdefault(kn, []).append(float(r["Counter_Value"]))
+            cut = (min(means) + max(means)) / 2
+            big = [v for v in means if v >= cut]
+            small = [v for v in means if v < cut] or [0.0]
+            out["kernel"] = (st.median(big) + st.median(small) +
+                             sum(st.median(v) for v in parts.values()))
         if workload == "delta32x8k":
             # the roofline covers the whole call: the sum of its three kernels' medians
             parts = {}
