@@ -66,7 +66,7 @@ WORKLOADS = {
     "llama32k": ("kvs_llama32k_kernel_stats.md", "score_colsum_llama32k_traffic.txt",
                  "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
     "cross32x16k": ("kvs_cross32x16k_kernel_stats.md", "score_colsum_cross32x16k_traffic.txt",
-                    "score_colsum", "32 x kvs_score (ALL_SUM) + kvs_aggregate_layers (SUM_L1)"),
+                    "score_colsum", "32 x kvs_score (GROUP_SUM) + kvs_aggregate_layers (SUM_L1)"),
     "gemfilter128k": ("kvs_gemfilter128k_kernel_stats.md", "score_raw_gemfilter128k_traffic.txt",
                       "score_raw", "score_raw_kernel (kvs_score_raw, SUM over heads, W = 1)"),
     "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
@@ -193,7 +193,7 @@ WORKLOAD_TITLES = {
     "mistral128k": "Mistral-7B GQA layer at L = 131072, softmax window scores + cluster top-k",
     "llama32k": "Llama-3.1-8B GQA layer at L = 32768, softmax window scores + max-pool 7 top-k",
     "cross32x16k": "32 layers of the Llama-3.1-8B GQA shape at L = 16384, per-layer scores summed over "
-                   "every head, L1-normalised sum over layers, top 20%",
+                   "the heads, L1-normalised sum over layers, top 20%",
     "gemfilter128k": "Mistral-7B GQA layer at L = 131072, GemFilter raw last-token scores + pooled top-k",
     "specprefill128k": "Mistral-7B GQA layer at L = 131072, Speculative-Prefill raw scores (8 lookahead "
                        "queries) + mean, pool and top-k",
@@ -1150,10 +1150,11 @@ def bench_softmax(args):
 
 def bench_cross(args):
     """Cross-layer aggregation over 32 layers of the Llama-3.1-8B GQA shape at
-    L = 16384: each layer's window score summed over every head (kvs_score
-    ALL_SUM, phase 0), L1-normalised and summed over the layers
-    (kvs_aggregate_layers SUM_L1), then the top 20% of the tokens (kvs_topk).
-    A step is the whole 32-layer pass; tokens/s = 32 * L / t."""
+    L = 16384: each layer's window scores per KV group (kvs_score GROUP_SUM,
+    phase 0), summed over the groups, L1-normalised and added over the layers
+    by kvs_aggregate_layers (SUM_L1, which sums its H rows first), then the top
+    20% of the tokens (kvs_topk).  A step is the whole 32-layer pass; tokens/s =
+    32 * L / t."""
     import torch
     import synth
     import prompt_token_importance_amd as kvs
@@ -1169,10 +1170,10 @@ def bench_cross(args):
         f"{sum(k.numel() for k in Ks) * 2 / 2**20:.0f} MiB)")
     budget = (2 * L) // 10
     a = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=layers[0].q_pos0,
-                       heads=kvs.HEADS_ALL_SUM)
+                       heads=kvs.HEADS_GROUP_SUM)
     ws_bytes = kvs.kvs_score_workspace(a)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    row = torch.empty(1, L, dtype=torch.float32, device="cuda")
+    row = torch.empty(H_kv, L, dtype=torch.float32, device="cuda")
     acc = torch.empty(1, L, dtype=torch.float32, device="cuda")
     idx = torch.empty(1, budget, dtype=torch.int32, device="cuda")
     ag_bytes = lib.kvs_aggregate_workspace(L)
@@ -1194,7 +1195,7 @@ def bench_cross(args):
             ev[0].record(stream)
         for l in range(n_layers):
             st |= lib.kvs_score(ra, pQs[l], pKs[l], prow, pws, ws_bytes, sp)
-            st |= lib.kvs_aggregate_layers(pacc, prow, 1, L, L, kvs.RED_SUM_L1, int(l == 0), pag,
+            st |= lib.kvs_aggregate_layers(pacc, prow, H_kv, L, L, kvs.RED_SUM_L1, int(l == 0), pag,
                                            ag_bytes, sp)
         if ev is not None:
             ev[1].record(stream)
@@ -1231,8 +1232,9 @@ def bench_cross(args):
         return e0.elapsed_time(e1) / args.steps
 
     copy_gbs = copy_calibration(timed) if args.copy_calibration else None
-    # algorithmic bytes of the 32-layer pass: every layer's K and Q once, one score row per layer
-    alg_bytes = n_layers * (H_kv * L * d_k * 2 + H_q * W * d_k * 2 + L * 4)
+    # algorithmic bytes of the 32-layer pass: every layer's K and Q once, one score row per
+    # KV group and layer
+    alg_bytes = n_layers * (H_kv * L * d_k * 2 + H_q * W * d_k * 2 + H_kv * L * 4)
     achieved = alg_bytes / (layers_ms * 1e-3) / 1e9
     stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
     out = {
@@ -1250,8 +1252,8 @@ def bench_cross(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "cross_layer_32x16k: 32 layers, H_q=32 H_kv=8 d_k=128 L=16384 W=32; "
-                               "per-layer score summed over every head -> L1-normalised sum over "
-                               "layers -> top 20% (3276)", "layers": n_layers, "L": L, "W": W,
+                               "per-layer score per KV group, summed over the groups -> L1-normalised "
+                               "sum over layers -> top 20% (3276)", "layers": n_layers, "L": L, "W": W,
                    "budget": budget},
         "roofline": {
             "kernel": label,
