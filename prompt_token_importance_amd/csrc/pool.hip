@@ -123,28 +123,32 @@ __global__ __launch_bounds__(kThreads) void cluster_kernel(const float* __restri
   prio[(int64_t)row * n + t] = hit;
 }
 
-constexpr int kAggThreads = 256;
-constexpr int kAggItems = 8;
-constexpr int kAggTile = kAggThreads * kAggItems;
+constexpr int kAggThreads = 256;   // one token per thread
+constexpr int kAggBatch = 8;       // head rows loaded together
 
+// Sum over the H rows of token t, left to right in float32; the rows are
+// loaded kAggBatch at a time so their latencies overlap.
 __device__ __forceinline__ float head_sum(const float* S, int H, int64_t ld, int t) {
-  float v = S[t];
-  for (int h = 1; h < H; ++h) v += S[(int64_t)h * ld + t];
+  float v = 0.f;
+  for (int h0 = 0; h0 < H; h0 += kAggBatch) {
+    float x[kAggBatch];
+#pragma unroll
+    for (int i = 0; i < kAggBatch; ++i) x[i] = h0 + i < H ? S[(int64_t)(h0 + i) * ld + t] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kAggBatch; ++i)
+      if (h0 + i < H) v = h0 + i == 0 ? x[i] : v + x[i];
+  }
   return v;
 }
 
-// Partial L1 norms, one float64 per workgroup, in a fixed order.
+// Partial L1 norms, one float64 per workgroup (a fixed-order tree over its
+// tokens).
 __global__ __launch_bounds__(kAggThreads) void agg_norm_kernel(const float* __restrict__ S, int H,
                                                                int n, int64_t ld,
                                                                double* __restrict__ part) {
   __shared__ double red[kAggThreads];
-  const int base = blockIdx.x * kAggTile;
-  double s = 0.0;
-  for (int k = 0; k < kAggItems; ++k) {
-    const int t = base + k * kAggThreads + threadIdx.x;
-    if (t < n) s += fabs((double)head_sum(S, H, ld, t));
-  }
-  red[threadIdx.x] = s;
+  const int t = blockIdx.x * kAggThreads + threadIdx.x;
+  red[threadIdx.x] = t < n ? fabs((double)head_sum(S, H, ld, t)) : 0.0;
   __syncthreads();
   for (int w = kAggThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
@@ -153,26 +157,34 @@ __global__ __launch_bounds__(kAggThreads) void agg_norm_kernel(const float* __re
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
+// acc (=|+=|max) the head sum of token t, SUM_L1 scaled by 1 / (sum of the
+// partial norms).  The first wave adds the partials: lane l the partials
+// l, l + 64, ... in order, then the lanes in a fixed tree, so every workgroup
+// and every call gets the same norm.
 __global__ __launch_bounds__(kAggThreads) void agg_apply_kernel(
     float* __restrict__ acc, const float* __restrict__ S, int H, int n, int64_t ld, int mode,
     int first, const double* __restrict__ part, int n_part) {
+  __shared__ float inv_norm_s;
+  const int t = blockIdx.x * kAggThreads + threadIdx.x;
+  const float s = t < n ? head_sum(S, H, ld, t) : 0.f;
   float inv_norm = 0.f;
   if (mode == KVS_RED_SUM_L1) {
-    double norm = 0.0;
-    for (int i = 0; i < n_part; ++i) norm += part[i];
-    inv_norm = (float)(1.0 / norm);
-  }
-  const int base = blockIdx.x * kAggTile;
-  for (int k = 0; k < kAggItems; ++k) {
-    const int t = base + k * kAggThreads + threadIdx.x;
-    if (t >= n) continue;
-    const float s = head_sum(S, H, ld, t);
-    if (mode == KVS_RED_SUM_L1) {
-      const float v = s * inv_norm;
-      acc[t] = first ? v : acc[t] + v;
-    } else {
-      acc[t] = first ? s : fmaxf(acc[t], s);
+    if (threadIdx.x < 64) {
+      double norm = 0.0;
+      for (int i = threadIdx.x; i < n_part; i += 64) norm += part[i];
+#pragma unroll
+      for (int d = 32; d > 0; d >>= 1) norm += __shfl_xor(norm, d);
+      if (threadIdx.x == 0) inv_norm_s = (float)(1.0 / norm);
     }
+    __syncthreads();
+    inv_norm = inv_norm_s;
+  }
+  if (t >= n) return;
+  if (mode == KVS_RED_SUM_L1) {
+    const float v = s * inv_norm;
+    acc[t] = first ? v : acc[t] + v;
+  } else {
+    acc[t] = first ? s : fmaxf(acc[t], s);
   }
 }
 
@@ -202,13 +214,13 @@ kvs_status cluster_priority_run(const float* page, const int32_t* page_arg, int 
 }
 
 size_t aggregate_ws_bytes(int n) {
-  const size_t blocks = ((size_t)n + kAggTile - 1) / kAggTile;
+  const size_t blocks = ((size_t)n + kAggThreads - 1) / kAggThreads;
   return align_up(blocks * sizeof(double), kWsAlign);
 }
 
 kvs_status aggregate_run(float* acc, const float* S, int H, int n, int64_t ld, int mode, int first,
                          void* ws, hipStream_t stream) {
-  const int blocks = (n + kAggTile - 1) / kAggTile;
+  const int blocks = (n + kAggThreads - 1) / kAggThreads;
   double* part = static_cast<double*>(ws);
   if (mode == KVS_RED_SUM_L1)
     hipLaunchKernelGGL(agg_norm_kernel, dim3(blocks), dim3(kAggThreads), 0, stream, S, H, n, ld, part);

@@ -1318,8 +1318,15 @@ __global__ __launch_bounds__(256) void score_head_sum_kernel(const float* __rest
                                                              int accumulate) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= L) return;
-  float v = rows[t];
-  for (int g = 1; g < H; ++g) v += rows[(int64_t)g * rows_ld + t];
+  float v = 0.f;
+  for (int g0 = 0; g0 < H; g0 += 8) {   // 8 rows loaded together, added in order
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = g0 + i < H ? rows[(int64_t)(g0 + i) * rows_ld + t] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (g0 + i < H) v = g0 + i == 0 ? x[i] : v + x[i];
+  }
   store_out(S + t, v, accumulate);
 }
 
@@ -1334,7 +1341,13 @@ __global__ __launch_bounds__(256) void score_head_max_kernel(const float* __rest
   if (t >= L) return;
   const float* r = rows + (int64_t)g * G * rows_ld + t;
   float mx = r[0];
-  for (int h = 1; h < G; ++h) mx = fmaxf(mx, r[(int64_t)h * rows_ld]);
+  for (int h0 = 1; h0 < G; h0 += 8) {   // 8 rows loaded together
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = h0 + i < G ? r[(int64_t)(h0 + i) * rows_ld] : mx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  }
   store_out(S + (int64_t)g * s_ld + t, mx, accumulate);
 }
 
