@@ -29,11 +29,15 @@
 //    of the key range; each pass-2 workgroup folds the splits of its group's
 //    rows by log-sum-exp into one constant b_r = m_r + log2 Z_r per row (+inf
 //    for padding rows) before its tile loop.
-//  * Pass 2 recomputes the tile, forms p = exp2(x - b_r) (no division), adds
-//    the rows a lane holds, transposes the 32 x 32 tile of partial sums
-//    through a per-wave LDS buffer and adds across lanes.  Every output element
-//    is written by exactly one lane, in a fixed order: results are
-//    bit-reproducible and no atomics are used.
+//  * Pass 2 (sums over every row of the group) recomputes the tile with the
+//    MFMA operands swapped, so a lane holds one key against 16 rows of each
+//    row tile, and a ninth k-step adds each row's -b_r (scaled and split into
+//    three bf16 parts) to its logits on the matrix cores.  It forms
+//    p = exp2(c * acc) (no division), sums the rows inside the lane and
+//    across the two lane halves, and stores one score per key.  Every output
+//    element is written by exactly one lane, in a fixed order: results are
+//    bit-reproducible and no atomics are used.  Per-head sums take a
+//    non-pipelined path with an LDS transpose.
 //  * No R x L logit matrix is ever stored: K is read once per pass.
 #include <math.h>
 
@@ -51,7 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStride = 36;  // floats per row of the LDS transpose buffers
+constexpr int kStride = 36;  // floats per row of the per-head LDS transpose buffers
 constexpr int kStages = 4;   // K tiles per wave in the LDS ring
 static_assert((kStages & (kStages - 1)) == 0, "ring stages are indexed with a mask");
 constexpr float kNegInf = -__builtin_inff();
@@ -149,16 +153,6 @@ __device__ __forceinline__ void ds_read_b128(u32x4& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
 }
 
-template <int OFF>
-__device__ __forceinline__ void ds_read_b32(float& v, uint32_t addr) {
-  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
-}
-
-template <int OFF>
-__device__ __forceinline__ void ds_write_b128(uint32_t addr, const f32x4& v) {
-  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_lgkm(u32x4 (&v)[N]) {
   if constexpr (N == 8)
@@ -167,13 +161,6 @@ __device__ __forceinline__ void wait_lgkm(u32x4 (&v)[N]) {
                    "+v"(v[6]), "+v"(v[7]));
   else
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
-}
-
-__device__ __forceinline__ void wait_lgkm16(float (&v)[16]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
-                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
-                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
 }
 
 template <int KS>
@@ -376,22 +363,6 @@ __device__ __forceinline__ void mfma_all_a(f32x16 (&acc)[NT], const u32x4 (&f)[D
     }
 }
 
-// Probabilities of a full tile (no masking) summed over rows LO .. LO+N-1.
-template <int NT, int LO, int N, bool ADD>
-__device__ __forceinline__ void probs_full(const f32x16 (&acc)[N > 0 ? N : 1], float (&part)[16],
-                                           const float (&b)[NT], float c) {
-  if constexpr (!ADD) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) part[i] = 0.f;
-  }
-  if constexpr (N > 0) {
-#pragma unroll
-    for (int T = 0; T < N; ++T)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) part[i] += ex2(fmaf(acc[T][i], c, -b[LO + T]));
-  }
-}
-
 // Online (max, sum of exp2) update of query rows LO .. LO+N-1 for one tile.
 // The running max m only stabilises the exponentials, so it may lag the true
 // max: terms are summed against the current m, and m is refreshed (the whole
@@ -454,27 +425,6 @@ __device__ __forceinline__ void stats_part(const f32x16 (&acc)[N > 0 ? N : 1], f
         }
       }
     }
-  }
-}
-
-// Probabilities of query rows LO .. LO+N-1 for one tile, summed over those
-// rows into part[] (ADD: part += ..., else part = ...).
-template <int NT, int LO, int N, bool ADD>
-__device__ __forceinline__ void probs_part(const f32x16 (&acc)[N > 0 ? N : 1], float (&part)[16],
-                                           const float (&b)[NT], float c, bool full, int t0,
-                                           int hl, const int (&vis)[NT]) {
-  if constexpr (!ADD) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) part[i] = 0.f;
-  }
-  if constexpr (N > 0) {
-#pragma unroll
-    for (int T = 0; T < N; ++T)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = ex2(fmaf(acc[T][i], c, -b[LO + T]));
-        part[i] += (full || t0 + key_of(i, hl) <= vis[LO + T]) ? e : 0.f;
-      }
   }
 }
 
@@ -569,6 +519,70 @@ __device__ __forceinline__ void pipe_step(f32x16 (&accC)[NT], f32x16 (&accP)[NT]
       work(e / 16, e % 16, accP[e / 16][e % 16]);
     }
     side(k, M);
+    if constexpr (ISSUE) {
+#pragma unroll
+      for (int jj = 0; jj < KS; ++jj)
+        if (SL::issue(jj) == k) issue_chunk_full<D>(issue_stage, issue_base, kts, coff, jj);
+    }
+    if constexpr (NEXT) {
+      if (k == SL::kWait) wait_vm<WAITN>();
+#pragma unroll
+      for (int jj = 0; jj < KS; ++jj)
+        if (SL::read(jj) == k) ds_read_b128_a<0>(fn[jj], next_stage + foff[jj]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (NEXT) wait_lgkm_a<KS>(fn);
+}
+
+// Swapped-operand tile: A = query fragments, B = K fragments, then a ninth
+// k-step A = the rows' -b/c parts, B = ones.  acc[T] = (x - b/c) for rows
+// 32T + 8(i/4) + 4hl + i%4 against key lane % 32.
+__device__ __forceinline__ void mfma_rows(f32x16& acc, const bf16x8& qa, const u32x4& kf, bool zero) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, __builtin_bit_cast(bf16x8, kf),
+                                               zero ? f32x16{} : acc, 0, 0, 0);
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void mfma_rows_all(f32x16 (&acc)[NT], const u32x4 (&f)[D / 16],
+                                              const bf16x8 (&q)[NT][D / 16],
+                                              const bf16x8 (&qx)[NT], const bf16x8& ones) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int T = 0; T < NT; ++T) mfma_rows(acc[T], q[T][s], f[s], s == 0);
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+    acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qx[T], ones, acc[T], 0, 0, 0);
+}
+
+// pipe_step for the swapped-operand tile: (KS + 1) * NT MFMA slots, the
+// 16 * NT elements of the previous tile spread over them.
+template <int D, int NT, bool ISSUE, bool NEXT, int WAITN, typename Work>
+__device__ __forceinline__ void pipe_step_rows(f32x16 (&accC)[NT], f32x16 (&accP)[NT],
+                                               const u32x4 (&fc)[D / 16], u32x4 (&fn)[D / 16],
+                                               const bf16x8 (&q)[NT][D / 16],
+                                               const bf16x8 (&qx)[NT], const bf16x8& ones,
+                                               uint8_t* issue_stage, const uint8_t* issue_base,
+                                               int64_t kts,
+                                               const uint32_t (&coff)[ChunkGeom<D>::NQ],
+                                               uint32_t next_stage,
+                                               const uint32_t (&foff)[D / 16], Work&& work) {
+  constexpr int KS = D / 16;
+  constexpr int M = (KS + 1) * NT;
+  constexpr int E = 16 * NT;
+  using SL = StepSlots<M, KS>;
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    if (k < KS * NT) {
+      const int s = k / NT, T = k % NT;
+      mfma_rows(accC[T], q[T][s], fc[s], s == 0);
+    } else {
+      const int T = k - KS * NT;
+      accC[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qx[T], ones, accC[T], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = (k * E) / M; e < ((k + 1) * E) / M; ++e) work(e / 16, e % 16, accP[e / 16][e % 16]);
     if constexpr (ISSUE) {
 #pragma unroll
       for (int jj = 0; jj < KS; ++jj)
@@ -890,7 +904,21 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   } else {
     load_q<D, NT>(q, vis, a, g, lane);
   }
-  // row constants from pass 1's split statistics
+  // last visible key of every padded row (-1 for padding rows), for the
+  // masked tiles of the swapped-operand column sums
+  __shared__ __attribute__((aligned(16))) int rvis[128];
+  if constexpr (MODE == 0) {
+    if (threadIdx.x < 32 * NT) {
+      const int r = a.row0 + threadIdx.x;
+      const int hq = r / a.head_rows, jr = r % a.head_rows;
+      const int64_t pos = a.p.q_pos0 + jr;
+      rvis[threadIdx.x] = hq < a.p.G && jr < a.p.W
+                              ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1)
+                              : -1;
+    }
+  }
+  // row constants from pass 1's split statistics (the merge's barrier also
+  // orders rvis)
   __shared__ float brow[128];
   merge_rows(a, g, 32 * NT, brow);
   float b[NT];
@@ -898,7 +926,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
   __builtin_amdgcn_s_waitcnt(0);   // Q, the first tile and the row constants are in
 
-  __shared__ float tr[kWaves][32 * kStride];
+  __shared__ float tr[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * kStride : 1];
   __shared__ float hacc[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * 32 : 1];
   float* wl = tr[wave];
 
@@ -911,53 +939,51 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const int k = lane & 31;
   const auto tile_at = [&](int x) { return tb + wave + (a.rev ? nt - 1 - x : x) * kWaves; };
   if constexpr (MODE == 0) {
+    // Column sums with the MFMA operands swapped: A = the query rows, B = the
+    // K fragments, so lane l holds key l % 32 of the tile against 16 rows of
+    // each row tile, and a key's sum over rows is a sum inside the lane plus
+    // one exchange between the lane halves.  Each row's constant b enters the
+    // MFMA as a ninth k-step: the rows carry -b/c split into three bf16 parts
+    // (about 24 bits), the keys carry ones, so the accumulators hold x - b/c
+    // and p = exp2(c * acc).
     constexpr int KS = D / 16;
     const uint32_t ring0 = lds_addr(ring[wave][0]);
-    // column sums of one tile's probabilities (part[i]: key 8(i/4) + 4hl + i%4,
-    // summed over this lane's rows) -> transpose through this wave's LDS buffer
-    // -> one store per key.  In the pipeline the LDS writes and reads run
-    // inside the next step's MFMA slots (flush_side) and only the adds and the
-    // store follow it (flush_finish).
-    const uint32_t waddr = lds_addr(wl) + (nl * kStride + 4 * hl) * 4;
-    const uint32_t raddr = lds_addr(wl) + (16 * hl * kStride + k) * 4;
-    float r[16];
-    const auto flush_write = [&](const float (&part)[16]) {
-      ds_write_b128<0>(waddr, f32x4{part[0], part[1], part[2], part[3]});
-      ds_write_b128<32>(waddr, f32x4{part[4], part[5], part[6], part[7]});
-      ds_write_b128<64>(waddr, f32x4{part[8], part[9], part[10], part[11]});
-      ds_write_b128<96>(waddr, f32x4{part[12], part[13], part[14], part[15]});
-    };
-    const auto read_pair = [&](auto pc) {
-      constexpr int P = decltype(pc)::value;
-      ds_read_b32<(2 * P) * kStride * 4>(r[2 * P], raddr);
-      ds_read_b32<(2 * P + 1) * kStride * 4>(r[2 * P + 1], raddr);
-    };
-    const auto read_all = [&]() {
-      read_pair(std::integral_constant<int, 0>{});
-      read_pair(std::integral_constant<int, 1>{});
-      read_pair(std::integral_constant<int, 2>{});
-      read_pair(std::integral_constant<int, 3>{});
-      read_pair(std::integral_constant<int, 4>{});
-      read_pair(std::integral_constant<int, 5>{});
-      read_pair(std::integral_constant<int, 6>{});
-      read_pair(std::integral_constant<int, 7>{});
-    };
-    const auto flush_finish = [&](int t0) {
-      wait_lgkm16(r);
+    bf16x8 qx[NT];
+    bf16x8 ones{};
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      qx[T] = bf16x8{};
+      if (hl == 0) {
+        const float v = -b[T] / c;
+        if (v == kNegInf || v == kPosInf) {
+          qx[T][0] = (__bf16)v;
+        } else {
+          const __bf16 h1 = (__bf16)v;
+          const float r1 = v - (float)h1;
+          const __bf16 h2 = (__bf16)r1;
+          const __bf16 h3 = (__bf16)(r1 - (float)h2);
+          qx[T][0] = h1;
+          qx[T][1] = h2;
+          qx[T][2] = h3;
+        }
+      }
+    }
+    if (hl == 0) {
+      ones[0] = (__bf16)1.f;
+      ones[1] = (__bf16)1.f;
+      ones[2] = (__bf16)1.f;
+    }
+    // sums of one tile's probabilities: 2 per row tile, then the lane halves
+    const auto finish = [&](float (&pc)[2 * NT], int t0) {
       float v = 0.f;
 #pragma unroll
-      for (int n = 0; n < 16; ++n) v += r[n];
-      v += __shfl_xor(v, 32);
-      const int tt = t0 + k;
+      for (int u = 0; u < 2 * NT; ++u) v += pc[u];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                       false, false);
+      v += __uint_as_float(sw[1]);
+      const int tt = t0 + nl;
       if (hl == 0 && tt < L) store_out(a.out + (int64_t)g * a.out_ld + tt, v, a.acc);
     };
-    const auto flush = [&](const float (&part)[16], int t0) {
-      flush_write(part);
-      read_all();
-      flush_finish(t0);
-    };
-    // The full tiles run the software pipeline (in reverse order when a.rev);
-    // the masked ones (causal window, ragged end) follow one at a time.
     if (nf > 0) {
       const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
       uint32_t coff[ChunkGeom<D>::NQ];
@@ -973,7 +999,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         wait_vm<0>();
       read_frags_a<KS>(f0, ring0, foff);
       wait_lgkm_a<KS>(f0);
-      mfma_all_a<D, NT>(acc0, f0, q);
+      mfma_rows_all<D, NT>(acc0, f0, q, qx, ones);
       if (nf > 1) {
         if (pre == S)
           wait_vm<(S - 2) * KS>();
@@ -982,88 +1008,89 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
         read_frags_a<KS>(f1, ring0 + tile_bytes<D>(), foff);
         wait_lgkm_a<KS>(f1);
       }
-      float partA[16], partB[16], nb[NT];
+      // step x: MFMAs of tile x || probabilities of tile x-1, whose sums
+      // are stored after the step
+      const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
+                            u32x4(&fn)[KS], int x) {
+        float pc[2 * NT];
 #pragma unroll
-      for (int T = 0; T < NT; ++T) nb[T] = -b[T];
-      // step x: MFMAs of tile x || probabilities of tile x-1 into pc; with
-      // FL, the LDS transpose of tile x-2's sums pp runs in the same slots and
-      // its store follows the step
-      const auto step = [&](auto fl, f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
-                            u32x4(&fn)[KS], float(&pc)[16], const float(&pp)[16], int x) {
-        constexpr bool FL = decltype(fl)::value;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) pc[i2] = 0.f;
-        const auto work = [&](int T, int i2, float v) {
-          pc[i2] += ex2(fmaf(v, c, nb[T]));
-        };
-        const auto side = [&](int kk, int M) {
-          if constexpr (FL) {
-            if (kk == 0) flush_write(pp);
-            // the 8 read pairs in slots 1..8 (the last slot when M is small)
-            const auto at = [&](int pr) { return 1 + pr < M ? 1 + pr : M - 1; };
-            if (at(0) == kk) read_pair(std::integral_constant<int, 0>{});
-            if (at(1) == kk) read_pair(std::integral_constant<int, 1>{});
-            if (at(2) == kk) read_pair(std::integral_constant<int, 2>{});
-            if (at(3) == kk) read_pair(std::integral_constant<int, 3>{});
-            if (at(4) == kk) read_pair(std::integral_constant<int, 4>{});
-            if (at(5) == kk) read_pair(std::integral_constant<int, 5>{});
-            if (at(6) == kk) read_pair(std::integral_constant<int, 6>{});
-            if (at(7) == kk) read_pair(std::integral_constant<int, 7>{});
-          }
-        };
+        for (int u = 0; u < 2 * NT; ++u) pc[u] = 0.f;
+        const auto work = [&](int T, int i, float v) { pc[2 * T + (i & 1)] += ex2(v * c); };
         const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
         if (x + S - 1 < nf)
-          pipe_step<D, NT, true, true, (S - 2) * KS>(
-              accC, accP, fc, fn, q, stage_of(x + S - 1),
+          pipe_step_rows<D, NT, true, true, (S - 2) * KS>(
+              accC, accP, fc, fn, q, qx, ones, stage_of(x + S - 1),
               reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t0_of(x + S - 1) * kts * 2, kts,
-              coff, nxt, foff, work, side);
+              coff, nxt, foff, work);
         else if (x + 1 < nf)
-          pipe_step<D, NT, false, true, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
-                                           nxt, foff, work, side);
+          pipe_step_rows<D, NT, false, true, 0>(accC, accP, fc, fn, q, qx, ones, nullptr, nullptr,
+                                                kts, coff, nxt, foff, work);
         else
-          pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
-                                            nxt, foff, work, side);
-        if constexpr (FL) flush_finish(t0_of(x - 2));
+          pipe_step_rows<D, NT, false, false, 0>(accC, accP, fc, fn, q, qx, ones, nullptr,
+                                                 nullptr, kts, coff, nxt, foff, work);
+        finish(pc, t0_of(x - 1));
       };
-      using NoFl = std::integral_constant<bool, false>;
-      using Fl = std::integral_constant<bool, true>;
-      // partB holds the sums of odd steps, partA of even ones
-      if (nf > 1) step(NoFl{}, acc1, acc0, f1, f0, partB, partA, 1);
-      int x = 2;
+      int x = 1;
       for (; x + 1 < nf; x += 2) {
-        step(Fl{}, acc0, acc1, f0, f1, partA, partB, x);
-        step(Fl{}, acc1, acc0, f1, f0, partB, partA, x + 1);
+        step(acc1, acc0, f1, f0, x);
+        step(acc0, acc1, f0, f1, x + 1);
       }
-      if (x < nf) step(Fl{}, acc0, acc1, f0, f1, partA, partB, x);
-      // sums of tile nf-2 (computed by step nf-1, not yet flushed), then the
-      // last tile's
-      if (nf > 1) {
-        if ((nf - 1) & 1)
-          flush(partB, t0_of(nf - 2));
-        else
-          flush(partA, t0_of(nf - 2));
-      }
+      if (x < nf) step(acc1, acc0, f1, f0, x);
+      // the last full tile's sums
       const auto tail = [&](f32x16(&accP)[NT]) {
-        probs_full<NT, 0, NT, false>(accP, partA, b, c);
-        flush(partA, t0_of(nf - 1));
+        float pc[2 * NT];
+#pragma unroll
+        for (int T = 0; T < NT; ++T) {
+          float sa = 0.f, sb = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            sa += ex2(accP[T][i] * c);
+            sb += ex2(accP[T][i + 1] * c);
+          }
+          pc[2 * T] = sa;
+          pc[2 * T + 1] = sb;
+        }
+        finish(pc, t0_of(nf - 1));
       };
       if ((nf - 1) & 1)
         tail(acc1);
       else
         tail(acc0);
     }
+    // masked tiles (causal window, ragged end): key nl of the tile against
+    // each row's last visible key
     for (int j = nf; j < nt; ++j) {
       f32x16 acc[NT];
       u32x4 f[KS];
-      float part[16];
       const int t0 = (tb + wave + j * kWaves) * 32;
       issue_tile<D>(ring[wave][0], kbase, kts, t0, L, lane);
       wait_vm<0>();
       read_frags<KS>(f, ring0, foff);
       wait_lgkm<KS>(f);
-      mfma_part<D, NT, 0, NT>(acc, f, q);
-      probs_part<NT, 0, NT, false>(acc, part, b, c, false, t0, hl, vis);
-      flush(part, t0);
+      mfma_rows_all<D, NT>(acc, f, q, qx, ones);
+      float pc[2 * NT];
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int4 vv = *reinterpret_cast<const int4*>(&rvis[32 * T + 8 * i4 + 4 * hl]);
+          const int vr[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+          for (int i1 = 0; i1 < 4; ++i1) {
+            const int i = 4 * i4 + i1;
+            const float e = ex2(acc[T][i] * c);
+            const float pv = (t0 + nl <= vr[i1]) ? e : 0.f;
+            if (i & 1)
+              sb += pv;
+            else
+              sa += pv;
+          }
+        }
+        pc[2 * T] = sa;
+        pc[2 * T + 1] = sb;
+      }
+      finish(pc, t0);
     }
   } else {
     for (int i = 0; i < S - 1 && i < nt; ++i)
