@@ -20,12 +20,12 @@
 //    j's logits (all N-tiles, k-major, fragments in AGPRs), the VALU works on
 //    tile j-1's logits, two of them per MFMA slot; tile j+3's loads go out
 //    together in the first slot and tile j+1's fragments are read together
-//    after the wait in the middle one.  Causally masked and ragged tiles take a separate exact path.
+//    after the wait in the middle one.  Causally masked and ragged tiles take
+//    a separate exact path.
 //  * Pass 1 keeps, per lane and query row, sums of exp2(x - m) over the keys
 //    it sees, in log2 units (x = s * scale * log2 e), against a max m fixed
 //    from the wave's first tile, so the pipeline carries no branch; a wave
-//    whose sums overflow [0, 2^64] redoes its tiles with the exact online
-//    update.  Lane halves and waves are merged in LDS and written per split
+//    with a sum past 2^100 redoes its tiles with the exact online update.  Lane halves and waves are merged in LDS and written per split
 //    of the key range; each pass-2 workgroup folds the splits of its group's
 //    rows by log-sum-exp into one constant b_r = m_r + log2 Z_r per row (+inf
 //    for padding rows) before its tile loop.
@@ -607,8 +607,9 @@ __device__ __forceinline__ void pipe_step_rows(f32x16 (&accC)[NT], f32x16 (&accP
 // cores compute tile j's logits, the VALU sums tile j-1's exponentials
 // against a running max m that was set exactly from the wave's first tile
 // and never changes in the pipeline, so the sums need no branch.  A lane
-// whose tile sum leaves [0, 2^64] sets a flag; a wave with a flagged lane
-// recomputes its full tiles with the exact online update.  The few masked
+// whose row sum exceeds 2^100 (or is not finite) after the last full tile
+// sets a flag; a wave with a flagged lane recomputes its full tiles with the
+// exact online update.  The few masked
 // tiles (causal window, ragged end) use the exact update directly.
 template <int D, int NT>
 __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
@@ -699,18 +700,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     float sa[NT], sb[NT], nm[NT];
 #pragma unroll
     for (int T = 0; T < NT; ++T) nm[T] = -m[T];
-    bool flag = false;
 #pragma unroll
     for (int T = 0; T < NT; ++T) sa[T] = sb[T] = 0.f;
-    const auto commit = [&]() {
-#pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        const float s2 = sa[T] + sb[T];
-        flag |= !(s2 <= 0x1p64f);
-        z[T] += s2;
-        sa[T] = sb[T] = 0.f;
-      }
-    };
     const auto no_side = [](int, int) {};
     // step j: MFMAs of tile j (fc) || sums of tile j-1 (accP); loads of tile
     // j + S - 1 while it exists; then tile j + 1's fragments into fn.
@@ -733,7 +724,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
       else
         pipe_step<D, NT, false, false, 0>(accC, accP, fc, fn, q, nullptr, nullptr, kts, coff,
                                           nxt, foff, work, no_side);
-      commit();
     };
     int j = 1;
     for (; j + 1 < nf; j += 2) {
@@ -752,14 +742,25 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
           else
             sa[T] += ex2(fmaf(accP[T][i], c, -m[T]));
         }
-      commit();
     };
     if ((nf - 1) & 1)
       tail(acc1);
     else
       tail(acc0);
+    // The sums run over every full tile against the first tile's max.  A sum
+    // keeps its full relative precision however far the row's max rose above
+    // that reference; it only has to stay far enough inside the float range
+    // for the merges of lane halves, waves and splits (at most 2^27 partial
+    // sums of at most 2^100 each), and a term or sum past the range shows as
+    // inf or NaN, which fails the same test.
+    bool flag = false;
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      z[T] = sa[T] + sb[T];
+      flag |= !(z[T] <= 0x1p100f);
+    }
     if (__any(flag)) {
-      // some logit rose more than 64 (log2 units) above the first tile's max:
+      // some logit rose about 100 log2 units above the first tile's max:
       // redo the full tiles with the exact online update
 #pragma unroll
       for (int T = 0; T < NT; ++T) {

@@ -1,11 +1,14 @@
 """GPU parity against the fp64 oracle with outlier logits (attention-sink-like keys).
 
 The score statistics pass sums exp2 against a running maximum taken from each
-wave's first key tile, and a wave in which a later logit rises far above that
-maximum (so a sum would leave [0, 2^64]) redoes its tiles with the exact
-online update.  Seeded N(0,1) inputs never reach that branch; these cases plant
-keys whose logit exceeds every ordinary logit of some rows by about 60, 140
-and 420 (about 86, 202 and 606 in log2 units), in later tiles of several waves
+wave's first key tile.  A later logit far above that maximum either leaves the
+sums dominated by huge but representable terms (86 log2 units above it:
+terms near 2^86), or pushes a sum past 2^100 or out of the float range, and
+then the wave redoes its tiles with the exact online update (202 and 606
+log2 units).  Seeded N(0,1)
+inputs reach neither; these cases plant keys whose logit exceeds every
+ordinary logit of some rows by about 60, 140 and 420 (about 86, 202 and 606
+in log2 units), in later tiles of several waves
 and key splits, in a wave's first tile, inside the causal window and in the
 ragged last tile.  Every head mode, the split statistics/column-sum calls, the
 DELTA decode page scores and the raw-logit scores are checked against the
