@@ -29,15 +29,14 @@
 //    of the key range; each pass-2 workgroup folds the splits of its group's
 //    rows by log-sum-exp into one constant b_r = m_r + log2 Z_r per row (+inf
 //    for padding rows) before its tile loop.
-//  * Pass 2 (sums over every row of the group) recomputes the tile with the
-//    MFMA operands swapped, so a lane holds one key against 16 rows of each
-//    row tile, and a ninth k-step adds each row's -b_r (scaled and split into
-//    three bf16 parts) to its logits on the matrix cores.  It forms
-//    p = exp2(c * acc) (no division), sums the rows inside the lane and
-//    across the two lane halves, and stores one score per key.  Every output
-//    element is written by exactly one lane, in a fixed order: results are
-//    bit-reproducible and no atomics are used.  Per-head sums take a
-//    non-pipelined path with an LDS transpose.
+//  * Pass 2 recomputes the tile with the MFMA operands swapped, so a lane
+//    holds one key against 16 rows of each row tile, and a ninth k-step adds
+//    each row's -b_r (scaled and split into three bf16 parts) to its logits on
+//    the matrix cores.  It forms p = exp2(c * acc) (no division), sums the
+//    rows of the group, or of each head, inside the lane and across the two
+//    lane halves, and stores one score per key (per head, or their maximum).
+//    Every output element is written by exactly one lane, in a fixed order:
+//    results are bit-reproducible and no atomics are used.
 //  * No R x L logit matrix is ever stored: K is read once per pass.
 #include <math.h>
 
@@ -55,7 +54,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStride = 36;  // floats per row of the per-head LDS transpose buffers
 constexpr int kStages = 4;   // K tiles per wave in the LDS ring
 static_assert((kStages & (kStages - 1)) == 0, "ring stages are indexed with a mask");
 constexpr float kNegInf = -__builtin_inff();
@@ -72,21 +70,12 @@ struct KArgs {
   int h0, h1;     // query heads (inside the KV group) whose rows this launch holds
   int acc;        // column sums: 0 store, 1 add
   int per_head;   // MODE 1: 1 writes each head's row, 0 the maximum over the heads
-  float* out;     // MODE 1 output rows (S, or the per-head workspace rows)
+  float* out;     // output rows (S, or the per-group / per-head workspace rows)
   int64_t out_ld;
 };
 
-__device__ __forceinline__ bf16x8 load16(const uint16_t* ptr) {
-  u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ void lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
 
 // K tiles travel HBM -> LDS with gfx950's direct-to-LDS 16-byte loads, so
 // several tiles per wave are in flight without holding VGPRs.  Each wave owns
@@ -193,39 +182,6 @@ __device__ __forceinline__ void wait_lgkm_a(u32x4 (&v)[N]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]));
 }
 
-// Waits for the tile issued `ahead` tiles before the newest one.
-template <int D, int S>
-__device__ __forceinline__ void wait_tile(int ahead) {
-  constexpr int KS = D / 16;
-  if (S > 3 && ahead >= 3) wait_vm<3 * KS>();
-  else if (S > 2 && ahead == 2) wait_vm<2 * KS>();
-  else if (ahead == 1) wait_vm<KS>();
-  else wait_vm<0>();
-}
-
-// Query row fragments (B operand): N-tile T, lane l -> padded row 32T + l%32.
-template <int D, int NT>
-__device__ __forceinline__ void load_q(bf16x8 (&q)[NT][D / 16], int (&vis)[NT], const KArgs& a,
-                                       int g, int lane) {
-  const int nl = lane & 31, hl = lane >> 5;
-#pragma unroll
-  for (int T = 0; T < NT; ++T) {
-    const int r = a.row0 + 32 * T + nl;
-    const int hq = r / a.head_rows, j = r % a.head_rows;
-    const bool valid = hq < a.p.G && j < a.p.W;
-    const int64_t pos = a.p.q_pos0 + j;
-    vis[T] = valid ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1) : -1;
-    const uint16_t* qp =
-        a.p.Q + (int64_t)(g * a.p.G + (valid ? hq : 0)) * a.p.qhs + (int64_t)(valid ? j : 0) * a.p.qrs +
-        hl * (D / 2);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      bf16x8 v = load16(qp + 8 * s);
-      q[T][s] = valid ? v : bf16x8{};
-    }
-  }
-}
-
 // Last visible key of the padded query rows a lane holds (N-tile T, lane l ->
 // padded row 32T + l%32), -1 for padding rows.
 template <int NT>
@@ -291,25 +247,6 @@ __device__ __forceinline__ void read_q_agpr(bf16x8 (&q)[NT][D / 16], uint32_t ba
                      "+a"(q[T][5]), "+a"(q[T][6]), "+a"(q[T][7]));
     else
       asm volatile("s_waitcnt lgkmcnt(0)" : "+a"(q[T][0]), "+a"(q[T][1]), "+a"(q[T][2]), "+a"(q[T][3]));
-  }
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void tile_logits(f32x16 (&acc)[NT], const uint8_t* stage,
-                                            const bf16x8 (&q)[NT][D / 16],
-                                            const uint32_t (&off)[D / 16]) {
-  constexpr int KS = D / 16;
-  u32x4 f[KS];
-  read_frags<KS>(f, lds_addr(stage), off);
-  wait_lgkm<KS>(f);
-#pragma unroll
-  for (int T = 0; T < NT; ++T) acc[T] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const bf16x8 kf = __builtin_bit_cast(bf16x8, f[s]);
-#pragma unroll
-    for (int T = 0; T < NT; ++T)
-      acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[T][s], acc[T], 0, 0, 0);
   }
 }
 
@@ -866,8 +803,10 @@ __device__ __forceinline__ void store_out(float* o, float v, int accumulate) {
   *o = accumulate ? *o + v : v;
 }
 
-// MODE 0: sum over every row of the group (GROUP_SUM).
+// MODE 0: sum over every row of the group (GROUP_SUM, ALL_SUM's group rows,
+// and a query head whose rows span both row groups).
 // MODE 1: per query head sums (NONE) or their maximum (GROUP_MAX).
+// Both run the same swapped-operand pipeline; only the per-tile finish differs.
 template <int D, int NT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const int lane = threadIdx.x & 63;
@@ -880,7 +819,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const float c = a.p.c;
   const int L = a.p.L;
 
-  constexpr int S = MODE == 0 ? kStages : kStages - 1;
+  constexpr int S = kStages;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
   const int64_t kts = a.p.kts;
@@ -897,29 +836,21 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
 
   bf16x8 q[NT][D / 16];
-  int vis[NT];
-  if constexpr (MODE == 0) {
-    // The query rows (through every wave's last ring stage, see the pass-1
-    // kernel) and the first full tile load while the row constants are
-    // merged; the merge's barrier waits for all three.
-    q_vis<NT>(vis, a, lane);
-    if (wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
-    if (nf > 0) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
-  } else {
-    load_q<D, NT>(q, vis, a, g, lane);
-  }
+  // The query rows (through every wave's last ring stage, see the pass-1
+  // kernel) and the first full tile load while the row constants are merged;
+  // the merge's barrier waits for all three.
+  if (wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
+  if (nf > 0) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
   // last visible key of every padded row (-1 for padding rows), for the
-  // masked tiles of the swapped-operand column sums
+  // masked tiles
   __shared__ __attribute__((aligned(16))) int rvis[128];
-  if constexpr (MODE == 0) {
-    if (threadIdx.x < 32 * NT) {
-      const int r = a.row0 + threadIdx.x;
-      const int hq = r / a.head_rows, jr = r % a.head_rows;
-      const int64_t pos = a.p.q_pos0 + jr;
-      rvis[threadIdx.x] = hq < a.p.G && jr < a.p.W
-                              ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1)
-                              : -1;
-    }
+  if (threadIdx.x < 32 * NT) {
+    const int r = a.row0 + threadIdx.x;
+    const int hq = r / a.head_rows, jr = r % a.head_rows;
+    const int64_t pos = a.p.q_pos0 + jr;
+    rvis[threadIdx.x] = hq < a.p.G && jr < a.p.W
+                            ? (int)(pos < (int64_t)a.p.L - 1 ? pos : (int64_t)a.p.L - 1)
+                            : -1;
   }
   // row constants from pass 1's split statistics (the merge's barrier also
   // orders rvis)
@@ -930,19 +861,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
   __builtin_amdgcn_s_waitcnt(0);   // Q, the first tile and the row constants are in
 
-  __shared__ float tr[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * kStride : 1];
-  __shared__ float hacc[MODE == 1 ? kWaves : 1][MODE == 1 ? 32 * 32 : 1];
-  float* wl = tr[wave];
-
   uint32_t foff[D / 16];
   frag_offsets<D>(foff, lane);
-  if constexpr (MODE == 0) {
-    read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
-    __builtin_amdgcn_s_barrier();   // every wave has its copy before the stage is refilled
-  }
-  const int k = lane & 31;
-  const auto tile_at = [&](int x) { return tb + wave + (a.rev ? nt - 1 - x : x) * kWaves; };
-  if constexpr (MODE == 0) {
+  read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
+  __builtin_amdgcn_s_barrier();   // every wave has its copy before the stage is refilled
+  {
     // Column sums with the MFMA operands swapped: A = the query rows, B = the
     // K fragments, so lane l holds key l % 32 of the tile against 16 rows of
     // each row tile, and a key's sum over rows is a sum inside the lane plus
@@ -977,16 +900,71 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       ones[1] = (__bf16)1.f;
       ones[2] = (__bf16)1.f;
     }
-    // sums of one tile's probabilities: 2 per row tile, then the lane halves
-    const auto finish = [&](float (&pc)[2 * NT], int t0) {
-      float v = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2 * NT; ++u) v += pc[u];
+    // A tile's partial sums per lane: MODE 0 two per row tile (every row of
+    // the group is summed); MODE 1 one per block of 4 rows (rows 8q + 4hl ..
+    // 8q + 4hl + 3 of a row tile), the unit a head is made of.
+    constexpr int NPC = MODE == 0 ? 2 * NT : 4 * NT;
+    const auto pc_of = [](int T, int i) { return MODE == 0 ? 2 * T + (i & 1) : 4 * T + (i >> 2); };
+    // the partner lane's value (lane l xor 32)
+    const auto other_half = [&](float v) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                        false, false);
-      v += __uint_as_float(sw[1]);
+      return __uint_as_float(hl ? sw[0] : sw[1]);
+    };
+    const auto finish = [&](float (&pc)[NPC], int t0) {
       const int tt = t0 + nl;
-      if (hl == 0 && tt < L) store_out(a.out + (int64_t)g * a.out_ld + tt, v, a.acc);
+      if constexpr (MODE == 0) {
+        float v = 0.f;
+#pragma unroll
+        for (int u = 0; u < NPC; ++u) v += pc[u];
+        v += other_half(v);
+        if (hl == 0 && tt < L) store_out(a.out + (int64_t)g * a.out_ld + tt, v, a.acc);
+      } else {
+        // Heads are runs of head_rows consecutive padded rows (4, 8, 16 or a
+        // multiple of 32, inside one row group): with 4 a block is a whole
+        // head of its lane half; otherwise the two halves' blocks q of a row
+        // tile (rows 8q .. 8q+7) lie in one head, added across the halves,
+        // and a head is the run of such blocks in (T, q) order.
+        float mx = kNegInf;
+        const auto put = [&](int hq, float v, bool lane_ok) {
+          if (hq >= a.h0 && hq < a.h1) {
+            if (a.per_head) {
+              if (lane_ok && tt < L)
+                store_out(a.out + (int64_t)(g * a.p.G + hq) * a.out_ld + tt, v, a.acc);
+            } else {
+              mx = fmaxf(mx, v);
+            }
+          }
+        };
+        if (a.head_rows == 4) {
+#pragma unroll
+          for (int T = 0; T < NT; ++T)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb)
+              put((a.row0 + 32 * T + 8 * qb + 4 * hl) >> 2, pc[4 * T + qb], true);
+          if (!a.per_head) mx = fmaxf(mx, other_half(mx));
+        } else {
+          // a head's blocks are added inside the lane first, then once
+          // across the halves
+          int cur_h = a.row0 / a.head_rows;
+          float cur = 0.f;
+#pragma unroll
+          for (int T = 0; T < NT; ++T)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+              const int hq = (a.row0 + 32 * T + 8 * qb) / a.head_rows;
+              if (hq != cur_h) {
+                put(cur_h, cur + other_half(cur), hl == 0);
+                cur_h = hq;
+                cur = 0.f;
+              }
+              cur += pc[4 * T + qb];
+            }
+          put(cur_h, cur + other_half(cur), hl == 0);
+        }
+        if (!a.per_head && hl == 0 && tt < L)
+          store_out(a.out + (int64_t)g * a.out_ld + tt, mx, a.acc);
+      }
     };
     if (nf > 0) {
       const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
@@ -1016,10 +994,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       // are stored after the step
       const auto step = [&](f32x16(&accC)[NT], f32x16(&accP)[NT], const u32x4(&fc)[KS],
                             u32x4(&fn)[KS], int x) {
-        float pc[2 * NT];
+        float pc[NPC];
 #pragma unroll
-        for (int u = 0; u < 2 * NT; ++u) pc[u] = 0.f;
-        const auto work = [&](int T, int i, float v) { pc[2 * T + (i & 1)] += ex2(v * c); };
+        for (int u = 0; u < NPC; ++u) pc[u] = 0.f;
+        const auto work = [&](int T, int i, float v) { pc[pc_of(T, i)] += ex2(v * c); };
         const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
         if (x + S - 1 < nf)
           pipe_step_rows<D, NT, true, true, (S - 2) * KS>(
@@ -1042,18 +1020,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       if (x < nf) step(acc1, acc0, f1, f0, x);
       // the last full tile's sums
       const auto tail = [&](f32x16(&accP)[NT]) {
-        float pc[2 * NT];
+        float pc[NPC];
 #pragma unroll
-        for (int T = 0; T < NT; ++T) {
-          float sa = 0.f, sb = 0.f;
+        for (int u = 0; u < NPC; ++u) pc[u] = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            sa += ex2(accP[T][i] * c);
-            sb += ex2(accP[T][i + 1] * c);
-          }
-          pc[2 * T] = sa;
-          pc[2 * T + 1] = sb;
-        }
+        for (int T = 0; T < NT; ++T)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pc[pc_of(T, i)] += ex2(accP[T][i] * c);
         finish(pc, t0_of(nf - 1));
       };
       if ((nf - 1) & 1)
@@ -1072,10 +1045,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       read_frags<KS>(f, ring0, foff);
       wait_lgkm<KS>(f);
       mfma_rows_all<D, NT>(acc, f, q, qx, ones);
-      float pc[2 * NT];
+      float pc[NPC];
+#pragma unroll
+      for (int u = 0; u < NPC; ++u) pc[u] = 0.f;
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
-        float sa = 0.f, sb = 0.f;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int4 vv = *reinterpret_cast<const int4*>(&rvis[32 * T + 8 * i4 + 4 * hl]);
@@ -1084,77 +1058,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           for (int i1 = 0; i1 < 4; ++i1) {
             const int i = 4 * i4 + i1;
             const float e = ex2(acc[T][i] * c);
-            const float pv = (t0 + nl <= vr[i1]) ? e : 0.f;
-            if (i & 1)
-              sb += pv;
-            else
-              sa += pv;
+            pc[pc_of(T, i)] += (t0 + nl <= vr[i1]) ? e : 0.f;
           }
         }
-        pc[2 * T] = sa;
-        pc[2 * T + 1] = sb;
       }
       finish(pc, t0);
-    }
-  } else {
-    for (int i = 0; i < S - 1 && i < nt; ++i)
-      issue_tile<D>(ring[wave][i], kbase, a.p.kts, tile_at(i) * 32, L, lane);
-    for (int i = 0; i < nt; ++i) {
-      if (i + S - 1 < nt)
-        issue_tile<D>(ring[wave][(i + S - 1) % S], kbase, a.p.kts,
-                      tile_at(i + S - 1) * 32, L, lane);
-      wait_tile<D, S>(min(S - 1, nt - 1 - i));
-      const int tile = tile_at(i);
-      f32x16 acc[NT];
-      tile_logits<D, NT>(acc, ring[wave][i % S], q, foff);
-      const int t0 = tile * 32;
-      const bool full = t0 + 31 <= a.min_vis;
-      float p[NT][16];
-#pragma unroll
-      for (int T = 0; T < NT; ++T)
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) {
-          const float e = ex2(fmaf(acc[T][i2], c, -b[T]));
-          p[T][i2] = (full || t0 + key_of(i2, hl) <= vis[T]) ? e : 0.f;
-        }
-      const int t = t0 + k;
-      float* ha = hacc[wave];   // column sums of heads h0 .. h1-1, 32 keys each
-      for (int x = lane; x < (a.h1 - a.h0) * 32; x += 64) ha[x] = 0.f;
-#pragma unroll
-      for (int T = 0; T < NT; ++T) {
-#pragma unroll
-        for (int aa = 0; aa < 4; ++aa)
-          *reinterpret_cast<f32x4*>(&wl[nl * kStride + 8 * aa + 4 * hl]) =
-              f32x4{p[T][4 * aa], p[T][4 * aa + 1], p[T][4 * aa + 2], p[T][4 * aa + 3]};
-        lds_order();
-        const int r0 = a.row0 + 32 * T;   // padded row of the tile's first row
-        int h_first = r0 / a.head_rows;
-        h_first = h_first > a.h0 ? h_first : a.h0;
-        int h_last = (r0 + 31) / a.head_rows;
-        h_last = h_last < a.h1 - 1 ? h_last : a.h1 - 1;
-        for (int hq = h_first; hq <= h_last; ++hq) {
-          if ((hq & 1) != hl) continue;
-          int lo = hq * a.head_rows, hi = lo + a.p.W;
-          lo = lo > r0 ? lo : r0;
-          hi = hi < r0 + 32 ? hi : r0 + 32;
-          float v = 0.f;
-          for (int r = lo; r < hi; ++r) v += wl[(r - r0) * kStride + k];
-          ha[(hq - a.h0) * 32 + k] += v;
-        }
-        lds_order();
-      }
-      if (a.per_head) {
-        for (int hq = a.h0 + hl; hq < a.h1; hq += 2)
-          if (t < L)
-            store_out(a.out + (int64_t)(g * a.p.G + hq) * a.out_ld + t, ha[(hq - a.h0) * 32 + k],
-                      a.acc);
-      } else {
-        float mx = kNegInf;
-        for (int hq = a.h0 + hl; hq < a.h1; hq += 2) mx = fmaxf(mx, ha[(hq - a.h0) * 32 + k]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (hl == 0 && t < L) store_out(a.out + (int64_t)g * a.out_ld + t, mx, a.acc);
-      }
-      lds_order();
     }
   }
 }
