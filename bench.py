@@ -61,12 +61,12 @@ def parse():
 
 WORKLOADS = {
     # workload: (kernel-stats summary, traffic summary, kernel name fragment, kernel label)
-    "mistral128k": ("kvs_mistral128k_kernel_stats.md", "score_colsum_mistral128k_traffic.txt",
-                    "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
-    "llama32k": ("kvs_llama32k_kernel_stats.md", "score_colsum_llama32k_traffic.txt",
-                 "score_colsum", "score_colsum_kernel (kvs_score column-sum pass)"),
-    "cross32x16k": ("kvs_cross32x16k_kernel_stats.md", "score_colsum_cross32x16k_traffic.txt",
-                    "score_colsum", "32 x kvs_score (GROUP_SUM) + kvs_aggregate_layers (SUM_L1)"),
+    "mistral128k": ("kvs_mistral128k_kernel_stats.md", "score_fused_mistral128k_traffic.txt",
+                    "score_fused", "score_fused_kernel (kvs_score, both passes in one launch)"),
+    "llama32k": ("kvs_llama32k_kernel_stats.md", "score_fused_llama32k_traffic.txt",
+                 "score_fused", "score_fused_kernel (kvs_score, both passes in one launch)"),
+    "cross32x16k": ("kvs_cross32x16k_kernel_stats.md", "score_fused_cross32x16k_traffic.txt",
+                    "score_fused", "32 x kvs_score (GROUP_SUM) + kvs_aggregate_layers (SUM_L1)"),
     "gemfilter128k": ("kvs_gemfilter128k_kernel_stats.md", "score_raw_gemfilter128k_traffic.txt",
                       "score_raw", "score_raw_kernel (kvs_score_raw, SUM over heads, W = 1)"),
     "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
@@ -137,17 +137,6 @@ def measured_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
     kv = traffic_summary(path, workload)
     try:
         return float(kv["traffic_bytes_per_launch"]) if kv else None
-    except (KeyError, ValueError):
-        return None
-
-
-def measured_stats_traffic(path=TRAFFIC_SUMMARY, workload="mistral128k"):
-    """HBM bytes per launch of the score statistics pass from the same counter
-    runs (scaled like the roofline kernel's), or None."""
-    kv = traffic_summary(path, workload)
-    try:
-        return (float(kv["stats_fetch_kib"]) * float(kv["fetch_scale"]) +
-                float(kv["stats_write_kib"]) * float(kv["write_scale"])) * 1024 if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -246,8 +235,7 @@ def summarize_profiles(out_dir, workload="mistral128k"):
         per = {}
         for r in rows:
             n = r["Kernel_Name"]
-            key = ("kernel" if frag in n else "stats" if "score_stats" in n else
-                   "copy" if "copyBuffer" in n else None)
+            key = "kernel" if frag in n else "copy" if "copyBuffer" in n else None
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
         out = {k: st.median(v) for k, v in per.items()}
@@ -298,8 +286,6 @@ def summarize_profiles(out_dir, workload="mistral128k"):
         f"kernel_fetch_kib: {fetch['kernel']:.1f}",
         f"kernel_write_kib: {write['kernel']:.1f}",
     ]
-    if "stats" in fetch:
-        txt += [f"stats_fetch_kib: {fetch['stats']:.1f}", f"stats_write_kib: {write['stats']:.1f}"]
     txt += [f"traffic_bytes_per_launch: {traffic:.0f}", ""]
     open(os.path.join(ROOT, "profiles", traffic_name), "w").write(NL.join(txt))
     print(NL.join(lines[-6:]))
@@ -977,8 +963,8 @@ def cpu_baseline_softmax(ly, sel, min_seconds=5.0, max_reps=8):
 
 
 def bench_softmax(args):
-    """The softmax window-score path on one layer: kvs_score phase 1 and phase 2,
-    then kvs_select.  mistral128k: page max P = 16 + cluster priority (theta =
+    """The softmax window-score path on one layer: kvs_score (both passes, one
+    launch), then kvs_select.  mistral128k: page max P = 16 + cluster priority (theta =
     2e-3, r = 3) + top 1024 per KV head with the window; llama32k: max-pool 7 +
     top 1024 per KV head with the window."""
     import torch
@@ -999,9 +985,10 @@ def bench_softmax(args):
     Ks = [K0] + [K0.clone() for _ in range(max(0, rotate - 1))]
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
 
+    a0 = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0)
     a1 = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, phase=1)
     a2 = kvs.score_args(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, phase=2)
-    ws_bytes = kvs.kvs_score_workspace(a1)
+    ws_bytes = kvs.kvs_score_workspace(a0)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     S = torch.empty(H_kv, L, dtype=torch.float32, device="cuda")
     idx = torch.empty(H_kv, budget + n_forced, dtype=torch.int32, device="cuda")
@@ -1022,21 +1009,30 @@ def bench_softmax(args):
     pKs = [V(k.data_ptr()) for k in Ks]
     pidx = V(idx.data_ptr())
     ptk = V(tk_ws.data_ptr())
-    ra1, ra2, rsel = ctypes.byref(a1), ctypes.byref(a2), ctypes.byref(sel_args)
+    ra0, ra1, ra2, rsel = (ctypes.byref(a0), ctypes.byref(a1), ctypes.byref(a2),
+                           ctypes.byref(sel_args))
 
     def step(i, ev=None):
         pK = pKs[i % len(pKs)]
         if ev is not None:
             ev[0].record(stream)
-        st = lib.kvs_score(ra1, pQ, pK, pS, pws, ws_bytes, sp)
+        st = lib.kvs_score(ra0, pQ, pK, pS, pws, ws_bytes, sp)
         if ev is not None:
             ev[1].record(stream)
-        st |= lib.kvs_score(ra2, pQ, pK, pS, pws, ws_bytes, sp)
-        if ev is not None:
-            ev[2].record(stream)
         st |= lib.kvs_select(pS, H_kv, n, L, rsel, pidx, ptk, tk_bytes, sp)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libkvs call failed in step {i}")
+
+    def two_launch(i, ev):
+        """The score as its two phase calls (one launch per pass), for comparison."""
+        pK = pKs[i % len(pKs)]
+        ev[0].record(stream)
+        st = lib.kvs_score(ra1, pQ, pK, pS, pws, ws_bytes, sp)
+        ev[1].record(stream)
+        st |= lib.kvs_score(ra2, pQ, pK, pS, pws, ws_bytes, sp)
+        ev[2].record(stream)
         if st != 0:
             raise RuntimeError(f"libkvs call failed in step {i}")
 
@@ -1054,16 +1050,20 @@ def bench_softmax(args):
     # Kernel timing: K more steps with HIP events on the launch stream between
     # the parts of each step, so every kernel is timed under the same
     # conditions (clock, caches, neighbours) as in the timed region.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + args.steps + i, evs[i])
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        two_launch(args.warmup + 2 * args.steps + i, ev2[i])
     torch.cuda.synchronize()
 
-    def part(a):
-        return sum(ev[a].elapsed_time(ev[a + 1]) for ev in evs) / args.steps
+    def part(evl, a):
+        return sum(ev[a].elapsed_time(ev[a + 1]) for ev in evl) / args.steps
 
-    pass1, pass2, select = part(0), part(1), part(2)
-    step_us = sorted(ev[0].elapsed_time(ev[3]) * 1e3 for ev in evs)
+    score, select = part(evs, 0), part(evs, 1)
+    pass1, pass2 = part(ev2, 0), part(ev2, 1)
+    step_us = sorted(ev[0].elapsed_time(ev[2]) * 1e3 for ev in evs)
 
     def timed(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1074,23 +1074,27 @@ def bench_softmax(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    log(f"per step: {ms_step * 1e3:.1f} us wall; events: score pass1 {pass1 * 1e3:.1f} us, "
-        f"pass2 {pass2 * 1e3:.1f} us, select {select * 1e3:.1f} us")
+    log(f"per step: {ms_step * 1e3:.1f} us wall; events: score {score * 1e3:.1f} us (one launch; "
+        f"as two launches: pass1 {pass1 * 1e3:.1f} us, pass2 {pass2 * 1e3:.1f} us), "
+        f"select {select * 1e3:.1f} us")
     copy_gbs = copy_calibration(timed) if args.copy_calibration else None
 
-    # Algorithmic bytes of the layer (and of one column-sum launch): K once, Q
-    # once, S written once -> 2048 + 32 + ~2 bytes per token.
+    # Algorithmic bytes of the layer (and of one score launch): K once, Q once,
+    # S written once -> 2048 + 32 + ~2 bytes per token.  The two-pass design
+    # streams K twice: its bytes, and the time at which they would move at 70%
+    # of the HBM peak, are reported beside.
     k_bytes = H_kv * L * d_k * 2
     q_bytes = H_q * W * d_k * 2
     s_bytes = H_kv * L * 4
     alg_bytes = k_bytes + q_bytes + s_bytes
-    dom_ms = pass2
+    two_pass_bytes = 2 * k_bytes + q_bytes + s_bytes
+    dom_ms = score
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     stats_name, traffic_name, frag, label = WORKLOADS[args.workload]
     tpath = os.path.join(ROOT, "profiles", traffic_name)
-    t2, t1 = measured_traffic(tpath, args.workload), measured_stats_traffic(tpath, args.workload)
-    passes_gbs = (t1 + t2) / ((pass1 + pass2) * 1e-3) / 1e9 if (t1 and t2) else None
-    flops = 2.0 * H_q * W * L * d_k
+    traffic = measured_traffic(tpath, args.workload)
+    counter_gbs = traffic / (dom_ms * 1e-3) / 1e9 if traffic else None
+    flops = 2 * 2.0 * H_q * W * L * d_k   # both passes multiply the window rows by K
     tag = "128K" if mistral else "32K"
     out = {
         "metric": f"prompt tokens scored/sec at L={tag}, 8B GQA shape; % of HBM roofline",
@@ -1123,21 +1127,27 @@ def bench_softmax(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": t2,
+            "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us": dom_ms * 1e3,
             "mfma_frac": flops / (dom_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "kernel_source_sha256_16": source_hash(args.workload),
-            "event_us": {"score_pass1_stats": pass1 * 1e3, "score_pass2_colsum": pass2 * 1e3,
-                         "selection": select * 1e3},
+            "event_us": {"score_one_launch": score * 1e3, "selection": select * 1e3,
+                         "two_launch_pass1_stats": pass1 * 1e3,
+                         "two_launch_pass2_colsum": pass2 * 1e3},
             "copy_256MiB_GBs": copy_gbs,
-            # the layer's algorithmic bytes (K once) over the time of both score passes,
-            # and over the whole step
-            "alg_frac_score_pair": alg_bytes / ((pass1 + pass2) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # the layer's algorithmic bytes (K once) over the score launch (both passes; the
+            # same figure as frac) and over the whole step
+            "alg_frac_score_pair": alg_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alg_frac_step": alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            # both score passes from the counter runs (K read twice): their bytes over their time
-            "score_passes_counter_GBs": passes_gbs,
-            "score_passes_counter_frac": passes_gbs / HBM_PEAK_GBS if passes_gbs else None,
+            # the score launch's bytes from the counter runs over its time
+            "score_passes_counter_GBs": counter_gbs,
+            "score_passes_counter_frac": counter_gbs / HBM_PEAK_GBS if counter_gbs else None,
+            # K twice, Q and S once: the bytes of a two-pass design over the launch's time,
+            # and the launch time at which they move at 70% of the peak
+            "two_pass_bytes": two_pass_bytes,
+            "two_pass_frac": two_pass_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "two_pass_us_at_70pct": two_pass_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6,
         },
     }
     if not args.no_cpu_baseline:

@@ -112,10 +112,14 @@ int32_t kvs_version(void);
  * once per group).
  * The workspace holds per-split softmax statistics (and, for GROUP_MAX over
  * two row groups, every query head's column sums, 4 * H_q * L bytes; for
- * ALL_SUM each KV group's, 4 * H_kv * L bytes); its size depends only on the
- * arguments.  `phase` splits the call into its
+ * ALL_SUM each KV group's, 4 * H_kv * L bytes) and one 8-byte flag per KV head
+ * and split; its size depends only on the arguments and its contents are
+ * undefined on entry.  `phase` splits the call into its
  * statistics pass and its column-sum pass (each reads K once per row group).
- * The result is bit-identical from run to run.
+ * With phase 0 and at most 128 padded rows, both passes run in one launch
+ * when the device holds its whole grid at once (the flags order them); the
+ * result is the same bit for bit as the two phases called one after the
+ * other, and bit-identical from run to run.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t L, W, d_k, H_q, H_kv;
@@ -134,6 +138,17 @@ typedef struct {
 size_t kvs_score_workspace(const kvs_score_args* a);
 kvs_status kvs_score(const kvs_score_args* a, const void* Q, const void* K, float* S,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* kvs_score_wait_limit - bound, in microseconds, on how long a workgroup of
+ * kvs_score's one-launch form (above) waits for the statistics of the other
+ * workgroups of its KV head; 2000 by default.  A workgroup still waiting at
+ * the bound (the device shared with other work that holds back part of the
+ * grid) computes the missing statistics itself, so the result is unchanged
+ * and only time is lost; 0 sends every workgroup that finds its head
+ * incomplete down that path at once (for testing it).  A negative argument
+ * only queries.  Returns the previous bound.  Process-wide; calls already
+ * enqueued keep the bound they were enqueued with. */
+int32_t kvs_score_wait_limit(int32_t microseconds);
 
 /* kvs_score_noalloc - kvs_score without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving

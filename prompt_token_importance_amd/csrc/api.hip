@@ -139,6 +139,8 @@ size_t kvs_score_workspace(const kvs_score_args* in) {
   return pl.ws_total;
 }
 
+int32_t kvs_score_wait_limit(int32_t microseconds) { return kvs::score_wait_limit(microseconds); }
+
 kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, float* S, void* ws,
                      size_t ws_bytes, void* stream) {
   kvs_score_args a;
@@ -158,6 +160,7 @@ kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, flo
   p.stats = static_cast<float2*>(ws);
   p.head_rows_ws = pl.ws_heads ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.ws_stats)
                                : nullptr;
+  p.flags = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + pl.ws_stats + pl.ws_heads);
   p.qhs = a.q_head_stride;
   p.qrs = a.q_row_stride;
   p.khs = a.k_head_stride;

@@ -32,6 +32,7 @@ struct ScorePlan {
   int grp_h0[2], grp_h1[2];   // query heads of each group
   size_t ws_stats;  // bytes of per-split (max, sum) pairs
   size_t ws_heads;  // bytes of per-head column sums (GROUP_MAX over two groups)
+  size_t ws_flags;  // bytes of the per-(KV head, split) flags of a fused launch
   size_t ws_total;
 };
 
@@ -41,6 +42,7 @@ struct ScoreLaunch {
   float* S;
   float2* stats;  // [H_kv][rows_pad][n_split]
   float* head_rows_ws;   // [H_q][L] per-head column sums (GROUP_MAX over two row groups)
+  uint64_t* flags;       // [H_kv][n_split] flags of the fused launch (see score.hip)
   int64_t qhs, qrs, khs, kts, s_ld;
   int64_t q_pos0;
   int L, W, G, H_kv, d_k, heads, accumulate, phase;
@@ -48,6 +50,9 @@ struct ScoreLaunch {
 };
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* plan);
+// Sets the one-launch score form's wait bound (microseconds, < 0: unchanged);
+// returns the previous one.
+int32_t score_wait_limit(int32_t us);
 kvs_status score_run(const ScorePlan& plan, const ScoreLaunch& p, hipStream_t stream);
 
 // Raw logits reduced over all heads (kvs_score_raw); head_rows pads each

@@ -40,6 +40,10 @@
 //  * No R x L logit matrix is ever stored: K is read once per pass.
 #include <math.h>
 
+#include <atomic>
+#include <chrono>
+#include <mutex>
+
 #include <type_traits>
 
 #include "kvs_internal.h"
@@ -72,6 +76,9 @@ struct KArgs {
   int per_head;   // MODE 1: 1 writes each head's row, 0 the maximum over the heads
   float* out;     // output rows (S, or the per-group / per-head workspace rows)
   int64_t out_ld;
+  uint64_t* flag;     // fused launch: one word per (KV head, split), [H_kv][n_split]
+  uint64_t epoch;     // this launch's tag, stored in a flag once its split is published
+  int64_t wait_ticks; // bound on a fused workgroup's wait, in 100 MHz clock ticks
 };
 
 
@@ -548,21 +555,28 @@ __device__ __forceinline__ void pipe_step_rows(f32x16 (&accC)[NT], f32x16 (&accP
 // sets a flag; a wave with a flagged lane recomputes its full tiles with the
 // exact online update.  The few masked
 // tiles (causal window, ragged end) use the exact update directly.
-template <int D, int NT>
-__global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
+// ATOMIC: the split statistics are stored with device-scope atomic stores,
+// which reach the device's point of coherence, for a later reader in the
+// same launch on another XCD (the fused launch); plain stores otherwise.
+// Returns (per wave) whether the wave's ring still holds its last full tiles,
+// tile j in stage j % kStages: true unless it had masked tiles or redid its
+// full tiles, both of which pass through stage 0.
+template <int D, int NT, bool ATOMIC>
+__device__ __forceinline__ bool stats_body(const KArgs& a, int split,
+                                           uint8_t (&ring)[kWaves][kStages][tile_bytes<D>()],
+                                           float2 (&sm)[kWaves][32 * NT],
+                                           bf16x8 (&q)[NT][D / 16]) {
   constexpr int KS = D / 16;
   constexpr int S = kStages;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 31, hl = lane >> 5;
   const int g = a.g0 + blockIdx.y;
-  const int split = blockIdx.x;
   const int tb = split * a.tps;
   const int te = min(tb + a.tps, a.n_tiles);
   const float c = a.p.c;
   const int L = a.p.L;
 
-  bf16x8 q[NT][KS];
   int vis[NT];
   q_vis<NT>(vis, a, lane);
   float m[NT], z[NT];
@@ -571,7 +585,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     m[T] = kNegInf;
     z[T] = 0.f;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
   const int64_t kts = a.p.kts;
   uint32_t foff[KS];
@@ -582,6 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
   const int full_end = (a.min_vis - 31) >= 0 ? (a.min_vis - 31) / 32 + 1 : 0;  // tiles < full_end are full
   int nf = full_end > tb + wave ? (full_end - tb - wave + kWaves - 1) / kWaves : 0;
   nf = nf < nt ? nf : nt;
+  bool kept = nf > 0 && nf == nt;
   const auto tile_t0 = [&](int j) { return (tb + wave + j * kWaves) * 32; };
   const auto stage_of = [&](int j) { return ring[wave][j & (S - 1)]; };
   const auto tile_base = [&](int j) {
@@ -699,6 +713,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     if (__any(flag)) {
       // some logit rose about 100 log2 units above the first tile's max:
       // redo the full tiles with the exact online update
+      kept = false;
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
         m[T] = kNegInf;
@@ -726,7 +741,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
     stats_part<NT, 0, NT>(acc, m, z, c, false, tile_t0(j), hl, vis);
   }
 
-  __shared__ float2 sm[kWaves][32 * NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
     const float m2 = __shfl_xor(m[T], 32);
@@ -745,8 +759,23 @@ __global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) zz += sm[w][r].y * ex2(sm[w][r].x - mm);
     }
-    a.p.stats[((int64_t)g * a.rows_pad + a.row0 + r) * a.n_split + split] = make_float2(mm, zz);
+    float2* dst = a.p.stats + ((int64_t)g * a.rows_pad + a.row0 + r) * a.n_split + split;
+    if constexpr (ATOMIC)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(dst),
+                         __builtin_bit_cast(uint64_t, make_float2(mm, zz)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *dst = make_float2(mm, zz);
   }
+  return kept;
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads, 1) void score_stats_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kStages][tile_bytes<D>()];
+  __shared__ float2 sm[kWaves][32 * NT];
+  bf16x8 q[NT][D / 16];
+  stats_body<D, NT, false>(a, blockIdx.x, ring, sm, q);
 }
 
 // ------------------------------------------------------------------ merge
@@ -768,6 +797,9 @@ __device__ __forceinline__ void fold_pair(float& mm, float& zz, float2 v) {
   }
 }
 
+// ATOMIC: the pairs were written earlier in the same launch (by workgroups
+// on other XCDs) and are read with device-scope atomic loads.
+template <bool ATOMIC>
 __device__ __forceinline__ void merge_rows(const KArgs& a, int g, int rows, float* brow) {
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
   if (r < rows) {
@@ -778,7 +810,14 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, int g, int rows, floa
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) {
         const int s = s0 + 2 * i;
-        v[i] = s < a.n_split ? st[s] : make_float2(kNegInf, 0.f);
+        if constexpr (ATOMIC)
+          v[i] = s < a.n_split
+                     ? __builtin_bit_cast(float2, __hip_atomic_load(
+                                                      reinterpret_cast<const uint64_t*>(st + s),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                     : make_float2(kNegInf, 0.f);
+        else
+          v[i] = s < a.n_split ? st[s] : make_float2(kNegInf, 0.f);
       }
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) fold_pair(mm, zz, v[i]);
@@ -798,6 +837,53 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, int g, int rows, floa
   __syncthreads();
 }
 
+// ------------------------------------------------------------------ fused launch
+// Both passes in one launch: a workgroup streams its split for the row
+// statistics, publishes them, and starts its column-sum pass once every split
+// of its KV head is published (each pass-2 workgroup folds all of its head's
+// splits).  Every (KV head, split) has a 64-bit flag in the workspace, and
+// publishing stores the launch's epoch in it: a value no earlier launch of the
+// process used, so flags left by earlier launches never read as published and
+// the workspace needs no clearing.  Nothing is read-modify-written: the 32 or
+// so workgroups of a head finish together, and updates of one shared counter
+// would queue one device-scope round trip behind another.  The XCDs' L2
+// caches are not coherent with each other, so statistics and flags travel as
+// device-scope atomic stores and loads, which reach the device's point of
+// coherence, and a workgroup publishes only after its statistics stores have
+// completed.  The host takes this launch only when the whole grid fits on the
+// device at once.  Should a split still be unpublished when a waiter's time
+// bound runs out (the device shared with other work), the waiter computes
+// that split's statistics itself; they come out bit-identical to the owner's.
+__device__ __forceinline__ void split_publish(uint64_t* flag, uint64_t epoch) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's statistics are stored
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 polls the n flags of a head (lane s reads splits s, s + 64, ...)
+// until all hold epoch or wait_ticks of the 100 MHz clock have passed.
+// Returns in every thread whether all were published.
+__device__ __forceinline__ bool head_wait(const uint64_t* flags, uint64_t epoch, int n,
+                                          int64_t wait_ticks, int* sh) {
+  if (threadIdx.x < 64) {
+    const int64_t t0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+    int all;
+    for (;;) {
+      int ok = 1;
+      for (int s = threadIdx.x; s < n; s += 64)
+        ok &= __hip_atomic_load(flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      all = __all(ok);
+      if (all || (int64_t)__builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x == 0) *sh = all;
+  }
+  __syncthreads();
+  const int r = __builtin_amdgcn_readfirstlane(*sh);
+  __syncthreads();   // before sh is written again
+  return r != 0;
+}
+
 // ------------------------------------------------------------------ pass 2
 __device__ __forceinline__ void store_out(float* o, float v, int accumulate) {
   *o = accumulate ? *o + v : v;
@@ -807,8 +893,19 @@ __device__ __forceinline__ void store_out(float* o, float v, int accumulate) {
 // and a query head whose rows span both row groups).
 // MODE 1: per query head sums (NONE) or their maximum (GROUP_MAX).
 // Both run the same swapped-operand pipeline; only the per-tile finish differs.
-template <int D, int NT, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
+// FUSED: the query fragments are already in q (the statistics pass of the
+// same launch loaded them), and the statistics come from that pass: settle()
+// returns once all of the head's splits are published, true if it had to use
+// the ring to compute some of them itself.  kept: the statistics pass left
+// this wave's last full tiles in the ring (tile j in stage j % kStages), and
+// this pass, walking the full tiles last to first, starts on them without
+// loading them again.
+template <int D, int NT, int MODE, bool FUSED, class Settle>
+__device__ __forceinline__ void colsum_body(const KArgs& a,
+                                            uint8_t (&ring)[kWaves][kStages][tile_bytes<D>()],
+                                            int (&rvis)[128], float (&brow)[128],
+                                            bf16x8 (&q)[NT][D / 16], bool kept,
+                                            Settle&& settle) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 31, hl = lane >> 5;
@@ -820,7 +917,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   const int L = a.p.L;
 
   constexpr int S = kStages;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][S][tile_bytes<D>()];
   const uint16_t* kbase = a.p.K + (int64_t)g * a.p.khs;
   const int64_t kts = a.p.kts;
   const int nt = te > tb + wave ? (te - tb - wave + kWaves - 1) / kWaves : 0;
@@ -834,16 +930,15 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   // memory-side cache, are read first.  x-th processed full tile:
   const auto tj = [&](int x) { return a.rev ? nf - 1 - x : x; };
   const auto t0_of = [&](int x) { return (tb + wave + tj(x) * kWaves) * 32; };
+  kept = FUSED && kept && a.rev;
 
-  bf16x8 q[NT][D / 16];
   // The query rows (through every wave's last ring stage, see the pass-1
   // kernel) and the first full tile load while the row constants are merged;
   // the merge's barrier waits for all three.
-  if (wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
-  if (nf > 0) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
+  if (!FUSED && wave < NT) issue_q_rows<D>(ring[wave][S - 1], a, g, wave, lane);
+  if (nf > 0 && !kept) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
   // last visible key of every padded row (-1 for padding rows), for the
   // masked tiles
-  __shared__ __attribute__((aligned(16))) int rvis[128];
   if (threadIdx.x < 32 * NT) {
     const int r = a.row0 + threadIdx.x;
     const int hq = r / a.head_rows, jr = r % a.head_rows;
@@ -853,9 +948,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
                             : -1;
   }
   // row constants from pass 1's split statistics (the merge's barrier also
-  // orders rvis)
-  __shared__ float brow[128];
-  merge_rows(a, g, 32 * NT, brow);
+  // orders rvis); in a fused launch, once every split of the head is in
+  if constexpr (FUSED) {
+    if (settle()) {
+      kept = false;
+      if (nf > 0) issue_tile<D>(ring[wave][0], kbase, kts, t0_of(0), L, lane);
+    }
+  }
+  merge_rows<FUSED>(a, g, 32 * NT, brow);
   float b[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) b[T] = brow[32 * T + nl];
@@ -863,8 +963,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 
   uint32_t foff[D / 16];
   frag_offsets<D>(foff, lane);
-  read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
-  __builtin_amdgcn_s_barrier();   // every wave has its copy before the stage is refilled
+  if constexpr (!FUSED) {
+    read_q_agpr<D, NT>(q, lds_addr(ring[0][S - 1]), S * tile_bytes<D>(), foff);
+    __builtin_amdgcn_s_barrier();   // every wave has its copy before the stage is refilled
+  }
   {
     // Column sums with the MFMA operands swapped: A = the query rows, B = the
     // K fragments, so lane l holds key l % 32 of the tile against 16 rows of
@@ -967,19 +1069,24 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       }
     };
     if (nf > 0) {
-      const auto stage_of = [&](int x) { return ring[wave][x & (S - 1)]; };
+      // tile x's stage: x % S, or, on the tiles the statistics pass left,
+      // (nf - 1 - x) % S; either way tile x + S reuses tile x's stage
+      const int s0 = kept ? nf - 1 : 0, sd = kept ? -1 : 1;
+      const auto sidx = [&](int x) { return (s0 + sd * x) & (S - 1); };
+      const auto stage_of = [&](int x) { return ring[wave][sidx(x)]; };
       uint32_t coff[ChunkGeom<D>::NQ];
       chunk_offsets<D>(coff, lane, kts);
       f32x16 acc0[NT], acc1[NT];
       u32x4 f0[KS], f1[KS];
       const int pre = nf < S ? nf : S;
-      // tile 0 was issued before the merge and has arrived
-      for (int x = 1; x < pre; ++x) issue_tile<D>(stage_of(x), kbase, kts, t0_of(x), L, lane);
+      // tile 0 was issued before the merge and has arrived (or was kept)
+      if (!kept)
+        for (int x = 1; x < pre; ++x) issue_tile<D>(stage_of(x), kbase, kts, t0_of(x), L, lane);
       if (pre == S)
         wait_vm<(S - 1) * KS>();
       else
         wait_vm<0>();
-      read_frags_a<KS>(f0, ring0, foff);
+      read_frags_a<KS>(f0, ring0 + sidx(0) * tile_bytes<D>(), foff);
       wait_lgkm_a<KS>(f0);
       mfma_rows_all<D, NT>(acc0, f0, q, qx, ones);
       if (nf > 1) {
@@ -987,7 +1094,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
           wait_vm<(S - 2) * KS>();
         else
           wait_vm<0>();
-        read_frags_a<KS>(f1, ring0 + tile_bytes<D>(), foff);
+        read_frags_a<KS>(f1, ring0 + sidx(1) * tile_bytes<D>(), foff);
         wait_lgkm_a<KS>(f1);
       }
       // step x: MFMAs of tile x || probabilities of tile x-1, whose sums
@@ -998,7 +1105,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
 #pragma unroll
         for (int u = 0; u < NPC; ++u) pc[u] = 0.f;
         const auto work = [&](int T, int i, float v) { pc[pc_of(T, i)] += ex2(v * c); };
-        const uint32_t nxt = ring0 + ((x + 1) & (S - 1)) * tile_bytes<D>();
+        const uint32_t nxt = ring0 + sidx(x + 1) * tile_bytes<D>();
         if (x + S - 1 < nf)
           pipe_step_rows<D, NT, true, true, (S - 2) * KS>(
               accC, accP, fc, fn, q, qx, ones, stage_of(x + S - 1),
@@ -1065,6 +1172,48 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
       finish(pc, t0);
     }
   }
+}
+
+template <int D, int NT, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kStages][tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) int rvis[128];
+  __shared__ float brow[128];
+  bf16x8 q[NT][D / 16];
+  colsum_body<D, NT, MODE, false>(a, ring, rvis, brow, q, false, [] { return false; });
+}
+
+// Both passes of one row group in one launch (see split_publish).
+template <int D, int NT, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void score_fused_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kStages][tile_bytes<D>()];
+  __shared__ float2 sm[kWaves][32 * NT];
+  __shared__ __attribute__((aligned(16))) int rvis[128];
+  __shared__ float brow[128];
+  __shared__ int sh;
+  bf16x8 q[NT][D / 16];
+  uint64_t* flags = a.flag + (int64_t)(a.g0 + blockIdx.y) * a.n_split;
+  const bool kept = stats_body<D, NT, true>(a, blockIdx.x, ring, sm, q);
+  split_publish(flags + blockIdx.x, a.epoch);
+  const auto settle = [&]() -> bool {
+    if (head_wait(flags, a.epoch, a.n_split, a.wait_ticks, &sh)) return false;
+    // some split is late: compute it here (its first tile's load lands first)
+    wait_vm<0>();
+    __syncthreads();
+    for (int s = 0; s < a.n_split; ++s) {
+      if (threadIdx.x == 0)
+        sh = __hip_atomic_load(flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+      __syncthreads();
+      const int done = __builtin_amdgcn_readfirstlane(sh);
+      __syncthreads();
+      if (!done) {
+        stats_body<D, NT, true>(a, s, ring, sm, q);
+        split_publish(flags + s, a.epoch);
+      }
+    }
+    return true;
+  };
+  colsum_body<D, NT, MODE, true>(a, ring, rvis, brow, q, kept, settle);
 }
 
 // ------------------------------------------------------------------ raw logits
@@ -1300,6 +1449,72 @@ void launch_group(const KArgs& a, int pass, int mode, dim3 grid, hipStream_t str
     hipLaunchKernelGGL((score_colsum_kernel<D, NT, 1>), grid, dim3(kThreads), 0, stream, a);
 }
 
+// The fused launch needs every workgroup resident at once (a workgroup waits
+// for the others of its KV head), so it is taken only when the occupancy the
+// runtime reports for the kernel, times the device's CUs, covers the grid.
+// The answer is kept per device and kernel.
+struct FitEntry {
+  int dev;
+  const void* fn;
+  int blocks;   // resident workgroups the device holds, -1: unknown
+};
+
+int fused_capacity(const void* fn) {
+  static std::mutex mu;
+  static FitEntry table[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (table[i].dev == dev && table[i].fn == fn) return table[i].blocks;
+  int per_cu = 0, cus = 0;
+  int blocks = -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    blocks = per_cu * cus;
+  (void)hipGetLastError();
+  if (used < 64) table[used++] = FitEntry{dev, fn, blocks};
+  return blocks;
+}
+
+// Launches the fused kernel; false (nothing launched) when the grid does not
+// fit on the device at once.
+template <int D, int NT>
+bool launch_fused(const KArgs& a, int mode, dim3 grid, hipStream_t stream) {
+  const void* fn = mode == 0 ? reinterpret_cast<const void*>(&score_fused_kernel<D, NT, 0>)
+                             : reinterpret_cast<const void*>(&score_fused_kernel<D, NT, 1>);
+  if ((int64_t)grid.x * grid.y > (int64_t)fused_capacity(fn)) return false;
+  if (mode == 0)
+    hipLaunchKernelGGL((score_fused_kernel<D, NT, 0>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_fused_kernel<D, NT, 1>), grid, dim3(kThreads), 0, stream, a);
+  return true;
+}
+
+template <int D>
+bool launch_fused_nt(int nt, const KArgs& a, int mode, dim3 grid, hipStream_t stream) {
+  switch (nt) {
+    case 1: return launch_fused<D, 1>(a, mode, grid, stream);
+    case 2: return launch_fused<D, 2>(a, mode, grid, stream);
+    case 3: return launch_fused<D, 3>(a, mode, grid, stream);
+    default: return launch_fused<D, 4>(a, mode, grid, stream);
+  }
+}
+
+// A fresh tag for every fused launch of the process, never 0 (the value of a
+// zeroed workspace); the start is drawn from the clock, so flags left in a
+// recycled workspace by another process are not mistaken for this launch's.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> next{
+      ((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull) >> 8};
+  return next.fetch_add(1, std::memory_order_relaxed) | (1ull << 63);
+}
+
+// Bound on a fused workgroup's wait for the rest of its KV head, in ticks of
+// the 100 MHz clock (kvs_score_wait_limit); 2 ms by default.
+std::atomic<int64_t> g_wait_ticks{200000};
+
 template <int D>
 void launch_group_nt(int nt, const KArgs& a, int pass, int mode, dim3 grid, hipStream_t stream) {
   switch (nt) {
@@ -1333,6 +1548,27 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
   const bool all_sum = p.heads == KVS_HEADS_ALL_SUM;
   const int mode =
       (p.heads == KVS_HEADS_GROUP_SUM || all_sum || pl.head_rows > 128) ? 0 : 1;
+  a.flag = p.flags;
+  a.epoch = 0;
+  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+  // Both passes of a single row group in one launch when the device can hold
+  // the whole grid at once.
+  if (p.phase == 0 && pl.n_groups == 1 && p.flags) {
+    a.row0 = pl.grp_row0[0];
+    a.h0 = pl.grp_h0[0];
+    a.h1 = pl.grp_h1[0];
+    a.per_head = p.heads == KVS_HEADS_NONE;
+    a.out = all_sum ? p.head_rows_ws : p.S;
+    a.out_ld = all_sum ? (int64_t)p.L : p.s_ld;
+    a.acc = all_sum ? 0 : p.accumulate;
+    a.epoch = next_epoch();
+    if (launch_fused_nt<D>(pl.grp_rows[0] / 32, a, mode, grid, stream)) {
+      if (all_sum)
+        hipLaunchKernelGGL(score_head_sum_kernel, dim3((p.L + 255) / 256), dim3(256), 0, stream,
+                           p.head_rows_ws, (int64_t)p.L, p.H_kv, p.L, p.S, p.accumulate);
+      return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+    }
+  }
   for (int pass = 1; pass <= 2; ++pass) {
     if ((pass == 1 && p.phase == 2) || (pass == 2 && p.phase == 1)) continue;
     for (int gr = 0; gr < pl.n_groups; ++gr) {
@@ -1358,6 +1594,12 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
 }
 
 }  // namespace
+
+int32_t score_wait_limit(int32_t us) {
+  const int64_t prev = g_wait_ticks.load(std::memory_order_relaxed);
+  if (us >= 0) g_wait_ticks.store((int64_t)us * 100, std::memory_order_relaxed);
+  return (int32_t)(prev / 100);
+}
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   const int G = a->H_q / a->H_kv;
@@ -1404,7 +1646,6 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   pl->tiles_per_split = tps;
   pl->n_split = (pl->n_tiles + tps - 1) / tps;
   pl->ws_stats = align_up((size_t)a->H_kv * pl->n_split * pl->rows_pad * sizeof(float2), kWsAlign);
-  // GROUP_MAX over two row groups keeps every query head's column sums
   // GROUP_MAX over two row groups keeps every query head's column sums; the
   // sum over every head keeps each KV head's
   const bool split_max = pl->n_groups > 1 && a->heads == KVS_HEADS_GROUP_MAX && G > 1;
@@ -1412,7 +1653,8 @@ kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
                  : a->heads == KVS_HEADS_ALL_SUM
                      ? align_up((size_t)a->H_kv * a->L * sizeof(float), kWsAlign)
                      : 0;
-  pl->ws_total = pl->ws_stats + pl->ws_heads;
+  pl->ws_flags = align_up((size_t)a->H_kv * pl->n_split * sizeof(uint64_t), kWsAlign);
+  pl->ws_total = pl->ws_stats + pl->ws_heads + pl->ws_flags;
   return KVS_OK;
 }
 

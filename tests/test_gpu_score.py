@@ -178,6 +178,43 @@ def test_phase_split_matches_one_call(kvs, which):
     assert torch.equal(one.view(torch.int32), S.view(torch.int32))
 
 
+@pytest.mark.parametrize("heads", [1, 0, 2, 3], ids=["group_sum", "none", "group_max", "all_sum"])
+@pytest.mark.parametrize("name,L,W,d_k,H_q,H_kv", [
+    ("gqa_w32", 4113, 32, 128, 32, 8),     # 26 splits x 8 KV heads in one launch
+    ("tiny", 512, 16, 64, 4, 1),
+    ("g3_w32", 2500, 32, 128, 6, 2),
+], ids=["gqa_w32", "tiny", "g3_w32"])
+def test_one_launch_late_split_path(kvs, name, L, W, d_k, H_q, H_kv, heads):
+    """With the wait bound at 0, every workgroup of the one-launch form that finds its KV head
+    incomplete computes the missing splits' statistics itself.  The scores must equal the
+    two-phase calls bit for bit and the oracle within tolerance; the flags and statistics
+    left in the workspace (garbage on entry, then an earlier call's) change nothing."""
+    print(f"late-split path {name} heads={heads}", flush=True)
+    ly = synth.gaussian_layer(L + 17 * H_kv, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv)
+    Q = kvs.bf16_from_bits(ly.Q)
+    K = kvs.bf16_from_bits(ly.K)
+    shape = dict(L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0, heads=heads)
+    ws = torch.empty(kvs.kvs_score_workspace(kvs.score_args(**shape)), dtype=torch.uint8,
+                     device="cuda")
+    two = kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=1), ws=ws)
+    two = kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=2), S=two, ws=ws)
+    ws.fill_(0xA5)
+    prev = kvs.kvs_score_wait_limit(0)
+    try:
+        late = [kvs.kvs_score(Q, K, kvs.score_args(**shape), ws=ws) for _ in range(2)]
+    finally:
+        assert kvs.kvs_score_wait_limit(prev) == 0
+    ws.fill_(0xFF)
+    fast = kvs.kvs_score(Q, K, kvs.score_args(**shape), ws=ws)
+    torch.cuda.synchronize()
+    for got in late + [fast]:
+        assert torch.equal(two.view(torch.int32), got.view(torch.int32))
+    So = oracle.score(ly.Q, ly.K, L=L, W=W, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=ly.q_pos0,
+                      heads=heads)
+    R = W * (H_q // H_kv) if heads == 1 else W * H_q if heads == 3 else W
+    assert_scores_close(fast.cpu().numpy(), So, R, L, "one launch")
+
+
 ALL_SUM_CASES = [
     # (name, L, W, d_k, H_q, H_kv): the CLAA layer score, summed over every head
     ("claa_w8", 3000, 8, 128, 32, 8),
