@@ -72,7 +72,8 @@ WORKLOADS = {
     "specprefill128k": ("kvs_specprefill128k_kernel_stats.md", "score_raw_specprefill128k_traffic.txt",
                         "score_raw", "score_raw_kernel (kvs_score_raw, MAX over heads, W = 8)"),
     "delta32x8k": ("kvs_delta32x8k_kernel_stats.md", "delta_pages_delta32x8k_traffic.txt",
-                   "delta", "kvs_delta_pages (delta_logits_kernel + delta_page_kernel + topk_delta_kernel)"),
+                   "delta", "kvs_delta_pages (delta_fused_kernel: logits, page scores and page sets in "
+                            "one launch)"),
     "gather128k": ("kvs_gather128k_kernel_stats.md", "gather_gather128k_traffic.txt",
                    "gather_kernel", "gather_kernel (kvs_gather_kv, K and V)"),
     "chunksel128k": ("kvs_chunksel128k_kernel_stats.md", "block_topp_chunksel128k_traffic.txt",
@@ -256,11 +257,13 @@ def summarize_profiles(out_dir, workload="mistral128k"):
             out["kernel"] = (st.median(big) + st.median(small) +
                              sum(st.median(v) for v in parts.values()))
         if workload == "delta32x8k":
-            # the roofline covers the whole call: the sum of its three kernels' medians
+            # the roofline covers the whole call: the sum of its kernels' medians (one launch,
+            # or the logits, page and selection kernels where that form does not apply)
             parts = {}
             for r in rows:
                 n = r["Kernel_Name"]
-                for kn in ("delta_logits_kernel", "delta_page_kernel", "topk_delta_kernel"):
+                for kn in ("delta_fused_kernel", "delta_logits_kernel", "delta_page_kernel",
+                           "topk_delta_kernel"):
                     if kn in n:
                         parts.setdefault(kn, []).append(float(r["Counter_Value"]))
             out["kernel"] = sum(st.median(v) for v in parts.values())

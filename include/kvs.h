@@ -139,16 +139,17 @@ size_t kvs_score_workspace(const kvs_score_args* a);
 kvs_status kvs_score(const kvs_score_args* a, const void* Q, const void* K, float* S,
                      void* ws, size_t ws_bytes, void* stream);
 
-/* kvs_score_wait_limit - bound, in microseconds, on how long a workgroup of
- * kvs_score's one-launch form (above) waits for the statistics of the other
- * workgroups of its KV head; 2000 by default.  A workgroup still waiting at
- * the bound (the device shared with other work that holds back part of the
- * grid) computes the missing statistics itself, so the result is unchanged
- * and only time is lost; 0 sends every workgroup that finds its head
- * incomplete down that path at once (for testing it).  A negative argument
- * only queries.  Returns the previous bound.  Process-wide; calls already
- * enqueued keep the bound they were enqueued with. */
-int32_t kvs_score_wait_limit(int32_t microseconds);
+/* kvs_wait_limit - bound, in microseconds, on how long a workgroup of a
+ * one-launch form (kvs_score above, kvs_delta_pages below) waits for the
+ * softmax statistics of the other workgroups of its KV head or sequence;
+ * 2000 by default.  A workgroup still waiting at the bound (the device shared
+ * with other work that holds back part of the grid) computes the missing
+ * statistics itself, so the result is unchanged and only time is lost; 0
+ * sends every workgroup that finds its group incomplete down that path at
+ * once (for testing it).  A negative argument only queries.  Returns the
+ * previous bound.  Process-wide; calls already enqueued keep the bound they
+ * were enqueued with. */
+int32_t kvs_wait_limit(int32_t microseconds);
 
 /* kvs_score_noalloc - kvs_score without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
@@ -234,7 +235,11 @@ kvs_status kvs_score_raw(const kvs_raw_args* a, const void* Q, const void* K, fl
  * each sequence (other entries untouched), or NULL.
  * Workspace: kvs_delta_workspace bytes, 16-byte aligned, contents undefined
  * on entry and return (the logits of every head, 4 * H_q bytes per cached
- * token, and per-chunk softmax statistics).
+ * token, per-chunk softmax statistics and an 8-byte flag per chunk).  With
+ * H_q <= 32, when the logits of the batch fit in registers (B * L_max up to
+ * about 256K tokens) and the device holds the whole grid at once, one launch
+ * computes the page scores without writing the logits (the flags order its
+ * workgroups); the result is the same bit for bit.
  * Limits (else KVS_EUNSUPPORTED): d_k in {64, 128}; H_q <= 128; P divides
  * 512; ceil(L_max / P) <= 16384.  K is read once; the result is
  * bit-identical from run to run.

@@ -95,7 +95,7 @@ def _load():
         "kvs_score_workspace": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvs_score": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvs_score_noalloc": (I32, [ctypes.POINTER(ScoreArgs), P, P, P, P]),
-        "kvs_score_wait_limit": (I32, [I32]),
+        "kvs_wait_limit": (I32, [I32]),
         "kvs_score_raw": (I32, [ctypes.POINTER(RawArgs), P, P, P, P]),
         "kvs_delta_workspace": (SZ, [ctypes.POINTER(DeltaArgs)]),
         "kvs_gather_kv": (I32, [P, P, I32, I32, I32, I64, I64, P, I64, P, I32, I32, P, P, P]),
@@ -128,7 +128,7 @@ _lib = _load()
 
 EXPORTED = (
     "kvs_status_string", "kvs_version", "kvs_score_workspace", "kvs_score", "kvs_score_noalloc",
-    "kvs_score_wait_limit",
+    "kvs_wait_limit",
     "kvs_score_raw",
     "kvs_delta_workspace", "kvs_delta_pages", "kvs_gather_kv",
     "kvs_pool_pages",
@@ -200,9 +200,9 @@ def kvs_score(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs, S: Optional[tor
     return S
 
 
-def kvs_score_wait_limit(microseconds: int) -> int:
-    """Sets the one-launch score form's wait bound (< 0: query only); returns the previous."""
-    return int(_lib.kvs_score_wait_limit(int(microseconds)))
+def kvs_wait_limit(microseconds: int) -> int:
+    """Sets the one-launch forms' wait bound (< 0: query only); returns the previous."""
+    return int(_lib.kvs_wait_limit(int(microseconds)))
 
 
 def kvs_score_noalloc(Q: torch.Tensor, K: torch.Tensor, args: ScoreArgs,

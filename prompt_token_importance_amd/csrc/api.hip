@@ -43,7 +43,7 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
 }
 
 struct DeltaPlan {
-  size_t x2, cstats, S, total;   // byte offsets of the workspace parts
+  size_t x2, cstats, S, flags, total;   // byte offsets of the workspace parts
   int chunk, n_chunk, n_pages_max;
   int64_t x2_ld;
 };
@@ -74,6 +74,8 @@ kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
   off = align_up(off + (size_t)a->B * pl->n_chunk * a->H_q * sizeof(float2), kWsAlign);
   pl->S = off;
   off = align_up(off + (size_t)a->B * n_pages * sizeof(float), kWsAlign);
+  pl->flags = off;
+  off = align_up(off + 2 * (size_t)a->B * pl->n_chunk * sizeof(uint64_t), kWsAlign);
   pl->total = off;
   return KVS_OK;
 }
@@ -139,7 +141,7 @@ size_t kvs_score_workspace(const kvs_score_args* in) {
   return pl.ws_total;
 }
 
-int32_t kvs_score_wait_limit(int32_t microseconds) { return kvs::score_wait_limit(microseconds); }
+int32_t kvs_wait_limit(int32_t microseconds) { return kvs::wait_limit(microseconds); }
 
 kvs_status kvs_score(const kvs_score_args* in, const void* Q, const void* K, float* S, void* ws,
                      size_t ws_bytes, void* stream) {
@@ -272,6 +274,10 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
   p.cstats = reinterpret_cast<float2*>(w + pl.cstats);
   p.S = page_scores ? page_scores : reinterpret_cast<float*>(w + pl.S);
   p.rho = rho;
+  p.flags = reinterpret_cast<uint64_t*>(w + pl.flags);
+  p.pflags = p.flags + (size_t)a->B * pl.n_chunk;
+  p.epoch = 0;
+  p.wait_ticks = 0;
   p.khs = a->k_head_stride;
   p.kts = a->k_tok_stride ? a->k_tok_stride : a->d_k;
   p.B = a->B;
@@ -290,9 +296,10 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
   const double scale = a->scale > 0.f ? (double)a->scale : 1.0 / sqrt((double)a->d_k);
   p.c = (float)(scale * 1.4426950408889634073599246810018921);  // scale * log2(e)
   hipStream_t s = as_stream(stream);
-  st = delta_scores_run(p, s);
+  int selected = 0;
+  st = delta_scores_run(p, s, &selected);
   if (st != KVS_OK) return st;
-  return delta_topk_run(p, s);
+  return selected ? KVS_OK : delta_topk_run(p, s);
 }
 
 kvs_status kvs_gather_kv(const void* K, const void* V, int32_t H, int32_t L, int32_t d_k,

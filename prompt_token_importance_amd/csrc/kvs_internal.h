@@ -50,9 +50,9 @@ struct ScoreLaunch {
 };
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* plan);
-// Sets the one-launch score form's wait bound (microseconds, < 0: unchanged);
+// Sets the one-launch forms' wait bound (microseconds, < 0: unchanged);
 // returns the previous one.
-int32_t score_wait_limit(int32_t us);
+int32_t wait_limit(int32_t us);
 kvs_status score_run(const ScorePlan& plan, const ScoreLaunch& p, hipStream_t stream);
 
 // Raw logits reduced over all heads (kvs_score_raw); head_rows pads each
@@ -76,6 +76,10 @@ struct DeltaLaunch {
   float2* cstats;                  // [B][n_chunk][H_q] per-chunk (max, sum of exp2)
   float* S;                        // [B][n_pages_max] page scores
   int32_t* rho;                    // [B][K_pages]
+  uint64_t* flags;                 // [B][n_chunk] flags of the one-launch form: statistics
+  uint64_t* pflags;                //   and page scores published
+  uint64_t epoch;                  // set by the launcher
+  int64_t wait_ticks;              // set by the launcher
   int64_t khs, kts;                // khs 0: L_b * d_k
   int B, H_q, H_kv, G, d_k, P, K_pages, L_recent, L_max, n_chunk, n_pages_max;
   int chunk;                       // keys per logits workgroup, a multiple of 128
@@ -85,7 +89,8 @@ struct DeltaLaunch {
 // Keys per logits workgroup for a batch: enough workgroups for every CU,
 // each streaming as long a run of keys as that allows.
 int delta_chunk(int B, int L_max);
-kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream);
+// Page scores; *selected = 1 when the same launch also wrote rho.
+kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream, int* selected);
 kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream);
 
 // ---------------------------------------------------------------- others

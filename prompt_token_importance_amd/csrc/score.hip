@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "kvs_internal.h"
+#include "select_ops.h"
 
 namespace kvs {
 namespace {
@@ -1511,8 +1512,8 @@ uint64_t next_epoch() {
   return next.fetch_add(1, std::memory_order_relaxed) | (1ull << 63);
 }
 
-// Bound on a fused workgroup's wait for the rest of its KV head, in ticks of
-// the 100 MHz clock (kvs_score_wait_limit); 2 ms by default.
+// Bound on a one-launch workgroup's wait for the rest of its KV head or
+// sequence, in ticks of the 100 MHz clock (kvs_wait_limit); 2 ms by default.
 std::atomic<int64_t> g_wait_ticks{200000};
 
 template <int D>
@@ -1595,7 +1596,7 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
 
 }  // namespace
 
-int32_t score_wait_limit(int32_t us) {
+int32_t wait_limit(int32_t us) {
   const int64_t prev = g_wait_ticks.load(std::memory_order_relaxed);
   if (us >= 0) g_wait_ticks.store((int64_t)us * 100, std::memory_order_relaxed);
   return (int32_t)(prev / 100);
@@ -1723,7 +1724,25 @@ namespace {
 // folds them into per-lane online statistics.
 struct DeltaArgs {
   DeltaLaunch p;
+  int sel;   // one-launch form: the last chunk of each sequence also selects its pages
 };
+
+// Log-sum-exp folds of the DELTA kernels with a fixed rounding order (the
+// running sum's product rounded, the incoming term's fused), so that every
+// kernel folds the same statistics to the same bits whatever contraction
+// the compiler would otherwise choose in each.
+// (m, z) <- (m, z) combined with (m2, z2):
+__device__ __forceinline__ void lse_fold(float& m, float& z, float m2, float z2) {
+  const float mx = fmaxf(m, m2);
+  z = mx == kNegInf ? 0.f : __builtin_fmaf(z2, ex2(m2 - mx), z * ex2(m - mx));
+  m = mx;
+}
+// (m, z) <- (m, z) with one more term x:
+__device__ __forceinline__ void lse_add(float& m, float& z, float x) {
+  const float mn = fmaxf(m, x);
+  z = __builtin_fmaf(z, ex2(m - mn), ex2(x - mn));
+  m = mn;
+}
 
 template <int D>
 __device__ __forceinline__ void issue_delta_q(uint8_t* dst, const DeltaLaunch& p, int b, int T,
@@ -1849,9 +1868,7 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
           if (valid && own[T][i] < H) {
             const float x = out[T][i];
             x2b[(int64_t)h * p.x2_ld + t] = x;
-            const float mn = fmaxf(m[T][i], x);
-            z[T][i] = z[T][i] * ex2(m[T][i] - mn) + ex2(x - mn);
-            m[T][i] = mn;
+            lse_add(m[T][i], z[T][i], x);
           }
         }
     }
@@ -1885,9 +1902,7 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
 #pragma unroll
       for (int d = 1; d < 32; d *= 2) {
         const float m2 = __shfl_xor(mm, d), z2 = __shfl_xor(zz, d);
-        const float mx = fmaxf(mm, m2);
-        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + z2 * ex2(m2 - mx);
-        mm = mx;
+        lse_fold(mm, zz, m2, z2);
       }
       if (nl == 0) red[wave][32 * T + 8 * (i / 4) + 4 * hl + (i % 4)] = make_float2(mm, zz);
     }
@@ -1897,9 +1912,7 @@ __global__ __launch_bounds__(kThreads, 1) void delta_logits_kernel(DeltaArgs a) 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float2 v = red[w][h];
-      const float mx = fmaxf(mm, v.x);
-      zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + v.y * ex2(v.x - mx);
-      mm = mx;
+      lse_fold(mm, zz, v.x, v.y);
     }
     p.cstats[((int64_t)b * p.n_chunk + chunk) * p.H_q + h] = make_float2(mm, zz);
   }
@@ -1949,11 +1962,7 @@ __global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs 
         w[q] = c < nch ? cs[(int64_t)c * p.H_q] : make_float2(kNegInf, 0.f);
       }
 #pragma unroll
-      for (int q = 0; q < kCsBatch; ++q) {
-        const float mx = fmaxf(mm, w[q].x);
-        zz = mx == kNegInf ? 0.f : zz * ex2(mm - mx) + w[q].y * ex2(w[q].x - mx);
-        mm = mx;
-      }
+      for (int q = 0; q < kCsBatch; ++q) lse_fold(mm, zz, w[q].x, w[q].y);
     }
   }
   part[threadIdx.x] = make_float2(mm, zz);
@@ -1962,9 +1971,7 @@ __global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs 
     float m2 = kNegInf, z2 = 0.f;
     for (int q = 0; q < tph; ++q) {
       const float2 w = part[threadIdx.x * tph + q];
-      const float mx = fmaxf(m2, w.x);
-      z2 = mx == kNegInf ? 0.f : z2 * ex2(m2 - mx) + w.y * ex2(w.x - mx);
-      m2 = mx;
+      lse_fold(m2, z2, w.x, w.y);
     }
     bh[threadIdx.x] = m2 + log2f(z2);
   }
@@ -1995,9 +2002,317 @@ __global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs 
   }
 }
 
+// ------------------------------------------------------------------ DELTA in one launch
+// When the logits of the whole batch fit in registers (one row tile, H_q <=
+// 32, and at most kDeltaKeepTiles key tiles per wave: 16 floats per lane and
+// tile) and the grid is resident at once, one launch does what the two
+// kernels above do, without writing the logits anywhere: each workgroup
+// streams its chunk as delta_logits_kernel does and keeps its logits in
+// registers, publishes its chunk's statistics (flags as in the one-launch
+// score form, see split_publish), waits for the other chunks of its
+// sequence, folds them into b_h in delta_page_kernel's order, and forms the
+// token and page scores from its registers.  Results are bit-identical to
+// the two kernels'.  A chunk still unpublished at the wait bound is computed
+// by the waiter (statistics only), bit-identically.
+constexpr int kDeltaKeepTiles = 8;
+// K ring stages per wave of the one-launch form: with no stores in the loop,
+// a deeper ring keeps more of the stream in flight.
+constexpr int kDeltaStages = 3;
+
+// Streams chunk `chunk` of sequence b (logits of every head, as
+// delta_logits_kernel) and stores its per-head statistics with device-scope
+// atomic stores; RETAIN keeps tile j's logits (this lane's 16 rows of key
+// t0 + lane % 32) in keep[j].
+template <int D, bool RETAIN>
+__device__ __forceinline__ void delta_chunk_pass(const DeltaLaunch& p, int b, int chunk,
+                                                 uint8_t (&qs)[tile_bytes<D>()],
+                                                 uint8_t (&ring)[kWaves][kDeltaStages][tile_bytes<D>()],
+                                                 float2 (&red)[kWaves][32],
+                                                 float (&keep)[kDeltaKeepTiles][16]) {
+  constexpr int KS = D / 16;
+  constexpr int S = kDeltaStages;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 31, hl = lane >> 5;
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int tb = chunk * p.chunk;
+  const int te = min(tb + p.chunk, Lb);
+  const uint16_t* Kb = p.K[b];
+  const int64_t khs = p.khs ? p.khs : (int64_t)Lb * D;
+  const int H = p.H_kv;
+  const int n_tiles = (te - tb + 31) / 32;
+  const int nt = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+  const int steps = nt * H;   // (key tile, KV head) pairs, KV head fastest
+  const auto t0_of = [&](int s) { return tb + (wave + kWaves * (s / H)) * 32; };
+  const auto issue_k = [&](int s) {
+    issue_tile<D>(ring[wave][s % S], Kb + (int64_t)(s % H) * khs, p.kts, t0_of(s), Lb, lane);
+  };
+  // at most n tiles' loads of this wave still in flight (n wave-uniform)
+  const auto wait_tiles = [&](int n) {
+    static_assert(S <= 4, "wait_tiles covers up to three tiles in flight");
+    if (n >= 3)
+      wait_vm<3 * KS>();
+    else if (n == 2)
+      wait_vm<2 * KS>();
+    else if (n == 1)
+      wait_vm<KS>();
+    else
+      wait_vm<0>();
+  };
+  if (wave == 0) issue_delta_q<D>(qs, p, b, 0, lane);
+  const int pre = steps < S - 1 ? steps : S - 1;
+  for (int s = 0; s < pre; ++s) issue_k(s);
+  wait_tiles(pre);   // wave 0's query rows, issued first, are in
+  __builtin_amdgcn_s_barrier();   // bare: a fenced barrier would wait for the K tiles too
+
+  uint32_t foff[KS];
+  frag_offsets<D>(foff, lane);
+  float out[16], m[16], z[16];
+  int own[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    out[i] = 0.f;
+    m[i] = kNegInf;
+    z[i] = 0.f;
+    const int h = 8 * (i / 4) + 4 * hl + (i % 4);
+    own[i] = h < p.H_q ? h / p.G : H;
+  }
+  u32x4 qf[KS];
+  const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&kn)[KS]) {
+    const int g = s % H;
+    if (s + S - 1 < steps) issue_k(s + S - 1);
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf[k]),
+                                                    __builtin_bit_cast(bf16x8, kc[k]), acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = own[i] == g ? acc[i] * p.c : out[i];
+    if (s + 1 < steps) {
+      // tile s+1 in; the tiles issued after it may still be on their way
+      wait_tiles(min(S - 2, steps - 2 - s));
+      read_frags<KS>(kn, lds_addr(ring[wave][(s + 1) % S]), foff);
+    }
+    if (g == H - 1) {
+      // every head's logit of key t is in: keep it and fold it into the statistics
+      const int t = t0_of(s) + nl;
+      const bool valid = t < Lb;
+      if constexpr (RETAIN) {
+        const int j = s / H;
+#pragma unroll
+        for (int jj = 0; jj < kDeltaKeepTiles; ++jj)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) keep[jj][i] = jj == j ? out[i] : keep[jj][i];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (valid && own[i] < H) lse_add(m[i], z[i], out[i]);
+      }
+    }
+    if (s + 1 < steps) wait_lgkm<KS>(kn);
+  };
+  u32x4 k0[KS], k1[KS];
+  if (steps > 0) {
+    wait_tiles(pre - 1);
+    read_frags<KS>(k0, lds_addr(ring[wave][0]), foff);
+    wait_lgkm<KS>(k0);
+    read_frags<KS>(qf, lds_addr(qs), foff);
+    wait_lgkm<KS>(qf);
+  }
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(s, k0, k1);
+    step(s + 1, k1, k0);
+  }
+  if (s < steps) step(s, k0, k1);
+  // statistics of each row over the workgroup's keys: lanes of a half, then waves
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float mm = m[i], zz = z[i];
+#pragma unroll
+    for (int d = 1; d < 32; d *= 2) {
+      const float m2 = __shfl_xor(mm, d), z2 = __shfl_xor(zz, d);
+      lse_fold(mm, zz, m2, z2);
+    }
+    if (nl == 0) red[wave][8 * (i / 4) + 4 * hl + (i % 4)] = make_float2(mm, zz);
+  }
+  __syncthreads();
+  for (int h = threadIdx.x; h < p.H_q; h += kThreads) {
+    float mm = kNegInf, zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float2 v = red[w][h];
+      lse_fold(mm, zz, v.x, v.y);
+    }
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p.cstats + ((int64_t)b * p.n_chunk + chunk) * p.H_q + h),
+                       __builtin_bit_cast(uint64_t, make_float2(mm, zz)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// rho of sequence b from its page scores (written earlier in the launch by
+// other workgroups, so read with device-scope loads): the top K - L older
+// pages (ascending), the last min(L, pages) pages, then -1, as
+// topk_delta_kernel computes it, with kThreads threads of kKpt pages each.
+__device__ __forceinline__ void delta_select(const DeltaLaunch& p, int b, uint32_t* hist,
+                                             Shared& sh) {
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int n_pages = (Lb + p.P - 1) / p.P;
+  const int n_recent = min(p.L_recent, n_pages);
+  const int n_cand = n_pages - n_recent;
+  const int keep = min(p.K_pages - p.L_recent, n_cand);
+  const float* Sb = p.S + (int64_t)b * p.n_pages_max;
+  int32_t* out = p.rho + (int64_t)b * p.K_pages;
+  const int i0 = (int)threadIdx.x * kKpt;
+  uint32_t o[kKpt], valid = 0;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool in = i0 + e < n_cand;
+    valid |= in ? (1u << e) : 0u;
+    o[e] = ord_key(in ? __uint_as_float(__hip_atomic_load(
+                            reinterpret_cast<const uint32_t*>(Sb + i0 + e), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT))
+                      : 0.f);
+  }
+  int ph = 0;
+  Kstar ks{0u, 0u, 0u};
+  uint32_t gt = valid, eq = 0u;
+  if (keep == 0) {
+    gt = 0u;
+  } else if (keep < n_cand) {
+    ks = select_regs<kThreads>(o, 0u, valid, (uint32_t)keep, hist, sh, ph);
+    classify(o, 0u, valid, ks, gt, eq);
+  }
+  uint32_t pos, rank, tg, te;
+  place<kThreads>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool q = (eq >> e) & 1u;
+    if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = i0 + e;
+    rank += q;
+  }
+  for (int i = threadIdx.x; i < p.K_pages - keep; i += kThreads)
+    out[keep + i] = i < n_recent ? n_cand + i : -1;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t qs[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDeltaStages][tile_bytes<D>()];
+  __shared__ float2 red[kWaves][32];
+  __shared__ float bh[32];
+  __shared__ float ys[kDeltaKeepTiles * kWaves * 32];
+  __shared__ int sh;
+  __shared__ Shared ssel;
+  const DeltaLaunch& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 31, hl = lane >> 5;
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int Lb = min(max(p.L[b], 0), p.L_max);
+  const int tb = chunk * p.chunk;
+  if (tb >= Lb) {   // the whole workgroup: nothing of this sequence here
+    if (a.sel && chunk == 0) delta_select(p, b, nullptr, ssel);   // an empty sequence's row
+    return;
+  }
+  const int te = min(tb + p.chunk, Lb);
+  float keep[kDeltaKeepTiles][16];
+  delta_chunk_pass<D, true>(p, b, chunk, qs, ring, red, keep);
+  uint64_t* flags = p.flags + (int64_t)b * p.n_chunk;
+  split_publish(flags + chunk, p.epoch);
+  const int nch = (Lb + p.chunk - 1) / p.chunk;
+  if (!head_wait(flags, p.epoch, nch, p.wait_ticks, &sh)) {
+    for (int c = 0; c < nch; ++c) {
+      if (threadIdx.x == 0)
+        sh = __hip_atomic_load(flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch;
+      __syncthreads();
+      const int done = __builtin_amdgcn_readfirstlane(sh);
+      __syncthreads();
+      if (!done) {
+        delta_chunk_pass<D, false>(p, b, c, qs, ring, red, keep);
+        split_publish(flags + c, p.epoch);
+      }
+    }
+  }
+  // b_h = m_h + log2 Z_h over the sequence's chunks, folded in the order
+  // delta_page_kernel folds them (strided shares of its threads per head,
+  // then the shares in turn), so the two paths agree bit for bit
+  if (threadIdx.x < p.H_q) {
+    const int h = threadIdx.x;
+    const int tph = kDeltaPageTokens / p.H_q;
+    const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q + h;
+    float m2 = kNegInf, z2 = 0.f;
+    for (int j = 0; j < tph; ++j) {
+      float mm = kNegInf, zz = 0.f;
+      for (int c = j; c < nch; c += tph) {
+        const float2 w = __builtin_bit_cast(
+            float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(cs + (int64_t)c * p.H_q),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        lse_fold(mm, zz, w.x, w.y);
+      }
+      lse_fold(m2, z2, mm, zz);
+    }
+    bh[h] = m2 + log2f(z2);
+  }
+  __syncthreads();
+  // token scores: the maximum over heads of exp2(x - b_h), this lane's 16
+  // rows, then the other half's
+  const int n_tiles = (te - tb + 31) / 32;
+  const int nt = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+  float bl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = 8 * (i / 4) + 4 * hl + (i % 4);
+    bl[i] = h < p.H_q ? bh[h] : kPosInf;   // exp2(x - inf) = 0 leaves the max at >= 0
+  }
+#pragma unroll
+  for (int j = 0; j < kDeltaKeepTiles; ++j) {
+    if (j < nt) {
+      float sv = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv = fmaxf(sv, ex2(keep[j][i] - bl[i]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv), __float_as_uint(sv),
+                                                       false, false);
+      sv = fmaxf(sv, __uint_as_float(hl ? sw[0] : sw[1]));
+      const int t = tb + (wave + kWaves * j) * 32 + nl;
+      if (hl == 0 && t < te) ys[t - tb] = sv;
+    }
+  }
+  __syncthreads();
+  // page sums, left to right (the chunk is a whole number of pages)
+  const int u0 = tb / p.P, u1 = (te + p.P - 1) / p.P;
+  float* Sb = p.S + (int64_t)b * p.n_pages_max;
+  for (int u = u0 + (int)threadIdx.x; u < u1; u += kThreads) {
+    const int a0 = u * p.P, a1 = min(a0 + p.P, te);
+    float acc = 0.f;
+    for (int tt = a0; tt < a1; ++tt) acc += ys[tt - tb];
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(Sb + u), __float_as_uint(acc), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!a.sel) return;
+  // The workgroup that finds every chunk of its sequence published selects
+  // the pages (no waiting: the last to publish sees all the flags; two that
+  // publish together both select and write the same row).
+  uint64_t* pflags = p.pflags + (int64_t)b * p.n_chunk;
+  split_publish(pflags + chunk, p.epoch);
+  if (!head_wait(pflags, p.epoch, nch, 0, &sh)) return;
+  delta_select(p, b, reinterpret_cast<uint32_t*>(&ring[0][0][0]), ssel);
+}
+
 template <int D, int NT>
-kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream) {
-  DeltaArgs a{p};
+kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream, int* selected) {
+  DeltaArgs a{p, 0};
+  *selected = 0;
+  if (NT == 1 && p.flags && p.chunk <= 32 * kWaves * kDeltaKeepTiles && p.chunk % p.P == 0 &&
+      (int64_t)p.n_chunk * p.B <=
+          (int64_t)fused_capacity(reinterpret_cast<const void*>(&delta_fused_kernel<D>))) {
+    a.p.epoch = next_epoch();
+    a.p.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+    a.sel = p.pflags && p.n_pages_max <= kThreads * kKpt;
+    hipLaunchKernelGGL((delta_fused_kernel<D>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
+    *selected = a.sel;
+    return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+  }
   hipLaunchKernelGGL((delta_logits_kernel<D, NT>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
   const int n_page_wg = (p.L_max + kDeltaPageTokens - 1) / kDeltaPageTokens;
   hipLaunchKernelGGL(delta_page_kernel, dim3(n_page_wg, p.B), dim3(kDeltaPageTokens), 0, stream, a);
@@ -2005,12 +2320,12 @@ kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream) {
 }
 
 template <int D>
-kvs_status delta_launch_d(const DeltaLaunch& p, hipStream_t stream) {
+kvs_status delta_launch_d(const DeltaLaunch& p, hipStream_t stream, int* selected) {
   switch ((p.H_q + 31) / 32) {
-    case 1: return delta_launch<D, 1>(p, stream);
-    case 2: return delta_launch<D, 2>(p, stream);
-    case 3: return delta_launch<D, 3>(p, stream);
-    case 4: return delta_launch<D, 4>(p, stream);
+    case 1: return delta_launch<D, 1>(p, stream, selected);
+    case 2: return delta_launch<D, 2>(p, stream, selected);
+    case 3: return delta_launch<D, 3>(p, stream, selected);
+    case 4: return delta_launch<D, 4>(p, stream, selected);
     default: return KVS_EUNSUPPORTED;
   }
 }
@@ -2024,9 +2339,9 @@ int delta_chunk(int B, int L_max) {
   return (int)(32 * kWaves * tpw);
 }
 
-kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream) {
-  if (p.d_k == 128) return delta_launch_d<128>(p, stream);
-  if (p.d_k == 64) return delta_launch_d<64>(p, stream);
+kvs_status delta_scores_run(const DeltaLaunch& p, hipStream_t stream, int* selected) {
+  if (p.d_k == 128) return delta_launch_d<128>(p, stream, selected);
+  if (p.d_k == 64) return delta_launch_d<64>(p, stream, selected);
   return KVS_EUNSUPPORTED;
 }
 

@@ -84,6 +84,8 @@ CASES = [
     ([777, 1234], 16, 16, 128, 32, 10, 0),                          # MHA, no recent pages
     ([900, 2049], 96, 8, 64, 16, 8, 2),                             # three row tiles, G = 12
     ([1500, 700], 128, 8, 128, 16, 16, 4),                          # four row tiles, G = 16
+    ([1, 15, 16, 17, 100, 1000, 2500, 0], 32, 8, 128, 16, 8, 2),   # ragged, in one launch
+    ([5000, 3000], 32, 8, 64, 512, 4, 1),                           # pages longer than a chunk
 ]
 
 
@@ -101,6 +103,28 @@ def test_delta_sequence_major_and_deterministic(kvs):
     b = _run_batch(kvs, lens, 32, 8, 128, 16, 64, 8, seq_major=True, seed=3)
     assert np.array_equal(a[1], b[1])
     assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+
+
+@pytest.mark.parametrize("lens,H_q,H_kv,d_k,P", [
+    ([3000, 17, 2600, 0, 1024], 32, 8, 128, 16),
+    ([1500], 32, 1, 64, 8),
+    ([777, 1234], 16, 16, 128, 32),
+], ids=["ragged", "one_kv_head", "mha"])
+def test_delta_one_launch_late_chunk_path(kvs, lens, H_q, H_kv, d_k, P):
+    """With the wait bound at 0, every workgroup of the one-launch form that finds its
+    sequence incomplete computes the missing chunks' statistics itself: the page scores and
+    page sets must equal the default run's bit for bit, and the oracle's."""
+    print(f"delta late-chunk path lens={lens} H_q={H_q}", flush=True)
+    want = _run_batch(kvs, lens, H_q, H_kv, d_k, P, 16, 4, seed=5)
+    prev = kvs.kvs_wait_limit(0)
+    try:
+        got = [_run_batch(kvs, lens, H_q, H_kv, d_k, P, 16, 4, seed=5) for _ in range(2)]
+    finally:
+        assert kvs.kvs_wait_limit(prev) == 0
+    for g in got:
+        assert np.array_equal(want[1], g[1])
+        assert np.array_equal(want[2].view(np.uint32), g[2].view(np.uint32))
+    _check(want[0], lens, want[1], want[2], H_q, H_kv, d_k, P, 16, 4)
 
 
 @pytest.mark.slow

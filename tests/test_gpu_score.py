@@ -199,11 +199,11 @@ def test_one_launch_late_split_path(kvs, name, L, W, d_k, H_q, H_kv, heads):
     two = kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=1), ws=ws)
     two = kvs.kvs_score(Q, K, kvs.score_args(**shape, phase=2), S=two, ws=ws)
     ws.fill_(0xA5)
-    prev = kvs.kvs_score_wait_limit(0)
+    prev = kvs.kvs_wait_limit(0)
     try:
         late = [kvs.kvs_score(Q, K, kvs.score_args(**shape), ws=ws) for _ in range(2)]
     finally:
-        assert kvs.kvs_score_wait_limit(prev) == 0
+        assert kvs.kvs_wait_limit(prev) == 0
     ws.fill_(0xFF)
     fast = kvs.kvs_score(Q, K, kvs.score_args(**shape), ws=ws)
     torch.cuda.synchronize()
