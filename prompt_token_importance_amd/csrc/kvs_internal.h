@@ -50,8 +50,13 @@ struct ScoreLaunch {
 };
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* plan);
-// Sets the one-launch forms' wait bound (microseconds, < 0: unchanged);
-// returns the previous one.
+// One-launch forms (grid.hip, grid_sync.h): the workgroups of kernel fn
+// (of `threads` threads) the current device holds at once (-1: unknown), a
+// fresh launch tag, and the wait bound in 100 MHz ticks; wait_limit sets that
+// bound (microseconds, < 0: unchanged) and returns the previous one.
+int grid_capacity(const void* fn, int threads);
+uint64_t grid_epoch();
+int64_t grid_wait_ticks();
 int32_t wait_limit(int32_t us);
 kvs_status score_run(const ScorePlan& plan, const ScoreLaunch& p, hipStream_t stream);
 

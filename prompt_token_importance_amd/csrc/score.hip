@@ -40,13 +40,11 @@
 //  * No R x L logit matrix is ever stored: K is read once per pass.
 #include <math.h>
 
-#include <atomic>
-#include <chrono>
-#include <mutex>
 
 #include <type_traits>
 
 #include "kvs_internal.h"
+#include "grid_sync.h"
 #include "select_ops.h"
 
 namespace kvs {
@@ -838,53 +836,6 @@ __device__ __forceinline__ void merge_rows(const KArgs& a, int g, int rows, floa
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ fused launch
-// Both passes in one launch: a workgroup streams its split for the row
-// statistics, publishes them, and starts its column-sum pass once every split
-// of its KV head is published (each pass-2 workgroup folds all of its head's
-// splits).  Every (KV head, split) has a 64-bit flag in the workspace, and
-// publishing stores the launch's epoch in it: a value no earlier launch of the
-// process used, so flags left by earlier launches never read as published and
-// the workspace needs no clearing.  Nothing is read-modify-written: the 32 or
-// so workgroups of a head finish together, and updates of one shared counter
-// would queue one device-scope round trip behind another.  The XCDs' L2
-// caches are not coherent with each other, so statistics and flags travel as
-// device-scope atomic stores and loads, which reach the device's point of
-// coherence, and a workgroup publishes only after its statistics stores have
-// completed.  The host takes this launch only when the whole grid fits on the
-// device at once.  Should a split still be unpublished when a waiter's time
-// bound runs out (the device shared with other work), the waiter computes
-// that split's statistics itself; they come out bit-identical to the owner's.
-__device__ __forceinline__ void split_publish(uint64_t* flag, uint64_t epoch) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's statistics are stored
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave 0 polls the n flags of a head (lane s reads splits s, s + 64, ...)
-// until all hold epoch or wait_ticks of the 100 MHz clock have passed.
-// Returns in every thread whether all were published.
-__device__ __forceinline__ bool head_wait(const uint64_t* flags, uint64_t epoch, int n,
-                                          int64_t wait_ticks, int* sh) {
-  if (threadIdx.x < 64) {
-    const int64_t t0 = (int64_t)__builtin_amdgcn_s_memrealtime();
-    int all;
-    for (;;) {
-      int ok = 1;
-      for (int s = threadIdx.x; s < n; s += 64)
-        ok &= __hip_atomic_load(flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-      all = __all(ok);
-      if (all || (int64_t)__builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-    if (threadIdx.x == 0) *sh = all;
-  }
-  __syncthreads();
-  const int r = __builtin_amdgcn_readfirstlane(*sh);
-  __syncthreads();   // before sh is written again
-  return r != 0;
-}
-
 // ------------------------------------------------------------------ pass 2
 __device__ __forceinline__ void store_out(float* o, float v, int accumulate) {
   *o = accumulate ? *o + v : v;
@@ -1184,7 +1135,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_colsum_kernel(KArgs a) {
   colsum_body<D, NT, MODE, false>(a, ring, rvis, brow, q, false, [] { return false; });
 }
 
-// Both passes of one row group in one launch (see split_publish).
+// Both passes of one row group in one launch (see grid_sync.h).
 template <int D, int NT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void score_fused_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kStages][tile_bytes<D>()];
@@ -1195,9 +1146,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_fused_kernel(KArgs a) {
   bf16x8 q[NT][D / 16];
   uint64_t* flags = a.flag + (int64_t)(a.g0 + blockIdx.y) * a.n_split;
   const bool kept = stats_body<D, NT, true>(a, blockIdx.x, ring, sm, q);
-  split_publish(flags + blockIdx.x, a.epoch);
+  publish_flag(flags + blockIdx.x, a.epoch);
   const auto settle = [&]() -> bool {
-    if (head_wait(flags, a.epoch, a.n_split, a.wait_ticks, &sh)) return false;
+    if (wait_flags(flags, a.epoch, a.n_split, a.wait_ticks, &sh)) return false;
     // some split is late: compute it here (its first tile's load lands first)
     wait_vm<0>();
     __syncthreads();
@@ -1209,7 +1160,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_fused_kernel(KArgs a) {
       __syncthreads();
       if (!done) {
         stats_body<D, NT, true>(a, s, ring, sm, q);
-        split_publish(flags + s, a.epoch);
+        publish_flag(flags + s, a.epoch);
       }
     }
     return true;
@@ -1450,42 +1401,13 @@ void launch_group(const KArgs& a, int pass, int mode, dim3 grid, hipStream_t str
     hipLaunchKernelGGL((score_colsum_kernel<D, NT, 1>), grid, dim3(kThreads), 0, stream, a);
 }
 
-// The fused launch needs every workgroup resident at once (a workgroup waits
-// for the others of its KV head), so it is taken only when the occupancy the
-// runtime reports for the kernel, times the device's CUs, covers the grid.
-// The answer is kept per device and kernel.
-struct FitEntry {
-  int dev;
-  const void* fn;
-  int blocks;   // resident workgroups the device holds, -1: unknown
-};
-
-int fused_capacity(const void* fn) {
-  static std::mutex mu;
-  static FitEntry table[64];
-  static int used = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (table[i].dev == dev && table[i].fn == fn) return table[i].blocks;
-  int per_cu = 0, cus = 0;
-  int blocks = -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-    blocks = per_cu * cus;
-  (void)hipGetLastError();
-  if (used < 64) table[used++] = FitEntry{dev, fn, blocks};
-  return blocks;
-}
-
 // Launches the fused kernel; false (nothing launched) when the grid does not
 // fit on the device at once.
 template <int D, int NT>
 bool launch_fused(const KArgs& a, int mode, dim3 grid, hipStream_t stream) {
   const void* fn = mode == 0 ? reinterpret_cast<const void*>(&score_fused_kernel<D, NT, 0>)
                              : reinterpret_cast<const void*>(&score_fused_kernel<D, NT, 1>);
-  if ((int64_t)grid.x * grid.y > (int64_t)fused_capacity(fn)) return false;
+  if ((int64_t)grid.x * grid.y > (int64_t)grid_capacity(fn, kThreads)) return false;
   if (mode == 0)
     hipLaunchKernelGGL((score_fused_kernel<D, NT, 0>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -1502,19 +1424,6 @@ bool launch_fused_nt(int nt, const KArgs& a, int mode, dim3 grid, hipStream_t st
     default: return launch_fused<D, 4>(a, mode, grid, stream);
   }
 }
-
-// A fresh tag for every fused launch of the process, never 0 (the value of a
-// zeroed workspace); the start is drawn from the clock, so flags left in a
-// recycled workspace by another process are not mistaken for this launch's.
-uint64_t next_epoch() {
-  static std::atomic<uint64_t> next{
-      ((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull) >> 8};
-  return next.fetch_add(1, std::memory_order_relaxed) | (1ull << 63);
-}
-
-// Bound on a one-launch workgroup's wait for the rest of its KV head or
-// sequence, in ticks of the 100 MHz clock (kvs_wait_limit); 2 ms by default.
-std::atomic<int64_t> g_wait_ticks{200000};
 
 template <int D>
 void launch_group_nt(int nt, const KArgs& a, int pass, int mode, dim3 grid, hipStream_t stream) {
@@ -1551,7 +1460,7 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
       (p.heads == KVS_HEADS_GROUP_SUM || all_sum || pl.head_rows > 128) ? 0 : 1;
   a.flag = p.flags;
   a.epoch = 0;
-  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+  a.wait_ticks = grid_wait_ticks();
   // Both passes of a single row group in one launch when the device can hold
   // the whole grid at once.
   if (p.phase == 0 && pl.n_groups == 1 && p.flags) {
@@ -1562,7 +1471,7 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
     a.out = all_sum ? p.head_rows_ws : p.S;
     a.out_ld = all_sum ? (int64_t)p.L : p.s_ld;
     a.acc = all_sum ? 0 : p.accumulate;
-    a.epoch = next_epoch();
+    a.epoch = grid_epoch();
     if (launch_fused_nt<D>(pl.grp_rows[0] / 32, a, mode, grid, stream)) {
       if (all_sum)
         hipLaunchKernelGGL(score_head_sum_kernel, dim3((p.L + 255) / 256), dim3(256), 0, stream,
@@ -1595,12 +1504,6 @@ kvs_status launch_d(const ScorePlan& pl, const ScoreLaunch& p, hipStream_t strea
 }
 
 }  // namespace
-
-int32_t wait_limit(int32_t us) {
-  const int64_t prev = g_wait_ticks.load(std::memory_order_relaxed);
-  if (us >= 0) g_wait_ticks.store((int64_t)us * 100, std::memory_order_relaxed);
-  return (int32_t)(prev / 100);
-}
 
 kvs_status score_plan(const kvs_score_args* a, ScorePlan* pl) {
   const int G = a->H_q / a->H_kv;
@@ -2009,7 +1912,7 @@ __global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs 
 // kernels above do, without writing the logits anywhere: each workgroup
 // streams its chunk as delta_logits_kernel does and keeps its logits in
 // registers, publishes its chunk's statistics (flags as in the one-launch
-// score form, see split_publish), waits for the other chunks of its
+// score form, see grid_sync.h), waits for the other chunks of its
 // sequence, folds them into b_h in delta_page_kernel's order, and forms the
 // token and page scores from its registers.  Results are bit-identical to
 // the two kernels'.  A chunk still unpublished at the wait bound is computed
@@ -2219,9 +2122,9 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
   float keep[kDeltaKeepTiles][16];
   delta_chunk_pass<D, true>(p, b, chunk, qs, ring, red, keep);
   uint64_t* flags = p.flags + (int64_t)b * p.n_chunk;
-  split_publish(flags + chunk, p.epoch);
+  publish_flag(flags + chunk, p.epoch);
   const int nch = (Lb + p.chunk - 1) / p.chunk;
-  if (!head_wait(flags, p.epoch, nch, p.wait_ticks, &sh)) {
+  if (!wait_flags(flags, p.epoch, nch, p.wait_ticks, &sh)) {
     for (int c = 0; c < nch; ++c) {
       if (threadIdx.x == 0)
         sh = __hip_atomic_load(flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch;
@@ -2230,7 +2133,7 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
       __syncthreads();
       if (!done) {
         delta_chunk_pass<D, false>(p, b, c, qs, ring, red, keep);
-        split_publish(flags + c, p.epoch);
+        publish_flag(flags + c, p.epoch);
       }
     }
   }
@@ -2294,8 +2197,8 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
   // the pages (no waiting: the last to publish sees all the flags; two that
   // publish together both select and write the same row).
   uint64_t* pflags = p.pflags + (int64_t)b * p.n_chunk;
-  split_publish(pflags + chunk, p.epoch);
-  if (!head_wait(pflags, p.epoch, nch, 0, &sh)) return;
+  publish_flag(pflags + chunk, p.epoch);
+  if (!wait_flags(pflags, p.epoch, nch, 0, &sh)) return;
   delta_select(p, b, reinterpret_cast<uint32_t*>(&ring[0][0][0]), ssel);
 }
 
@@ -2305,9 +2208,9 @@ kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream, int* selected)
   *selected = 0;
   if (NT == 1 && p.flags && p.chunk <= 32 * kWaves * kDeltaKeepTiles && p.chunk % p.P == 0 &&
       (int64_t)p.n_chunk * p.B <=
-          (int64_t)fused_capacity(reinterpret_cast<const void*>(&delta_fused_kernel<D>))) {
-    a.p.epoch = next_epoch();
-    a.p.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+          (int64_t)grid_capacity(reinterpret_cast<const void*>(&delta_fused_kernel<D>), kThreads)) {
+    a.p.epoch = grid_epoch();
+    a.p.wait_ticks = grid_wait_ticks();
     a.sel = p.pflags && p.n_pages_max <= kThreads * kKpt;
     hipLaunchKernelGGL((delta_fused_kernel<D>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
     *selected = a.sel;

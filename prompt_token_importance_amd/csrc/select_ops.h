@@ -217,6 +217,30 @@ __device__ __forceinline__ void hist_add(uint32_t* h, const uint32_t (&o)[kKpt],
       atomicAdd(&h[(o[e] >> shift) & dm], 1u);
 }
 
+// hist_add with one atomic per run of equal digits among a thread's keys
+// (consecutive elements): pooled or smoothed scores put neighbours in the
+// same few bins, where one atomic per key would queue on the same address.
+// It costs more than it saves on unsmoothed scores.
+__device__ __forceinline__ void hist_add_runs(uint32_t* h, const uint32_t (&o)[kKpt], uint32_t cm,
+                                              uint32_t prefix, int hi, int w, bool first) {
+  const int shift = hi - w;
+  const uint32_t dm = (1u << w) - 1u;
+  uint32_t cur = 0, cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    if (((cm >> e) & 1u) && (first || ((o[e] ^ prefix) >> hi) == 0u)) {
+      const uint32_t d = (o[e] >> shift) & dm;
+      if (cnt && d != cur) {
+        atomicAdd(&h[cur], cnt);
+        cnt = 0;
+      }
+      cur = d;
+      ++cnt;
+    }
+  }
+  if (cnt) atomicAdd(&h[cur], cnt);
+}
+
 // Radix select over keys held in registers.  `hist` holds kSelWords words:
 // the three pass histograms, then the list.  After the first pass only the
 // class keys of the chosen bin can hold K*; when they fit the list they are

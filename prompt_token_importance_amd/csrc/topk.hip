@@ -24,6 +24,9 @@
 // Both stages run the in-register selection of select_ops.h.
 #include <math.h>
 
+#include <type_traits>
+
+#include "grid_sync.h"
 #include "kvs_internal.h"
 #include "select_ops.h"
 #include "wave_ops.h"
@@ -212,8 +215,10 @@ __device__ __forceinline__ void cluster_page_keys(const Params& s, const float* 
 
 // Keys of this thread's elements i0 + e (i0 = p0 + 16 * tid) of the part
 // [p0, p1): value bits o[e], priority bit e of pb, and bit e of `valid` when
-// i0 + e < p1.  Leaves `smem` free.
-template <int T, int NT>
+// i0 + e < p1.  Leaves `smem` free.  FAST takes the register-window forms of
+// the pooling and cluster transforms where they apply; without it the scores
+// are staged in LDS (the same keys, fewer registers).
+template <int T, int NT, bool FAST = true>
 __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int p1, uint32_t* smem,
                                           int* cen, uint32_t (&o)[kKpt], uint32_t& pb,
                                           uint32_t& valid) {
@@ -250,7 +255,7 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
   } else if constexpr (T == kPool) {
     // pooled value over [t - r, t + r] clipped to [0, n): max (NaN if any term
     // is NaN) or the left-to-right float32 mean of the in-range terms
-    if (s.pool_r <= kWin && s.vec && s.n % 4 == 0) {
+    if (FAST && s.pool_r <= kWin && s.vec && s.n % 4 == 0) {
       float w[kKpt + 2 * kWin];
       load_window(s, x, i0, w);
       if (s.pool_r == 3)
@@ -292,7 +297,7 @@ __device__ __forceinline__ void part_keys(const Params& s, int row, int p0, int 
     // argmax (lowest index) of a page of P tokens whose maximum is >= theta;
     // a page holding a NaN has no centre.  Pages [qa, qb] hold every centre
     // that can reach the part.
-    if (s.P == 16 && s.r <= kWin && s.vec && s.n % 4 == 0) {
+    if (FAST && s.P == 16 && s.r <= kWin && s.vec && s.n % 4 == 0) {
       cluster_page_keys<NT>(s, x, i0, p0, cen, o, pb);
       return;
     }
@@ -721,6 +726,243 @@ __global__ __launch_bounds__(kT) void topk_wide_kernel(Params s) {
   }
 }
 
+// ------------------------------------------------------------------ one launch
+// Wide rows (2 to kWideMaxParts parts of kCap elements) run the whole
+// selection in one launch when the grid fits on the device at once: the phases
+// (class statistics, up to three digit histograms, the counts of keys above
+// and equal to K*) become exchanges between the parts of a row, with every
+// part's keys in registers from first to last.  An exchanged value travels as
+// 16-bit fields of 64-bit words whose upper 48 bits carry the launch's tag, a
+// value no earlier launch of the process used (grid_sync.h): a part stores
+// its words with device-scope stores and reads the others' with device-scope
+// loads until every tag matches, one memory round trip when the parts keep
+// pace, and no word needs clearing between launches.  A part whose words are
+// still missing when a reader's bound runs out is computed by the reader from
+// the scores (its keys, then that phase's integers, identical to the owner's).
+constexpr int kGridStat = 9;                      // count, then 4 x (hi, lo) of min/max
+constexpr int kGridCnt = kGridStat;               // gt, eq
+constexpr int kGridHist = 16;                     // the digit histograms start here
+constexpr int kGridWords = kGridHist + 1024 + 2048 + 2048;   // per (row, part)
+constexpr int kGridPhases = 5;                    // statistics, three digit passes, counts
+constexpr int kGridCopies = 4;                    // LDS copies of a digit histogram
+static_assert(kGridCopies * 2048 <= kSelWords, "the histogram copies fit a selection's LDS");
+
+// Digit widths of the one-launch passes (10 + 11 + 11 = 32 bits in three
+// passes, the widest first pass one bin per thread) and their histogram
+// offsets.
+__device__ __forceinline__ constexpr int grid_pass_width(int p) { return p == 0 ? 10 : 11; }
+__device__ __forceinline__ constexpr int grid_pass_offset(int p) {
+  return p == 0 ? 0 : p == 1 ? 1024 : 3072;
+}
+
+struct GridArgs {
+  Params s;
+  uint64_t* words;   // [H][parts][kGridWords]
+  uint64_t tag;      // the launch's tag in the upper 48 bits
+  int64_t wait_ticks;
+};
+
+template <int T>
+__global__ __launch_bounds__(kT) void topk_grid_kernel(GridArgs g) {
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LdsWords<T, kT>::value];
+  __shared__ int cen[T == kCluster ? kT + 2 : 1];
+  __shared__ Shared sh;
+  __shared__ uint32_t missing;   // parts whose words a reader gave up waiting for
+  const Params& s = g.s;
+  const int row = blockIdx.y, part = blockIdx.x;
+  const uint64_t tag = g.tag;
+  uint64_t* rw = g.words + (int64_t)row * s.parts * kGridWords;
+  const auto word = [&](int q, int i) { return rw + (int64_t)q * kGridWords + i; };
+  const auto put16 = [&](int q, int i, uint32_t v) {
+    __hip_atomic_store(word(q, i), tag | (v & 0xFFFFu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint32_t o[kKpt], pb, valid;
+  // keys of part q; in the late-part path (inside the phase loop) through
+  // LDS staging, which needs fewer registers than the register windows
+  const auto keys_of = [&](int q, auto fast) {
+    // q opaque: the addresses are computed at each call rather than kept
+    // live from the first to the last
+    asm volatile("" : "+s"(q));
+    const int q0 = q * kCap, q1 = min(q0 + kCap, s.n);
+    part_keys<T, kT, decltype(fast)::value>(s, row, q0, q1, smem, cen, o, pb, valid);
+  };
+  keys_of(part, std::true_type{});
+  SelectStart a{0u, 0u, 0u, 0};
+  int ph_scan = 0;
+  // Phase ph's words of part q, from the keys in o / pb / valid.
+  const auto put = [&](int ph, int q) {
+    if (ph == 0) {
+      uint32_t st[5];
+      class_stats<kT>(o, pb, valid, sh, st);
+      const int j = threadIdx.x;
+      if (j < kGridStat) {
+        const uint32_t v = j == 0 ? st[0] : j <= 2 ? st[1] : j <= 4 ? st[2] : j <= 6 ? st[3] : st[4];
+        put16(q, j, j == 0 ? v : (j & 1) ? v >> 16 : v);
+      }
+      __syncthreads();   // sh.r is written again by the next use
+    } else if (ph <= 3) {
+      const int p = ph - 1;
+      const int w = min(a.hi, grid_pass_width(p));
+      const int nb = 1 << w;
+      // kGridCopies copies of the histogram, one per group of waves: keys
+      // that crowd into a few bins then queue on kGridCopies times fewer
+      // atomics each
+      __syncthreads();   // smem is free (key staging, the last sums)
+      for (int b = threadIdx.x; b < kGridCopies * nb; b += kT) smem[b] = 0u;
+      __syncthreads();
+      // the wide rows' scores are pooled or smoothed more often than not
+      hist_add_runs(smem + ((threadIdx.x >> 6) % kGridCopies) * nb, o,
+                    valid & (a.cls ? pb : ~pb), a.prefix, a.hi, w, p == 0);
+      __syncthreads();
+      for (int b = threadIdx.x; b < nb; b += kT) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int c = 0; c < kGridCopies; ++c) v += smem[c * nb + b];
+        put16(q, kGridHist + grid_pass_offset(p) + b, v);
+      }
+    } else {
+      uint32_t gt, eq, total;
+      classify(o, pb, valid, Kstar{a.cls, a.prefix, a.need}, gt, eq);
+      block_scan<kT>(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq), sh, ph_scan, total);
+      if (threadIdx.x == 0) {
+        put16(q, kGridCnt, total >> 16);
+        put16(q, kGridCnt + 1, total & 0xFFFFu);
+      }
+    }
+  };
+  // Reads this thread's words of phase ph into LDS: ph 0, word t of the
+  // row's statistics (9 per part); ph 1-3, the sum over the parts of bin t;
+  // ph 4, word t of the counts of the parts before this one.  Each load is
+  // repeated until its tag matches or the bound runs out; parts then still
+  // missing are marked in `missing`.
+  const auto gather = [&](int ph) {
+    const int t = threadIdx.x;
+    const int64_t t0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+    uint32_t miss = 0;
+    if (ph == 0 || ph == 4) {
+      const bool mine = ph == 0 ? t < kGridStat * s.parts : t < 2 * part;
+      const int q = ph == 0 ? t / kGridStat : t / 2;
+      const int i = ph == 0 ? t % kGridStat : kGridCnt + t % 2;
+      if (mine) {
+        for (;;) {
+          const uint64_t x = __hip_atomic_load(word(q, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((x >> 16) == (tag >> 16)) {
+            smem[t] = (uint32_t)(x & 0xFFFFu);
+            break;
+          }
+          if ((int64_t)__builtin_amdgcn_s_memrealtime() - t0 >= g.wait_ticks) {
+            miss = 1u << q;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    } else {
+      const int p = ph - 1;
+      const int nb = 1 << min(a.hi, grid_pass_width(p));
+      constexpr int QB = kWideMaxParts / 2;   // parts read at once
+      for (int b = t; b < nb; b += kT) {
+        uint32_t need = (1u << s.parts) - 1u;   // parts whose bin is not in yet
+        uint32_t v = 0;
+        for (;;) {
+          for (int q0 = 0; q0 < s.parts; q0 += QB) {
+            // QB parts' words at once: clamped addresses, no branch
+            uint64_t x[QB];
+#pragma unroll
+            for (int k = 0; k < QB; ++k)
+              x[k] = __hip_atomic_load(word(min(q0 + k, s.parts - 1), kGridHist + grid_pass_offset(p) + b),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+              const int q = q0 + k;
+              if (((need >> q) & 1u) && (x[k] >> 16) == (tag >> 16)) {
+                v += (uint32_t)(x[k] & 0xFFFFu);
+                need &= ~(1u << q);
+              }
+            }
+          }
+          if (!need) break;
+          if ((int64_t)__builtin_amdgcn_s_memrealtime() - t0 >= g.wait_ticks) {
+            miss |= need;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        smem[b] = v;
+      }
+    }
+    if (miss) atomicOr(&missing, miss);
+  };
+#pragma unroll 1
+  for (int ph = 0; ph < kGridPhases; ++ph) {
+    if (ph >= 1 && ph <= 3 && a.hi == 0) continue;   // K* settled (the same in every part)
+    put(ph, part);
+    // read the row's words; a part still missing at the bound is computed
+    // here, in this part's key registers, whose own keys are computed again
+    // afterwards (the transform is deterministic), and the words read again
+    for (int round = 0;; ++round) {
+      __syncthreads();   // smem is free; `missing` is read by nobody
+      if (threadIdx.x == 0) missing = 0u;
+      __syncthreads();
+      gather(ph);
+      __syncthreads();
+      const uint32_t m = __builtin_amdgcn_readfirstlane(missing);
+      if (!m || round == 1) break;   // after a round of computing, every word is in
+      for (int q = 0; q < s.parts; ++q) {
+        if (!((m >> q) & 1u)) continue;
+        keys_of(q, std::false_type{});
+        put(ph, q);
+      }
+      keys_of(part, std::false_type{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the words computed here are stored
+      __syncthreads();
+    }
+    if (ph == 0) {
+      uint32_t st[5] = {0u, ~0u, 0u, ~0u, 0u};
+      for (int q = 0; q < s.parts; ++q) {
+        const uint32_t* w = smem + kGridStat * q;
+        st[0] += w[0];
+        st[1] = min(st[1], (w[1] << 16) | w[2]);
+        st[2] = max(st[2], (w[3] << 16) | w[4]);
+        st[3] = min(st[3], (w[5] << 16) | w[6]);
+        st[4] = max(st[4], (w[7] << 16) | w[8]);
+      }
+      a = select_start(st, (uint32_t)s.budget);
+    } else if (ph <= 3) {
+      // the digit from the summed histogram
+      const int p = ph - 1;
+      const int w = min(a.hi, grid_pass_width(p));
+      pick_digit(smem, 1 << w, a.need, sh);
+      a.hi -= w;
+      a.prefix |= sh.digit << a.hi;
+      a.need = sh.need;
+    }
+  }
+  // this part's output offset and its share of the K*-equal keys
+  const Kstar ks{a.cls, a.prefix, a.need};
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int q = 0; q < part; ++q) {
+    gt_before += smem[2 * q];
+    eq_before += smem[2 * q + 1];
+  }
+  uint32_t gt, eq;
+  classify(o, pb, valid, ks, gt, eq);
+  uint32_t pos, rank, tg, te;
+  place<kT>(gt, eq, ks.need_eq, gt_before, eq_before, sh, ph_scan, pos, rank, tg, te);
+  const int i0 = part * kCap + (int)threadIdx.x * kKpt;
+  int32_t* out = s.idx + (int64_t)row * (s.budget + s.n_forced);
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool q = (eq >> e) & 1u;
+    if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) {
+      if (pos < (uint32_t)s.budget) out[pos] = i0 + e;   // the counts make pos < budget
+      ++pos;
+    }
+    rank += q;
+  }
+  if (part == 0) write_forced<kT>(s, out);
+}
+
 // ------------------------------------------------------------------ DELTA page sets
 // One workgroup per sequence (one wave when the pages fit 16 per lane): rho =
 // the top K - L older pages by page score (ascending), then the last min(L,
@@ -821,6 +1063,24 @@ void launch(const Params& s, int H, hipStream_t stream) {
   if (s.parts > 1) hipLaunchKernelGGL(topk_merge_kernel, dim3(H), dim3(kT), 0, stream, s);
 }
 
+// The one-launch form for rows of 2 to kWideMaxParts parts of kCap elements;
+// false (nothing launched) when the grid does not fit on the device at once.
+template <int T>
+bool launch_grid(const Params& s0, int H, void* ws, hipStream_t stream) {
+  GridArgs g;
+  g.s = s0;
+  g.s.part = kCap;
+  g.s.parts = ceil_div(s0.n, kCap);
+  if (g.s.parts < 2 || g.s.parts > kWideMaxParts) return false;
+  const void* fn = reinterpret_cast<const void*>(&topk_grid_kernel<T>);
+  if ((int64_t)g.s.parts * H > (int64_t)grid_capacity(fn, kT)) return false;
+  g.words = static_cast<uint64_t*>(ws);
+  g.tag = grid_epoch() << 16;
+  g.wait_ticks = grid_wait_ticks();
+  hipLaunchKernelGGL((topk_grid_kernel<T>), dim3(g.s.parts, H), dim3(kT), 0, stream, g);
+  return true;
+}
+
 template <int T>
 void launch_wide(const Params& s, int H, hipStream_t stream) {
   const dim3 grid(s.parts, H);
@@ -836,12 +1096,18 @@ void launch_wide(const Params& s, int H, hipStream_t stream) {
 
 size_t topk_ws_bytes(int H, int n, int budget) {
   if (budget <= 0 || n <= kCap) return 0;
+  const size_t parts = (size_t)ceil_div(n, kCap);
+  // the one-launch form of wide rows: tagged words per (row, part)
+  const size_t grid =
+      wide_path(n, budget) ? (size_t)H * parts * kGridWords * sizeof(uint64_t) : 0;
+  size_t other;
   if (wide_path(n, budget)) {
-    const size_t parts = (size_t)ceil_div(n, kCap);
     const size_t words = parts * kPartWords + kRowState + parts * kCap + parts * kT / 2;
-    return align_up((size_t)H * words * sizeof(uint32_t), kWsAlign);
+    other = (size_t)H * words * sizeof(uint32_t);
+  } else {
+    other = (size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t);
   }
-  return align_up((size_t)H * cand_ld_of(n, budget) * sizeof(uint64_t), kWsAlign);
+  return align_up(grid > other ? grid : other, kWsAlign);
 }
 
 kvs_status delta_topk_run(const DeltaLaunch& p, hipStream_t stream) {
@@ -897,6 +1163,16 @@ kvs_status select_indices(const SelectCall& c, hipStream_t stream) {
   s.idx = c.idx;
   const bool wide = wide_path(c.n, c.budget);
   if (!wide && (int64_t)s.parts * c.H > 0x7FFFFFFF) return KVS_EUNSUPPORTED;
+  // Rows selected across all their parts: one launch when the grid fits the
+  // device.  (Its exchanges cost about what a launch boundary does, 4-5 us
+  // each, so rows whose candidates fit one merge keep the two launches of
+  // local candidates and merge: one boundary against five exchanges.)
+  if (wide) {
+    const bool one = c.cluster_P > 0    ? launch_grid<kCluster>(s, c.H, c.ws, stream)
+                     : c.pool != KVS_RED_NONE ? launch_grid<kPool>(s, c.H, c.ws, stream)
+                                              : launch_grid<kPlain>(s, c.H, c.ws, stream);
+    if (one) return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
+  }
   if (c.cluster_P > 0)
     wide ? launch_wide<kCluster>(s, c.H, stream) : launch<kCluster>(s, c.H, stream);
   else if (c.pool != KVS_RED_NONE)

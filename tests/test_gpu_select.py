@@ -370,3 +370,51 @@ def test_select_matches_three_call_path(kvs):
                                              cluster_theta=theta, cluster_r=r))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind,budget", [("plain", 6000), ("plain", 20000), ("pool", 8000),
+                                         ("cluster", 6000)])
+def test_one_launch_select_late_part_path(kvs, kind, budget):
+    """Wide rows (more candidates than one merge holds) run in one launch whose parts exchange
+    their statistics, digit histograms and counts.  With the wait bound at 0, every part that
+    finds a word of its row missing computes the late parts' words itself: the indices must
+    equal the default run's and the oracle's."""
+    print(f"late-part select {kind} budget={budget}", flush=True)
+    H, n, nf = 3, 50000, 4
+    x = synth.score_array(7100 + budget, H, n, levels=6 if kind == "plain" else 0,
+                          signed=kind == "plain", with_zeros=kind == "plain")
+    prio = synth.priority_array(n, H, n) if kind == "plain" else None
+    if kind == "plain":
+        run = lambda: kvs.kvs_topk(dev(x), n, budget, priority=dev(prio), n_forced=nf)
+        want = oracle.topk(x, budget, prio, nf)
+    elif kind == "pool":
+        a = kvs.select_args(budget=budget, n_forced=nf, pool=kvs.RED_MAX, pool_k=7)
+        run = lambda: kvs.kvs_select(dev(x), n, a)
+        want = oracle.topk(oracle.pool(x, oracle.RED_MAX, 7), budget, None, nf)
+    else:
+        x = x * np.float32(1e-3)
+        a = kvs.select_args(budget=budget, n_forced=nf, cluster_P=16, cluster_theta=2e-3,
+                            cluster_r=3)
+        run = lambda: kvs.kvs_select(dev(x), n, a)
+        z, arg = oracle.pages(x, 16, oracle.RED_MAX)
+        want = oracle.topk(x, budget, oracle.cluster_priority(z, arg, n, float(np.float32(2e-3)), 3),
+                           nf)
+    base = run().cpu().numpy()
+    prev = kvs.kvs_wait_limit(0)
+    try:
+        late = [run().cpu().numpy() for _ in range(2)]
+    finally:
+        assert kvs.kvs_wait_limit(prev) == 0
+    np.testing.assert_array_equal(base, want)
+    for got in late:
+        np.testing.assert_array_equal(got, want)
+
+
+def test_select_grid_larger_than_device(kvs):
+    """130 wide rows of two parts each: more workgroups than the device holds at once, so the
+    selection takes the launch-per-phase form."""
+    H, n, budget = 130, 20000, 10000
+    x = synth.score_array(7300, H, n, levels=4, signed=True, with_zeros=True)
+    got = kvs.kvs_topk(dev(x), n, budget, n_forced=3)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x, budget, None, 3))
