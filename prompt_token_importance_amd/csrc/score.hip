@@ -1943,12 +1943,15 @@ __device__ __forceinline__ void delta_chunk_pass(const DeltaLaunch& p, int b, in
   const uint16_t* Kb = p.K[b];
   const int64_t khs = p.khs ? p.khs : (int64_t)Lb * D;
   const int H = p.H_kv;
+  // KV heads in an order rotated per workgroup, so that the workgroups do not
+  // all read the same head's region at the same offset at once
+  const int rot = (chunk + b) % H;
   const int n_tiles = (te - tb + 31) / 32;
   const int nt = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
   const int steps = nt * H;   // (key tile, KV head) pairs, KV head fastest
   const auto t0_of = [&](int s) { return tb + (wave + kWaves * (s / H)) * 32; };
   const auto issue_k = [&](int s) {
-    issue_tile<D>(ring[wave][s % S], Kb + (int64_t)(s % H) * khs, p.kts, t0_of(s), Lb, lane);
+    issue_tile<D>(ring[wave][s % S], Kb + (int64_t)((s % H + rot) % H) * khs, p.kts, t0_of(s), Lb, lane);
   };
   // at most n tiles' loads of this wave still in flight (n wave-uniform)
   const auto wait_tiles = [&](int n) {
@@ -1982,7 +1985,7 @@ __device__ __forceinline__ void delta_chunk_pass(const DeltaLaunch& p, int b, in
   }
   u32x4 qf[KS];
   const auto step = [&](int s, u32x4(&kc)[KS], u32x4(&kn)[KS]) {
-    const int g = s % H;
+    const int g = (s % H + rot) % H;
     if (s + S - 1 < steps) issue_k(s + S - 1);
     f32x16 acc = f32x16{};
 #pragma unroll
@@ -1996,7 +1999,7 @@ __device__ __forceinline__ void delta_chunk_pass(const DeltaLaunch& p, int b, in
       wait_tiles(min(S - 2, steps - 2 - s));
       read_frags<KS>(kn, lds_addr(ring[wave][(s + 1) % S]), foff);
     }
-    if (g == H - 1) {
+    if (s % H == H - 1) {   // the tile's last step
       // every head's logit of key t is in: keep it and fold it into the statistics
       const int t = t0_of(s) + nl;
       const bool valid = t < Lb;
@@ -2068,14 +2071,16 @@ __device__ __forceinline__ void delta_select(const DeltaLaunch& p, int b, uint32
   int32_t* out = p.rho + (int64_t)b * p.K_pages;
   const int i0 = (int)threadIdx.x * kKpt;
   uint32_t o[kKpt], valid = 0;
+  // clamped indices and no branch, so all the loads are in flight at once
+  const int last = n_cand > 0 ? n_cand - 1 : 0;
 #pragma unroll
   for (int e = 0; e < kKpt; ++e) {
     const bool in = i0 + e < n_cand;
     valid |= in ? (1u << e) : 0u;
-    o[e] = ord_key(in ? __uint_as_float(__hip_atomic_load(
-                            reinterpret_cast<const uint32_t*>(Sb + i0 + e), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT))
-                      : 0.f);
+    const float v = __uint_as_float(__hip_atomic_load(
+        reinterpret_cast<const uint32_t*>(Sb + min(i0 + e, last)), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT));
+    o[e] = ord_key(in ? v : 0.f);
   }
   int ph = 0;
   Kstar ks{0u, 0u, 0u};
@@ -2139,25 +2144,44 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
   }
   // b_h = m_h + log2 Z_h over the sequence's chunks, folded in the order
   // delta_page_kernel folds them (strided shares of its threads per head,
-  // then the shares in turn), so the two paths agree bit for bit
-  if (threadIdx.x < p.H_q) {
-    const int h = threadIdx.x;
-    const int tph = kDeltaPageTokens / p.H_q;
-    const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q + h;
-    float m2 = kNegInf, z2 = 0.f;
-    for (int j = 0; j < tph; ++j) {
-      float mm = kNegInf, zz = 0.f;
-      for (int c = j; c < nch; c += tph) {
-        const float2 w = __builtin_bit_cast(
-            float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(cs + (int64_t)c * p.H_q),
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        lse_fold(mm, zz, w.x, w.y);
-      }
-      lse_fold(m2, z2, mm, zz);
+  // then the shares in turn), so the two paths agree bit for bit.  The
+  // statistics are first staged in the idle K ring, one load per thread, all
+  // in flight together; a sequence with more than the ring holds is read in
+  // place.
+  {
+    const float2* cs = p.cstats + (int64_t)b * p.n_chunk * p.H_q;
+    float2* st = reinterpret_cast<float2*>(&ring[0][0][0]);
+    constexpr int kStaged = (int)(sizeof(ring) / sizeof(float2));
+    const int n_st = nch * p.H_q;
+    const bool staged = n_st <= kStaged;
+    if (staged) {
+      for (int i = threadIdx.x; i < n_st; i += kThreads)
+        st[i] = __builtin_bit_cast(
+            float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(cs + i), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT));
+      __syncthreads();
     }
-    bh[h] = m2 + log2f(z2);
+    if (threadIdx.x < p.H_q) {
+      const int h = threadIdx.x;
+      const int tph = kDeltaPageTokens / p.H_q;
+      float m2 = kNegInf, z2 = 0.f;
+      for (int j = 0; j < tph; ++j) {
+        float mm = kNegInf, zz = 0.f;
+        for (int c = j; c < nch; c += tph) {
+          const float2 w =
+              staged ? st[c * p.H_q + h]
+                     : __builtin_bit_cast(
+                           float2, __hip_atomic_load(
+                                       reinterpret_cast<const uint64_t*>(cs + (int64_t)c * p.H_q + h),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          lse_fold(mm, zz, w.x, w.y);
+        }
+        lse_fold(m2, z2, mm, zz);
+      }
+      bh[h] = m2 + log2f(z2);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // token scores: the maximum over heads of exp2(x - b_h), this lane's 16
   // rows, then the other half's
   const int n_tiles = (te - tb + 31) / 32;
