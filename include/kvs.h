@@ -330,8 +330,11 @@ kvs_status kvs_pool_pages(const float* S, int32_t H, int32_t n, int64_t ld,
  * undefined on entry and on return.  It holds the per-part candidates of the
  * two-stage select or, for rows whose candidates would not fit one merge
  * (more than 16384 of them: a large budget over several parts of 16384), the
- * rows' ranking keys with per-part histograms and counts; calls that share one
- * must not overlap in time.
+ * rows' per-part histograms and counts (and ranking keys); calls that share
+ * one must not overlap in time.  Those wide rows run in one launch when the
+ * device holds its whole grid at once, their parts exchanging histograms
+ * (kvs_wait_limit bounds their waits), else in one launch per phase; the
+ * result is the same.
  * ---------------------------------------------------------------------- */
 size_t kvs_topk_workspace(int32_t H, int32_t n, int32_t budget);
 kvs_status kvs_topk(const float* S, int32_t H, int32_t n, int64_t ld, int32_t budget,
