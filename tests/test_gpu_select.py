@@ -411,9 +411,9 @@ def test_one_launch_select_late_part_path(kvs, kind, budget):
 
 
 def test_select_grid_larger_than_device(kvs):
-    """130 wide rows of two parts each: more workgroups than the device holds at once, so the
+    """130 wide rows of three parts each: more workgroups than the device holds at once, so the
     selection takes the launch-per-phase form."""
-    H, n, budget = 130, 20000, 10000
+    H, n, budget = 130, 40000, 10000
     x = synth.score_array(7300, H, n, levels=4, signed=True, with_zeros=True)
     got = kvs.kvs_topk(dev(x), n, budget, n_forced=3)
     torch.cuda.synchronize()
