@@ -235,11 +235,13 @@ kvs_status kvs_score_raw(const kvs_raw_args* a, const void* Q, const void* K, fl
  * each sequence (other entries untouched), or NULL.
  * Workspace: kvs_delta_workspace bytes, 16-byte aligned, contents undefined
  * on entry and return (the logits of every head, 4 * H_q bytes per cached
- * token, per-chunk softmax statistics and an 8-byte flag per chunk).  With
+ * token, per-chunk softmax statistics, an 8-byte flag per chunk and an 8-byte
+ * word per page).  With
  * H_q <= 32, when the logits of the batch fit in registers (B * L_max up to
  * about 256K tokens) and the device holds the whole grid at once, one launch
- * computes the page scores without writing the logits (the flags order its
- * workgroups); the result is the same bit for bit.
+ * computes the page scores and rho without writing the logits (the flags
+ * and the launch-tagged page words order its workgroups); the result is the
+ * same bit for bit.
  * Limits (else KVS_EUNSUPPORTED): d_k in {64, 128}; H_q <= 128; P divides
  * 512; ceil(L_max / P) <= 16384.  K is read once; the result is
  * bit-identical from run to run.

@@ -43,7 +43,7 @@ kvs_status check_score(const kvs_score_args* in, kvs_score_args* a) {
 }
 
 struct DeltaPlan {
-  size_t x2, cstats, S, flags, total;   // byte offsets of the workspace parts
+  size_t x2, cstats, S, flags, pwords, total;   // byte offsets of the workspace parts
   int chunk, n_chunk, n_pages_max;
   int64_t x2_ld;
 };
@@ -75,7 +75,9 @@ kvs_status delta_plan(const kvs_delta_args* a, DeltaPlan* pl) {
   pl->S = off;
   off = align_up(off + (size_t)a->B * n_pages * sizeof(float), kWsAlign);
   pl->flags = off;
-  off = align_up(off + 2 * (size_t)a->B * pl->n_chunk * sizeof(uint64_t), kWsAlign);
+  off = align_up(off + (size_t)a->B * pl->n_chunk * sizeof(uint64_t), kWsAlign);
+  pl->pwords = off;
+  off = align_up(off + (size_t)a->B * n_pages * sizeof(uint64_t), kWsAlign);
   pl->total = off;
   return KVS_OK;
 }
@@ -275,7 +277,7 @@ kvs_status kvs_delta_pages(const kvs_delta_args* a, const void* Q, const void* c
   p.S = page_scores ? page_scores : reinterpret_cast<float*>(w + pl.S);
   p.rho = rho;
   p.flags = reinterpret_cast<uint64_t*>(w + pl.flags);
-  p.pflags = p.flags + (size_t)a->B * pl.n_chunk;
+  p.pwords = reinterpret_cast<uint64_t*>(w + pl.pwords);
   p.epoch = 0;
   p.wait_ticks = 0;
   p.khs = a->k_head_stride;

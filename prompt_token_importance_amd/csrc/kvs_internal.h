@@ -81,8 +81,9 @@ struct DeltaLaunch {
   float2* cstats;                  // [B][n_chunk][H_q] per-chunk (max, sum of exp2)
   float* S;                        // [B][n_pages_max] page scores
   int32_t* rho;                    // [B][K_pages]
-  uint64_t* flags;                 // [B][n_chunk] flags of the one-launch form: statistics
-  uint64_t* pflags;                //   and page scores published
+  uint64_t* flags;                 // [B][n_chunk] one-launch form: statistics published
+  uint64_t* pwords;                // [B][n_pages_max] one-launch form: page scores tagged
+                                   //   with the launch (tag << 32 | float bits)
   uint64_t epoch;                  // set by the launcher
   int64_t wait_ticks;              // set by the launcher
   int64_t khs, kts;                // khs 0: L_b * d_k

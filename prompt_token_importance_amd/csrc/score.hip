@@ -2056,32 +2056,50 @@ __device__ __forceinline__ void delta_chunk_pass(const DeltaLaunch& p, int b, in
   }
 }
 
-// rho of sequence b from its page scores (written earlier in the launch by
-// other workgroups, so read with device-scope loads): the top K - L older
-// pages (ascending), the last min(L, pages) pages, then -1, as
-// topk_delta_kernel computes it, with kThreads threads of kKpt pages each.
+// rho of sequence b from its page scores: the top K - L older pages
+// (ascending), the last min(L, pages) pages, then -1, as topk_delta_kernel
+// computes it, with kThreads threads of kKpt pages each.  The scores are the
+// tagged words the chunks of the sequence stored earlier in the launch, read
+// with device-scope loads; when any word does not carry `tag` yet, some
+// chunk is still to store its pages, and the call returns (in every thread,
+// having written nothing) with *all = 0.  *all must be 1 on entry, set
+// before a barrier.
 __device__ __forceinline__ void delta_select(const DeltaLaunch& p, int b, uint32_t* hist,
-                                             Shared& sh) {
+                                             Shared& sh, const uint64_t* words, uint32_t tag,
+                                             int* all) {
   const int Lb = min(max(p.L[b], 0), p.L_max);
   const int n_pages = (Lb + p.P - 1) / p.P;
   const int n_recent = min(p.L_recent, n_pages);
   const int n_cand = n_pages - n_recent;
   const int keep = min(p.K_pages - p.L_recent, n_cand);
-  const float* Sb = p.S + (int64_t)b * p.n_pages_max;
   int32_t* out = p.rho + (int64_t)b * p.K_pages;
   const int i0 = (int)threadIdx.x * kKpt;
   uint32_t o[kKpt], valid = 0;
-  // clamped indices and no branch, so all the loads are in flight at once
+  // Threads past the pages load nothing; within a thread the indices are
+  // clamped with no branch, so all its loads are in flight at once.
   const int last = n_cand > 0 ? n_cand - 1 : 0;
+  bool ok = true;
+  if (i0 < n_cand) {
+    uint64_t raw[kKpt];
 #pragma unroll
-  for (int e = 0; e < kKpt; ++e) {
-    const bool in = i0 + e < n_cand;
-    valid |= in ? (1u << e) : 0u;
-    const float v = __uint_as_float(__hip_atomic_load(
-        reinterpret_cast<const uint32_t*>(Sb + min(i0 + e, last)), __ATOMIC_RELAXED,
-        __HIP_MEMORY_SCOPE_AGENT));
-    o[e] = ord_key(in ? v : 0.f);
+    for (int e = 0; e < kKpt; ++e)
+      raw[e] = __hip_atomic_load(words + min(i0 + e, last), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      const bool in = i0 + e < n_cand;
+      valid |= in ? (1u << e) : 0u;
+      ok &= !in || (uint32_t)(raw[e] >> 32) == tag;
+      o[e] = ord_key(in ? __uint_as_float((uint32_t)raw[e]) : 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) o[e] = 0u;
   }
+  if (!__all(ok) && (threadIdx.x & 63) == 0) *all = 0;
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(*all)) return;
   int ph = 0;
   Kstar ks{0u, 0u, 0u};
   uint32_t gt = valid, eq = 0u;
@@ -2120,7 +2138,11 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
   const int Lb = min(max(p.L[b], 0), p.L_max);
   const int tb = chunk * p.chunk;
   if (tb >= Lb) {   // the whole workgroup: nothing of this sequence here
-    if (a.sel && chunk == 0) delta_select(p, b, nullptr, ssel);   // an empty sequence's row
+    if (a.sel && chunk == 0) {   // an empty sequence's row
+      if (threadIdx.x == 0) sh = 1;
+      __syncthreads();
+      delta_select(p, b, nullptr, ssel, nullptr, 0u, &sh);
+    }
     return;
   }
   const int te = min(tb + p.chunk, Lb);
@@ -2161,69 +2183,118 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
                                       __HIP_MEMORY_SCOPE_AGENT));
       __syncthreads();
     }
+    // Shares past the last chunk are empty, and folding an empty share leaves
+    // finite statistics unchanged, so they are skipped.
     if (threadIdx.x < p.H_q) {
       const int h = threadIdx.x;
       const int tph = kDeltaPageTokens / p.H_q;
       float m2 = kNegInf, z2 = 0.f;
-      for (int j = 0; j < tph; ++j) {
-        float mm = kNegInf, zz = 0.f;
-        for (int c = j; c < nch; c += tph) {
-          const float2 w =
-              staged ? st[c * p.H_q + h]
-                     : __builtin_bit_cast(
-                           float2, __hip_atomic_load(
-                                       reinterpret_cast<const uint64_t*>(cs + (int64_t)c * p.H_q + h),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          lse_fold(mm, zz, w.x, w.y);
+      if (staged && nch <= tph) {
+        // share j is chunk j alone: the statistics are read ahead in batches,
+        // so only the folds into (m2, z2) form a chain
+        constexpr int kB = 8;
+        for (int j0 = 0; j0 < nch; j0 += kB) {
+          float2 w[kB];
+#pragma unroll
+          for (int q = 0; q < kB; ++q) w[q] = st[min(j0 + q, nch - 1) * p.H_q + h];
+#pragma unroll
+          for (int q = 0; q < kB; ++q) {
+            if (j0 + q < nch) {
+              float mm = kNegInf, zz = 0.f;
+              lse_fold(mm, zz, w[q].x, w[q].y);
+              lse_fold(m2, z2, mm, zz);
+            }
+          }
         }
-        lse_fold(m2, z2, mm, zz);
+      } else {
+        for (int j = 0; j < min(tph, nch); ++j) {
+          float mm = kNegInf, zz = 0.f;
+          for (int c = j; c < nch; c += tph) {
+            const float2 w =
+                staged ? st[c * p.H_q + h]
+                       : __builtin_bit_cast(
+                             float2, __hip_atomic_load(
+                                         reinterpret_cast<const uint64_t*>(cs + (int64_t)c * p.H_q + h),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            lse_fold(mm, zz, w.x, w.y);
+          }
+          lse_fold(m2, z2, mm, zz);
+        }
       }
       bh[h] = m2 + log2f(z2);
     }
     __syncthreads();
   }
-  // token scores: the maximum over heads of exp2(x - b_h), this lane's 16
-  // rows, then the other half's
+  // Token scores: the maximum over heads of exp2(x - b_h), this lane's 16
+  // rows, then the other half's.  exp2 (v_exp_f32) is non-decreasing over
+  // every non-NaN float, so that maximum is exp2 of the largest x - b_h: one
+  // exp2 per token, the same value bit for bit.
   const int n_tiles = (te - tb + 31) / 32;
   const int nt = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
   float bl[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int h = 8 * (i / 4) + 4 * hl + (i % 4);
-    bl[i] = h < p.H_q ? bh[h] : kPosInf;   // exp2(x - inf) = 0 leaves the max at >= 0
+    bl[i] = h < p.H_q ? bh[h] : kPosInf;   // x - inf = -inf: no say in the maximum
   }
+  // Page sums, left to right (the chunk is a whole number of pages).  With
+  // pages of 16 tokens a page is one 16-lane row of a tile: after step s of a
+  // running sum along the row, lane k (k <= s) holds the left-to-right sum of
+  // the row's lanes 0..k, the order the other form sums in.
+  const bool row_pages = p.P == 16;
+  float* Sb = p.S + (int64_t)b * p.n_pages_max;
+  uint64_t* Wb = p.pwords + (int64_t)b * p.n_pages_max;
+  const uint32_t tag = (uint32_t)p.epoch;
+  // a page's score: the output, and for the selection a word tagged with the
+  // launch (device scope)
+  const auto put_page = [&](int u, float v) {
+    Sb[u] = v;
+    if (a.sel)
+      __hip_atomic_store(Wb + u, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
 #pragma unroll
   for (int j = 0; j < kDeltaKeepTiles; ++j) {
     if (j < nt) {
-      float sv = 0.f;
+      float y = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv = fmaxf(sv, ex2(keep[j][i] - bl[i]));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv), __float_as_uint(sv),
+      for (int i = 0; i < 16; ++i) y = fmaxf(y, keep[j][i] - bl[i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
                                                        false, false);
-      sv = fmaxf(sv, __uint_as_float(hl ? sw[0] : sw[1]));
+      y = fmaxf(y, __uint_as_float(hl ? sw[0] : sw[1]));
       const int t = tb + (wave + kWaves * j) * 32 + nl;
-      if (hl == 0 && t < te) ys[t - tb] = sv;
+      const float sv = t < te ? ex2(y) : 0.f;   // tokens past the end add +0
+      if (row_pages) {
+        float acc = sv;
+#pragma unroll
+        for (int k = 1; k < 16; ++k)
+          acc = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x111, 0xF, 0xF,
+                                                           true)) + sv;   // row_shr:1
+        if (hl == 0 && (nl & 15) == 15 && t - 15 < te) put_page((t - 15) / 16, acc);
+      } else if (hl == 0 && t < te) {
+        ys[t - tb] = sv;
+      }
     }
   }
-  __syncthreads();
-  // page sums, left to right (the chunk is a whole number of pages)
-  const int u0 = tb / p.P, u1 = (te + p.P - 1) / p.P;
-  float* Sb = p.S + (int64_t)b * p.n_pages_max;
-  for (int u = u0 + (int)threadIdx.x; u < u1; u += kThreads) {
-    const int a0 = u * p.P, a1 = min(a0 + p.P, te);
-    float acc = 0.f;
-    for (int tt = a0; tt < a1; ++tt) acc += ys[tt - tb];
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(Sb + u), __float_as_uint(acc), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (!row_pages) {
+    __syncthreads();
+    const int u0 = tb / p.P, u1 = (te + p.P - 1) / p.P;
+    for (int u = u0 + (int)threadIdx.x; u < u1; u += kThreads) {
+      const int a0 = u * p.P, a1 = min(a0 + p.P, te);
+      float acc = 0.f;
+      for (int tt = a0; tt < a1; ++tt) acc += ys[tt - tb];
+      put_page(u, acc);
+    }
   }
   if (!a.sel) return;
-  // The workgroup that finds every chunk of its sequence published selects
-  // the pages (no waiting: the last to publish sees all the flags; two that
-  // publish together both select and write the same row).
-  uint64_t* pflags = p.pflags + (int64_t)b * p.n_chunk;
-  publish_flag(pflags + chunk, p.epoch);
-  if (!wait_flags(pflags, p.epoch, nch, 0, &sh)) return;
-  delta_select(p, b, reinterpret_cast<uint32_t*>(&ring[0][0][0]), ssel);
+  // The workgroup that finds every page word of its sequence tagged selects
+  // the pages, with no waiting: each workgroup reads the words once its own
+  // stores have completed, so the last to complete sees all of them (two that
+  // complete together both select and write the same row).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (threadIdx.x == 0) sh = 1;
+  __syncthreads();
+  delta_select(p, b, reinterpret_cast<uint32_t*>(&ring[0][0][0]), ssel, Wb, tag, &sh);
 }
 
 template <int D, int NT>
@@ -2235,7 +2306,7 @@ kvs_status delta_launch(const DeltaLaunch& p, hipStream_t stream, int* selected)
           (int64_t)grid_capacity(reinterpret_cast<const void*>(&delta_fused_kernel<D>), kThreads)) {
     a.p.epoch = grid_epoch();
     a.p.wait_ticks = grid_wait_ticks();
-    a.sel = p.pflags && p.n_pages_max <= kThreads * kKpt;
+    a.sel = p.pwords && p.n_pages_max <= kThreads * kKpt;
     hipLaunchKernelGGL((delta_fused_kernel<D>), dim3(p.n_chunk, p.B), dim3(kThreads), 0, stream, a);
     *selected = a.sel;
     return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;

@@ -245,6 +245,11 @@ __device__ __forceinline__ void hist_add_runs(uint32_t* h, const uint32_t (&o)[k
 // the three pass histograms, then the list.  After the first pass only the
 // class keys of the chosen bin can hold K*; when they fit the list they are
 // compacted into it, and the later passes read the list instead of every key.
+// Once a pass finds that every key of its chosen bin is taken (the need within
+// the bin equals the bin's count), K* stops at that bin: the value returned
+// keeps the bits fixed so far and zeros below, so every key of the bin is at
+// least K* (above it, or equal with all of them taken) and every key of a
+// lower bin below it.  The chosen set is the same.
 template <int NT>
 __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t pb,
                                              uint32_t valid, uint32_t budget, uint32_t* hist,
@@ -265,7 +270,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
   a.prefix |= sh.digit << a.hi;
   a.need = sh.need;
   const uint32_t c0 = sh.cnt;
-  if (a.hi == 0) return {a.cls, a.prefix, a.need};
+  if (a.hi == 0 || a.need == c0) return {a.cls, a.prefix, a.need};
   if (c0 <= (uint32_t)kList) {
     uint32_t* list = hist + kHistWords;
     uint32_t mm = 0;
@@ -301,6 +306,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
+      if (a.need == sh.cnt) break;
     }
   } else {
 #pragma unroll 1
@@ -313,6 +319,7 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
+      if (a.need == sh.cnt) break;
     }
   }
   return {a.cls, a.prefix, a.need};

@@ -516,6 +516,7 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
+      if (a.need == sh.cnt) break;   // the bin is taken whole: K* stops at it
     }
     const Kstar ks{a.cls, a.prefix, a.need};
     uint32_t gt_base = 0, eq_base = 0;
@@ -788,6 +789,7 @@ __global__ __launch_bounds__(kT) void topk_grid_kernel(GridArgs g) {
   };
   keys_of(part, std::true_type{});
   SelectStart a{0u, 0u, 0u, 0};
+  bool whole = false;   // a digit pass found its bin taken whole: K* stops there
   int ph_scan = 0;
   // Phase ph's words of part q, from the keys in o / pb / valid.
   const auto put = [&](int ph, int q) {
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(kT) void topk_grid_kernel(GridArgs g) {
   };
 #pragma unroll 1
   for (int ph = 0; ph < kGridPhases; ++ph) {
-    if (ph >= 1 && ph <= 3 && a.hi == 0) continue;   // K* settled (the same in every part)
+    if (ph >= 1 && ph <= 3 && (a.hi == 0 || whole)) continue;   // K* settled (alike in every part)
     put(ph, part);
     // read the row's words; a part still missing at the bound is computed
     // here, in this part's key registers, whose own keys are computed again
@@ -936,6 +938,7 @@ __global__ __launch_bounds__(kT) void topk_grid_kernel(GridArgs g) {
       a.hi -= w;
       a.prefix |= sh.digit << a.hi;
       a.need = sh.need;
+      whole = a.need == sh.cnt;
     }
   }
   // this part's output offset and its share of the K*-equal keys
