@@ -2100,6 +2100,29 @@ __device__ __forceinline__ void delta_select(const DeltaLaunch& p, int b, uint32
   if (!__all(ok) && (threadIdx.x & 63) == 0) *all = 0;
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*all)) return;
+  if (n_cand <= 64 * kKpt) {
+    // every page is in wave 0: it selects alone, the other waves are done
+    if (threadIdx.x >= 64) return;
+    Kstar ks{0u, 0u, 0u};
+    uint32_t gt = valid, eq = 0u;
+    if (keep == 0) {
+      gt = 0u;
+    } else if (keep < n_cand) {
+      ks = select_wave(o, valid, (uint32_t)keep, hist);
+      classify(o, 0u, valid, ks, gt, eq);
+    }
+    uint32_t pos, rank;
+    place_wave(gt, eq, ks.need_eq, pos, rank);
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e) {
+      const bool q = (eq >> e) & 1u;
+      if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = i0 + e;
+      rank += q;
+    }
+    for (int i = threadIdx.x; i < p.K_pages - keep; i += 64)
+      out[keep + i] = i < n_recent ? n_cand + i : -1;
+    return;
+  }
   int ph = 0;
   Kstar ks{0u, 0u, 0u};
   uint32_t gt = valid, eq = 0u;

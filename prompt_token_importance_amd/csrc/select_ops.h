@@ -325,6 +325,78 @@ __device__ __forceinline__ Kstar select_regs(const uint32_t (&o)[kKpt], uint32_t
   return {a.cls, a.prefix, a.need};
 }
 
+// ------------------------------------------------------------------ one wave
+// The same selection by one wave alone (64 lanes of kKpt keys, all of one
+// class; no barrier, so the other waves of the workgroup may have left):
+// 8-bit digits below the leading bits the keys share, one LDS histogram of
+// at most 256 bins in `hist` (the wave's own), stopping early once a bin is
+// taken whole.  LDS operations of one wave take effect in program order; the
+// fences keep the compiler from moving them across the phases.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ Kstar select_wave(const uint32_t (&o)[kKpt], uint32_t valid,
+                                             uint32_t budget, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < kKpt; ++e) {
+    const bool ok = (valid >> e) & 1u;
+    mn = ok && o[e] < mn ? o[e] : mn;
+    mx = ok && o[e] > mx ? o[e] : mx;
+  }
+  mn = __builtin_amdgcn_readlane(wave_scan<OpMin>(mn, ~0u), 63);
+  mx = __builtin_amdgcn_readlane(wave_scan<OpMax>(mx, 0u), 63);
+  int hi = mn == mx ? 0 : 32 - __clz(mn ^ mx);
+  uint32_t prefix = hi == 32 ? 0u : (mn >> hi) << hi, need = budget;
+  while (hi > 0) {
+    const int w = hi < 8 ? hi : 8, shift = hi - w, nb = 1 << w;
+    const uint32_t fixed = hi >= 32 ? 0u : ~0u << hi;   // the bits already decided
+    if (4 * lane < nb) reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_fence();
+#pragma unroll
+    for (int e = 0; e < kKpt; ++e)
+      if (((valid >> e) & 1u) && ((o[e] ^ prefix) & fixed) == 0u)
+        atomicAdd(&hist[(o[e] >> shift) & (uint32_t)(nb - 1)], 1u);
+    wave_lds_fence();
+    // lane l holds bins nb-1-4l .. nb-4-4l, the highest first
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bin = nb - 1 - 4 * lane - j;
+      c[j] = bin >= 0 ? hist[bin] : 0u;
+    }
+    const uint32_t ls = c[0] + c[1] + c[2] + c[3];
+    const uint32_t inc = wave_scan<OpAdd>(ls, 0u);
+    const int L = (int)__builtin_ctzll(__ballot(inc >= need));
+    uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(inc - ls), L);
+    uint32_t cl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cl[j] = (uint32_t)__builtin_amdgcn_readlane((int)c[j], L);
+    int j = 0;
+    while (j < 3 && above + cl[j] < need) above += cl[j++];
+    need -= above;
+    hi = shift;
+    prefix |= (uint32_t)(nb - 1 - 4 * L - j) << shift;
+    wave_lds_fence();   // the reads are done before the next pass clears the bins
+    if (need == cl[j]) break;   // the bin is taken whole
+  }
+  return {0u, prefix, need};
+}
+
+// Output slot of this lane's first chosen element and the rank of its first
+// K*-equal element within one wave (place for a single wave).
+__device__ __forceinline__ void place_wave(uint32_t gt, uint32_t eq, uint32_t need_eq,
+                                           uint32_t& pos, uint32_t& rank) {
+  const uint32_t v = ((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(eq);
+  const uint32_t before = wave_scan<OpAdd>(v, 0u) - v;
+  const uint32_t gb = before >> 16, eb = before & 0xFFFFu;
+  pos = gb + min(eb, need_eq);
+  rank = eb;
+}
+
 // Chosen-key masks of this thread: gt = above K*, eq = equal to K*.
 __device__ __forceinline__ void classify(const uint32_t (&o)[kKpt], uint32_t pb, uint32_t valid,
                                          const Kstar& ks, uint32_t& gt, uint32_t& eq) {
