@@ -105,6 +105,43 @@ def test_delta_sequence_major_and_deterministic(kvs):
     assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
 
 
+@pytest.mark.parametrize("H_q,H_kv", [(32, 8), (64, 8)], ids=["one_launch", "three_kernels"])
+def test_delta_tied_page_scores(kvs, H_q, H_kv):
+    """Zero keys give every token of a sequence the same logit, so all of its full pages
+    score the same: rho must hold the lowest-index older pages.  The sequences cover the
+    one-wave selection (504 and 86 candidate pages), the workgroup one (1 242) and, with 64
+    query heads, the separate selection kernel; the page scores still match the oracle."""
+    lens, d_k, P, K_pages, L_recent = [8192, 1500, 20000, 8192], 128, 16, 64, 8
+    print(f"delta tied pages lens={lens} H_q={H_q}", flush=True)
+    B, L_max = len(lens), max(lens)
+    Qs, Ks, Kbits = [], [], []
+    for b, L in enumerate(lens):
+        ly = synth.gaussian_layer(700 + b, L=L, W=1, d_k=d_k, H_q=H_q, H_kv=H_kv, q_pos0=L - 1)
+        Qs.append(ly.Q[:, 0, :])
+        Kbits.append(np.zeros((H_kv, L, d_k), dtype=np.uint16))
+        Ks.append(kvs.bf16_from_bits(Kbits[-1]))
+    Q = kvs.bf16_from_bits(np.stack(Qs))
+    ptrs = torch.tensor([k.data_ptr() for k in Ks], dtype=torch.int64, device="cuda")
+    Lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    a = kvs.delta_args(B=B, d_k=d_k, H_q=H_q, H_kv=H_kv, L_max=L_max, P=P, K_pages=K_pages,
+                       L_recent=L_recent)
+    S = torch.full((B, (L_max + P - 1) // P), -7.0, dtype=torch.float32, device="cuda")
+    rho = kvs.kvs_delta_pages(Q, ptrs, Lt, a, page_scores=S).cpu().numpy()
+    S = S.cpu().numpy()
+    for b, L in enumerate(lens):
+        n_pages = (L + P - 1) // P
+        n_recent = min(L_recent, n_pages)
+        n_cand = n_pages - n_recent
+        keep = min(K_pages - L_recent, n_cand)
+        assert (S[b, :n_cand] == S[b, 0]).all(), "full pages of equal tokens must tie exactly"
+        want = list(range(keep)) + list(range(n_cand, n_pages))
+        want += [-1] * (K_pages - len(want))
+        np.testing.assert_array_equal(rho[b], want)
+        _, z = oracle.delta_pages(Qs[b], Kbits[b], L=L, d_k=d_k, H_q=H_q, H_kv=H_kv, P=P,
+                                  K_pages=K_pages, L_recent=L_recent)
+        np.testing.assert_allclose(S[b, :n_pages], z, rtol=REL, atol=1e-9)
+
+
 @pytest.mark.parametrize("lens,H_q,H_kv,d_k,P", [
     ([3000, 17, 2600, 0, 1024], 32, 8, 128, 16),
     ([1500], 32, 1, 64, 8),

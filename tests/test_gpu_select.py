@@ -230,6 +230,25 @@ def test_topk_equal_values(kvs, n, budget):
         np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x, budget, pr, 3))
 
 
+@pytest.mark.parametrize("n,top,budget", [(5000, 200, 1200), (131040, 200, 1200),
+                                           (131072, 10000, 26214)],
+                         ids=["one_part", "parts_and_merge", "wide_rows"])
+def test_topk_whole_bin(kvs, n, top, budget):
+    """The budget ends exactly at the edge of a radix bin, after the first, second and third
+    digit (rows 0, 1, 2: below a block of 4.0 the next values are 2.0, 1 + 2^-12 and
+    1 + 2^-22 over a floor of 1.0), so the selection stops at that bin; the chosen set must
+    still be the oracle's, in one part, through the candidate merge and across wide rows."""
+    x = np.ones((3, n), dtype=np.float32)
+    nxt = [np.float32(2.0), np.float32(1.0 + 2.0 ** -12), np.float32(1.0 + 2.0 ** -22)]
+    for r in range(3):
+        order = np.argsort(synth.u64(500 + r, 1, np.arange(n)))   # a seeded placement
+        x[r, order[:top]] = np.float32(4.0)
+        x[r, order[top:budget]] = nxt[r]
+    got = kvs.kvs_topk(dev(x), n, budget, n_forced=5)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.topk(x, budget, None, 5))
+
+
 @pytest.mark.parametrize("n,budget", [(16000, 1600), (131040, 1024), (60000, 20000)])
 def test_topk_narrow_values(kvs, n, budget):
     """Values within a few ulps of each other share all their leading bits."""
