@@ -88,12 +88,12 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", WORKLOADS["mistral128k"][1])
 
 # Sources of each workload's roofline kernel(s), besides the shared header.
 KERNEL_SOURCES = {
-    "mistral128k": ("score.hip",),
-    "llama32k": ("score.hip",),
-    "cross32x16k": ("score.hip",),
+    "mistral128k": ("grid_sync.h", "score.hip"),
+    "llama32k": ("grid_sync.h", "score.hip"),
+    "cross32x16k": ("grid_sync.h", "score.hip"),
     "gemfilter128k": ("score.hip",),
     "specprefill128k": ("score.hip",),
-    "delta32x8k": ("score.hip", "topk.hip", "wave_ops.h"),
+    "delta32x8k": ("grid_sync.h", "score.hip", "select_ops.h", "topk.hip", "wave_ops.h"),
     "gather128k": ("gather.hip",),
     "chunksel128k": ("blocks.hip", "wave_ops.h"),
     "chunksel128k_uncached": ("blocks.hip", "wave_ops.h"),
