@@ -1916,10 +1916,13 @@ __global__ __launch_bounds__(kDeltaPageTokens) void delta_page_kernel(DeltaArgs 
 // sequence, folds them into b_h in delta_page_kernel's order, and forms the
 // token and page scores from its registers.  Results are bit-identical to
 // the two kernels'.  A chunk still unpublished at the wait bound is computed
-// by the waiter (statistics only), bit-identically.
+// by the waiter (statistics only), bit-identically.  With the selection in
+// the launch too, the page scores also go out as words tagged with the
+// launch, and the workgroup that finds all of its sequence's words tagged
+// selects the pages (topk_delta_kernel's selection, in one wave when the
+// pages fit it).
 constexpr int kDeltaKeepTiles = 8;
-// K ring stages per wave of the one-launch form: with no stores in the loop,
-// a deeper ring keeps more of the stream in flight.
+// K ring stages per wave of the one-launch form (a fourth was no faster).
 constexpr int kDeltaStages = 3;
 
 // Streams chunk `chunk` of sequence b (logits of every head, as
