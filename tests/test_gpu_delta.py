@@ -86,6 +86,8 @@ CASES = [
     ([1500, 700], 128, 8, 128, 16, 16, 4),                          # four row tiles, G = 16
     ([1, 15, 16, 17, 100, 1000, 2500, 0], 32, 8, 128, 16, 8, 2),   # ragged, in one launch
     ([5000, 3000], 32, 8, 64, 512, 4, 1),                           # pages longer than a chunk
+    ([16512, 16528, 16496], 32, 8, 128, 16, 64, 8),   # 1 024 / 1 025 / 1 023 candidate pages:
+                                                      # the one-wave selection's edge
 ]
 
 
