@@ -465,8 +465,12 @@ __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, in
   }
 }
 
-// The final selection among the candidates of all parts of a row.
-__global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
+// The final selection among the candidates of all parts of a row, by NT
+// threads: as many as hold the candidates in registers (a phase costs each
+// SIMD the instructions of all its waves, filled or not), or kT with the
+// candidates re-read by tiles when they are more.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(Params s) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWords];
   __shared__ Shared sh;
   const int row = blockIdx.x;
@@ -476,18 +480,18 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
   uint32_t o[kKpt], ix[kKpt], pb, valid;
   int ph = 0;
   uint32_t gt, eq, pos, rank, tg, te;
-  if (count <= kCap) {
+  if (count <= (int64_t)NT * kKpt) {
     cand_keys(s, c, 0, count, o, pb, ix, valid);
-    const Kstar ks = select_regs<kT>(o, pb, valid, (uint32_t)s.budget, hist, sh, ph);
+    const Kstar ks = select_regs<NT>(o, pb, valid, (uint32_t)s.budget, hist, sh, ph);
     classify(o, pb, valid, ks, gt, eq);
-    place<kT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
+    place<NT>(gt, eq, ks.need_eq, 0u, 0u, sh, ph, pos, rank, tg, te);
 #pragma unroll
     for (int e = 0; e < kKpt; ++e) {
       const bool q = (eq >> e) & 1u;
       if (((gt >> e) & 1u) || (q && rank < ks.need_eq)) out[pos++] = (int32_t)ix[e];
       rank += q;
     }
-  } else {
+  } else if constexpr (NT == kT) {
     // more candidates than registers hold: every pass re-reads them by tiles
     for (int b = threadIdx.x; b < kHistWords; b += kT) hist[b] = 0u;
     uint32_t acc[5] = {0u, ~0u, 0u, ~0u, 0u};
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(kT) void topk_merge_kernel(Params s) {
       eq_base += te;
     }
   }
-  write_forced<kT>(s, out);
+  write_forced<NT>(s, out);
 }
 
 // ------------------------------------------------------------------ wide rows
@@ -1059,11 +1063,23 @@ int64_t cand_ld_of(int n, int budget) {
 template <int T>
 void launch(const Params& s, int H, hipStream_t stream) {
   const unsigned grid = (unsigned)s.parts * (unsigned)H;
-  if (s.part == kSmallCap)
+  // a single part gets only the threads its elements fill (as the merge below)
+  const bool one = s.parts == 1;
+  if (one && s.n <= 256 * kKpt)
+    hipLaunchKernelGGL((topk_part_kernel<T, 256>), dim3(grid), dim3(256), 0, stream, s, H);
+  else if (s.part == kSmallCap || (one && s.n <= kSmallCap))
     hipLaunchKernelGGL((topk_part_kernel<T, kSmallT>), dim3(grid), dim3(kSmallT), 0, stream, s, H);
   else
     hipLaunchKernelGGL((topk_part_kernel<T, kT>), dim3(grid), dim3(kT), 0, stream, s, H);
-  if (s.parts > 1) hipLaunchKernelGGL(topk_merge_kernel, dim3(H), dim3(kT), 0, stream, s);
+  if (s.parts > 1) {
+    const int64_t count = (int64_t)s.parts * s.stride;
+    if (count <= 256 * kKpt)
+      hipLaunchKernelGGL(topk_merge_kernel<256>, dim3(H), dim3(256), 0, stream, s);
+    else if (count <= kSmallCap)
+      hipLaunchKernelGGL(topk_merge_kernel<kSmallT>, dim3(H), dim3(kSmallT), 0, stream, s);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel<kT>, dim3(H), dim3(kT), 0, stream, s);
+  }
 }
 
 // The one-launch form for rows of 2 to kWideMaxParts parts of kCap elements;
