@@ -10,9 +10,10 @@
 // An element's rank is decided by its class (1 = priority) and then by an
 // order-preserving 32-bit map of its float32 value.  Selection runs inside
 // single workgroups, so no workgroup ever waits for another:
-//  stage 1  a row is cut into parts (8192 elements for 512-thread workgroups
-//           when the candidates of all parts fit one merge, else 16384 for
-//           1024 threads), one workgroup per (part, row).  The workgroup
+//  stage 1  a row is cut into parts (4096 or 8192 elements for 256- or
+//           512-thread workgroups when the candidates of all parts fit one
+//           merge, else 16384 for 1024 threads), one workgroup per (part,
+//           row).  The workgroup
 //           computes its keys in registers (16 per thread; the pooling or
 //           cluster transform is applied here and never stored), finds its
 //           local top-`budget` and writes the chosen (key, index) pairs in
@@ -37,6 +38,8 @@ namespace {
 constexpr int kCap = kT * kKpt;             // keys of a 1024-thread workgroup (16384)
 constexpr int kSmallT = 512;                // threads of a stage-1 workgroup on small parts
 constexpr int kSmallCap = kSmallT * kKpt;   // 8192
+constexpr int kTinyT = 256;                 // ... and on the smallest parts
+constexpr int kTinyCap = kTinyT * kKpt;     // 4096
 constexpr uint32_t kIdxMask = 0x7FFFFFFFu;
 
 enum Transform { kPlain = 0, kPool = 1, kCluster = 2 };
@@ -1045,12 +1048,16 @@ bool wide_path(int n, int budget) {
   return parts > 1 && parts <= kWideMaxParts && (int64_t)parts * stride > kCap;
 }
 
-// Elements per stage-1 part: small parts (twice the workgroups, each with half
-// the keys) when the candidates of all of them still fit one merge workgroup.
+// Elements per stage-1 part: the smallest of 4 096, 8 192 and 16 384 (more
+// workgroups, each with fewer keys) whose parts' candidates all still fit one
+// merge workgroup.
 int part_of(int n, int budget) {
   if (n <= kCap || wide_path(n, budget)) return kCap;
-  const int stride = budget < kSmallCap ? budget : kSmallCap;
-  return (int64_t)ceil_div(n, kSmallCap) * stride <= kCap ? kSmallCap : kCap;
+  for (const int part : {kTinyCap, kSmallCap}) {
+    const int stride = budget < part ? budget : part;
+    if ((int64_t)ceil_div(n, part) * stride <= kCap) return part;
+  }
+  return kCap;
 }
 
 int64_t cand_ld_of(int n, int budget) {
@@ -1065,16 +1072,16 @@ void launch(const Params& s, int H, hipStream_t stream) {
   const unsigned grid = (unsigned)s.parts * (unsigned)H;
   // a single part gets only the threads its elements fill (as the merge below)
   const bool one = s.parts == 1;
-  if (one && s.n <= 256 * kKpt)
-    hipLaunchKernelGGL((topk_part_kernel<T, 256>), dim3(grid), dim3(256), 0, stream, s, H);
+  if (s.part == kTinyCap || (one && s.n <= kTinyCap))
+    hipLaunchKernelGGL((topk_part_kernel<T, kTinyT>), dim3(grid), dim3(kTinyT), 0, stream, s, H);
   else if (s.part == kSmallCap || (one && s.n <= kSmallCap))
     hipLaunchKernelGGL((topk_part_kernel<T, kSmallT>), dim3(grid), dim3(kSmallT), 0, stream, s, H);
   else
     hipLaunchKernelGGL((topk_part_kernel<T, kT>), dim3(grid), dim3(kT), 0, stream, s, H);
   if (s.parts > 1) {
     const int64_t count = (int64_t)s.parts * s.stride;
-    if (count <= 256 * kKpt)
-      hipLaunchKernelGGL(topk_merge_kernel<256>, dim3(H), dim3(256), 0, stream, s);
+    if (count <= kTinyCap)
+      hipLaunchKernelGGL(topk_merge_kernel<kTinyT>, dim3(H), dim3(kTinyT), 0, stream, s);
     else if (count <= kSmallCap)
       hipLaunchKernelGGL(topk_merge_kernel<kSmallT>, dim3(H), dim3(kSmallT), 0, stream, s);
     else
