@@ -172,7 +172,9 @@ __device__ __forceinline__ void topp_pick(ToppShared& sh, uint32_t need) {
 }
 
 // ------------------------------------------------------------------ top-p per (head, query block)
-// One workgroup per (head, query block); thread t holds key blocks t + 256 u.
+// One workgroup per (head, query block); thread t holds key blocks t + 256 u,
+// u < PT, with PT the fewest of 4, 8 and 16 that cover the KV blocks (every
+// slot is worked through in every phase, filled or not).
 // Softmax over the visible blocks with wave and workgroup reductions in a
 // fixed order.  The kept blocks are a prefix of the order (probability desc,
 // j asc): a block is kept while the mass ranked strictly before it is <
@@ -182,6 +184,7 @@ __device__ __forceinline__ void topp_pick(ToppShared& sh, uint32_t need) {
 // all keys, then the keys of the crossing bin are compacted into a list; a
 // short list is finished by one wave (each lane sums the mass of the keys
 // above its own), a long one by three more digits over the list.
+template <int PT>
 __global__ __launch_bounds__(kThreads) void block_topp_kernel(
     const float* __restrict__ logit, int n_qb, int n_kvb, int block, int Lq,
     int64_t q_pos0, float p_mass, uint8_t* __restrict__ M) {
@@ -192,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
   const int64_t end_pos = q_pos0 + last_row;
   const float* lr = logit + ((int64_t)h * n_qb + i) * n_kvb;
   // 1. logits of the visible blocks and their maximum
-  float v[kPerThread];
+  float v[PT];
   uint32_t vis = 0;
   float mloc = -__builtin_inff();
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < PT; ++u) {
     const int j = tid + kThreads * u;
     const bool in = j < n_kvb && (int64_t)j * block <= end_pos;
     v[u] = in ? lr[j] : -__builtin_inff();
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
   // 2. softmax numerators and their sum
   float sloc = 0.f;
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < PT; ++u) {
     const float e = ((vis >> u) & 1u) ? expf(v[u] - mx) : 0.f;
     v[u] = e;
     sloc += e;
@@ -227,16 +230,16 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
 #pragma unroll
   for (int w = 1; w < kThreads / 64; ++w) z += sh.red[1][w];
   const float inv_z = 1.0f / z;
-  uint32_t o[kPerThread];
+  uint32_t o[PT];
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < PT; ++u) {
     v[u] *= inv_z;   // probability
     o[u] = ord_pos(v[u]);
   }
   // 3. first digit: the 11 leading bits of the key (o >> 21), over every key
   const uint32_t need0 = (uint32_t)((double)p_mass * 1073741824.0);
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u)
+  for (int u = 0; u < PT; ++u)
     if ((vis >> u) & 1u) atomicAdd(&sh.hm[o[u] >> 21], mass_of(v[u]));
   __syncthreads();
   if (wave == 0) topp_pick(sh, need0);
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
     const uint32_t d0 = sh.digit;
     uint32_t need = sh.need;
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u)
+    for (int u = 0; u < PT; ++u)
       if (((vis >> u) & 1u) && (o[u] >> 21) == d0) {
         const uint32_t at = atomicAdd(&sh.n, 1u);
         sh.lo[at] = o[u];
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void block_topp_kernel(
   // 4. keep the visible blocks at or above K* (every visible block when `all`)
   uint8_t* mrow = M + ((int64_t)h * n_qb + i) * n_kvb;
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
+  for (int u = 0; u < PT; ++u) {
     const int j = tid + kThreads * u;
     if (j < n_kvb) mrow[j] = (((vis >> u) & 1u) && (all || key44(o[u], j) >= kstar)) ? 1 : 0;
   }
@@ -476,8 +479,11 @@ kvs_status block_select_run(const kvs_block_select_args* a, const BlockPlan& pl,
                      dim3((pl.n_kvb + kLt - 1) / kLt, a->H_kv, (G * pl.n_qb + kLt - 1) / kLt),
                      dim3(kThreads), 0, stream, Qb, Kb, kb_ld, G, pl.n_qb, pl.n_kvb, a->d_k, scale,
                      logit);
-  hipLaunchKernelGGL(block_topp_kernel, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, logit,
-                     pl.n_qb, pl.n_kvb, a->block, a->Lq, a->q_pos0, a->p_mass, M);
+  const auto topp = pl.n_kvb <= 4 * kThreads   ? &block_topp_kernel<4>
+                    : pl.n_kvb <= 8 * kThreads ? &block_topp_kernel<8>
+                                               : &block_topp_kernel<kPerThread>;
+  hipLaunchKernelGGL(topp, dim3(pl.n_qb, a->H_q), dim3(kThreads), 0, stream, logit, pl.n_qb,
+                     pl.n_kvb, a->block, a->Lq, a->q_pos0, a->p_mass, M);
   return hipGetLastError() == hipSuccess ? KVS_OK : KVS_EHIP;
 }
 
