@@ -469,9 +469,9 @@ __device__ __forceinline__ void cand_keys(const Params& s, const uint64_t* c, in
 }
 
 // The final selection among the candidates of all parts of a row, by NT
-// threads: as many as hold the candidates in registers (a phase costs each
-// SIMD the instructions of all its waves, filled or not), or kT with the
-// candidates re-read by tiles when they are more.
+// threads: as many as hold the candidates in registers (every wave runs
+// every phase, filled or not, and each barrier waits for the slowest), or kT
+// with the candidates re-read by tiles when they are more.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_merge_kernel(Params s) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWords];
