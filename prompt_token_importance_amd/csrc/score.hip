@@ -2279,27 +2279,40 @@ __global__ __launch_bounds__(kThreads, 1) void delta_fused_kernel(DeltaArgs a) {
       __hip_atomic_store(Wb + u, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   };
+  // every tile's scores first (tiles past this wave's are 0), so the tiles'
+  // running sums below are independent chains that interleave
+  float sv[kDeltaKeepTiles];
 #pragma unroll
   for (int j = 0; j < kDeltaKeepTiles; ++j) {
-    if (j < nt) {
-      float y = kNegInf;
+    float y = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y = fmaxf(y, keep[j][i] - bl[i]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
-                                                       false, false);
-      y = fmaxf(y, __uint_as_float(hl ? sw[0] : sw[1]));
+    for (int i = 0; i < 16; ++i) y = fmaxf(y, keep[j][i] - bl[i]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y),
+                                                     false, false);
+    y = fmaxf(y, __uint_as_float(hl ? sw[0] : sw[1]));
+    const int t = tb + (wave + kWaves * j) * 32 + nl;
+    sv[j] = j < nt && t < te ? ex2(y) : 0.f;   // tokens past the end add +0
+  }
+  if (row_pages) {
+    float acc[kDeltaKeepTiles];
+#pragma unroll
+    for (int j = 0; j < kDeltaKeepTiles; ++j) acc[j] = sv[j];
+#pragma unroll
+    for (int k = 1; k < 16; ++k)
+#pragma unroll
+      for (int j = 0; j < kDeltaKeepTiles; ++j)
+        acc[j] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[j]), 0x111, 0xF,
+                                                            0xF, true)) + sv[j];   // row_shr:1
+#pragma unroll
+    for (int j = 0; j < kDeltaKeepTiles; ++j) {
       const int t = tb + (wave + kWaves * j) * 32 + nl;
-      const float sv = t < te ? ex2(y) : 0.f;   // tokens past the end add +0
-      if (row_pages) {
-        float acc = sv;
+      if (j < nt && hl == 0 && (nl & 15) == 15 && t - 15 < te) put_page((t - 15) / 16, acc[j]);
+    }
+  } else {
 #pragma unroll
-        for (int k = 1; k < 16; ++k)
-          acc = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x111, 0xF, 0xF,
-                                                           true)) + sv;   // row_shr:1
-        if (hl == 0 && (nl & 15) == 15 && t - 15 < te) put_page((t - 15) / 16, acc);
-      } else if (hl == 0 && t < te) {
-        ys[t - tb] = sv;
-      }
+    for (int j = 0; j < kDeltaKeepTiles; ++j) {
+      const int t = tb + (wave + kWaves * j) * 32 + nl;
+      if (j < nt && hl == 0 && t < te) ys[t - tb] = sv[j];
     }
   }
   if (!row_pages) {
